@@ -1,0 +1,212 @@
+/*
+ * tfb.h -- C ABI of the MI355X (gfx950) tensor-autograd hot path.
+ *
+ * The operations are those of the tensor autograd engine described in
+ *   [Autograd-1] arabroot.io, "Build a language model in C# from scratch (1):
+ *                the Autograd engine"
+ *   [GPT2-4]     arabroot.io, "Build a language model in C# from scratch (4):
+ *                running the GPT-2 weights"
+ * Each forward call computes its output on the GPU and, unless gradients are
+ * disabled, records one entry on the context's tape; tfb_backward replays the
+ * entries' backward rules in reverse order.
+ *
+ * Conventions
+ *  - Every function returns 0 (TFB_OK) or a negative TFB_ERR_* code.  The text
+ *    of the last error of the calling thread is available from tfb_last_error().
+ *    Argument and shape checks happen on the host before anything is enqueued;
+ *    a failed call enqueues nothing and leaves the context usable.
+ *  - All work is enqueued asynchronously on the HIP stream given to tfb_init.
+ *    GPU faults surface as TFB_ERR_HIP from tfb_sync or a later call.
+ *  - Tensors are float32, row-major, contiguous.  A tensor's "rows" are the
+ *    product of all dimensions but the last ([Autograd-1, "The Tensor class"]).
+ *  - Pointers named dev_* are device pointers; host_* are host pointers.
+ *  - Handles (tfb_tensor) are small non-negative integers owned by the context.
+ *
+ * Memory
+ *  - The caller gives tfb_init one device buffer (the arena).  The library never
+ *    calls hipMalloc for tensors: persistent allocations (parameters created with
+ *    dev_ptr == NULL, parameter gradients, optimizer moments) grow from the low
+ *    end, per-step allocations (op outputs, saved tensors, non-leaf gradients,
+ *    scratch) from the high end.  Exhaustion returns TFB_ERR_OOM.
+ *  - Op outputs and everything the tape saved are valid until tfb_tape_reset.
+ */
+#ifndef TFB_H
+#define TFB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tfb_ctx tfb_ctx;
+typedef struct tfb_opt tfb_opt;
+typedef int32_t tfb_tensor;
+
+#define TFB_OK 0
+#define TFB_ERR_ARG (-1)    /* bad argument: null pointer, unknown handle, bad enum */
+#define TFB_ERR_SHAPE (-2)  /* shapes do not fit the op */
+#define TFB_ERR_STATE (-3)  /* e.g. backward from a non-scalar, released tensor in use */
+#define TFB_ERR_OOM (-4)    /* arena exhausted */
+#define TFB_ERR_HIP (-5)    /* a HIP runtime call failed */
+
+/* Arithmetic of the contractions (MatMul family and the attention products). */
+#define TFB_FP32 0       /* fp32 operands, fp32 MFMA, fp32 accumulation */
+#define TFB_BF16_MFMA 1  /* operands rounded to bf16 (nearest-even), fp32 accumulation;
+                            every other op and all stored tensors stay fp32 */
+
+#define TFB_MAX_DIMS 6
+
+/* ---------------------------------------------------------------- context */
+
+/* Create a context on `device` that enqueues on `hip_stream` (a hipStream_t;
+ * NULL = the null stream) and sub-allocates from [arena, arena + arena_bytes)
+ * (device memory owned by the caller, at least 256-byte aligned). */
+int tfb_init(tfb_ctx** out, int device, void* hip_stream, void* arena, size_t arena_bytes, int precision);
+int tfb_destroy(tfb_ctx* ctx);
+const char* tfb_last_error(void);
+int tfb_set_precision(tfb_ctx* ctx, int precision);
+/* Inference mode: with enabled == 0 ops record nothing ([Autograd-1, "The
+ * Tensor class": the NoGrad flag]).  Per context. */
+int tfb_set_grad_enabled(tfb_ctx* ctx, int enabled);
+/* Wait for all enqueued work; returns TFB_ERR_HIP if any of it failed. */
+int tfb_sync(tfb_ctx* ctx);
+/* Bytes in use at the low (persistent) and high (step) ends of the arena. */
+int tfb_arena_usage(tfb_ctx* ctx, size_t* persistent, size_t* step);
+
+/* ---------------------------------------------------------------- tensors */
+
+/* A leaf tensor ([Autograd-1, "The Tensor class": op "leaf"]).  With dev_ptr
+ * != NULL the tensor borrows that device memory (the caller keeps it alive and
+ * 256-byte aligned); with NULL it is allocated in the persistent arena and
+ * zero-filled.  is_param marks optimizer parameters (informational). */
+int tfb_tensor_create(tfb_ctx* ctx, const int64_t* shape, int ndim, void* dev_ptr, int is_param,
+                      tfb_tensor* out);
+/* Shape, rank and device pointers of a tensor; *grad is NULL while the tensor
+ * has no gradient buffer.  Any output pointer may be NULL. */
+int tfb_tensor_info(tfb_ctx* ctx, tfb_tensor t, int64_t* shape, int* ndim, void** data, void** grad);
+/* Copy n floats between host memory and the tensor's data (which == 0) or
+ * gradient (which == 1; reading a gradient that was cleared returns zeros,
+ * reading one that never existed is TFB_ERR_STATE).  Synchronous. */
+int tfb_tensor_write(tfb_ctx* ctx, tfb_tensor t, const float* host_src, int64_t n);
+int tfb_tensor_read(tfb_ctx* ctx, tfb_tensor t, int which, float* host_dst, int64_t n);
+/* Release a leaf tensor.  Op outputs are released by tfb_tape_reset. */
+int tfb_tensor_release(tfb_ctx* ctx, tfb_tensor t);
+
+/* ---------------------------------------------------------------- ops
+ * Each op writes its new output handle to *y.  Backward rules add into the
+ * inputs' gradients ([Autograd-1, "Why += and not ="]). */
+
+/* y = a + b; b equals the trailing dims of a (bias broadcast); db sums over the
+ * leading dims.  [Autograd-1, table of ops: Add with broadcast] */
+int tfb_add(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y);
+/* y = a * b elementwise; sizes must match.  [Autograd-1, "Ops": Mul] */
+int tfb_mul(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y);
+/* y = s * a.  [Autograd-1, table of ops: Scale] */
+int tfb_scale(tfb_ctx* ctx, tfb_tensor a, float s, tfb_tensor* y);
+/* y[0] = sum of all elements of a.  [Autograd-1, table of ops: Sum] */
+int tfb_sum(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y);
+/* Same data, new shape of equal size.  [Autograd-1, table of ops: Reshape] */
+int tfb_reshape(tfb_ctx* ctx, tfb_tensor a, const int64_t* shape, int ndim, tfb_tensor* y);
+/* y = tanh(a); backward g(1 - y^2).  [Autograd-1, table of ops: Tanh] */
+int tfb_tanh(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y);
+/* y = 0.5 a (1 + tanh(sqrt(2/pi)(a + 0.044715 a^3))), GPT-2's tanh form.
+ * [GPT2-4, "Common mistakes"] */
+int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y);
+/* y = x[..., K] @ w[K, M] (rows of x flattened).  Backward dx = g w^T,
+ * dw = x^T g.  [Autograd-1, "Ops": MatMul] */
+int tfb_matmul(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y);
+/* y = x[..., C] @ w[V, C]^T, the weight-tied LM head.  Backward dx = g w,
+ * dw = g^T x.  [GPT2-4, "Loading the weights": weight tying] */
+int tfb_matmul_t(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y);
+/* y = x @ w + b as one op (MatMul followed by the bias Add, fused into the
+ * contraction's epilogue); w is [in, out] as GPT-2 stores it.
+ * [GPT2-4, "Loading the weights": Linear weights stored [in, out]] */
+int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y);
+/* Per row over the last dim: (x - mean)/sqrt(var + eps) * gamma + beta with the
+ * biased variance.  [Autograd-1, table of ops: LayerNorm] */
+int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y);
+/* y[b, t, :] = table[ids[b*T + t], :], y shape [batch, n/batch, C]; backward
+ * scatter-adds rows into table's gradient (sorted segment sum: deterministic).
+ * dev_ids: n int32 device values in [0, rows(table)), copied by the call.
+ * [Autograd-1, table of ops: Embedding; GPT2-4, "Generation with KV cache"] */
+int tfb_embedding(tfb_ctx* ctx, tfb_tensor table, const int32_t* dev_ids, int64_t n, int64_t batch,
+                  tfb_tensor* y);
+/* Slice [start, start+len) of the last dim.  [Autograd-1, table of ops: Narrow] */
+int tfb_narrow(tfb_ctx* ctx, tfb_tensor x, int64_t start, int64_t len, tfb_tensor* y);
+/* [B, T, H*hs] -> [B, H, T, hs], head h = columns h*hs..h*hs+hs-1; and back.
+ * [Autograd-1, table of ops: SplitHeads, MergeHeads] */
+int tfb_split_heads(tfb_ctx* ctx, tfb_tensor x, int heads, tfb_tensor* y);
+int tfb_merge_heads(tfb_ctx* ctx, tfb_tensor x, tfb_tensor* y);
+/* a[Z, n, k] @ b[Z, k, m] and a[Z, n, k] @ b[Z, m, k]^T per batch entry.
+ * [Autograd-1, table of ops: BatchMatMul, BatchMatMulT] */
+int tfb_batch_matmul(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y);
+int tfb_batch_matmul_t(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y);
+/* Row r of the [rows, T] view sees columns j <= r mod T; softmax over those,
+ * exact zeros elsewhere.  [GPT2-4, "The 12 unused tensors": the mask is
+ * computed, visible = r % t + 1] */
+int tfb_causal_softmax(tfb_ctx* ctx, tfb_tensor s, tfb_tensor* y);
+/* The attention core as one tape entry: from qkv [B, T, 3C] (q, k, v = the
+ * three column thirds, heads = hs-column slices) compute
+ * y = MergeHeads(CausalSoftmax(q k^T / sqrt(hs)) v), y [B, T, C].  Same
+ * arithmetic as Narrow/SplitHeads/BatchMatMulT/Scale/CausalSoftmax/
+ * BatchMatMul/MergeHeads; the head split is folded into the products'
+ * addressing and the masked upper triangle is never computed.
+ * [Autograd-1, table of ops; GPT2-4, "Generation with KV cache"] */
+int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y);
+/* loss[0] = mean over rows of -log(max(softmax(logits_row)[target], 1e-30));
+ * backward (g/n)(p - onehot).  dev_targets: n = rows(logits) int32 device
+ * values in [0, cols), copied by the call.  [Autograd-1, "Ops":
+ * SoftmaxCrossEntropy] */
+int tfb_softmax_cross_entropy(tfb_ctx* ctx, tfb_tensor logits, const int32_t* dev_targets, int64_t n,
+                              tfb_tensor* loss);
+
+/* ---------------------------------------------------------------- autograd */
+
+/* [Autograd-1, "How each op records itself in the graph"]: loss must have one
+ * element (else TFB_ERR_STATE); gradients of op outputs start at zero, the
+ * loss's gradient is seeded with 1 and the recorded rules run from the last
+ * entry to the first.  Leaf gradients keep accumulating across calls until
+ * tfb_zero_grad. */
+int tfb_backward(tfb_ctx* ctx, tfb_tensor loss);
+/* Clear the gradients of the given leaf tensors ([Autograd-1, "The
+ * Optimizer": ZeroGrad]).  Tensors that never had a gradient are skipped. */
+int tfb_zero_grad(tfb_ctx* ctx, const tfb_tensor* params, int n);
+/* End of step: drop the tape, release every op output and free the step end
+ * of the arena. */
+int tfb_tape_reset(tfb_ctx* ctx);
+
+/* ---------------------------------------------------------------- optimizers */
+
+/* AdamW ([Autograd-1, "The Optimizer": AdamW]): per step t += 1, bc1 = 1 -
+ * beta1^t, bc2 = 1 - beta2^t; for every parameter that has a gradient,
+ * m = b1 m + (1-b1) g, v = b2 v + (1-b2) g^2,
+ * p -= lr * ((m/bc1) / (sqrt(v/bc2) + eps) + wd_k p) with wd_k = wd for
+ * tensors of rank >= 2 and 0 otherwise.  m and v live in the persistent arena.
+ * One fused launch updates all parameters. */
+int tfb_adamw_create(tfb_ctx* ctx, const tfb_tensor* params, int n, float lr, float weight_decay, float beta1,
+                     float beta2, float eps, tfb_opt** out);
+int tfb_adamw_step(tfb_opt* opt);
+int tfb_adamw_set_lr(tfb_opt* opt, float lr);
+/* Read the moments of parameter i (copies n floats each; NULL skips). */
+int tfb_adamw_moments(tfb_opt* opt, int i, float* host_m, float* host_v, int64_t n);
+int tfb_adamw_destroy(tfb_opt* opt);
+/* w -= lr * g for every given parameter that has a gradient.
+ * [Autograd-1, "The Optimizer": SGD] */
+int tfb_sgd_step(tfb_ctx* ctx, const tfb_tensor* params, int n, float lr);
+
+/* ---------------------------------------------------------------- measurement */
+
+/* Between begin and end, every contraction launch (the MatMul family and the
+ * attention products, with any split-K reduction) is bracketed by HIP events on
+ * the context's stream.  end() synchronises and returns the summed kernel time
+ * in milliseconds, the algorithmic flops of those launches (2*M*N*K, causal
+ * products counted over the needed triangle only) and the number of launches. */
+int tfb_profile_begin(tfb_ctx* ctx);
+int tfb_profile_end(tfb_ctx* ctx, double* gemm_ms, double* gemm_flops, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TFB_H */

@@ -4,8 +4,17 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-if ROOT not in sys.path:
-    sys.path.insert(0, ROOT)
+for _p in (ROOT, os.path.join(ROOT, "tests")):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
+
+
+def gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
 
 
 def pytest_configure(config):
@@ -21,3 +30,14 @@ def golden():
         with open(os.path.join(ROOT, "tests", "golden", name)) as f:
             return json.load(f)
     return load
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    """A library context with a 4 GiB arena on cuda:0 (fp32 contractions)."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import transformer_fwd_bwd_amd as T
+    c = T.Context(arena_bytes=4 << 30, precision="fp32")
+    yield c
+    c.close()

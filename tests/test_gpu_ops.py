@@ -1,0 +1,311 @@
+"""Per-op parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs, forward values and every input gradient.  Sizes span
+several 128-wide tiles and leave ragged tails in every dimension."""
+import math
+
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import engine as E
+from parity import FWD_TOL, GRAD_TOL, assert_close, gpu_op_with_grads, oracle_op_with_grads
+
+pytestmark = pytest.mark.gpu
+
+T = pytest.importorskip("transformer_fwd_bwd_amd")
+
+
+def rnd(seed, shape, scale=1.0):
+    return S.random_array(seed, shape, scale)
+
+
+def check(ctx, prec, gpu_build, oracle_build, arrays, out_shape, seed=999, fwd_tol=None, grad_tol=None):
+    ctx.set_precision(prec)
+    R = rnd(seed, out_shape)
+    out, grads = gpu_op_with_grads(ctx, gpu_build, arrays, R)
+    ref, rgrads = oracle_op_with_grads(oracle_build, arrays, R)
+    assert_close(out, ref, fwd_tol or FWD_TOL[prec], "forward")
+    for i, (g, r) in enumerate(zip(grads, rgrads)):
+        assert_close(g, r, grad_tol or GRAD_TOL[prec], f"grad {i}")
+    ctx.set_precision("fp32")
+
+
+PRECS = ["fp32", "bf16"]
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_matmul(ctx, prec):
+    check(ctx, prec, T.matmul, E.matmul, [rnd(1, (3, 100, 200)), rnd(2, (200, 260), 0.1)], (3, 100, 260))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_matmul_t(ctx, prec):
+    check(ctx, prec, T.matmul_t, E.matmul_t, [rnd(3, (300, 200)), rnd(4, (261, 200), 0.1)], (300, 261))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_linear_is_matmul_plus_bias(ctx, prec):
+    check(ctx, prec, T.linear, lambda x, w, b: E.add(E.matmul(x, w), b),
+          [rnd(5, (300, 200)), rnd(6, (200, 260), 0.1), rnd(7, (260,))], (300, 260))
+
+
+def test_linear_long_k_split(ctx):
+    # a long reduction (the dW contractions of the GPT have K = 8192) takes the split-K path
+    check(ctx, "fp32", T.linear, lambda x, w, b: E.add(E.matmul(x, w), b),
+          [rnd(8, (4100, 96)), rnd(9, (96, 130), 0.1), rnd(10, (130,))], (4100, 130))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_batch_matmul(ctx, prec):
+    check(ctx, prec, T.batch_matmul, E.batch_matmul, [rnd(11, (3, 130, 70)), rnd(12, (3, 70, 150))], (3, 130, 150))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_batch_matmul_t(ctx, prec):
+    check(ctx, prec, T.batch_matmul_t, E.batch_matmul_t, [rnd(13, (3, 130, 70)), rnd(14, (3, 150, 70))],
+          (3, 130, 150))
+
+
+def test_add_broadcast_and_same_shape(ctx):
+    check(ctx, "fp32", T.add, E.add, [rnd(15, (5, 37, 48)), rnd(16, (48,))], (5, 37, 48))
+    check(ctx, "fp32", T.add, E.add, [rnd(17, (5, 37, 47)), rnd(18, (37, 47))], (5, 37, 47))
+    check(ctx, "fp32", T.add, E.add, [rnd(19, (300, 257)), rnd(20, (300, 257))], (300, 257))
+
+
+@pytest.mark.parametrize("name", ["mul", "scale", "tanh", "gelu", "reshape", "sum"])
+def test_pointwise(ctx, name):
+    a, b = rnd(21, (300, 257), 2.0), rnd(22, (300, 257))
+    if name == "mul":
+        check(ctx, "fp32", T.mul, E.mul, [a, b], a.shape)
+    elif name == "scale":
+        check(ctx, "fp32", lambda x: T.scale(x, 0.37), lambda x: E.scale(x, 0.37), [a], a.shape)
+    elif name == "tanh":
+        check(ctx, "fp32", T.tanh, E.tanh, [a], a.shape)
+    elif name == "gelu":
+        check(ctx, "fp32", T.gelu, E.gelu, [a], a.shape)
+    elif name == "reshape":
+        check(ctx, "fp32", lambda x: T.reshape(x, (257, 300)), lambda x: E.reshape(x, (257, 300)), [a], (257, 300))
+    else:
+        check(ctx, "fp32", T.sum_all, E.sum_all, [a], (1,))
+
+
+@pytest.mark.parametrize("C", [768, 100, 1500])
+def test_layernorm(ctx, C):
+    x = rnd(23, (3, 70, C), 2.0) + 0.5
+    g, b = 1 + rnd(24, (C,), 0.2), rnd(25, (C,), 0.2)
+    check(ctx, "fp32", lambda x, g, b: T.layernorm(x, g, b, 1e-5), lambda x, g, b: E.layernorm(x, g, b, 1e-5),
+          [x, g, b], x.shape)
+
+
+def test_embedding(ctx):
+    table = rnd(26, (50, 40))
+    ids = S.random_ids(27, (6, 35), 50)
+    check(ctx, "fp32", lambda t: T.embedding(t, ids, 6), lambda t: E.embedding(t, ids.reshape(-1), 6), [table],
+          (6, 35, 40))
+
+
+def test_embedding_routing_is_bit_exact(ctx):
+    """Forward rows are bitwise the table rows; with integer upstream gradients the
+    scatter-add sums are exact in fp32, so the table gradient must equal the
+    oracle's hit counts bit for bit (more ids than one sort chunk)."""
+    V, C, n = 97, 33, 9000
+    table = rnd(28, (V, C))
+    ids = S.random_ids(29, (n,), V)
+    up = S.rng_for(30).integers(-3, 4, size=(1, n, C)).astype(np.float32)
+    t = ctx.tensor(table.shape, table)
+    out = T.embedding(t, ids, 1)
+    assert np.array_equal(out.numpy().reshape(n, C), table[ids])
+    Rt = ctx.tensor(up.shape, up)
+    ctx.backward(T.sum_all(T.mul(out, Rt)))
+    expect = np.zeros((V, C), np.float64)
+    np.add.at(expect, ids, up.reshape(n, C))
+    assert np.array_equal(t.grad(), expect.astype(np.float32))
+    ctx.tape_reset()
+    t.release()
+    Rt.release()
+
+
+def test_narrow_split_merge(ctx):
+    x = rnd(31, (2, 37, 3 * 96))
+    check(ctx, "fp32", lambda a: T.narrow(a, 96, 96), lambda a: E.narrow(a, 96, 96), [x], (2, 37, 96))
+    y = rnd(32, (2, 37, 96))
+    check(ctx, "fp32", lambda a: T.split_heads(a, 3), lambda a: E.split_heads(a, 3), [y], (2, 3, 37, 32))
+    z = rnd(33, (2, 3, 37, 32))
+    check(ctx, "fp32", T.merge_heads, E.merge_heads, [z], (2, 37, 96))
+
+
+def test_causal_softmax(ctx):
+    s = rnd(34, (2, 3, 130, 130), 3.0)
+    check(ctx, "fp32", T.causal_softmax, E.causal_softmax, [s], s.shape)
+
+
+def _attention_oracle(qkv, heads):
+    B, Tn, C3 = qkv.shape
+    C = C3 // 3
+    hs = C // heads
+    q = E.split_heads(E.narrow(qkv, 0, C), heads)
+    k = E.split_heads(E.narrow(qkv, C, C), heads)
+    v = E.split_heads(E.narrow(qkv, 2 * C, C), heads)
+    r = lambda t: E.reshape(t, (B * heads, Tn, hs))
+    p = E.causal_softmax(E.scale(E.batch_matmul_t(r(q), r(k)), 1.0 / math.sqrt(hs)))
+    return E.merge_heads(E.reshape(E.batch_matmul(p, r(v)), (B, heads, Tn, hs)))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("B,Tn,H,hs", [(2, 200, 3, 32), (2, 130, 2, 64), (1, 1, 2, 64), (3, 64, 4, 32)])
+def test_causal_attention_equals_op_composition(ctx, prec, B, Tn, H, hs):
+    qkv = rnd(35, (B, Tn, 3 * H * hs))
+    check(ctx, prec, lambda a: T.causal_attention(a, H), lambda a: _attention_oracle(a, H), [qkv],
+          (B, Tn, H * hs))
+
+
+def test_attention_composed_from_ops_on_gpu(ctx):
+    """The separate GPU ops (Narrow/SplitHeads/BatchMatMulT/Scale/CausalSoftmax/
+    BatchMatMul/MergeHeads) give the same result as the oracle composition."""
+    B, Tn, H, hs = 2, 70, 2, 32
+    C = H * hs
+
+    def gpu(a):
+        q = T.split_heads(T.narrow(a, 0, C), H)
+        k = T.split_heads(T.narrow(a, C, C), H)
+        v = T.split_heads(T.narrow(a, 2 * C, C), H)
+        r = lambda t: T.reshape(t, (B * H, Tn, hs))
+        p = T.causal_softmax(T.scale(T.batch_matmul_t(r(q), r(k)), 1.0 / math.sqrt(hs)))
+        return T.merge_heads(T.reshape(T.batch_matmul(p, r(v)), (B, H, Tn, hs)))
+    check(ctx, "fp32", gpu, lambda a: _attention_oracle(a, H), [rnd(36, (B, Tn, 3 * C))], (B, Tn, C))
+
+
+@pytest.mark.parametrize("rows,V", [(300, 1000), (37, 50257)])
+def test_softmax_cross_entropy(ctx, rows, V):
+    logits = rnd(37, (rows, V), 3.0)
+    tg = S.random_ids(38, (rows,), V)
+    ctx.set_precision("fp32")
+    lt = ctx.tensor(logits.shape, logits)
+    loss = T.softmax_cross_entropy(lt, tg)
+    ctx.backward(loss)
+    ref = E.Tensor(logits.astype(np.float64))
+    rl = E.softmax_cross_entropy(ref, tg)
+    rl.backward()
+    assert abs(loss.item() - rl.item()) / max(abs(rl.item()), 1) <= 1e-5
+    assert_close(lt.grad(), ref.grad, 1e-4, "dlogits")
+    ctx.tape_reset()
+    lt.release()
+
+
+def test_ce_uniform_logits_is_log_v(ctx):
+    V = 50257
+    lt = ctx.tensor((4, V), np.zeros((4, V), np.float32))
+    loss = T.softmax_cross_entropy(lt, np.array([0, 1, V - 1, 7]))
+    assert abs(loss.item() - math.log(V)) < 1e-5
+    ctx.tape_reset()
+    lt.release()
+
+
+# ----------------------------------------------------------------------------- tape semantics
+def test_tensor_used_twice_accumulates(ctx):
+    """[Autograd-1, "Why += and not ="]: L = z*z at z = 7 gives dL/dz = 14."""
+    z = ctx.tensor((1,), [7.0])
+    ctx.backward(T.mul(z, z))
+    assert z.grad()[0] == 14.0
+    ctx.tape_reset()
+    z.release()
+
+
+def test_tiny_graph_values(ctx):
+    w, x, b = (ctx.tensor((1,), [v]) for v in (2.0, 3.0, 1.0))
+    z = T.add(T.mul(w, x), b)
+    L = T.mul(z, z)
+    ctx.backward(L)
+    assert (z.item(), L.item()) == (7.0, 49.0)
+    assert (z.grad()[0], w.grad()[0], x.grad()[0], b.grad()[0]) == (14.0, 42.0, 28.0, 14.0)
+    ctx.tape_reset()
+    for t in (w, x, b):
+        t.release()
+
+
+def test_leaf_grads_accumulate_until_zero_grad(ctx):
+    w = ctx.tensor((4,), [1, 2, 3, 4])
+    x = ctx.tensor((4,), [5, 6, 7, 8])
+    for k in (1, 2):
+        ctx.backward(T.sum_all(T.mul(w, x)))
+        assert np.array_equal(w.grad(), k * np.array([5, 6, 7, 8], np.float32))
+    ctx.zero_grad([w])
+    assert np.array_equal(w.grad(), np.zeros(4, np.float32))
+    ctx.backward(T.sum_all(T.mul(w, x)))
+    assert np.array_equal(w.grad(), np.array([5, 6, 7, 8], np.float32))
+    ctx.tape_reset()
+    w.release()
+    x.release()
+
+
+def test_errors_are_reported_and_context_survives(ctx):
+    a = ctx.tensor((3, 4))
+    b = ctx.tensor((5, 6))
+    with pytest.raises(T.TfbError) as e:
+        T.matmul(a, b)
+    assert e.value.code == -2
+    with pytest.raises(T.TfbError):
+        T.mul(a, b)
+    y = T.tanh(a)
+    with pytest.raises(T.TfbError) as e:
+        ctx.backward(y)
+    assert e.value.code == -3 and "scalar" in str(e.value)
+    with pytest.raises(T.TfbError):
+        T.softmax_cross_entropy(a, np.zeros(2, np.int32))
+    # still usable
+    ctx.backward(T.sum_all(T.tanh(a)))
+    assert np.allclose(a.grad(), 1.0)
+    ctx.tape_reset()
+    a.release()
+    b.release()
+
+
+def test_no_grad_records_nothing(ctx):
+    a = ctx.tensor((2, 3), rnd(40, (2, 3)))
+    ctx.set_grad_enabled(False)
+    y = T.sum_all(T.tanh(a))
+    ctx.set_grad_enabled(True)
+    ctx.backward(y)            # nothing recorded: only the seed is written
+    with pytest.raises(T.TfbError):
+        a.grad()
+    ctx.tape_reset()
+    a.release()
+
+
+# ----------------------------------------------------------------------------- optimizers
+def test_adamw_matches_oracle_over_steps(ctx):
+    from oracle import optim as OPT
+    shapes = [(37, 65), (65,), (3, 5, 7)]
+    params = [rnd(50 + i, s) for i, s in enumerate(shapes)]
+    gp = [ctx.tensor(s, p, param=True) for s, p in zip(shapes, params)]
+    op = [E.Tensor(p.astype(np.float64)) for p in params]
+    gopt = T.AdamW(gp, lr=1e-2, weight_decay=0.1)
+    oopt = OPT.AdamW(op, lr=1e-2, weight_decay=0.1)
+    for step in range(4):
+        grads = [rnd(60 + 10 * step + i, s) for i, s in enumerate(shapes)]
+        gopt.zero_grad()
+        for t, g in zip(gp, grads):
+            Gt = ctx.tensor(g.shape, g)
+            ctx.backward(T.sum_all(T.mul(t, Gt)))     # leaves exactly g in t.grad
+            ctx.tape_reset()
+            Gt.release()
+        gopt.step()
+        for t, g in zip(op, grads):
+            t.grad = g.astype(np.float64)
+        oopt.step()
+        for t, o in zip(gp, op):
+            assert_close(t.numpy(), o.data, 1e-6, f"step {step}")
+    gopt.close()
+    for t in gp:
+        t.release()
+
+
+def test_sgd(ctx):
+    w = ctx.tensor((3,), [1.0, 2.0, 3.0])
+    g = ctx.tensor((3,), [0.5, -1.0, 2.0])
+    ctx.backward(T.sum_all(T.mul(w, g)))
+    T.sgd_step([w], 0.1)
+    assert np.allclose(w.numpy(), [0.95, 2.1, 2.8])
+    ctx.tape_reset()
+    w.release()
+    g.release()

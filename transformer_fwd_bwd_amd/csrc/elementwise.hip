@@ -1,0 +1,324 @@
+// Bandwidth-bound elementwise and data-movement kernels: Add (with the bias
+// broadcast), Mul, Scale, Tanh, GELU (tanh form), Sum, Narrow and the head
+// permutations, with their backward rules ([Autograd-1, "Ops" and the table of
+// remaining ops; GPT2-4, "Common mistakes": GELU is the tanh approximation]).
+// Backward kernels take beta in {0, 1}: 0 overwrites a gradient that has not
+// been written yet in this pass, 1 adds to it (the "+=" rule).  Grid-stride
+// loops over float4 when the buffers allow it; reductions are two-stage and
+// deterministic.
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace tfb {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int NT = 256;
+
+inline unsigned grid_for(int64_t n, int per_thread = 1) {
+  int64_t b = (n + (int64_t)NT * per_thread - 1) / ((int64_t)NT * per_thread);
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 65536));
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+template <typename F>
+__global__ void map1(int64_t n, F f) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) f(i);
+}
+
+__global__ void fill_k(float* p, float v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) p[i] = v;
+}
+
+__global__ void add_bcast_k(const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ y,
+                            int64_t n, int64_t nb) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT)
+    y[i] = a[i] + b[i % nb];
+}
+
+__global__ void add_bcast4_k(const f4* __restrict__ a, const f4* __restrict__ b, f4* __restrict__ y, int64_t n4,
+                             int64_t nb4) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n4; i += (int64_t)gridDim.x * NT)
+    y[i] = a[i] + b[i % nb4];
+}
+
+__global__ void axpby_k(float* __restrict__ d, const float* __restrict__ s, float alpha, float beta, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    float v = alpha * s[i];
+    if (beta != 0.f) v += beta * d[i];
+    d[i] = v;
+  }
+}
+
+__device__ __forceinline__ float gelu_f(float x) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  const float u = c * (x + 0.044715f * x * x * x);
+  return 0.5f * x * (1.f + tanhf(u));
+}
+
+__device__ __forceinline__ float gelu_grad(float x) {
+  const float c = 0.7978845608028654f;
+  const float u = c * (x + 0.044715f * x * x * x);
+  const float t = tanhf(u);
+  return 0.5f * (1.f + t) + 0.5f * x * (1.f - t * t) * c * (1.f + 3.f * 0.044715f * x * x);
+}
+
+// out of one block: partial[blockIdx.y * cols + c] = sum of rows in the block's row range
+__global__ void colsum_stage1(const float* __restrict__ g, int64_t rows, int64_t cols, int64_t rows_per,
+                              float* __restrict__ partial) {
+  const int64_t c = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (c >= cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per;
+  const int64_t r1 = std::min(rows, r0 + rows_per);
+  float s = 0.f;
+  for (int64_t r = r0; r < r1; ++r) s += g[r * cols + c];
+  partial[(int64_t)blockIdx.y * cols + c] = s;
+}
+
+__global__ void colsum_stage2(const float* __restrict__ partial, int nparts, int64_t cols, float* __restrict__ out,
+                              float beta) {
+  const int64_t c = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (c >= cols) return;
+  float s = 0.f;
+  for (int p = 0; p < nparts; ++p) s += partial[(int64_t)p * cols + c];
+  if (beta != 0.f) s += beta * out[c];
+  out[c] = s;
+}
+
+__device__ __forceinline__ float block_sum(float v) {
+  __shared__ float sh[NT / 64];
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_down(v, o, 64);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  float r = 0.f;
+  if (threadIdx.x == 0)
+    for (int i = 0; i < NT / 64; ++i) r += sh[i];
+  __syncthreads();
+  return r;
+}
+
+__global__ void sum_stage1(const float* __restrict__ a, int64_t n, float* __restrict__ partial) {
+  float s = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) s += a[i];
+  s = block_sum(s);
+  if (threadIdx.x == 0) partial[blockIdx.x] = s;
+}
+
+__global__ void sum_stage2(const float* __restrict__ partial, int np, float* __restrict__ out) {
+  float s = 0.f;
+  for (int i = threadIdx.x; i < np; i += NT) s += partial[i];
+  s = block_sum(s);
+  if (threadIdx.x == 0) out[0] = s;
+}
+
+constexpr int SUM_BLOCKS = 1024;
+
+}  // namespace
+
+hipError_t fill(float* p, float v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t add_bcast(const float* a, const float* b, float* y, int64_t n, int64_t nb, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (nb % 4 == 0 && aligned16(a) && aligned16(b) && aligned16(y))
+    hipLaunchKernelGGL(add_bcast4_k, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, (const f4*)a, (const f4*)b, (f4*)y,
+                       n / 4, nb / 4);
+  else
+    hipLaunchKernelGGL(add_bcast_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, a, b, y, n, nb);
+  return hipGetLastError();
+}
+
+hipError_t axpby(float* dst, const float* src, float alpha, float beta, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(axpby_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, dst, src, alpha, beta, n);
+  return hipGetLastError();
+}
+
+hipError_t mul_fwd(const float* a, const float* b, float* y, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  auto f = [=] __device__(int64_t i) { y[i] = a[i] * b[i]; };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  return hipGetLastError();
+}
+
+hipError_t mul_bwd(const float* g, const float* other, float* d, float beta, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  auto f = [=] __device__(int64_t i) {
+    float v = g[i] * other[i];
+    if (beta != 0.f) v += d[i];
+    d[i] = v;
+  };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  return hipGetLastError();
+}
+
+hipError_t scale_fwd(const float* a, float sc, float* y, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  auto f = [=] __device__(int64_t i) { y[i] = sc * a[i]; };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  return hipGetLastError();
+}
+
+hipError_t tanh_fwd(const float* a, float* y, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  auto f = [=] __device__(int64_t i) { y[i] = tanhf(a[i]); };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  return hipGetLastError();
+}
+
+hipError_t tanh_bwd(const float* g, const float* y, float* d, float beta, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  auto f = [=] __device__(int64_t i) {
+    const float t = y[i];
+    float v = g[i] * (1.f - t * t);
+    if (beta != 0.f) v += d[i];
+    d[i] = v;
+  };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  return hipGetLastError();
+}
+
+hipError_t gelu_fwd(const float* a, float* y, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4 == 0 && aligned16(a) && aligned16(y)) {
+    const f4* a4 = (const f4*)a;
+    f4* y4 = (f4*)y;
+    auto f = [=] __device__(int64_t i) {
+      f4 v = a4[i];
+      y4[i] = f4{gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3])};
+    };
+    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
+  } else {
+    auto f = [=] __device__(int64_t i) { y[i] = gelu_f(a[i]); };
+    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  }
+  return hipGetLastError();
+}
+
+hipError_t gelu_bwd(const float* g, const float* x, float* d, float beta, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4 == 0 && aligned16(g) && aligned16(x) && aligned16(d)) {
+    const f4* g4 = (const f4*)g;
+    const f4* x4 = (const f4*)x;
+    f4* d4 = (f4*)d;
+    auto f = [=] __device__(int64_t i) {
+      f4 gv = g4[i], xv = x4[i];
+      f4 v = {gv[0] * gelu_grad(xv[0]), gv[1] * gelu_grad(xv[1]), gv[2] * gelu_grad(xv[2]),
+              gv[3] * gelu_grad(xv[3])};
+      if (beta != 0.f) v += d4[i];
+      d4[i] = v;
+    };
+    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
+  } else {
+    auto f = [=] __device__(int64_t i) {
+      float v = g[i] * gelu_grad(x[i]);
+      if (beta != 0.f) v += d[i];
+      d[i] = v;
+    };
+    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  }
+  return hipGetLastError();
+}
+
+size_t colsum_workspace_bytes(int64_t rows, int64_t cols) {
+  const int64_t parts = std::min<int64_t>(64, std::max<int64_t>(1, rows / 64));
+  return (size_t)parts * cols * sizeof(float);
+}
+
+hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s) {
+  if (cols <= 0) return hipSuccess;
+  const int64_t parts = std::min<int64_t>(64, std::max<int64_t>(1, rows / 64));
+  const int64_t rows_per = (rows + parts - 1) / parts;
+  float* partial = static_cast<float*>(ws);
+  dim3 g1((unsigned)((cols + NT - 1) / NT), (unsigned)parts);
+  hipLaunchKernelGGL(colsum_stage1, g1, dim3(NT), 0, s, g, rows, cols, rows_per, partial);
+  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + NT - 1) / NT)), dim3(NT), 0, s, partial, (int)parts,
+                     cols, out, beta);
+  return hipGetLastError();
+}
+
+size_t sum_workspace_bytes(int64_t) { return SUM_BLOCKS * sizeof(float); }
+
+hipError_t sum_all(const float* a, int64_t n, float* out, void* ws, hipStream_t s) {
+  float* partial = static_cast<float*>(ws);
+  hipLaunchKernelGGL(sum_stage1, dim3(SUM_BLOCKS), dim3(NT), 0, s, a, n, partial);
+  hipLaunchKernelGGL(sum_stage2, dim3(1), dim3(NT), 0, s, partial, SUM_BLOCKS, out);
+  return hipGetLastError();
+}
+
+hipError_t bcast_scalar_bwd(const float* gs, float* d, float beta, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  auto f = [=] __device__(int64_t i) {
+    float v = gs[0];
+    if (beta != 0.f) v += d[i];
+    d[i] = v;
+  };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  return hipGetLastError();
+}
+
+hipError_t narrow_fwd(const float* x, float* y, int64_t rows, int64_t cols, int64_t start, int64_t len,
+                      hipStream_t s) {
+  const int64_t n = rows * len;
+  if (n <= 0) return hipSuccess;
+  auto f = [=] __device__(int64_t i) {
+    const int64_t r = i / len, c = i % len;
+    y[i] = x[r * cols + start + c];
+  };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  return hipGetLastError();
+}
+
+hipError_t narrow_bwd(const float* g, float* d, int64_t rows, int64_t cols, int64_t start, int64_t len, float beta,
+                      hipStream_t s) {
+  const int64_t n = rows * cols;
+  if (n <= 0) return hipSuccess;
+  auto f = [=] __device__(int64_t i) {
+    const int64_t r = i / cols, c = i % cols;
+    const bool in = c >= start && c < start + len;
+    if (beta != 0.f) {
+      if (in) d[i] += g[r * len + c - start];
+    } else {
+      d[i] = in ? g[r * len + c - start] : 0.f;
+    }
+  };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  return hipGetLastError();
+}
+
+hipError_t permute_heads(const float* x, float* y, int64_t B, int64_t T, int64_t H, int64_t hs, bool to_heads,
+                         float beta, hipStream_t s) {
+  const int64_t n = B * T * H * hs;
+  if (n <= 0) return hipSuccess;
+  // i indexes the destination
+  auto f = [=] __device__(int64_t i) {
+    const int64_t d = i % hs;
+    int64_t rest = i / hs;
+    int64_t src;
+    if (to_heads) {  // dst [B, H, T, hs] <- src [B, T, H, hs]
+      const int64_t t = rest % T;
+      rest /= T;
+      const int64_t h = rest % H, b = rest / H;
+      src = ((b * T + t) * H + h) * hs + d;
+    } else {  // dst [B, T, H, hs] <- src [B, H, T, hs]
+      const int64_t h = rest % H;
+      rest /= H;
+      const int64_t t = rest % T, b = rest / T;
+      src = ((b * H + h) * T + t) * hs + d;
+    }
+    float v = x[src];
+    if (beta != 0.f) v += y[i];
+    y[i] = v;
+  };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  return hipGetLastError();
+}
+
+}  // namespace tfb

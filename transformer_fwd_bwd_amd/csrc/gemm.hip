@@ -1,0 +1,391 @@
+// MFMA contraction kernels for gfx950: the MatMul family and the attention
+// products ([Autograd-1, "Ops": MatMul with dx = g w^T and dw = x^T g; the
+// table of ops: MatMulT, BatchMatMul, BatchMatMulT]).
+//
+// One kernel template covers every layout the autograd rules need:
+//   NN  A(m,k) k-contiguous, B(k,n) n-contiguous   (forward x @ w, dx of MatMulT)
+//   NT  A k-contiguous,      B(k,n) k-contiguous   (x @ w^T, dx = g @ w^T, q k^T)
+//   TN  A(m,k) m-contiguous, B n-contiguous        (dw = x^T @ g, P^T @ dO)
+// A workgroup of WM x WN waves computes a (WM*TM*32) x (WN*TN*32) tile of C;
+// each wave owns TM x TN blocks of 32x32 accumulated by v_mfma_f32_32x32x16_bf16
+// (bf16 operands) or v_mfma_f32_32x32x2_f32 (fp32 operands), fp32 accumulation.
+// Both operands are staged through LDS as [row][k] with k contiguous, so every
+// lane reads its MFMA fragment as one 16-byte LDS load; an m- or n-contiguous
+// operand is transposed in 4x4 register micro-blocks on the way in.  The next
+// k-tile is fetched into registers while the current one is multiplied (two
+// LDS buffers, one barrier per k-tile).  Out-of-range rows and k are staged as
+// zeros; fp32 inputs are rounded to bf16 (nearest even) while staging when the
+// bf16 variant runs.
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace tfb {
+namespace {
+
+typedef __bf16 bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int BK = 32;
+
+template <bool BF16>
+struct Lds;
+template <>
+struct Lds<true> {
+  using T = bf16_t;
+  static constexpr int LDK = BK + 8;  // 80-byte rows
+};
+template <>
+struct Lds<false> {
+  using T = float;
+  static constexpr int LDK = BK + 4;  // 144-byte rows
+};
+
+__device__ __forceinline__ f4 load4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+
+__device__ __forceinline__ float mask_causal(float v, int causal, int m, int k) {
+  if (causal == CAUSAL_UPTO && k > m) return 0.f;
+  if (causal == CAUSAL_FROM && k < m) return 0.f;
+  return v;
+}
+
+// Registers holding one thread's share of an R_TILE x BK operand tile.
+template <int R_TILE, int NT, bool RCONTIG>
+struct Stage {
+  // k-contiguous: chunks of 4 consecutive k of one row
+  // r-contiguous: 4x4 micro-blocks (4 rows x 4 k), held as 4 r-vectors
+  static constexpr int UNITS = RCONTIG ? R_TILE * BK / 16 : R_TILE * BK / 4;
+  static constexpr int PER = (UNITS + NT - 1) / NT;
+  static constexpr int REGS = RCONTIG ? PER * 4 : PER;
+  f4 r[REGS];
+
+  __device__ __forceinline__ void load(const float* __restrict__ P, int64_t ld, int r0, int k0, int R, int K,
+                                       bool vec, int causal, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = tid + i * NT;
+      if (UNITS % NT != 0 && u >= UNITS) break;
+      if constexpr (!RCONTIG) {
+        const int rr = u / (BK / 4), kq = u % (BK / 4);
+        const int gr = r0 + rr, gk = k0 + kq * 4;
+        f4 v = {0.f, 0.f, 0.f, 0.f};
+        if (gr < R) {
+          const float* src = P + (int64_t)gr * ld + gk;
+          if (vec && gk + 3 < K) {
+            v = load4(src);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (gk + e < K) ? src[e] : 0.f;
+          }
+          if (causal != CAUSAL_NONE) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = mask_causal(v[e], causal, gr, gk + e);
+          }
+        }
+        r[i] = v;
+      } else {
+        const int rq = u % (R_TILE / 4), kq = u / (R_TILE / 4);
+        const int gr = r0 + rq * 4;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int gk = k0 + kq * 4 + kk;
+          f4 v = {0.f, 0.f, 0.f, 0.f};
+          if (gk < K) {
+            const float* src = P + (int64_t)gk * ld + gr;
+            if (vec && gr + 3 < R) {
+              v = load4(src);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = (gr + e < R) ? src[e] : 0.f;
+            }
+            if (causal != CAUSAL_NONE) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = mask_causal(v[e], causal, gr + e, gk);
+            }
+          }
+          r[i * 4 + kk] = v;
+        }
+      }
+    }
+  }
+
+  template <bool BF16>
+  __device__ __forceinline__ void store(typename Lds<BF16>::T* L, int tid) const {
+    constexpr int LDK = Lds<BF16>::LDK;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = tid + i * NT;
+      if (UNITS % NT != 0 && u >= UNITS) break;
+      if constexpr (!RCONTIG) {
+        const int rr = u / (BK / 4), kq = u % (BK / 4);
+        put<BF16>(L + rr * LDK + kq * 4, r[i]);
+      } else {
+        const int rq = u % (R_TILE / 4), kq = u / (R_TILE / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f4 v = {r[i * 4 + 0][e], r[i * 4 + 1][e], r[i * 4 + 2][e], r[i * 4 + 3][e]};
+          put<BF16>(L + (rq * 4 + e) * LDK + kq * 4, v);
+        }
+      }
+    }
+  }
+
+  template <bool BF16>
+  __device__ __forceinline__ static void put(typename Lds<BF16>::T* dst, f4 v) {
+    if constexpr (BF16) {
+      bf16x4 b = {(bf16_t)v[0], (bf16_t)v[1], (bf16_t)v[2], (bf16_t)v[3]};
+      *reinterpret_cast<bf16x4*>(dst) = b;
+    } else {
+      *reinterpret_cast<f4*>(dst) = v;
+    }
+  }
+};
+
+struct KArgs {
+  GemmArgs g;
+  int tiles_n;
+  int splits;
+  int k_per_split;  // multiple of BK
+  float* ws;        // split-K partials [batch*splits][M][N]
+};
+
+template <int WM, int WN, int TM, int TN, bool BF16, bool A_RC, bool B_KC>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int LDK = Lds<BF16>::LDK;
+  using LT = typename Lds<BF16>::T;
+  __shared__ __attribute__((aligned(16))) LT As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) LT Bs[2][BN * LDK];
+
+  const GemmArgs& g = ka.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int tn = blockIdx.x, tm = blockIdx.y;
+  const int zz = blockIdx.z;
+  const int z = zz / ka.splits, split = zz % ka.splits;
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (g.causal_out && n0 > m0 + BM - 1) return;
+
+  const int z1 = z / g.batch_div, z2 = z % g.batch_div;
+  const float* A = g.A + z1 * g.sa1 + z2 * g.sa2;
+  const float* B = g.B + z1 * g.sb1 + z2 * g.sb2;
+
+  int kb = split * ka.k_per_split;
+  int ke = min(g.K, kb + ka.k_per_split);
+  if (g.causal_a == CAUSAL_UPTO) ke = min(ke, m0 + BM);
+  if (g.causal_a == CAUSAL_FROM) kb = max(kb, (m0 / BK) * BK);
+
+  // 16-byte vector loads need 16-byte aligned rows and batch offsets
+  const bool vecA = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && (g.lda % 4 == 0);
+  const bool vecB = ((reinterpret_cast<uintptr_t>(B) & 15) == 0) && (g.ldb % 4 == 0);
+
+  Stage<BM, NT, A_RC> sa;
+  Stage<BN, NT, B_KC ? false : true> sb;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  int buf = 0;
+  if (kb < ke) {
+    sa.load(A, g.lda, m0, kb, g.M, ke, vecA, g.causal_a, tid);
+    sb.load(B, g.ldb, n0, kb, g.N, ke, vecB, CAUSAL_NONE, tid);
+    sa.template store<BF16>(As[0], tid);
+    sb.template store<BF16>(Bs[0], tid);
+  }
+  __syncthreads();
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    const bool more = k0 + BK < ke;
+    if (more) {
+      sa.load(A, g.lda, m0, k0 + BK, g.M, ke, vecA, g.causal_a, tid);
+      sb.load(B, g.ldb, n0, k0 + BK, g.N, ke, vecB, CAUSAL_NONE, tid);
+    }
+    const LT* Ab = As[buf] + (wm * TM * 32 + lrow) * LDK;
+    const LT* Bb = Bs[buf] + (wn * TN * 32 + lrow) * LDK;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int ks = 0; ks < BK; ks += 16) {
+        bf16x8 af[TM], bf[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(Ab + i * 32 * LDK + ks + lhalf * 8);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(Bb + j * 32 * LDK + ks + lhalf * 8);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kg = 0; kg < BK; kg += 8) {
+        f4 af[TM], bf[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const f4*>(Ab + i * 32 * LDK + kg + lhalf * 4);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const f4*>(Bb + j * 32 * LDK + kg + lhalf * 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][c], bf[j][c], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (more) {
+      sa.template store<BF16>(As[buf ^ 1], tid);
+      sb.template store<BF16>(Bs[buf ^ 1], tid);
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // epilogue: register r of a 32x32 block holds C[8*(r/4) + 4*(lane/32) + r%4][lane%32]
+  const bool to_ws = ka.splits > 1;
+  float* C;
+  int64_t ldc;
+  if (to_ws) {
+    C = ka.ws + (int64_t)zz * g.M * g.N;
+    ldc = g.N;
+  } else {
+    C = g.C + z1 * g.sc1 + z2 * g.sc2;
+    ldc = g.ldc;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * TN * 32 + j * 32 + lrow;
+      if (n >= g.N) continue;
+      const float bias = (!to_ws && g.bias) ? g.bias[n] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * TM * 32 + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+        if (m >= g.M) continue;
+        float* dst = C + (int64_t)m * ldc + n;
+        float v = g.alpha * acc[i][j][r];
+        if (to_ws) {
+          *dst = v;
+        } else {
+          v += bias;
+          if (g.beta != 0.f) v += g.beta * *dst;
+          *dst = v;
+        }
+      }
+    }
+  }
+}
+
+// C = sum over splits of the partials + beta*C + bias
+__global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, int N, float* C, int64_t ldc,
+                              int batch_div, int64_t sc1, int64_t sc2, float beta, const float* bias) {
+  const int z = blockIdx.y;
+  const int64_t MN = (int64_t)M * N;
+  const int z1 = z / batch_div, z2 = z % batch_div;
+  float* Cz = C + z1 * sc1 + z2 * sc2;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < MN; e += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(e / N), n = (int)(e % N);
+    float s = 0.f;
+    for (int p = 0; p < splits; ++p) s += ws[((int64_t)z * splits + p) * MN + e];
+    if (bias) s += bias[n];
+    float* dst = Cz + (int64_t)m * ldc + n;
+    if (beta != 0.f) s += beta * *dst;
+    *dst = s;
+  }
+}
+
+struct Plan {
+  int cfg;  // 0: 128x128 (2x2 waves, 2x2 blocks), 1: 128x64 (4x1 waves, 1x2 blocks)
+  int BM, BN;
+  int splits;
+  int k_per_split;
+};
+
+Plan make_plan(const GemmArgs& g) {
+  Plan p;
+  if (g.N <= 64) {
+    p.cfg = 1;
+    p.BM = 128;
+    p.BN = 64;
+  } else {
+    p.cfg = 0;
+    p.BM = 128;
+    p.BN = 128;
+  }
+  const int64_t tiles = (int64_t)((g.M + p.BM - 1) / p.BM) * ((g.N + p.BN - 1) / p.BN) * g.batch;
+  p.splits = 1;
+  if (g.causal_a == CAUSAL_NONE && !g.causal_out) {
+    // fill the 256 compute units at least twice when K is long
+    while (tiles * p.splits < 512 && g.K / (p.splits * 2) >= 1024 && p.splits < 16) p.splits *= 2;
+  }
+  const int kps = (g.K + p.splits - 1) / p.splits;
+  p.k_per_split = ((kps + BK - 1) / BK) * BK;
+  p.splits = (g.K + p.k_per_split - 1) / p.k_per_split;
+  if (p.splits < 1) p.splits = 1;
+  return p;
+}
+
+template <int WM, int WN, int TM, int TN, bool BF16>
+hipError_t launch_layout(const KArgs& ka, dim3 grid, hipStream_t s) {
+  const GemmArgs& g = ka.g;
+  dim3 block(WM * WN * 64);
+  if (!g.a_mcontig && !g.b_kcontig)
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BF16, false, false>), grid, block, 0, s, ka);
+  else if (!g.a_mcontig && g.b_kcontig)
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BF16, false, true>), grid, block, 0, s, ka);
+  else if (g.a_mcontig && !g.b_kcontig)
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BF16, true, false>), grid, block, 0, s, ka);
+  else
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BF16, true, true>), grid, block, 0, s, ka);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(const GemmArgs& g) {
+  Plan p = make_plan(g);
+  if (p.splits <= 1) return 0;
+  return (size_t)p.splits * g.batch * g.M * g.N * sizeof(float);
+}
+
+hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  // K == 0 needs no special case: the k loop is empty and the epilogue writes beta*C + bias
+  Plan p = make_plan(g);
+  if (p.splits > 1 && (size_t)p.splits * g.batch * g.M * g.N * sizeof(float) > ws_bytes) p.splits = 1;
+  if (p.splits == 1) p.k_per_split = ((std::max(g.K, 1) + BK - 1) / BK) * BK;
+  KArgs ka;
+  ka.g = g;
+  ka.splits = p.splits;
+  ka.k_per_split = p.k_per_split;
+  ka.ws = static_cast<float*>(workspace);
+  ka.tiles_n = (g.N + p.BN - 1) / p.BN;
+  dim3 grid(ka.tiles_n, (g.M + p.BM - 1) / p.BM, g.batch * p.splits);
+  hipError_t e;
+  const bool bf = g.prec == PREC_BF16;
+  if (p.cfg == 0)
+    e = bf ? launch_layout<2, 2, 2, 2, true>(ka, grid, s) : launch_layout<2, 2, 2, 2, false>(ka, grid, s);
+  else
+    e = bf ? launch_layout<4, 1, 1, 2, true>(ka, grid, s) : launch_layout<4, 1, 1, 2, false>(ka, grid, s);
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int64_t MN = (int64_t)g.M * g.N;
+  dim3 rgrid((unsigned)std::min<int64_t>((MN + 255) / 256, 4096), g.batch);
+  hipLaunchKernelGGL(splitk_reduce, rgrid, dim3(256), 0, s, ka.ws, p.splits, g.M, g.N, g.C, g.ldc, g.batch_div,
+                     g.sc1, g.sc2, g.beta, g.bias);
+  return hipGetLastError();
+}
+
+}  // namespace tfb

@@ -1,0 +1,121 @@
+// Internal interface between the host runtime (tfb_runtime.cpp) and the HIP
+// kernels.  Every launcher enqueues on the given stream and returns the launch
+// status; shape checks are the runtime's job.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace tfb {
+
+enum Prec { PREC_F32 = 0, PREC_BF16 = 1 };
+
+// Causal masks applied to the A operand while it is staged:
+//   CAUSAL_UPTO: A(m, k) = 0 for k > m  (P @ V, dS @ K: a query row sees keys <= itself)
+//   CAUSAL_FROM: A(m, k) = 0 for k < m  (P^T @ dO, dS^T @ Q: a key column gets queries >= itself)
+enum CausalA { CAUSAL_NONE = 0, CAUSAL_UPTO = 1, CAUSAL_FROM = 2 };
+
+// C = alpha * op(A) op(B) + beta * C (+ bias[n]), batched.
+//   A(m, k) = a_mcontig ? A[k*lda + m] : A[m*lda + k]
+//   B(k, n) = b_kcontig ? B[n*ldb + k] : B[k*ldb + n]
+//   C(m, n) = C[m*ldc + n]
+// Batch entry z (0 <= z < batch) uses z1 = z / batch_div, z2 = z % batch_div and
+// offsets A + z1*sa1 + z2*sa2 (likewise B, C): a [B, H] head split folds into
+// the addressing.  causal_out skips output tiles entirely above the diagonal.
+struct GemmArgs {
+  int M = 0, N = 0, K = 0;
+  const float* A = nullptr;
+  int64_t lda = 0;
+  bool a_mcontig = false;
+  const float* B = nullptr;
+  int64_t ldb = 0;
+  bool b_kcontig = false;
+  float* C = nullptr;
+  int64_t ldc = 0;
+  float alpha = 1.f, beta = 0.f;
+  const float* bias = nullptr;
+  int batch = 1, batch_div = 1;
+  int64_t sa1 = 0, sa2 = 0, sb1 = 0, sb2 = 0, sc1 = 0, sc2 = 0;
+  int causal_a = CAUSAL_NONE;
+  bool causal_out = false;
+  int prec = PREC_F32;
+};
+
+size_t gemm_workspace_bytes(const GemmArgs& g);
+hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t s);
+
+// ---- elementwise (elementwise.hip); beta in {0, 1}: overwrite or accumulate
+hipError_t fill(float* p, float v, int64_t n, hipStream_t s);
+hipError_t add_bcast(const float* a, const float* b, float* y, int64_t n, int64_t nb, hipStream_t s);
+hipError_t axpby(float* dst, const float* src, float alpha, float beta, int64_t n, hipStream_t s);
+hipError_t mul_fwd(const float* a, const float* b, float* y, int64_t n, hipStream_t s);
+hipError_t mul_bwd(const float* g, const float* other, float* d, float beta, int64_t n, hipStream_t s);
+hipError_t scale_fwd(const float* a, float sc, float* y, int64_t n, hipStream_t s);
+hipError_t tanh_fwd(const float* a, float* y, int64_t n, hipStream_t s);
+hipError_t tanh_bwd(const float* g, const float* y, float* d, float beta, int64_t n, hipStream_t s);
+hipError_t gelu_fwd(const float* a, float* y, int64_t n, hipStream_t s);
+hipError_t gelu_bwd(const float* g, const float* x, float* d, float beta, int64_t n, hipStream_t s);
+// out[c] = beta*out[c] + sum_r g[r*cols + c]; deterministic two-stage reduction
+size_t colsum_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s);
+// out[0] = sum of a (deterministic); sum_bwd: d = beta*d + g[0]
+size_t sum_workspace_bytes(int64_t n);
+hipError_t sum_all(const float* a, int64_t n, float* out, void* ws, hipStream_t s);
+hipError_t bcast_scalar_bwd(const float* g_scalar, float* d, float beta, int64_t n, hipStream_t s);
+// last-dim slice copy and its inverse (the inverse writes zeros outside the slice when beta == 0)
+hipError_t narrow_fwd(const float* x, float* y, int64_t rows, int64_t cols, int64_t start, int64_t len,
+                      hipStream_t s);
+hipError_t narrow_bwd(const float* g, float* d, int64_t rows, int64_t cols, int64_t start, int64_t len,
+                      float beta, hipStream_t s);
+// [B, T, H, hs] <-> [B, H, T, hs]; to_heads selects the direction
+hipError_t permute_heads(const float* x, float* y, int64_t B, int64_t T, int64_t H, int64_t hs, bool to_heads,
+                         float beta, hipStream_t s);
+
+// ---- row reductions (rowops.hip)
+hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, float* y, float* mean,
+                         float* rstd, int64_t rows, int64_t C, float eps, hipStream_t s);
+size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C);
+hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
+                         float* dx, float* dgamma, float* dbeta, int64_t rows, int64_t C, float beta_dx,
+                         float beta_dg, float beta_db, void* ws, hipStream_t s);
+// full == true: every element of the [rows, T] view is written (zeros where masked);
+// full == false: only the visible prefix of each row is touched.
+hipError_t causal_softmax_fwd(const float* x, float* p, int64_t rows, int64_t T, bool full, hipStream_t s);
+hipError_t causal_softmax_bwd(const float* g, const float* p, float* d, int64_t rows, int64_t T, float scale,
+                              float beta, bool full, hipStream_t s);
+size_t softmax_ce_workspace_bytes(int64_t rows);
+hipError_t softmax_ce_fwd(const float* logits, const int32_t* targets, int64_t rows, int64_t V, float* lse,
+                          float* loss, void* ws, hipStream_t s);
+hipError_t softmax_ce_bwd(const float* logits, const int32_t* targets, const float* lse, const float* g_scalar,
+                          float* dl, int64_t rows, int64_t V, float beta, hipStream_t s);
+
+// ---- embedding (embedding.hip)
+// ids outside [0, rows) give zero rows forward and are skipped backward
+hipError_t embedding_fwd(const float* table, int64_t rows, const int32_t* ids, float* y, int64_t n, int64_t C,
+                         hipStream_t s);
+size_t embedding_bwd_workspace_bytes(int64_t n);
+// dtable[ids[r]] += g[r] for every r; sums per table row in ascending r order
+hipError_t embedding_bwd(const float* g, const int32_t* ids, int64_t n, int64_t C, float* dtable, int64_t rows,
+                         void* ws, hipStream_t s);
+
+// ---- optimizers (optim.hip)
+struct AdamSeg {
+  float* p;
+  const float* g;
+  float* m;
+  float* v;
+  int64_t n;
+  float wd;
+  int pad;
+};
+struct AdamChunk {
+  int seg;
+  int pad;
+  int64_t off;
+};
+hipError_t adamw_step(const AdamSeg* segs, const AdamChunk* chunks, int nchunks, int64_t chunk_elems, float lr,
+                      float b1, float b2, float eps, float bc1, float bc2, hipStream_t s);
+hipError_t sgd_step(float* p, const float* g, float lr, int64_t n, hipStream_t s);
+
+}  // namespace tfb

@@ -1,0 +1,440 @@
+// Row reductions: LayerNorm, the causal row softmax and the fused softmax +
+// cross-entropy, forward and backward ([Autograd-1, "Ops": SoftmaxCrossEntropy
+// and Softmax, the table of ops: LayerNorm, CausalSoftmax; GPT2-4, "The 12
+// unused tensors": the causal mask is computed, row r sees r % T + 1 columns]).
+// One 64-lane wavefront per row, with the row cached in registers when it fits
+// (16 values per lane, rows up to 1024); wave-shuffle reductions; column sums
+// (LayerNorm's dgamma, dbeta) are per-block partials reduced in a second pass,
+// so every result is deterministic.
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace tfb {
+namespace {
+
+constexpr int NT = 256;
+constexpr int WAVES = NT / 64;
+constexpr int MAXV = 16;  // cached values per lane -> rows up to 1024
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ------------------------------------------------------------ LayerNorm
+template <bool CACHED>
+__global__ __launch_bounds__(NT) void ln_fwd_k(const float* __restrict__ x, const float* __restrict__ gamma,
+                                               const float* __restrict__ beta, float* __restrict__ y,
+                                               float* __restrict__ mean, float* __restrict__ rstd, int64_t rows,
+                                               int C, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * WAVES;
+  for (int64_t r = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); r < rows; r += nw) {
+    const float* xr = x + r * C;
+    float v[MAXV];
+    float s = 0.f;
+    if (CACHED) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int c = lane + 64 * j;
+        v[j] = c < C ? xr[c] : 0.f;
+        s += v[j];
+      }
+    } else {
+      for (int c = lane; c < C; c += 64) s += xr[c];
+    }
+    const float mu = wave_sum(s) / C;
+    float q = 0.f;
+    if (CACHED) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int c = lane + 64 * j;
+        const float d = c < C ? v[j] - mu : 0.f;
+        q += d * d;
+      }
+    } else {
+      for (int c = lane; c < C; c += 64) {
+        const float d = xr[c] - mu;
+        q += d * d;
+      }
+    }
+    const float rs = rsqrtf(wave_sum(q) / C + eps);
+    float* yr = y + r * C;
+    if (CACHED) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int c = lane + 64 * j;
+        if (c < C) yr[c] = (v[j] - mu) * rs * gamma[c] + beta[c];
+      }
+    } else {
+      for (int c = lane; c < C; c += 64) yr[c] = (xr[c] - mu) * rs * gamma[c] + beta[c];
+    }
+    if (lane == 0) {
+      mean[r] = mu;
+      rstd[r] = rs;
+    }
+  }
+}
+
+// dx per row; per-block partial column sums of g*xhat and g
+template <bool CACHED>
+__global__ __launch_bounds__(NT) void ln_bwd_k(const float* __restrict__ g, const float* __restrict__ x,
+                                               const float* __restrict__ gamma, const float* __restrict__ mean,
+                                               const float* __restrict__ rstd, float* __restrict__ dx,
+                                               float* __restrict__ part, int64_t rows, int C, float beta_dx) {
+  extern __shared__ float sh[];  // [WAVES][2][C]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float* dg = sh + (w * 2) * C;
+  float* db = sh + (w * 2 + 1) * C;
+  for (int c = lane; c < C; c += 64) dg[c] = db[c] = 0.f;
+  const int64_t nw = (int64_t)gridDim.x * WAVES;
+  for (int64_t r = (int64_t)blockIdx.x * WAVES + w; r < rows; r += nw) {
+    const float mu = mean[r], rs = rstd[r];
+    const float* gr = g + r * C;
+    const float* xr = x + r * C;
+    float xh[MAXV], gg[MAXV];
+    float s1 = 0.f, s2 = 0.f;
+    if (CACHED) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int c = lane + 64 * j;
+        if (c < C) {
+          xh[j] = (xr[c] - mu) * rs;
+          gg[j] = gr[c];
+          const float d = gg[j] * gamma[c];
+          s1 += d;
+          s2 += d * xh[j];
+          dg[c] += gg[j] * xh[j];
+          db[c] += gg[j];
+        } else {
+          xh[j] = gg[j] = 0.f;
+        }
+      }
+    } else {
+      for (int c = lane; c < C; c += 64) {
+        const float xv = (xr[c] - mu) * rs, gv = gr[c];
+        const float d = gv * gamma[c];
+        s1 += d;
+        s2 += d * xv;
+        dg[c] += gv * xv;
+        db[c] += gv;
+      }
+    }
+    const float m1 = wave_sum(s1) / C, m2 = wave_sum(s2) / C;
+    float* dr = dx + r * C;
+    if (CACHED) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int c = lane + 64 * j;
+        if (c < C) {
+          float v = rs * (gg[j] * gamma[c] - m1 - xh[j] * m2);
+          if (beta_dx != 0.f) v += dr[c];
+          dr[c] = v;
+        }
+      }
+    } else {
+      for (int c = lane; c < C; c += 64) {
+        const float xv = (xr[c] - mu) * rs;
+        float v = rs * (gr[c] * gamma[c] - m1 - xv * m2);
+        if (beta_dx != 0.f) v += dr[c];
+        dr[c] = v;
+      }
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < C; c += NT) {
+    float a = 0.f, b = 0.f;
+    for (int i = 0; i < WAVES; ++i) {
+      a += sh[(i * 2) * C + c];
+      b += sh[(i * 2 + 1) * C + c];
+    }
+    part[((int64_t)blockIdx.x * 2) * C + c] = a;
+    part[((int64_t)blockIdx.x * 2 + 1) * C + c] = b;
+  }
+}
+
+__global__ void ln_bwd_reduce(const float* __restrict__ part, int nparts, int C, float* __restrict__ dgamma,
+                              float* __restrict__ dbeta, float beta_dg, float beta_db) {
+  const int c = blockIdx.x * NT + threadIdx.x;
+  if (c >= C) return;
+  float a = 0.f, b = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    a += part[((int64_t)p * 2) * C + c];
+    b += part[((int64_t)p * 2 + 1) * C + c];
+  }
+  if (beta_dg != 0.f) a += dgamma[c];
+  if (beta_db != 0.f) b += dbeta[c];
+  dgamma[c] = a;
+  dbeta[c] = b;
+}
+
+int ln_bwd_blocks(int64_t rows) { return (int)std::max<int64_t>(1, std::min<int64_t>(256, (rows + WAVES - 1) / WAVES)); }
+
+// ------------------------------------------------------------ causal softmax
+template <bool CACHED>
+__global__ __launch_bounds__(NT) void csm_fwd_k(const float* __restrict__ x, float* __restrict__ p, int64_t rows,
+                                                int T, bool full) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * WAVES;
+  for (int64_t r = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); r < rows; r += nw) {
+    const int vis = (int)(r % T) + 1;
+    const float* xr = x + r * T;
+    float* pr = p + r * T;
+    float v[MAXV];
+    float mx = -INFINITY;
+    if (CACHED) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int c = lane + 64 * j;
+        v[j] = c < vis ? xr[c] : -INFINITY;
+        mx = fmaxf(mx, v[j]);
+      }
+    } else {
+      for (int c = lane; c < vis; c += 64) mx = fmaxf(mx, xr[c]);
+    }
+    mx = wave_max(mx);
+    float s = 0.f;
+    if (CACHED) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int c = lane + 64 * j;
+        v[j] = c < vis ? expf(v[j] - mx) : 0.f;
+        s += v[j];
+      }
+    } else {
+      for (int c = lane; c < vis; c += 64) s += expf(xr[c] - mx);
+    }
+    const float inv = 1.f / wave_sum(s);
+    if (CACHED) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int c = lane + 64 * j;
+        if (c < vis)
+          pr[c] = v[j] * inv;
+        else if (full && c < T)
+          pr[c] = 0.f;
+      }
+    } else {
+      for (int c = lane; c < T; c += 64) {
+        if (c < vis)
+          pr[c] = expf(xr[c] - mx) * inv;
+        else if (full)
+          pr[c] = 0.f;
+      }
+    }
+  }
+}
+
+template <bool CACHED>
+__global__ __launch_bounds__(NT) void csm_bwd_k(const float* __restrict__ g, const float* __restrict__ p,
+                                                float* __restrict__ d, int64_t rows, int T, float scale, float beta,
+                                                bool full) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * WAVES;
+  for (int64_t r = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); r < rows; r += nw) {
+    const int vis = (int)(r % T) + 1;
+    const float* gr = g + r * T;
+    const float* pr = p + r * T;
+    float* dr = d + r * T;
+    float gv[MAXV], pv[MAXV];
+    float s = 0.f;
+    if (CACHED) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int c = lane + 64 * j;
+        gv[j] = c < vis ? gr[c] : 0.f;
+        pv[j] = c < vis ? pr[c] : 0.f;
+        s += gv[j] * pv[j];
+      }
+    } else {
+      for (int c = lane; c < vis; c += 64) s += gr[c] * pr[c];
+    }
+    s = wave_sum(s);
+    if (CACHED) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int c = lane + 64 * j;
+        if (c < vis) {
+          float v = scale * pv[j] * (gv[j] - s);
+          if (beta != 0.f) v += dr[c];
+          dr[c] = v;
+        } else if (full && beta == 0.f && c < T) {
+          dr[c] = 0.f;
+        }
+      }
+    } else {
+      for (int c = lane; c < T; c += 64) {
+        if (c < vis) {
+          float v = scale * pr[c] * (gr[c] - s);
+          if (beta != 0.f) v += dr[c];
+          dr[c] = v;
+        } else if (full && beta == 0.f) {
+          dr[c] = 0.f;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ softmax + cross-entropy
+__device__ __forceinline__ void online_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * expf(m - mn) + s2 * expf(m2 - mn);
+  m = mn;
+}
+
+// one block per row: lse[r] = log(sum exp(logits)), loss_rows[r] = -log(max(p_target, 1e-30))
+__global__ __launch_bounds__(NT) void ce_fwd_k(const float* __restrict__ logits, const int32_t* __restrict__ tgt,
+                                               int64_t V, float* __restrict__ lse, float* __restrict__ loss_rows) {
+  __shared__ float sm[WAVES], ss[WAVES];
+  const int64_t r = blockIdx.x;
+  const float* lr = logits + r * V;
+  float m = -INFINITY, s = 0.f;
+  for (int64_t c = threadIdx.x; c < V; c += NT) {
+    const float x = lr[c];
+    if (x > m) {
+      s = s * expf(m - x) + 1.f;
+      m = x;
+    } else {
+      s += expf(x - m);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    online_merge(m, s, m2, s2);
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+    sm[w] = m;
+    ss[w] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = sm[0], S = ss[0];
+    for (int i = 1; i < WAVES; ++i) online_merge(M, S, sm[i], ss[i]);
+    const float L = M + logf(S);
+    lse[r] = L;
+    // -log(max(p_t, 1e-30)) with p_t = exp(x_t - L); -log(1e-30) = 69.0775527898...
+    // (a target outside [0, V) is a caller error: it yields NaN instead of a stray read)
+    const int t = tgt[r];
+    loss_rows[r] = (t >= 0 && t < V) ? fminf(L - lr[t], 69.07755278982137f) : NAN;
+  }
+}
+
+__global__ __launch_bounds__(NT) void mean_k(const float* __restrict__ v, int64_t n, float* __restrict__ out) {
+  __shared__ double sh[NT];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += NT) s += (double)v[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = (float)(sh[0] / (double)n);
+}
+
+__global__ __launch_bounds__(NT) void ce_bwd_k(const float* __restrict__ logits, const int32_t* __restrict__ tgt,
+                                               const float* __restrict__ lse, const float* __restrict__ gsc,
+                                               float* __restrict__ dl, int64_t rows, int64_t V, float beta) {
+  const int64_t r = blockIdx.x;
+  const float gn = gsc[0] / (float)rows;
+  const float L = lse[r];
+  const int t = tgt[r];
+  const float* lr = logits + r * V;
+  float* dr = dl + r * V;
+  for (int64_t c = threadIdx.x; c < V; c += NT) {
+    float v = gn * (expf(lr[c] - L) - (c == t ? 1.f : 0.f));
+    if (beta != 0.f) v += dr[c];
+    dr[c] = v;
+  }
+}
+
+inline unsigned row_blocks(int64_t rows) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>((rows + WAVES - 1) / WAVES, 65536));
+}
+
+}  // namespace
+
+hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, float* y, float* mean, float* rstd,
+                         int64_t rows, int64_t C, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (C <= 64 * MAXV)
+    hipLaunchKernelGGL(ln_fwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, mean, rstd, rows,
+                       (int)C, eps);
+  else
+    hipLaunchKernelGGL(ln_fwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, mean, rstd, rows,
+                       (int)C, eps);
+  return hipGetLastError();
+}
+
+size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C) {
+  return (size_t)ln_bwd_blocks(rows) * 2 * C * sizeof(float);
+}
+
+hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
+                         float* dx, float* dgamma, float* dbeta, int64_t rows, int64_t C, float beta_dx,
+                         float beta_dg, float beta_db, void* ws, hipStream_t s) {
+  if (C <= 0) return hipSuccess;
+  const int nb = ln_bwd_blocks(rows);
+  const size_t shmem = (size_t)WAVES * 2 * C * sizeof(float);
+  if (shmem > 64 * 1024) return hipErrorInvalidValue;
+  float* part = static_cast<float*>(ws);
+  if (C <= 64 * MAXV)
+    hipLaunchKernelGGL(ln_bwd_k<true>, dim3(nb), dim3(NT), shmem, s, g, x, gamma, mean, rstd, dx, part, rows, (int)C,
+                       beta_dx);
+  else
+    hipLaunchKernelGGL(ln_bwd_k<false>, dim3(nb), dim3(NT), shmem, s, g, x, gamma, mean, rstd, dx, part, rows,
+                       (int)C, beta_dx);
+  hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + NT - 1) / NT)), dim3(NT), 0, s, part, nb, (int)C, dgamma,
+                     dbeta, beta_dg, beta_db);
+  return hipGetLastError();
+}
+
+hipError_t causal_softmax_fwd(const float* x, float* p, int64_t rows, int64_t T, bool full, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (T <= 64 * MAXV)
+    hipLaunchKernelGGL(csm_fwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, p, rows, (int)T, full);
+  else
+    hipLaunchKernelGGL(csm_fwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, p, rows, (int)T, full);
+  return hipGetLastError();
+}
+
+hipError_t causal_softmax_bwd(const float* g, const float* p, float* d, int64_t rows, int64_t T, float scale,
+                              float beta, bool full, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (T <= 64 * MAXV)
+    hipLaunchKernelGGL(csm_bwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, p, d, rows, (int)T, scale, beta,
+                       full);
+  else
+    hipLaunchKernelGGL(csm_bwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, p, d, rows, (int)T, scale, beta,
+                       full);
+  return hipGetLastError();
+}
+
+size_t softmax_ce_workspace_bytes(int64_t rows) { return (size_t)rows * sizeof(float); }
+
+hipError_t softmax_ce_fwd(const float* logits, const int32_t* targets, int64_t rows, int64_t V, float* lse,
+                          float* loss, void* ws, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  float* loss_rows = static_cast<float*>(ws);
+  hipLaunchKernelGGL(ce_fwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, targets, V, lse, loss_rows);
+  hipLaunchKernelGGL(mean_k, dim3(1), dim3(NT), 0, s, loss_rows, rows, loss);
+  return hipGetLastError();
+}
+
+hipError_t softmax_ce_bwd(const float* logits, const int32_t* targets, const float* lse, const float* g_scalar,
+                          float* dl, int64_t rows, int64_t V, float beta, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, targets, lse, g_scalar, dl, rows, V,
+                     beta);
+  return hipGetLastError();
+}
+
+}  // namespace tfb

@@ -1,0 +1,1349 @@
+// Host runtime of the C ABI declared in include/tfb.h: tensor table, arena,
+// tape and the backward replay.
+//
+// The tape follows [Autograd-1, "How each op records itself in the graph"]:
+// each op appends one record (inputs, output, saved values) after it has
+// enqueued its forward kernels; backward() walks the records from the last to
+// the first.  Records are appended in execution order, which is a topological
+// order of the graph, so the reverse walk visits a node only after everything
+// that consumed it.  A record whose output never received a gradient cannot
+// reach the loss and is skipped (its contribution would be zero).
+//
+// Gradient buffers carry a state: NONE (no buffer), ZERO (cleared, contents
+// not yet materialised) or VALID.  The first backward rule that writes a
+// ZERO/NONE gradient overwrites it (beta = 0), every later one adds (beta = 1),
+// which is the "+=" rule without a separate clearing pass.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <stdexcept>
+#include <string>
+#include <vector>
+
+#include "../../include/tfb.h"
+#include "kernels.h"
+
+using namespace tfb;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Err {
+  int code;
+  std::string msg;
+};
+
+[[noreturn]] void fail(int code, const std::string& msg) { throw Err{code, msg}; }
+
+void hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) fail(TFB_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+enum GradState { G_NONE = 0, G_ZERO = 1, G_VALID = 2 };
+
+struct TensorRec {
+  bool live = false;
+  bool leaf = true;
+  bool is_param = false;
+  bool owns_persistent = false;
+  int ndim = 0;
+  int64_t shape[TFB_MAX_DIMS] = {0};
+  int64_t numel = 0;
+  float* data = nullptr;
+  float* grad = nullptr;
+  int gstate = G_NONE;
+  size_t persist_off = 0, persist_bytes = 0;
+
+  int64_t cols() const { return ndim ? shape[ndim - 1] : 1; }
+  int64_t rows() const { return cols() ? numel / cols() : 0; }
+};
+
+enum OpKind {
+  OP_ADD,
+  OP_MUL,
+  OP_SCALE,
+  OP_SUM,
+  OP_RESHAPE,
+  OP_TANH,
+  OP_GELU,
+  OP_MATMUL,
+  OP_MATMUL_T,
+  OP_LINEAR,
+  OP_LAYERNORM,
+  OP_EMBEDDING,
+  OP_NARROW,
+  OP_SPLIT_HEADS,
+  OP_MERGE_HEADS,
+  OP_BMM,
+  OP_BMM_T,
+  OP_CSOFTMAX,
+  OP_ATTENTION,
+  OP_SOFTMAX_CE,
+};
+
+struct Rec {
+  OpKind op;
+  int in[3] = {-1, -1, -1};
+  int out = -1;
+  float f = 0.f;
+  int64_t i0 = 0, i1 = 0, i2 = 0, i3 = 0;
+  void* s0 = nullptr;  // saved buffers (step arena)
+  void* s1 = nullptr;
+};
+
+constexpr size_t ALIGN = 256;
+
+struct Arena {
+  char* base = nullptr;
+  size_t size = 0;
+  size_t lo = 0;   // persistent allocations: [0, lo)
+  size_t hi = 0;   // step allocations: [hi, size)
+
+  static size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
+  size_t alloc_persist(size_t n) {
+    n = up(std::max<size_t>(n, 1));
+    if (lo + n > hi) fail(TFB_ERR_OOM, "arena exhausted (persistent allocation of " + std::to_string(n) + " bytes)");
+    size_t off = lo;
+    lo += n;
+    return off;
+  }
+  void* alloc_step(size_t n) {
+    n = up(std::max<size_t>(n, 1));
+    if (hi < lo + n) fail(TFB_ERR_OOM, "arena exhausted (step allocation of " + std::to_string(n) + " bytes)");
+    hi -= n;
+    return base + hi;
+  }
+};
+
+}  // namespace
+
+struct ProfileState {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  int used = 0;
+  double flops = 0.0;
+  int launches = 0;
+};
+
+struct tfb_ctx {
+  ProfileState prof;
+  int device = 0;
+  hipStream_t stream = nullptr;
+  Arena arena;
+  int precision = TFB_FP32;
+  bool grad_enabled = true;
+  std::deque<TensorRec> tensors;  // deque: handles' references survive growth
+  std::vector<int> free_handles;
+  std::vector<Rec> tape;
+};
+
+struct tfb_opt {
+  tfb_ctx* ctx = nullptr;
+  std::vector<int> params;
+  std::vector<float*> m, v;
+  float lr, wd, b1, b2, eps;
+  int t = 0;
+  int64_t chunk_elems = 1 << 16;
+  AdamSeg* d_segs = nullptr;
+  AdamChunk* d_chunks = nullptr;
+  int d_nseg_cap = 0, d_nchunk_cap = 0;
+  std::vector<int> uploaded_active;
+  int nchunks = 0;
+};
+
+namespace {
+
+// ------------------------------------------------------------------ helpers
+struct Ctx {
+  tfb_ctx* c;
+  explicit Ctx(tfb_ctx* ctx) : c(ctx) {
+    if (!ctx) fail(TFB_ERR_ARG, "null context");
+    hip_check(hipSetDevice(ctx->device), "hipSetDevice");
+  }
+  TensorRec& T(int h) {
+    if (h < 0 || h >= (int)c->tensors.size() || !c->tensors[h].live)
+      fail(TFB_ERR_ARG, "invalid or released tensor handle " + std::to_string(h));
+    return c->tensors[h];
+  }
+  hipStream_t s() const { return c->stream; }
+
+  int new_handle() {
+    if (!c->free_handles.empty()) {
+      int h = c->free_handles.back();
+      c->free_handles.pop_back();
+      c->tensors[h] = TensorRec();
+      return h;
+    }
+    c->tensors.emplace_back();
+    return (int)c->tensors.size() - 1;
+  }
+
+  static int64_t numel_of(const int64_t* shape, int ndim) {
+    if (ndim < 1 || ndim > TFB_MAX_DIMS) fail(TFB_ERR_SHAPE, "rank must be 1.." + std::to_string(TFB_MAX_DIMS));
+    int64_t n = 1;
+    for (int i = 0; i < ndim; ++i) {
+      if (shape[i] < 0) fail(TFB_ERR_SHAPE, "negative dimension");
+      n *= shape[i];
+    }
+    return n;
+  }
+
+  // an op output in the step arena
+  int make_output(const std::vector<int64_t>& shape) {
+    int64_t n = numel_of(shape.data(), (int)shape.size());
+    float* p = static_cast<float*>(c->arena.alloc_step((size_t)n * sizeof(float)));
+    int h = new_handle();
+    TensorRec& t = c->tensors[h];
+    t.live = true;
+    t.leaf = false;
+    t.ndim = (int)shape.size();
+    for (int i = 0; i < t.ndim; ++i) t.shape[i] = shape[i];
+    t.numel = n;
+    t.data = p;
+    return h;
+  }
+
+  void ensure_grad_buffer(TensorRec& t) {
+    if (t.grad) return;
+    if (t.leaf) {
+      size_t off = c->arena.alloc_persist((size_t)t.numel * sizeof(float));
+      t.grad = reinterpret_cast<float*>(c->arena.base + off);
+    } else {
+      t.grad = static_cast<float*>(c->arena.alloc_step((size_t)t.numel * sizeof(float)));
+    }
+    t.gstate = G_ZERO;
+  }
+
+  // destination of a gradient contribution: (pointer, beta)
+  std::pair<float*, float> gdst(int h) {
+    TensorRec& t = T(h);
+    ensure_grad_buffer(t);
+    if (t.gstate == G_VALID) return {t.grad, 1.f};
+    t.gstate = G_VALID;
+    return {t.grad, 0.f};
+  }
+
+  void materialize_zero(TensorRec& t) {
+    if (t.grad && t.gstate == G_ZERO) {
+      hip_check(fill(t.grad, 0.f, t.numel, s()), "fill");
+      t.gstate = G_VALID;
+    }
+  }
+
+  void record(const Rec& r) {
+    if (c->grad_enabled) c->tape.push_back(r);
+  }
+
+  GemmArgs gemm_base() const {
+    GemmArgs g;
+    g.prec = c->precision == TFB_BF16_MFMA ? PREC_BF16 : PREC_F32;
+    return g;
+  }
+
+  void run_gemm(const GemmArgs& g) {
+    size_t ws = gemm_workspace_bytes(g);
+    size_t mark = c->arena.hi;
+    void* w = ws ? c->arena.alloc_step(ws) : nullptr;
+    ProfileState& pf = c->prof;
+    if (pf.on) {
+      while ((int)pf.pool.size() < pf.used + 2) {
+        hipEvent_t e;
+        hip_check(hipEventCreate(&e), "hipEventCreate");
+        pf.pool.push_back(e);
+      }
+      hip_check(hipEventRecord(pf.pool[pf.used], s()), "hipEventRecord");
+    }
+    hip_check(gemm(g, w, ws, s()), "gemm launch");
+    if (pf.on) {
+      hip_check(hipEventRecord(pf.pool[pf.used + 1], s()), "hipEventRecord");
+      pf.used += 2;
+      pf.flops += needed_flops(g);
+      pf.launches += 1;
+    }
+    c->arena.hi = mark;  // scratch: later work on the same stream runs after this gemm
+  }
+
+  // multiply-adds the contraction must do, x2; a causal product needs only the
+  // triangle j <= i: T(T+1)/2 of the T*T (query, key) pairs
+  static double needed_flops(const GemmArgs& g) {
+    double f = 2.0 * g.M * (double)g.N * g.K * g.batch;
+    if (g.causal_out) f = 2.0 * g.K * (g.M * (g.M + 1.0) / 2.0) * g.batch;
+    if (g.causal_a != CAUSAL_NONE) f = 2.0 * g.N * (g.M * (g.M + 1.0) / 2.0) * g.batch;
+    return f;
+  }
+
+  void* scratch(size_t n) { return c->arena.alloc_step(n); }
+};
+
+template <typename F>
+int guarded(F&& f) {
+  try {
+    f();
+    return TFB_OK;
+  } catch (const Err& e) {
+    g_last_error = e.msg;
+    return e.code;
+  } catch (const std::exception& e) {
+    g_last_error = e.what();
+    return TFB_ERR_STATE;
+  }
+}
+
+void need(bool cond, int code, const std::string& msg) {
+  if (!cond) fail(code, msg);
+}
+
+std::string shape_str(const TensorRec& t) {
+  std::string s = "[";
+  for (int i = 0; i < t.ndim; ++i) s += (i ? "," : "") + std::to_string(t.shape[i]);
+  return s + "]";
+}
+
+std::vector<int64_t> shape_vec(const TensorRec& t) { return std::vector<int64_t>(t.shape, t.shape + t.ndim); }
+
+// ------------------------------------------------------------------ contraction layouts
+// y[rows, N] = x[rows, K] @ w[K, N] (+ bias)
+void gemm_nn(Ctx& C, const float* x, const float* w, float* y, int64_t rows, int64_t K, int64_t N, float beta,
+             const float* bias) {
+  GemmArgs g = C.gemm_base();
+  g.M = (int)rows, g.N = (int)N, g.K = (int)K;
+  g.A = x, g.lda = K;
+  g.B = w, g.ldb = N;
+  g.C = y, g.ldc = N;
+  g.beta = beta, g.bias = bias;
+  C.run_gemm(g);
+}
+// y[rows, N] = x[rows, K] @ w[N, K]^T
+void gemm_nt(Ctx& C, const float* x, const float* w, float* y, int64_t rows, int64_t K, int64_t N, float beta) {
+  GemmArgs g = C.gemm_base();
+  g.M = (int)rows, g.N = (int)N, g.K = (int)K;
+  g.A = x, g.lda = K;
+  g.B = w, g.ldb = K, g.b_kcontig = true;
+  g.C = y, g.ldc = N;
+  g.beta = beta;
+  C.run_gemm(g);
+}
+// y[M, N] = x[K, M]^T @ g[K, N]
+void gemm_tn(Ctx& C, const float* x, const float* gr, float* y, int64_t M, int64_t K, int64_t N, float beta) {
+  GemmArgs g = C.gemm_base();
+  g.M = (int)M, g.N = (int)N, g.K = (int)K;
+  g.A = x, g.lda = M, g.a_mcontig = true;
+  g.B = gr, g.ldb = N;
+  g.C = y, g.ldc = N;
+  g.beta = beta;
+  C.run_gemm(g);
+}
+
+void check_gemm_dims(int64_t a, int64_t b, int64_t c) {
+  need(a < (1ll << 31) && b < (1ll << 31) && c < (1ll << 31), TFB_ERR_SHAPE, "contraction dimension too large");
+}
+
+// ------------------------------------------------------------------ backward rules
+void backward_rec(Ctx& C, const Rec& r) {
+  TensorRec& out = C.T(r.out);
+  const float* g = out.grad;
+  hipStream_t s = C.s();
+  switch (r.op) {
+    case OP_ADD: {
+      TensorRec& a = C.T(r.in[0]);
+      TensorRec& b = C.T(r.in[1]);
+      auto da = C.gdst(r.in[0]);
+      hip_check(axpby(da.first, g, 1.f, da.second, a.numel, s), "add bwd");
+      auto db = C.gdst(r.in[1]);
+      const int64_t rows = b.numel ? a.numel / b.numel : 0;
+      size_t mark = C.c->arena.hi;
+      void* ws = C.scratch(colsum_workspace_bytes(rows, b.numel));
+      hip_check(colsum(g, rows, b.numel, db.first, db.second, ws, s), "add bwd colsum");
+      C.c->arena.hi = mark;
+      break;
+    }
+    case OP_MUL: {
+      TensorRec& a = C.T(r.in[0]);
+      TensorRec& b = C.T(r.in[1]);
+      auto da = C.gdst(r.in[0]);
+      hip_check(mul_bwd(g, b.data, da.first, da.second, a.numel, s), "mul bwd a");
+      auto db = C.gdst(r.in[1]);
+      hip_check(mul_bwd(g, a.data, db.first, db.second, b.numel, s), "mul bwd b");
+      break;
+    }
+    case OP_SCALE: {
+      auto da = C.gdst(r.in[0]);
+      hip_check(axpby(da.first, g, r.f, da.second, out.numel, s), "scale bwd");
+      break;
+    }
+    case OP_SUM: {
+      TensorRec& a = C.T(r.in[0]);
+      auto da = C.gdst(r.in[0]);
+      hip_check(bcast_scalar_bwd(g, da.first, da.second, a.numel, s), "sum bwd");
+      break;
+    }
+    case OP_RESHAPE: {
+      auto da = C.gdst(r.in[0]);
+      hip_check(axpby(da.first, g, 1.f, da.second, out.numel, s), "reshape bwd");
+      break;
+    }
+    case OP_TANH: {
+      auto da = C.gdst(r.in[0]);
+      hip_check(tanh_bwd(g, out.data, da.first, da.second, out.numel, s), "tanh bwd");
+      break;
+    }
+    case OP_GELU: {
+      TensorRec& a = C.T(r.in[0]);
+      auto da = C.gdst(r.in[0]);
+      hip_check(gelu_bwd(g, a.data, da.first, da.second, out.numel, s), "gelu bwd");
+      break;
+    }
+    case OP_MATMUL:
+    case OP_LINEAR: {
+      TensorRec& x = C.T(r.in[0]);
+      TensorRec& w = C.T(r.in[1]);
+      const int64_t rows = x.rows(), K = w.shape[0], N = w.shape[1];
+      auto dx = C.gdst(r.in[0]);
+      gemm_nt(C, g, w.data, dx.first, rows, N, K, dx.second);           // dx = g @ w^T
+      auto dw = C.gdst(r.in[1]);
+      gemm_tn(C, x.data, g, dw.first, K, rows, N, dw.second);            // dw = x^T @ g
+      if (r.op == OP_LINEAR) {
+        auto db = C.gdst(r.in[2]);
+        size_t mark = C.c->arena.hi;
+        void* ws = C.scratch(colsum_workspace_bytes(rows, N));
+        hip_check(colsum(g, rows, N, db.first, db.second, ws, s), "linear bias bwd");
+        C.c->arena.hi = mark;
+      }
+      break;
+    }
+    case OP_MATMUL_T: {
+      TensorRec& x = C.T(r.in[0]);
+      TensorRec& w = C.T(r.in[1]);
+      const int64_t rows = x.rows(), V = w.shape[0], Cc = w.shape[1];
+      auto dx = C.gdst(r.in[0]);
+      gemm_nn(C, g, w.data, dx.first, rows, V, Cc, dx.second, nullptr);  // dx = g @ w
+      auto dw = C.gdst(r.in[1]);
+      gemm_tn(C, g, x.data, dw.first, V, rows, Cc, dw.second);           // dw = g^T @ x
+      break;
+    }
+    case OP_LAYERNORM: {
+      TensorRec& x = C.T(r.in[0]);
+      TensorRec& gm = C.T(r.in[1]);
+      const int64_t rows = x.rows(), Cc = x.cols();
+      auto dx = C.gdst(r.in[0]);
+      auto dg = C.gdst(r.in[1]);
+      auto db = C.gdst(r.in[2]);
+      size_t mark = C.c->arena.hi;
+      void* ws = C.scratch(layernorm_bwd_workspace_bytes(rows, Cc));
+      hip_check(layernorm_bwd(g, x.data, gm.data, static_cast<float*>(r.s0), static_cast<float*>(r.s1), dx.first,
+                              dg.first, db.first, rows, Cc, dx.second, dg.second, db.second, ws, s),
+                "layernorm bwd");
+      C.c->arena.hi = mark;
+      break;
+    }
+    case OP_EMBEDDING: {
+      TensorRec& tab = C.T(r.in[0]);
+      auto dt = C.gdst(r.in[0]);
+      if (dt.second == 0.f) hip_check(fill(dt.first, 0.f, tab.numel, s), "embedding bwd clear");
+      size_t mark = C.c->arena.hi;
+      void* ws = C.scratch(embedding_bwd_workspace_bytes(r.i0));
+      hip_check(embedding_bwd(g, static_cast<const int32_t*>(r.s0), r.i0, tab.cols(), dt.first, tab.rows(), ws, s),
+                "embedding bwd");
+      C.c->arena.hi = mark;
+      break;
+    }
+    case OP_NARROW: {
+      TensorRec& x = C.T(r.in[0]);
+      auto dx = C.gdst(r.in[0]);
+      hip_check(narrow_bwd(g, dx.first, x.rows(), x.cols(), r.i0, r.i1, dx.second, s), "narrow bwd");
+      break;
+    }
+    case OP_SPLIT_HEADS: {  // out [B, H, T, hs] -> dx [B, T, H, hs]
+      auto dx = C.gdst(r.in[0]);
+      hip_check(permute_heads(g, dx.first, out.shape[0], out.shape[2], out.shape[1], out.shape[3], false, dx.second, s),
+                "split_heads bwd");
+      break;
+    }
+    case OP_MERGE_HEADS: {  // in [B, H, T, hs]
+      TensorRec& x = C.T(r.in[0]);
+      auto dx = C.gdst(r.in[0]);
+      hip_check(permute_heads(g, dx.first, x.shape[0], x.shape[2], x.shape[1], x.shape[3], true, dx.second, s),
+                "merge_heads bwd");
+      break;
+    }
+    case OP_BMM:
+    case OP_BMM_T: {
+      TensorRec& a = C.T(r.in[0]);
+      TensorRec& b = C.T(r.in[1]);
+      const int64_t Z = a.shape[0], n = a.shape[1], k = a.shape[2];
+      const int64_t m = out.shape[2];
+      auto da = C.gdst(r.in[0]);
+      {
+        GemmArgs q = C.gemm_base();
+        q.M = (int)n, q.N = (int)k, q.K = (int)m;
+        q.A = g, q.lda = m, q.sa1 = n * m;
+        q.B = b.data;
+        if (r.op == OP_BMM) {  // da = g @ b^T, b [Z, k, m]
+          q.ldb = m, q.b_kcontig = true, q.sb1 = k * m;
+        } else {               // da = g @ b, b [Z, m, k]
+          q.ldb = k, q.sb1 = m * k;
+        }
+        q.C = da.first, q.ldc = k, q.sc1 = n * k;
+        q.beta = da.second, q.batch = (int)Z;
+        C.run_gemm(q);
+      }
+      auto db = C.gdst(r.in[1]);
+      {
+        GemmArgs q = C.gemm_base();
+        q.batch = (int)Z;
+        q.beta = db.second;
+        if (r.op == OP_BMM) {  // db [k, m] = a^T @ g
+          q.M = (int)k, q.N = (int)m, q.K = (int)n;
+          q.A = a.data, q.lda = k, q.a_mcontig = true, q.sa1 = n * k;
+          q.B = g, q.ldb = m, q.sb1 = n * m;
+          q.C = db.first, q.ldc = m, q.sc1 = k * m;
+        } else {               // db [m, k] = g^T @ a
+          q.M = (int)m, q.N = (int)k, q.K = (int)n;
+          q.A = g, q.lda = m, q.a_mcontig = true, q.sa1 = n * m;
+          q.B = a.data, q.ldb = k, q.sb1 = n * k;
+          q.C = db.first, q.ldc = k, q.sc1 = m * k;
+        }
+        C.run_gemm(q);
+      }
+      break;
+    }
+    case OP_CSOFTMAX: {
+      auto dx = C.gdst(r.in[0]);
+      hip_check(causal_softmax_bwd(g, out.data, dx.first, out.rows(), out.cols(), 1.f, dx.second, true, s),
+                "causal_softmax bwd");
+      break;
+    }
+    case OP_ATTENTION: {
+      TensorRec& qkv = C.T(r.in[0]);
+      const int64_t B = qkv.shape[0], T = qkv.shape[1], C3 = qkv.shape[2], Cc = C3 / 3, H = r.i0, hs = Cc / H;
+      const float scale = r.f;
+      float* P = static_cast<float*>(r.s0);
+      // the gradient buffer first: it must outlive the scratch released below
+      auto dq = C.gdst(r.in[0]);
+      float* dqkv = dq.first;
+      size_t mark = C.c->arena.hi;
+      float* dP = static_cast<float*>(C.scratch((size_t)B * H * T * T * sizeof(float)));
+      const float* q = qkv.data;
+      {  // dP = dY_h @ V_h^T (lower triangle of tiles)
+        GemmArgs a = C.gemm_base();
+        a.M = (int)T, a.N = (int)T, a.K = (int)hs;
+        a.A = g, a.lda = Cc, a.sa1 = T * Cc, a.sa2 = hs;
+        a.B = q + 2 * Cc, a.ldb = C3, a.b_kcontig = true, a.sb1 = T * C3, a.sb2 = hs;
+        a.C = dP, a.ldc = T, a.sc1 = H * T * T, a.sc2 = T * T;
+        a.batch = (int)(B * H), a.batch_div = (int)H;
+        a.causal_out = true;
+        C.run_gemm(a);
+      }
+      // dS = scale * P (dP - rowsum(P dP)), in place, visible part only
+      hip_check(causal_softmax_bwd(dP, P, dP, B * H * T, T, scale, 0.f, false, s), "attention softmax bwd");
+      {  // dQ = dS @ K
+        GemmArgs a = C.gemm_base();
+        a.M = (int)T, a.N = (int)hs, a.K = (int)T;
+        a.A = dP, a.lda = T, a.sa1 = H * T * T, a.sa2 = T * T, a.causal_a = CAUSAL_UPTO;
+        a.B = q + Cc, a.ldb = C3, a.sb1 = T * C3, a.sb2 = hs;
+        a.C = dqkv, a.ldc = C3, a.sc1 = T * C3, a.sc2 = hs;
+        a.beta = dq.second, a.batch = (int)(B * H), a.batch_div = (int)H;
+        C.run_gemm(a);
+      }
+      {  // dK = dS^T @ Q
+        GemmArgs a = C.gemm_base();
+        a.M = (int)T, a.N = (int)hs, a.K = (int)T;
+        a.A = dP, a.lda = T, a.a_mcontig = true, a.sa1 = H * T * T, a.sa2 = T * T, a.causal_a = CAUSAL_FROM;
+        a.B = q, a.ldb = C3, a.sb1 = T * C3, a.sb2 = hs;
+        a.C = dqkv + Cc, a.ldc = C3, a.sc1 = T * C3, a.sc2 = hs;
+        a.beta = dq.second, a.batch = (int)(B * H), a.batch_div = (int)H;
+        C.run_gemm(a);
+      }
+      {  // dV = P^T @ dY_h
+        GemmArgs a = C.gemm_base();
+        a.M = (int)T, a.N = (int)hs, a.K = (int)T;
+        a.A = P, a.lda = T, a.a_mcontig = true, a.sa1 = H * T * T, a.sa2 = T * T, a.causal_a = CAUSAL_FROM;
+        a.B = g, a.ldb = Cc, a.sb1 = T * Cc, a.sb2 = hs;
+        a.C = dqkv + 2 * Cc, a.ldc = C3, a.sc1 = T * C3, a.sc2 = hs;
+        a.beta = dq.second, a.batch = (int)(B * H), a.batch_div = (int)H;
+        C.run_gemm(a);
+      }
+      C.c->arena.hi = mark;
+      break;
+    }
+    case OP_SOFTMAX_CE: {
+      TensorRec& lg = C.T(r.in[0]);
+      auto dl = C.gdst(r.in[0]);
+      hip_check(softmax_ce_bwd(lg.data, static_cast<const int32_t*>(r.s0), static_cast<const float*>(r.s1), g,
+                               dl.first, lg.rows(), lg.cols(), dl.second, s),
+                "softmax_ce bwd");
+      break;
+    }
+  }
+}
+
+}  // namespace
+
+// ==================================================================== C ABI
+extern "C" {
+
+const char* tfb_last_error(void) { return g_last_error.c_str(); }
+
+int tfb_init(tfb_ctx** out, int device, void* hip_stream, void* arena, size_t arena_bytes, int precision) {
+  return guarded([&] {
+    need(out != nullptr, TFB_ERR_ARG, "null output pointer");
+    need(arena != nullptr && arena_bytes >= ALIGN, TFB_ERR_ARG, "arena must be a device buffer of at least 256 bytes");
+    need((reinterpret_cast<uintptr_t>(arena) & (ALIGN - 1)) == 0, TFB_ERR_ARG, "arena must be 256-byte aligned");
+    need(precision == TFB_FP32 || precision == TFB_BF16_MFMA, TFB_ERR_ARG, "unknown precision");
+    int n = 0;
+    hip_check(hipGetDeviceCount(&n), "hipGetDeviceCount");
+    need(device >= 0 && device < n, TFB_ERR_ARG, "no such device");
+    hip_check(hipSetDevice(device), "hipSetDevice");
+    tfb_ctx* c = new tfb_ctx();
+    c->device = device;
+    c->stream = static_cast<hipStream_t>(hip_stream);
+    c->arena.base = static_cast<char*>(arena);
+    c->arena.size = arena_bytes / ALIGN * ALIGN;
+    c->arena.lo = 0;
+    c->arena.hi = c->arena.size;
+    c->precision = precision;
+    *out = c;
+  });
+}
+
+int tfb_destroy(tfb_ctx* ctx) {
+  return guarded([&] {
+    need(ctx != nullptr, TFB_ERR_ARG, "null context");
+    (void)hipSetDevice(ctx->device);
+    (void)hipStreamSynchronize(ctx->stream);
+    for (hipEvent_t e : ctx->prof.pool) (void)hipEventDestroy(e);
+    delete ctx;
+  });
+}
+
+int tfb_set_precision(tfb_ctx* ctx, int precision) {
+  return guarded([&] {
+    need(ctx != nullptr, TFB_ERR_ARG, "null context");
+    need(precision == TFB_FP32 || precision == TFB_BF16_MFMA, TFB_ERR_ARG, "unknown precision");
+    ctx->precision = precision;
+  });
+}
+
+int tfb_set_grad_enabled(tfb_ctx* ctx, int enabled) {
+  return guarded([&] {
+    need(ctx != nullptr, TFB_ERR_ARG, "null context");
+    ctx->grad_enabled = enabled != 0;
+  });
+}
+
+int tfb_sync(tfb_ctx* ctx) {
+  return guarded([&] {
+    Ctx C(ctx);
+    hip_check(hipStreamSynchronize(C.s()), "stream synchronize");
+    hip_check(hipGetLastError(), "last error");
+  });
+}
+
+int tfb_arena_usage(tfb_ctx* ctx, size_t* persistent, size_t* step) {
+  return guarded([&] {
+    need(ctx != nullptr, TFB_ERR_ARG, "null context");
+    if (persistent) *persistent = ctx->arena.lo;
+    if (step) *step = ctx->arena.size - ctx->arena.hi;
+  });
+}
+
+int tfb_tensor_create(tfb_ctx* ctx, const int64_t* shape, int ndim, void* dev_ptr, int is_param, tfb_tensor* out) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need(shape != nullptr && out != nullptr, TFB_ERR_ARG, "null argument");
+    int64_t n = Ctx::numel_of(shape, ndim);
+    need(dev_ptr == nullptr || (reinterpret_cast<uintptr_t>(dev_ptr) & (ALIGN - 1)) == 0, TFB_ERR_ARG,
+         "borrowed tensor memory must be 256-byte aligned");
+    float* p;
+    size_t off = 0, bytes = 0;
+    if (dev_ptr) {
+      p = static_cast<float*>(dev_ptr);
+    } else {
+      bytes = (size_t)n * sizeof(float);
+      off = ctx->arena.alloc_persist(bytes);
+      p = reinterpret_cast<float*>(ctx->arena.base + off);
+      hip_check(fill(p, 0.f, n, C.s()), "zero fill");
+    }
+    int h = C.new_handle();
+    TensorRec& t = ctx->tensors[h];
+    t.live = true;
+    t.leaf = true;
+    t.is_param = is_param != 0;
+    t.ndim = ndim;
+    for (int i = 0; i < ndim; ++i) t.shape[i] = shape[i];
+    t.numel = n;
+    t.data = p;
+    t.owns_persistent = dev_ptr == nullptr;
+    t.persist_off = off;
+    t.persist_bytes = Arena::up(std::max<size_t>(bytes, 1));
+    *out = h;
+  });
+}
+
+int tfb_tensor_info(tfb_ctx* ctx, tfb_tensor h, int64_t* shape, int* ndim, void** data, void** grad) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& t = C.T(h);
+    if (shape)
+      for (int i = 0; i < t.ndim; ++i) shape[i] = t.shape[i];
+    if (ndim) *ndim = t.ndim;
+    if (data) *data = t.data;
+    if (grad) {
+      C.materialize_zero(t);
+      *grad = t.grad;
+    }
+  });
+}
+
+int tfb_tensor_write(tfb_ctx* ctx, tfb_tensor h, const float* src, int64_t n) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& t = C.T(h);
+    need(src != nullptr && n == t.numel, TFB_ERR_SHAPE, "write of " + std::to_string(n) + " floats into " +
+                                                            shape_str(t));
+    hip_check(hipMemcpyAsync(t.data, src, (size_t)n * sizeof(float), hipMemcpyHostToDevice, C.s()), "copy in");
+    hip_check(hipStreamSynchronize(C.s()), "sync");
+  });
+}
+
+int tfb_tensor_read(tfb_ctx* ctx, tfb_tensor h, int which, float* dst, int64_t n) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& t = C.T(h);
+    need(dst != nullptr && n == t.numel, TFB_ERR_SHAPE, "read of " + std::to_string(n) + " floats from " +
+                                                            shape_str(t));
+    need(which == 0 || which == 1, TFB_ERR_ARG, "which must be 0 (data) or 1 (grad)");
+    const float* src = t.data;
+    if (which == 1) {
+      need(t.grad != nullptr, TFB_ERR_STATE, "tensor has no gradient");
+      C.materialize_zero(t);
+      src = t.grad;
+    }
+    hip_check(hipMemcpyAsync(dst, src, (size_t)n * sizeof(float), hipMemcpyDeviceToHost, C.s()), "copy out");
+    hip_check(hipStreamSynchronize(C.s()), "sync");
+  });
+}
+
+int tfb_tensor_release(tfb_ctx* ctx, tfb_tensor h) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& t = C.T(h);
+    need(t.leaf, TFB_ERR_STATE, "op outputs are released by tfb_tape_reset");
+    for (const Rec& r : ctx->tape)
+      for (int i : r.in)
+        need(i != h, TFB_ERR_STATE, "tensor is still referenced by the tape");
+    // free the tail of the persistent region when possible
+    if (t.owns_persistent && t.persist_off + t.persist_bytes == ctx->arena.lo) ctx->arena.lo = t.persist_off;
+    t.live = false;
+    ctx->free_handles.push_back(h);
+  });
+}
+
+// ------------------------------------------------------------------ ops
+int tfb_add(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& A = C.T(a);
+    TensorRec& B = C.T(b);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    bool ok = B.ndim <= A.ndim;
+    for (int i = 0; ok && i < B.ndim; ++i) ok = A.shape[A.ndim - B.ndim + i] == B.shape[i];
+    need(ok, TFB_ERR_SHAPE, "add: " + shape_str(B) + " must equal the trailing dims of " + shape_str(A));
+    int h = C.make_output(shape_vec(A));
+    TensorRec& Y = ctx->tensors[h];
+    const float* ad = ctx->tensors[a].data;
+    const float* bd = ctx->tensors[b].data;
+    hip_check(add_bcast(ad, bd, Y.data, Y.numel, ctx->tensors[b].numel, C.s()), "add");
+    Rec r{OP_ADD};
+    r.in[0] = a, r.in[1] = b, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_mul(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& A = C.T(a);
+    TensorRec& B = C.T(b);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    need(A.numel == B.numel, TFB_ERR_SHAPE, "shapes differ: " + shape_str(A) + " " + shape_str(B));
+    int h = C.make_output(shape_vec(A));
+    hip_check(mul_fwd(ctx->tensors[a].data, ctx->tensors[b].data, ctx->tensors[h].data, ctx->tensors[h].numel, C.s()),
+              "mul");
+    Rec r{OP_MUL};
+    r.in[0] = a, r.in[1] = b, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_scale(tfb_ctx* ctx, tfb_tensor a, float sc, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& A = C.T(a);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    int h = C.make_output(shape_vec(A));
+    hip_check(scale_fwd(ctx->tensors[a].data, sc, ctx->tensors[h].data, ctx->tensors[h].numel, C.s()), "scale");
+    Rec r{OP_SCALE};
+    r.in[0] = a, r.out = h, r.f = sc;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_sum(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    C.T(a);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    int h = C.make_output({1});
+    size_t mark = ctx->arena.hi;
+    void* ws = C.scratch(sum_workspace_bytes(ctx->tensors[a].numel));
+    hip_check(sum_all(ctx->tensors[a].data, ctx->tensors[a].numel, ctx->tensors[h].data, ws, C.s()), "sum");
+    ctx->arena.hi = mark;
+    Rec r{OP_SUM};
+    r.in[0] = a, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_reshape(tfb_ctx* ctx, tfb_tensor a, const int64_t* shape, int ndim, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& A = C.T(a);
+    need(y != nullptr && shape != nullptr, TFB_ERR_ARG, "null argument");
+    int64_t n = Ctx::numel_of(shape, ndim);
+    need(n == A.numel, TFB_ERR_SHAPE, "reshape changes the size of " + shape_str(A));
+    float* data = A.data;
+    int h = C.new_handle();
+    TensorRec& t = ctx->tensors[h];
+    t.live = true;
+    t.leaf = false;
+    t.ndim = ndim;
+    for (int i = 0; i < ndim; ++i) t.shape[i] = shape[i];
+    t.numel = n;
+    t.data = data;  // a view of the same data
+    Rec r{OP_RESHAPE};
+    r.in[0] = a, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_tanh(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& A = C.T(a);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    int h = C.make_output(shape_vec(A));
+    hip_check(tanh_fwd(ctx->tensors[a].data, ctx->tensors[h].data, ctx->tensors[h].numel, C.s()), "tanh");
+    Rec r{OP_TANH};
+    r.in[0] = a, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& A = C.T(a);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    int h = C.make_output(shape_vec(A));
+    hip_check(gelu_fwd(ctx->tensors[a].data, ctx->tensors[h].data, ctx->tensors[h].numel, C.s()), "gelu");
+    Rec r{OP_GELU};
+    r.in[0] = a, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y, OpKind kind) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& X = C.T(x);
+    TensorRec& W = C.T(w);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    need(W.ndim == 2, TFB_ERR_SHAPE, "matmul weight must be 2-D, got " + shape_str(W));
+    const int64_t K = X.cols(), rows = X.rows();
+    int64_t N;
+    if (kind == OP_MATMUL_T) {
+      need(W.shape[1] == K, TFB_ERR_SHAPE, "matmul_t " + shape_str(X) + " @ " + shape_str(W) + "^T");
+      N = W.shape[0];
+    } else {
+      need(W.shape[0] == K, TFB_ERR_SHAPE, "matmul " + shape_str(X) + " @ " + shape_str(W));
+      N = W.shape[1];
+    }
+    const float* bias = nullptr;
+    if (kind == OP_LINEAR) {
+      TensorRec& Bv = C.T(b);
+      need(Bv.numel == N && Bv.ndim == 1, TFB_ERR_SHAPE, "linear bias must be [" + std::to_string(N) + "]");
+      bias = Bv.data;
+    }
+    check_gemm_dims(rows, K, N);
+    std::vector<int64_t> shp = shape_vec(X);
+    shp.back() = N;
+    int h = C.make_output(shp);
+    float* yd = ctx->tensors[h].data;
+    const float* xd = ctx->tensors[x].data;
+    const float* wd = ctx->tensors[w].data;
+    if (kind == OP_MATMUL_T)
+      gemm_nt(C, xd, wd, yd, rows, K, N, 0.f);
+    else
+      gemm_nn(C, xd, wd, yd, rows, K, N, 0.f, bias);
+    Rec r{kind};
+    r.in[0] = x, r.in[1] = w, r.in[2] = kind == OP_LINEAR ? b : -1, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_matmul(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y) {
+  return matmul_impl(ctx, x, w, -1, y, OP_MATMUL);
+}
+int tfb_matmul_t(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y) {
+  return matmul_impl(ctx, x, w, -1, y, OP_MATMUL_T);
+}
+int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y) {
+  return matmul_impl(ctx, x, w, b, y, OP_LINEAR);
+}
+
+int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& X = C.T(x);
+    TensorRec& G = C.T(gamma);
+    TensorRec& Bt = C.T(beta);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    const int64_t Cc = X.cols(), rows = X.rows();
+    need(G.numel == Cc && Bt.numel == Cc, TFB_ERR_SHAPE, "layernorm gain/shift must have " + std::to_string(Cc) +
+                                                             " elements");
+    need(Cc <= 2048, TFB_ERR_SHAPE, "layernorm rows longer than 2048 are not supported");
+    int h = C.make_output(shape_vec(X));
+    float* mean = static_cast<float*>(C.scratch((size_t)rows * sizeof(float)));
+    float* rstd = static_cast<float*>(C.scratch((size_t)rows * sizeof(float)));
+    hip_check(layernorm_fwd(ctx->tensors[x].data, ctx->tensors[gamma].data, ctx->tensors[beta].data,
+                            ctx->tensors[h].data, mean, rstd, rows, Cc, eps, C.s()),
+              "layernorm");
+    Rec r{OP_LAYERNORM};
+    r.in[0] = x, r.in[1] = gamma, r.in[2] = beta, r.out = h, r.f = eps;
+    r.s0 = mean, r.s1 = rstd;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_embedding(tfb_ctx* ctx, tfb_tensor table, const int32_t* dev_ids, int64_t n, int64_t batch, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& Tb = C.T(table);
+    need(y != nullptr && dev_ids != nullptr, TFB_ERR_ARG, "null argument");
+    need(Tb.ndim == 2, TFB_ERR_SHAPE, "embedding table must be 2-D");
+    need(n >= 0 && batch > 0 && n % batch == 0, TFB_ERR_SHAPE, "ids count must be a multiple of batch");
+    need(n < (1ll << 31), TFB_ERR_SHAPE, "too many ids");
+    const int64_t Cc = Tb.shape[1], trows = Tb.shape[0];
+    int h = C.make_output({batch, n / batch, Cc});
+    int32_t* ids = static_cast<int32_t*>(C.scratch((size_t)std::max<int64_t>(n, 1) * sizeof(int32_t)));
+    if (n)
+      hip_check(hipMemcpyAsync(ids, dev_ids, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToDevice, C.s()),
+                "copy ids");
+    hip_check(embedding_fwd(ctx->tensors[table].data, trows, ids, ctx->tensors[h].data, n, Cc, C.s()), "embedding");
+    Rec r{OP_EMBEDDING};
+    r.in[0] = table, r.out = h, r.i0 = n;
+    r.s0 = ids;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_narrow(tfb_ctx* ctx, tfb_tensor x, int64_t start, int64_t len, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& X = C.T(x);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    need(start >= 0 && len >= 0 && start + len <= X.cols(), TFB_ERR_SHAPE, "narrow out of range");
+    const int64_t rows = X.rows(), cols = X.cols();
+    std::vector<int64_t> shp = shape_vec(X);
+    shp.back() = len;
+    int h = C.make_output(shp);
+    hip_check(narrow_fwd(ctx->tensors[x].data, ctx->tensors[h].data, rows, cols, start, len, C.s()), "narrow");
+    Rec r{OP_NARROW};
+    r.in[0] = x, r.out = h, r.i0 = start, r.i1 = len;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_split_heads(tfb_ctx* ctx, tfb_tensor x, int heads, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& X = C.T(x);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    need(X.ndim == 3 && heads > 0 && X.shape[2] % heads == 0, TFB_ERR_SHAPE,
+         "split_heads needs [B, T, H*hs], got " + shape_str(X));
+    const int64_t B = X.shape[0], T = X.shape[1], hs = X.shape[2] / heads;
+    int h = C.make_output({B, heads, T, hs});
+    hip_check(permute_heads(ctx->tensors[x].data, ctx->tensors[h].data, B, T, heads, hs, true, 0.f, C.s()),
+              "split_heads");
+    Rec r{OP_SPLIT_HEADS};
+    r.in[0] = x, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_merge_heads(tfb_ctx* ctx, tfb_tensor x, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& X = C.T(x);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    need(X.ndim == 4, TFB_ERR_SHAPE, "merge_heads needs [B, H, T, hs], got " + shape_str(X));
+    const int64_t B = X.shape[0], H = X.shape[1], T = X.shape[2], hs = X.shape[3];
+    int h = C.make_output({B, T, H * hs});
+    hip_check(permute_heads(ctx->tensors[x].data, ctx->tensors[h].data, B, T, H, hs, false, 0.f, C.s()),
+              "merge_heads");
+    Rec r{OP_MERGE_HEADS};
+    r.in[0] = x, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+static int bmm_impl(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y, bool transb) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& A = C.T(a);
+    TensorRec& B = C.T(b);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    need(A.ndim == 3 && B.ndim == 3 && A.shape[0] == B.shape[0], TFB_ERR_SHAPE,
+         "batch_matmul needs [Z, n, k] and [Z, ., .]: " + shape_str(A) + " " + shape_str(B));
+    const int64_t Z = A.shape[0], n = A.shape[1], k = A.shape[2];
+    int64_t m;
+    if (transb) {
+      need(B.shape[2] == k, TFB_ERR_SHAPE, "batch_matmul_t " + shape_str(A) + " @ " + shape_str(B) + "^T");
+      m = B.shape[1];
+    } else {
+      need(B.shape[1] == k, TFB_ERR_SHAPE, "batch_matmul " + shape_str(A) + " @ " + shape_str(B));
+      m = B.shape[2];
+    }
+    check_gemm_dims(n, k, m);
+    int h = C.make_output({Z, n, m});
+    GemmArgs q = C.gemm_base();
+    q.M = (int)n, q.N = (int)m, q.K = (int)k;
+    q.A = ctx->tensors[a].data, q.lda = k, q.sa1 = n * k;
+    q.B = ctx->tensors[b].data;
+    if (transb)
+      q.ldb = k, q.b_kcontig = true, q.sb1 = m * k;
+    else
+      q.ldb = m, q.sb1 = k * m;
+    q.C = ctx->tensors[h].data, q.ldc = m, q.sc1 = n * m;
+    q.batch = (int)Z;
+    C.run_gemm(q);
+    Rec r{transb ? OP_BMM_T : OP_BMM};
+    r.in[0] = a, r.in[1] = b, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_batch_matmul(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y) { return bmm_impl(ctx, a, b, y, false); }
+int tfb_batch_matmul_t(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y) { return bmm_impl(ctx, a, b, y, true); }
+
+int tfb_causal_softmax(tfb_ctx* ctx, tfb_tensor sx, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& S = C.T(sx);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    const int64_t rows = S.rows(), T = S.cols();
+    int h = C.make_output(shape_vec(S));
+    hip_check(causal_softmax_fwd(ctx->tensors[sx].data, ctx->tensors[h].data, rows, T, true, C.s()),
+              "causal_softmax");
+    Rec r{OP_CSOFTMAX};
+    r.in[0] = sx, r.out = h;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& Q = C.T(qkv);
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    need(Q.ndim == 3 && Q.shape[2] % 3 == 0 && heads > 0 && (Q.shape[2] / 3) % heads == 0, TFB_ERR_SHAPE,
+         "causal_attention needs qkv [B, T, 3C] with C divisible by heads, got " + shape_str(Q));
+    const int64_t B = Q.shape[0], T = Q.shape[1], C3 = Q.shape[2], Cc = C3 / 3, H = heads, hs = Cc / H;
+    check_gemm_dims(T, T, hs);
+    need(B * H < 65536, TFB_ERR_SHAPE, "too many (batch, head) pairs");
+    const float scale = 1.f / std::sqrt((float)hs);
+    int h = C.make_output({B, T, Cc});
+    float* P = static_cast<float*>(C.scratch((size_t)B * H * T * T * sizeof(float)));
+    const float* q = ctx->tensors[qkv].data;
+    float* yd = ctx->tensors[h].data;
+    {  // S = (Q_h K_h^T) * scale, tiles on or below the diagonal
+      GemmArgs a = C.gemm_base();
+      a.M = (int)T, a.N = (int)T, a.K = (int)hs;
+      a.A = q, a.lda = C3, a.sa1 = T * C3, a.sa2 = hs;
+      a.B = q + Cc, a.ldb = C3, a.b_kcontig = true, a.sb1 = T * C3, a.sb2 = hs;
+      a.C = P, a.ldc = T, a.sc1 = H * T * T, a.sc2 = T * T;
+      a.alpha = scale, a.batch = (int)(B * H), a.batch_div = (int)H;
+      a.causal_out = true;
+      C.run_gemm(a);
+    }
+    hip_check(causal_softmax_fwd(P, P, B * H * T, T, false, C.s()), "attention softmax");
+    {  // Y_h = P V_h, written straight into the merged [B, T, C] layout
+      GemmArgs a = C.gemm_base();
+      a.M = (int)T, a.N = (int)hs, a.K = (int)T;
+      a.A = P, a.lda = T, a.sa1 = H * T * T, a.sa2 = T * T, a.causal_a = CAUSAL_UPTO;
+      a.B = q + 2 * Cc, a.ldb = C3, a.sb1 = T * C3, a.sb2 = hs;
+      a.C = yd, a.ldc = Cc, a.sc1 = T * Cc, a.sc2 = hs;
+      a.batch = (int)(B * H), a.batch_div = (int)H;
+      C.run_gemm(a);
+    }
+    Rec r{OP_ATTENTION};
+    r.in[0] = qkv, r.out = h, r.i0 = H, r.f = scale;
+    r.s0 = P;
+    C.record(r);
+    *y = h;
+  });
+}
+
+int tfb_softmax_cross_entropy(tfb_ctx* ctx, tfb_tensor logits, const int32_t* dev_targets, int64_t n,
+                              tfb_tensor* loss) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& L = C.T(logits);
+    need(loss != nullptr && dev_targets != nullptr, TFB_ERR_ARG, "null argument");
+    need(n == L.rows(), TFB_ERR_SHAPE, "one target per row");
+    const int64_t rows = L.rows(), V = L.cols();
+    int h = C.make_output({1});
+    int32_t* tg = static_cast<int32_t*>(C.scratch((size_t)std::max<int64_t>(rows, 1) * sizeof(int32_t)));
+    float* lse = static_cast<float*>(C.scratch((size_t)std::max<int64_t>(rows, 1) * sizeof(float)));
+    if (rows)
+      hip_check(hipMemcpyAsync(tg, dev_targets, (size_t)rows * sizeof(int32_t), hipMemcpyDeviceToDevice, C.s()),
+                "copy targets");
+    size_t mark = ctx->arena.hi;
+    void* ws = C.scratch(softmax_ce_workspace_bytes(rows));
+    hip_check(softmax_ce_fwd(ctx->tensors[logits].data, tg, rows, V, lse, ctx->tensors[h].data, ws, C.s()),
+              "softmax_ce");
+    ctx->arena.hi = mark;
+    Rec r{OP_SOFTMAX_CE};
+    r.in[0] = logits, r.out = h;
+    r.s0 = tg, r.s1 = lse;
+    C.record(r);
+    *loss = h;
+  });
+}
+
+// ------------------------------------------------------------------ autograd
+int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& L = C.T(loss);
+    need(L.numel == 1, TFB_ERR_STATE, "backward() starts from a scalar loss");
+    for (TensorRec& t : ctx->tensors)
+      if (t.live && !t.leaf && t.grad) t.gstate = G_ZERO;
+    C.ensure_grad_buffer(L);
+    hip_check(fill(L.grad, 1.f, 1, C.s()), "seed");
+    L.gstate = G_VALID;
+    for (int i = (int)ctx->tape.size() - 1; i >= 0; --i) {
+      const Rec& r = ctx->tape[i];
+      TensorRec& out = ctx->tensors[r.out];
+      if (!out.live || out.gstate != G_VALID) continue;
+      backward_rec(C, r);
+    }
+  });
+}
+
+int tfb_zero_grad(tfb_ctx* ctx, const tfb_tensor* params, int n) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need(n == 0 || params != nullptr, TFB_ERR_ARG, "null parameter list");
+    for (int i = 0; i < n; ++i) {
+      TensorRec& t = C.T(params[i]);
+      if (t.grad) t.gstate = G_ZERO;
+    }
+  });
+}
+
+int tfb_tape_reset(tfb_ctx* ctx) {
+  return guarded([&] {
+    Ctx C(ctx);
+    ctx->tape.clear();
+    for (int h = 0; h < (int)ctx->tensors.size(); ++h) {
+      TensorRec& t = ctx->tensors[h];
+      if (t.live && !t.leaf) {
+        t.live = false;
+        ctx->free_handles.push_back(h);
+      }
+    }
+    ctx->arena.hi = ctx->arena.size;
+  });
+}
+
+// ------------------------------------------------------------------ optimizers
+int tfb_adamw_create(tfb_ctx* ctx, const tfb_tensor* params, int n, float lr, float weight_decay, float beta1,
+                     float beta2, float eps, tfb_opt** out) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need(out != nullptr && (n == 0 || params != nullptr), TFB_ERR_ARG, "null argument");
+    tfb_opt* o = new tfb_opt();
+    o->ctx = ctx;
+    o->lr = lr, o->wd = weight_decay, o->b1 = beta1, o->b2 = beta2, o->eps = eps;
+    try {
+      int64_t nchunks = 0;
+      for (int i = 0; i < n; ++i) {
+        TensorRec& t = C.T(params[i]);
+        o->params.push_back(params[i]);
+        size_t mo = ctx->arena.alloc_persist((size_t)t.numel * sizeof(float));
+        size_t vo = ctx->arena.alloc_persist((size_t)t.numel * sizeof(float));
+        o->m.push_back(reinterpret_cast<float*>(ctx->arena.base + mo));
+        o->v.push_back(reinterpret_cast<float*>(ctx->arena.base + vo));
+        hip_check(fill(o->m.back(), 0.f, t.numel, C.s()), "zero m");
+        hip_check(fill(o->v.back(), 0.f, t.numel, C.s()), "zero v");
+        nchunks += (t.numel + o->chunk_elems - 1) / o->chunk_elems;
+      }
+      o->d_nseg_cap = std::max(n, 1);
+      o->d_nchunk_cap = (int)std::max<int64_t>(nchunks, 1);
+      o->d_segs = reinterpret_cast<AdamSeg*>(ctx->arena.base +
+                                             ctx->arena.alloc_persist(sizeof(AdamSeg) * o->d_nseg_cap));
+      o->d_chunks = reinterpret_cast<AdamChunk*>(ctx->arena.base +
+                                                 ctx->arena.alloc_persist(sizeof(AdamChunk) * o->d_nchunk_cap));
+    } catch (...) {
+      delete o;
+      throw;
+    }
+    *out = o;
+  });
+}
+
+int tfb_adamw_set_lr(tfb_opt* opt, float lr) {
+  return guarded([&] {
+    need(opt != nullptr, TFB_ERR_ARG, "null optimizer");
+    opt->lr = lr;
+  });
+}
+
+int tfb_adamw_step(tfb_opt* o) {
+  return guarded([&] {
+    need(o != nullptr, TFB_ERR_ARG, "null optimizer");
+    Ctx C(o->ctx);
+    tfb_ctx* ctx = o->ctx;
+    // parameters without a gradient are skipped; a cleared gradient reads as zeros
+    std::vector<int> active;
+    for (int i = 0; i < (int)o->params.size(); ++i) {
+      TensorRec& t = C.T(o->params[i]);
+      if (!t.grad) continue;
+      C.materialize_zero(t);
+      active.push_back(i);
+    }
+    o->t += 1;
+    const float bc1 = 1.f - std::pow(o->b1, (float)o->t);
+    const float bc2 = 1.f - std::pow(o->b2, (float)o->t);
+    if (active != o->uploaded_active) {
+      std::vector<AdamSeg> segs;
+      std::vector<AdamChunk> chunks;
+      for (int i : active) {
+        TensorRec& t = C.T(o->params[i]);
+        AdamSeg sg;
+        sg.p = t.data, sg.g = t.grad, sg.m = o->m[i], sg.v = o->v[i], sg.n = t.numel;
+        sg.wd = t.ndim >= 2 ? o->wd : 0.f;
+        sg.pad = 0;
+        for (int64_t off = 0; off < t.numel; off += o->chunk_elems) {
+          AdamChunk ch;
+          ch.seg = (int)segs.size(), ch.pad = 0, ch.off = off;
+          chunks.push_back(ch);
+        }
+        segs.push_back(sg);
+      }
+      if (!segs.empty()) {
+        hip_check(hipMemcpyAsync(o->d_segs, segs.data(), segs.size() * sizeof(AdamSeg), hipMemcpyHostToDevice, C.s()),
+                  "upload segments");
+        hip_check(hipMemcpyAsync(o->d_chunks, chunks.data(), chunks.size() * sizeof(AdamChunk),
+                                 hipMemcpyHostToDevice, C.s()),
+                  "upload chunks");
+        hip_check(hipStreamSynchronize(C.s()), "sync");
+      }
+      o->nchunks = (int)chunks.size();
+      o->uploaded_active = active;
+    }
+    (void)ctx;
+    hip_check(adamw_step(o->d_segs, o->d_chunks, o->nchunks, o->chunk_elems, o->lr, o->b1, o->b2, o->eps, bc1, bc2,
+                         C.s()),
+              "adamw");
+  });
+}
+
+int tfb_adamw_moments(tfb_opt* o, int i, float* host_m, float* host_v, int64_t n) {
+  return guarded([&] {
+    need(o != nullptr, TFB_ERR_ARG, "null optimizer");
+    Ctx C(o->ctx);
+    need(i >= 0 && i < (int)o->params.size(), TFB_ERR_ARG, "no such parameter");
+    TensorRec& t = C.T(o->params[i]);
+    need(n == t.numel, TFB_ERR_SHAPE, "size mismatch");
+    if (host_m)
+      hip_check(hipMemcpyAsync(host_m, o->m[i], n * sizeof(float), hipMemcpyDeviceToHost, C.s()), "copy m");
+    if (host_v)
+      hip_check(hipMemcpyAsync(host_v, o->v[i], n * sizeof(float), hipMemcpyDeviceToHost, C.s()), "copy v");
+    hip_check(hipStreamSynchronize(C.s()), "sync");
+  });
+}
+
+int tfb_adamw_destroy(tfb_opt* o) {
+  return guarded([&] {
+    need(o != nullptr, TFB_ERR_ARG, "null optimizer");
+    delete o;
+  });
+}
+
+int tfb_profile_begin(tfb_ctx* ctx) {
+  return guarded([&] {
+    Ctx C(ctx);
+    ProfileState& pf = ctx->prof;
+    pf.on = true;
+    pf.used = 0;
+    pf.flops = 0.0;
+    pf.launches = 0;
+  });
+}
+
+int tfb_profile_end(tfb_ctx* ctx, double* gemm_ms, double* gemm_flops, int* launches) {
+  return guarded([&] {
+    Ctx C(ctx);
+    ProfileState& pf = ctx->prof;
+    need(pf.on, TFB_ERR_STATE, "profiling was not started");
+    pf.on = false;
+    hip_check(hipStreamSynchronize(C.s()), "sync");
+    double ms = 0.0;
+    for (int i = 0; i + 1 < pf.used; i += 2) {
+      float e = 0.f;
+      hip_check(hipEventElapsedTime(&e, pf.pool[i], pf.pool[i + 1]), "hipEventElapsedTime");
+      ms += e;
+    }
+    if (gemm_ms) *gemm_ms = ms;
+    if (gemm_flops) *gemm_flops = pf.flops;
+    if (launches) *launches = pf.launches;
+  });
+}
+
+int tfb_sgd_step(tfb_ctx* ctx, const tfb_tensor* params, int n, float lr) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need(n == 0 || params != nullptr, TFB_ERR_ARG, "null parameter list");
+    for (int i = 0; i < n; ++i) {
+      TensorRec& t = C.T(params[i]);
+      if (!t.grad) continue;
+      C.materialize_zero(t);
+      hip_check(sgd_step(t.data, t.grad, lr, t.numel, C.s()), "sgd");
+    }
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+"""The workloads composed from libtfb ops: tiny MLP, char-level MLP and the GPT.
+
+Composition follows the pages ([Autograd-1, "Training loop": Linear = MatMul +
+bias Add, Tanh, SoftmaxCrossEntropy; GPT2-4, "Loading the weights" and
+"Generation with KV cache": token + position embedding, pre-LN blocks with a
+fused c_attn [C, 3C], MLP C -> 4C -> C with GELU, ln_f, the LM head tied to
+wte).  Linear is the fused MatMul+bias op and the attention core is the single
+tfb_causal_attention op; both compute exactly the pages' op sequence.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Sequence
+
+import numpy as np
+
+from . import (AdamW, Context, Tensor, add, causal_attention, embedding, gelu, layernorm, linear, matmul_t, reshape,
+               softmax_cross_entropy, tanh)
+
+
+def upload_params(ctx: Context, params: Dict[str, np.ndarray]) -> Dict[str, Tensor]:
+    return {k: ctx.tensor(v.shape, v, param=True) for k, v in params.items()}
+
+
+class Gpt:
+    def __init__(self, ctx: Context, n_layer: int, n_head: int, params: Dict[str, np.ndarray]):
+        self.ctx = ctx
+        self.n_layer, self.n_head = n_layer, n_head
+        self.P = upload_params(ctx, params)
+        self.names = list(params.keys())
+        self._pos = {}
+
+    @property
+    def param_list(self) -> List[Tensor]:
+        return [self.P[k] for k in self.names]
+
+    def positions(self, T: int):
+        if T not in self._pos:
+            import torch
+            self._pos[T] = torch.arange(T, dtype=torch.int32, device=f"cuda:{self.ctx.device}")
+        return self._pos[T]
+
+    def logits(self, ids) -> Tensor:
+        """ids: [B, T] int32 (numpy or a device torch tensor)."""
+        P = self.P
+        B, T = ids.shape
+        C = P["wte.weight"].shape[1]
+        tok = embedding(P["wte.weight"], ids, B)                          # [B, T, C]
+        pos = reshape(embedding(P["wpe.weight"], self.positions(T), 1), (T, C))
+        x = add(tok, pos)
+        for i in range(self.n_layer):
+            p = f"h.{i}."
+            h = layernorm(x, P[p + "ln_1.weight"], P[p + "ln_1.bias"])
+            qkv = linear(h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"])
+            a = causal_attention(qkv, self.n_head)
+            x = add(x, linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"]))
+            h = layernorm(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"])
+            f = gelu(linear(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"]))
+            x = add(x, linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"]))
+        xf = layernorm(x, P["ln_f.weight"], P["ln_f.bias"])
+        return matmul_t(xf, P["wte.weight"])
+
+    def loss(self, inputs, targets):
+        logits = self.logits(inputs)
+        return softmax_cross_entropy(logits, targets), logits
+
+
+def split_ids(ids_full):
+    """[B, T+1] -> inputs [B, T], targets [B*T] (works for numpy and torch)."""
+    inputs = ids_full[:, :-1]
+    targets = ids_full[:, 1:]
+    if hasattr(inputs, "contiguous"):
+        return inputs.contiguous(), targets.contiguous().reshape(-1)
+    return np.ascontiguousarray(inputs), np.ascontiguousarray(targets).reshape(-1)
+
+
+def train_step(model: Gpt, opt: AdamW, inputs, targets, read_loss: bool = True):
+    """One fwd + backward + AdamW step; returns the loss (or None)."""
+    ctx = model.ctx
+    loss, _ = model.loss(inputs, targets)
+    opt.zero_grad()
+    ctx.backward(loss)
+    opt.step()
+    val = loss.item() if read_loss else None
+    ctx.tape_reset()
+    return val
+
+
+class TinyMlp:
+    """Linear 16->32 tanh -> 32->32 tanh -> 32->4."""
+
+    def __init__(self, ctx: Context, params: Dict[str, np.ndarray]):
+        self.ctx = ctx
+        self.P = upload_params(ctx, params)
+        self.names = list(params.keys())
+
+    @property
+    def param_list(self):
+        return [self.P[k] for k in self.names]
+
+    def loss(self, x: Tensor, y):
+        P = self.P
+        h = tanh(linear(x, P["w1"], P["b1"]))
+        h = tanh(linear(h, P["w2"], P["b2"]))
+        logits = linear(h, P["w3"], P["b3"])
+        return softmax_cross_entropy(logits, y), logits
+
+
+class CharMlp:
+    """Embedding 64x24 of 8 context ids, concatenated to 192 -> 256 tanh -> 64."""
+
+    def __init__(self, ctx: Context, params: Dict[str, np.ndarray]):
+        self.ctx = ctx
+        self.P = upload_params(ctx, params)
+        self.names = list(params.keys())
+
+    @property
+    def param_list(self):
+        return [self.P[k] for k in self.names]
+
+    def loss(self, ctx_ids, target):
+        P = self.P
+        B, K = ctx_ids.shape
+        emb = embedding(P["emb"], ctx_ids, B)
+        x = reshape(emb, (B, K * P["emb"].shape[1]))
+        h = tanh(linear(x, P["w1"], P["b1"]))
+        logits = linear(h, P["w2"], P["b2"])
+        return softmax_cross_entropy(logits, target), logits
