@@ -309,3 +309,37 @@ def test_sgd(ctx):
     ctx.tape_reset()
     w.release()
     g.release()
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_lm_head_with_padded_rows(ctx, prec):
+    """A vocabulary-sized LM head (V not a multiple of 64) stores its rows
+    padded; the cross-entropy reads them in place and every gradient matches."""
+    V, C, rows = 1030, 64, 300
+    x, w = rnd(41, (rows, C)), rnd(42, (V, C), 0.2)
+    tg = S.random_ids(43, (rows,), V)
+    ctx.set_precision(prec)
+    xt, wt = ctx.tensor(x.shape, x), ctx.tensor(w.shape, w)
+    logits = T.matmul_t(xt, wt)
+    loss = T.softmax_cross_entropy(logits, tg)
+    ctx.backward(loss)
+    ox, ow = E.Tensor(x.astype(np.float64)), E.Tensor(w.astype(np.float64))
+    ol = E.matmul_t(ox, ow)
+    oloss = E.softmax_cross_entropy(ol, tg)
+    oloss.backward()
+    tol_f, tol_g = FWD_TOL[prec], GRAD_TOL[prec]
+    assert_close(logits.numpy(), ol.data, tol_f, "logits")
+    assert abs(loss.item() - oloss.item()) / abs(oloss.item()) <= tol_f
+    assert_close(logits.grad(), ol.grad, tol_g, "dlogits")
+    assert_close(xt.grad(), ox.grad, tol_g, "dx")
+    assert_close(wt.grad(), ow.grad, tol_g, "dw")
+    ctx.tape_reset()
+    xt.release()
+    wt.release()
+    ctx.set_precision("fp32")
+
+
+def test_padded_output_feeds_other_ops(ctx):
+    """Another op consuming a padded LM-head output gets a recorded dense copy."""
+    check(ctx, "fp32", lambda x, w: T.tanh(T.matmul_t(x, w)), lambda x, w: E.tanh(E.matmul_t(x, w)),
+          [rnd(44, (70, 32)), rnd(45, (1100, 32), 0.2)], (70, 1100))

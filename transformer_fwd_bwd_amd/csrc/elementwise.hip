@@ -29,6 +29,24 @@ __global__ void map1(int64_t n, F f) {
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) f(i);
 }
 
+__global__ void to_bf16_k(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    const __bf16 b = (__bf16)src[i];
+    dst[i] = __builtin_bit_cast(uint16_t, b);
+  }
+}
+
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+__global__ void to_bf16_4_k(const f4* __restrict__ src, u16x4* __restrict__ dst, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n4; i += (int64_t)gridDim.x * NT) {
+    const f4 v = src[i];
+    u16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+    dst[i] = o;
+  }
+}
+
 __global__ void fill_k(float* p, float v, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) p[i] = v;
 }
@@ -66,16 +84,23 @@ __device__ __forceinline__ float gelu_grad(float x) {
   return 0.5f * (1.f + t) + 0.5f * x * (1.f - t * t) * c * (1.f + 3.f * 0.044715f * x * x);
 }
 
-// out of one block: partial[blockIdx.y * cols + c] = sum of rows in the block's row range
+// partial[blockIdx.y * cols + c] = sum of the rows in slab blockIdx.y (4 independent loads in flight)
 __global__ void colsum_stage1(const float* __restrict__ g, int64_t rows, int64_t cols, int64_t rows_per,
                               float* __restrict__ partial) {
   const int64_t c = (int64_t)blockIdx.x * NT + threadIdx.x;
   if (c >= cols) return;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per;
   const int64_t r1 = std::min(rows, r0 + rows_per);
-  float s = 0.f;
-  for (int64_t r = r0; r < r1; ++r) s += g[r * cols + c];
-  partial[(int64_t)blockIdx.y * cols + c] = s;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    s0 += g[r * cols + c];
+    s1 += g[(r + 1) * cols + c];
+    s2 += g[(r + 2) * cols + c];
+    s3 += g[(r + 3) * cols + c];
+  }
+  for (; r < r1; ++r) s0 += g[r * cols + c];
+  partial[(int64_t)blockIdx.y * cols + c] = (s0 + s1) + (s2 + s3);
 }
 
 __global__ void colsum_stage2(const float* __restrict__ partial, int nparts, int64_t cols, float* __restrict__ out,
@@ -125,6 +150,15 @@ hipError_t fill(float* p, float v, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4 == 0 && aligned16(src) && (reinterpret_cast<uintptr_t>(dst) & 7) == 0)
+    hipLaunchKernelGGL(to_bf16_4_k, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, (const f4*)src, (u16x4*)dst, n / 4);
+  else
+    hipLaunchKernelGGL(to_bf16_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
 hipError_t add_bcast(const float* a, const float* b, float* y, int64_t n, int64_t nb, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (nb % 4 == 0 && aligned16(a) && aligned16(b) && aligned16(y))
@@ -138,6 +172,20 @@ hipError_t add_bcast(const float* a, const float* b, float* y, int64_t n, int64_
 hipError_t axpby(float* dst, const float* src, float alpha, float beta, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(axpby_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, dst, src, alpha, beta, n);
+  return hipGetLastError();
+}
+
+hipError_t copy_pitched(const float* src, int64_t lds, float* dst, int64_t ldd, int64_t rows, int64_t cols,
+                        float beta, hipStream_t s) {
+  const int64_t n = rows * cols;
+  if (n <= 0) return hipSuccess;
+  auto f = [=] __device__(int64_t i) {
+    const int64_t r = i / cols, c = i % cols;
+    float v = src[r * lds + c];
+    if (beta != 0.f) v += dst[r * ldd + c];
+    dst[r * ldd + c] = v;
+  };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
@@ -227,14 +275,22 @@ hipError_t gelu_bwd(const float* g, const float* x, float* d, float beta, int64_
   return hipGetLastError();
 }
 
+static int64_t colsum_parts(int64_t rows, int64_t cols) {
+  // enough row slabs to put ~2048 waves in flight, each slab at least 16 rows
+  const int64_t col_blocks = (cols + NT - 1) / NT;
+  int64_t parts = std::max<int64_t>(1, 512 / std::max<int64_t>(col_blocks, 1));
+  parts = std::min<int64_t>(parts, std::max<int64_t>(1, rows / 16));
+  return std::min<int64_t>(parts, 256);
+}
+
 size_t colsum_workspace_bytes(int64_t rows, int64_t cols) {
-  const int64_t parts = std::min<int64_t>(64, std::max<int64_t>(1, rows / 64));
-  return (size_t)parts * cols * sizeof(float);
+  return (size_t)colsum_parts(rows, cols) * cols * sizeof(float);
 }
 
 hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s) {
   if (cols <= 0) return hipSuccess;
-  const int64_t parts = std::min<int64_t>(64, std::max<int64_t>(1, rows / 64));
+  if (rows == 1) return axpby(out, g, 1.f, beta, cols, s);
+  const int64_t parts = colsum_parts(rows, cols);
   const int64_t rows_per = (rows + parts - 1) / parts;
   float* partial = static_cast<float*>(ws);
   dim3 g1((unsigned)((cols + NT - 1) / NT), (unsigned)parts);

@@ -6,17 +6,21 @@
 //   NN  A(m,k) k-contiguous, B(k,n) n-contiguous   (forward x @ w, dx of MatMulT)
 //   NT  A k-contiguous,      B(k,n) k-contiguous   (x @ w^T, dx = g @ w^T, q k^T)
 //   TN  A(m,k) m-contiguous, B n-contiguous        (dw = x^T @ g, P^T @ dO)
-// A workgroup of WM x WN waves computes a (WM*TM*32) x (WN*TN*32) tile of C;
-// each wave owns TM x TN blocks of 32x32 accumulated by v_mfma_f32_32x32x16_bf16
-// (bf16 operands) or v_mfma_f32_32x32x2_f32 (fp32 operands), fp32 accumulation.
-// Both operands are staged through LDS as [row][k] with k contiguous, so every
-// lane reads its MFMA fragment as one 16-byte LDS load; an m- or n-contiguous
-// operand is transposed in 4x4 register micro-blocks on the way in.  The next
-// k-tile is fetched into registers while the current one is multiplied (two
-// LDS buffers, one barrier per k-tile).  Out-of-range rows and k are staged as
-// zeros; fp32 inputs are rounded to bf16 (nearest even) while staging when the
-// bf16 variant runs.
+// A workgroup of WM x WN wavefronts computes a BM x BN tile of C; each wave owns
+// TM x TN blocks of 32x32 accumulated by v_mfma_f32_32x32x16_bf16 (bf16
+// operands) or v_mfma_f32_32x32x2_f32 (fp32 operands), fp32 accumulation.
+// Operands are staged through LDS as [row][k] with k contiguous, so a lane reads
+// its MFMA fragment with one 16-byte LDS load; an m- or n-contiguous operand is
+// transposed in small register blocks on the way in.  Operands may be stored
+// as fp32 (rounded to bf16, nearest even, while staging in the bf16 variant) or
+// already as bf16.  The next k-tile is fetched into registers while the current
+// one is multiplied (two LDS buffers, one barrier per k-tile).
+//
+// Workgroups are numbered so that each of the 8 XCDs (dispatched round-robin)
+// gets a contiguous run of output tiles: neighbouring tiles share A rows and
+// B columns through that XCD's L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -28,23 +32,23 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 32;
+constexpr int KALIGN = 32;  // split-K chunks are multiples of this (and of every k-tile depth)
 
-template <bool BF16>
+template <bool BF16, int BK>
 struct Lds;
-template <>
-struct Lds<true> {
+template <int BK>
+struct Lds<true, BK> {
   using T = bf16_t;
-  static constexpr int LDK = BK + 8;  // 80-byte rows
+  static constexpr int LDK = BK + 8;  // rows padded by 16 bytes: conflict-free 16-byte fragment reads
 };
-template <>
-struct Lds<false> {
+template <int BK>
+struct Lds<false, BK> {
   using T = float;
-  static constexpr int LDK = BK + 4;  // 144-byte rows
+  static constexpr int LDK = BK + 4;
 };
-
-__device__ __forceinline__ f4 load4(const float* p) { return *reinterpret_cast<const f4*>(p); }
 
 __device__ __forceinline__ float mask_causal(float v, int causal, int m, int k) {
   if (causal == CAUSAL_UPTO && k > m) return 0.f;
@@ -52,89 +56,177 @@ __device__ __forceinline__ float mask_causal(float v, int causal, int m, int k) 
   return v;
 }
 
-// Registers holding one thread's share of an R_TILE x BK operand tile.
-template <int R_TILE, int NT, bool RCONTIG>
-struct Stage {
-  // k-contiguous: chunks of 4 consecutive k of one row
-  // r-contiguous: 4x4 micro-blocks (4 rows x 4 k), held as 4 r-vectors
-  static constexpr int UNITS = RCONTIG ? R_TILE * BK / 16 : R_TILE * BK / 4;
-  static constexpr int PER = (UNITS + NT - 1) / NT;
-  static constexpr int REGS = RCONTIG ? PER * 4 : PER;
-  f4 r[REGS];
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
 
-  __device__ __forceinline__ void load(const float* __restrict__ P, int64_t ld, int r0, int k0, int R, int K,
+// One thread's share of an R_TILE x BK operand tile held in registers.
+//   SRC_BF16 = false: fp32 source; k-contiguous units are 4 k of one row,
+//                     r-contiguous units are 4 rows x 4 k (four 16-byte loads)
+//   SRC_BF16 = true:  bf16 source; k-contiguous units are 8 k of one row (16 B),
+//                     r-contiguous units are 4 rows x 8 k (eight 8-byte loads)
+template <int R_TILE, int NT, bool RCONTIG, bool SRC_BF16, int BK>
+struct Stage {
+  static constexpr int UK = SRC_BF16 ? 8 : 4;   // k per unit
+  static constexpr int UR = RCONTIG ? 4 : 1;    // rows per unit
+  static constexpr int UNITS = R_TILE * BK / (UK * UR);
+  static constexpr int PER = (UNITS + NT - 1) / NT;
+  // fp32: f4 per (unit, k-row of the block); bf16: raw 16-bit lanes
+  static constexpr int REGS = SRC_BF16 ? (RCONTIG ? PER * 8 : PER) : (RCONTIG ? PER * 4 : PER);
+  using R = typename std::conditional<SRC_BF16, typename std::conditional<RCONTIG, u16x4, u16x8>::type, f4>::type;
+  R r[REGS];
+
+  __device__ __forceinline__ void load(const void* __restrict__ Pv, int64_t ld, int r0, int k0, int R_, int K,
                                        bool vec, int causal, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int u = tid + i * NT;
       if (UNITS % NT != 0 && u >= UNITS) break;
       if constexpr (!RCONTIG) {
-        const int rr = u / (BK / 4), kq = u % (BK / 4);
-        const int gr = r0 + rr, gk = k0 + kq * 4;
-        f4 v = {0.f, 0.f, 0.f, 0.f};
-        if (gr < R) {
-          const float* src = P + (int64_t)gr * ld + gk;
-          if (vec && gk + 3 < K) {
-            v = load4(src);
-          } else {
+        const int rr = u / (BK / UK), kq = u % (BK / UK);
+        const int gr = r0 + rr, gk = k0 + kq * UK;
+        if constexpr (!SRC_BF16) {
+          const float* P = static_cast<const float*>(Pv);
+          f4 v = {0.f, 0.f, 0.f, 0.f};
+          if (gr < R_) {
+            const float* src = P + (int64_t)gr * ld + gk;
+            if (vec && gk + 3 < K) {
+              v = *reinterpret_cast<const f4*>(src);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (gk + e < K) ? src[e] : 0.f;
-          }
-          if (causal != CAUSAL_NONE) {
+              for (int e = 0; e < 4; ++e) v[e] = (gk + e < K) ? src[e] : 0.f;
+            }
+            if (causal != CAUSAL_NONE) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = mask_causal(v[e], causal, gr, gk + e);
+              for (int e = 0; e < 4; ++e) v[e] = mask_causal(v[e], causal, gr, gk + e);
+            }
           }
+          r[i] = v;
+        } else {
+          const unsigned short* P = static_cast<const unsigned short*>(Pv);
+          u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+          if (gr < R_) {
+            const unsigned short* src = P + (int64_t)gr * ld + gk;
+            if (vec && gk + 7 < K) {
+              v = *reinterpret_cast<const u16x8*>(src);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] = (gk + e < K) ? src[e] : (unsigned short)0;
+            }
+            if (causal != CAUSAL_NONE) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if ((causal == CAUSAL_UPTO && gk + e > gr) || (causal == CAUSAL_FROM && gk + e < gr)) v[e] = 0;
+            }
+          }
+          r[i] = v;
         }
-        r[i] = v;
       } else {
         const int rq = u % (R_TILE / 4), kq = u / (R_TILE / 4);
         const int gr = r0 + rq * 4;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int gk = k0 + kq * 4 + kk;
-          f4 v = {0.f, 0.f, 0.f, 0.f};
-          if (gk < K) {
-            const float* src = P + (int64_t)gk * ld + gr;
-            if (vec && gr + 3 < R) {
-              v = load4(src);
-            } else {
+        for (int kk = 0; kk < UK; ++kk) {
+          const int gk = k0 + kq * UK + kk;
+          if constexpr (!SRC_BF16) {
+            const float* P = static_cast<const float*>(Pv);
+            f4 v = {0.f, 0.f, 0.f, 0.f};
+            if (gk < K) {
+              const float* src = P + (int64_t)gk * ld + gr;
+              if (vec && gr + 3 < R_) {
+                v = *reinterpret_cast<const f4*>(src);
+              } else {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = (gr + e < R) ? src[e] : 0.f;
-            }
-            if (causal != CAUSAL_NONE) {
+                for (int e = 0; e < 4; ++e) v[e] = (gr + e < R_) ? src[e] : 0.f;
+              }
+              if (causal != CAUSAL_NONE) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = mask_causal(v[e], causal, gr + e, gk);
+                for (int e = 0; e < 4; ++e) v[e] = mask_causal(v[e], causal, gr + e, gk);
+              }
             }
+            r[i * 4 + kk] = v;
+          } else {
+            const unsigned short* P = static_cast<const unsigned short*>(Pv);
+            u16x4 v = {0, 0, 0, 0};
+            if (gk < K) {
+              const unsigned short* src = P + (int64_t)gk * ld + gr;
+              if (vec && gr + 3 < R_) {
+                v = *reinterpret_cast<const u16x4*>(src);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (gr + e < R_) ? src[e] : (unsigned short)0;
+              }
+              if (causal != CAUSAL_NONE) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if ((causal == CAUSAL_UPTO && gk > gr + e) || (causal == CAUSAL_FROM && gk < gr + e)) v[e] = 0;
+              }
+            }
+            r[i * 8 + kk] = v;
           }
-          r[i * 4 + kk] = v;
         }
       }
     }
   }
 
-  template <bool BF16>
-  __device__ __forceinline__ void store(typename Lds<BF16>::T* L, int tid) const {
-    constexpr int LDK = Lds<BF16>::LDK;
+  // Interior tile: every element of the R_TILE x BK block is in range, the
+  // rows are 16-byte aligned and no causal mask applies -- straight-line loads.
+  __device__ __forceinline__ void load_fast(const void* __restrict__ Pv, int64_t ld, int r0, int k0, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int u = tid + i * NT;
       if (UNITS % NT != 0 && u >= UNITS) break;
       if constexpr (!RCONTIG) {
-        const int rr = u / (BK / 4), kq = u % (BK / 4);
-        put<BF16>(L + rr * LDK + kq * 4, r[i]);
+        const int rr = u / (BK / UK), kq = u % (BK / UK);
+        const int64_t off = (int64_t)(r0 + rr) * ld + k0 + kq * UK;
+        if constexpr (!SRC_BF16)
+          r[i] = *reinterpret_cast<const f4*>(static_cast<const float*>(Pv) + off);
+        else
+          r[i] = *reinterpret_cast<const u16x8*>(static_cast<const unsigned short*>(Pv) + off);
       } else {
         const int rq = u % (R_TILE / 4), kq = u / (R_TILE / 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f4 v = {r[i * 4 + 0][e], r[i * 4 + 1][e], r[i * 4 + 2][e], r[i * 4 + 3][e]};
-          put<BF16>(L + (rq * 4 + e) * LDK + kq * 4, v);
+        for (int kk = 0; kk < UK; ++kk) {
+          const int64_t off = (int64_t)(k0 + kq * UK + kk) * ld + r0 + rq * 4;
+          if constexpr (!SRC_BF16)
+            r[i * 4 + kk] = *reinterpret_cast<const f4*>(static_cast<const float*>(Pv) + off);
+          else
+            r[i * 8 + kk] = *reinterpret_cast<const u16x4*>(static_cast<const unsigned short*>(Pv) + off);
         }
       }
     }
   }
 
   template <bool BF16>
-  __device__ __forceinline__ static void put(typename Lds<BF16>::T* dst, f4 v) {
+  __device__ __forceinline__ void store(typename Lds<BF16, BK>::T* L, int tid) const {
+    constexpr int LDK = Lds<BF16, BK>::LDK;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = tid + i * NT;
+      if (UNITS % NT != 0 && u >= UNITS) break;
+      if constexpr (!RCONTIG) {
+        const int rr = u / (BK / UK), kq = u % (BK / UK);
+        if constexpr (!SRC_BF16)
+          put4<BF16>(L + rr * LDK + kq * 4, r[i]);
+        else
+          *reinterpret_cast<u16x8*>(L + rr * LDK + kq * 8) = r[i];
+      } else {
+        const int rq = u % (R_TILE / 4), kq = u / (R_TILE / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (!SRC_BF16) {
+            f4 v = {r[i * 4 + 0][e], r[i * 4 + 1][e], r[i * 4 + 2][e], r[i * 4 + 3][e]};
+            put4<BF16>(L + (rq * 4 + e) * LDK + kq * 4, v);
+          } else {
+            u16x8 v;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) v[kk] = r[i * 8 + kk][e];
+            *reinterpret_cast<u16x8*>(L + (rq * 4 + e) * LDK + kq * 8) = v;
+          }
+        }
+      }
+    }
+  }
+
+  template <bool BF16>
+  __device__ __forceinline__ static void put4(typename Lds<BF16, BK>::T* dst, f4 v) {
     if constexpr (BF16) {
       bf16x4 b = {(bf16_t)v[0], (bf16_t)v[1], (bf16_t)v[2], (bf16_t)v[3]};
       *reinterpret_cast<bf16x4*>(dst) = b;
@@ -146,18 +238,18 @@ struct Stage {
 
 struct KArgs {
   GemmArgs g;
-  int tiles_n;
+  int tiles_m, tiles_n;
   int splits;
-  int k_per_split;  // multiple of BK
+  int k_per_split;  // multiple of KALIGN
   float* ws;        // split-K partials [batch*splits][M][N]
 };
 
-template <int WM, int WN, int TM, int TN, bool BF16, bool A_RC, bool B_KC>
+template <int WM, int WN, int TM, int TN, int BK, bool BF16, bool A_RC, bool B_KC, bool A_BF, bool B_BF>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
   constexpr int NT = WM * WN * 64;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  constexpr int LDK = Lds<BF16>::LDK;
-  using LT = typename Lds<BF16>::T;
+  constexpr int LDK = Lds<BF16, BK>::LDK;
+  using LT = typename Lds<BF16, BK>::T;
   __shared__ __attribute__((aligned(16))) LT As[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) LT Bs[2][BN * LDK];
 
@@ -166,15 +258,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  const int tn = blockIdx.x, tm = blockIdx.y;
-  const int zz = blockIdx.z;
+  // XCD-contiguous tile order: workgroup w runs on XCD w % 8
+  const int ntiles = ka.tiles_m * ka.tiles_n;
+  int id = blockIdx.x;
+  if ((ntiles & 7) == 0) id = (id & 7) * (ntiles >> 3) + (id >> 3);
+  const int tm = id / ka.tiles_n, tn = id % ka.tiles_n;
+  const int zz = blockIdx.y;
   const int z = zz / ka.splits, split = zz % ka.splits;
   const int m0 = tm * BM, n0 = tn * BN;
   if (g.causal_out && n0 > m0 + BM - 1) return;
 
   const int z1 = z / g.batch_div, z2 = z % g.batch_div;
-  const float* A = g.A + z1 * g.sa1 + z2 * g.sa2;
-  const float* B = g.B + z1 * g.sb1 + z2 * g.sb2;
+  const int eA = A_BF ? 2 : 4, eB = B_BF ? 2 : 4;
+  const char* A = reinterpret_cast<const char*>(g.A) + (z1 * g.sa1 + z2 * g.sa2) * eA;
+  const char* B = reinterpret_cast<const char*>(g.B) + (z1 * g.sb1 + z2 * g.sb2) * eB;
 
   int kb = split * ka.k_per_split;
   int ke = min(g.K, kb + ka.k_per_split);
@@ -182,11 +279,27 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
   if (g.causal_a == CAUSAL_FROM) kb = max(kb, (m0 / BK) * BK);
 
   // 16-byte vector loads need 16-byte aligned rows and batch offsets
-  const bool vecA = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && (g.lda % 4 == 0);
-  const bool vecB = ((reinterpret_cast<uintptr_t>(B) & 15) == 0) && (g.ldb % 4 == 0);
+  const bool vecA = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && (g.lda % (16 / eA) == 0);
+  const bool vecB = ((reinterpret_cast<uintptr_t>(B) & 15) == 0) && (g.ldb % (16 / eB) == 0);
+  // the m/n extent of this tile is entirely in range for both operands
+  const bool interior = vecA && vecB && m0 + BM <= g.M && n0 + BN <= g.N;
 
-  Stage<BM, NT, A_RC> sa;
-  Stage<BN, NT, B_KC ? false : true> sb;
+  Stage<BM, NT, A_RC, A_BF, BK> sa;
+  Stage<BN, NT, !B_KC, B_BF, BK> sb;
+
+  // a k-tile is loaded without checks when it is interior, complete and away from the causal diagonal
+  auto load_tile = [&](int k0) {
+    bool fast = interior && k0 + BK <= ke;
+    if (g.causal_a == CAUSAL_UPTO) fast = fast && k0 + BK - 1 <= m0;
+    if (g.causal_a == CAUSAL_FROM) fast = fast && k0 >= m0 + BM - 1;
+    if (fast) {
+      sa.load_fast(A, g.lda, m0, k0, tid);
+      sb.load_fast(B, g.ldb, n0, k0, tid);
+    } else {
+      sa.load(A, g.lda, m0, k0, g.M, ke, vecA, g.causal_a, tid);
+      sb.load(B, g.ldb, n0, k0, g.N, ke, vecB, CAUSAL_NONE, tid);
+    }
+  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -198,8 +311,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
 
   int buf = 0;
   if (kb < ke) {
-    sa.load(A, g.lda, m0, kb, g.M, ke, vecA, g.causal_a, tid);
-    sb.load(B, g.ldb, n0, kb, g.N, ke, vecB, CAUSAL_NONE, tid);
+    load_tile(kb);
     sa.template store<BF16>(As[0], tid);
     sb.template store<BF16>(Bs[0], tid);
   }
@@ -208,10 +320,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
   const int lrow = lane & 31, lhalf = lane >> 5;
   for (int k0 = kb; k0 < ke; k0 += BK) {
     const bool more = k0 + BK < ke;
-    if (more) {
-      sa.load(A, g.lda, m0, k0 + BK, g.M, ke, vecA, g.causal_a, tid);
-      sb.load(B, g.ldb, n0, k0 + BK, g.N, ke, vecB, CAUSAL_NONE, tid);
-    }
+    if (more) load_tile(k0 + BK);
     const LT* Ab = As[buf] + (wm * TM * 32 + lrow) * LDK;
     const LT* Bb = Bs[buf] + (wn * TN * 32 + lrow) * LDK;
     if constexpr (BF16) {
@@ -307,8 +416,10 @@ __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, i
   }
 }
 
+enum Cfg { CFG_128x128 = 1, CFG_128x64 = 2 };
+
 struct Plan {
-  int cfg;  // 0: 128x128 (2x2 waves, 2x2 blocks), 1: 128x64 (4x1 waves, 1x2 blocks)
+  int cfg;
   int BM, BN;
   int splits;
   int k_per_split;
@@ -317,40 +428,51 @@ struct Plan {
 Plan make_plan(const GemmArgs& g) {
   Plan p;
   if (g.N <= 64) {
-    p.cfg = 1;
-    p.BM = 128;
-    p.BN = 64;
+    p.cfg = CFG_128x64, p.BM = 128, p.BN = 64;
   } else {
-    p.cfg = 0;
-    p.BM = 128;
-    p.BN = 128;
+    p.cfg = CFG_128x128, p.BM = 128, p.BN = 128;
   }
   const int64_t tiles = (int64_t)((g.M + p.BM - 1) / p.BM) * ((g.N + p.BN - 1) / p.BN) * g.batch;
   p.splits = 1;
   if (g.causal_a == CAUSAL_NONE && !g.causal_out) {
-    // fill the 256 compute units at least twice when K is long
-    while (tiles * p.splits < 512 && g.K / (p.splits * 2) >= 1024 && p.splits < 16) p.splits *= 2;
+    // fill the 256 compute units at least once when K is long
+    while (tiles * p.splits < 256 && g.K / (p.splits * 2) >= 1024 && p.splits < 16) p.splits *= 2;
   }
   const int kps = (g.K + p.splits - 1) / p.splits;
-  p.k_per_split = ((kps + BK - 1) / BK) * BK;
-  p.splits = (g.K + p.k_per_split - 1) / p.k_per_split;
-  if (p.splits < 1) p.splits = 1;
+  p.k_per_split = ((kps + KALIGN - 1) / KALIGN) * KALIGN;
+  p.splits = std::max(1, (g.K + p.k_per_split - 1) / p.k_per_split);
   return p;
 }
 
-template <int WM, int WN, int TM, int TN, bool BF16>
+template <int WM, int WN, int TM, int TN, int BK, bool BF16, bool A_BF, bool B_BF>
 hipError_t launch_layout(const KArgs& ka, dim3 grid, hipStream_t s) {
   const GemmArgs& g = ka.g;
   dim3 block(WM * WN * 64);
   if (!g.a_mcontig && !g.b_kcontig)
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BF16, false, false>), grid, block, 0, s, ka);
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BK, BF16, false, false, A_BF, B_BF>), grid, block, 0, s, ka);
   else if (!g.a_mcontig && g.b_kcontig)
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BF16, false, true>), grid, block, 0, s, ka);
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BK, BF16, false, true, A_BF, B_BF>), grid, block, 0, s, ka);
   else if (g.a_mcontig && !g.b_kcontig)
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BF16, true, false>), grid, block, 0, s, ka);
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BK, BF16, true, false, A_BF, B_BF>), grid, block, 0, s, ka);
   else
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BF16, true, true>), grid, block, 0, s, ka);
+    return hipErrorInvalidValue;  // A^T B^T is never needed
   return hipGetLastError();
+}
+
+// k-tile depth: 64 when both operands are stored as bf16 (16 bytes of k per
+// row per load, 32 MFMAs per wave between barriers), 32 otherwise (fp32
+// staging registers would double)
+template <int WM, int WN, int TM, int TN>
+hipError_t launch_prec(const KArgs& ka, dim3 grid, hipStream_t s) {
+  const GemmArgs& g = ka.g;
+  if (g.prec != PREC_BF16) {
+    if (g.a_bf16 || g.b_bf16) return hipErrorInvalidValue;
+    return launch_layout<WM, WN, TM, TN, 32, false, false, false>(ka, grid, s);
+  }
+  if (g.a_bf16 && g.b_bf16) return launch_layout<WM, WN, TM, TN, 64, true, true, true>(ka, grid, s);
+  if (g.a_bf16) return launch_layout<WM, WN, TM, TN, 32, true, true, false>(ka, grid, s);
+  if (g.b_bf16) return launch_layout<WM, WN, TM, TN, 32, true, false, true>(ka, grid, s);
+  return launch_layout<WM, WN, TM, TN, 32, true, false, false>(ka, grid, s);
 }
 
 }  // namespace
@@ -366,20 +488,20 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   // K == 0 needs no special case: the k loop is empty and the epilogue writes beta*C + bias
   Plan p = make_plan(g);
   if (p.splits > 1 && (size_t)p.splits * g.batch * g.M * g.N * sizeof(float) > ws_bytes) p.splits = 1;
-  if (p.splits == 1) p.k_per_split = ((std::max(g.K, 1) + BK - 1) / BK) * BK;
+  if (p.splits == 1) p.k_per_split = ((std::max(g.K, 1) + KALIGN - 1) / KALIGN) * KALIGN;
   KArgs ka;
   ka.g = g;
   ka.splits = p.splits;
   ka.k_per_split = p.k_per_split;
   ka.ws = static_cast<float*>(workspace);
+  ka.tiles_m = (g.M + p.BM - 1) / p.BM;
   ka.tiles_n = (g.N + p.BN - 1) / p.BN;
-  dim3 grid(ka.tiles_n, (g.M + p.BM - 1) / p.BM, g.batch * p.splits);
+  dim3 grid(ka.tiles_m * ka.tiles_n, g.batch * p.splits);
   hipError_t e;
-  const bool bf = g.prec == PREC_BF16;
-  if (p.cfg == 0)
-    e = bf ? launch_layout<2, 2, 2, 2, true>(ka, grid, s) : launch_layout<2, 2, 2, 2, false>(ka, grid, s);
+  if (p.cfg == CFG_128x128)
+    e = launch_prec<2, 2, 2, 2>(ka, grid, s);
   else
-    e = bf ? launch_layout<4, 1, 1, 2, true>(ka, grid, s) : launch_layout<4, 1, 1, 2, false>(ka, grid, s);
+    e = launch_prec<4, 1, 1, 2>(ka, grid, s);
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t MN = (int64_t)g.M * g.N;
   dim3 rgrid((unsigned)std::min<int64_t>((MN + 255) / 256, 4096), g.batch);

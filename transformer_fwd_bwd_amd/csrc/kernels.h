@@ -40,6 +40,8 @@ struct GemmArgs {
   int causal_a = CAUSAL_NONE;
   bool causal_out = false;
   int prec = PREC_F32;
+  // bf16 storage of an operand (bf16 variant only): A/B then point at uint16 data
+  bool a_bf16 = false, b_bf16 = false;
 };
 
 size_t gemm_workspace_bytes(const GemmArgs& g);
@@ -47,8 +49,13 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
 
 // ---- elementwise (elementwise.hip); beta in {0, 1}: overwrite or accumulate
 hipError_t fill(float* p, float v, int64_t n, hipStream_t s);
+// dst[i] = bf16(src[i]), round to nearest even
+hipError_t to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 hipError_t add_bcast(const float* a, const float* b, float* y, int64_t n, int64_t nb, hipStream_t s);
 hipError_t axpby(float* dst, const float* src, float alpha, float beta, int64_t n, hipStream_t s);
+// dst[r*ldd + c] = src[r*lds + c] (+ dst when beta == 1), c < cols
+hipError_t copy_pitched(const float* src, int64_t lds, float* dst, int64_t ldd, int64_t rows, int64_t cols,
+                        float beta, hipStream_t s);
 hipError_t mul_fwd(const float* a, const float* b, float* y, int64_t n, hipStream_t s);
 hipError_t mul_bwd(const float* g, const float* other, float* d, float beta, int64_t n, hipStream_t s);
 hipError_t scale_fwd(const float* a, float sc, float* y, int64_t n, hipStream_t s);
@@ -85,10 +92,11 @@ hipError_t causal_softmax_fwd(const float* x, float* p, int64_t rows, int64_t T,
 hipError_t causal_softmax_bwd(const float* g, const float* p, float* d, int64_t rows, int64_t T, float scale,
                               float beta, bool full, hipStream_t s);
 size_t softmax_ce_workspace_bytes(int64_t rows);
-hipError_t softmax_ce_fwd(const float* logits, const int32_t* targets, int64_t rows, int64_t V, float* lse,
-                          float* loss, void* ws, hipStream_t s);
-hipError_t softmax_ce_bwd(const float* logits, const int32_t* targets, const float* lse, const float* g_scalar,
-                          float* dl, int64_t rows, int64_t V, float beta, hipStream_t s);
+// logits rows have V valid columns at a row stride of ld >= V
+hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* targets, int64_t rows, int64_t V,
+                          float* lse, float* loss, void* ws, hipStream_t s);
+hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* targets, const float* lse,
+                          const float* g_scalar, float* dl, int64_t rows, int64_t V, float beta, hipStream_t s);
 
 // ---- embedding (embedding.hip)
 // ids outside [0, rows) give zero rows forward and are skipped backward
@@ -105,6 +113,7 @@ struct AdamSeg {
   const float* g;
   float* m;
   float* v;
+  uint16_t* pbf;  // bf16 copy of p refreshed by the step, or null
   int64_t n;
   float wd;
   int pad;

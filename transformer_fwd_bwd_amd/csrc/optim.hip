@@ -47,6 +47,10 @@ __global__ __launch_bounds__(NT) void adamw_k(const AdamSeg* __restrict__ segs, 
       *reinterpret_cast<f4*>(sg.p + q) = p;
       *reinterpret_cast<f4*>(sg.m + q) = m;
       *reinterpret_cast<f4*>(sg.v + q) = v;
+      if (sg.pbf) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sg.pbf[q + e] = __builtin_bit_cast(uint16_t, (__bf16)p[e]);
+      }
     }
     i = end4;
   }
@@ -56,6 +60,7 @@ __global__ __launch_bounds__(NT) void adamw_k(const AdamSeg* __restrict__ segs, 
     sg.p[q] = p;
     sg.m[q] = m;
     sg.v[q] = v;
+    if (sg.pbf) sg.pbf[q] = __builtin_bit_cast(uint16_t, (__bf16)p);
   }
 }
 

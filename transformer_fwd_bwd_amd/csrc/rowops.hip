@@ -81,48 +81,34 @@ __global__ __launch_bounds__(NT) void ln_fwd_k(const float* __restrict__ x, cons
   }
 }
 
-// dx per row; per-block partial column sums of g*xhat and g
+// dx per row (one wavefront per row, many rows in flight)
 template <bool CACHED>
-__global__ __launch_bounds__(NT) void ln_bwd_k(const float* __restrict__ g, const float* __restrict__ x,
-                                               const float* __restrict__ gamma, const float* __restrict__ mean,
-                                               const float* __restrict__ rstd, float* __restrict__ dx,
-                                               float* __restrict__ part, int64_t rows, int C, float beta_dx) {
-  extern __shared__ float sh[];  // [WAVES][2][C]
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float* dg = sh + (w * 2) * C;
-  float* db = sh + (w * 2 + 1) * C;
-  for (int c = lane; c < C; c += 64) dg[c] = db[c] = 0.f;
+__global__ __launch_bounds__(NT) void ln_bwd_dx_k(const float* __restrict__ g, const float* __restrict__ x,
+                                                  const float* __restrict__ gamma, const float* __restrict__ mean,
+                                                  const float* __restrict__ rstd, float* __restrict__ dx, int64_t rows,
+                                                  int C, float beta_dx) {
+  const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * WAVES;
-  for (int64_t r = (int64_t)blockIdx.x * WAVES + w; r < rows; r += nw) {
+  for (int64_t r = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); r < rows; r += nw) {
     const float mu = mean[r], rs = rstd[r];
     const float* gr = g + r * C;
     const float* xr = x + r * C;
-    float xh[MAXV], gg[MAXV];
+    float xh[MAXV], dg[MAXV];
     float s1 = 0.f, s2 = 0.f;
     if (CACHED) {
 #pragma unroll
       for (int j = 0; j < MAXV; ++j) {
         const int c = lane + 64 * j;
-        if (c < C) {
-          xh[j] = (xr[c] - mu) * rs;
-          gg[j] = gr[c];
-          const float d = gg[j] * gamma[c];
-          s1 += d;
-          s2 += d * xh[j];
-          dg[c] += gg[j] * xh[j];
-          db[c] += gg[j];
-        } else {
-          xh[j] = gg[j] = 0.f;
-        }
+        xh[j] = c < C ? (xr[c] - mu) * rs : 0.f;
+        dg[j] = c < C ? gr[c] * gamma[c] : 0.f;
+        s1 += dg[j];
+        s2 += dg[j] * xh[j];
       }
     } else {
       for (int c = lane; c < C; c += 64) {
-        const float xv = (xr[c] - mu) * rs, gv = gr[c];
-        const float d = gv * gamma[c];
+        const float xv = (xr[c] - mu) * rs, d = gr[c] * gamma[c];
         s1 += d;
         s2 += d * xv;
-        dg[c] += gv * xv;
-        db[c] += gv;
       }
     }
     const float m1 = wave_sum(s1) / C, m2 = wave_sum(s2) / C;
@@ -132,7 +118,7 @@ __global__ __launch_bounds__(NT) void ln_bwd_k(const float* __restrict__ g, cons
       for (int j = 0; j < MAXV; ++j) {
         const int c = lane + 64 * j;
         if (c < C) {
-          float v = rs * (gg[j] * gamma[c] - m1 - xh[j] * m2);
+          float v = rs * (dg[j] - m1 - xh[j] * m2);
           if (beta_dx != 0.f) v += dr[c];
           dr[c] = v;
         }
@@ -146,16 +132,38 @@ __global__ __launch_bounds__(NT) void ln_bwd_k(const float* __restrict__ g, cons
       }
     }
   }
-  __syncthreads();
-  for (int c = threadIdx.x; c < C; c += NT) {
-    float a = 0.f, b = 0.f;
-    for (int i = 0; i < WAVES; ++i) {
-      a += sh[(i * 2) * C + c];
-      b += sh[(i * 2 + 1) * C + c];
+}
+
+// partial column sums over a slab of rows: part[p][0][c] = sum g*xhat, part[p][1][c] = sum g
+__global__ __launch_bounds__(NT) void ln_bwd_cols_k(const float* __restrict__ g, const float* __restrict__ x,
+                                                    const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                    float* __restrict__ part, int64_t rows, int C, int64_t rows_per) {
+  const int c = blockIdx.x * NT + threadIdx.x;
+  if (c >= C) return;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per;
+  const int64_t r1 = r0 + rows_per < rows ? r0 + rows_per : rows;
+  float a = 0.f, b = 0.f;
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    float gv[4], xv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      gv[u] = g[(r + u) * C + c];
+      xv[u] = x[(r + u) * C + c];
     }
-    part[((int64_t)blockIdx.x * 2) * C + c] = a;
-    part[((int64_t)blockIdx.x * 2 + 1) * C + c] = b;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a += gv[u] * (xv[u] - mean[r + u]) * rstd[r + u];
+      b += gv[u];
+    }
   }
+  for (; r < r1; ++r) {
+    const float gv = g[r * C + c];
+    a += gv * (x[r * C + c] - mean[r]) * rstd[r];
+    b += gv;
+  }
+  part[((int64_t)blockIdx.y * 2) * C + c] = a;
+  part[((int64_t)blockIdx.y * 2 + 1) * C + c] = b;
 }
 
 __global__ void ln_bwd_reduce(const float* __restrict__ part, int nparts, int C, float* __restrict__ dgamma,
@@ -173,7 +181,9 @@ __global__ void ln_bwd_reduce(const float* __restrict__ part, int nparts, int C,
   dbeta[c] = b;
 }
 
-int ln_bwd_blocks(int64_t rows) { return (int)std::max<int64_t>(1, std::min<int64_t>(256, (rows + WAVES - 1) / WAVES)); }
+int ln_bwd_parts(int64_t rows) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>(256, (rows + 31) / 32));
+}
 
 // ------------------------------------------------------------ causal softmax
 template <bool CACHED>
@@ -290,11 +300,12 @@ __device__ __forceinline__ void online_merge(float& m, float& s, float m2, float
 }
 
 // one block per row: lse[r] = log(sum exp(logits)), loss_rows[r] = -log(max(p_target, 1e-30))
-__global__ __launch_bounds__(NT) void ce_fwd_k(const float* __restrict__ logits, const int32_t* __restrict__ tgt,
-                                               int64_t V, float* __restrict__ lse, float* __restrict__ loss_rows) {
+__global__ __launch_bounds__(NT) void ce_fwd_k(const float* __restrict__ logits, int64_t ld,
+                                               const int32_t* __restrict__ tgt, int64_t V, float* __restrict__ lse,
+                                               float* __restrict__ loss_rows) {
   __shared__ float sm[WAVES], ss[WAVES];
   const int64_t r = blockIdx.x;
-  const float* lr = logits + r * V;
+  const float* lr = logits + r * ld;
   float m = -INFINITY, s = 0.f;
   for (int64_t c = threadIdx.x; c < V; c += NT) {
     const float x = lr[c];
@@ -340,15 +351,16 @@ __global__ __launch_bounds__(NT) void mean_k(const float* __restrict__ v, int64_
   if (threadIdx.x == 0) out[0] = (float)(sh[0] / (double)n);
 }
 
-__global__ __launch_bounds__(NT) void ce_bwd_k(const float* __restrict__ logits, const int32_t* __restrict__ tgt,
-                                               const float* __restrict__ lse, const float* __restrict__ gsc,
-                                               float* __restrict__ dl, int64_t rows, int64_t V, float beta) {
+__global__ __launch_bounds__(NT) void ce_bwd_k(const float* __restrict__ logits, int64_t ld,
+                                               const int32_t* __restrict__ tgt, const float* __restrict__ lse,
+                                               const float* __restrict__ gsc, float* __restrict__ dl, int64_t rows,
+                                               int64_t V, float beta) {
   const int64_t r = blockIdx.x;
   const float gn = gsc[0] / (float)rows;
   const float L = lse[r];
   const int t = tgt[r];
-  const float* lr = logits + r * V;
-  float* dr = dl + r * V;
+  const float* lr = logits + r * ld;
+  float* dr = dl + r * ld;
   for (int64_t c = threadIdx.x; c < V; c += NT) {
     float v = gn * (expf(lr[c] - L) - (c == t ? 1.f : 0.f));
     if (beta != 0.f) v += dr[c];
@@ -375,24 +387,27 @@ hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, 
 }
 
 size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C) {
-  return (size_t)ln_bwd_blocks(rows) * 2 * C * sizeof(float);
+  return (size_t)ln_bwd_parts(rows) * 2 * C * sizeof(float);
 }
 
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
                          float* dx, float* dgamma, float* dbeta, int64_t rows, int64_t C, float beta_dx,
                          float beta_dg, float beta_db, void* ws, hipStream_t s) {
   if (C <= 0) return hipSuccess;
-  const int nb = ln_bwd_blocks(rows);
-  const size_t shmem = (size_t)WAVES * 2 * C * sizeof(float);
-  if (shmem > 64 * 1024) return hipErrorInvalidValue;
+  if (rows > 0) {
+    if (C <= 64 * MAXV)
+      hipLaunchKernelGGL(ln_bwd_dx_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
+                         rows, (int)C, beta_dx);
+    else
+      hipLaunchKernelGGL(ln_bwd_dx_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
+                         rows, (int)C, beta_dx);
+  }
+  const int parts = ln_bwd_parts(rows);
+  const int64_t rows_per = (rows + parts - 1) / parts;
   float* part = static_cast<float*>(ws);
-  if (C <= 64 * MAXV)
-    hipLaunchKernelGGL(ln_bwd_k<true>, dim3(nb), dim3(NT), shmem, s, g, x, gamma, mean, rstd, dx, part, rows, (int)C,
-                       beta_dx);
-  else
-    hipLaunchKernelGGL(ln_bwd_k<false>, dim3(nb), dim3(NT), shmem, s, g, x, gamma, mean, rstd, dx, part, rows,
-                       (int)C, beta_dx);
-  hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + NT - 1) / NT)), dim3(NT), 0, s, part, nb, (int)C, dgamma,
+  hipLaunchKernelGGL(ln_bwd_cols_k, dim3((unsigned)((C + NT - 1) / NT), (unsigned)parts), dim3(NT), 0, s, g, x,
+                     mean, rstd, part, rows, (int)C, rows_per);
+  hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + NT - 1) / NT)), dim3(NT), 0, s, part, parts, (int)C, dgamma,
                      dbeta, beta_dg, beta_db);
   return hipGetLastError();
 }
@@ -420,19 +435,19 @@ hipError_t causal_softmax_bwd(const float* g, const float* p, float* d, int64_t 
 
 size_t softmax_ce_workspace_bytes(int64_t rows) { return (size_t)rows * sizeof(float); }
 
-hipError_t softmax_ce_fwd(const float* logits, const int32_t* targets, int64_t rows, int64_t V, float* lse,
-                          float* loss, void* ws, hipStream_t s) {
+hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* targets, int64_t rows, int64_t V,
+                          float* lse, float* loss, void* ws, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   float* loss_rows = static_cast<float*>(ws);
-  hipLaunchKernelGGL(ce_fwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, targets, V, lse, loss_rows);
+  hipLaunchKernelGGL(ce_fwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
   hipLaunchKernelGGL(mean_k, dim3(1), dim3(NT), 0, s, loss_rows, rows, loss);
   return hipGetLastError();
 }
 
-hipError_t softmax_ce_bwd(const float* logits, const int32_t* targets, const float* lse, const float* g_scalar,
-                          float* dl, int64_t rows, int64_t V, float beta, hipStream_t s) {
+hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* targets, const float* lse,
+                          const float* g_scalar, float* dl, int64_t rows, int64_t V, float beta, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, targets, lse, g_scalar, dl, rows, V,
+  hipLaunchKernelGGL(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, rows, V,
                      beta);
   return hipGetLastError();
 }

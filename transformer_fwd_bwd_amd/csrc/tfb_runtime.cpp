@@ -58,9 +58,19 @@ struct TensorRec {
   float* grad = nullptr;
   int gstate = G_NONE;
   size_t persist_off = 0, persist_bytes = 0;
+  // bf16 copies of data / grad used as contraction operands in the bf16 variant
+  uint16_t* bf = nullptr;
+  bool bf_valid = false;
+  uint16_t* gbf = nullptr;
+  bool gbf_valid = false;
+
+  int64_t ld = 0;  // row stride of the last dim when rows are padded (0: dense)
 
   int64_t cols() const { return ndim ? shape[ndim - 1] : 1; }
   int64_t rows() const { return cols() ? numel / cols() : 0; }
+  bool padded() const { return ld != 0 && ld != cols(); }
+  int64_t stride() const { return padded() ? ld : cols(); }
+  int64_t storage() const { return padded() ? rows() * ld : numel; }
 };
 
 enum OpKind {
@@ -84,6 +94,7 @@ enum OpKind {
   OP_CSOFTMAX,
   OP_ATTENTION,
   OP_SOFTMAX_CE,
+  OP_COMPACT,  // dense copy of a row-padded tensor (inserted by the library)
 };
 
 struct Rec {
@@ -153,6 +164,7 @@ struct tfb_opt {
   AdamChunk* d_chunks = nullptr;
   int d_nseg_cap = 0, d_nchunk_cap = 0;
   std::vector<int> uploaded_active;
+  std::vector<uint16_t*> uploaded_shadows;
   int nchunks = 0;
 };
 
@@ -193,10 +205,12 @@ struct Ctx {
     return n;
   }
 
-  // an op output in the step arena
-  int make_output(const std::vector<int64_t>& shape) {
+  // an op output in the step arena; ld > last dim pads every row to ld floats
+  int make_output(const std::vector<int64_t>& shape, int64_t ld = 0) {
     int64_t n = numel_of(shape.data(), (int)shape.size());
-    float* p = static_cast<float*>(c->arena.alloc_step((size_t)n * sizeof(float)));
+    const int64_t cols = shape.back();
+    const int64_t stor = (ld > cols && cols > 0) ? n / cols * ld : n;
+    float* p = static_cast<float*>(c->arena.alloc_step((size_t)stor * sizeof(float)));
     int h = new_handle();
     TensorRec& t = c->tensors[h];
     t.live = true;
@@ -204,17 +218,34 @@ struct Ctx {
     t.ndim = (int)shape.size();
     for (int i = 0; i < t.ndim; ++i) t.shape[i] = shape[i];
     t.numel = n;
+    t.ld = ld > cols ? ld : 0;
     t.data = p;
     return h;
   }
 
+  // ops other than the cross-entropy read dense rows: a padded input is first
+  // copied to a dense tensor by a recorded compaction op
+  int dense_in(int h) {
+    TensorRec& t = T(h);
+    if (!t.padded()) return h;
+    const int64_t rows = t.rows(), cols = t.cols(), ld = t.ld;
+    const float* src = t.data;
+    int o = make_output(std::vector<int64_t>(t.shape, t.shape + t.ndim));
+    hip_check(copy_pitched(src, ld, c->tensors[o].data, cols, rows, cols, 0.f, s()), "compact");
+    Rec r{OP_COMPACT};
+    r.in[0] = h, r.out = o;
+    record(r);
+    return o;
+  }
+
   void ensure_grad_buffer(TensorRec& t) {
     if (t.grad) return;
+    const size_t bytes = (size_t)t.storage() * sizeof(float);
     if (t.leaf) {
-      size_t off = c->arena.alloc_persist((size_t)t.numel * sizeof(float));
+      size_t off = c->arena.alloc_persist(bytes);
       t.grad = reinterpret_cast<float*>(c->arena.base + off);
     } else {
-      t.grad = static_cast<float*>(c->arena.alloc_step((size_t)t.numel * sizeof(float)));
+      t.grad = static_cast<float*>(c->arena.alloc_step(bytes));
     }
     t.gstate = G_ZERO;
   }
@@ -223,14 +254,44 @@ struct Ctx {
   std::pair<float*, float> gdst(int h) {
     TensorRec& t = T(h);
     ensure_grad_buffer(t);
+    t.gbf_valid = false;
     if (t.gstate == G_VALID) return {t.grad, 1.f};
     t.gstate = G_VALID;
     return {t.grad, 0.f};
   }
 
+  bool bf16_mode() const { return c->precision == TFB_BF16_MFMA; }
+
+  uint16_t* alloc_bf16(const TensorRec& t) {
+    const size_t bytes = (size_t)std::max<int64_t>(t.storage(), 1) * sizeof(uint16_t);
+    if (t.leaf) return reinterpret_cast<uint16_t*>(c->arena.base + c->arena.alloc_persist(bytes));
+    return static_cast<uint16_t*>(c->arena.alloc_step(bytes));
+  }
+
+  // bf16 copy of a tensor's data, converted once and reused until the data changes
+  const uint16_t* data_bf16(TensorRec& t) {
+    if (!t.bf_valid) {
+      if (!t.bf) t.bf = alloc_bf16(t);
+      hip_check(to_bf16(t.data, t.bf, t.storage(), s()), "to_bf16");
+      t.bf_valid = true;
+    }
+    return t.bf;
+  }
+
+  // bf16 copy of a finished gradient (all contributions already added)
+  const uint16_t* grad_bf16(TensorRec& t) {
+    materialize_zero(t);
+    if (!t.gbf_valid) {
+      if (!t.gbf) t.gbf = alloc_bf16(t);
+      hip_check(to_bf16(t.grad, t.gbf, t.storage(), s()), "to_bf16");
+      t.gbf_valid = true;
+    }
+    return t.gbf;
+  }
+
   void materialize_zero(TensorRec& t) {
     if (t.grad && t.gstate == G_ZERO) {
-      hip_check(fill(t.grad, 0.f, t.numel, s()), "fill");
+      hip_check(fill(t.grad, 0.f, t.storage(), s()), "fill");
       t.gstate = G_VALID;
     }
   }
@@ -307,33 +368,58 @@ std::string shape_str(const TensorRec& t) {
 std::vector<int64_t> shape_vec(const TensorRec& t) { return std::vector<int64_t>(t.shape, t.shape + t.ndim); }
 
 // ------------------------------------------------------------------ contraction layouts
+// A contraction operand: fp32 data, or its bf16 copy in the bf16 variant.
+struct Opnd {
+  const void* p;
+  bool bf;
+};
+
+Opnd op_data(Ctx& C, TensorRec& t) {
+  if (C.bf16_mode()) return {C.data_bf16(t), true};
+  return {t.data, false};
+}
+Opnd op_grad(Ctx& C, TensorRec& t) {
+  if (C.bf16_mode()) return {C.grad_bf16(t), true};
+  C.materialize_zero(t);
+  return {t.grad, false};
+}
+
+void set_a(GemmArgs& g, Opnd o) {
+  g.A = static_cast<const float*>(o.p);
+  g.a_bf16 = o.bf;
+}
+void set_b(GemmArgs& g, Opnd o) {
+  g.B = static_cast<const float*>(o.p);
+  g.b_bf16 = o.bf;
+}
+
 // y[rows, N] = x[rows, K] @ w[K, N] (+ bias)
-void gemm_nn(Ctx& C, const float* x, const float* w, float* y, int64_t rows, int64_t K, int64_t N, float beta,
-             const float* bias) {
+void gemm_nn(Ctx& C, Opnd x, Opnd w, float* y, int64_t rows, int64_t K, int64_t N, float beta, const float* bias,
+             int64_t lda = -1) {
   GemmArgs g = C.gemm_base();
   g.M = (int)rows, g.N = (int)N, g.K = (int)K;
-  g.A = x, g.lda = K;
-  g.B = w, g.ldb = N;
+  set_a(g, x), g.lda = lda < 0 ? K : lda;
+  set_b(g, w), g.ldb = N;
   g.C = y, g.ldc = N;
   g.beta = beta, g.bias = bias;
   C.run_gemm(g);
 }
 // y[rows, N] = x[rows, K] @ w[N, K]^T
-void gemm_nt(Ctx& C, const float* x, const float* w, float* y, int64_t rows, int64_t K, int64_t N, float beta) {
+void gemm_nt(Ctx& C, Opnd x, Opnd w, float* y, int64_t rows, int64_t K, int64_t N, float beta, int64_t ldc = -1) {
   GemmArgs g = C.gemm_base();
   g.M = (int)rows, g.N = (int)N, g.K = (int)K;
-  g.A = x, g.lda = K;
-  g.B = w, g.ldb = K, g.b_kcontig = true;
-  g.C = y, g.ldc = N;
+  set_a(g, x), g.lda = K;
+  set_b(g, w), g.ldb = K, g.b_kcontig = true;
+  g.C = y, g.ldc = ldc < 0 ? N : ldc;
   g.beta = beta;
   C.run_gemm(g);
 }
 // y[M, N] = x[K, M]^T @ g[K, N]
-void gemm_tn(Ctx& C, const float* x, const float* gr, float* y, int64_t M, int64_t K, int64_t N, float beta) {
+void gemm_tn(Ctx& C, Opnd x, Opnd gr, float* y, int64_t M, int64_t K, int64_t N, float beta, int64_t lda = -1) {
   GemmArgs g = C.gemm_base();
   g.M = (int)M, g.N = (int)N, g.K = (int)K;
-  g.A = x, g.lda = M, g.a_mcontig = true;
-  g.B = gr, g.ldb = N;
+  set_a(g, x), g.lda = lda < 0 ? M : lda, g.a_mcontig = true;
+  set_b(g, gr), g.ldb = N;
   g.C = y, g.ldc = N;
   g.beta = beta;
   C.run_gemm(g);
@@ -403,10 +489,11 @@ void backward_rec(Ctx& C, const Rec& r) {
       TensorRec& x = C.T(r.in[0]);
       TensorRec& w = C.T(r.in[1]);
       const int64_t rows = x.rows(), K = w.shape[0], N = w.shape[1];
+      const Opnd go = op_grad(C, out);
       auto dx = C.gdst(r.in[0]);
-      gemm_nt(C, g, w.data, dx.first, rows, N, K, dx.second);           // dx = g @ w^T
+      gemm_nt(C, go, op_data(C, w), dx.first, rows, N, K, dx.second);   // dx = g @ w^T
       auto dw = C.gdst(r.in[1]);
-      gemm_tn(C, x.data, g, dw.first, K, rows, N, dw.second);            // dw = x^T @ g
+      gemm_tn(C, op_data(C, x), go, dw.first, K, rows, N, dw.second);   // dw = x^T @ g
       if (r.op == OP_LINEAR) {
         auto db = C.gdst(r.in[2]);
         size_t mark = C.c->arena.hi;
@@ -420,10 +507,12 @@ void backward_rec(Ctx& C, const Rec& r) {
       TensorRec& x = C.T(r.in[0]);
       TensorRec& w = C.T(r.in[1]);
       const int64_t rows = x.rows(), V = w.shape[0], Cc = w.shape[1];
+      const Opnd go = op_grad(C, out);
+      const int64_t ldg = out.stride();
       auto dx = C.gdst(r.in[0]);
-      gemm_nn(C, g, w.data, dx.first, rows, V, Cc, dx.second, nullptr);  // dx = g @ w
+      gemm_nn(C, go, op_data(C, w), dx.first, rows, V, Cc, dx.second, nullptr, ldg);  // dx = g @ w
       auto dw = C.gdst(r.in[1]);
-      gemm_tn(C, g, x.data, dw.first, V, rows, Cc, dw.second);           // dw = g^T @ x
+      gemm_tn(C, go, op_data(C, x), dw.first, V, rows, Cc, dw.second, ldg);           // dw = g^T @ x
       break;
     }
     case OP_LAYERNORM: {
@@ -574,9 +663,15 @@ void backward_rec(Ctx& C, const Rec& r) {
     case OP_SOFTMAX_CE: {
       TensorRec& lg = C.T(r.in[0]);
       auto dl = C.gdst(r.in[0]);
-      hip_check(softmax_ce_bwd(lg.data, static_cast<const int32_t*>(r.s0), static_cast<const float*>(r.s1), g,
-                               dl.first, lg.rows(), lg.cols(), dl.second, s),
+      hip_check(softmax_ce_bwd(lg.data, lg.stride(), static_cast<const int32_t*>(r.s0),
+                               static_cast<const float*>(r.s1), g, dl.first, lg.rows(), lg.cols(), dl.second, s),
                 "softmax_ce bwd");
+      break;
+    }
+    case OP_COMPACT: {
+      TensorRec& x = C.T(r.in[0]);
+      auto dx = C.gdst(r.in[0]);
+      hip_check(copy_pitched(g, out.cols(), dx.first, x.stride(), x.rows(), x.cols(), dx.second, s), "compact bwd");
       break;
     }
   }
@@ -706,7 +801,13 @@ int tfb_tensor_write(tfb_ctx* ctx, tfb_tensor h, const float* src, int64_t n) {
     TensorRec& t = C.T(h);
     need(src != nullptr && n == t.numel, TFB_ERR_SHAPE, "write of " + std::to_string(n) + " floats into " +
                                                             shape_str(t));
-    hip_check(hipMemcpyAsync(t.data, src, (size_t)n * sizeof(float), hipMemcpyHostToDevice, C.s()), "copy in");
+    if (t.padded())
+      hip_check(hipMemcpy2DAsync(t.data, t.ld * sizeof(float), src, t.cols() * sizeof(float),
+                                 t.cols() * sizeof(float), t.rows(), hipMemcpyHostToDevice, C.s()),
+                "copy in");
+    else
+      hip_check(hipMemcpyAsync(t.data, src, (size_t)n * sizeof(float), hipMemcpyHostToDevice, C.s()), "copy in");
+    t.bf_valid = false;
     hip_check(hipStreamSynchronize(C.s()), "sync");
   });
 }
@@ -724,7 +825,12 @@ int tfb_tensor_read(tfb_ctx* ctx, tfb_tensor h, int which, float* dst, int64_t n
       C.materialize_zero(t);
       src = t.grad;
     }
-    hip_check(hipMemcpyAsync(dst, src, (size_t)n * sizeof(float), hipMemcpyDeviceToHost, C.s()), "copy out");
+    if (t.padded())
+      hip_check(hipMemcpy2DAsync(dst, t.cols() * sizeof(float), src, t.ld * sizeof(float), t.cols() * sizeof(float),
+                                 t.rows(), hipMemcpyDeviceToHost, C.s()),
+                "copy out");
+    else
+      hip_check(hipMemcpyAsync(dst, src, (size_t)n * sizeof(float), hipMemcpyDeviceToHost, C.s()), "copy out");
     hip_check(hipStreamSynchronize(C.s()), "sync");
   });
 }
@@ -748,6 +854,7 @@ int tfb_tensor_release(tfb_ctx* ctx, tfb_tensor h) {
 int tfb_add(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    a = C.dense_in(a), b = C.dense_in(b);
     TensorRec& A = C.T(a);
     TensorRec& B = C.T(b);
     need(y != nullptr, TFB_ERR_ARG, "null output");
@@ -769,6 +876,7 @@ int tfb_add(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y) {
 int tfb_mul(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    a = C.dense_in(a), b = C.dense_in(b);
     TensorRec& A = C.T(a);
     TensorRec& B = C.T(b);
     need(y != nullptr, TFB_ERR_ARG, "null output");
@@ -786,6 +894,7 @@ int tfb_mul(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y) {
 int tfb_scale(tfb_ctx* ctx, tfb_tensor a, float sc, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    a = C.dense_in(a);
     TensorRec& A = C.T(a);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     int h = C.make_output(shape_vec(A));
@@ -800,6 +909,7 @@ int tfb_scale(tfb_ctx* ctx, tfb_tensor a, float sc, tfb_tensor* y) {
 int tfb_sum(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    a = C.dense_in(a);
     C.T(a);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     int h = C.make_output({1});
@@ -817,6 +927,7 @@ int tfb_sum(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
 int tfb_reshape(tfb_ctx* ctx, tfb_tensor a, const int64_t* shape, int ndim, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    a = C.dense_in(a);
     TensorRec& A = C.T(a);
     need(y != nullptr && shape != nullptr, TFB_ERR_ARG, "null argument");
     int64_t n = Ctx::numel_of(shape, ndim);
@@ -840,6 +951,7 @@ int tfb_reshape(tfb_ctx* ctx, tfb_tensor a, const int64_t* shape, int ndim, tfb_
 int tfb_tanh(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    a = C.dense_in(a);
     TensorRec& A = C.T(a);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     int h = C.make_output(shape_vec(A));
@@ -854,6 +966,7 @@ int tfb_tanh(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
 int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    a = C.dense_in(a);
     TensorRec& A = C.T(a);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     int h = C.make_output(shape_vec(A));
@@ -868,6 +981,8 @@ int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
 static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y, OpKind kind) {
   return guarded([&] {
     Ctx C(ctx);
+    x = C.dense_in(x), w = C.dense_in(w);
+    if (kind == OP_LINEAR) b = C.dense_in(b);
     TensorRec& X = C.T(x);
     TensorRec& W = C.T(w);
     need(y != nullptr, TFB_ERR_ARG, "null output");
@@ -890,14 +1005,19 @@ static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, t
     check_gemm_dims(rows, K, N);
     std::vector<int64_t> shp = shape_vec(X);
     shp.back() = N;
-    int h = C.make_output(shp);
+    // a vocabulary-sized LM-head output gets rows padded to a multiple of 64
+    // floats so that its rows (and its gradient's) stay 16-byte aligned
+    const int64_t ld = (kind == OP_MATMUL_T && N % 64 != 0 && N >= 1024) ? (N + 63) / 64 * 64 : 0;
+    int h = C.make_output(shp, ld);
     float* yd = ctx->tensors[h].data;
     const float* xd = ctx->tensors[x].data;
     const float* wd = ctx->tensors[w].data;
+    const Opnd xo = op_data(C, ctx->tensors[x]), wo = op_data(C, ctx->tensors[w]);
+    (void)xd, (void)wd;
     if (kind == OP_MATMUL_T)
-      gemm_nt(C, xd, wd, yd, rows, K, N, 0.f);
+      gemm_nt(C, xo, wo, yd, rows, K, N, 0.f, ld ? ld : N);
     else
-      gemm_nn(C, xd, wd, yd, rows, K, N, 0.f, bias);
+      gemm_nn(C, xo, wo, yd, rows, K, N, 0.f, bias);
     Rec r{kind};
     r.in[0] = x, r.in[1] = w, r.in[2] = kind == OP_LINEAR ? b : -1, r.out = h;
     C.record(r);
@@ -918,6 +1038,7 @@ int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tenso
 int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    x = C.dense_in(x), gamma = C.dense_in(gamma), beta = C.dense_in(beta);
     TensorRec& X = C.T(x);
     TensorRec& G = C.T(gamma);
     TensorRec& Bt = C.T(beta);
@@ -943,6 +1064,7 @@ int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta,
 int tfb_embedding(tfb_ctx* ctx, tfb_tensor table, const int32_t* dev_ids, int64_t n, int64_t batch, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    table = C.dense_in(table);
     TensorRec& Tb = C.T(table);
     need(y != nullptr && dev_ids != nullptr, TFB_ERR_ARG, "null argument");
     need(Tb.ndim == 2, TFB_ERR_SHAPE, "embedding table must be 2-D");
@@ -966,6 +1088,7 @@ int tfb_embedding(tfb_ctx* ctx, tfb_tensor table, const int32_t* dev_ids, int64_
 int tfb_narrow(tfb_ctx* ctx, tfb_tensor x, int64_t start, int64_t len, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    x = C.dense_in(x);
     TensorRec& X = C.T(x);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     need(start >= 0 && len >= 0 && start + len <= X.cols(), TFB_ERR_SHAPE, "narrow out of range");
@@ -984,6 +1107,7 @@ int tfb_narrow(tfb_ctx* ctx, tfb_tensor x, int64_t start, int64_t len, tfb_tenso
 int tfb_split_heads(tfb_ctx* ctx, tfb_tensor x, int heads, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    x = C.dense_in(x);
     TensorRec& X = C.T(x);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     need(X.ndim == 3 && heads > 0 && X.shape[2] % heads == 0, TFB_ERR_SHAPE,
@@ -1002,6 +1126,7 @@ int tfb_split_heads(tfb_ctx* ctx, tfb_tensor x, int heads, tfb_tensor* y) {
 int tfb_merge_heads(tfb_ctx* ctx, tfb_tensor x, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    x = C.dense_in(x);
     TensorRec& X = C.T(x);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     need(X.ndim == 4, TFB_ERR_SHAPE, "merge_heads needs [B, H, T, hs], got " + shape_str(X));
@@ -1019,6 +1144,7 @@ int tfb_merge_heads(tfb_ctx* ctx, tfb_tensor x, tfb_tensor* y) {
 static int bmm_impl(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y, bool transb) {
   return guarded([&] {
     Ctx C(ctx);
+    a = C.dense_in(a), b = C.dense_in(b);
     TensorRec& A = C.T(a);
     TensorRec& B = C.T(b);
     need(y != nullptr, TFB_ERR_ARG, "null output");
@@ -1059,6 +1185,7 @@ int tfb_batch_matmul_t(tfb_ctx* ctx, tfb_tensor a, tfb_tensor b, tfb_tensor* y) 
 int tfb_causal_softmax(tfb_ctx* ctx, tfb_tensor sx, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    sx = C.dense_in(sx);
     TensorRec& S = C.T(sx);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     const int64_t rows = S.rows(), T = S.cols();
@@ -1075,6 +1202,7 @@ int tfb_causal_softmax(tfb_ctx* ctx, tfb_tensor sx, tfb_tensor* y) {
 int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    qkv = C.dense_in(qkv);
     TensorRec& Q = C.T(qkv);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     need(Q.ndim == 3 && Q.shape[2] % 3 == 0 && heads > 0 && (Q.shape[2] / 3) % heads == 0, TFB_ERR_SHAPE,
@@ -1131,7 +1259,8 @@ int tfb_softmax_cross_entropy(tfb_ctx* ctx, tfb_tensor logits, const int32_t* de
                 "copy targets");
     size_t mark = ctx->arena.hi;
     void* ws = C.scratch(softmax_ce_workspace_bytes(rows));
-    hip_check(softmax_ce_fwd(ctx->tensors[logits].data, tg, rows, V, lse, ctx->tensors[h].data, ws, C.s()),
+    hip_check(softmax_ce_fwd(ctx->tensors[logits].data, ctx->tensors[logits].stride(), tg, rows, V, lse,
+                             ctx->tensors[h].data, ws, C.s()),
               "softmax_ce");
     ctx->arena.hi = mark;
     Rec r{OP_SOFTMAX_CE};
@@ -1148,8 +1277,10 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
     Ctx C(ctx);
     TensorRec& L = C.T(loss);
     need(L.numel == 1, TFB_ERR_STATE, "backward() starts from a scalar loss");
-    for (TensorRec& t : ctx->tensors)
+    for (TensorRec& t : ctx->tensors) {
       if (t.live && !t.leaf && t.grad) t.gstate = G_ZERO;
+      t.gbf_valid = false;
+    }
     C.ensure_grad_buffer(L);
     hip_check(fill(L.grad, 1.f, 1, C.s()), "seed");
     L.gstate = G_VALID;
@@ -1169,6 +1300,7 @@ int tfb_zero_grad(tfb_ctx* ctx, const tfb_tensor* params, int n) {
     for (int i = 0; i < n; ++i) {
       TensorRec& t = C.T(params[i]);
       if (t.grad) t.gstate = G_ZERO;
+      t.gbf_valid = false;
     }
   });
 }
@@ -1238,22 +1370,25 @@ int tfb_adamw_step(tfb_opt* o) {
     tfb_ctx* ctx = o->ctx;
     // parameters without a gradient are skipped; a cleared gradient reads as zeros
     std::vector<int> active;
+    std::vector<uint16_t*> shadows;
     for (int i = 0; i < (int)o->params.size(); ++i) {
       TensorRec& t = C.T(o->params[i]);
       if (!t.grad) continue;
       C.materialize_zero(t);
       active.push_back(i);
+      shadows.push_back(t.bf);
     }
     o->t += 1;
     const float bc1 = 1.f - std::pow(o->b1, (float)o->t);
     const float bc2 = 1.f - std::pow(o->b2, (float)o->t);
-    if (active != o->uploaded_active) {
+    if (active != o->uploaded_active || shadows != o->uploaded_shadows) {
       std::vector<AdamSeg> segs;
       std::vector<AdamChunk> chunks;
       for (int i : active) {
         TensorRec& t = C.T(o->params[i]);
         AdamSeg sg;
         sg.p = t.data, sg.g = t.grad, sg.m = o->m[i], sg.v = o->v[i], sg.n = t.numel;
+        sg.pbf = t.bf;  // the step keeps an existing bf16 copy current
         sg.wd = t.ndim >= 2 ? o->wd : 0.f;
         sg.pad = 0;
         for (int64_t off = 0; off < t.numel; off += o->chunk_elems) {
@@ -1273,6 +1408,11 @@ int tfb_adamw_step(tfb_opt* o) {
       }
       o->nchunks = (int)chunks.size();
       o->uploaded_active = active;
+      o->uploaded_shadows = shadows;
+    }
+    for (int i : active) {
+      TensorRec& t = C.T(o->params[i]);
+      t.bf_valid = t.bf != nullptr;
     }
     (void)ctx;
     hip_check(adamw_step(o->d_segs, o->d_chunks, o->nchunks, o->chunk_elems, o->lr, o->b1, o->b2, o->eps, bc1, bc2,
@@ -1342,6 +1482,7 @@ int tfb_sgd_step(tfb_ctx* ctx, const tfb_tensor* params, int n, float lr) {
       if (!t.grad) continue;
       C.materialize_zero(t);
       hip_check(sgd_step(t.data, t.grad, lr, t.numel, C.s()), "sgd");
+      t.bf_valid = false;
     }
   });
 }
