@@ -343,3 +343,13 @@ def test_padded_output_feeds_other_ops(ctx):
     """Another op consuming a padded LM-head output gets a recorded dense copy."""
     check(ctx, "fp32", lambda x, w: T.tanh(T.matmul_t(x, w)), lambda x, w: E.tanh(E.matmul_t(x, w)),
           [rnd(44, (70, 32)), rnd(45, (1100, 32), 0.2)], (70, 1100))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_causal_attention_gpt2_shape(ctx, prec):
+    """At the GPT-2 step's own shape (8 x 1024 tokens, 12 heads of 64) -- the fused
+    kernels in the bf16 variant, the materialised path in fp32."""
+    B, Tn, H, hs = 8, 1024, 12, 64
+    qkv = rnd(46, (B, Tn, 3 * H * hs))
+    check(ctx, prec, lambda a: T.causal_attention(a, H), lambda a: _attention_oracle(a, H), [qkv],
+          (B, Tn, H * hs))

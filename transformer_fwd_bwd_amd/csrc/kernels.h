@@ -98,6 +98,17 @@ hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* target
 hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* targets, const float* lse,
                           const float* g_scalar, float* dl, int64_t rows, int64_t V, float beta, hipStream_t s);
 
+// ---- fused causal attention, bf16 variant (attention.hip)
+// qkv: bf16 [B, T, 3C] (q | k | v thirds, head h = columns h*hs .. h*hs+hs-1 of each third)
+// y: fp32 [B, T, C]; lse: [B*H, T] base-2 log-sum-exp of the scaled scores (saved for backward)
+bool flash_attention_supported(int hs, int64_t C);
+hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, float* lse, int B, int T, int H, int C, float scale,
+                               hipStream_t s);
+// dqkv = beta*dqkv + d(qkv); D: [B*H, T] scratch
+hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float* dyf, const uint16_t* dy,
+                               const float* lse, float* D, float* dqkv, float beta, int B, int T, int H, int C,
+                               float scale, hipStream_t s);
+
 // ---- embedding (embedding.hip)
 // ids outside [0, rows) give zero rows forward and are skipped backward
 hipError_t embedding_fwd(const float* table, int64_t rows, const int32_t* ids, float* y, int64_t n, int64_t C,

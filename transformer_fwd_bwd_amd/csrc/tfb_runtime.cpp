@@ -611,6 +611,18 @@ void backward_rec(Ctx& C, const Rec& r) {
       TensorRec& qkv = C.T(r.in[0]);
       const int64_t B = qkv.shape[0], T = qkv.shape[1], C3 = qkv.shape[2], Cc = C3 / 3, H = r.i0, hs = Cc / H;
       const float scale = r.f;
+      if (r.i1 == 1) {  // fused kernels: recompute probabilities from the saved log-sum-exp
+        const uint16_t* qb = C.data_bf16(qkv);
+        const uint16_t* dyb = C.grad_bf16(out);
+        auto dq = C.gdst(r.in[0]);
+        size_t mark = C.c->arena.hi;
+        float* D = static_cast<float*>(C.scratch((size_t)B * H * T * sizeof(float)));
+        hip_check(flash_attention_bwd(qb, out.data, g, dyb, static_cast<const float*>(r.s1), D, dq.first, dq.second,
+                                      (int)B, (int)T, (int)H, (int)Cc, scale, s),
+                  "attention bwd");
+        C.c->arena.hi = mark;
+        break;
+      }
       float* P = static_cast<float*>(r.s0);
       // the gradient buffer first: it must outlive the scratch released below
       auto dq = C.gdst(r.in[0]);
@@ -1212,6 +1224,19 @@ int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y)
     need(B * H < 65536, TFB_ERR_SHAPE, "too many (batch, head) pairs");
     const float scale = 1.f / std::sqrt((float)hs);
     int h = C.make_output({B, T, Cc});
+    if (C.bf16_mode() && flash_attention_supported((int)hs, Cc) && T < (1 << 30)) {
+      // bf16 variant: fused kernels, no T x T buffers
+      const uint16_t* qb = C.data_bf16(ctx->tensors[qkv]);
+      float* lse = static_cast<float*>(C.scratch((size_t)B * H * T * sizeof(float)));
+      hip_check(flash_attention_fwd(qb, ctx->tensors[h].data, lse, (int)B, (int)T, (int)H, (int)Cc, scale, C.s()),
+                "attention");
+      Rec r{OP_ATTENTION};
+      r.in[0] = qkv, r.out = h, r.i0 = H, r.i1 = 1, r.f = scale;
+      r.s1 = lse;
+      C.record(r);
+      *y = h;
+      return;
+    }
     float* P = static_cast<float*>(C.scratch((size_t)B * H * T * T * sizeof(float)));
     const float* q = ctx->tensors[qkv].data;
     float* yd = ctx->tensors[h].data;
