@@ -103,14 +103,24 @@ __global__ void colsum_stage1(const float* __restrict__ g, int64_t rows, int64_t
   partial[(int64_t)blockIdx.y * cols + c] = (s0 + s1) + (s2 + s3);
 }
 
-__global__ void colsum_stage2(const float* __restrict__ partial, int nparts, int64_t cols, float* __restrict__ out,
-                              float beta) {
-  const int64_t c = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (c >= cols) return;
-  float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += partial[(int64_t)p * cols + c];
-  if (beta != 0.f) s += beta * out[c];
-  out[c] = s;
+// out[c] (+)= sum over the partial rows; 64 columns x 16 partial-groups per workgroup
+__global__ __launch_bounds__(1024) void colsum_stage2(const float* __restrict__ partial, int nparts, int64_t cols,
+                                                      float* __restrict__ out, float beta) {
+  __shared__ float sh[16][65];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 64 + tx;
+  float a = 0.f;
+  if (c < cols)
+    for (int p = ty; p < nparts; p += 16) a += partial[(int64_t)p * cols + c];
+  sh[ty][tx] = a;
+  __syncthreads();
+  if (ty == 0 && c < cols) {
+    float r = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += sh[i][tx];
+    if (beta != 0.f) r += beta * out[c];
+    out[c] = r;
+  }
 }
 
 __device__ __forceinline__ float block_sum(float v) {
@@ -295,8 +305,8 @@ hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float 
   float* partial = static_cast<float*>(ws);
   dim3 g1((unsigned)((cols + NT - 1) / NT), (unsigned)parts);
   hipLaunchKernelGGL(colsum_stage1, g1, dim3(NT), 0, s, g, rows, cols, rows_per, partial);
-  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + NT - 1) / NT)), dim3(NT), 0, s, partial, (int)parts,
-                     cols, out, beta);
+  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, (int)parts, cols,
+                     out, beta);
   return hipGetLastError();
 }
 

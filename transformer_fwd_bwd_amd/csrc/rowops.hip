@@ -13,6 +13,8 @@
 namespace tfb {
 namespace {
 
+typedef float f4 __attribute__((ext_vector_type(4)));
+
 constexpr int NT = 256;
 constexpr int WAVES = NT / 64;
 constexpr int MAXV = 16;  // cached values per lane -> rows up to 1024
@@ -77,6 +79,88 @@ __global__ __launch_bounds__(NT) void ln_fwd_k(const float* __restrict__ x, cons
     if (lane == 0) {
       mean[r] = mu;
       rstd[r] = rs;
+    }
+  }
+}
+
+// float4 variants: rows of C = 4 * 64 * J floats or fewer (C % 4 == 0, C <= 1024),
+// lane holds the quads lane + 64 j
+template <int J>
+__global__ __launch_bounds__(NT) void ln_fwd4_k(const f4* __restrict__ x, const f4* __restrict__ gamma,
+                                                const f4* __restrict__ beta, f4* __restrict__ y,
+                                                float* __restrict__ mean, float* __restrict__ rstd, int64_t rows,
+                                                int C4, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * WAVES;
+  const float invC = 1.f / (4 * C4);
+  for (int64_t r = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); r < rows; r += nw) {
+    const f4* xr = x + r * C4;
+    f4 v[J];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = lane + 64 * j;
+      v[j] = c < C4 ? xr[c] : f4{0.f, 0.f, 0.f, 0.f};
+      s += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
+    }
+    const float mu = wave_sum(s) * invC;
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = lane + 64 * j;
+      if (c < C4) {
+        const f4 d = v[j] - mu;
+        q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+      }
+    }
+    const float rs = rsqrtf(wave_sum(q) * invC + eps);
+    f4* yr = y + r * C4;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = lane + 64 * j;
+      if (c < C4) yr[c] = (v[j] - mu) * rs * gamma[c] + beta[c];
+    }
+    if (lane == 0) {
+      mean[r] = mu;
+      rstd[r] = rs;
+    }
+  }
+}
+
+template <int J>
+__global__ __launch_bounds__(NT) void ln_bwd_dx4_k(const f4* __restrict__ g, const f4* __restrict__ x,
+                                                   const f4* __restrict__ gamma, const float* __restrict__ mean,
+                                                   const float* __restrict__ rstd, f4* __restrict__ dx, int64_t rows,
+                                                   int C4, float beta_dx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * WAVES;
+  const float invC = 1.f / (4 * C4);
+  for (int64_t r = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); r < rows; r += nw) {
+    const float mu = mean[r], rs = rstd[r];
+    f4 xh[J], dg[J];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = lane + 64 * j;
+      if (c < C4) {
+        xh[j] = (x[r * C4 + c] - mu) * rs;
+        dg[j] = g[r * C4 + c] * gamma[c];
+      } else {
+        xh[j] = dg[j] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+      s1 += (dg[j][0] + dg[j][1]) + (dg[j][2] + dg[j][3]);
+      const f4 t = dg[j] * xh[j];
+      s2 += (t[0] + t[1]) + (t[2] + t[3]);
+    }
+    const float m1 = wave_sum(s1) * invC, m2 = wave_sum(s2) * invC;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = lane + 64 * j;
+      if (c < C4) {
+        f4 v = rs * (dg[j] - m1 - xh[j] * m2);
+        if (beta_dx != 0.f) v += dx[r * C4 + c];
+        dx[r * C4 + c] = v;
+      }
     }
   }
 }
@@ -166,23 +250,39 @@ __global__ __launch_bounds__(NT) void ln_bwd_cols_k(const float* __restrict__ g,
   part[((int64_t)blockIdx.y * 2 + 1) * C + c] = b;
 }
 
-__global__ void ln_bwd_reduce(const float* __restrict__ part, int nparts, int C, float* __restrict__ dgamma,
-                              float* __restrict__ dbeta, float beta_dg, float beta_db) {
-  const int c = blockIdx.x * NT + threadIdx.x;
-  if (c >= C) return;
+// out_a[c] (+)= sum_p part[p][0][c], out_b[c] (+)= sum_p part[p][1][c]; 64 columns x 16 groups per workgroup
+__global__ __launch_bounds__(1024) void ln_bwd_reduce(const float* __restrict__ part, int nparts, int C,
+                                                      float* __restrict__ dgamma, float* __restrict__ dbeta,
+                                                      float beta_dg, float beta_db) {
+  __shared__ float sa[16][65], sb[16][65];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + tx;
   float a = 0.f, b = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    a += part[((int64_t)p * 2) * C + c];
-    b += part[((int64_t)p * 2 + 1) * C + c];
+  if (c < C) {
+    for (int p = ty; p < nparts; p += 16) {
+      a += part[((int64_t)p * 2) * C + c];
+      b += part[((int64_t)p * 2 + 1) * C + c];
+    }
   }
-  if (beta_dg != 0.f) a += dgamma[c];
-  if (beta_db != 0.f) b += dbeta[c];
-  dgamma[c] = a;
-  dbeta[c] = b;
+  sa[ty][tx] = a;
+  sb[ty][tx] = b;
+  __syncthreads();
+  if (ty == 0 && c < C) {
+    float ra = 0.f, rb = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ra += sa[i][tx];
+      rb += sb[i][tx];
+    }
+    if (beta_dg != 0.f) ra += dgamma[c];
+    if (beta_db != 0.f) rb += dbeta[c];
+    dgamma[c] = ra;
+    dbeta[c] = rb;
+  }
 }
 
 int ln_bwd_parts(int64_t rows) {
-  return (int)std::max<int64_t>(1, std::min<int64_t>(256, (rows + 31) / 32));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(128, (rows + 31) / 32));
 }
 
 // ------------------------------------------------------------ causal softmax
@@ -368,6 +468,8 @@ __global__ __launch_bounds__(NT) void ce_bwd_k(const float* __restrict__ logits,
   }
 }
 
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 inline unsigned row_blocks(int64_t rows) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>((rows + WAVES - 1) / WAVES, 65536));
 }
@@ -377,7 +479,15 @@ inline unsigned row_blocks(int64_t rows) {
 hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, float* y, float* mean, float* rstd,
                          int64_t rows, int64_t C, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (C <= 64 * MAXV)
+  if (C % 4 == 0 && C <= 1024 && aligned16(x) && aligned16(y) && aligned16(gamma) && aligned16(beta)) {
+    const int C4 = (int)(C / 4);
+    if (C4 <= 64)
+      hipLaunchKernelGGL(ln_fwd4_k<1>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
+                         (const f4*)beta, (f4*)y, mean, rstd, rows, C4, eps);
+    else
+      hipLaunchKernelGGL(ln_fwd4_k<4>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
+                         (const f4*)beta, (f4*)y, mean, rstd, rows, C4, eps);
+  } else if (C <= 64 * MAXV)
     hipLaunchKernelGGL(ln_fwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, mean, rstd, rows,
                        (int)C, eps);
   else
@@ -395,7 +505,15 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
                          float beta_dg, float beta_db, void* ws, hipStream_t s) {
   if (C <= 0) return hipSuccess;
   if (rows > 0) {
-    if (C <= 64 * MAXV)
+    if (C % 4 == 0 && C <= 1024 && aligned16(g) && aligned16(x) && aligned16(gamma) && aligned16(dx)) {
+      const int C4 = (int)(C / 4);
+      if (C4 <= 64)
+        hipLaunchKernelGGL(ln_bwd_dx4_k<1>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
+                           (const f4*)gamma, mean, rstd, (f4*)dx, rows, C4, beta_dx);
+      else
+        hipLaunchKernelGGL(ln_bwd_dx4_k<4>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
+                           (const f4*)gamma, mean, rstd, (f4*)dx, rows, C4, beta_dx);
+    } else if (C <= 64 * MAXV)
       hipLaunchKernelGGL(ln_bwd_dx_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
                          rows, (int)C, beta_dx);
     else
@@ -407,7 +525,7 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
   float* part = static_cast<float*>(ws);
   hipLaunchKernelGGL(ln_bwd_cols_k, dim3((unsigned)((C + NT - 1) / NT), (unsigned)parts), dim3(NT), 0, s, g, x,
                      mean, rstd, part, rows, (int)C, rows_per);
-  hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + NT - 1) / NT)), dim3(NT), 0, s, part, parts, (int)C, dgamma,
+  hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + 63) / 64)), dim3(1024), 0, s, part, parts, (int)C, dgamma,
                      dbeta, beta_dg, beta_db);
   return hipGetLastError();
 }
