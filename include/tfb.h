@@ -196,6 +196,29 @@ int tfb_adamw_destroy(tfb_opt* opt);
  * [Autograd-1, "The Optimizer": SGD] */
 int tfb_sgd_step(tfb_ctx* ctx, const tfb_tensor* params, int n, float lr);
 
+/* ---------------------------------------------------------------- KV-cached inference
+ * [GPT2-4, "Generation with KV cache"; "Temperature and Top-k"].  None of these
+ * calls is recorded on the tape. */
+
+typedef struct tfb_kv tfb_kv;
+/* A key/value cache of `layers` x 2 x batch x tmax x channels fp32 values in the
+ * persistent arena, zero-filled (tmax <= 16384). */
+int tfb_kv_create(tfb_ctx* ctx, int layers, int batch, int tmax, int channels, tfb_kv** out);
+int tfb_kv_destroy(tfb_kv* kv);
+/* Copy the keys and values (the second and third column thirds) of qkv
+ * [batch, T, 3C] into positions pos0 .. pos0+T-1 of `layer` (a batched prompt). */
+int tfb_kv_store(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos0);
+/* One new token per sequence: qkv [batch, 1, 3C].  Appends its key and value at
+ * `pos`, then y[b, 0, head slice] = sum_j softmax_j(q . k_j / sqrt(hs)) v_j over
+ * positions 0..pos -- no mask, the cache holds only the past.  y [batch, 1, C]. */
+int tfb_kv_attend(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos, int heads, tfb_tensor* y);
+/* One id per row of logits [..., V]: keep every logit >= the k-th largest (ties
+ * kept; k = 0 or k >= V keeps all), p = softmax((l - max)/temperature) summed in
+ * double, and return the first id (ascending) whose cumulative p exceeds u[row].
+ * dev_uniforms: rows doubles in [0, 1); dev_out: rows int32 (device memory). */
+int tfb_sample_topk(tfb_ctx* ctx, tfb_tensor logits, int k, float temperature, const double* dev_uniforms,
+                    int32_t* dev_out);
+
 /* ---------------------------------------------------------------- measurement */
 
 /* Between begin and end, every contraction launch (the MatMul family and the

@@ -1,0 +1,134 @@
+"""KV-cached inference through the C ABI against the oracle: the top-k /
+temperature sampler, the per-step logits of generation (teacher-forced: the
+oracle consumes the GPU's sampled tokens), the pages' invariant that the cached
+path equals the full forward, and the inference workload at its own size
+(16 prompts of 768 tokens, 256 sampled steps)."""
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import decode as D
+from oracle import engine as E
+from oracle import models as M
+from parity import FWD_TOL, assert_close
+
+pytestmark = pytest.mark.gpu
+
+T = pytest.importorskip("transformer_fwd_bwd_amd")
+from transformer_fwd_bwd_amd import gpt as G  # noqa: E402
+
+
+def near_boundary(probs, u, tol=1e-6):
+    c = np.cumsum(probs)
+    return np.min(np.abs(c - u)) < tol
+
+
+def test_sampler_matches_oracle(ctx):
+    import torch
+    rng = S.rng_for(70)
+    B, V = 6, 1000
+    logits = rng.standard_normal((B, V)).astype(np.float32) * 3
+    logits[0, :50] = 2.5           # a block of ties across the k-th value
+    logits[1, :] = 0.0             # all equal
+    u = rng.random(B)
+    for k, temp in ((40, 1.0), (1, 1.0), (0, 0.7), (5, 2.0)):
+        lt = ctx.tensor(logits.shape, logits)
+        ud = torch.from_numpy(u).to("cuda:0")
+        got = T.sample_topk(lt, k, temp, ud).cpu().numpy()
+        for b in range(B):
+            p = D.top_k_temperature_probs(logits[b].astype(np.float64), k, temp)
+            want = D.sample(p, u[b])
+            assert got[b] == want or near_boundary(p, u[b]), (k, b, got[b], want)
+        lt.release()
+        ctx.tape_reset()
+
+
+def _teacher_forced(ctx, prec, B=4, Pn=16, steps=20, k=40, temp=1.0):
+    import torch
+    s, params, _ = S.tiny_gpt()
+    ctx.set_precision(prec)
+    model = G.Gpt(ctx, s.n_layer, s.n_head, params)
+    prompts = S.random_ids(71, (B, Pn), s.vocab)
+    u = S.rng_for(72).random((B, steps))
+    seen = []
+    toks = model.generate(torch.from_numpy(prompts).to("cuda:0"), steps, torch.from_numpy(u).to("cuda:0"), k, temp,
+                          on_step=lambda i, lg, tk: seen.append(lg.numpy().reshape(B, -1)))
+    toks = toks.cpu().numpy()
+    # oracle: every prompt token then every sampled token through its own KV step
+    P64 = {kk: v.astype(np.float64) for kk, v in params.items()}
+    cache = D.KvCache(s.n_layer)
+    for pos in range(Pn - 1):
+        D.step(P64, prompts[:, pos], pos, cache, s.n_layer, s.n_head)
+    tok = prompts[:, -1]
+    for i in range(steps):
+        ref = D.step(P64, tok, Pn - 1 + i, cache, s.n_layer, s.n_head)
+        assert_close(seen[i], ref, FWD_TOL[prec], f"step {i} logits")
+        for b in range(B):
+            p = D.top_k_temperature_probs(ref[b], k, temp)
+            want = D.sample(p, u[b, i])
+            assert toks[b, i] == want or near_boundary(p, u[b, i]) or prec == "bf16", (i, b)
+        tok = toks[:, i]
+    for t in model.param_list:
+        t.release()
+    ctx.set_precision("fp32")
+    return toks
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_generation_teacher_forced_tiny_gpt(ctx, prec):
+    _teacher_forced(ctx, prec)
+
+
+def test_kv_step_equals_full_forward(ctx):
+    """[GPT2-4, "Generation with KV cache"]: the cached step's logits equal the
+    full forward's logits at the same position."""
+    import torch
+    s, params, _ = S.tiny_gpt()
+    model = G.Gpt(ctx, s.n_layer, s.n_head, params)
+    ids = S.random_ids(73, (3, 24), s.vocab)
+    ctx.set_grad_enabled(False)
+    full = model.logits(ids).numpy()
+    ctx.tape_reset()
+    kv = T.KvCache(ctx, s.n_layer, 3, 24, s.n_embd)
+    ids_d = torch.from_numpy(ids).to("cuda:0")
+    model.prefill(ids_d[:, :12].contiguous(), kv)
+    ctx.tape_reset()
+    for pos in range(12, 24):
+        lg = model.decode_step(ids_d[:, pos].contiguous(), pos, kv, 24).numpy().reshape(3, -1)
+        assert_close(lg, full[:, pos], 1e-5, f"pos {pos}")
+        ctx.tape_reset()
+    ctx.set_grad_enabled(True)
+    kv.close()
+    for t in model.param_list:
+        t.release()
+
+
+def test_inference_workload_gpt2_shape(ctx):
+    """16 prompts x 768 tokens, then 256 sampled steps (top-k 40, temperature 1)
+    at the GPT-2-124M shape; sampled steps of sequence 5 against the oracle's
+    full forward over that sequence's prompt and the GPU's sampled tokens."""
+    import torch
+    s, params, prompts, u = S.gpt2_infer()
+    B, Pn = prompts.shape
+    steps = u.shape[1]
+    ctx.set_precision("fp32")
+    big = T.Context(arena_bytes=16 << 30, precision="fp32")
+    model = G.Gpt(big, s.n_layer, s.n_head, params)
+    b, check = 5, (0, 1, 128, 255)
+    seen = {}
+
+    def on_step(i, lg, tk):
+        if i in check:
+            seen[i] = lg.numpy().reshape(B, -1)[b]
+    toks = model.generate(torch.from_numpy(prompts).to("cuda:0"), steps, torch.from_numpy(u).to("cuda:0"), 40, 1.0,
+                          on_step=on_step).cpu().numpy()
+    assert toks.shape == (B, steps) and toks.min() >= 0 and toks.max() < s.vocab
+    seq = np.concatenate([prompts[b], toks[b, :-1]])[None, :]          # 1023 positions
+    with E.no_grad():
+        ref = M.gpt_logits(M.as_tensors(params), seq, s.n_layer, s.n_head).data[0]
+    for i in check:
+        r = ref[Pn - 1 + i]
+        assert_close(seen[i], r, FWD_TOL["fp32"], f"step {i}")
+        p = D.top_k_temperature_probs(r, 40, 1.0)
+        assert toks[b, i] == D.sample(p, u[b, i]) or near_boundary(p, u[b, i]), i
+    big.close()

@@ -69,6 +69,11 @@ SIGNATURES = {
     "tfb_adamw_moments": [c_void_p, c_int, c_void_p, c_void_p, c_int64],
     "tfb_adamw_destroy": [c_void_p],
     "tfb_sgd_step": [c_void_p, P(c_int32), c_int, c_float],
+    "tfb_kv_create": [c_void_p, c_int, c_int, c_int, c_int, P(c_void_p)],
+    "tfb_kv_destroy": [c_void_p],
+    "tfb_kv_store": [c_void_p, c_void_p, c_int, c_int32, c_int],
+    "tfb_kv_attend": [c_void_p, c_void_p, c_int, c_int32, c_int, c_int, P(c_int32)],
+    "tfb_sample_topk": [c_void_p, c_int32, c_int, c_float, c_void_p, c_void_p],
     "tfb_profile_begin": [c_void_p],
     "tfb_profile_end": [c_void_p, P(ctypes.c_double), P(ctypes.c_double), P(c_int)],
 }
@@ -369,6 +374,38 @@ class AdamW:
         if getattr(self, "ptr", None):
             _check(_lib.tfb_adamw_destroy(self.ptr))
             self.ptr = None
+
+
+# ------------------------------------------------------------------------- KV-cached inference
+class KvCache:
+    def __init__(self, ctx: Context, layers: int, batch: int, tmax: int, channels: int):
+        self.ctx = ctx
+        ptr = c_void_p()
+        _check(_lib.tfb_kv_create(ctx.ptr, layers, batch, tmax, channels, ctypes.byref(ptr)))
+        self.ptr = ptr
+
+    def store(self, layer: int, qkv: Tensor, pos0: int):
+        _check(_lib.tfb_kv_store(self.ctx.ptr, self.ptr, layer, qkv.h, pos0))
+
+    def attend(self, layer: int, qkv: Tensor, pos: int, heads: int) -> Tensor:
+        return _out(self.ctx, _lib.tfb_kv_attend, self.ptr, layer, qkv.h, pos, heads)
+
+    def close(self):
+        if getattr(self, "ptr", None):
+            _check(_lib.tfb_kv_destroy(self.ptr))
+            self.ptr = None
+
+
+def sample_topk(logits: Tensor, k: int, temperature: float, uniforms, out=None):
+    """uniforms: a float64 device tensor (one per row); returns an int32 device tensor of ids."""
+    import torch
+    ctx = logits.ctx
+    rows = logits.size // logits.shape[-1]
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int32, device=f"cuda:{ctx.device}")
+    _check(_lib.tfb_sample_topk(ctx.ptr, logits.h, int(k), c_float(temperature), c_void_p(uniforms.data_ptr()),
+                                c_void_p(out.data_ptr())))
+    return out
 
 
 def sgd_step(params: Sequence[Tensor], lr: float):

@@ -1,0 +1,227 @@
+// KV-cached inference ([GPT2-4, "Generation with KV cache" and "Temperature
+// and Top-k"]).
+//
+// Cache layout: fp32 [L][2][B][Tmax][C] (keys then values of every layer);
+// position p of sequence b in layer l is one contiguous row of C floats, so a
+// head's slice is hs contiguous floats.
+//
+// kv_attend: one workgroup per (sequence, head).  It appends the new token's
+// key and value at position pos, then computes the single-query attention
+// over positions 0..pos: scores q.k_j / sqrt(hs) (no mask: the cache holds
+// only the past), a softmax, and sum_j p_j v_j.  Memory-bound: every cached
+// key and value of the head is read once.
+//
+// sample_topk: one workgroup per sequence.  The k-th largest logit is found
+// exactly by a 32-step bitwise search over order-preserving integer keys
+// (count of keys >= candidate, one block reduction per step); every logit
+// below it is dropped and ties with it are kept; exp((l - max)/T) is summed
+// in double; the drawn id is the first (in ascending id order) whose
+// cumulative weight exceeds u * sum, found by a block scan over contiguous id
+// ranges and a walk inside the range that contains the crossing.
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace tfb {
+namespace {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  float r = sh[0];
+  for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, sh[i]);
+  return r;
+}
+
+__device__ __forceinline__ float block_sumf(float v, float* sh) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  float r = 0.f;
+  for (int i = 0; i < NT / 64; ++i) r += sh[i];
+  return r;
+}
+
+__device__ __forceinline__ int block_sumi(int v, int* sh) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  int r = 0;
+  for (int i = 0; i < NT / 64; ++i) r += sh[i];
+  return r;
+}
+
+// key(x) is increasing in x for every finite float
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__global__ __launch_bounds__(NT) void kv_store_k(const float* __restrict__ qkv, int64_t T, int C, float* __restrict__ kv,
+                                                 int layer, int B, int Tmax, int pos0) {
+  // qkv [B, T, 3C] -> cache rows pos0 .. pos0 + T - 1
+  const int64_t n = (int64_t)B * T * C;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    const int c = (int)(i % C);
+    const int64_t bt = i / C;
+    const int b = (int)(bt / T), t = (int)(bt % T);
+    const float* src = qkv + bt * 3 * C;
+    const int64_t row = (int64_t)b * Tmax + pos0 + t;
+    kv[((int64_t)(layer * 2 + 0) * B * Tmax + row) * C + c] = src[C + c];
+    kv[((int64_t)(layer * 2 + 1) * B * Tmax + row) * C + c] = src[2 * C + c];
+  }
+}
+
+// one workgroup per (b, head); qkv [B, 1, 3C]; y [B, 1, C]; scratch: Tmax floats of LDS
+__global__ __launch_bounds__(NT) void kv_attend_k(const float* __restrict__ qkv, float* __restrict__ kv,
+                                                  float* __restrict__ y, int layer, int B, int Tmax, int C, int H,
+                                                  int pos, float scale) {
+  extern __shared__ float sc[];  // [pos + 1] scores, then 4 x hs partial outputs
+  __shared__ float red[NT / 64];
+  const int b = blockIdx.x / H, hd = blockIdx.x % H;
+  const int hs = C / H;
+  const float* src = qkv + (int64_t)b * 3 * C;
+  float* Kc = kv + ((int64_t)(layer * 2 + 0) * B + b) * Tmax * C + hd * hs;
+  float* Vc = kv + ((int64_t)(layer * 2 + 1) * B + b) * Tmax * C + hd * hs;
+  for (int d = threadIdx.x; d < hs; d += NT) {
+    Kc[(int64_t)pos * C + d] = src[C + hd * hs + d];
+    Vc[(int64_t)pos * C + d] = src[2 * C + hd * hs + d];
+  }
+  __syncthreads();
+  const float* q = src + hd * hs;
+  for (int j = threadIdx.x; j <= pos; j += NT) {
+    const float* kr = Kc + (int64_t)j * C;
+    float s = 0.f;
+    for (int d = 0; d < hs; ++d) s += q[d] * kr[d];
+    sc[j] = s * scale;
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j <= pos; j += NT) mx = fmaxf(mx, sc[j]);
+  mx = block_max(mx, red);
+  float sum = 0.f;
+  for (int j = threadIdx.x; j <= pos; j += NT) {
+    const float e = expf(sc[j] - mx);
+    sc[j] = e;
+    sum += e;
+  }
+  sum = block_sumf(sum, red);
+  const float inv = 1.f / sum;
+  __syncthreads();
+  // y[d] = sum_j p_j v_j[d]: 64 d-lanes x 4 position groups
+  float* part = sc + Tmax;
+  const int d = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  for (int d0 = 0; d0 < hs; d0 += 64) {
+    float acc = 0.f;
+    if (d0 + d < hs)
+      for (int j = grp; j <= pos; j += NT / 64) acc += sc[j] * Vc[(int64_t)j * C + d0 + d];
+    part[grp * 64 + d] = acc;
+    __syncthreads();
+    if (grp == 0 && d0 + d < hs) {
+      float r = 0.f;
+      for (int g = 0; g < NT / 64; ++g) r += part[g * 64 + d];
+      y[(int64_t)b * C + hd * hs + d0 + d] = r * inv;
+    }
+    __syncthreads();
+  }
+}
+
+// one workgroup per sequence; logits rows [B, V] at stride ld; u [B] (double); out [B] ids
+__global__ __launch_bounds__(NT) void sample_topk_k(const float* __restrict__ logits, int64_t ld, int V, int k,
+                                                    float temperature, const double* __restrict__ u,
+                                                    int32_t* __restrict__ out) {
+  __shared__ int ired[NT / 64];
+  __shared__ float fred[NT / 64];
+  __shared__ double dsum[NT];
+  const int b = blockIdx.x;
+  const float* l = logits + (int64_t)b * ld;
+  // k-th largest key: the largest t with #(key >= t) >= k
+  uint32_t thr = 0;
+  const bool filter = k > 0 && k < V;
+  if (filter) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+      for (int j = threadIdx.x; j < V; j += NT) cnt += order_key(l[j]) >= cand;
+      cnt = block_sumi(cnt, ired);
+      if (cnt >= k) thr = cand;
+    }
+  }
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j < V; j += NT) mx = fmaxf(mx, l[j]);
+  mx = block_max(mx, fred);
+  // contiguous id range per thread, weights in double
+  const int chunk = (V + NT - 1) / NT;
+  const int j0 = threadIdx.x * chunk, j1 = min(V, j0 + chunk);
+  double local = 0.0;
+  for (int j = j0; j < j1; ++j)
+    if (!filter || order_key(l[j]) >= thr) local += exp(((double)l[j] - (double)mx) / (double)temperature);
+  dsum[threadIdx.x] = local;
+  __syncthreads();
+  // inclusive scan over the 256 per-thread sums (thread 0, in order: deterministic)
+  if (threadIdx.x == 0)
+    for (int i = 1; i < NT; ++i) dsum[i] += dsum[i - 1];
+  __syncthreads();
+  const double total = dsum[NT - 1];
+  const double target = u[b] * total;
+  const double before = threadIdx.x ? dsum[threadIdx.x - 1] : 0.0;
+  if (before <= target && target < dsum[threadIdx.x]) {
+    double c = before;
+    int pick = j1 - 1;
+    for (int j = j0; j < j1; ++j) {
+      if (filter && order_key(l[j]) < thr) continue;
+      c += exp(((double)l[j] - (double)mx) / (double)temperature);
+      if (c > target) {
+        pick = j;
+        break;
+      }
+    }
+    out[b] = pick;
+  }
+  // rounding left target at or above the total: the last id with a weight
+  if (threadIdx.x == 0 && target >= total) {
+    int last = V - 1;
+    for (int j = V - 1; j >= 0; --j)
+      if (!filter || order_key(l[j]) >= thr) {
+        last = j;
+        break;
+      }
+    out[b] = last;
+  }
+}
+
+}  // namespace
+
+hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, int B, int Tmax, int pos0,
+                    hipStream_t s) {
+  const int64_t n = (int64_t)B * T * C;
+  if (n <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<int64_t>((n + NT - 1) / NT, 65536);
+  hipLaunchKernelGGL(kv_store_k, dim3(blocks), dim3(NT), 0, s, qkv, T, C, kv, layer, B, Tmax, pos0);
+  return hipGetLastError();
+}
+
+hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, int Tmax, int C, int H, int pos,
+                     float scale, hipStream_t s) {
+  const size_t shmem = ((size_t)Tmax + 4 * 64) * sizeof(float);
+  hipLaunchKernelGGL(kv_attend_k, dim3(B * H), dim3(NT), shmem, s, qkv, kv, y, layer, B, Tmax, C, H, pos, scale);
+  return hipGetLastError();
+}
+
+hipError_t sample_topk(const float* logits, int64_t ld, int B, int V, int k, float temperature, const double* u,
+                       int32_t* out, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sample_topk_k, dim3(B), dim3(NT), 0, s, logits, ld, V, k, temperature, u, out);
+  return hipGetLastError();
+}
+
+}  // namespace tfb

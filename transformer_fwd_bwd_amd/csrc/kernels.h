@@ -109,6 +109,14 @@ hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float*
                                const float* lse, float* D, float* dqkv, float beta, int B, int T, int H, int C,
                                float scale, hipStream_t s);
 
+// ---- KV-cached inference (decode.hip); cache fp32 [L][2][B][Tmax][C]
+hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, int B, int Tmax, int pos0,
+                    hipStream_t s);
+hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, int Tmax, int C, int H, int pos,
+                     float scale, hipStream_t s);
+hipError_t sample_topk(const float* logits, int64_t ld, int B, int V, int k, float temperature, const double* u,
+                       int32_t* out, hipStream_t s);
+
 // ---- embedding (embedding.hip)
 // ids outside [0, rows) give zero rows forward and are skipped backward
 hipError_t embedding_fwd(const float* table, int64_t rows, const int32_t* ids, float* y, int64_t n, int64_t C,

@@ -153,6 +153,12 @@ struct tfb_ctx {
   std::vector<Rec> tape;
 };
 
+struct tfb_kv {
+  tfb_ctx* ctx = nullptr;
+  int layers = 0, batch = 0, tmax = 0, channels = 0;
+  float* data = nullptr;  // persistent arena: [layers][2][batch][tmax][channels] fp32
+};
+
 struct tfb_opt {
   tfb_ctx* ctx = nullptr;
   std::vector<int> params;
@@ -1495,6 +1501,80 @@ int tfb_profile_end(tfb_ctx* ctx, double* gemm_ms, double* gemm_flops, int* laun
     if (gemm_ms) *gemm_ms = ms;
     if (gemm_flops) *gemm_flops = pf.flops;
     if (launches) *launches = pf.launches;
+  });
+}
+
+// ------------------------------------------------------------------ KV-cached inference
+int tfb_kv_create(tfb_ctx* ctx, int layers, int batch, int tmax, int channels, tfb_kv** out) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need(out != nullptr, TFB_ERR_ARG, "null output");
+    need(layers > 0 && batch > 0 && tmax > 0 && channels > 0, TFB_ERR_SHAPE, "kv cache sizes must be positive");
+    need(tmax <= 16384, TFB_ERR_SHAPE, "kv cache longer than 16384 positions is not supported");
+    const size_t n = (size_t)layers * 2 * batch * tmax * channels;
+    float* p = reinterpret_cast<float*>(ctx->arena.base + ctx->arena.alloc_persist(n * sizeof(float)));
+    hip_check(fill(p, 0.f, (int64_t)n, C.s()), "kv clear");
+    tfb_kv* kv = new tfb_kv();
+    kv->ctx = ctx, kv->layers = layers, kv->batch = batch, kv->tmax = tmax, kv->channels = channels, kv->data = p;
+    *out = kv;
+  });
+}
+
+int tfb_kv_destroy(tfb_kv* kv) {
+  return guarded([&] {
+    need(kv != nullptr, TFB_ERR_ARG, "null cache");
+    delete kv;
+  });
+}
+
+int tfb_kv_store(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos0) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need(kv != nullptr && kv->ctx == ctx, TFB_ERR_ARG, "cache of another context");
+    qkv = C.dense_in(qkv);
+    TensorRec& Q = C.T(qkv);
+    need(Q.ndim == 3 && Q.shape[0] == kv->batch && Q.shape[2] == 3LL * kv->channels, TFB_ERR_SHAPE,
+         "kv_store needs qkv [batch, T, 3C], got " + shape_str(Q));
+    need(layer >= 0 && layer < kv->layers, TFB_ERR_ARG, "no such layer");
+    need(pos0 >= 0 && pos0 + Q.shape[1] <= kv->tmax, TFB_ERR_SHAPE, "positions past the cache length");
+    hip_check(kv_store(Q.data, Q.shape[1], kv->channels, kv->data, layer, kv->batch, kv->tmax, pos0, C.s()),
+              "kv_store");
+  });
+}
+
+int tfb_kv_attend(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos, int heads, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need(kv != nullptr && kv->ctx == ctx && y != nullptr, TFB_ERR_ARG, "bad argument");
+    qkv = C.dense_in(qkv);
+    TensorRec& Q = C.T(qkv);
+    const int Cc = kv->channels;
+    need(Q.ndim == 3 && Q.shape[0] == kv->batch && Q.shape[1] == 1 && Q.shape[2] == 3LL * Cc, TFB_ERR_SHAPE,
+         "kv_attend needs qkv [batch, 1, 3C], got " + shape_str(Q));
+    need(layer >= 0 && layer < kv->layers, TFB_ERR_ARG, "no such layer");
+    need(pos >= 0 && pos < kv->tmax, TFB_ERR_SHAPE, "position past the cache length");
+    need(heads > 0 && Cc % heads == 0, TFB_ERR_SHAPE, "channels not divisible by heads");
+    const float scale = 1.f / std::sqrt((float)(Cc / heads));
+    const float* qd = Q.data;
+    int h = C.make_output({kv->batch, 1, Cc});
+    hip_check(kv_attend(qd, kv->data, ctx->tensors[h].data, layer, kv->batch, kv->tmax, Cc, heads, pos, scale, C.s()),
+              "kv_attend");
+    *y = h;  // inference only: not recorded on the tape
+  });
+}
+
+int tfb_sample_topk(tfb_ctx* ctx, tfb_tensor logits, int k, float temperature, const double* dev_uniforms,
+                    int32_t* dev_out) {
+  return guarded([&] {
+    Ctx C(ctx);
+    TensorRec& L = C.T(logits);
+    need(dev_uniforms != nullptr && dev_out != nullptr, TFB_ERR_ARG, "null argument");
+    need(temperature > 0.f, TFB_ERR_ARG, "temperature must be positive");
+    need(k >= 0, TFB_ERR_ARG, "k must be >= 0");
+    need(L.cols() < (1LL << 31) && L.rows() < 65536, TFB_ERR_SHAPE, "logits too large");
+    hip_check(sample_topk(L.data, L.stride(), (int)L.rows(), (int)L.cols(), k, temperature, dev_uniforms, dev_out,
+                          C.s()),
+              "sample_topk");
   });
 }
 

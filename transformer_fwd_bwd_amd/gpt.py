@@ -13,8 +13,8 @@ from typing import Dict, List, Sequence
 
 import numpy as np
 
-from . import (AdamW, Context, Tensor, add, causal_attention, embedding, gelu, layernorm, linear, matmul_t, reshape,
-               softmax_cross_entropy, tanh)
+from . import (AdamW, Context, KvCache, Tensor, add, causal_attention, embedding, gelu, layernorm, linear, matmul_t,
+               reshape, sample_topk, softmax_cross_entropy, tanh)
 
 
 def upload_params(ctx: Context, params: Dict[str, np.ndarray]) -> Dict[str, Tensor]:
@@ -62,6 +62,79 @@ class Gpt:
     def loss(self, inputs, targets):
         logits = self.logits(inputs)
         return softmax_cross_entropy(logits, targets), logits
+
+    # ------------------------------------------------------------------ KV-cached inference
+    # [GPT2-4, "Generation with KV cache"]: the prompt's keys and values are
+    # computed once (here in one batched pass instead of token by token -- the
+    # same arithmetic), then each new token runs through every block alone,
+    # attending over the cached past.
+
+    def prefill(self, ids, kv: KvCache):
+        """Run positions 0..P-1 of ids [B, P] through the blocks, storing every layer's keys/values."""
+        P = self.P
+        B, T = ids.shape
+        C = P["wte.weight"].shape[1]
+        x = add(embedding(P["wte.weight"], ids, B), reshape(embedding(P["wpe.weight"], self.positions(T), 1), (T, C)))
+        for i in range(self.n_layer):
+            p = f"h.{i}."
+            h = layernorm(x, P[p + "ln_1.weight"], P[p + "ln_1.bias"])
+            qkv = linear(h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"])
+            kv.store(i, qkv, 0)
+            if i == self.n_layer - 1:
+                break   # the last block's output is not needed: the next token comes from a decode step
+            a = causal_attention(qkv, self.n_head)
+            x = add(x, linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"]))
+            h = layernorm(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"])
+            f = gelu(linear(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"]))
+            x = add(x, linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"]))
+
+    def decode_step(self, tokens, pos: int, kv: KvCache, tmax: int) -> Tensor:
+        """One token per sequence (tokens: [B] int32) at position pos -> logits [B, 1, V]."""
+        P = self.P
+        B = tokens.shape[0]
+        C = P["wte.weight"].shape[1]
+        x = add(embedding(P["wte.weight"], tokens, B),
+                reshape(embedding(P["wpe.weight"], self.positions(tmax)[pos:pos + 1], 1), (1, C)))
+        for i in range(self.n_layer):
+            p = f"h.{i}."
+            h = layernorm(x, P[p + "ln_1.weight"], P[p + "ln_1.bias"])
+            qkv = linear(h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"])
+            a = kv.attend(i, qkv, pos, self.n_head)
+            x = add(x, linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"]))
+            h = layernorm(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"])
+            f = gelu(linear(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"]))
+            x = add(x, linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"]))
+        return matmul_t(layernorm(x, P["ln_f.weight"], P["ln_f.bias"]), P["wte.weight"])
+
+    def generate(self, prompts, steps: int, uniforms, k: int, temperature: float, on_step=None):
+        """[GPT2-4, "Temperature and Top-k"]: prompts [B, P] (device int32), uniforms [B, steps]
+        (device float64).  Returns the sampled ids [B, steps] (device int32).  on_step(i, logits,
+        token) sees every step's logits before the tape is reset."""
+        import torch
+        ctx = self.ctx
+        B, Pn = prompts.shape
+        tmax = Pn + steps - 1
+        C = self.P["wte.weight"].shape[1]
+        kv = KvCache(ctx, self.n_layer, B, max(tmax, 1), C)
+        out = torch.empty((steps, B), dtype=torch.int32, device=f"cuda:{ctx.device}")
+        u = uniforms.t().contiguous()
+        ctx.set_grad_enabled(False)
+        try:
+            if Pn > 1:
+                self.prefill(prompts[:, :-1].contiguous(), kv)
+                ctx.tape_reset()
+            tok = prompts[:, -1].contiguous()
+            for i in range(steps):
+                logits = self.decode_step(tok, Pn - 1 + i, kv, tmax)
+                sample_topk(logits, k, temperature, u[i], out=out[i])
+                if on_step is not None:
+                    on_step(i, logits, out[i])
+                ctx.tape_reset()
+                tok = out[i]
+        finally:
+            ctx.set_grad_enabled(True)
+            kv.close()
+        return out.t().contiguous()
 
 
 def split_ids(ids_full):
