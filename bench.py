@@ -8,12 +8,19 @@ libtfb's HIP kernels.  Batch 8 x 1024 tokens of uniform random ids (synthetic
 data, random N(0, 0.02) weights); inputs are resident in HBM before timing.
 
 Prints one JSON line (see the fields below).  Options:
-  --gpus N         only N = 1 is supported (a single-GPU build)
+  --gpus N         only N = 1 is supported (libtfb runs on one GPU)
   --steps K        timed steps (default 20)
   --warmup W       untimed warmup steps (default 5)
   --precision P    bf16 (default: bf16 MFMA operands, fp32 master weights and
                    all other arithmetic in fp32) or fp32
   --no-cpu-baseline  skip timing the CPU oracle
+  --copy-probe     first run a plain 1 GiB device-to-device copy (3 times), the
+                   known-size reference that HBM byte counters are scaled by
+
+roofline.traffic is the contraction kernel's HBM bytes per launch as read by the
+FETCH_SIZE and WRITE_SIZE counters (scaled by the copy probe), taken from the
+committed counter summary when that summary was made from the same gemm.hip;
+otherwise null.
 """
 from __future__ import annotations
 
@@ -25,6 +32,9 @@ import time
 
 METRIC = "train tokens/sec (fwd+bwd+AdamW) at GPT-2-124M shape; MFMA util %, HBM GB/s"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense MFMA, published
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_SUMMARY = {p: os.path.join(ROOT, "profiles", f"gemm_kernel_hbm_traffic_gpt2_124m_train_step_{p}.md")
+                   for p in ("bf16", "fp32")}
 
 
 def parse():
@@ -37,6 +47,7 @@ def parse():
     ap.add_argument("--seq", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seq", type=int, default=1024)
+    ap.add_argument("--copy-probe", action="store_true")
     return ap.parse_args()
 
 
@@ -65,11 +76,45 @@ def cpu_baseline(seq: int):
                       f"({dt:.1f} s; numpy/OpenBLAS on {cores} threads)"}
 
 
+def gemm_traffic(precision: str):
+    """HBM bytes per contraction launch from the committed counter summary, if it was
+    taken on the current gemm.hip (its sha256 is recorded there); else None."""
+    import hashlib
+    path = TRAFFIC_SUMMARY[precision]
+    if not os.path.exists(path):
+        return None
+    src = os.path.join(ROOT, "transformer_fwd_bwd_amd", "csrc", "gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("gemm.hip sha256") != digest:
+        return None
+    try:
+        return int(fields["bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    import torch
+    n = 1 << 28                                   # 2^28 floats = 1 GiB each way
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)                   # one streaming kernel: reads 1 GiB, writes 1 GiB
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
-              "the data-parallel split is described in DESIGN.md but not built", file=sys.stderr)
+        print(f"bench.py: libtfb runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              "data parallelism across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -78,6 +123,8 @@ def main():
     import transformer_fwd_bwd_amd as T
     from transformer_fwd_bwd_amd import gpt as G
 
+    if args.copy_probe:
+        copy_probe()
     B, L = args.batch, args.seq
     s, params, ids = S.gpt2(batch=B, seq=L)
     ctx = T.Context(arena_bytes=int(os.environ.get("TFB_ARENA_GB", "64")) << 30, precision=args.precision)
@@ -141,7 +188,8 @@ def main():
                    else "fp32 throughout"},
         "roofline": {"bound": "mfma", "kernel": "gemm_kernel (all contraction launches)",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": gemm_traffic(args.precision) if (B, L) == (8, 1024) else None,
                      "gemm_ms_per_step": round(gemm_ms / args.steps, 3),
                      "gemm_tflop_per_step": round(gemm_flops / args.steps / 1e12, 4),
                      "launches_per_step": launches // args.steps},

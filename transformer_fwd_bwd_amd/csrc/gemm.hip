@@ -9,16 +9,20 @@
 // A workgroup of WM x WN wavefronts computes a BM x BN tile of C; each wave owns
 // TM x TN blocks of 32x32 accumulated by v_mfma_f32_32x32x16_bf16 (bf16
 // operands) or v_mfma_f32_32x32x2_f32 (fp32 operands), fp32 accumulation.
-// Operands are staged through LDS as [row][k] with k contiguous, so a lane reads
-// its MFMA fragment with one 16-byte LDS load; an m- or n-contiguous operand is
-// transposed in small register blocks on the way in.  Operands may be stored
-// as fp32 (rounded to bf16, nearest even, while staging in the bf16 variant) or
-// already as bf16.  The next k-tile is fetched into registers while the current
-// one is multiplied (two LDS buffers, one barrier per k-tile).
+// A k-contiguous operand is staged through LDS as [row][k] (16-byte padded rows),
+// so a lane reads its MFMA fragment with one 16-byte LDS load.  An m- or
+// n-contiguous operand stored as bf16 keeps its own [k][row] layout in LDS and
+// its fragments are gathered by the transposing LDS read (ds_read_b64_tr_b16);
+// in fp32 storage it is transposed in small register blocks on the way in.
+// Operands may be stored as fp32 (rounded to bf16, nearest even, while staging
+// in the bf16 variant) or already as bf16.  The next k-tile is fetched into
+// registers while the current one is multiplied (two LDS buffers, one barrier
+// per k-tile).
 //
-// Workgroups are numbered so that each of the 8 XCDs (dispatched round-robin)
-// gets a contiguous run of output tiles: neighbouring tiles share A rows and
-// B columns through that XCD's L2.
+// Work items (output tiles of every batch entry and K split) are renumbered so
+// that each of the 8 XCDs (dispatched round-robin) gets one contiguous range,
+// walked in groups of GEMM_GROUP_M tile rows: the workgroups an XCD holds at
+// once share A row panels and B column panels through its L2.
 #include <algorithm>
 #include <type_traits>
 
@@ -36,6 +40,9 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KALIGN = 32;  // split-K chunks are multiples of this (and of every k-tile depth)
+#ifndef GEMM_GROUP_M
+#define GEMM_GROUP_M 8       // tile rows per raster group
+#endif
 
 template <bool BF16, int BK>
 struct Lds;
@@ -194,9 +201,9 @@ struct Stage {
     }
   }
 
-  template <bool BF16>
+  // LDK: LDS row pitch in elements
+  template <bool BF16, int LDK>
   __device__ __forceinline__ void store(typename Lds<BF16, BK>::T* L, int tid) const {
-    constexpr int LDK = Lds<BF16, BK>::LDK;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int u = tid + i * NT;
@@ -236,6 +243,84 @@ struct Stage {
   }
 };
 
+// A bf16 r-contiguous (m- or n-contiguous) operand staged in its own layout:
+// LDS holds the tile as [k][r] with rows of R_TILE + 16 elements, filled by
+// straight 16-byte copies; the MFMA fragments (8 consecutive k of one r per
+// lane) are read with the transposing LDS read ds_read_b64_tr_b16.  Within a
+// group of 16 lanes that instruction hands lane j element e of the 8 bytes
+// addressed by lane 4e + j/4, at position j%4; so lane i of the group points at
+// row kb + i/4, columns rb + 4(i%4) .. +3, and lane j receives r = rb + j,
+// k = kb .. kb + 3.  The 32-byte row pad puts the four rows one such read
+// touches in four different bank groups.
+template <int R_TILE, int NT, int BK>
+struct StageTr {
+  static constexpr int LDR = R_TILE + 16;
+  static constexpr int CPR = R_TILE / 8;  // 16-byte chunks per k-row
+  static constexpr int UNITS = BK * CPR;
+  static constexpr int PER = (UNITS + NT - 1) / NT;
+  u16x8 r[PER];
+
+  __device__ __forceinline__ void load(const void* __restrict__ Pv, int64_t ld, int r0, int k0, int R_, int K,
+                                       bool vec, int causal, int tid) {
+    const unsigned short* P = static_cast<const unsigned short*>(Pv);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = tid + i * NT;
+      if (UNITS % NT != 0 && u >= UNITS) break;
+      const int kk = u / CPR, rc = u % CPR;
+      const int gk = k0 + kk, gr = r0 + rc * 8;
+      u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (gk < K) {
+        const unsigned short* src = P + (int64_t)gk * ld + gr;
+        if (vec && gr + 7 < R_) {
+          v = *reinterpret_cast<const u16x8*>(src);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (gr + e < R_) ? src[e] : (unsigned short)0;
+        }
+        if (causal != CAUSAL_NONE) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if ((causal == CAUSAL_UPTO && gk > gr + e) || (causal == CAUSAL_FROM && gk < gr + e)) v[e] = 0;
+        }
+      }
+      r[i] = v;
+    }
+  }
+
+  __device__ __forceinline__ void load_fast(const void* __restrict__ Pv, int64_t ld, int r0, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = tid + i * NT;
+      if (UNITS % NT != 0 && u >= UNITS) break;
+      const int kk = u / CPR, rc = u % CPR;
+      r[i] = *reinterpret_cast<const u16x8*>(static_cast<const unsigned short*>(Pv) + (int64_t)(k0 + kk) * ld + r0 +
+                                              rc * 8);
+    }
+  }
+
+  template <bool BF16, int LDK>
+  __device__ __forceinline__ void store(bf16_t* L, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = tid + i * NT;
+      if (UNITS % NT != 0 && u >= UNITS) break;
+      const int kk = u / CPR, rc = u % CPR;
+      *reinterpret_cast<u16x8*>(L + kk * LDR + rc * 8) = r[i];
+    }
+  }
+};
+
+// the 8 bf16 of one MFMA fragment from two transposing reads, 4 k-rows apart
+__device__ __forceinline__ bf16x8 frag_tr(const bf16_t* p, int ld) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 4 * ld));
+  const v8i16 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
 struct KArgs {
   GemmArgs g;
   int tiles_m, tiles_n;
@@ -250,20 +335,41 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int LDK = Lds<BF16, BK>::LDK;
   using LT = typename Lds<BF16, BK>::T;
-  __shared__ __attribute__((aligned(16))) LT As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) LT Bs[2][BN * LDK];
+  // a bf16 r-contiguous operand keeps its own [k][r] layout in LDS (StageTr)
+  constexpr bool TRA = BF16 && A_BF && A_RC && BK == 64;
+  constexpr bool TRB = BF16 && B_BF && !B_KC && BK == 64;
+  constexpr int LDA = TRA ? BM + 16 : LDK, LDB = TRB ? BN + 16 : LDK;
+  __shared__ __attribute__((aligned(16))) LT As[2][TRA ? BK * LDA : BM * LDA];
+  __shared__ __attribute__((aligned(16))) LT Bs[2][TRB ? BK * LDB : BN * LDB];
 
   const GemmArgs& g = ka.g;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // XCD-contiguous tile order: workgroup w runs on XCD w % 8
+  // Work item order.  The grid is 1-D over (batch x split) slabs of tiles_m x
+  // tiles_n tiles.  Workgroup w runs on XCD w % 8, so the ids are renumbered to
+  // give each XCD one contiguous range of work items; inside a slab, items run
+  // in groups of GEMM_GROUP_M tile rows, column by column, so the workgroups an
+  // XCD holds at once share a few A row panels and B column panels in its L2.
   const int ntiles = ka.tiles_m * ka.tiles_n;
-  int id = blockIdx.x;
-  if ((ntiles & 7) == 0) id = (id & 7) * (ntiles >> 3) + (id >> 3);
-  const int tm = id / ka.tiles_n, tn = id % ka.tiles_n;
-  const int zz = blockIdx.y;
+  const int total = (int)gridDim.x;
+  int id;
+  {
+    const int w = blockIdx.x, xcd = w & 7, per = total >> 3, rem = total & 7;
+    id = xcd * per + min(xcd, rem) + (w >> 3);
+  }
+  const int zz = id / ntiles;
+  int t = id - zz * ntiles;
+  int tm, tn;
+  {
+    const int band = GEMM_GROUP_M * ka.tiles_n;
+    const int first = (t / band) * GEMM_GROUP_M;
+    const int rows = min(ka.tiles_m - first, GEMM_GROUP_M);
+    t -= (first / GEMM_GROUP_M) * band;
+    tm = first + t % rows;
+    tn = t / rows;
+  }
   const int z = zz / ka.splits, split = zz % ka.splits;
   const int m0 = tm * BM, n0 = tn * BN;
   if (g.causal_out && n0 > m0 + BM - 1) return;
@@ -284,21 +390,22 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
   // the m/n extent of this tile is entirely in range for both operands
   const bool interior = vecA && vecB && m0 + BM <= g.M && n0 + BN <= g.N;
 
-  Stage<BM, NT, A_RC, A_BF, BK> sa;
-  Stage<BN, NT, !B_KC, B_BF, BK> sb;
-
   // a k-tile is loaded without checks when it is interior, complete and away from the causal diagonal
-  auto load_tile = [&](int k0) {
+  auto load_tile = [&](auto& xa, auto& xb, int k0) {
     bool fast = interior && k0 + BK <= ke;
     if (g.causal_a == CAUSAL_UPTO) fast = fast && k0 + BK - 1 <= m0;
     if (g.causal_a == CAUSAL_FROM) fast = fast && k0 >= m0 + BM - 1;
     if (fast) {
-      sa.load_fast(A, g.lda, m0, k0, tid);
-      sb.load_fast(B, g.ldb, n0, k0, tid);
+      xa.load_fast(A, g.lda, m0, k0, tid);
+      xb.load_fast(B, g.ldb, n0, k0, tid);
     } else {
-      sa.load(A, g.lda, m0, k0, g.M, ke, vecA, g.causal_a, tid);
-      sb.load(B, g.ldb, n0, k0, g.N, ke, vecB, CAUSAL_NONE, tid);
+      xa.load(A, g.lda, m0, k0, g.M, ke, vecA, g.causal_a, tid);
+      xb.load(B, g.ldb, n0, k0, g.N, ke, vecB, CAUSAL_NONE, tid);
     }
+  };
+  auto store_tile = [&](const auto& xa, const auto& xb, int b) {
+    xa.template store<BF16, LDA>(As[b], tid);
+    xb.template store<BF16, LDB>(Bs[b], tid);
   };
 
   f32x16 acc[TM][TN];
@@ -309,28 +416,31 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  int buf = 0;
-  if (kb < ke) {
-    load_tile(kb);
-    sa.template store<BF16>(As[0], tid);
-    sb.template store<BF16>(Bs[0], tid);
-  }
-  __syncthreads();
-
   const int lrow = lane & 31, lhalf = lane >> 5;
-  for (int k0 = kb; k0 < ke; k0 += BK) {
-    const bool more = k0 + BK < ke;
-    if (more) load_tile(k0 + BK);
-    const LT* Ab = As[buf] + (wm * TM * 32 + lrow) * LDK;
-    const LT* Bb = Bs[buf] + (wn * TN * 32 + lrow) * LDK;
+  // transposing-read lane offsets: lane 16g + i reads row 8(g/2) + i/4 (+4 for the
+  // second half), columns 16(g%2) + 4(i%4)
+  const int tr_row = 8 * (lane >> 5) + ((lane & 15) >> 2), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto compute = [&](int b) {
+    const LT* Ab = TRA ? As[b] + tr_row * LDA + wm * TM * 32 + tr_col : As[b] + (wm * TM * 32 + lrow) * LDA;
+    const LT* Bb = TRB ? Bs[b] + tr_row * LDB + wn * TN * 32 + tr_col : Bs[b] + (wn * TN * 32 + lrow) * LDB;
     if constexpr (BF16) {
 #pragma unroll
       for (int ks = 0; ks < BK; ks += 16) {
         bf16x8 af[TM], bf[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(Ab + i * 32 * LDK + ks + lhalf * 8);
+        for (int i = 0; i < TM; ++i) {
+          if constexpr (TRA)
+            af[i] = frag_tr(Ab + ks * LDA + i * 32, LDA);
+          else
+            af[i] = *reinterpret_cast<const bf16x8*>(Ab + i * 32 * LDA + ks + lhalf * 8);
+        }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(Bb + j * 32 * LDK + ks + lhalf * 8);
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (TRB)
+            bf[j] = frag_tr(Bb + ks * LDB + j * 32, LDB);
+          else
+            bf[j] = *reinterpret_cast<const bf16x8*>(Bb + j * 32 * LDB + ks + lhalf * 8);
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -342,9 +452,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
       for (int kg = 0; kg < BK; kg += 8) {
         f4 af[TM], bf[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const f4*>(Ab + i * 32 * LDK + kg + lhalf * 4);
+        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const f4*>(Ab + i * 32 * LDA + kg + lhalf * 4);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const f4*>(Bb + j * 32 * LDK + kg + lhalf * 4);
+        for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const f4*>(Bb + j * 32 * LDB + kg + lhalf * 4);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -354,10 +464,25 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][c], bf[j][c], acc[i][j], 0, 0, 0);
       }
     }
-    if (more) {
-      sa.template store<BF16>(As[buf ^ 1], tid);
-      sb.template store<BF16>(Bs[buf ^ 1], tid);
-    }
+  };
+
+  // Pipeline: k-tile t is multiplied out of LDS buffer t % 2 while tile t + 1
+  // is fetched into registers; one barrier per k-tile.
+  using SA = typename std::conditional<TRA, StageTr<BM, NT, BK>, Stage<BM, NT, A_RC, A_BF, BK>>::type;
+  using SB = typename std::conditional<TRB, StageTr<BN, NT, BK>, Stage<BN, NT, !B_KC, B_BF, BK>>::type;
+  SA sa;
+  SB sb;
+  if (kb < ke) {
+    load_tile(sa, sb, kb);
+    store_tile(sa, sb, 0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    const bool more = k0 + BK < ke;
+    if (more) load_tile(sa, sb, k0 + BK);
+    compute(buf);
+    if (more) store_tile(sa, sb, buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
@@ -496,7 +621,7 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   ka.ws = static_cast<float*>(workspace);
   ka.tiles_m = (g.M + p.BM - 1) / p.BM;
   ka.tiles_n = (g.N + p.BN - 1) / p.BN;
-  dim3 grid(ka.tiles_m * ka.tiles_n, g.batch * p.splits);
+  dim3 grid(ka.tiles_m * ka.tiles_n * g.batch * p.splits);
   hipError_t e;
   if (p.cfg == CFG_128x128)
     e = launch_prec<2, 2, 2, 2>(ka, grid, s);
