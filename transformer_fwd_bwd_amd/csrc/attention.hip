@@ -55,49 +55,66 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& acc, int base) {
 // row index (within a 32x32 block) held by accumulator r of lane half h
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// --- staging into LDS (all 256 threads; rows past `valid` are zero) ----------------------
-// rows layout: dst[row][HS + 8], one 16-byte chunk of 8 values per transfer
+// --- staging ------------------------------------------------------------------------------
+// A KVB x HS block of rows (keys or queries) goes global -> registers -> LDS as
+// X[row][HS + 8], one 16-byte chunk of 8 values per transfer; rows past
+// `valid` are zero.  The register step lets the next block be fetched while
+// the current one is multiplied.
 template <int HS>
-__device__ __forceinline__ void stage_rows(unsigned short* dst, const unsigned short* __restrict__ src, int64_t ld,
-                                           int row0, int valid, int tid) {
-  constexpr int CPR = HS / 8;
-  for (int c = tid; c < KVB * CPR; c += NT) {
-    const int row = c / CPR, col = (c % CPR) * 8;
-    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (row0 + row < valid) v = *reinterpret_cast<const u16x8*>(src + (int64_t)(row0 + row) * ld + col);
-    *reinterpret_cast<u16x8*>(dst + row * (HS + 8) + col) = v;
-  }
-}
-
-// transposed layout: dst[col][KVB + 8]; 4 rows x 8 columns per thread
-template <int HS>
-__device__ __forceinline__ void stage_cols(unsigned short* dst, const unsigned short* __restrict__ src, int64_t ld,
-                                           int row0, int valid, int tid) {
-  constexpr int BLOCKS = (KVB / 4) * (HS / 8);
-  for (int b = tid; b < BLOCKS; b += NT) {
-    const int rq = b % (KVB / 4), cq = b / (KVB / 4);
-    u16x8 v[4];
+struct RowStage {
+  static constexpr int CPR = HS / 8, CHUNKS = KVB * CPR, PER = (CHUNKS + NT - 1) / NT;
+  u16x8 v[PER];
+  __device__ __forceinline__ void load(const unsigned short* __restrict__ src, int64_t ld, int row0, int valid,
+                                       int tid) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = row0 + rq * 4 + i;
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS % NT != 0 && c >= CHUNKS) break;
+      const int row = c / CPR, col = (c % CPR) * 8;
       v[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (row < valid) v[i] = *reinterpret_cast<const u16x8*>(src + (int64_t)row * ld + cq * 8);
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      u16x4 w = {v[0][c], v[1][c], v[2][c], v[3][c]};
-      *reinterpret_cast<u16x4*>(dst + (cq * 8 + c) * (KVB + 8) + rq * 4) = w;
+      if (row0 + row < valid) v[i] = *reinterpret_cast<const u16x8*>(src + (int64_t)(row0 + row) * ld + col);
     }
   }
+  __device__ __forceinline__ void store(unsigned short* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS % NT != 0 && c >= CHUNKS) break;
+      *reinterpret_cast<u16x8*>(dst + (c / CPR) * (HS + 8) + (c % CPR) * 8) = v[i];
+    }
+  }
+};
+
+// A fragment of X^T (rows d = d0 + lane%32, k = rows of X in the packed-register
+// order 16s + 4h + {0..3}, 16s + 8 + 4h + {0..3}) from the row-major tile X[row][HS + 8],
+// by two transposing LDS reads.  ds_read_b64_tr_b16 hands lane j of a 16-lane
+// group element e of the 8 bytes addressed by lane 4e + j/4, at position j%4:
+// lane i of group g therefore points at row 16s + 4(g/2) + i/4 (+8 for the
+// second read), columns d0 + 16(g%2) + 4(i%4), and receives column d0 + 16(g%2) + i.
+template <int HS>
+__device__ __forceinline__ bf16x8 frag_tr(const unsigned short* X, int d0, int s, int lane) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const int g = lane >> 4, i = lane & 15;
+  const unsigned short* p = X + (16 * s + 4 * (g >> 1) + (i >> 2)) * (HS + 8) + d0 + 16 * (g & 1) + 4 * (i & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 8 * (HS + 8)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// A fragment with k in the packed-register order: Xt[d][key], keys 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3}
-__device__ __forceinline__ bf16x8 frag_t(const unsigned short* Xt, int d, int s, int h) {
-  const unsigned short* p = Xt + d * (KVB + 8) + 16 * s + 4 * h;
-  u16x4 a = *reinterpret_cast<const u16x4*>(p);
-  u16x4 b = *reinterpret_cast<const u16x4*>(p + 8);
-  u16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return as_bf(v);
+// Work assignment.  The grid is 1-D over nx blocks x (B*H rounded up to 8).
+// Workgroup w runs on XCD w % 8, and causal work grows (forward, dQ) or shrinks
+// (dK/dV) with the block index, so consecutive ids on one XCD walk the block
+// indices of a fixed set of heads: every XCD gets the same mix, largest first.
+struct BlockId {
+  int x, bh;
+};
+__device__ __forceinline__ BlockId block_id(int nx, bool large_x_first) {
+  const int L = blockIdx.x, xi = (L >> 3) % nx;
+  BlockId r;
+  r.bh = (L & 7) + 8 * (L / (8 * nx));
+  r.x = large_x_first ? nx - 1 - xi : xi;
+  return r;
 }
 
 // A/B fragment with k contiguous: X[row][d], d = 16s + 8h + {0..7}
@@ -130,11 +147,13 @@ struct AttnArgs {
 // ------------------------------------------------------------------------------------ forward
 template <int HS>
 __global__ __launch_bounds__(NT) void attn_fwd_k(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned short Ks[KVB * (HS + 8)];
-  __shared__ __attribute__((aligned(16))) unsigned short Vt[HS * (KVB + 8)];
+  __shared__ __attribute__((aligned(16))) unsigned short Ks[2][KVB * (HS + 8)];
+  __shared__ __attribute__((aligned(16))) unsigned short Vs[2][KVB * (HS + 8)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.y, b = bh / a.H, hd = bh % a.H;
-  const int q0 = blockIdx.x * 128, qw = q0 + 32 * w, q = qw + l32;
+  const BlockId id = block_id((a.T + 127) / 128, true);
+  if (id.bh >= a.B * a.H) return;
+  const int bh = id.bh, b = bh / a.H, hd = bh % a.H;
+  const int q0 = id.x * 128, qw = q0 + 32 * w, q = qw + l32;
   const int64_t ld = 3LL * a.C;
   const unsigned short* base = a.qkv + (int64_t)b * a.T * ld + hd * HS;
   const unsigned short* Kg = base + a.C;
@@ -153,56 +172,71 @@ __global__ __launch_bounds__(NT) void attn_fwd_k(AttnArgs a) {
   const float sc = a.scale * LOG2E;
 
   const int kv_end = min(a.T, q0 + 128);
+  RowStage<HS> kst, vst;
+  kst.load(Kg, ld, 0, a.T, tid);
+  vst.load(Vg, ld, 0, a.T, tid);
+  kst.store(Ks[0], tid);
+  vst.store(Vs[0], tid);
+  __syncthreads();
+  int buf = 0;
   for (int kv0 = 0; kv0 < kv_end; kv0 += KVB) {
-    __syncthreads();
-    stage_rows<HS>(Ks, Kg, ld, kv0, a.T, tid);
-    stage_cols<HS>(Vt, Vg, ld, kv0, a.T, tid);
-    __syncthreads();
-    if (kv0 > qw + 31) continue;  // every key of this block is after every query of this wave
-    f32x16 st[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < HS / 16; ++s) st[kt] = mfma(frag_r<HS>(Ks, 32 * kt + l32, s, h), qf[s], st[kt]);
+    const bool more = kv0 + KVB < kv_end;
+    if (more) {
+      kst.load(Kg, ld, kv0 + KVB, a.T, tid);
+      vst.load(Vg, ld, kv0 + KVB, a.T, tid);
     }
-    float mx = -INFINITY;
+    if (kv0 <= qw + 31) {  // else every key of this block is after every query of this wave
+      f32x16 st[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * kt + acc_row(r, h);
-        const float v = (key <= q && key < a.T) ? st[kt][r] * sc : -INFINITY;
-        st[kt][r] = v;
-        mx = fmaxf(mx, v);
+        for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < HS / 16; ++s) st[kt] = mfma(frag_r<HS>(Ks[buf], 32 * kt + l32, s, h), qf[s], st[kt]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    const float mref = mn == -INFINITY ? 0.f : mn;
-    const float alpha = exp2f(m - mref);
-    float sum = 0.f;
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(st[kt][r] - mref);
-        st[kt][r] = p;
-        sum += p;
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * kt + acc_row(r, h);
+          const float v = (key <= q && key < a.T) ? st[kt][r] * sc : -INFINITY;
+          st[kt][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      const float alpha = exp2f(m - mref);
+      float sum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2f(st[kt][r] - mref);
+          st[kt][r] = p;
+          sum += p;
+        }
+      sum += __shfl_xor(sum, 32, 64);
+      l = l * alpha + sum;
+      m = mn;
+#pragma unroll
+      for (int i = 0; i < HS / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+#pragma unroll
+      for (int s = 0; s < KVB / 16; ++s) {
+        const bf16x8 pb = pack8(st[s >> 1], 8 * (s & 1));
+#pragma unroll
+        for (int i = 0; i < HS / 32; ++i) o[i] = mfma(frag_tr<HS>(Vs[buf], 32 * i, s, lane), pb, o[i]);
       }
-    sum += __shfl_xor(sum, 32, 64);
-    l = l * alpha + sum;
-    m = mn;
-#pragma unroll
-    for (int i = 0; i < HS / 32; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-#pragma unroll
-    for (int s = 0; s < KVB / 16; ++s) {
-      const bf16x8 pb = pack8(st[s >> 1], 8 * (s & 1));
-#pragma unroll
-      for (int i = 0; i < HS / 32; ++i) o[i] = mfma(frag_t(Vt, 32 * i + l32, s, h), pb, o[i]);
     }
+    if (more) {
+      kst.store(Ks[buf ^ 1], tid);
+      vst.store(Vs[buf ^ 1], tid);
+    }
+    __syncthreads();
+    buf ^= 1;
   }
   if (q < a.T) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -236,12 +270,13 @@ __global__ __launch_bounds__(NT) void attn_d_k(AttnArgs a) {
 // dQ for a block of 128 queries (4 waves x 32), looping over key blocks
 template <int HS>
 __global__ __launch_bounds__(NT) void attn_dq_k(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned short Ks[KVB * (HS + 8)];
-  __shared__ __attribute__((aligned(16))) unsigned short Kt[HS * (KVB + 8)];
-  __shared__ __attribute__((aligned(16))) unsigned short Vs[KVB * (HS + 8)];
+  __shared__ __attribute__((aligned(16))) unsigned short Ks[2][KVB * (HS + 8)];
+  __shared__ __attribute__((aligned(16))) unsigned short Vs[2][KVB * (HS + 8)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.y, b = bh / a.H, hd = bh % a.H;
-  const int q0 = blockIdx.x * 128, qw = q0 + 32 * w, q = qw + l32;
+  const BlockId id = block_id((a.T + 127) / 128, true);
+  if (id.bh >= a.B * a.H) return;
+  const int bh = id.bh, b = bh / a.H, hd = bh % a.H;
+  const int q0 = id.x * 128, qw = q0 + 32 * w, q = qw + l32;
   const int64_t ld = 3LL * a.C;
   const unsigned short* base = a.qkv + (int64_t)b * a.T * ld + hd * HS;
   const unsigned short* Kg = base + a.C;
@@ -265,39 +300,53 @@ __global__ __launch_bounds__(NT) void attn_dq_k(AttnArgs a) {
     for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
 
   const int kv_end = min(a.T, q0 + 128);
+  RowStage<HS> kst, vst;
+  kst.load(Kg, ld, 0, a.T, tid);
+  vst.load(Vg, ld, 0, a.T, tid);
+  kst.store(Ks[0], tid);
+  vst.store(Vs[0], tid);
+  __syncthreads();
+  int buf = 0;
   for (int kv0 = 0; kv0 < kv_end; kv0 += KVB) {
-    __syncthreads();
-    stage_rows<HS>(Ks, Kg, ld, kv0, a.T, tid);
-    stage_cols<HS>(Kt, Kg, ld, kv0, a.T, tid);
-    stage_rows<HS>(Vs, Vg, ld, kv0, a.T, tid);
-    __syncthreads();
-    if (kv0 > qw + 31) continue;
-    f32x16 st[2], dp[2];
+    const bool more = kv0 + KVB < kv_end;
+    if (more) {
+      kst.load(Kg, ld, kv0 + KVB, a.T, tid);
+      vst.load(Vg, ld, kv0 + KVB, a.T, tid);
+    }
+    if (kv0 <= qw + 31) {
+      f32x16 st[2], dp[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[kt][r] = dp[kt][r] = 0.f;
+        for (int r = 0; r < 16; ++r) st[kt][r] = dp[kt][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < HS / 16; ++s) {
-        st[kt] = mfma(frag_r<HS>(Ks, 32 * kt + l32, s, h), qf[s], st[kt]);
-        dp[kt] = mfma(frag_r<HS>(Vs, 32 * kt + l32, s, h), df[s], dp[kt]);
+        for (int s = 0; s < HS / 16; ++s) {
+          st[kt] = mfma(frag_r<HS>(Ks[buf], 32 * kt + l32, s, h), qf[s], st[kt]);
+          dp[kt] = mfma(frag_r<HS>(Vs[buf], 32 * kt + l32, s, h), df[s], dp[kt]);
+        }
+      }
+      // dS^T = P^T (dP^T - D)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * kt + acc_row(r, h);
+          const float p = (key <= q && key < a.T) ? exp2f(st[kt][r] * sc - lse) : 0.f;
+          st[kt][r] = p * (dp[kt][r] - Dq);
+        }
+#pragma unroll
+      for (int s = 0; s < KVB / 16; ++s) {
+        const bf16x8 sb = pack8(st[s >> 1], 8 * (s & 1));
+#pragma unroll
+        for (int i = 0; i < HS / 32; ++i) dq[i] = mfma(frag_tr<HS>(Ks[buf], 32 * i, s, lane), sb, dq[i]);
       }
     }
-    // dS^T = P^T (dP^T - D)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * kt + acc_row(r, h);
-        const float p = (key <= q && key < a.T) ? exp2f(st[kt][r] * sc - lse) : 0.f;
-        st[kt][r] = p * (dp[kt][r] - Dq);
-      }
-#pragma unroll
-    for (int s = 0; s < KVB / 16; ++s) {
-      const bf16x8 sb = pack8(st[s >> 1], 8 * (s & 1));
-#pragma unroll
-      for (int i = 0; i < HS / 32; ++i) dq[i] = mfma(frag_t(Kt, 32 * i + l32, s, h), sb, dq[i]);
+    if (more) {
+      kst.store(Ks[buf ^ 1], tid);
+      vst.store(Vs[buf ^ 1], tid);
     }
+    __syncthreads();
+    buf ^= 1;
   }
   if (q < a.T) {
     float* dst = a.out + ((int64_t)b * a.T + q) * ld + hd * HS;
@@ -316,17 +365,19 @@ __global__ __launch_bounds__(NT) void attn_dq_k(AttnArgs a) {
 // dK and dV for a block of 128 keys (4 waves x 32), looping over query blocks
 template <int HS>
 __global__ __launch_bounds__(NT) void attn_dkv_k(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned short Qs[KVB * (HS + 8)];
-  __shared__ __attribute__((aligned(16))) unsigned short Qt[HS * (KVB + 8)];
-  __shared__ __attribute__((aligned(16))) unsigned short Ds[KVB * (HS + 8)];
-  __shared__ __attribute__((aligned(16))) unsigned short Dt[HS * (KVB + 8)];
-  __shared__ float Ls[KVB], Dd[KVB];
+  __shared__ __attribute__((aligned(16))) unsigned short Qs[2][KVB * (HS + 8)];
+  __shared__ __attribute__((aligned(16))) unsigned short Ds[2][KVB * (HS + 8)];
+  __shared__ float Ls[2][KVB], Dd[2][KVB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.y, b = bh / a.H, hd = bh % a.H;
-  const int k0 = blockIdx.x * 128, kw = k0 + 32 * w, key = kw + l32;
+  const BlockId id = block_id((a.T + 127) / 128, false);
+  if (id.bh >= a.B * a.H) return;
+  const int bh = id.bh, b = bh / a.H, hd = bh % a.H;
+  const int k0 = id.x * 128, kw = k0 + 32 * w, key = kw + l32;
   const int64_t ld = 3LL * a.C;
   const unsigned short* base = a.qkv + (int64_t)b * a.T * ld + hd * HS;
   const unsigned short* dyg = a.dy + (int64_t)b * a.T * a.C + hd * HS;
+  const float* lse_g = a.lse + (int64_t)bh * a.T;
+  const float* D_g = a.D + (int64_t)bh * a.T;
 
   bf16x8 kf[HS / 16], vf[HS / 16];
 #pragma unroll
@@ -341,50 +392,71 @@ __global__ __launch_bounds__(NT) void attn_dkv_k(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
 
-  for (int qb = (k0 / KVB) * KVB; qb < a.T; qb += KVB) {
-    __syncthreads();
-    stage_rows<HS>(Qs, base, ld, qb, a.T, tid);
-    stage_cols<HS>(Qt, base, ld, qb, a.T, tid);
-    stage_rows<HS>(Ds, dyg, a.C, qb, a.T, tid);
-    stage_cols<HS>(Dt, dyg, a.C, qb, a.T, tid);
+  const int qstart = (k0 / KVB) * KVB;
+  RowStage<HS> qst, dst_;
+  float lnext = 0.f, dnext = 0.f;
+  auto fetch = [&](int qb) {
+    qst.load(base, ld, qb, a.T, tid);
+    dst_.load(dyg, a.C, qb, a.T, tid);
     if (tid < KVB) {
       const int qq = qb + tid;
-      Ls[tid] = qq < a.T ? a.lse[(int64_t)bh * a.T + qq] : 0.f;
-      Dd[tid] = qq < a.T ? a.D[(int64_t)bh * a.T + qq] : 0.f;
+      lnext = qq < a.T ? lse_g[qq] : 0.f;
+      dnext = qq < a.T ? D_g[qq] : 0.f;
     }
+  };
+  auto put = [&](int bf) {
+    qst.store(Qs[bf], tid);
+    dst_.store(Ds[bf], tid);
+    if (tid < KVB) {
+      Ls[bf][tid] = lnext;
+      Dd[bf][tid] = dnext;
+    }
+  };
+  if (qstart < a.T) {
+    fetch(qstart);
+    put(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int qb = qstart; qb < a.T; qb += KVB) {
+    const bool more = qb + KVB < a.T;
+    if (more) fetch(qb + KVB);
+    if (qb + KVB - 1 >= kw) {  // else every query of this block precedes every key of this wave
+      f32x16 st[2], dp[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[qt][r] = dp[qt][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < HS / 16; ++s) {
+          st[qt] = mfma(frag_r<HS>(Qs[buf], 32 * qt + l32, s, h), kf[s], st[qt]);
+          dp[qt] = mfma(frag_r<HS>(Ds[buf], 32 * qt + l32, s, h), vf[s], dp[qt]);
+        }
+      }
+      // P and dS with queries in registers, this lane's key in the column
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = 32 * qt + acc_row(r, h), qq = qb + qi;
+          const float p = (key <= qq && qq < a.T && key < a.T) ? exp2f(st[qt][r] * sc - Ls[buf][qi]) : 0.f;
+          st[qt][r] = p;
+          dp[qt][r] = p * (dp[qt][r] - Dd[buf][qi]);
+        }
+#pragma unroll
+      for (int s = 0; s < KVB / 16; ++s) {
+        const bf16x8 pb = pack8(st[s >> 1], 8 * (s & 1));
+        const bf16x8 db = pack8(dp[s >> 1], 8 * (s & 1));
+#pragma unroll
+        for (int i = 0; i < HS / 32; ++i) {
+          dv[i] = mfma(frag_tr<HS>(Ds[buf], 32 * i, s, lane), pb, dv[i]);
+          dk[i] = mfma(frag_tr<HS>(Qs[buf], 32 * i, s, lane), db, dk[i]);
+        }
+      }
+    }
+    if (more) put(buf ^ 1);
     __syncthreads();
-    if (qb + KVB - 1 < kw) continue;  // every query of this block precedes every key of this wave
-    f32x16 st[2], dp[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[qt][r] = dp[qt][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < HS / 16; ++s) {
-        st[qt] = mfma(frag_r<HS>(Qs, 32 * qt + l32, s, h), kf[s], st[qt]);
-        dp[qt] = mfma(frag_r<HS>(Ds, 32 * qt + l32, s, h), vf[s], dp[qt]);
-      }
-    }
-    // P and dS with queries in registers, this lane's key in the column
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = 32 * qt + acc_row(r, h), qq = qb + qi;
-        const float p = (key <= qq && qq < a.T && key < a.T) ? exp2f(st[qt][r] * sc - Ls[qi]) : 0.f;
-        st[qt][r] = p;
-        dp[qt][r] = p * (dp[qt][r] - Dd[qi]);
-      }
-#pragma unroll
-    for (int s = 0; s < KVB / 16; ++s) {
-      const bf16x8 pb = pack8(st[s >> 1], 8 * (s & 1));
-      const bf16x8 db = pack8(dp[s >> 1], 8 * (s & 1));
-#pragma unroll
-      for (int i = 0; i < HS / 32; ++i) {
-        dv[i] = mfma(frag_t(Dt, 32 * i + l32, s, h), pb, dv[i]);
-        dk[i] = mfma(frag_t(Qt, 32 * i + l32, s, h), db, dk[i]);
-      }
-    }
+    buf ^= 1;
   }
   if (key < a.T) {
     float* dst = a.out + ((int64_t)b * a.T + key) * ld + hd * HS;
@@ -404,6 +476,9 @@ __global__ __launch_bounds__(NT) void attn_dkv_k(AttnArgs a) {
   }
 }
 
+// 1-D grid for block_id: (T/128 blocks) x (B*H rounded up to a multiple of 8)
+unsigned attn_grid(int T, int BH) { return (unsigned)(((T + 127) / 128) * ((BH + 7) / 8 * 8)); }
+
 }  // namespace
 
 bool flash_attention_supported(int hs, int64_t C) { return (hs == 64 || hs == 32) && C % 8 == 0; }
@@ -413,7 +488,7 @@ hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, float* lse, int B,
   if (B <= 0 || T <= 0) return hipSuccess;
   AttnArgs a{};
   a.qkv = qkv, a.out = y, a.lse = lse, a.B = B, a.T = T, a.H = H, a.C = C, a.scale = scale;
-  dim3 grid((T + 127) / 128, B * H);
+  dim3 grid(attn_grid(T, B * H));
   const int hs = C / H;
   if (hs == 64)
     hipLaunchKernelGGL(attn_fwd_k<64>, grid, dim3(NT), 0, s, a);
@@ -433,7 +508,7 @@ hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float*
   a.B = B, a.T = T, a.H = H, a.C = C, a.scale = scale, a.beta = beta;
   const int hs = C / H;
   dim3 gd((unsigned)(((int64_t)B * T + 3) / 4));
-  dim3 grid((T + 127) / 128, B * H);
+  dim3 grid(attn_grid(T, B * H));
   if (hs == 64) {
     hipLaunchKernelGGL(attn_d_k<64>, gd, dim3(NT), 0, s, a);
     hipLaunchKernelGGL(attn_dq_k<64>, grid, dim3(NT), 0, s, a);
