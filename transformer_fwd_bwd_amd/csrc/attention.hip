@@ -364,7 +364,7 @@ __global__ __launch_bounds__(NT) void attn_dq_k(AttnArgs a) {
 
 // dK and dV for a block of 128 keys (4 waves x 32), looping over query blocks
 template <int HS>
-__global__ __launch_bounds__(NT) void attn_dkv_k(AttnArgs a) {
+__global__ __launch_bounds__(NT, 2) void attn_dkv_k(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned short Qs[2][KVB * (HS + 8)];
   __shared__ __attribute__((aligned(16))) unsigned short Ds[2][KVB * (HS + 8)];
   __shared__ float Ls[2][KVB], Dd[2][KVB];
