@@ -52,6 +52,8 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& acc, int base) {
   return as_bf(v);
 }
 
+__device__ __forceinline__ u16x4 pack4(f4 v) { return u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])}; }
+
 // row index (within a 32x32 block) held by accumulator r of lane half h
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -137,6 +139,7 @@ struct AttnArgs {
   const float* y;             // fp32 [B, T, C] forward output (backward: D = rowsum(dy * y))
   const float* dyf;           // fp32 [B, T, C] (backward)
   float* out;                 // forward: y; backward: dqkv fp32 [B, T, 3C]
+  unsigned short* outbf;      // optional bf16 copy of `out` (same layout)
   float* lse;                 // [B*H, T] base-2 log-sum-exp of the scaled scores
   float* D;                   // [B*H, T]
   int B, T, H, C;
@@ -240,11 +243,16 @@ __global__ __launch_bounds__(NT) void attn_fwd_k(AttnArgs a) {
   }
   if (q < a.T) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* yq = a.out + ((int64_t)b * a.T + q) * a.C + hd * HS;
+    const int64_t off = ((int64_t)b * a.T + q) * a.C + hd * HS;
 #pragma unroll
     for (int i = 0; i < HS / 32; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) yq[32 * i + acc_row(r, h)] = o[i][r] * inv;
+      for (int r = 0; r < 16; r += 4) {  // registers r .. r+3 hold 4 consecutive columns of this query's row
+        const f4 v = f4{o[i][r], o[i][r + 1], o[i][r + 2], o[i][r + 3]} * inv;
+        const int d = 32 * i + acc_row(r, h);
+        *reinterpret_cast<f4*>(a.out + off + d) = v;
+        if (a.outbf) *reinterpret_cast<u16x4*>(a.outbf + off + d) = pack4(v);
+      }
     if (h == 0) a.lse[(int64_t)bh * a.T + q] = m + log2f(l);
   }
 }
@@ -349,15 +357,17 @@ __global__ __launch_bounds__(NT) void attn_dq_k(AttnArgs a) {
     buf ^= 1;
   }
   if (q < a.T) {
-    float* dst = a.out + ((int64_t)b * a.T + q) * ld + hd * HS;
+    const int64_t off = ((int64_t)b * a.T + q) * ld + hd * HS;
 #pragma unroll
     for (int i = 0; i < HS / 32; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = a.scale * dq[i][r];
-        float* p = dst + 32 * i + acc_row(r, h);
+      for (int r = 0; r < 16; r += 4) {
+        const int d = 32 * i + acc_row(r, h);
+        f4* p = reinterpret_cast<f4*>(a.out + off + d);
+        f4 v = f4{dq[i][r], dq[i][r + 1], dq[i][r + 2], dq[i][r + 3]} * a.scale;
         if (a.beta != 0.f) v += *p;
         *p = v;
+        if (a.outbf) *reinterpret_cast<u16x4*>(a.outbf + off + d) = pack4(v);
       }
   }
 }
@@ -459,19 +469,26 @@ __global__ __launch_bounds__(NT, 2) void attn_dkv_k(AttnArgs a) {
     buf ^= 1;
   }
   if (key < a.T) {
-    float* dst = a.out + ((int64_t)b * a.T + key) * ld + hd * HS;
+    const int64_t off = ((int64_t)b * a.T + key) * ld + hd * HS;
 #pragma unroll
     for (int i = 0; i < HS / 32; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 16; r += 4) {
         const int d = 32 * i + acc_row(r, h);
-        float vk = a.scale * dk[i][r], vv = dv[i][r];
+        f4* pk = reinterpret_cast<f4*>(a.out + off + a.C + d);
+        f4* pv = reinterpret_cast<f4*>(a.out + off + 2 * a.C + d);
+        f4 vk = f4{dk[i][r], dk[i][r + 1], dk[i][r + 2], dk[i][r + 3]} * a.scale;
+        f4 vv = f4{dv[i][r], dv[i][r + 1], dv[i][r + 2], dv[i][r + 3]};
         if (a.beta != 0.f) {
-          vk += dst[a.C + d];
-          vv += dst[2 * a.C + d];
+          vk += *pk;
+          vv += *pv;
         }
-        dst[a.C + d] = vk;
-        dst[2 * a.C + d] = vv;
+        *pk = vk;
+        *pv = vv;
+        if (a.outbf) {
+          *reinterpret_cast<u16x4*>(a.outbf + off + a.C + d) = pack4(vk);
+          *reinterpret_cast<u16x4*>(a.outbf + off + 2 * a.C + d) = pack4(vv);
+        }
       }
   }
 }
@@ -483,11 +500,11 @@ unsigned attn_grid(int T, int BH) { return (unsigned)(((T + 127) / 128) * ((BH +
 
 bool flash_attention_supported(int hs, int64_t C) { return (hs == 64 || hs == 32) && C % 8 == 0; }
 
-hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, float* lse, int B, int T, int H, int C, float scale,
-                               hipStream_t s) {
+hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, uint16_t* ybf, float* lse, int B, int T, int H, int C,
+                               float scale, hipStream_t s) {
   if (B <= 0 || T <= 0) return hipSuccess;
   AttnArgs a{};
-  a.qkv = qkv, a.out = y, a.lse = lse, a.B = B, a.T = T, a.H = H, a.C = C, a.scale = scale;
+  a.qkv = qkv, a.out = y, a.outbf = ybf, a.lse = lse, a.B = B, a.T = T, a.H = H, a.C = C, a.scale = scale;
   dim3 grid(attn_grid(T, B * H));
   const int hs = C / H;
   if (hs == 64)
@@ -500,11 +517,12 @@ hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, float* lse, int B,
 }
 
 hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float* dyf, const uint16_t* dy,
-                               const float* lse, float* D, float* dqkv, float beta, int B, int T, int H, int C,
-                               float scale, hipStream_t s) {
+                               const float* lse, float* D, float* dqkv, uint16_t* dqkv_bf, float beta, int B, int T,
+                               int H, int C, float scale, hipStream_t s) {
   if (B <= 0 || T <= 0) return hipSuccess;
   AttnArgs a{};
   a.qkv = qkv, a.y = y, a.dyf = dyf, a.dy = dy, a.lse = const_cast<float*>(lse), a.D = D, a.out = dqkv;
+  a.outbf = dqkv_bf;
   a.B = B, a.T = T, a.H = H, a.C = C, a.scale = scale, a.beta = beta;
   const int hs = C / H;
   dim3 gd((unsigned)(((int64_t)B * T + 3) / 4));

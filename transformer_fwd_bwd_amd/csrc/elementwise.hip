@@ -29,6 +29,9 @@ __global__ void map1(int64_t n, F f) {
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) f(i);
 }
 
+// bf16 bits of x, rounded to nearest even (the rounding of every bf16 operand copy)
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
 __global__ void to_bf16_k(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
     const __bf16 b = (__bf16)src[i];
@@ -243,35 +246,44 @@ hipError_t tanh_bwd(const float* g, const float* y, float* d, float beta, int64_
   return hipGetLastError();
 }
 
-hipError_t gelu_fwd(const float* a, float* y, int64_t n, hipStream_t s) {
+hipError_t gelu_fwd(const float* a, float* y, uint16_t* ybf, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (n % 4 == 0 && aligned16(a) && aligned16(y)) {
+  if (n % 4 == 0 && aligned16(a) && aligned16(y) && (reinterpret_cast<uintptr_t>(ybf) & 7) == 0) {
     const f4* a4 = (const f4*)a;
     f4* y4 = (f4*)y;
+    u16x4* b4 = (u16x4*)ybf;
     auto f = [=] __device__(int64_t i) {
       f4 v = a4[i];
-      y4[i] = f4{gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3])};
+      const f4 o = {gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3])};
+      y4[i] = o;
+      if (b4) b4[i] = u16x4{bf16_bits(o[0]), bf16_bits(o[1]), bf16_bits(o[2]), bf16_bits(o[3])};
     };
     hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
   } else {
-    auto f = [=] __device__(int64_t i) { y[i] = gelu_f(a[i]); };
+    auto f = [=] __device__(int64_t i) {
+      const float o = gelu_f(a[i]);
+      y[i] = o;
+      if (ybf) ybf[i] = bf16_bits(o);
+    };
     hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   }
   return hipGetLastError();
 }
 
-hipError_t gelu_bwd(const float* g, const float* x, float* d, float beta, int64_t n, hipStream_t s) {
+hipError_t gelu_bwd(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (n % 4 == 0 && aligned16(g) && aligned16(x) && aligned16(d)) {
+  if (n % 4 == 0 && aligned16(g) && aligned16(x) && aligned16(d) && (reinterpret_cast<uintptr_t>(dbf) & 7) == 0) {
     const f4* g4 = (const f4*)g;
     const f4* x4 = (const f4*)x;
     f4* d4 = (f4*)d;
+    u16x4* b4 = (u16x4*)dbf;
     auto f = [=] __device__(int64_t i) {
       f4 gv = g4[i], xv = x4[i];
       f4 v = {gv[0] * gelu_grad(xv[0]), gv[1] * gelu_grad(xv[1]), gv[2] * gelu_grad(xv[2]),
               gv[3] * gelu_grad(xv[3])};
       if (beta != 0.f) v += d4[i];
       d4[i] = v;
+      if (b4) b4[i] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
     };
     hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
   } else {
@@ -279,6 +291,7 @@ hipError_t gelu_bwd(const float* g, const float* x, float* d, float beta, int64_
       float v = g[i] * gelu_grad(x[i]);
       if (beta != 0.f) v += d[i];
       d[i] = v;
+      if (dbf) dbf[i] = bf16_bits(v);
     };
     hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   }

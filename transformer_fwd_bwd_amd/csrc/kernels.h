@@ -61,8 +61,11 @@ hipError_t mul_bwd(const float* g, const float* other, float* d, float beta, int
 hipError_t scale_fwd(const float* a, float sc, float* y, int64_t n, hipStream_t s);
 hipError_t tanh_fwd(const float* a, float* y, int64_t n, hipStream_t s);
 hipError_t tanh_bwd(const float* g, const float* y, float* d, float beta, int64_t n, hipStream_t s);
-hipError_t gelu_fwd(const float* a, float* y, int64_t n, hipStream_t s);
-hipError_t gelu_bwd(const float* g, const float* x, float* d, float beta, int64_t n, hipStream_t s);
+// Producers of contraction operands take an optional `*bf` pointer: when it is
+// non-null they also write the bf16 (round-to-nearest-even) copy of what they
+// store, in the same layout, sparing a separate conversion pass.
+hipError_t gelu_fwd(const float* a, float* y, uint16_t* ybf, int64_t n, hipStream_t s);
+hipError_t gelu_bwd(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t n, hipStream_t s);
 // out[c] = beta*out[c] + sum_r g[r*cols + c]; deterministic two-stage reduction
 size_t colsum_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s);
@@ -80,7 +83,7 @@ hipError_t permute_heads(const float* x, float* y, int64_t B, int64_t T, int64_t
                          float beta, hipStream_t s);
 
 // ---- row reductions (rowops.hip)
-hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, float* y, float* mean,
+hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, float* y, uint16_t* ybf, float* mean,
                          float* rstd, int64_t rows, int64_t C, float eps, hipStream_t s);
 size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C);
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
@@ -96,18 +99,19 @@ size_t softmax_ce_workspace_bytes(int64_t rows);
 hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* targets, int64_t rows, int64_t V,
                           float* lse, float* loss, void* ws, hipStream_t s);
 hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* targets, const float* lse,
-                          const float* g_scalar, float* dl, int64_t rows, int64_t V, float beta, hipStream_t s);
+                          const float* g_scalar, float* dl, uint16_t* dlbf, int64_t rows, int64_t V, float beta,
+                          hipStream_t s);
 
 // ---- fused causal attention, bf16 variant (attention.hip)
 // qkv: bf16 [B, T, 3C] (q | k | v thirds, head h = columns h*hs .. h*hs+hs-1 of each third)
 // y: fp32 [B, T, C]; lse: [B*H, T] base-2 log-sum-exp of the scaled scores (saved for backward)
 bool flash_attention_supported(int hs, int64_t C);
-hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, float* lse, int B, int T, int H, int C, float scale,
-                               hipStream_t s);
+hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, uint16_t* ybf, float* lse, int B, int T, int H, int C,
+                               float scale, hipStream_t s);
 // dqkv = beta*dqkv + d(qkv); D: [B*H, T] scratch
 hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float* dyf, const uint16_t* dy,
-                               const float* lse, float* D, float* dqkv, float beta, int B, int T, int H, int C,
-                               float scale, hipStream_t s);
+                               const float* lse, float* D, float* dqkv, uint16_t* dqkv_bf, float beta, int B, int T,
+                               int H, int C, float scale, hipStream_t s);
 
 // ---- KV-cached inference (decode.hip); cache fp32 [L][2][B][Tmax][C]
 hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, int B, int Tmax, int pos0,

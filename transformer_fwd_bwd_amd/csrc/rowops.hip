@@ -13,6 +13,11 @@
 namespace tfb {
 namespace {
 
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+// bf16 bits of x, rounded to nearest even (the rounding of every bf16 operand copy)
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;
@@ -32,8 +37,8 @@ __device__ __forceinline__ float wave_max(float v) {
 template <bool CACHED>
 __global__ __launch_bounds__(NT) void ln_fwd_k(const float* __restrict__ x, const float* __restrict__ gamma,
                                                const float* __restrict__ beta, float* __restrict__ y,
-                                               float* __restrict__ mean, float* __restrict__ rstd, int64_t rows,
-                                               int C, float eps) {
+                                               uint16_t* __restrict__ ybf, float* __restrict__ mean,
+                                               float* __restrict__ rstd, int64_t rows, int C, float eps) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * WAVES;
   for (int64_t r = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); r < rows; r += nw) {
@@ -71,10 +76,18 @@ __global__ __launch_bounds__(NT) void ln_fwd_k(const float* __restrict__ x, cons
 #pragma unroll
       for (int j = 0; j < MAXV; ++j) {
         const int c = lane + 64 * j;
-        if (c < C) yr[c] = (v[j] - mu) * rs * gamma[c] + beta[c];
+        if (c < C) {
+          const float o = (v[j] - mu) * rs * gamma[c] + beta[c];
+          yr[c] = o;
+          if (ybf) ybf[r * C + c] = bf16_bits(o);
+        }
       }
     } else {
-      for (int c = lane; c < C; c += 64) yr[c] = (xr[c] - mu) * rs * gamma[c] + beta[c];
+      for (int c = lane; c < C; c += 64) {
+        const float o = (xr[c] - mu) * rs * gamma[c] + beta[c];
+        yr[c] = o;
+        if (ybf) ybf[r * C + c] = bf16_bits(o);
+      }
     }
     if (lane == 0) {
       mean[r] = mu;
@@ -88,8 +101,8 @@ __global__ __launch_bounds__(NT) void ln_fwd_k(const float* __restrict__ x, cons
 template <int J>
 __global__ __launch_bounds__(NT) void ln_fwd4_k(const f4* __restrict__ x, const f4* __restrict__ gamma,
                                                 const f4* __restrict__ beta, f4* __restrict__ y,
-                                                float* __restrict__ mean, float* __restrict__ rstd, int64_t rows,
-                                                int C4, float eps) {
+                                                u16x4* __restrict__ ybf, float* __restrict__ mean,
+                                                float* __restrict__ rstd, int64_t rows, int C4, float eps) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * WAVES;
   const float invC = 1.f / (4 * C4);
@@ -118,7 +131,11 @@ __global__ __launch_bounds__(NT) void ln_fwd4_k(const f4* __restrict__ x, const 
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int c = lane + 64 * j;
-      if (c < C4) yr[c] = (v[j] - mu) * rs * gamma[c] + beta[c];
+      if (c < C4) {
+        const f4 o = (v[j] - mu) * rs * gamma[c] + beta[c];
+        yr[c] = o;
+        if (ybf) ybf[r * C4 + c] = u16x4{bf16_bits(o[0]), bf16_bits(o[1]), bf16_bits(o[2]), bf16_bits(o[3])};
+      }
     }
     if (lane == 0) {
       mean[r] = mu;
@@ -453,18 +470,20 @@ __global__ __launch_bounds__(NT) void mean_k(const float* __restrict__ v, int64_
 
 __global__ __launch_bounds__(NT) void ce_bwd_k(const float* __restrict__ logits, int64_t ld,
                                                const int32_t* __restrict__ tgt, const float* __restrict__ lse,
-                                               const float* __restrict__ gsc, float* __restrict__ dl, int64_t rows,
-                                               int64_t V, float beta) {
+                                               const float* __restrict__ gsc, float* __restrict__ dl,
+                                               uint16_t* __restrict__ dlbf, int64_t rows, int64_t V, float beta) {
   const int64_t r = blockIdx.x;
   const float gn = gsc[0] / (float)rows;
   const float L = lse[r];
   const int t = tgt[r];
   const float* lr = logits + r * ld;
   float* dr = dl + r * ld;
+  uint16_t* br = dlbf ? dlbf + r * ld : nullptr;
   for (int64_t c = threadIdx.x; c < V; c += NT) {
     float v = gn * (expf(lr[c] - L) - (c == t ? 1.f : 0.f));
     if (beta != 0.f) v += dr[c];
     dr[c] = v;
+    if (br) br[c] = bf16_bits(v);
   }
 }
 
@@ -476,22 +495,23 @@ inline unsigned row_blocks(int64_t rows) {
 
 }  // namespace
 
-hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, float* y, float* mean, float* rstd,
-                         int64_t rows, int64_t C, float eps, hipStream_t s) {
+hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, float* y, uint16_t* ybf, float* mean,
+                         float* rstd, int64_t rows, int64_t C, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (C % 4 == 0 && C <= 1024 && aligned16(x) && aligned16(y) && aligned16(gamma) && aligned16(beta)) {
+  if (C % 4 == 0 && C <= 1024 && aligned16(x) && aligned16(y) && aligned16(gamma) && aligned16(beta) &&
+      (reinterpret_cast<uintptr_t>(ybf) & 7) == 0) {
     const int C4 = (int)(C / 4);
     if (C4 <= 64)
       hipLaunchKernelGGL(ln_fwd4_k<1>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
-                         (const f4*)beta, (f4*)y, mean, rstd, rows, C4, eps);
+                         (const f4*)beta, (f4*)y, (u16x4*)ybf, mean, rstd, rows, C4, eps);
     else
       hipLaunchKernelGGL(ln_fwd4_k<4>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
-                         (const f4*)beta, (f4*)y, mean, rstd, rows, C4, eps);
+                         (const f4*)beta, (f4*)y, (u16x4*)ybf, mean, rstd, rows, C4, eps);
   } else if (C <= 64 * MAXV)
-    hipLaunchKernelGGL(ln_fwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, mean, rstd, rows,
+    hipLaunchKernelGGL(ln_fwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, ybf, mean, rstd, rows,
                        (int)C, eps);
   else
-    hipLaunchKernelGGL(ln_fwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, mean, rstd, rows,
+    hipLaunchKernelGGL(ln_fwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, ybf, mean, rstd, rows,
                        (int)C, eps);
   return hipGetLastError();
 }
@@ -563,10 +583,11 @@ hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* target
 }
 
 hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* targets, const float* lse,
-                          const float* g_scalar, float* dl, int64_t rows, int64_t V, float beta, hipStream_t s) {
+                          const float* g_scalar, float* dl, uint16_t* dlbf, int64_t rows, int64_t V, float beta,
+                          hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, rows, V,
-                     beta);
+  hipLaunchKernelGGL(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
+                     rows, V, beta);
   return hipGetLastError();
 }
 

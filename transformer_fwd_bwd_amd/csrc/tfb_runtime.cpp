@@ -274,6 +274,19 @@ struct Ctx {
     return static_cast<uint16_t*>(c->arena.alloc_step(bytes));
   }
 
+  // bf16 copy written by the producing kernel beside its fp32 output (bf16
+  // variant only; null otherwise).  The caller marks it valid after the launch.
+  uint16_t* twin_data(TensorRec& t) {
+    if (!bf16_mode()) return nullptr;
+    if (!t.bf) t.bf = alloc_bf16(t);
+    return t.bf;
+  }
+  uint16_t* twin_grad(TensorRec& t) {
+    if (!bf16_mode()) return nullptr;
+    if (!t.gbf) t.gbf = alloc_bf16(t);
+    return t.gbf;
+  }
+
   // bf16 copy of a tensor's data, converted once and reused until the data changes
   const uint16_t* data_bf16(TensorRec& t) {
     if (!t.bf_valid) {
@@ -487,7 +500,9 @@ void backward_rec(Ctx& C, const Rec& r) {
     case OP_GELU: {
       TensorRec& a = C.T(r.in[0]);
       auto da = C.gdst(r.in[0]);
-      hip_check(gelu_bwd(g, a.data, da.first, da.second, out.numel, s), "gelu bwd");
+      uint16_t* db = C.twin_grad(a);
+      hip_check(gelu_bwd(g, a.data, da.first, db, da.second, out.numel, s), "gelu bwd");
+      if (db) a.gbf_valid = true;
       break;
     }
     case OP_MATMUL:
@@ -621,12 +636,14 @@ void backward_rec(Ctx& C, const Rec& r) {
         const uint16_t* qb = C.data_bf16(qkv);
         const uint16_t* dyb = C.grad_bf16(out);
         auto dq = C.gdst(r.in[0]);
+        uint16_t* dqb = C.twin_grad(qkv);
         size_t mark = C.c->arena.hi;
         float* D = static_cast<float*>(C.scratch((size_t)B * H * T * sizeof(float)));
-        hip_check(flash_attention_bwd(qb, out.data, g, dyb, static_cast<const float*>(r.s1), D, dq.first, dq.second,
-                                      (int)B, (int)T, (int)H, (int)Cc, scale, s),
+        hip_check(flash_attention_bwd(qb, out.data, g, dyb, static_cast<const float*>(r.s1), D, dq.first, dqb,
+                                      dq.second, (int)B, (int)T, (int)H, (int)Cc, scale, s),
                   "attention bwd");
         C.c->arena.hi = mark;
+        qkv.gbf_valid = true;
         break;
       }
       float* P = static_cast<float*>(r.s0);
@@ -681,9 +698,11 @@ void backward_rec(Ctx& C, const Rec& r) {
     case OP_SOFTMAX_CE: {
       TensorRec& lg = C.T(r.in[0]);
       auto dl = C.gdst(r.in[0]);
+      uint16_t* dlb = C.twin_grad(lg);
       hip_check(softmax_ce_bwd(lg.data, lg.stride(), static_cast<const int32_t*>(r.s0),
-                               static_cast<const float*>(r.s1), g, dl.first, lg.rows(), lg.cols(), dl.second, s),
+                               static_cast<const float*>(r.s1), g, dl.first, dlb, lg.rows(), lg.cols(), dl.second, s),
                 "softmax_ce bwd");
+      if (dlb) lg.gbf_valid = true;
       break;
     }
     case OP_COMPACT: {
@@ -988,7 +1007,9 @@ int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
     TensorRec& A = C.T(a);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     int h = C.make_output(shape_vec(A));
-    hip_check(gelu_fwd(ctx->tensors[a].data, ctx->tensors[h].data, ctx->tensors[h].numel, C.s()), "gelu");
+    uint16_t* yb = C.twin_data(ctx->tensors[h]);
+    hip_check(gelu_fwd(ctx->tensors[a].data, ctx->tensors[h].data, yb, ctx->tensors[h].numel, C.s()), "gelu");
+    if (yb) ctx->tensors[h].bf_valid = true;
     Rec r{OP_GELU};
     r.in[0] = a, r.out = h;
     C.record(r);
@@ -1068,9 +1089,11 @@ int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta,
     int h = C.make_output(shape_vec(X));
     float* mean = static_cast<float*>(C.scratch((size_t)rows * sizeof(float)));
     float* rstd = static_cast<float*>(C.scratch((size_t)rows * sizeof(float)));
+    uint16_t* yb = C.twin_data(ctx->tensors[h]);
     hip_check(layernorm_fwd(ctx->tensors[x].data, ctx->tensors[gamma].data, ctx->tensors[beta].data,
-                            ctx->tensors[h].data, mean, rstd, rows, Cc, eps, C.s()),
+                            ctx->tensors[h].data, yb, mean, rstd, rows, Cc, eps, C.s()),
               "layernorm");
+    if (yb) ctx->tensors[h].bf_valid = true;
     Rec r{OP_LAYERNORM};
     r.in[0] = x, r.in[1] = gamma, r.in[2] = beta, r.out = h, r.f = eps;
     r.s0 = mean, r.s1 = rstd;
@@ -1234,8 +1257,10 @@ int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y)
       // bf16 variant: fused kernels, no T x T buffers
       const uint16_t* qb = C.data_bf16(ctx->tensors[qkv]);
       float* lse = static_cast<float*>(C.scratch((size_t)B * H * T * sizeof(float)));
-      hip_check(flash_attention_fwd(qb, ctx->tensors[h].data, lse, (int)B, (int)T, (int)H, (int)Cc, scale, C.s()),
+      uint16_t* yb = C.twin_data(ctx->tensors[h]);
+      hip_check(flash_attention_fwd(qb, ctx->tensors[h].data, yb, lse, (int)B, (int)T, (int)H, (int)Cc, scale, C.s()),
                 "attention");
+      ctx->tensors[h].bf_valid = true;
       Rec r{OP_ATTENTION};
       r.in[0] = qkv, r.out = h, r.i0 = H, r.i1 = 1, r.f = scale;
       r.s1 = lse;
