@@ -336,8 +336,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
   constexpr int LDK = Lds<BF16, BK>::LDK;
   using LT = typename Lds<BF16, BK>::T;
   // a bf16 r-contiguous operand keeps its own [k][r] layout in LDS (StageTr)
-  constexpr bool TRA = BF16 && A_BF && A_RC && BK == 64;
-  constexpr bool TRB = BF16 && B_BF && !B_KC && BK == 64;
+  constexpr bool TRA = BF16 && A_BF && A_RC && BK % 16 == 0;
+  constexpr bool TRB = BF16 && B_BF && !B_KC && BK % 16 == 0;
   constexpr int LDA = TRA ? BM + 16 : LDK, LDB = TRB ? BN + 16 : LDK;
   __shared__ __attribute__((aligned(16))) LT As[2][TRA ? BK * LDA : BM * LDA];
   __shared__ __attribute__((aligned(16))) LT Bs[2][TRB ? BK * LDB : BN * LDB];
@@ -546,6 +546,7 @@ enum Cfg { CFG_128x128 = 1, CFG_128x64 = 2 };
 struct Plan {
   int cfg;
   int BM, BN;
+  int bk;  // k-tile depth when both operands are stored as bf16
   int splits;
   int k_per_split;
 };
@@ -563,6 +564,10 @@ Plan make_plan(const GemmArgs& g) {
     // fill the 256 compute units at least once when K is long
     while (tiles * p.splits < 256 && g.K / (p.splits * 2) >= 1024 && p.splits < 16) p.splits *= 2;
   }
+  // Both operands bf16: 64-deep k-tiles (72 KB of LDS, two workgroups per CU)
+  // amortize the per-tile barrier best; a short K over many tiles does better
+  // with 32-deep ones (40 KB, three workgroups per CU hide more latency).
+  p.bk = (g.K <= 1024 && tiles * p.splits >= 512) ? 32 : 64;
   const int kps = (g.K + p.splits - 1) / p.splits;
   p.k_per_split = ((kps + KALIGN - 1) / KALIGN) * KALIGN;
   p.splits = std::max(1, (g.K + p.k_per_split - 1) / p.k_per_split);
@@ -584,17 +589,18 @@ hipError_t launch_layout(const KArgs& ka, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// k-tile depth: 64 when both operands are stored as bf16 (16 bytes of k per
-// row per load, 32 MFMAs per wave between barriers), 32 otherwise (fp32
-// staging registers would double)
+// k-tile depth: the plan's choice (32 or 64) when both operands are stored as
+// bf16, 32 otherwise (fp32 staging registers would double)
 template <int WM, int WN, int TM, int TN>
-hipError_t launch_prec(const KArgs& ka, dim3 grid, hipStream_t s) {
+hipError_t launch_prec(const KArgs& ka, int bk, dim3 grid, hipStream_t s) {
   const GemmArgs& g = ka.g;
   if (g.prec != PREC_BF16) {
     if (g.a_bf16 || g.b_bf16) return hipErrorInvalidValue;
     return launch_layout<WM, WN, TM, TN, 32, false, false, false>(ka, grid, s);
   }
-  if (g.a_bf16 && g.b_bf16) return launch_layout<WM, WN, TM, TN, 64, true, true, true>(ka, grid, s);
+  if (g.a_bf16 && g.b_bf16)
+    return bk == 32 ? launch_layout<WM, WN, TM, TN, 32, true, true, true>(ka, grid, s)
+                    : launch_layout<WM, WN, TM, TN, 64, true, true, true>(ka, grid, s);
   if (g.a_bf16) return launch_layout<WM, WN, TM, TN, 32, true, true, false>(ka, grid, s);
   if (g.b_bf16) return launch_layout<WM, WN, TM, TN, 32, true, false, true>(ka, grid, s);
   return launch_layout<WM, WN, TM, TN, 32, true, false, false>(ka, grid, s);
@@ -624,9 +630,9 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   dim3 grid(ka.tiles_m * ka.tiles_n * g.batch * p.splits);
   hipError_t e;
   if (p.cfg == CFG_128x128)
-    e = launch_prec<2, 2, 2, 2>(ka, grid, s);
+    e = launch_prec<2, 2, 2, 2>(ka, p.bk, grid, s);
   else
-    e = launch_prec<4, 1, 1, 2>(ka, grid, s);
+    e = launch_prec<4, 1, 1, 2>(ka, p.bk, grid, s);
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t MN = (int64_t)g.M * g.N;
   dim3 rgrid((unsigned)std::min<int64_t>((MN + 255) / 256, 4096), g.batch);
