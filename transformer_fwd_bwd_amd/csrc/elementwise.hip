@@ -106,6 +106,34 @@ __global__ void colsum_stage1(const float* __restrict__ g, int64_t rows, int64_t
   partial[(int64_t)blockIdx.y * cols + c] = (s0 + s1) + (s2 + s3);
 }
 
+// The same over float4 columns: a workgroup covers 256 columns (64 lanes x 4)
+// and 4 row groups that interleave over the slab's rows, 8 rows in flight per
+// thread; the 4 group sums are added in LDS, in a fixed order.
+__global__ __launch_bounds__(NT) void colsum4_stage1(const f4* __restrict__ g, int64_t rows, int64_t cols4,
+                                                    int64_t rows_per, f4* __restrict__ partial) {
+  __shared__ f4 sh[3][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 64 + tx;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per;
+  const int64_t r1 = std::min(rows, r0 + rows_per);
+  f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+  if (c < cols4) {
+    int64_t r = r0 + ty;
+    for (; r + 28 < r1; r += 32) {
+      f4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = g[(r + 4 * u) * cols4 + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u & 1] += v[u];
+    }
+    for (; r < r1; r += 4) acc[0] += g[r * cols4 + c];
+  }
+  const f4 t = acc[0] + acc[1];
+  if (ty > 0) sh[ty - 1][tx] = t;
+  __syncthreads();
+  if (ty == 0 && c < cols4) partial[(int64_t)blockIdx.y * cols4 + c] = ((t + sh[0][tx]) + sh[1][tx]) + sh[2][tx];
+}
+
 // out[c] (+)= sum over the partial rows; 64 columns x 16 partial-groups per workgroup
 __global__ __launch_bounds__(1024) void colsum_stage2(const float* __restrict__ partial, int nparts, int64_t cols,
                                                       float* __restrict__ out, float beta) {
@@ -306,18 +334,28 @@ static int64_t colsum_parts(int64_t rows, int64_t cols) {
   return std::min<int64_t>(parts, 256);
 }
 
+// float4 path: slabs of at least 128 rows (32 per row group: four rounds of 8 loads in flight)
+static int64_t colsum4_parts(int64_t rows) { return std::min<int64_t>(256, std::max<int64_t>(1, rows / 128)); }
+
 size_t colsum_workspace_bytes(int64_t rows, int64_t cols) {
-  return (size_t)colsum_parts(rows, cols) * cols * sizeof(float);
+  return (size_t)std::max(colsum_parts(rows, cols), colsum4_parts(rows)) * cols * sizeof(float);
 }
 
 hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s) {
   if (cols <= 0) return hipSuccess;
   if (rows == 1) return axpby(out, g, 1.f, beta, cols, s);
-  const int64_t parts = colsum_parts(rows, cols);
-  const int64_t rows_per = (rows + parts - 1) / parts;
   float* partial = static_cast<float*>(ws);
-  dim3 g1((unsigned)((cols + NT - 1) / NT), (unsigned)parts);
-  hipLaunchKernelGGL(colsum_stage1, g1, dim3(NT), 0, s, g, rows, cols, rows_per, partial);
+  const bool vec = cols % 4 == 0 && aligned16(g) && aligned16(partial);
+  const int64_t parts = vec ? colsum4_parts(rows) : colsum_parts(rows, cols);
+  const int64_t rows_per = (rows + parts - 1) / parts;
+  if (vec) {
+    const int64_t cols4 = cols / 4;
+    dim3 g1((unsigned)((cols4 + 63) / 64), (unsigned)parts);
+    hipLaunchKernelGGL(colsum4_stage1, g1, dim3(NT), 0, s, (const f4*)g, rows, cols4, rows_per, (f4*)partial);
+  } else {
+    dim3 g1((unsigned)((cols + NT - 1) / NT), (unsigned)parts);
+    hipLaunchKernelGGL(colsum_stage1, g1, dim3(NT), 0, s, g, rows, cols, rows_per, partial);
+  }
   hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, (int)parts, cols,
                      out, beta);
   return hipGetLastError();

@@ -493,6 +493,105 @@ inline unsigned row_blocks(int64_t rows) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>((rows + WAVES - 1) / WAVES, 65536));
 }
 
+
+// The same over float4 (rows 16-byte aligned): 16 logits in flight per thread,
+// one max / rescale per 16, then the scalar tail of V % 4 logits.
+__global__ __launch_bounds__(NT) void ce_fwd4_k(const float* __restrict__ logits, int64_t ld,
+                                                const int32_t* __restrict__ tgt, int64_t V, float* __restrict__ lse,
+                                                float* __restrict__ loss_rows) {
+  __shared__ float sm[WAVES], ss[WAVES];
+  const int64_t r = blockIdx.x;
+  const float* lr = logits + r * ld;
+  const f4* lr4 = reinterpret_cast<const f4*>(lr);
+  const int64_t V4 = V / 4;
+  float m = -INFINITY, s = 0.f;
+  for (int64_t c = threadIdx.x; c < V4; c += 4 * NT) {
+    f4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = c + u * NT;
+      x[u] = i < V4 ? lr4[i] : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
+    s *= expf(m - mx);  // m = -inf the first time: s is 0 and stays 0
+    m = mx;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s += (expf(x[u][0] - m) + expf(x[u][1] - m)) + (expf(x[u][2] - m) + expf(x[u][3] - m));
+  }
+  for (int64_t c = 4 * V4 + threadIdx.x; c < V; c += NT) {
+    const float x = lr[c];
+    if (x > m) {
+      s = s * expf(m - x) + 1.f;
+      m = x;
+    } else {
+      s += expf(x - m);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    online_merge(m, s, m2, s2);
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+    sm[w] = m;
+    ss[w] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = sm[0], S = ss[0];
+    for (int i = 1; i < WAVES; ++i) online_merge(M, S, sm[i], ss[i]);
+    const float L = M + logf(S);
+    lse[r] = L;
+    const int t = tgt[r];
+    loss_rows[r] = (t >= 0 && t < V) ? fminf(L - lr[t], 69.07755278982137f) : NAN;
+  }
+}
+
+
+// float4 form of ce_bwd_k (rows 16-byte aligned): two float4 per thread in flight
+__global__ __launch_bounds__(NT) void ce_bwd4_k(const float* __restrict__ logits, int64_t ld,
+                                                const int32_t* __restrict__ tgt, const float* __restrict__ lse,
+                                                const float* __restrict__ gsc, float* __restrict__ dl,
+                                                uint16_t* __restrict__ dlbf, int64_t rows, int64_t V, float beta) {
+  const int64_t r = blockIdx.x;
+  const float gn = gsc[0] / (float)rows;
+  const float L = lse[r];
+  const int t = tgt[r];
+  const f4* lr4 = reinterpret_cast<const f4*>(logits + r * ld);
+  f4* dr4 = reinterpret_cast<f4*>(dl + r * ld);
+  u16x4* br4 = dlbf ? reinterpret_cast<u16x4*>(dlbf + r * ld) : nullptr;
+  const int64_t V4 = V / 4;
+  for (int64_t c = threadIdx.x; c < V4; c += 2 * NT) {
+    f4 x[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t i = c + u * NT;
+      if (i < V4) x[u] = lr4[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t i = c + u * NT;
+      if (i >= V4) continue;
+      f4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = gn * (expf(x[u][e] - L) - (4 * i + e == t ? 1.f : 0.f));
+      if (beta != 0.f) v += dr4[i];
+      dr4[i] = v;
+      if (br4) br4[i] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
+    }
+  }
+  const float* lr = logits + r * ld;
+  float* dr = dl + r * ld;
+  for (int64_t c = 4 * V4 + threadIdx.x; c < V; c += NT) {
+    float v = gn * (expf(lr[c] - L) - (c == t ? 1.f : 0.f));
+    if (beta != 0.f) v += dr[c];
+    dr[c] = v;
+    if (dlbf) dlbf[r * ld + c] = bf16_bits(v);
+  }
+}
+
 }  // namespace
 
 hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, float* y, uint16_t* ybf, float* mean,
@@ -577,7 +676,10 @@ hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* target
                           float* lse, float* loss, void* ws, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   float* loss_rows = static_cast<float*>(ws);
-  hipLaunchKernelGGL(ce_fwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
+  if (ld % 4 == 0 && aligned16(logits))
+    hipLaunchKernelGGL(ce_fwd4_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
+  else
+    hipLaunchKernelGGL(ce_fwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
   hipLaunchKernelGGL(mean_k, dim3(1), dim3(NT), 0, s, loss_rows, rows, loss);
   return hipGetLastError();
 }
@@ -586,8 +688,12 @@ hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* target
                           const float* g_scalar, float* dl, uint16_t* dlbf, int64_t rows, int64_t V, float beta,
                           hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
-                     rows, V, beta);
+  if (ld % 4 == 0 && aligned16(logits) && aligned16(dl) && (reinterpret_cast<uintptr_t>(dlbf) & 7) == 0)
+    hipLaunchKernelGGL(ce_bwd4_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
+                       rows, V, beta);
+  else
+    hipLaunchKernelGGL(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
+                       rows, V, beta);
   return hipGetLastError();
 }
 
