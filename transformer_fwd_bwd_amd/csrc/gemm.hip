@@ -559,15 +559,29 @@ Plan make_plan(const GemmArgs& g) {
     p.cfg = CFG_128x128, p.BM = 128, p.BN = 128;
   }
   const int64_t tiles = (int64_t)((g.M + p.BM - 1) / p.BM) * ((g.N + p.BN - 1) / p.BN) * g.batch;
-  p.splits = 1;
-  if (g.causal_a == CAUSAL_NONE && !g.causal_out) {
-    // fill the 256 compute units at least once when K is long
-    while (tiles * p.splits < 256 && g.K / (p.splits * 2) >= 1024 && p.splits < 16) p.splits *= 2;
-  }
   // Both operands bf16: 64-deep k-tiles (72 KB of LDS, two workgroups per CU)
   // amortize the per-tile barrier best; a short K over many tiles does better
   // with 32-deep ones (40 KB, three workgroups per CU hide more latency).
-  p.bk = (g.K <= 1024 && tiles * p.splits >= 512) ? 32 : 64;
+  p.bk = (g.K <= 1024 && tiles >= 512) ? 32 : 64;
+  // K split: the workgroups resident at once (slots) run in rounds, so a tile
+  // count just past a multiple of the slots wastes most of a round.  Pick the
+  // split that minimizes rounds x (k-tiles per item) plus the partials'
+  // traffic (written and read once more by the reduction, ~5 TB/s), with at
+  // least 512 k per item.
+  p.splits = 1;
+  if (g.causal_a == CAUSAL_NONE && !g.causal_out && g.K >= 1024) {
+    const int64_t slots = 256 * (p.bk == 32 ? 3 : 2);
+    const double tile_s_per_k = 2.0 * p.BM * p.BN / 1.0e12;  // ~1 TFLOP/s per resident workgroup
+    const double out_bytes = 4.0 * g.M * g.N * g.batch;
+    double best = 0.0;
+    for (int sp = 1; sp <= 16; ++sp) {
+      if (sp > 1 && g.K / sp < 512) break;
+      const int64_t items = tiles * sp;
+      const double rounds = (double)((items + slots - 1) / slots);
+      const double t = rounds * ((double)g.K / sp) * tile_s_per_k + (sp > 1 ? (sp + 1) * out_bytes / 5.0e12 : 0.0);
+      if (sp == 1 || t < best * 0.97) best = t, p.splits = sp;
+    }
+  }
   const int kps = (g.K + p.splits - 1) / p.splits;
   p.k_per_split = ((kps + KALIGN - 1) / KALIGN) * KALIGN;
   p.splits = std::max(1, (g.K + p.k_per_split - 1) / p.k_per_split);
