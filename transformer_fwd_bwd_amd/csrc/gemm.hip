@@ -40,6 +40,9 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KALIGN = 32;  // split-K chunks are multiples of this (and of every k-tile depth)
+#ifndef GEMM_BIG_TILES
+#define GEMM_BIG_TILES 4096  // products with at least this many 256x128 tiles use them (vocabulary-sized)
+#endif
 #ifndef GEMM_GROUP_M
 #define GEMM_GROUP_M 8       // tile rows per raster group
 #endif
@@ -330,7 +333,7 @@ struct KArgs {
 };
 
 template <int WM, int WN, int TM, int TN, int BK, bool BF16, bool A_RC, bool B_KC, bool A_BF, bool B_BF>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(KArgs ka) {
+__global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
   constexpr int NT = WM * WN * 64;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int LDK = Lds<BF16, BK>::LDK;
@@ -541,7 +544,7 @@ __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, i
   }
 }
 
-enum Cfg { CFG_128x128 = 1, CFG_128x64 = 2 };
+enum Cfg { CFG_128x128 = 1, CFG_128x64 = 2, CFG_256x128 = 3 };
 
 struct Plan {
   int cfg;
@@ -555,6 +558,11 @@ Plan make_plan(const GemmArgs& g) {
   Plan p;
   if (g.N <= 64) {
     p.cfg = CFG_128x64, p.BM = 128, p.BN = 64;
+  } else if (g.prec == PREC_BF16 && g.a_bf16 && g.b_bf16 && g.causal_a == CAUSAL_NONE && !g.causal_out &&
+             (int64_t)((g.M + 255) / 256) * ((g.N + 127) / 128) * g.batch >= GEMM_BIG_TILES) {
+    // 4 waves of 128x64 read a quarter less LDS per MFMA; two workgroups fit per CU
+    // only with 32-deep k-tiles, which pays off on vocabulary-sized products
+    p.cfg = CFG_256x128, p.BM = 256, p.BN = 128;
   } else {
     p.cfg = CFG_128x128, p.BM = 128, p.BN = 128;
   }
@@ -562,7 +570,7 @@ Plan make_plan(const GemmArgs& g) {
   // Both operands bf16: 64-deep k-tiles (72 KB of LDS, two workgroups per CU)
   // amortize the per-tile barrier best; a short K over many tiles does better
   // with 32-deep ones (40 KB, three workgroups per CU hide more latency).
-  p.bk = (g.K <= 1024 && tiles >= 512) ? 32 : 64;
+  p.bk = (p.cfg == CFG_256x128 || (g.K <= 1024 && tiles >= 512)) ? 32 : 64;
   // K split: the workgroups resident at once (slots) run in rounds, so a tile
   // count just past a multiple of the slots wastes most of a round.  Pick the
   // split that minimizes rounds x (k-tiles per item) plus the partials'
@@ -645,6 +653,8 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   hipError_t e;
   if (p.cfg == CFG_128x128)
     e = launch_prec<2, 2, 2, 2>(ka, p.bk, grid, s);
+  else if (p.cfg == CFG_256x128)
+    e = launch_prec<2, 2, 4, 2>(ka, 32, grid, s);
   else
     e = launch_prec<4, 1, 1, 2>(ka, p.bk, grid, s);
   if (e != hipSuccess || p.splits == 1) return e;
