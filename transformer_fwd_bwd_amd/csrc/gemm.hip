@@ -39,9 +39,12 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int KALIGN = 32;  // split-K chunks are multiples of this (and of every k-tile depth)
+constexpr int KALIGN = 64;  // split-K chunks are multiples of this (and of every k-tile depth)
 #ifndef GEMM_BIG_TILES
 #define GEMM_BIG_TILES 4096  // products with at least this many 256x128 tiles use them (vocabulary-sized)
+#endif
+#ifndef GEMM_PIPE
+#define GEMM_PIPE 1
 #endif
 #ifndef GEMM_GROUP_M
 #define GEMM_GROUP_M 8       // tile rows per raster group
@@ -473,21 +476,91 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
   // is fetched into registers; one barrier per k-tile.
   using SA = typename std::conditional<TRA, StageTr<BM, NT, BK>, Stage<BM, NT, A_RC, A_BF, BK>>::type;
   using SB = typename std::conditional<TRB, StageTr<BN, NT, BK>, Stage<BN, NT, !B_KC, B_BF, BK>>::type;
-  SA sa;
-  SB sb;
-  if (kb < ke) {
-    load_tile(sa, sb, kb);
-    store_tile(sa, sb, 0);
+  bool done = false;
+  if constexpr (GEMM_PIPE && BF16 && A_BF && B_BF && TM * TN <= 4 && BK == 64) {
+    // Interior tile free of the causal mask: a branch-free two-deep pipeline over
+    // its whole k-tiles.  Tile j waits in register set j % 2; at step t the loads
+    // of tile t + 2, the LDS stores of tile t + 1 and the MFMAs of tile t are
+    // interleaved in one basic block, one barrier per step.  A ragged last k-tile
+    // follows through the checked loader.
+    const int nt = (ke - kb) / BK;
+    if (interior && g.causal_a == CAUSAL_NONE && nt >= 1) {
+      done = true;
+      SA a0, a1;
+      SB b0, b1;
+      a0.load_fast(A, g.lda, m0, kb, tid);
+      b0.load_fast(B, g.ldb, n0, kb, tid);
+      if (nt > 1) {
+        a1.load_fast(A, g.lda, m0, kb + BK, tid);
+        b1.load_fast(B, g.ldb, n0, kb + BK, tid);
+      }
+      store_tile(a0, b0, 0);
+      __syncthreads();
+      auto hint = [&]() {
+        constexpr int NMF = TM * TN * (BK / 16);
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        }
+      };
+      int t = 0;
+      for (; t + 3 < nt; t += 2) {
+        a0.load_fast(A, g.lda, m0, kb + (t + 2) * BK, tid);
+        b0.load_fast(B, g.ldb, n0, kb + (t + 2) * BK, tid);
+        compute(0);
+        store_tile(a1, b1, 1);
+        hint();
+        __syncthreads();
+        a1.load_fast(A, g.lda, m0, kb + (t + 3) * BK, tid);
+        b1.load_fast(B, g.ldb, n0, kb + (t + 3) * BK, tid);
+        compute(1);
+        store_tile(a0, b0, 0);
+        hint();
+        __syncthreads();
+      }
+      for (; t < nt; ++t) {  // the last one to three tiles; t is even on entry
+        if ((t & 1) == 0) {
+          if (t + 2 < nt) {
+            a0.load_fast(A, g.lda, m0, kb + (t + 2) * BK, tid);
+            b0.load_fast(B, g.ldb, n0, kb + (t + 2) * BK, tid);
+          }
+          compute(0);
+          if (t + 1 < nt) store_tile(a1, b1, 1);
+        } else {
+          compute(1);
+          if (t + 1 < nt) store_tile(a0, b0, 0);
+        }
+        __syncthreads();
+      }
+      const int kt = kb + nt * BK;
+      if (kt < ke) {  // ragged last k-tile; every LDS buffer is free after the barrier above
+        load_tile(a0, b0, kt);
+        store_tile(a0, b0, 0);
+        __syncthreads();
+        compute(0);
+      }
+    }
   }
-  __syncthreads();
-  int buf = 0;
-  for (int k0 = kb; k0 < ke; k0 += BK) {
-    const bool more = k0 + BK < ke;
-    if (more) load_tile(sa, sb, k0 + BK);
-    compute(buf);
-    if (more) store_tile(sa, sb, buf ^ 1);
+  if (!done) {
+    SA sa;
+    SB sb;
+    if (kb < ke) {
+      load_tile(sa, sb, kb);
+      store_tile(sa, sb, 0);
+    }
     __syncthreads();
-    buf ^= 1;
+    int buf = 0;
+    for (int k0 = kb; k0 < ke; k0 += BK) {
+      const bool more = k0 + BK < ke;
+      if (more) load_tile(sa, sb, k0 + BK);
+      compute(buf);
+      if (more) store_tile(sa, sb, buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
   }
 
   // epilogue: register r of a 32x32 block holds C[8*(r/4) + 4*(lane/32) + r%4][lane%32]
