@@ -640,10 +640,9 @@ Plan make_plan(const GemmArgs& g) {
     p.cfg = CFG_128x128, p.BM = 128, p.BN = 128;
   }
   const int64_t tiles = (int64_t)((g.M + p.BM - 1) / p.BM) * ((g.N + p.BN - 1) / p.BN) * g.batch;
-  // Both operands bf16: 64-deep k-tiles (72 KB of LDS, two workgroups per CU)
-  // amortize the per-tile barrier best; a short K over many tiles does better
-  // with 32-deep ones (40 KB, three workgroups per CU hide more latency).
-  p.bk = (p.cfg == CFG_256x128 || (g.K <= 1024 && tiles >= 512)) ? 32 : 64;
+  // Both operands bf16: 64-deep k-tiles (72 KB of LDS, two workgroups per CU,
+  // the pipelined path); the 256x128 tiles fit two per CU only 32 deep.
+  p.bk = p.cfg == CFG_256x128 ? 32 : 64;
   // K split: the workgroups resident at once (slots) run in rounds, so a tile
   // count just past a multiple of the slots wastes most of a round.  Pick the
   // split that minimizes rounds x (k-tiles per item) plus the partials'
