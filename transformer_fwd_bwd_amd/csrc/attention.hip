@@ -40,6 +40,10 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 2^x by the hardware instruction; arguments here are <= 0 (or -inf), so the
+// only difference from exp2f is that results below 2^-126 flush to zero
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ unsigned short f2bf(float x) { return __builtin_bit_cast(unsigned short, (__bf16)x); }
 
 __device__ __forceinline__ bf16x8 as_bf(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -197,26 +201,36 @@ __global__ __launch_bounds__(NT) void attn_fwd_k(AttnArgs a) {
 #pragma unroll
         for (int s = 0; s < HS / 16; ++s) st[kt] = mfma(frag_r<HS>(Ks[buf], 32 * kt + l32, s, h), qf[s], st[kt]);
       }
+      // every key of the block visible to every query of the wave: no mask
+      const bool full = kv0 + KVB - 1 <= qw && kv0 + KVB <= a.T;
       float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * kt + acc_row(r, h);
-          const float v = (key <= q && key < a.T) ? st[kt][r] * sc : -INFINITY;
-          st[kt][r] = v;
-          mx = fmaxf(mx, v);
-        }
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
+        mx *= sc;
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + 32 * kt + acc_row(r, h);
+            const bool vis = key <= q && key < a.T;
+            st[kt][r] = vis ? st[kt][r] : -INFINITY;
+            mx = fmaxf(mx, vis ? st[kt][r] * sc : -INFINITY);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mn = fmaxf(m, mx);
       const float mref = mn == -INFINITY ? 0.f : mn;
-      const float alpha = exp2f(m - mref);
+      const float alpha = fexp2(m - mref);
       float sum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(st[kt][r] - mref);
+          const float p = fexp2(fmaf(st[kt][r], sc, -mref));  // -inf (masked) -> 0
           st[kt][r] = p;
           sum += p;
         }
@@ -333,13 +347,17 @@ __global__ __launch_bounds__(NT) void attn_dq_k(AttnArgs a) {
           dp[kt] = mfma(frag_r<HS>(Vs[buf], 32 * kt + l32, s, h), df[s], dp[kt]);
         }
       }
-      // dS^T = P^T (dP^T - D)
+      // dS^T = P^T (dP^T - D); a block every query of the wave sees whole needs no mask
+      const bool full = kv0 + KVB - 1 <= qw && kv0 + KVB <= a.T;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * kt + acc_row(r, h);
-          const float p = (key <= q && key < a.T) ? exp2f(st[kt][r] * sc - lse) : 0.f;
+          float p = fexp2(fmaf(st[kt][r], sc, -lse));
+          if (!full) {
+            const int key = kv0 + 32 * kt + acc_row(r, h);
+            p = (key <= q && key < a.T) ? p : 0.f;
+          }
           st[kt][r] = p * (dp[kt][r] - Dq);
         }
 #pragma unroll
@@ -377,7 +395,8 @@ template <int HS>
 __global__ __launch_bounds__(NT, 2) void attn_dkv_k(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned short Qs[2][KVB * (HS + 8)];
   __shared__ __attribute__((aligned(16))) unsigned short Ds[2][KVB * (HS + 8)];
-  __shared__ float Ls[2][KVB], Dd[2][KVB];
+  __shared__ __attribute__((aligned(16))) float Ls[2][KVB];
+  __shared__ __attribute__((aligned(16))) float Dd[2][KVB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const BlockId id = block_id((a.T + 127) / 128, false);
   if (id.bh >= a.B * a.H) return;
@@ -443,15 +462,28 @@ __global__ __launch_bounds__(NT, 2) void attn_dkv_k(AttnArgs a) {
           dp[qt] = mfma(frag_r<HS>(Ds[buf], 32 * qt + l32, s, h), vf[s], dp[qt]);
         }
       }
-      // P and dS with queries in registers, this lane's key in the column
+      // P and dS with queries in registers, this lane's key in the column; the
+      // saved statistics of 4 consecutive query rows come in one 16-byte read.
+      // A block whose every query sees every key of the wave needs no mask.
+      const bool full = qb >= kw + 31 && qb + KVB <= a.T && kw + 32 <= a.T;
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = 32 * qt + acc_row(r, h), qq = qb + qi;
-          const float p = (key <= qq && qq < a.T && key < a.T) ? exp2f(st[qt][r] * sc - Ls[buf][qi]) : 0.f;
-          st[qt][r] = p;
-          dp[qt][r] = p * (dp[qt][r] - Dd[buf][qi]);
+        for (int r4 = 0; r4 < 16; r4 += 4) {
+          const int qi0 = 32 * qt + acc_row(r4, h);
+          const f4 L4 = *reinterpret_cast<const f4*>(&Ls[buf][qi0]);
+          const f4 D4 = *reinterpret_cast<const f4*>(&Dd[buf][qi0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = r4 + e;
+            float p = fexp2(fmaf(st[qt][r], sc, -L4[e]));
+            if (!full) {
+              const int qq = qb + qi0 + e;
+              p = (key <= qq && qq < a.T && key < a.T) ? p : 0.f;
+            }
+            st[qt][r] = p;
+            dp[qt][r] = p * (dp[qt][r] - D4[e]);
+          }
         }
 #pragma unroll
       for (int s = 0; s < KVB / 16; ++s) {
