@@ -153,7 +153,7 @@ struct AttnArgs {
 
 // ------------------------------------------------------------------------------------ forward
 template <int HS>
-__global__ __launch_bounds__(NT) void attn_fwd_k(AttnArgs a) {
+__global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned short Ks[2][KVB * (HS + 8)];
   __shared__ __attribute__((aligned(16))) unsigned short Vs[2][KVB * (HS + 8)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(NT) void attn_d_k(AttnArgs a) {
 
 // dQ for a block of 128 queries (4 waves x 32), looping over key blocks
 template <int HS>
-__global__ __launch_bounds__(NT) void attn_dq_k(AttnArgs a) {
+__global__ __launch_bounds__(NT, 2) void attn_dq_k(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned short Ks[2][KVB * (HS + 8)];
   __shared__ __attribute__((aligned(16))) unsigned short Vs[2][KVB * (HS + 8)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
