@@ -77,8 +77,10 @@ struct RowStage {
       const int c = tid + i * NT;
       if (CHUNKS % NT != 0 && c >= CHUNKS) break;
       const int row = c / CPR, col = (c % CPR) * 8;
-      v[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (row0 + row < valid) v[i] = *reinterpret_cast<const u16x8*>(src + (int64_t)(row0 + row) * ld + col);
+      // branch-free: read a row clamped into range (valid >= 1), then zero it if it was past the end
+      const int rr = min(row0 + row, valid - 1);
+      const u16x8 t = *reinterpret_cast<const u16x8*>(src + (int64_t)rr * ld + col);
+      v[i] = row0 + row < valid ? t : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
   __device__ __forceinline__ void store(unsigned short* dst, int tid) const {
@@ -110,16 +112,19 @@ __device__ __forceinline__ bf16x8 frag_tr(const unsigned short* X, int d0, int s
 
 // Work assignment.  The grid is 1-D over nx blocks x (B*H rounded up to 8).
 // Workgroup w runs on XCD w % 8, and causal work grows (forward, dQ) or shrinks
-// (dK/dV) with the block index, so consecutive ids on one XCD walk the block
-// indices of a fixed set of heads: every XCD gets the same mix, largest first.
+// (dK/dV) with the block index, so each XCD takes a fixed eighth of the heads
+// and walks them block-index-major, largest blocks first: every XCD gets the
+// same mix, and the short blocks fill in behind the long ones.
 struct BlockId {
   int x, bh;
 };
 __device__ __forceinline__ BlockId block_id(int nx, bool large_x_first) {
-  const int L = blockIdx.x, xi = (L >> 3) % nx;
+  const int L = blockIdx.x, local = L >> 3;
+  const int heads_per_xcd = (int)(gridDim.x >> 3) / nx;
+  const int rank = local / heads_per_xcd;
   BlockId r;
-  r.bh = (L & 7) + 8 * (L / (8 * nx));
-  r.x = large_x_first ? nx - 1 - xi : xi;
+  r.bh = (L & 7) + 8 * (local % heads_per_xcd);
+  r.x = large_x_first ? nx - 1 - rank : rank;
   return r;
 }
 
@@ -156,7 +161,8 @@ template <int HS>
 __global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned short Ks[2][KVB * (HS + 8)];
   __shared__ __attribute__((aligned(16))) unsigned short Vs[2][KVB * (HS + 8)];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform by construction
   const BlockId id = block_id((a.T + 127) / 128, true);
   if (id.bh >= a.B * a.H) return;
   const int bh = id.bh, b = bh / a.H, hd = bh % a.H;
@@ -294,7 +300,8 @@ template <int HS>
 __global__ __launch_bounds__(NT, 2) void attn_dq_k(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned short Ks[2][KVB * (HS + 8)];
   __shared__ __attribute__((aligned(16))) unsigned short Vs[2][KVB * (HS + 8)];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform by construction
   const BlockId id = block_id((a.T + 127) / 128, true);
   if (id.bh >= a.B * a.H) return;
   const int bh = id.bh, b = bh / a.H, hd = bh % a.H;
@@ -397,7 +404,8 @@ __global__ __launch_bounds__(NT, 2) void attn_dkv_k(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned short Ds[2][KVB * (HS + 8)];
   __shared__ __attribute__((aligned(16))) float Ls[2][KVB];
   __shared__ __attribute__((aligned(16))) float Dd[2][KVB];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform by construction
   const BlockId id = block_id((a.T + 127) / 128, false);
   if (id.bh >= a.B * a.H) return;
   const int bh = id.bh, b = bh / a.H, hd = bh % a.H;
