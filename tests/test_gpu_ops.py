@@ -260,6 +260,33 @@ def test_errors_are_reported_and_context_survives(ctx):
     b.release()
 
 
+def test_add_of_single_use_outputs_and_repeated_backward(ctx):
+    """[Autograd-1, "Backward pass"]: an op output read only by an Add gets exactly the
+    Add's output gradient (the library lets it use that buffer), leaf gradients add up
+    over repeated backward passes, and intermediate gradients are per pass."""
+    xv, zv, rv = rnd(41, (6, 40)), rnd(42, (6, 40)), rnd(43, (6, 40))
+    x = ctx.tensor(xv.shape, xv)
+    z = ctx.tensor(zv.shape, zv)
+    R = ctx.tensor(rv.shape, rv)
+    p, q = T.tanh(x), T.gelu(z)                  # each read once, by the Add
+    s_ = T.add(p, q)
+    loss = T.sum_all(T.mul(s_, R))
+    ctx.backward(loss)
+    ctx.backward(loss)                           # a second pass over the same tape
+    X, Z = E.Tensor(xv.astype(np.float64)), E.Tensor(zv.astype(np.float64))
+    P, Q = E.tanh(X), E.gelu(Z)
+    L = E.sum_all(E.mul(E.add(P, Q), E.Tensor(rv.astype(np.float64))))
+    L.backward()
+    assert_close(p.grad(), rv, 1e-6, "p.grad")
+    assert_close(q.grad(), rv, 1e-6, "q.grad")
+    assert_close(s_.grad(), rv, 1e-6, "s.grad")
+    assert_close(x.grad(), 2 * X.grad, 1e-5, "x.grad after two passes")
+    assert_close(z.grad(), 2 * Z.grad, 1e-5, "z.grad after two passes")
+    ctx.tape_reset()
+    for t in (x, z, R):
+        t.release()
+
+
 def test_no_grad_records_nothing(ctx):
     a = ctx.tensor((2, 3), rnd(40, (2, 3)))
     ctx.set_grad_enabled(False)

@@ -278,23 +278,6 @@ __global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------ backward
-// D[bh, q] = sum_d dy[b, q, h*hs + d] * y[b, q, h*hs + d]
-template <int HS>
-__global__ __launch_bounds__(NT) void attn_d_k(AttnArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6);  // (b, q)
-  const int lane = threadIdx.x & 63;
-  if (row >= (int64_t)a.B * a.T) return;
-  const int b = (int)(row / a.T), q = (int)(row % a.T);
-  const float* g = a.dyf + row * a.C;
-  const float* y = a.y + row * a.C;
-  for (int hd = 0; hd < a.H; ++hd) {
-    float s = 0.f;
-    for (int d = lane; d < HS; d += 64) s += g[hd * HS + d] * y[hd * HS + d];
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (lane == 0) a.D[((int64_t)b * a.H + hd) * a.T + q] = s;
-  }
-}
-
 // dQ for a block of 128 queries (4 waves x 32), looping over key blocks
 template <int HS>
 __global__ __launch_bounds__(NT, 2) void attn_dq_k(AttnArgs a) {
@@ -319,7 +302,20 @@ __global__ __launch_bounds__(NT, 2) void attn_dq_k(AttnArgs a) {
     df[s] = frag_g(dyg, a.C, q, a.T, s, h);
   }
   const float lse = q < a.T ? a.lse[(int64_t)bh * a.T + q] : 0.f;
-  const float Dq = q < a.T ? a.D[(int64_t)bh * a.T + q] : 0.f;
+  // D = rowsum(dO * O) of this query (fp32 inputs): each lane half sums half the head's
+  // columns, one exchange adds the halves; it is stored for the dK/dV kernel that follows
+  float Dq = 0.f;
+  if (q < a.T) {
+    const int64_t off = ((int64_t)b * a.T + q) * a.C + hd * HS + h * (HS / 2);
+    const f4* g4 = reinterpret_cast<const f4*>(a.dyf + off);
+    const f4* y4 = reinterpret_cast<const f4*>(a.y + off);
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < HS / 8; ++j) acc += g4[j] * y4[j];
+    Dq = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
+  Dq += __shfl_xor(Dq, 32, 64);
+  if (h == 0 && q < a.T) a.D[(int64_t)bh * a.T + q] = Dq;
   const float sc = a.scale * LOG2E;
 
   f32x16 dq[HS / 32];
@@ -565,14 +561,11 @@ hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float*
   a.outbf = dqkv_bf;
   a.B = B, a.T = T, a.H = H, a.C = C, a.scale = scale, a.beta = beta;
   const int hs = C / H;
-  dim3 gd((unsigned)(((int64_t)B * T + 3) / 4));
   dim3 grid(attn_grid(T, B * H));
   if (hs == 64) {
-    hipLaunchKernelGGL(attn_d_k<64>, gd, dim3(NT), 0, s, a);
     hipLaunchKernelGGL(attn_dq_k<64>, grid, dim3(NT), 0, s, a);
     hipLaunchKernelGGL(attn_dkv_k<64>, grid, dim3(NT), 0, s, a);
   } else if (hs == 32) {
-    hipLaunchKernelGGL(attn_d_k<32>, gd, dim3(NT), 0, s, a);
     hipLaunchKernelGGL(attn_dq_k<32>, grid, dim3(NT), 0, s, a);
     hipLaunchKernelGGL(attn_dkv_k<32>, grid, dim3(NT), 0, s, a);
   } else {

@@ -350,7 +350,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
 
   const GemmArgs& g = ka.g;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform by construction
   const int wm = wave / WN, wn = wave % WN;
 
   // Work item order.  The grid is 1-D over (batch x split) slabs of tiles_m x

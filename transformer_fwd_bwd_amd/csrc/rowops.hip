@@ -144,44 +144,6 @@ __global__ __launch_bounds__(NT) void ln_fwd4_k(const f4* __restrict__ x, const 
   }
 }
 
-template <int J>
-__global__ __launch_bounds__(NT) void ln_bwd_dx4_k(const f4* __restrict__ g, const f4* __restrict__ x,
-                                                   const f4* __restrict__ gamma, const float* __restrict__ mean,
-                                                   const float* __restrict__ rstd, f4* __restrict__ dx, int64_t rows,
-                                                   int C4, float beta_dx) {
-  const int lane = threadIdx.x & 63;
-  const int64_t nw = (int64_t)gridDim.x * WAVES;
-  const float invC = 1.f / (4 * C4);
-  for (int64_t r = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); r < rows; r += nw) {
-    const float mu = mean[r], rs = rstd[r];
-    f4 xh[J], dg[J];
-    float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int c = lane + 64 * j;
-      if (c < C4) {
-        xh[j] = (x[r * C4 + c] - mu) * rs;
-        dg[j] = g[r * C4 + c] * gamma[c];
-      } else {
-        xh[j] = dg[j] = f4{0.f, 0.f, 0.f, 0.f};
-      }
-      s1 += (dg[j][0] + dg[j][1]) + (dg[j][2] + dg[j][3]);
-      const f4 t = dg[j] * xh[j];
-      s2 += (t[0] + t[1]) + (t[2] + t[3]);
-    }
-    const float m1 = wave_sum(s1) * invC, m2 = wave_sum(s2) * invC;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int c = lane + 64 * j;
-      if (c < C4) {
-        f4 v = rs * (dg[j] - m1 - xh[j] * m2);
-        if (beta_dx != 0.f) v += dx[r * C4 + c];
-        dx[r * C4 + c] = v;
-      }
-    }
-  }
-}
-
 // dx per row (one wavefront per row, many rows in flight)
 template <bool CACHED>
 __global__ __launch_bounds__(NT) void ln_bwd_dx_k(const float* __restrict__ g, const float* __restrict__ x,
@@ -236,6 +198,80 @@ __global__ __launch_bounds__(NT) void ln_bwd_dx_k(const float* __restrict__ g, c
 }
 
 // partial column sums over a slab of rows: part[p][0][c] = sum g*xhat, part[p][1][c] = sum g
+// LayerNorm backward over float4 rows, one wavefront per row (the row held in
+// registers): dx = rstd (g*gamma - mean(g*gamma) - xhat mean(g*gamma*xhat)),
+// plus the dgamma / dbeta column partials of the rows this workgroup handles: each lane keeps sum g*xhat and sum g for its float4
+// columns over its wave's rows, the 4 waves are added in LDS in a fixed order,
+// and part[block][0 | 1][C] receives the result (reduced by ln_bwd_reduce).
+template <int J>
+__global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, const f4* __restrict__ x,
+                                                      const f4* __restrict__ gamma, const float* __restrict__ mean,
+                                                      const float* __restrict__ rstd, f4* __restrict__ dx,
+                                                      f4* __restrict__ part, int64_t rows, int C4, float beta_dx) {
+  __shared__ f4 sh[WAVES - 1][2][64 * J];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t nw = (int64_t)gridDim.x * WAVES;
+  const float invC = 1.f / (4 * C4);
+  f4 pa[J], pb[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) pa[j] = pb[j] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t r = (int64_t)blockIdx.x * WAVES + w; r < rows; r += nw) {
+    const float mu = mean[r], rs = rstd[r];
+    f4 xh[J], gv[J], dg[J];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = lane + 64 * j;
+      if (c < C4) {
+        xh[j] = (x[r * C4 + c] - mu) * rs;
+        gv[j] = g[r * C4 + c];
+        dg[j] = gv[j] * gamma[c];
+      } else {
+        xh[j] = gv[j] = dg[j] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+      pa[j] += gv[j] * xh[j];
+      pb[j] += gv[j];
+      s1 += (dg[j][0] + dg[j][1]) + (dg[j][2] + dg[j][3]);
+      const f4 t = dg[j] * xh[j];
+      s2 += (t[0] + t[1]) + (t[2] + t[3]);
+    }
+    const float m1 = wave_sum(s1) * invC, m2 = wave_sum(s2) * invC;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = lane + 64 * j;
+      if (c < C4) {
+        f4 v = rs * (dg[j] - m1 - xh[j] * m2);
+        if (beta_dx != 0.f) v += dx[r * C4 + c];
+        dx[r * C4 + c] = v;
+      }
+    }
+  }
+  if (w > 0) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      sh[w - 1][0][lane + 64 * j] = pa[j];
+      sh[w - 1][1][lane + 64 * j] = pb[j];
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = lane + 64 * j;
+      if (c < C4) {
+        f4 a = pa[j], b = pb[j];
+#pragma unroll
+        for (int i = 0; i < WAVES - 1; ++i) {
+          a += sh[i][0][c];
+          b += sh[i][1][c];
+        }
+        part[((int64_t)blockIdx.x * 2) * C4 + c] = a;
+        part[((int64_t)blockIdx.x * 2 + 1) * C4 + c] = b;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(NT) void ln_bwd_cols_k(const float* __restrict__ g, const float* __restrict__ x,
                                                     const float* __restrict__ mean, const float* __restrict__ rstd,
                                                     float* __restrict__ part, int64_t rows, int C, int64_t rows_per) {
@@ -301,6 +337,10 @@ __global__ __launch_bounds__(1024) void ln_bwd_reduce(const float* __restrict__ 
 int ln_bwd_parts(int64_t rows) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(128, (rows + 31) / 32));
 }
+
+// workgroups of the fused LayerNorm backward: at most 512, so each of its waves
+// takes several rows and the column partials stay small
+int64_t ln_fused_blocks(int64_t rows) { return std::max<int64_t>(1, std::min<int64_t>(512, (rows + WAVES - 1) / WAVES)); }
 
 // ------------------------------------------------------------ causal softmax
 template <bool CACHED>
@@ -616,34 +656,41 @@ hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, 
 }
 
 size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C) {
-  return (size_t)ln_bwd_parts(rows) * 2 * C * sizeof(float);
+  return (size_t)std::max<int64_t>(ln_bwd_parts(rows), ln_fused_blocks(rows)) * 2 * C * sizeof(float);
 }
 
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
                          float* dx, float* dgamma, float* dbeta, int64_t rows, int64_t C, float beta_dx,
                          float beta_dg, float beta_db, void* ws, hipStream_t s) {
   if (C <= 0) return hipSuccess;
-  if (rows > 0) {
-    if (C % 4 == 0 && C <= 1024 && aligned16(g) && aligned16(x) && aligned16(gamma) && aligned16(dx)) {
-      const int C4 = (int)(C / 4);
-      if (C4 <= 64)
-        hipLaunchKernelGGL(ln_bwd_dx4_k<1>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
-                           (const f4*)gamma, mean, rstd, (f4*)dx, rows, C4, beta_dx);
-      else
-        hipLaunchKernelGGL(ln_bwd_dx4_k<4>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
-                           (const f4*)gamma, mean, rstd, (f4*)dx, rows, C4, beta_dx);
-    } else if (C <= 64 * MAXV)
-      hipLaunchKernelGGL(ln_bwd_dx_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
-                         rows, (int)C, beta_dx);
-    else
-      hipLaunchKernelGGL(ln_bwd_dx_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
-                         rows, (int)C, beta_dx);
-  }
-  const int parts = ln_bwd_parts(rows);
-  const int64_t rows_per = (rows + parts - 1) / parts;
   float* part = static_cast<float*>(ws);
-  hipLaunchKernelGGL(ln_bwd_cols_k, dim3((unsigned)((C + NT - 1) / NT), (unsigned)parts), dim3(NT), 0, s, g, x,
-                     mean, rstd, part, rows, (int)C, rows_per);
+  int parts = 0;
+  if (rows > 0 && C % 4 == 0 && C <= 1024 && aligned16(g) && aligned16(x) && aligned16(gamma) && aligned16(dx) &&
+      aligned16(part)) {
+    // dx and the column partials in one pass over g and x
+    const int C4 = (int)(C / 4);
+    const int64_t blocks = ln_fused_blocks(rows);
+    if (C4 <= 64)
+      hipLaunchKernelGGL(ln_bwd_fused4_k<1>, dim3((unsigned)blocks), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
+                         (const f4*)gamma, mean, rstd, (f4*)dx, (f4*)part, rows, C4, beta_dx);
+    else
+      hipLaunchKernelGGL(ln_bwd_fused4_k<4>, dim3((unsigned)blocks), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
+                         (const f4*)gamma, mean, rstd, (f4*)dx, (f4*)part, rows, C4, beta_dx);
+    parts = (int)blocks;
+  } else {
+    if (rows > 0) {
+      if (C <= 64 * MAXV)
+        hipLaunchKernelGGL(ln_bwd_dx_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
+                           rows, (int)C, beta_dx);
+      else
+        hipLaunchKernelGGL(ln_bwd_dx_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
+                           rows, (int)C, beta_dx);
+    }
+    parts = ln_bwd_parts(rows);
+    const int64_t rows_per = (rows + parts - 1) / parts;
+    hipLaunchKernelGGL(ln_bwd_cols_k, dim3((unsigned)((C + NT - 1) / NT), (unsigned)parts), dim3(NT), 0, s, g, x,
+                       mean, rstd, part, rows, (int)C, rows_per);
+  }
   hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + 63) / 64)), dim3(1024), 0, s, part, parts, (int)C, dgamma,
                      dbeta, beta_dg, beta_db);
   return hipGetLastError();

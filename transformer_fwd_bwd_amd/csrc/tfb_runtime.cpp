@@ -65,6 +65,7 @@ struct TensorRec {
   bool gbf_valid = false;
 
   int64_t ld = 0;  // row stride of the last dim when rows are padded (0: dense)
+  int uses = 0;    // ops on the tape that read this tensor
 
   int64_t cols() const { return ndim ? shape[ndim - 1] : 1; }
   int64_t rows() const { return cols() ? numel / cols() : 0; }
@@ -316,7 +317,23 @@ struct Ctx {
   }
 
   void record(const Rec& r) {
-    if (c->grad_enabled) c->tape.push_back(r);
+    if (!c->grad_enabled) return;
+    c->tape.push_back(r);
+    for (int h : r.in)
+      if (h >= 0) c->tensors[h].uses += 1;
+  }
+
+  // An op output read by exactly one op (this one, during its backward) whose
+  // gradient is a plain copy of `out`'s finished gradient can use out's
+  // gradient buffer itself: no later contribution can reach it.
+  bool share_grad(TensorRec& x, const TensorRec& out) {
+    if (x.leaf || x.is_param || x.uses != 1 || x.grad || x.gstate != G_NONE) return false;
+    if (x.padded() || out.padded() || x.numel != out.numel || !out.grad) return false;
+    x.grad = out.grad;
+    x.gstate = G_VALID;
+    x.gbf = out.gbf_valid ? out.gbf : nullptr;
+    x.gbf_valid = out.gbf_valid;
+    return true;
   }
 
   GemmArgs gemm_base() const {
@@ -457,8 +474,11 @@ void backward_rec(Ctx& C, const Rec& r) {
     case OP_ADD: {
       TensorRec& a = C.T(r.in[0]);
       TensorRec& b = C.T(r.in[1]);
-      auto da = C.gdst(r.in[0]);
-      hip_check(axpby(da.first, g, 1.f, da.second, a.numel, s), "add bwd");
+      if (r.in[0] == r.in[1] || !C.share_grad(a, out)) {
+        auto da = C.gdst(r.in[0]);
+        hip_check(axpby(da.first, g, 1.f, da.second, a.numel, s), "add bwd");
+      }
+      if (b.numel == out.numel && r.in[0] != r.in[1] && C.share_grad(b, out)) break;
       auto db = C.gdst(r.in[1]);
       const int64_t rows = b.numel ? a.numel / b.numel : 0;
       size_t mark = C.c->arena.hi;
