@@ -86,9 +86,10 @@ hipError_t permute_heads(const float* x, float* y, int64_t B, int64_t T, int64_t
 hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, float* y, uint16_t* ybf, float* mean,
                          float* rstd, int64_t rows, int64_t C, float eps, hipStream_t s);
 size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C);
+// dxbf (optional) receives the bf16 copy of the final dx
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
-                         float* dx, float* dgamma, float* dbeta, int64_t rows, int64_t C, float beta_dx,
-                         float beta_dg, float beta_db, void* ws, hipStream_t s);
+                         float* dx, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows, int64_t C,
+                         float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s);
 // full == true: every element of the [rows, T] view is written (zeros where masked);
 // full == false: only the visible prefix of each row is touched.
 hipError_t causal_softmax_fwd(const float* x, float* p, int64_t rows, int64_t T, bool full, hipStream_t s);

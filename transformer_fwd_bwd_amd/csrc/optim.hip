@@ -9,6 +9,8 @@
 namespace tfb {
 namespace {
 
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
 constexpr int NT = 256;
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -27,7 +29,8 @@ __global__ __launch_bounds__(NT) void adamw_k(const AdamSeg* __restrict__ segs, 
   const AdamSeg sg = segs[ch.seg];
   const int64_t end = std::min(sg.n, ch.off + chunk_elems);
   const bool v4 = ((reinterpret_cast<uintptr_t>(sg.p) | reinterpret_cast<uintptr_t>(sg.g) |
-                    reinterpret_cast<uintptr_t>(sg.m) | reinterpret_cast<uintptr_t>(sg.v)) & 15) == 0;
+                    reinterpret_cast<uintptr_t>(sg.m) | reinterpret_cast<uintptr_t>(sg.v)) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(sg.pbf) & 7) == 0;
   int64_t i = ch.off;
   if (v4) {
     const int64_t end4 = ch.off + ((end - ch.off) / 4) * 4;
@@ -48,8 +51,10 @@ __global__ __launch_bounds__(NT) void adamw_k(const AdamSeg* __restrict__ segs, 
       *reinterpret_cast<f4*>(sg.m + q) = m;
       *reinterpret_cast<f4*>(sg.v + q) = v;
       if (sg.pbf) {
+        u16x4 b;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sg.pbf[q + e] = __builtin_bit_cast(uint16_t, (__bf16)p[e]);
+        for (int e = 0; e < 4; ++e) b[e] = __builtin_bit_cast(uint16_t, (__bf16)p[e]);
+        *reinterpret_cast<u16x4*>(sg.pbf + q) = b;
       }
     }
     i = end4;

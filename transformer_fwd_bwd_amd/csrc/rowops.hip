@@ -200,14 +200,17 @@ __global__ __launch_bounds__(NT) void ln_bwd_dx_k(const float* __restrict__ g, c
 // partial column sums over a slab of rows: part[p][0][c] = sum g*xhat, part[p][1][c] = sum g
 // LayerNorm backward over float4 rows, one wavefront per row (the row held in
 // registers): dx = rstd (g*gamma - mean(g*gamma) - xhat mean(g*gamma*xhat)),
-// plus the dgamma / dbeta column partials of the rows this workgroup handles: each lane keeps sum g*xhat and sum g for its float4
-// columns over its wave's rows, the 4 waves are added in LDS in a fixed order,
-// and part[block][0 | 1][C] receives the result (reduced by ln_bwd_reduce).
+// plus the dgamma / dbeta column partials of the rows this workgroup handles:
+// each lane keeps sum g*xhat and sum g for its float4 columns over its wave's
+// rows, the 4 waves are added in LDS in a fixed order, and part[block][0 | 1][C]
+// receives the result (reduced by ln_bwd_reduce).  A wave loads its rows two at
+// a time, so two rows' reads are in flight.
 template <int J>
 __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, const f4* __restrict__ x,
                                                       const f4* __restrict__ gamma, const float* __restrict__ mean,
                                                       const float* __restrict__ rstd, f4* __restrict__ dx,
-                                                      f4* __restrict__ part, int64_t rows, int C4, float beta_dx) {
+                                                      u16x4* __restrict__ dxbf, f4* __restrict__ part, int64_t rows,
+                                                      int C4, float beta_dx) {
   __shared__ f4 sh[WAVES - 1][2][64 * J];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t nw = (int64_t)gridDim.x * WAVES;
@@ -215,34 +218,46 @@ __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, 
   f4 pa[J], pb[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) pa[j] = pb[j] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t r = (int64_t)blockIdx.x * WAVES + w; r < rows; r += nw) {
-    const float mu = mean[r], rs = rstd[r];
-    f4 xh[J], gv[J], dg[J];
-    float s1 = 0.f, s2 = 0.f;
+  for (int64_t r0 = (int64_t)blockIdx.x * WAVES + w; r0 < rows; r0 += 2 * nw) {
+    const int64_t rr[2] = {r0, r0 + nw};
+    f4 xv[2][J], gv[2][J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int c = lane + 64 * j;
-      if (c < C4) {
-        xh[j] = (x[r * C4 + c] - mu) * rs;
-        gv[j] = g[r * C4 + c];
-        dg[j] = gv[j] * gamma[c];
-      } else {
-        xh[j] = gv[j] = dg[j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int c = lane + 64 * j;
+        const bool ok = c < C4 && rr[u] < rows;
+        xv[u][j] = ok ? x[rr[u] * C4 + c] : f4{0.f, 0.f, 0.f, 0.f};
+        gv[u][j] = ok ? g[rr[u] * C4 + c] : f4{0.f, 0.f, 0.f, 0.f};
       }
-      pa[j] += gv[j] * xh[j];
-      pb[j] += gv[j];
-      s1 += (dg[j][0] + dg[j][1]) + (dg[j][2] + dg[j][3]);
-      const f4 t = dg[j] * xh[j];
-      s2 += (t[0] + t[1]) + (t[2] + t[3]);
-    }
-    const float m1 = wave_sum(s1) * invC, m2 = wave_sum(s2) * invC;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int c = lane + 64 * j;
-      if (c < C4) {
-        f4 v = rs * (dg[j] - m1 - xh[j] * m2);
-        if (beta_dx != 0.f) v += dx[r * C4 + c];
-        dx[r * C4 + c] = v;
+    for (int u = 0; u < 2; ++u) {
+      const int64_t r = rr[u];
+      if (r >= rows) break;
+      const float mu = mean[r], rs = rstd[r];
+      f4 xh[J], dg[J];
+      float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int c = lane + 64 * j;
+        xh[j] = c < C4 ? (xv[u][j] - mu) * rs : f4{0.f, 0.f, 0.f, 0.f};
+        dg[j] = c < C4 ? gv[u][j] * gamma[c] : f4{0.f, 0.f, 0.f, 0.f};
+        pa[j] += gv[u][j] * xh[j];
+        pb[j] += gv[u][j];
+        s1 += (dg[j][0] + dg[j][1]) + (dg[j][2] + dg[j][3]);
+        const f4 t = dg[j] * xh[j];
+        s2 += (t[0] + t[1]) + (t[2] + t[3]);
+      }
+      const float m1 = wave_sum(s1) * invC, m2 = wave_sum(s2) * invC;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int c = lane + 64 * j;
+        if (c < C4) {
+          f4 v = rs * (dg[j] - m1 - xh[j] * m2);
+          if (beta_dx != 0.f) v += dx[r * C4 + c];
+          dx[r * C4 + c] = v;
+          if (dxbf) dxbf[r * C4 + c] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
+        }
       }
     }
   }
@@ -307,12 +322,13 @@ __global__ __launch_bounds__(NT) void ln_bwd_cols_k(const float* __restrict__ g,
 __global__ __launch_bounds__(1024) void ln_bwd_reduce(const float* __restrict__ part, int nparts, int C,
                                                       float* __restrict__ dgamma, float* __restrict__ dbeta,
                                                       float beta_dg, float beta_db) {
-  __shared__ float sa[16][65], sb[16][65];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + tx;
+  // 16 columns x 64 partial groups per workgroup; the groups are added in a fixed order
+  __shared__ float sa[64][17], sb[64][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int c = blockIdx.x * 16 + tx;
   float a = 0.f, b = 0.f;
   if (c < C) {
-    for (int p = ty; p < nparts; p += 16) {
+    for (int p = ty; p < nparts; p += 64) {
       a += part[((int64_t)p * 2) * C + c];
       b += part[((int64_t)p * 2 + 1) * C + c];
     }
@@ -322,8 +338,7 @@ __global__ __launch_bounds__(1024) void ln_bwd_reduce(const float* __restrict__ 
   __syncthreads();
   if (ty == 0 && c < C) {
     float ra = 0.f, rb = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 64; ++i) {
       ra += sa[i][tx];
       rb += sb[i][tx];
     }
@@ -338,8 +353,8 @@ int ln_bwd_parts(int64_t rows) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(128, (rows + 31) / 32));
 }
 
-// workgroups of the fused LayerNorm backward: at most 512, so each of its waves
-// takes several rows and the column partials stay small
+// workgroups of the fused LayerNorm backward: at most 512 (two per CU), each
+// wave taking two rows per step; the column partials stay a few MB
 int64_t ln_fused_blocks(int64_t rows) { return std::max<int64_t>(1, std::min<int64_t>(512, (rows + WAVES - 1) / WAVES)); }
 
 // ------------------------------------------------------------ causal softmax
@@ -660,22 +675,22 @@ size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C) {
 }
 
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
-                         float* dx, float* dgamma, float* dbeta, int64_t rows, int64_t C, float beta_dx,
+                         float* dx, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows, int64_t C, float beta_dx,
                          float beta_dg, float beta_db, void* ws, hipStream_t s) {
   if (C <= 0) return hipSuccess;
   float* part = static_cast<float*>(ws);
   int parts = 0;
   if (rows > 0 && C % 4 == 0 && C <= 1024 && aligned16(g) && aligned16(x) && aligned16(gamma) && aligned16(dx) &&
-      aligned16(part)) {
-    // dx and the column partials in one pass over g and x
+      aligned16(part) && (reinterpret_cast<uintptr_t>(dxbf) & 7) == 0) {
+    // dx (and its bf16 copy) and the column partials in one pass over g and x
     const int C4 = (int)(C / 4);
     const int64_t blocks = ln_fused_blocks(rows);
     if (C4 <= 64)
       hipLaunchKernelGGL(ln_bwd_fused4_k<1>, dim3((unsigned)blocks), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
-                         (const f4*)gamma, mean, rstd, (f4*)dx, (f4*)part, rows, C4, beta_dx);
+                         (const f4*)gamma, mean, rstd, (f4*)dx, (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
     else
       hipLaunchKernelGGL(ln_bwd_fused4_k<4>, dim3((unsigned)blocks), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
-                         (const f4*)gamma, mean, rstd, (f4*)dx, (f4*)part, rows, C4, beta_dx);
+                         (const f4*)gamma, mean, rstd, (f4*)dx, (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
     parts = (int)blocks;
   } else {
     if (rows > 0) {
@@ -690,8 +705,12 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
     const int64_t rows_per = (rows + parts - 1) / parts;
     hipLaunchKernelGGL(ln_bwd_cols_k, dim3((unsigned)((C + NT - 1) / NT), (unsigned)parts), dim3(NT), 0, s, g, x,
                        mean, rstd, part, rows, (int)C, rows_per);
+    if (dxbf) {
+      const hipError_t e = to_bf16(dx, dxbf, rows * C, s);
+      if (e != hipSuccess) return e;
+    }
   }
-  hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + 63) / 64)), dim3(1024), 0, s, part, parts, (int)C, dgamma,
+  hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + 15) / 16)), dim3(1024), 0, s, part, parts, (int)C, dgamma,
                      dbeta, beta_dg, beta_db);
   return hipGetLastError();
 }

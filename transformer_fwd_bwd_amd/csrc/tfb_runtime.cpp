@@ -563,12 +563,16 @@ void backward_rec(Ctx& C, const Rec& r) {
       auto dx = C.gdst(r.in[0]);
       auto dg = C.gdst(r.in[1]);
       auto db = C.gdst(r.in[2]);
+      // the bf16 copy of dx serves the contractions when this is the gradient's last
+      // contribution (a later one invalidates it); a residual-stream gradient is one
+      uint16_t* dxb = x.leaf ? nullptr : C.twin_grad(x);
       size_t mark = C.c->arena.hi;
       void* ws = C.scratch(layernorm_bwd_workspace_bytes(rows, Cc));
       hip_check(layernorm_bwd(g, x.data, gm.data, static_cast<float*>(r.s0), static_cast<float*>(r.s1), dx.first,
-                              dg.first, db.first, rows, Cc, dx.second, dg.second, db.second, ws, s),
+                              dxb, dg.first, db.first, rows, Cc, dx.second, dg.second, db.second, ws, s),
                 "layernorm bwd");
       C.c->arena.hi = mark;
+      if (dxb) x.gbf_valid = true;
       break;
     }
     case OP_EMBEDDING: {
