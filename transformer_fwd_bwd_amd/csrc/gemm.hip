@@ -451,7 +451,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
       }
     } else {
 #pragma unroll
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
           for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][c], bf[j][c], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bf[j][c], af[i][c], acc[i][j], 0, 0, 0);
       }
     }
   };
@@ -563,7 +563,10 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
     }
   }
 
-  // epilogue: register r of a 32x32 block holds C[8*(r/4) + 4*(lane/32) + r%4][lane%32]
+  // Epilogue.  The MFMAs take B's fragment as their first operand, so each
+  // 32x32 block accumulates C^T: register r holds C[lane%32][8*(r/4) + 4*(lane/32) + r%4],
+  // and registers 4q .. 4q+3 are four consecutive columns of one row -- one
+  // 16-byte store (and 16-byte bias / beta reads) where the row pitch allows.
   const bool to_ws = ka.splits > 1;
   float* C;
   int64_t ldc;
@@ -574,25 +577,34 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
     C = g.C + z1 * g.sc1 + z2 * g.sc2;
     ldc = g.ldc;
   }
+  const float* bias = to_ws ? nullptr : g.bias;
+  const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(bias) & 15) == 0);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * TM * 32 + i * 32 + lrow;
+    if (m >= g.M) continue;
+    float* row = C + (int64_t)m * ldc;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * TN * 32 + j * 32 + lrow;
-      if (n >= g.N) continue;
-      const float bias = (!to_ws && g.bias) ? g.bias[n] : 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * TM * 32 + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-        if (m >= g.M) continue;
-        float* dst = C + (int64_t)m * ldc + n;
-        float v = g.alpha * acc[i][j][r];
-        if (to_ws) {
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * TN * 32 + j * 32 + 8 * q + 4 * lhalf;
+        f4 v = f4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]} * g.alpha;
+        if (vec && n + 3 < g.N) {
+          if (bias) v += *reinterpret_cast<const f4*>(bias + n);
+          f4* dst = reinterpret_cast<f4*>(row + n);
+          if (!to_ws && g.beta != 0.f) v += g.beta * *dst;
           *dst = v;
         } else {
-          v += bias;
-          if (g.beta != 0.f) v += g.beta * *dst;
-          *dst = v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e >= g.N) break;
+            float x = v[e];
+            if (bias) x += bias[n + e];
+            if (!to_ws && g.beta != 0.f) x += g.beta * row[n + e];
+            row[n + e] = x;
+          }
         }
       }
     }
