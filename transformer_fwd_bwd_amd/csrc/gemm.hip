@@ -9,11 +9,13 @@
 // A workgroup of WM x WN wavefronts computes a BM x BN tile of C; each wave owns
 // TM x TN blocks of 32x32 accumulated by v_mfma_f32_32x32x16_bf16 (bf16
 // operands) or v_mfma_f32_32x32x2_f32 (fp32 operands), fp32 accumulation.
-// A k-contiguous operand is staged through LDS as [row][k] (16-byte padded rows),
-// so a lane reads its MFMA fragment with one 16-byte LDS load.  An m- or
-// n-contiguous operand stored as bf16 keeps its own [k][row] layout in LDS and
-// its fragments are gathered by the transposing LDS read (ds_read_b64_tr_b16);
-// in fp32 storage it is transposed in small register blocks on the way in.
+// A k-contiguous operand is staged through LDS as [row][k] (16-byte padded rows
+// for 64-deep k-tiles, XOR-swizzled 16-byte chunks for 32-deep ones), so a lane
+// reads its MFMA fragment with one 16-byte LDS load.  An m- or n-contiguous
+// operand stored as bf16 keeps its own [k][row] layout in LDS and its fragments
+// are gathered by the transposing LDS read (ds_read_b64_tr_b16); in fp32
+// storage it is transposed in small register blocks on the way in.  Every
+// layout is free of bank conflicts on gfx950's 64 four-byte LDS banks.
 // Operands may be stored as fp32 (rounded to bf16, nearest even, while staging
 // in the bf16 variant) or already as bf16.  The next k-tile is fetched into
 // registers while the current one is multiplied (two LDS buffers, one barrier
@@ -55,12 +57,22 @@ struct Lds;
 template <int BK>
 struct Lds<true, BK> {
   using T = bf16_t;
-  static constexpr int LDK = BK + 8;  // rows padded by 16 bytes: conflict-free 16-byte fragment reads
+  // 64-deep rows are padded by 16 bytes (a 16-lane fragment read then walks
+  // all 64 banks); 32-deep rows are unpadded with chunk c of row r stored at
+  // chunk c ^ ((r >> 2) & 3), which keeps both the 16-row fragment reads and
+  // the 4-rows-at-a-time staging stores on distinct banks
+  static constexpr bool SWZ = BK == 32;
+  static constexpr int LDK = SWZ ? BK : BK + 8;
+  // element offset of (row r, k) for k a multiple of 4
+  __device__ __forceinline__ static int off(int r, int k) {
+    return SWZ ? r * LDK + ((((k >> 3) ^ ((r >> 2) & 3)) << 3) | (k & 7)) : r * LDK + k;
+  }
 };
 template <int BK>
 struct Lds<false, BK> {
   using T = float;
   static constexpr int LDK = BK + 4;
+  __device__ __forceinline__ static int off(int r, int k) { return r * LDK + k; }
 };
 
 __device__ __forceinline__ float mask_causal(float v, int causal, int m, int k) {
@@ -207,7 +219,7 @@ struct Stage {
     }
   }
 
-  // LDK: LDS row pitch in elements
+  // LDK: LDS row pitch in elements (Lds<BF16, BK>::LDK)
   template <bool BF16, int LDK>
   __device__ __forceinline__ void store(typename Lds<BF16, BK>::T* L, int tid) const {
 #pragma unroll
@@ -217,21 +229,21 @@ struct Stage {
       if constexpr (!RCONTIG) {
         const int rr = u / (BK / UK), kq = u % (BK / UK);
         if constexpr (!SRC_BF16)
-          put4<BF16>(L + rr * LDK + kq * 4, r[i]);
+          put4<BF16>(L + Lds<BF16, BK>::off(rr, kq * 4), r[i]);
         else
-          *reinterpret_cast<u16x8*>(L + rr * LDK + kq * 8) = r[i];
+          *reinterpret_cast<u16x8*>(L + Lds<BF16, BK>::off(rr, kq * 8)) = r[i];
       } else {
         const int rq = u % (R_TILE / 4), kq = u / (R_TILE / 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (!SRC_BF16) {
             f4 v = {r[i * 4 + 0][e], r[i * 4 + 1][e], r[i * 4 + 2][e], r[i * 4 + 3][e]};
-            put4<BF16>(L + (rq * 4 + e) * LDK + kq * 4, v);
+            put4<BF16>(L + Lds<BF16, BK>::off(rq * 4 + e, kq * 4), v);
           } else {
             u16x8 v;
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) v[kk] = r[i * 8 + kk][e];
-            *reinterpret_cast<u16x8*>(L + (rq * 4 + e) * LDK + kq * 8) = v;
+            *reinterpret_cast<u16x8*>(L + Lds<BF16, BK>::off(rq * 4 + e, kq * 8)) = v;
           }
         }
       }
@@ -250,17 +262,18 @@ struct Stage {
 };
 
 // A bf16 r-contiguous (m- or n-contiguous) operand staged in its own layout:
-// LDS holds the tile as [k][r] with rows of R_TILE + 16 elements, filled by
+// LDS holds the tile as [k][r] with rows of R_TILE + 32 elements, filled by
 // straight 16-byte copies; the MFMA fragments (8 consecutive k of one r per
 // lane) are read with the transposing LDS read ds_read_b64_tr_b16.  Within a
 // group of 16 lanes that instruction hands lane j element e of the 8 bytes
 // addressed by lane 4e + j/4, at position j%4; so lane i of the group points at
 // row kb + i/4, columns rb + 4(i%4) .. +3, and lane j receives r = rb + j,
-// k = kb .. kb + 3.  The 32-byte row pad puts the four rows one such read
-// touches in four different bank groups.
+// k = kb .. kb + 3.  A 32-lane phase of the read covers four k-rows x 64
+// bytes; the 64-byte row pad staggers consecutive rows by 16 banks, so the
+// phase touches each of the 64 banks once.
 template <int R_TILE, int NT, int BK>
 struct StageTr {
-  static constexpr int LDR = R_TILE + 16;
+  static constexpr int LDR = R_TILE + 32;
   static constexpr int CPR = R_TILE / 8;  // 16-byte chunks per k-row
   static constexpr int UNITS = BK * CPR;
   static constexpr int PER = (UNITS + NT - 1) / NT;
@@ -344,9 +357,14 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
   // a bf16 r-contiguous operand keeps its own [k][r] layout in LDS (StageTr)
   constexpr bool TRA = BF16 && A_BF && A_RC && BK % 16 == 0;
   constexpr bool TRB = BF16 && B_BF && !B_KC && BK % 16 == 0;
-  constexpr int LDA = TRA ? BM + 16 : LDK, LDB = TRB ? BN + 16 : LDK;
-  __shared__ __attribute__((aligned(16))) LT As[2][TRA ? BK * LDA : BM * LDA];
-  __shared__ __attribute__((aligned(16))) LT Bs[2][TRB ? BK * LDB : BN * LDB];
+  constexpr int LDA = TRA ? BM + 32 : LDK, LDB = TRB ? BN + 32 : LDK;
+  constexpr int ASZ = TRA ? BK * LDA : BM * LDA, BSZ = TRB ? BK * LDB : BN * LDB;
+  // after the k loop the epilogue restages each wave's 32-row slabs of C here
+  constexpr int EP = TN * 32 + 4;
+  constexpr int SMEM = std::max<int>((2 * ASZ + 2 * BSZ) * (int)sizeof(LT), WM * WN * 32 * EP * 4);
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  LT(*As)[ASZ] = reinterpret_cast<LT(*)[ASZ]>(smem);
+  LT(*Bs)[BSZ] = reinterpret_cast<LT(*)[BSZ]>(smem + 2 * ASZ * sizeof(LT));
 
   const GemmArgs& g = ka.g;
   const int tid = threadIdx.x;
@@ -438,14 +456,16 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
           if constexpr (TRA)
             af[i] = frag_tr(Ab + ks * LDA + i * 32, LDA);
           else
-            af[i] = *reinterpret_cast<const bf16x8*>(Ab + i * 32 * LDA + ks + lhalf * 8);
+            af[i] = *reinterpret_cast<const bf16x8*>(Ab + i * 32 * LDA + Lds<true, BK>::off(lrow, ks + lhalf * 8) -
+                                                     lrow * LDA);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           if constexpr (TRB)
             bf[j] = frag_tr(Bb + ks * LDB + j * 32, LDB);
           else
-            bf[j] = *reinterpret_cast<const bf16x8*>(Bb + j * 32 * LDB + ks + lhalf * 8);
+            bf[j] = *reinterpret_cast<const bf16x8*>(Bb + j * 32 * LDB + Lds<true, BK>::off(lrow, ks + lhalf * 8) -
+                                                     lrow * LDB);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -565,8 +585,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
 
   // Epilogue.  The MFMAs take B's fragment as their first operand, so each
   // 32x32 block accumulates C^T: register r holds C[lane%32][8*(r/4) + 4*(lane/32) + r%4],
-  // and registers 4q .. 4q+3 are four consecutive columns of one row -- one
-  // 16-byte store (and 16-byte bias / beta reads) where the row pitch allows.
+  // and registers 4q .. 4q+3 are four consecutive columns of one row.
   const bool to_ws = ka.splits > 1;
   float* C;
   int64_t ldc;
@@ -580,18 +599,32 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
   const float* bias = to_ws ? nullptr : g.bias;
   const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(bias) & 15) == 0);
+  if (vec) {
+    // 16-byte rows: each wave writes one 32-row slab of its blocks to its own
+    // LDS region and reads it back so that 16 lanes hold 64 consecutive
+    // columns of one row; a store instruction then writes 4 rows x 256
+    // contiguous bytes (whole cache lines) instead of 32 rows x 32 bytes.  The
+    // regions are wave-private: one workgroup barrier frees the operand tiles.
+    __syncthreads();
+    float* E = reinterpret_cast<float*>(smem) + wave * 32 * EP;
+    constexpr int C4 = TN * 8;  // float4 per slab row
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * TM * 32 + i * 32 + lrow;
-    if (m >= g.M) continue;
-    float* row = C + (int64_t)m * ldc;
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * TN * 32 + j * 32 + 8 * q + 4 * lhalf;
-        f4 v = f4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]} * g.alpha;
-        if (vec && n + 3 < g.N) {
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f4*>(E + lrow * EP + j * 32 + 8 * q + 4 * lhalf) =
+              f4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < 32 * C4 / 64; ++it) {
+        const int f = it * 64 + lane, r = f / C4, c4 = f % C4;
+        f4 v = *reinterpret_cast<const f4*>(E + r * EP + c4 * 4) * g.alpha;
+        const int m = m0 + wm * TM * 32 + i * 32 + r, n = n0 + wn * TN * 32 + c4 * 4;
+        if (m >= g.M) continue;
+        float* row = C + (int64_t)m * ldc;
+        if (n + 3 < g.N) {
           if (bias) v += *reinterpret_cast<const f4*>(bias + n);
           f4* dst = reinterpret_cast<f4*>(row + n);
           if (!to_ws && g.beta != 0.f) v += g.beta * *dst;
@@ -605,6 +638,31 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
             if (!to_ws && g.beta != 0.f) x += g.beta * row[n + e];
             row[n + e] = x;
           }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    return;
+  }
+  // otherwise element stores straight from the accumulators
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * TM * 32 + i * 32 + lrow;
+    if (m >= g.M) continue;
+    float* row = C + (int64_t)m * ldc;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * TN * 32 + j * 32 + 8 * q + 4 * lhalf;
+        const f4 v = f4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]} * g.alpha;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (n + e >= g.N) break;
+          float x = v[e];
+          if (bias) x += bias[n + e];
+          if (!to_ws && g.beta != 0.f) x += g.beta * row[n + e];
+          row[n + e] = x;
         }
       }
     }
