@@ -124,6 +124,13 @@ int tfb_matmul_t(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y);
  * contraction's epilogue); w is [in, out] as GPT-2 stores it.
  * [GPT2-4, "Loading the weights": Linear weights stored [in, out]] */
 int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y);
+/* tfb_linear with flags.  TFB_OUT_BF16_COPY: in the bf16 variant the product's
+ * epilogue also writes the bf16 copy of y that bf16 consumers (the contraction
+ * and attention kernels) read, sparing them a conversion pass; it changes no
+ * value and is ignored in the fp32 variant.  Unknown flags: TFB_ERR_ARG.
+ * [GPT2-4, "Loading the weights": Linear weights stored [in, out]] */
+#define TFB_OUT_BF16_COPY 1
+int tfb_linear_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int flags, tfb_tensor* y);
 /* Per row over the last dim: (x - mean)/sqrt(var + eps) * gamma + beta with the
  * biased variance.  [Autograd-1, table of ops: LayerNorm] */
 int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y);

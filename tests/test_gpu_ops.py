@@ -287,6 +287,72 @@ def test_add_of_single_use_outputs_and_repeated_backward(ctx):
         t.release()
 
 
+@pytest.mark.parametrize("prec", PRECS)
+def test_residual_gradients_without_copies(ctx, prec):
+    """[Autograd-1, "Backward pass"]: gradients of residual-stream tensors, which the
+    library carries from an Add to the tensor's next contribution without a copy:
+    taken up by a LayerNorm backward (x0), by another op's contribution (u, read by a
+    Mul recorded before the Add), or by no further op at all (v: its other reader
+    does not reach the loss).  Two passes over one tape; leaf gradients add up."""
+    ctx.set_precision(prec)
+    xin, uin, vin = rnd(81, (4, 24, 64)), rnd(82, (4, 24, 64)), rnd(83, (4, 24, 64))
+    gam, bet = rnd(84, (64,), 0.5) + 1.0, rnd(85, (64,), 0.1)
+    Wv, bv, Rv, Mv = rnd(86, (64, 64), 0.1), rnd(87, (64,), 0.1), rnd(88, (4, 24, 64)), rnd(89, (4, 24, 64))
+    leaves = {k: ctx.tensor(v.shape, v) for k, v in
+              dict(xin=xin, uin=uin, vin=vin, gam=gam, bet=bet, W=Wv, b=bv, R=Rv, M=Mv).items()}
+    L = leaves
+
+    def build(ops, t):
+        x0 = ops.tanh(t["xin"])
+        y = ops.add(ops.matmul(ops.layernorm(x0, t["gam"], t["bet"]), t["W"]), t["b"])
+        x1 = ops.add(x0, y)                                  # x0: deferred, then the LayerNorm's share
+        u = ops.tanh(t["uin"])
+        m = ops.mul(u, t["M"])                               # u's other reader, recorded before the Add
+        x2 = ops.add(u, ops.gelu(x1))                        # u: deferred, then the Mul's share
+        v = ops.tanh(t["vin"])
+        ops.gelu(v)                                          # v's other reader: not on the loss path
+        x3 = ops.add(v, ops.mul(x2, m))                      # v: deferred, nothing else arrives
+        return ops.sum_all(ops.mul(x3, t["R"])), (x0, u, v)
+
+    loss, inter = build(T, L)
+    ctx.backward(loss)
+    ctx.backward(loss)
+    O = {k: E.Tensor(a.astype(np.float64)) for k, a in
+         dict(xin=xin, uin=uin, vin=vin, gam=gam, bet=bet, W=Wv, b=bv, R=Rv, M=Mv).items()}
+    oloss, ointer = build(E, O)
+    oloss.backward()
+    tol = GRAD_TOL[prec]
+    for name, g, r in zip(("x0", "u", "v"), inter, ointer):
+        assert_close(g.grad(), r.grad, tol, f"{name}.grad (one pass)")
+    for k in ("xin", "uin", "vin", "gam", "bet", "W", "b", "M"):
+        assert_close(L[k].grad(), 2 * O[k].grad, tol, f"{k}.grad after two passes")
+    ctx.tape_reset()
+    for t in L.values():
+        t.release()
+    ctx.set_precision("fp32")
+
+
+def test_linear_bf16_copy_changes_nothing(ctx):
+    """The bf16 copy a linear's product writes for its reader (here the attention
+    kernels) is the same rounding the reader would have made: outputs and every
+    gradient agree bit for bit with the plain linear."""
+    ctx.set_precision("bf16")
+    B, Tn, C, H = 2, 96, 128, 2
+    xv, wv, bv, rv = rnd(91, (B, Tn, C)), rnd(92, (C, 3 * C), 0.05), rnd(93, (3 * C,), 0.1), rnd(94, (B, Tn, C))
+    res = []
+    for flag in (False, True):
+        x, w, b, R = (ctx.tensor(a.shape, a) for a in (xv, wv, bv, rv))
+        y = T.causal_attention(T.linear(x, w, b, bf16_copy=flag), H)
+        ctx.backward(T.sum_all(T.mul(y, R)))
+        res.append([y.numpy(), x.grad(), w.grad(), b.grad()])
+        ctx.tape_reset()
+        for t in (x, w, b, R):
+            t.release()
+    for a, b_ in zip(*res):
+        np.testing.assert_array_equal(a, b_)
+    ctx.set_precision("fp32")
+
+
 def test_no_grad_records_nothing(ctx):
     a = ctx.tensor((2, 3), rnd(40, (2, 3)))
     ctx.set_grad_enabled(False)

@@ -50,6 +50,7 @@ SIGNATURES = {
     "tfb_matmul": [c_void_p, c_int32, c_int32, P(c_int32)],
     "tfb_matmul_t": [c_void_p, c_int32, c_int32, P(c_int32)],
     "tfb_linear": [c_void_p, c_int32, c_int32, c_int32, P(c_int32)],
+    "tfb_linear_ex": [c_void_p, c_int32, c_int32, c_int32, c_int32, P(c_int32)],
     "tfb_layernorm": [c_void_p, c_int32, c_int32, c_int32, c_float, P(c_int32)],
     "tfb_embedding": [c_void_p, c_int32, c_void_p, c_int64, c_int64, P(c_int32)],
     "tfb_narrow": [c_void_p, c_int32, c_int64, c_int64, P(c_int32)],
@@ -294,7 +295,14 @@ def matmul_t(x: Tensor, w: Tensor) -> Tensor:
     return _out(x.ctx, _lib.tfb_matmul_t, x.h, w.h)
 
 
-def linear(x: Tensor, w: Tensor, b: Tensor) -> Tensor:
+OUT_BF16_COPY = 1
+
+
+def linear(x: Tensor, w: Tensor, b: Tensor, bf16_copy: bool = False) -> Tensor:
+    """x @ w + b.  bf16_copy: the product also writes the output's bf16 copy (bf16
+    variant), for an output that a contraction or the attention kernels read next."""
+    if bf16_copy:
+        return _out(x.ctx, _lib.tfb_linear_ex, x.h, w.h, b.h, OUT_BF16_COPY)
     return _out(x.ctx, _lib.tfb_linear, x.h, w.h, b.h)
 
 

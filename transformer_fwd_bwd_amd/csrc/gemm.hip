@@ -82,6 +82,10 @@ __device__ __forceinline__ float mask_causal(float v, int causal, int m, int k) 
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
+__device__ __forceinline__ unsigned short bf16_bits(float x) { return __builtin_bit_cast(unsigned short, (bf16_t)x); }
+__device__ __forceinline__ u16x4 bf16x4_bits(f4 v) {
+  return u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
+}
 
 // One thread's share of an R_TILE x BK operand tile held in registers.
 //   SRC_BF16 = false: fp32 source; k-contiguous units are 4 k of one row,
@@ -597,8 +601,9 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
     ldc = g.ldc;
   }
   const float* bias = to_ws ? nullptr : g.bias;
+  uint16_t* Cbf = to_ws ? nullptr : g.Cbf;
   const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(bias) & 15) == 0);
+                   ((reinterpret_cast<uintptr_t>(bias) & 15) == 0) && ((reinterpret_cast<uintptr_t>(Cbf) & 7) == 0);
   if (vec) {
     // 16-byte rows: each wave writes one 32-row slab of its blocks to its own
     // LDS region and reads it back so that 16 lanes hold 64 consecutive
@@ -629,6 +634,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
           f4* dst = reinterpret_cast<f4*>(row + n);
           if (!to_ws && g.beta != 0.f) v += g.beta * *dst;
           *dst = v;
+          if (Cbf) *reinterpret_cast<u16x4*>(Cbf + (int64_t)m * ldc + n) = bf16x4_bits(v);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -637,6 +643,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
             if (bias) x += bias[n + e];
             if (!to_ws && g.beta != 0.f) x += g.beta * row[n + e];
             row[n + e] = x;
+            if (Cbf) Cbf[(int64_t)m * ldc + n + e] = bf16_bits(x);
           }
         }
       }
@@ -663,6 +670,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
           if (bias) x += bias[n + e];
           if (!to_ws && g.beta != 0.f) x += g.beta * row[n + e];
           row[n + e] = x;
+          if (Cbf) Cbf[(int64_t)m * ldc + n + e] = bf16_bits(x);
         }
       }
     }
@@ -671,7 +679,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
 
 // The same over float4 (N, ldc multiples of 4, 16-byte aligned C and bias)
 __global__ void splitk_reduce4(const f4* __restrict__ ws, int splits, int M, int N4, float* C, int64_t ldc,
-                               int batch_div, int64_t sc1, int64_t sc2, float beta, const f4* bias) {
+                               int batch_div, int64_t sc1, int64_t sc2, float beta, const f4* bias, uint16_t* Cbf) {
   const int z = blockIdx.y;
   const int64_t MN4 = (int64_t)M * N4;
   const int z1 = z / batch_div, z2 = z % batch_div;
@@ -684,12 +692,13 @@ __global__ void splitk_reduce4(const f4* __restrict__ ws, int splits, int M, int
     f4* dst = reinterpret_cast<f4*>(Cz + (int64_t)m * ldc) + n4;
     if (beta != 0.f) s += beta * *dst;
     *dst = s;
+    if (Cbf) *reinterpret_cast<u16x4*>(Cbf + (Cz - C) + (int64_t)m * ldc + 4 * n4) = bf16x4_bits(s);
   }
 }
 
 // C = sum over splits of the partials + beta*C + bias
 __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, int N, float* C, int64_t ldc,
-                              int batch_div, int64_t sc1, int64_t sc2, float beta, const float* bias) {
+                              int batch_div, int64_t sc1, int64_t sc2, float beta, const float* bias, uint16_t* Cbf) {
   const int z = blockIdx.y;
   const int64_t MN = (int64_t)M * N;
   const int z1 = z / batch_div, z2 = z % batch_div;
@@ -702,6 +711,7 @@ __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, i
     float* dst = Cz + (int64_t)m * ldc + n;
     if (beta != 0.f) s += beta * *dst;
     *dst = s;
+    if (Cbf) Cbf[(Cz - C) + (int64_t)m * ldc + n] = bf16_bits(s);
   }
 }
 
@@ -820,15 +830,17 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t MN = (int64_t)g.M * g.N;
   const bool vec = g.N % 4 == 0 && g.ldc % 4 == 0 && g.sc1 % 4 == 0 && g.sc2 % 4 == 0 &&
-                   (reinterpret_cast<uintptr_t>(g.C) & 15) == 0 && (reinterpret_cast<uintptr_t>(g.bias) & 15) == 0;
+                   (reinterpret_cast<uintptr_t>(g.C) & 15) == 0 && (reinterpret_cast<uintptr_t>(g.bias) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(g.Cbf) & 7) == 0;
   if (vec) {
     dim3 rgrid((unsigned)std::min<int64_t>((MN / 4 + 255) / 256, 4096), g.batch);
     hipLaunchKernelGGL(splitk_reduce4, rgrid, dim3(256), 0, s, reinterpret_cast<const f4*>(ka.ws), p.splits, g.M,
-                       g.N / 4, g.C, g.ldc, g.batch_div, g.sc1, g.sc2, g.beta, reinterpret_cast<const f4*>(g.bias));
+                       g.N / 4, g.C, g.ldc, g.batch_div, g.sc1, g.sc2, g.beta, reinterpret_cast<const f4*>(g.bias),
+                       g.Cbf);
   } else {
     dim3 rgrid((unsigned)std::min<int64_t>((MN + 255) / 256, 4096), g.batch);
     hipLaunchKernelGGL(splitk_reduce, rgrid, dim3(256), 0, s, ka.ws, p.splits, g.M, g.N, g.C, g.ldc, g.batch_div,
-                       g.sc1, g.sc2, g.beta, g.bias);
+                       g.sc1, g.sc2, g.beta, g.bias, g.Cbf);
   }
   return hipGetLastError();
 }

@@ -42,6 +42,8 @@ struct GemmArgs {
   int prec = PREC_F32;
   // bf16 storage of an operand (bf16 variant only): A/B then point at uint16 data
   bool a_bf16 = false, b_bf16 = false;
+  // optional bf16 copy (round to nearest even) of the final C, same layout and ldc
+  uint16_t* Cbf = nullptr;
 };
 
 size_t gemm_workspace_bytes(const GemmArgs& g);
@@ -86,10 +88,11 @@ hipError_t permute_heads(const float* x, float* y, int64_t B, int64_t T, int64_t
 hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, float* y, uint16_t* ybf, float* mean,
                          float* rstd, int64_t rows, int64_t C, float eps, hipStream_t s);
 size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C);
-// dxbf (optional) receives the bf16 copy of the final dx
+// dxbf (optional) receives the bf16 copy of the final dx.  With beta_dx != 0 the
+// earlier gradient is read from dx_src (null: dx itself) and the sum written to dx.
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
-                         float* dx, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows, int64_t C,
-                         float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s);
+                         float* dx, const float* dx_src, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows,
+                         int64_t C, float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s);
 // full == true: every element of the [rows, T] view is written (zeros where masked);
 // full == false: only the visible prefix of each row is touched.
 hipError_t causal_softmax_fwd(const float* x, float* p, int64_t rows, int64_t T, bool full, hipStream_t s);

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(NT) void ln_bwd_dx_k(const float* __restrict__ g, c
 template <int J>
 __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, const f4* __restrict__ x,
                                                       const f4* __restrict__ gamma, const float* __restrict__ mean,
-                                                      const float* __restrict__ rstd, f4* __restrict__ dx,
+                                                      const float* __restrict__ rstd, f4* dx, const f4* dx_src,
                                                       u16x4* __restrict__ dxbf, f4* __restrict__ part, int64_t rows,
                                                       int C4, float beta_dx) {
   __shared__ f4 sh[WAVES - 1][2][64 * J];
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, 
         const int c = lane + 64 * j;
         if (c < C4) {
           f4 v = rs * (dg[j] - m1 - xh[j] * m2);
-          if (beta_dx != 0.f) v += dx[r * C4 + c];
+          if (beta_dx != 0.f) v += dx_src[r * C4 + c];  // may be dx itself: read before the write
           dx[r * C4 + c] = v;
           if (dxbf) dxbf[r * C4 + c] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
         }
@@ -675,24 +675,31 @@ size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C) {
 }
 
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
-                         float* dx, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows, int64_t C, float beta_dx,
-                         float beta_dg, float beta_db, void* ws, hipStream_t s) {
+                         float* dx, const float* dx_src, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows,
+                         int64_t C, float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s) {
   if (C <= 0) return hipSuccess;
+  if (!dx_src) dx_src = dx;
   float* part = static_cast<float*>(ws);
   int parts = 0;
   if (rows > 0 && C % 4 == 0 && C <= 1024 && aligned16(g) && aligned16(x) && aligned16(gamma) && aligned16(dx) &&
-      aligned16(part) && (reinterpret_cast<uintptr_t>(dxbf) & 7) == 0) {
+      aligned16(dx_src) && aligned16(part) && (reinterpret_cast<uintptr_t>(dxbf) & 7) == 0) {
     // dx (and its bf16 copy) and the column partials in one pass over g and x
     const int C4 = (int)(C / 4);
     const int64_t blocks = ln_fused_blocks(rows);
     if (C4 <= 64)
       hipLaunchKernelGGL(ln_bwd_fused4_k<1>, dim3((unsigned)blocks), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
-                         (const f4*)gamma, mean, rstd, (f4*)dx, (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+                         (const f4*)gamma, mean, rstd, (f4*)dx, (const f4*)dx_src, (u16x4*)dxbf, (f4*)part, rows, C4,
+                         beta_dx);
     else
       hipLaunchKernelGGL(ln_bwd_fused4_k<4>, dim3((unsigned)blocks), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
-                         (const f4*)gamma, mean, rstd, (f4*)dx, (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+                         (const f4*)gamma, mean, rstd, (f4*)dx, (const f4*)dx_src, (u16x4*)dxbf, (f4*)part, rows, C4,
+                         beta_dx);
     parts = (int)blocks;
   } else {
+    if (rows > 0 && beta_dx != 0.f && dx_src != dx) {  // the kernels below accumulate into dx itself
+      const hipError_t e = hipMemcpyAsync(dx, dx_src, (size_t)(rows * C) * sizeof(float), hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return e;
+    }
     if (rows > 0) {
       if (C <= 64 * MAXV)
         hipLaunchKernelGGL(ln_bwd_dx_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,

@@ -66,6 +66,12 @@ struct TensorRec {
 
   int64_t ld = 0;  // row stride of the last dim when rows are padded (0: dense)
   int uses = 0;    // ops on the tape that read this tensor
+  int producer = -1;  // tape index of the op that wrote it (-1: none on the tape)
+  // During backward: the gradient so far equals this finished gradient of
+  // another tensor (a copy not yet made).  The next contribution reads it as
+  // its accumulation source, or it is copied into `grad` before anyone reads
+  // `grad`.  The buffer it points to is never written again in the pass.
+  const float* gpend = nullptr;
 
   int64_t cols() const { return ndim ? shape[ndim - 1] : 1; }
   int64_t rows() const { return cols() ? numel / cols() : 0; }
@@ -260,11 +266,55 @@ struct Ctx {
   // destination of a gradient contribution: (pointer, beta)
   std::pair<float*, float> gdst(int h) {
     TensorRec& t = T(h);
+    settle(t);
     ensure_grad_buffer(t);
     t.gbf_valid = false;
     if (t.gstate == G_VALID) return {t.grad, 1.f};
     t.gstate = G_VALID;
     return {t.grad, 0.f};
+  }
+
+  // the same for a kernel that reads the earlier gradient from a separate
+  // pointer: (destination, beta, source of the earlier gradient)
+  struct GradDst {
+    float* dst;
+    float beta;
+    const float* src;
+  };
+  GradDst gdst_src(int h) {
+    TensorRec& t = T(h);
+    if (t.gpend) {
+      ensure_grad_buffer(t);
+      const float* src = t.gpend;
+      t.gpend = nullptr;
+      t.gstate = G_VALID;
+      t.gbf_valid = false;
+      return {t.grad, 1.f, src};
+    }
+    const auto d = gdst(h);
+    return {d.first, d.second, d.first};
+  }
+
+  // make a pending first contribution real
+  void settle(TensorRec& t) {
+    if (!t.gpend) return;
+    const float* src = t.gpend;
+    t.gpend = nullptr;
+    ensure_grad_buffer(t);
+    hip_check(axpby(t.grad, src, 1.f, 0.f, t.numel, s()), "gradient copy");
+    t.gstate = G_VALID;
+    t.gbf_valid = false;
+  }
+
+  // x's gradient so far is the finished gradient of `out` (a residual
+  // branch): remember the buffer instead of copying it.  Only for a
+  // gradient with no contribution yet, of the same dense shape.
+  bool defer_grad(TensorRec& x, const TensorRec& out) {
+    if (x.leaf || x.is_param || x.gpend || x.gstate == G_VALID) return false;
+    if (x.padded() || out.padded() || x.numel != out.numel || !out.grad || out.gpend) return false;
+    x.gpend = out.grad;
+    x.gbf_valid = false;
+    return true;
   }
 
   bool bf16_mode() const { return c->precision == TFB_BF16_MFMA; }
@@ -321,6 +371,15 @@ struct Ctx {
     c->tape.push_back(r);
     for (int h : r.in)
       if (h >= 0) c->tensors[h].uses += 1;
+    c->tensors[r.out].producer = (int)c->tape.size() - 1;
+  }
+
+  // the backward of t's producer reads t's gradient as the bf16 copy
+  bool grad_read_as_bf16(const TensorRec& t) const {
+    if (!bf16_mode() || t.producer < 0 || t.producer >= (int)c->tape.size()) return false;
+    const Rec& p = c->tape[t.producer];
+    if (&c->tensors[p.out] != &t) return false;
+    return p.op == OP_LINEAR || p.op == OP_MATMUL || p.op == OP_MATMUL_T || (p.op == OP_ATTENTION && p.i1 == 1);
   }
 
   // An op output read by exactly one op (this one, during its backward) whose
@@ -431,22 +490,23 @@ void set_b(GemmArgs& g, Opnd o) {
 
 // y[rows, N] = x[rows, K] @ w[K, N] (+ bias)
 void gemm_nn(Ctx& C, Opnd x, Opnd w, float* y, int64_t rows, int64_t K, int64_t N, float beta, const float* bias,
-             int64_t lda = -1) {
+             int64_t lda = -1, uint16_t* ybf = nullptr) {
   GemmArgs g = C.gemm_base();
   g.M = (int)rows, g.N = (int)N, g.K = (int)K;
   set_a(g, x), g.lda = lda < 0 ? K : lda;
   set_b(g, w), g.ldb = N;
-  g.C = y, g.ldc = N;
+  g.C = y, g.ldc = N, g.Cbf = ybf;
   g.beta = beta, g.bias = bias;
   C.run_gemm(g);
 }
 // y[rows, N] = x[rows, K] @ w[N, K]^T
-void gemm_nt(Ctx& C, Opnd x, Opnd w, float* y, int64_t rows, int64_t K, int64_t N, float beta, int64_t ldc = -1) {
+void gemm_nt(Ctx& C, Opnd x, Opnd w, float* y, int64_t rows, int64_t K, int64_t N, float beta, int64_t ldc = -1,
+             uint16_t* ybf = nullptr) {
   GemmArgs g = C.gemm_base();
   g.M = (int)rows, g.N = (int)N, g.K = (int)K;
   set_a(g, x), g.lda = K;
   set_b(g, w), g.ldb = K, g.b_kcontig = true;
-  g.C = y, g.ldc = ldc < 0 ? N : ldc;
+  g.C = y, g.ldc = ldc < 0 ? N : ldc, g.Cbf = ybf;
   g.beta = beta;
   C.run_gemm(g);
 }
@@ -474,7 +534,7 @@ void backward_rec(Ctx& C, const Rec& r) {
     case OP_ADD: {
       TensorRec& a = C.T(r.in[0]);
       TensorRec& b = C.T(r.in[1]);
-      if (r.in[0] == r.in[1] || !C.share_grad(a, out)) {
+      if (r.in[0] == r.in[1] || !(C.share_grad(a, out) || C.defer_grad(a, out))) {
         auto da = C.gdst(r.in[0]);
         hip_check(axpby(da.first, g, 1.f, da.second, a.numel, s), "add bwd");
       }
@@ -532,7 +592,10 @@ void backward_rec(Ctx& C, const Rec& r) {
       const int64_t rows = x.rows(), K = w.shape[0], N = w.shape[1];
       const Opnd go = op_grad(C, out);
       auto dx = C.gdst(r.in[0]);
-      gemm_nt(C, go, op_data(C, w), dx.first, rows, N, K, dx.second);   // dx = g @ w^T
+      // a first and only contribution read as bf16 by x's producer: the product writes that copy too
+      uint16_t* dxb = dx.second == 0.f && x.uses == 1 && !x.leaf && C.grad_read_as_bf16(x) ? C.twin_grad(x) : nullptr;
+      gemm_nt(C, go, op_data(C, w), dx.first, rows, N, K, dx.second, -1, dxb);   // dx = g @ w^T
+      if (dxb) x.gbf_valid = true;
       auto dw = C.gdst(r.in[1]);
       gemm_tn(C, op_data(C, x), go, dw.first, K, rows, N, dw.second);   // dw = x^T @ g
       if (r.op == OP_LINEAR) {
@@ -560,7 +623,7 @@ void backward_rec(Ctx& C, const Rec& r) {
       TensorRec& x = C.T(r.in[0]);
       TensorRec& gm = C.T(r.in[1]);
       const int64_t rows = x.rows(), Cc = x.cols();
-      auto dx = C.gdst(r.in[0]);
+      const auto dx = C.gdst_src(r.in[0]);
       auto dg = C.gdst(r.in[1]);
       auto db = C.gdst(r.in[2]);
       // the bf16 copy of dx serves the contractions when this is the gradient's last
@@ -568,8 +631,8 @@ void backward_rec(Ctx& C, const Rec& r) {
       uint16_t* dxb = x.leaf ? nullptr : C.twin_grad(x);
       size_t mark = C.c->arena.hi;
       void* ws = C.scratch(layernorm_bwd_workspace_bytes(rows, Cc));
-      hip_check(layernorm_bwd(g, x.data, gm.data, static_cast<float*>(r.s0), static_cast<float*>(r.s1), dx.first,
-                              dxb, dg.first, db.first, rows, Cc, dx.second, dg.second, db.second, ws, s),
+      hip_check(layernorm_bwd(g, x.data, gm.data, static_cast<float*>(r.s0), static_cast<float*>(r.s1), dx.dst,
+                              dx.src, dxb, dg.first, db.first, rows, Cc, dx.beta, dg.second, db.second, ws, s),
                 "layernorm bwd");
       C.c->arena.hi = mark;
       if (dxb) x.gbf_valid = true;
@@ -1041,7 +1104,8 @@ int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
   });
 }
 
-static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y, OpKind kind) {
+static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y, OpKind kind,
+                       bool bf_out = false) {
   return guarded([&] {
     Ctx C(ctx);
     x = C.dense_in(x), w = C.dense_in(w);
@@ -1077,10 +1141,12 @@ static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, t
     const float* wd = ctx->tensors[w].data;
     const Opnd xo = op_data(C, ctx->tensors[x]), wo = op_data(C, ctx->tensors[w]);
     (void)xd, (void)wd;
+    uint16_t* yb = bf_out ? C.twin_data(ctx->tensors[h]) : nullptr;
     if (kind == OP_MATMUL_T)
-      gemm_nt(C, xo, wo, yd, rows, K, N, 0.f, ld ? ld : N);
+      gemm_nt(C, xo, wo, yd, rows, K, N, 0.f, ld ? ld : N, yb);
     else
-      gemm_nn(C, xo, wo, yd, rows, K, N, 0.f, bias);
+      gemm_nn(C, xo, wo, yd, rows, K, N, 0.f, bias, -1, yb);
+    if (yb) ctx->tensors[h].bf_valid = true;
     Rec r{kind};
     r.in[0] = x, r.in[1] = w, r.in[2] = kind == OP_LINEAR ? b : -1, r.out = h;
     C.record(r);
@@ -1096,6 +1162,11 @@ int tfb_matmul_t(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y) {
 }
 int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y) {
   return matmul_impl(ctx, x, w, b, y, OP_LINEAR);
+}
+
+int tfb_linear_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int flags, tfb_tensor* y) {
+  if (flags & ~TFB_OUT_BF16_COPY) return guarded([&] { need(false, TFB_ERR_ARG, "unknown tfb_linear_ex flags"); });
+  return matmul_impl(ctx, x, w, b, y, OP_LINEAR, (flags & TFB_OUT_BF16_COPY) != 0);
 }
 
 int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y) {
@@ -1360,6 +1431,7 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
     for (TensorRec& t : ctx->tensors) {
       if (t.live && !t.leaf && t.grad) t.gstate = G_ZERO;
       t.gbf_valid = false;
+      t.gpend = nullptr;
     }
     C.ensure_grad_buffer(L);
     hip_check(fill(L.grad, 1.f, 1, C.s()), "seed");
@@ -1367,9 +1439,13 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
     for (int i = (int)ctx->tape.size() - 1; i >= 0; --i) {
       const Rec& r = ctx->tape[i];
       TensorRec& out = ctx->tensors[r.out];
-      if (!out.live || out.gstate != G_VALID) continue;
+      if (!out.live) continue;
+      C.settle(out);  // its gradient is complete: nothing else contributes
+      if (out.gstate != G_VALID) continue;
       backward_rec(C, r);
     }
+    for (TensorRec& t : ctx->tensors)
+      if (t.live) C.settle(t);
   });
 }
 

@@ -50,7 +50,7 @@ class Gpt:
         for i in range(self.n_layer):
             p = f"h.{i}."
             h = layernorm(x, P[p + "ln_1.weight"], P[p + "ln_1.bias"])
-            qkv = linear(h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"])
+            qkv = linear(h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"], bf16_copy=True)
             a = causal_attention(qkv, self.n_head)
             x = add(x, linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"]))
             h = layernorm(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"])
