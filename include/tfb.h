@@ -168,6 +168,16 @@ int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y)
  * SoftmaxCrossEntropy] */
 int tfb_softmax_cross_entropy(tfb_ctx* ctx, tfb_tensor logits, const int32_t* dev_targets, int64_t n,
                               tfb_tensor* loss);
+/* tfb_softmax_cross_entropy with flags.  TFB_CE_GRAD_BF16_ONLY (bf16 variant):
+ * when the logits come from a contraction and nothing else reads them, their
+ * gradient is written only as the bf16 copy that the contraction's backward
+ * reads; the fp32 gradient of the logits is not kept (reading it gives
+ * TFB_ERR_STATE).  Every other gradient is unchanged.  Ignored in the fp32
+ * variant or when those conditions do not hold.  Unknown flags: TFB_ERR_ARG.
+ * [Autograd-1, "Ops": SoftmaxCrossEntropy] */
+#define TFB_CE_GRAD_BF16_ONLY 1
+int tfb_softmax_cross_entropy_ex(tfb_ctx* ctx, tfb_tensor logits, const int32_t* dev_targets, int64_t n, int flags,
+                                 tfb_tensor* loss);
 
 /* ---------------------------------------------------------------- autograd */
 

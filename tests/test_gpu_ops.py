@@ -353,6 +353,46 @@ def test_linear_bf16_copy_changes_nothing(ctx):
     ctx.set_precision("fp32")
 
 
+@pytest.mark.parametrize("prec", PRECS)
+def test_cross_entropy_bf16_only_logit_gradient(ctx, prec):
+    """With the bf16-only option, an LM head's gradients are those of the plain call:
+    bit-identical in the bf16 variant (the products read the same bf16 copy), and the
+    option is ignored in fp32.  The logits' own fp32 gradient is not kept (bf16 only);
+    logits with another reader keep the plain behaviour."""
+    V, C, rows = 1030, 64, 300
+    x, w = rnd(44, (rows, C)), rnd(45, (V, C), 0.2)
+    tg = S.random_ids(46, (rows,), V)
+    ctx.set_precision(prec)
+    res = []
+    for only in (False, True):
+        xt, wt = ctx.tensor(x.shape, x), ctx.tensor(w.shape, w)
+        logits = T.matmul_t(xt, wt)
+        loss = T.softmax_cross_entropy(logits, tg, bf16_grad_only=only)
+        ctx.backward(loss)
+        ctx.backward(loss)                                   # a second pass: leaf gradients add up
+        res.append([loss.numpy(), xt.grad(), wt.grad()])
+        if only and prec == "bf16":
+            with pytest.raises(T.TfbError):
+                logits.grad()
+        else:
+            res[-1].append(logits.grad())
+        ctx.tape_reset()
+        xt.release()
+        wt.release()
+    for a, b_ in zip(res[0], res[1]):
+        np.testing.assert_array_equal(a, b_)
+    # another reader of the logits: the option does not apply
+    xt, wt = ctx.tensor(x.shape, x), ctx.tensor(w.shape, w)
+    logits = T.matmul_t(xt, wt)
+    loss = T.add(T.softmax_cross_entropy(logits, tg, bf16_grad_only=True), T.sum_all(T.scale(logits, 1e-3)))
+    ctx.backward(loss)
+    assert np.isfinite(logits.grad()).all()
+    ctx.tape_reset()
+    xt.release()
+    wt.release()
+    ctx.set_precision("fp32")
+
+
 def test_no_grad_records_nothing(ctx):
     a = ctx.tensor((2, 3), rnd(40, (2, 3)))
     ctx.set_grad_enabled(False)

@@ -61,6 +61,7 @@ SIGNATURES = {
     "tfb_causal_softmax": [c_void_p, c_int32, P(c_int32)],
     "tfb_causal_attention": [c_void_p, c_int32, c_int, P(c_int32)],
     "tfb_softmax_cross_entropy": [c_void_p, c_int32, c_void_p, c_int64, P(c_int32)],
+    "tfb_softmax_cross_entropy_ex": [c_void_p, c_int32, c_void_p, c_int64, c_int32, P(c_int32)],
     "tfb_backward": [c_void_p, c_int32],
     "tfb_zero_grad": [c_void_p, P(c_int32), c_int],
     "tfb_tape_reset": [c_void_p],
@@ -344,9 +345,19 @@ def causal_attention(qkv: Tensor, heads: int) -> Tensor:
     return _out(qkv.ctx, _lib.tfb_causal_attention, qkv.h, int(heads))
 
 
-def softmax_cross_entropy(logits: Tensor, targets) -> Tensor:
+CE_GRAD_BF16_ONLY = 1
+
+
+def softmax_cross_entropy(logits: Tensor, targets, bf16_grad_only: bool = False) -> Tensor:
+    """Mean cross-entropy of softmax(logits) against targets.  bf16_grad_only (bf16
+    variant): logits produced by a contraction and read by nothing else get their
+    gradient only as the bf16 copy that contraction's backward reads; logits.grad()
+    is then unavailable."""
     ctx = logits.ctx
     d = ctx.device_ints(targets)
+    if bf16_grad_only:
+        return _out(ctx, _lib.tfb_softmax_cross_entropy_ex, logits.h, c_void_p(d.data_ptr()), d.numel(),
+                    CE_GRAD_BF16_ONLY)
     return _out(ctx, _lib.tfb_softmax_cross_entropy, logits.h, c_void_p(d.data_ptr()), d.numel())
 
 

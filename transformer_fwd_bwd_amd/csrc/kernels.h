@@ -102,6 +102,7 @@ size_t softmax_ce_workspace_bytes(int64_t rows);
 // logits rows have V valid columns at a row stride of ld >= V
 hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* targets, int64_t rows, int64_t V,
                           float* lse, float* loss, void* ws, hipStream_t s);
+// dl may be null when dlbf is given (and beta == 0): only the bf16 copy is written
 hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* targets, const float* lse,
                           const float* g_scalar, float* dl, uint16_t* dlbf, int64_t rows, int64_t V, float beta,
                           hipStream_t s);

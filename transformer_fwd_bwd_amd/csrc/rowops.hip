@@ -532,12 +532,14 @@ __global__ __launch_bounds__(NT) void ce_bwd_k(const float* __restrict__ logits,
   const float L = lse[r];
   const int t = tgt[r];
   const float* lr = logits + r * ld;
-  float* dr = dl + r * ld;
+  float* dr = dl ? dl + r * ld : nullptr;  // null: the bf16 copy alone
   uint16_t* br = dlbf ? dlbf + r * ld : nullptr;
   for (int64_t c = threadIdx.x; c < V; c += NT) {
     float v = gn * (expf(lr[c] - L) - (c == t ? 1.f : 0.f));
-    if (beta != 0.f) v += dr[c];
-    dr[c] = v;
+    if (dr) {
+      if (beta != 0.f) v += dr[c];
+      dr[c] = v;
+    }
     if (br) br[c] = bf16_bits(v);
   }
 }
@@ -615,7 +617,7 @@ __global__ __launch_bounds__(NT) void ce_bwd4_k(const float* __restrict__ logits
   const float L = lse[r];
   const int t = tgt[r];
   const f4* lr4 = reinterpret_cast<const f4*>(logits + r * ld);
-  f4* dr4 = reinterpret_cast<f4*>(dl + r * ld);
+  f4* dr4 = dl ? reinterpret_cast<f4*>(dl + r * ld) : nullptr;  // null: the bf16 copy alone
   u16x4* br4 = dlbf ? reinterpret_cast<u16x4*>(dlbf + r * ld) : nullptr;
   const int64_t V4 = V / 4;
   for (int64_t c = threadIdx.x; c < V4; c += 2 * NT) {
@@ -632,17 +634,21 @@ __global__ __launch_bounds__(NT) void ce_bwd4_k(const float* __restrict__ logits
       f4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = gn * (expf(x[u][e] - L) - (4 * i + e == t ? 1.f : 0.f));
-      if (beta != 0.f) v += dr4[i];
-      dr4[i] = v;
+      if (dr4) {
+        if (beta != 0.f) v += dr4[i];
+        dr4[i] = v;
+      }
       if (br4) br4[i] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
     }
   }
   const float* lr = logits + r * ld;
-  float* dr = dl + r * ld;
+  float* dr = dl ? dl + r * ld : nullptr;
   for (int64_t c = 4 * V4 + threadIdx.x; c < V; c += NT) {
     float v = gn * (expf(lr[c] - L) - (c == t ? 1.f : 0.f));
-    if (beta != 0.f) v += dr[c];
-    dr[c] = v;
+    if (dr) {
+      if (beta != 0.f) v += dr[c];
+      dr[c] = v;
+    }
     if (dlbf) dlbf[r * ld + c] = bf16_bits(v);
   }
 }
@@ -761,6 +767,7 @@ hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* target
                           const float* g_scalar, float* dl, uint16_t* dlbf, int64_t rows, int64_t V, float beta,
                           hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (!dl && (!dlbf || beta != 0.f)) return hipErrorInvalidValue;
   if (ld % 4 == 0 && aligned16(logits) && aligned16(dl) && (reinterpret_cast<uintptr_t>(dlbf) & 7) == 0)
     hipLaunchKernelGGL(ce_bwd4_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
                        rows, V, beta);

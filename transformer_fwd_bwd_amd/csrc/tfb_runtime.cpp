@@ -44,7 +44,8 @@ void hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) fail(TFB_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-enum GradState { G_NONE = 0, G_ZERO = 1, G_VALID = 2 };
+// G_BF16: the gradient exists only as its bf16 copy (gbf); no fp32 gradient is kept
+enum GradState { G_NONE = 0, G_ZERO = 1, G_VALID = 2, G_BF16 = 3 };
 
 struct TensorRec {
   bool live = false;
@@ -784,6 +785,17 @@ void backward_rec(Ctx& C, const Rec& r) {
     }
     case OP_SOFTMAX_CE: {
       TensorRec& lg = C.T(r.in[0]);
+      if ((r.i0 & TFB_CE_GRAD_BF16_ONLY) && lg.uses == 1 && !lg.leaf && !lg.gpend && lg.gstate != G_VALID &&
+          C.grad_read_as_bf16(lg)) {
+        // the logits' only gradient, read by their producer as bf16: that copy alone
+        uint16_t* dlb = C.twin_grad(lg);
+        hip_check(softmax_ce_bwd(lg.data, lg.stride(), static_cast<const int32_t*>(r.s0),
+                                 static_cast<const float*>(r.s1), g, nullptr, dlb, lg.rows(), lg.cols(), 0.f, s),
+                  "softmax_ce bwd");
+        lg.gstate = G_BF16;
+        lg.gbf_valid = true;
+        break;
+      }
       auto dl = C.gdst(r.in[0]);
       uint16_t* dlb = C.twin_grad(lg);
       hip_check(softmax_ce_bwd(lg.data, lg.stride(), static_cast<const int32_t*>(r.s0),
@@ -1396,7 +1408,13 @@ int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y)
 
 int tfb_softmax_cross_entropy(tfb_ctx* ctx, tfb_tensor logits, const int32_t* dev_targets, int64_t n,
                               tfb_tensor* loss) {
+  return tfb_softmax_cross_entropy_ex(ctx, logits, dev_targets, n, 0, loss);
+}
+
+int tfb_softmax_cross_entropy_ex(tfb_ctx* ctx, tfb_tensor logits, const int32_t* dev_targets, int64_t n, int flags,
+                                 tfb_tensor* loss) {
   return guarded([&] {
+    need((flags & ~TFB_CE_GRAD_BF16_ONLY) == 0, TFB_ERR_ARG, "unknown tfb_softmax_cross_entropy_ex flags");
     Ctx C(ctx);
     TensorRec& L = C.T(logits);
     need(loss != nullptr && dev_targets != nullptr, TFB_ERR_ARG, "null argument");
@@ -1417,6 +1435,7 @@ int tfb_softmax_cross_entropy(tfb_ctx* ctx, tfb_tensor logits, const int32_t* de
     Rec r{OP_SOFTMAX_CE};
     r.in[0] = logits, r.out = h;
     r.s0 = tg, r.s1 = lse;
+    r.i0 = flags;
     C.record(r);
     *loss = h;
   });
@@ -1430,6 +1449,7 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
     need(L.numel == 1, TFB_ERR_STATE, "backward() starts from a scalar loss");
     for (TensorRec& t : ctx->tensors) {
       if (t.live && !t.leaf && t.grad) t.gstate = G_ZERO;
+      if (t.gstate == G_BF16) t.gstate = t.grad ? G_ZERO : G_NONE;
       t.gbf_valid = false;
       t.gpend = nullptr;
     }
@@ -1441,7 +1461,7 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
       TensorRec& out = ctx->tensors[r.out];
       if (!out.live) continue;
       C.settle(out);  // its gradient is complete: nothing else contributes
-      if (out.gstate != G_VALID) continue;
+      if (out.gstate != G_VALID && out.gstate != G_BF16) continue;
       backward_rec(C, r);
     }
     for (TensorRec& t : ctx->tensors)

@@ -60,8 +60,10 @@ class Gpt:
         return matmul_t(xf, P["wte.weight"])
 
     def loss(self, inputs, targets):
+        """(mean cross-entropy, logits).  In the bf16 variant the logits' gradient exists
+        only as the bf16 copy the LM head's backward reads (it is not kept in fp32)."""
         logits = self.logits(inputs)
-        return softmax_cross_entropy(logits, targets), logits
+        return softmax_cross_entropy(logits, targets, bf16_grad_only=True), logits
 
     # ------------------------------------------------------------------ KV-cached inference
     # [GPT2-4, "Generation with KV cache"]: the prompt's keys and values are
