@@ -393,6 +393,49 @@ def test_cross_entropy_bf16_only_logit_gradient(ctx, prec):
     ctx.set_precision("fp32")
 
 
+@pytest.mark.parametrize("prec", PRECS)
+def test_bias_gradients_from_fused_column_sums(ctx, prec):
+    """[Autograd-1, "Backward pass"; "Ops": the bias Add's rule sums g over rows]: a
+    Linear's bias gradient taken from the column sums that the kernel finishing its
+    output gradient leaves behind -- a LayerNorm backward (residual stream) and a GELU
+    backward (the MLP) -- against the oracle.  1000 and 300 rows: several row slabs
+    with ragged ends."""
+    ctx.set_precision(prec)
+    for rows in (1000, 300):
+        xin, R = rnd(101, (rows, 64)), rnd(102, (rows, 128))
+        gam, bet = rnd(103, (64,), 0.5) + 1.0, rnd(104, (64,), 0.1)
+        W1, b1 = rnd(105, (64, 128), 0.1), rnd(106, (128,), 0.1)
+        W2, b2 = rnd(107, (128, 64), 0.1), rnd(108, (64,), 0.1)
+        gam2, bet2 = rnd(109, (64,), 0.5) + 1.0, rnd(110, (64,), 0.1)
+        arrs = dict(xin=xin, gam=gam, bet=bet, W1=W1, b1=b1, W2=W2, b2=b2, gam2=gam2, bet2=bet2, R=R)
+
+        def gpu(t):
+            x0 = T.tanh(t["xin"])
+            h = T.linear(T.layernorm(x0, t["gam"], t["bet"]), t["W1"], t["b1"])
+            a = T.gelu(h)                                     # b1: from the GELU backward's sums
+            x1 = T.add(x0, T.linear(a, t["W2"], t["b2"]))      # b2: from the LayerNorm backward's sums
+            y = T.layernorm(x1, t["gam2"], t["bet2"])
+            return T.sum_all(T.mul(T.linear(y, t["W1"], t["b1"]), t["R"]))
+
+        def ora(t):
+            x0 = E.tanh(t["xin"])
+            h = E.add(E.matmul(E.layernorm(x0, t["gam"], t["bet"]), t["W1"]), t["b1"])
+            x1 = E.add(x0, E.add(E.matmul(E.gelu(h), t["W2"]), t["b2"]))
+            y = E.layernorm(x1, t["gam2"], t["bet2"])
+            return E.sum_all(E.mul(E.add(E.matmul(y, t["W1"]), t["b1"]), t["R"]))
+
+        G = {k: ctx.tensor(v.shape, v) for k, v in arrs.items()}
+        ctx.backward(gpu(G))
+        O = {k: E.Tensor(v.astype(np.float64)) for k, v in arrs.items()}
+        ora(O).backward()
+        for k in ("b1", "b2", "W1", "W2", "xin", "gam", "bet"):
+            assert_close(G[k].grad(), O[k].grad, GRAD_TOL[prec], f"{k}.grad ({rows} rows)")
+        ctx.tape_reset()
+        for t in G.values():
+            t.release()
+    ctx.set_precision("fp32")
+
+
 def test_no_grad_records_nothing(ctx):
     a = ctx.tensor((2, 3), rnd(40, (2, 3)))
     ctx.set_grad_enabled(False)

@@ -134,6 +134,47 @@ __global__ __launch_bounds__(NT) void colsum4_stage1(const f4* __restrict__ g, i
   if (ty == 0 && c < cols4) partial[(int64_t)blockIdx.y * cols4 + c] = ((t + sh[0][tx]) + sh[1][tx]) + sh[2][tx];
 }
 
+// GELU backward over a [rows, cols4] float4 view that also takes the column sums
+// of its result (a Linear's bias gradient when this is that Linear's output
+// gradient): workgroups as in colsum4_stage1 (256 columns x a slab of rows, 4
+// interleaved row groups, 4 rows in flight per thread), each element written once
+// and added into its column's slab partial.
+__global__ __launch_bounds__(NT) void gelu_bwd_cols4_k(const f4* __restrict__ g, const f4* __restrict__ x,
+                                                      f4* __restrict__ d, u16x4* __restrict__ dbf, float beta,
+                                                      int64_t rows, int64_t cols4, int64_t rows_per,
+                                                      f4* __restrict__ partial) {
+  __shared__ f4 sh[3][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 64 + tx;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per;
+  const int64_t r1 = std::min(rows, r0 + rows_per);
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto one = [&](f4 gv, f4 xv, int64_t i) {
+    f4 v = {gv[0] * gelu_grad(xv[0]), gv[1] * gelu_grad(xv[1]), gv[2] * gelu_grad(xv[2]), gv[3] * gelu_grad(xv[3])};
+    if (beta != 0.f) v += d[i];
+    d[i] = v;
+    if (dbf) dbf[i] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
+    acc += v;
+  };
+  if (c < cols4) {
+    int64_t r = r0 + ty;
+    for (; r + 12 < r1; r += 16) {
+      f4 gv[4], xv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        gv[u] = g[(r + 4 * u) * cols4 + c];
+        xv[u] = x[(r + 4 * u) * cols4 + c];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) one(gv[u], xv[u], (r + 4 * u) * cols4 + c);
+    }
+    for (; r < r1; r += 4) one(g[r * cols4 + c], x[r * cols4 + c], r * cols4 + c);
+  }
+  if (ty > 0) sh[ty - 1][tx] = acc;
+  __syncthreads();
+  if (ty == 0 && c < cols4) partial[(int64_t)blockIdx.y * cols4 + c] = ((acc + sh[0][tx]) + sh[1][tx]) + sh[2][tx];
+}
+
 // out[c] (+)= sum over the partial rows; 64 columns x 16 partial-groups per workgroup
 __global__ __launch_bounds__(1024) void colsum_stage2(const float* __restrict__ partial, int nparts, int64_t cols,
                                                       float* __restrict__ out, float beta) {
@@ -339,6 +380,22 @@ static int64_t colsum4_parts(int64_t rows) { return std::min<int64_t>(256, std::
 
 size_t colsum_workspace_bytes(int64_t rows, int64_t cols) {
   return (size_t)std::max(colsum_parts(rows, cols), colsum4_parts(rows)) * cols * sizeof(float);
+}
+
+hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t rows,
+                         int64_t cols, float* dcol, void* ws, hipStream_t s, bool* dcol_written) {
+  *dcol_written = false;
+  float* partial = static_cast<float*>(ws);
+  if (rows < 128 || cols % 4 != 0 || !aligned16(g) || !aligned16(x) || !aligned16(d) || !aligned16(partial) ||
+      (reinterpret_cast<uintptr_t>(dbf) & 7) != 0)
+    return gelu_bwd(g, x, d, dbf, beta, rows * cols, s);
+  const int64_t parts = colsum4_parts(rows), rows_per = (rows + parts - 1) / parts, cols4 = cols / 4;
+  hipLaunchKernelGGL(gelu_bwd_cols4_k, dim3((unsigned)((cols4 + 63) / 64), (unsigned)parts), dim3(NT), 0, s,
+                     (const f4*)g, (const f4*)x, (f4*)d, (u16x4*)dbf, beta, rows, cols4, rows_per, (f4*)partial);
+  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, (int)parts, cols,
+                     dcol, 0.f);
+  *dcol_written = true;
+  return hipGetLastError();
 }
 
 hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s) {

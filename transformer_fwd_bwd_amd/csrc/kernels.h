@@ -68,6 +68,10 @@ hipError_t tanh_bwd(const float* g, const float* y, float* d, float beta, int64_
 // store, in the same layout, sparing a separate conversion pass.
 hipError_t gelu_fwd(const float* a, float* y, uint16_t* ybf, int64_t n, hipStream_t s);
 hipError_t gelu_bwd(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t n, hipStream_t s);
+// the same over [rows, cols], also writing dcol[c] = sum over rows of the result
+// where the row-slab path runs (*dcol_written); ws: colsum_workspace_bytes(rows, cols)
+hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t rows,
+                         int64_t cols, float* dcol, void* ws, hipStream_t s, bool* dcol_written);
 // out[c] = beta*out[c] + sum_r g[r*cols + c]; deterministic two-stage reduction
 size_t colsum_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s);
@@ -90,9 +94,12 @@ hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, 
 size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C);
 // dxbf (optional) receives the bf16 copy of the final dx.  With beta_dx != 0 the
 // earlier gradient is read from dx_src (null: dx itself) and the sum written to dx.
+// dxsum (optional, [C]) receives the column sums of the final dx where the fused
+// path runs; *dxsum_written says whether it did.
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
                          float* dx, const float* dx_src, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows,
-                         int64_t C, float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s);
+                         int64_t C, float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s,
+                         float* dxsum = nullptr, bool* dxsum_written = nullptr);
 // full == true: every element of the [rows, T] view is written (zeros where masked);
 // full == false: only the visible prefix of each row is touched.
 hipError_t causal_softmax_fwd(const float* x, float* p, int64_t rows, int64_t T, bool full, hipStream_t s);

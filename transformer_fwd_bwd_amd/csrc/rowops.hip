@@ -202,22 +202,25 @@ __global__ __launch_bounds__(NT) void ln_bwd_dx_k(const float* __restrict__ g, c
 // registers): dx = rstd (g*gamma - mean(g*gamma) - xhat mean(g*gamma*xhat)),
 // plus the dgamma / dbeta column partials of the rows this workgroup handles:
 // each lane keeps sum g*xhat and sum g for its float4 columns over its wave's
-// rows, the 4 waves are added in LDS in a fixed order, and part[block][0 | 1][C]
-// receives the result (reduced by ln_bwd_reduce).  A wave loads its rows two at
-// a time, so two rows' reads are in flight.
-template <int J>
+// rows, the 4 waves are added in LDS in a fixed order, and part[block][plane][C]
+// receives the result (reduced by ln_bwd_reduce).  With SUMDX a third plane holds
+// the column sums of the final dx (the bias gradient of a Linear whose output
+// gradient this is).  A wave loads its rows two at a time, so two rows' reads are
+// in flight.
+template <int J, bool SUMDX>
 __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, const f4* __restrict__ x,
                                                       const f4* __restrict__ gamma, const float* __restrict__ mean,
                                                       const float* __restrict__ rstd, f4* dx, const f4* dx_src,
                                                       u16x4* __restrict__ dxbf, f4* __restrict__ part, int64_t rows,
                                                       int C4, float beta_dx) {
-  __shared__ f4 sh[WAVES - 1][2][64 * J];
+  constexpr int NP = SUMDX ? 3 : 2;
+  __shared__ f4 sh[WAVES - 1][NP][64 * J];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t nw = (int64_t)gridDim.x * WAVES;
   const float invC = 1.f / (4 * C4);
-  f4 pa[J], pb[J];
+  f4 pa[J], pb[J], pc[J];
 #pragma unroll
-  for (int j = 0; j < J; ++j) pa[j] = pb[j] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < J; ++j) pa[j] = pb[j] = pc[j] = f4{0.f, 0.f, 0.f, 0.f};
   for (int64_t r0 = (int64_t)blockIdx.x * WAVES + w; r0 < rows; r0 += 2 * nw) {
     const int64_t rr[2] = {r0, r0 + nw};
     f4 xv[2][J], gv[2][J];
@@ -256,6 +259,7 @@ __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, 
           f4 v = rs * (dg[j] - m1 - xh[j] * m2);
           if (beta_dx != 0.f) v += dx_src[r * C4 + c];  // may be dx itself: read before the write
           dx[r * C4 + c] = v;
+          if constexpr (SUMDX) pc[j] += v;
           if (dxbf) dxbf[r * C4 + c] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
         }
       }
@@ -266,6 +270,7 @@ __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, 
     for (int j = 0; j < J; ++j) {
       sh[w - 1][0][lane + 64 * j] = pa[j];
       sh[w - 1][1][lane + 64 * j] = pb[j];
+      if constexpr (SUMDX) sh[w - 1][2][lane + 64 * j] = pc[j];
     }
   }
   __syncthreads();
@@ -274,14 +279,16 @@ __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, 
     for (int j = 0; j < J; ++j) {
       const int c = lane + 64 * j;
       if (c < C4) {
-        f4 a = pa[j], b = pb[j];
+        f4 a = pa[j], b = pb[j], d = pc[j];
 #pragma unroll
         for (int i = 0; i < WAVES - 1; ++i) {
           a += sh[i][0][c];
           b += sh[i][1][c];
+          if constexpr (SUMDX) d += sh[i][2][c];
         }
-        part[((int64_t)blockIdx.x * 2) * C4 + c] = a;
-        part[((int64_t)blockIdx.x * 2 + 1) * C4 + c] = b;
+        part[((int64_t)blockIdx.x * NP) * C4 + c] = a;
+        part[((int64_t)blockIdx.x * NP + 1) * C4 + c] = b;
+        if constexpr (SUMDX) part[((int64_t)blockIdx.x * NP + 2) * C4 + c] = d;
       }
     }
   }
@@ -318,34 +325,39 @@ __global__ __launch_bounds__(NT) void ln_bwd_cols_k(const float* __restrict__ g,
   part[((int64_t)blockIdx.y * 2 + 1) * C + c] = b;
 }
 
-// out_a[c] (+)= sum_p part[p][0][c], out_b[c] (+)= sum_p part[p][1][c]; 64 columns x 16 groups per workgroup
-__global__ __launch_bounds__(1024) void ln_bwd_reduce(const float* __restrict__ part, int nparts, int C,
+// out_a[c] (+)= sum_p part[p][0][c], out_b[c] (+)= sum_p part[p][1][c], and with
+// dxsum (np == 3) dxsum[c] = sum_p part[p][2][c]
+__global__ __launch_bounds__(1024) void ln_bwd_reduce(const float* __restrict__ part, int nparts, int np, int C,
                                                       float* __restrict__ dgamma, float* __restrict__ dbeta,
-                                                      float beta_dg, float beta_db) {
+                                                      float* __restrict__ dxsum, float beta_dg, float beta_db) {
   // 16 columns x 64 partial groups per workgroup; the groups are added in a fixed order
-  __shared__ float sa[64][17], sb[64][17];
+  __shared__ float sa[64][17], sb[64][17], sd[64][17];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int c = blockIdx.x * 16 + tx;
-  float a = 0.f, b = 0.f;
+  float a = 0.f, b = 0.f, d = 0.f;
   if (c < C) {
     for (int p = ty; p < nparts; p += 64) {
-      a += part[((int64_t)p * 2) * C + c];
-      b += part[((int64_t)p * 2 + 1) * C + c];
+      a += part[((int64_t)p * np) * C + c];
+      b += part[((int64_t)p * np + 1) * C + c];
+      if (dxsum) d += part[((int64_t)p * np + 2) * C + c];
     }
   }
   sa[ty][tx] = a;
   sb[ty][tx] = b;
+  sd[ty][tx] = d;
   __syncthreads();
   if (ty == 0 && c < C) {
-    float ra = 0.f, rb = 0.f;
+    float ra = 0.f, rb = 0.f, rd = 0.f;
     for (int i = 0; i < 64; ++i) {
       ra += sa[i][tx];
       rb += sb[i][tx];
+      rd += sd[i][tx];
     }
     if (beta_dg != 0.f) ra += dgamma[c];
     if (beta_db != 0.f) rb += dbeta[c];
     dgamma[c] = ra;
     dbeta[c] = rb;
+    if (dxsum) dxsum[c] = rd;
   }
 }
 
@@ -677,31 +689,44 @@ hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, 
 }
 
 size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C) {
-  return (size_t)std::max<int64_t>(ln_bwd_parts(rows), ln_fused_blocks(rows)) * 2 * C * sizeof(float);
+  return (size_t)std::max<int64_t>(ln_bwd_parts(rows), ln_fused_blocks(rows)) * 3 * C * sizeof(float);
 }
 
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
                          float* dx, const float* dx_src, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows,
-                         int64_t C, float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s) {
+                         int64_t C, float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s,
+                         float* dxsum, bool* dxsum_written) {
+  if (dxsum_written) *dxsum_written = false;
   if (C <= 0) return hipSuccess;
   if (!dx_src) dx_src = dx;
   float* part = static_cast<float*>(ws);
-  int parts = 0;
+  int parts = 0, np = 2;
   if (rows > 0 && C % 4 == 0 && C <= 1024 && aligned16(g) && aligned16(x) && aligned16(gamma) && aligned16(dx) &&
       aligned16(dx_src) && aligned16(part) && (reinterpret_cast<uintptr_t>(dxbf) & 7) == 0) {
     // dx (and its bf16 copy) and the column partials in one pass over g and x
     const int C4 = (int)(C / 4);
     const int64_t blocks = ln_fused_blocks(rows);
-    if (C4 <= 64)
-      hipLaunchKernelGGL(ln_bwd_fused4_k<1>, dim3((unsigned)blocks), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
-                         (const f4*)gamma, mean, rstd, (f4*)dx, (const f4*)dx_src, (u16x4*)dxbf, (f4*)part, rows, C4,
-                         beta_dx);
-    else
-      hipLaunchKernelGGL(ln_bwd_fused4_k<4>, dim3((unsigned)blocks), dim3(NT), 0, s, (const f4*)g, (const f4*)x,
-                         (const f4*)gamma, mean, rstd, (f4*)dx, (const f4*)dx_src, (u16x4*)dxbf, (f4*)part, rows, C4,
-                         beta_dx);
+    const dim3 grid((unsigned)blocks), block(NT);
+    const f4 *g4 = (const f4*)g, *x4 = (const f4*)x, *gm4 = (const f4*)gamma, *src4 = (const f4*)dx_src;
+    if (dxsum) {
+      np = 3;
+      if (C4 <= 64)
+        hipLaunchKernelGGL((ln_bwd_fused4_k<1, true>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
+                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+      else
+        hipLaunchKernelGGL((ln_bwd_fused4_k<4, true>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
+                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+    } else {
+      if (C4 <= 64)
+        hipLaunchKernelGGL((ln_bwd_fused4_k<1, false>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
+                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+      else
+        hipLaunchKernelGGL((ln_bwd_fused4_k<4, false>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
+                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+    }
     parts = (int)blocks;
   } else {
+    dxsum = nullptr;  // not produced on this path
     if (rows > 0 && beta_dx != 0.f && dx_src != dx) {  // the kernels below accumulate into dx itself
       const hipError_t e = hipMemcpyAsync(dx, dx_src, (size_t)(rows * C) * sizeof(float), hipMemcpyDeviceToDevice, s);
       if (e != hipSuccess) return e;
@@ -723,8 +748,9 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + 15) / 16)), dim3(1024), 0, s, part, parts, (int)C, dgamma,
-                     dbeta, beta_dg, beta_db);
+  hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + 15) / 16)), dim3(1024), 0, s, part, parts, np, (int)C,
+                     dgamma, dbeta, dxsum, beta_dg, beta_db);
+  if (dxsum_written) *dxsum_written = dxsum != nullptr;
   return hipGetLastError();
 }
 

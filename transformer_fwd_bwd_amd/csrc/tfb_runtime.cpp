@@ -64,6 +64,11 @@ struct TensorRec {
   bool bf_valid = false;
   uint16_t* gbf = nullptr;
   bool gbf_valid = false;
+  // column sums (over every row of the [rows, cols] view) of the finished gradient,
+  // left by the kernel that wrote it: a Linear reading this as its output gradient
+  // takes its bias gradient from here
+  float* gcol = nullptr;
+  bool gcol_valid = false;
 
   int64_t ld = 0;  // row stride of the last dim when rows are padded (0: dense)
   int uses = 0;    // ops on the tape that read this tensor
@@ -270,6 +275,7 @@ struct Ctx {
     settle(t);
     ensure_grad_buffer(t);
     t.gbf_valid = false;
+    t.gcol_valid = false;
     if (t.gstate == G_VALID) return {t.grad, 1.f};
     t.gstate = G_VALID;
     return {t.grad, 0.f};
@@ -290,6 +296,7 @@ struct Ctx {
       t.gpend = nullptr;
       t.gstate = G_VALID;
       t.gbf_valid = false;
+      t.gcol_valid = false;
       return {t.grad, 1.f, src};
     }
     const auto d = gdst(h);
@@ -305,6 +312,7 @@ struct Ctx {
     hip_check(axpby(t.grad, src, 1.f, 0.f, t.numel, s()), "gradient copy");
     t.gstate = G_VALID;
     t.gbf_valid = false;
+    t.gcol_valid = false;
   }
 
   // x's gradient so far is the finished gradient of `out` (a residual
@@ -337,6 +345,13 @@ struct Ctx {
     if (!bf16_mode()) return nullptr;
     if (!t.gbf) t.gbf = alloc_bf16(t);
     return t.gbf;
+  }
+
+  // buffer for t's gradient column sums (non-leaf tensors only)
+  float* gcol_buf(TensorRec& t) {
+    if (t.leaf || t.cols() <= 0) return nullptr;
+    if (!t.gcol) t.gcol = static_cast<float*>(c->arena.alloc_step((size_t)t.cols() * sizeof(float)));
+    return t.gcol;
   }
 
   // bf16 copy of a tensor's data, converted once and reused until the data changes
@@ -393,6 +408,8 @@ struct Ctx {
     x.gstate = G_VALID;
     x.gbf = out.gbf_valid ? out.gbf : nullptr;
     x.gbf_valid = out.gbf_valid;
+    x.gcol = out.gcol_valid && x.cols() == out.cols() ? out.gcol : nullptr;
+    x.gcol_valid = x.gcol != nullptr;
     return true;
   }
 
@@ -582,7 +599,18 @@ void backward_rec(Ctx& C, const Rec& r) {
       TensorRec& a = C.T(r.in[0]);
       auto da = C.gdst(r.in[0]);
       uint16_t* db = C.twin_grad(a);
-      hip_check(gelu_bwd(g, a.data, da.first, db, da.second, out.numel, s), "gelu bwd");
+      float* dcol = a.padded() ? nullptr : C.gcol_buf(a);
+      if (dcol) {  // with the column sums a reading Linear takes as its bias gradient
+        size_t mark = C.c->arena.hi;
+        void* ws = C.scratch(colsum_workspace_bytes(a.rows(), a.cols()));
+        bool written = false;
+        hip_check(gelu_bwd_cols(g, a.data, da.first, db, da.second, a.rows(), a.cols(), dcol, ws, s, &written),
+                  "gelu bwd");
+        C.c->arena.hi = mark;
+        a.gcol_valid = written;
+      } else {
+        hip_check(gelu_bwd(g, a.data, da.first, db, da.second, out.numel, s), "gelu bwd");
+      }
       if (db) a.gbf_valid = true;
       break;
     }
@@ -601,10 +629,14 @@ void backward_rec(Ctx& C, const Rec& r) {
       gemm_tn(C, op_data(C, x), go, dw.first, K, rows, N, dw.second);   // dw = x^T @ g
       if (r.op == OP_LINEAR) {
         auto db = C.gdst(r.in[2]);
-        size_t mark = C.c->arena.hi;
-        void* ws = C.scratch(colsum_workspace_bytes(rows, N));
-        hip_check(colsum(g, rows, N, db.first, db.second, ws, s), "linear bias bwd");
-        C.c->arena.hi = mark;
+        if (out.gcol_valid && out.cols() == N) {  // summed by the kernel that finished g
+          hip_check(axpby(db.first, out.gcol, 1.f, db.second, N, s), "linear bias bwd");
+        } else {
+          size_t mark = C.c->arena.hi;
+          void* ws = C.scratch(colsum_workspace_bytes(rows, N));
+          hip_check(colsum(g, rows, N, db.first, db.second, ws, s), "linear bias bwd");
+          C.c->arena.hi = mark;
+        }
       }
       break;
     }
@@ -630,13 +662,18 @@ void backward_rec(Ctx& C, const Rec& r) {
       // the bf16 copy of dx serves the contractions when this is the gradient's last
       // contribution (a later one invalidates it); a residual-stream gradient is one
       uint16_t* dxb = x.leaf ? nullptr : C.twin_grad(x);
+      // and its column sums: the bias gradient of a Linear whose output this gradient also is
+      float* dxs = C.gcol_buf(x);
       size_t mark = C.c->arena.hi;
       void* ws = C.scratch(layernorm_bwd_workspace_bytes(rows, Cc));
+      bool summed = false;
       hip_check(layernorm_bwd(g, x.data, gm.data, static_cast<float*>(r.s0), static_cast<float*>(r.s1), dx.dst,
-                              dx.src, dxb, dg.first, db.first, rows, Cc, dx.beta, dg.second, db.second, ws, s),
+                              dx.src, dxb, dg.first, db.first, rows, Cc, dx.beta, dg.second, db.second, ws, s, dxs,
+                              &summed),
                 "layernorm bwd");
       C.c->arena.hi = mark;
       if (dxb) x.gbf_valid = true;
+      x.gcol_valid = summed;
       break;
     }
     case OP_EMBEDDING: {
@@ -1451,6 +1488,7 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
       if (t.live && !t.leaf && t.grad) t.gstate = G_ZERO;
       if (t.gstate == G_BF16) t.gstate = t.grad ? G_ZERO : G_NONE;
       t.gbf_valid = false;
+      t.gcol_valid = false;
       t.gpend = nullptr;
     }
     C.ensure_grad_buffer(L);
