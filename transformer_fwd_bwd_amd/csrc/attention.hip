@@ -350,19 +350,25 @@ __global__ __launch_bounds__(NT, 2) void attn_dq_k(AttnArgs a) {
           dp[kt] = mfma(frag_r<HS>(Vs[buf], 32 * kt + l32, s, h), df[s], dp[kt]);
         }
       }
-      // dS^T = P^T (dP^T - D); a block every query of the wave sees whole needs no mask
+      // dS^T = P^T (dP^T - D); a block every query of the wave sees whole needs no
+      // mask.  The test is wave-uniform: one scalar branch per block, then a
+      // straight loop either way.
       const bool full = kv0 + KVB - 1 <= qw && kv0 + KVB <= a.T;
+      if (full) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fexp2(fmaf(st[kt][r], sc, -lse));
-          if (!full) {
+          for (int r = 0; r < 16; ++r) st[kt][r] = fexp2(fmaf(st[kt][r], sc, -lse)) * (dp[kt][r] - Dq);
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 32 * kt + acc_row(r, h);
-            p = (key <= q && key < a.T) ? p : 0.f;
+            const float p = fexp2(fmaf(st[kt][r], sc, -lse));
+            st[kt][r] = (key <= q && key < a.T) ? p * (dp[kt][r] - Dq) : 0.f;
           }
-          st[kt][r] = p * (dp[kt][r] - Dq);
-        }
+      }
 #pragma unroll
       for (int s = 0; s < KVB / 16; ++s) {
         const bf16x8 sb = pack8(st[s >> 1], 8 * (s & 1));
@@ -469,34 +475,51 @@ __global__ __launch_bounds__(NT, 2) void attn_dkv_k(AttnArgs a) {
       // P and dS with queries in registers, this lane's key in the column; the
       // saved statistics of 4 consecutive query rows come in one 16-byte read.
       // A block whose every query sees every key of the wave needs no mask.
+      // The test is wave-uniform: one scalar branch per block, then a straight
+      // loop.  Each 32-query half is finished (P, dS, and its dV / dK products)
+      // before the next, so only one half's fp32 P and dS are live at a time.
       const bool full = qb >= kw + 31 && qb + KVB <= a.T && kw + 32 <= a.T;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < 2; ++qt) {
+        if (full) {
 #pragma unroll
-        for (int r4 = 0; r4 < 16; r4 += 4) {
-          const int qi0 = 32 * qt + acc_row(r4, h);
-          const f4 L4 = *reinterpret_cast<const f4*>(&Ls[buf][qi0]);
-          const f4 D4 = *reinterpret_cast<const f4*>(&Dd[buf][qi0]);
+          for (int r4 = 0; r4 < 16; r4 += 4) {
+            const int qi0 = 32 * qt + acc_row(r4, h);
+            const f4 L4 = *reinterpret_cast<const f4*>(&Ls[buf][qi0]);
+            const f4 D4 = *reinterpret_cast<const f4*>(&Dd[buf][qi0]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = r4 + e;
-            float p = fexp2(fmaf(st[qt][r], sc, -L4[e]));
-            if (!full) {
-              const int qq = qb + qi0 + e;
-              p = (key <= qq && qq < a.T && key < a.T) ? p : 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int r = r4 + e;
+              const float p = fexp2(fmaf(st[qt][r], sc, -L4[e]));
+              st[qt][r] = p;
+              dp[qt][r] = p * (dp[qt][r] - D4[e]);
             }
-            st[qt][r] = p;
-            dp[qt][r] = p * (dp[qt][r] - D4[e]);
+          }
+        } else {
+#pragma unroll
+          for (int r4 = 0; r4 < 16; r4 += 4) {
+            const int qi0 = 32 * qt + acc_row(r4, h);
+            const f4 L4 = *reinterpret_cast<const f4*>(&Ls[buf][qi0]);
+            const f4 D4 = *reinterpret_cast<const f4*>(&Dd[buf][qi0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = r4 + e, qq = qb + qi0 + e;
+              const bool vis = key <= qq && qq < a.T && key < a.T;
+              const float p = vis ? fexp2(fmaf(st[qt][r], sc, -L4[e])) : 0.f;
+              st[qt][r] = p;
+              dp[qt][r] = p * (dp[qt][r] - D4[e]);
+            }
           }
         }
 #pragma unroll
-      for (int s = 0; s < KVB / 16; ++s) {
-        const bf16x8 pb = pack8(st[s >> 1], 8 * (s & 1));
-        const bf16x8 db = pack8(dp[s >> 1], 8 * (s & 1));
+        for (int s = 2 * qt; s < 2 * qt + 2; ++s) {
+          const bf16x8 pb = pack8(st[qt], 8 * (s & 1));
+          const bf16x8 db = pack8(dp[qt], 8 * (s & 1));
 #pragma unroll
-        for (int i = 0; i < HS / 32; ++i) {
-          dv[i] = mfma(frag_tr<HS>(Ds[buf], 32 * i, s, lane), pb, dv[i]);
-          dk[i] = mfma(frag_tr<HS>(Qs[buf], 32 * i, s, lane), db, dk[i]);
+          for (int i = 0; i < HS / 32; ++i) {
+            dv[i] = mfma(frag_tr<HS>(Ds[buf], 32 * i, s, lane), pb, dv[i]);
+            dk[i] = mfma(frag_tr<HS>(Qs[buf], 32 * i, s, lane), db, dk[i]);
+          }
         }
       }
     }
