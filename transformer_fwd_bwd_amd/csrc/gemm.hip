@@ -744,8 +744,9 @@ Plan make_plan(const GemmArgs& g) {
   // K split: the workgroups resident at once (slots) run in rounds, so a tile
   // count just past a multiple of the slots wastes most of a round.  Pick the
   // split that minimizes rounds x (k-tiles per item) plus the partials'
-  // traffic (written and read once more by the reduction, ~5 TB/s), with at
-  // least 512 k per item.
+  // traffic (written and read once more by the reduction, priced at 2.5 TB/s:
+  // it competes with the product's own traffic; 5 TB/s chose splits 7% slower
+  // on the GPT-2 dW products), with at least 512 k per item.
   p.splits = 1;
   if (g.causal_a == CAUSAL_NONE && !g.causal_out && g.K >= 1024) {
     const int64_t slots = 256 * (p.bk == 32 ? 3 : 2);
@@ -756,7 +757,7 @@ Plan make_plan(const GemmArgs& g) {
       if (sp > 1 && g.K / sp < 512) break;
       const int64_t items = tiles * sp;
       const double rounds = (double)((items + slots - 1) / slots);
-      const double t = rounds * ((double)g.K / sp) * tile_s_per_k + (sp > 1 ? (sp + 1) * out_bytes / 5.0e12 : 0.0);
+      const double t = rounds * ((double)g.K / sp) * tile_s_per_k + (sp > 1 ? (sp + 1) * out_bytes / 2.5e12 : 0.0);
       if (sp == 1 || t < best * 0.97) best = t, p.splits = sp;
     }
   }
