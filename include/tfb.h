@@ -130,6 +130,13 @@ int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tenso
  * value and is ignored in the fp32 variant.  Unknown flags: TFB_ERR_ARG.
  * [GPT2-4, "Loading the weights": Linear weights stored [in, out]] */
 #define TFB_OUT_BF16_COPY 1
+/* y = r + (x @ w + b): a Linear and the residual Add that follows it, with the
+ * Add done in the product's epilogue (r is read there, once).  r has the
+ * output's shape [rows(x), cols(w)].  One op on the tape; its backward gives r
+ * the output's gradient and x, w, b the Linear's gradients.
+ * [Autograd-1, "Ops": MatMul, the bias Add and Add; GPT2-4, "Loading the
+ * weights": the residual stream x = x + attn(ln_1(x)), x = x + mlp(ln_2(x))] */
+int tfb_linear_residual(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor r, tfb_tensor* y);
 int tfb_linear_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int flags, tfb_tensor* y);
 /* Per row over the last dim: (x - mean)/sqrt(var + eps) * gamma + beta with the
  * biased variance.  [Autograd-1, table of ops: LayerNorm] */

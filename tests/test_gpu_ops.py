@@ -49,6 +49,43 @@ def test_linear_is_matmul_plus_bias(ctx, prec):
           [rnd(5, (300, 200)), rnd(6, (200, 260), 0.1), rnd(7, (260,))], (300, 260))
 
 
+@pytest.mark.parametrize("prec", PRECS)
+def test_linear_with_residual(ctx, prec):
+    """[Autograd-1, "Ops": MatMul, bias Add, Add]: r + (x @ w + b) as one op, ragged in
+    every dimension, against the oracle's three ops; every input's gradient."""
+    def gpu(x, w, b, r):
+        return T.linear(x, w, b, residual=r)
+
+    def ora(x, w, b, r):
+        return E.add(r, E.add(E.matmul(x, w), b))
+    check(ctx, prec, gpu, ora, [rnd(111, (3, 100, 200)), rnd(112, (200, 260), 0.1), rnd(113, (260,)),
+                                rnd(114, (3, 100, 260))], (3, 100, 260))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_linear_residual_is_input(ctx, prec):
+    """The residual is the product's own input: both gradient contributions reach it."""
+    def gpu(x, w, b):
+        return T.linear(x, w, b, residual=x)
+
+    def ora(x, w, b):
+        return E.add(x, E.add(E.matmul(x, w), b))
+    check(ctx, prec, gpu, ora, [rnd(115, (150, 96)), rnd(116, (96, 96), 0.1), rnd(117, (96,))], (150, 96))
+
+
+@pytest.mark.parametrize("N", [128, 130])
+def test_linear_residual_long_k_split(ctx, N):
+    """A long reduction takes the K-split path: the residual is added by the split
+    reduction (float4 and element forms)."""
+    def gpu(x, w, b, r):
+        return T.linear(x, w, b, residual=r)
+
+    def ora(x, w, b, r):
+        return E.add(r, E.add(E.matmul(x, w), b))
+    check(ctx, "fp32", gpu, ora, [rnd(118, (200, 3000)), rnd(119, (3000, N), 0.02), rnd(120, (N,)),
+                                  rnd(121, (200, N))], (200, N))
+
+
 def test_linear_long_k_split(ctx):
     # a long reduction (the dW contractions of the GPT have K = 8192) takes the split-K path
     check(ctx, "fp32", T.linear, lambda x, w, b: E.add(E.matmul(x, w), b),

@@ -51,6 +51,7 @@ SIGNATURES = {
     "tfb_matmul_t": [c_void_p, c_int32, c_int32, P(c_int32)],
     "tfb_linear": [c_void_p, c_int32, c_int32, c_int32, P(c_int32)],
     "tfb_linear_ex": [c_void_p, c_int32, c_int32, c_int32, c_int32, P(c_int32)],
+    "tfb_linear_residual": [c_void_p, c_int32, c_int32, c_int32, c_int32, P(c_int32)],
     "tfb_layernorm": [c_void_p, c_int32, c_int32, c_int32, c_float, P(c_int32)],
     "tfb_embedding": [c_void_p, c_int32, c_void_p, c_int64, c_int64, P(c_int32)],
     "tfb_narrow": [c_void_p, c_int32, c_int64, c_int64, P(c_int32)],
@@ -299,9 +300,14 @@ def matmul_t(x: Tensor, w: Tensor) -> Tensor:
 OUT_BF16_COPY = 1
 
 
-def linear(x: Tensor, w: Tensor, b: Tensor, bf16_copy: bool = False) -> Tensor:
-    """x @ w + b.  bf16_copy: the product also writes the output's bf16 copy (bf16
-    variant), for an output that a contraction or the attention kernels read next."""
+def linear(x: Tensor, w: Tensor, b: Tensor, bf16_copy: bool = False, residual: Tensor = None) -> Tensor:
+    """x @ w + b (+ residual).  bf16_copy: the product also writes the output's bf16
+    copy (bf16 variant), for an output that a contraction or the attention kernels
+    read next.  residual: added in the product's epilogue (one op on the tape)."""
+    if residual is not None:
+        if bf16_copy:
+            raise ValueError("linear: bf16_copy and residual are not combined")
+        return _out(x.ctx, _lib.tfb_linear_residual, x.h, w.h, b.h, residual.h)
     if bf16_copy:
         return _out(x.ctx, _lib.tfb_linear_ex, x.h, w.h, b.h, OUT_BF16_COPY)
     return _out(x.ctx, _lib.tfb_linear, x.h, w.h, b.h)

@@ -44,6 +44,9 @@ struct GemmArgs {
   bool a_bf16 = false, b_bf16 = false;
   // optional bf16 copy (round to nearest even) of the final C, same layout and ldc
   uint16_t* Cbf = nullptr;
+  // optional residual added to the result, same layout and ldc as C (batch 1):
+  // C = alpha A B + bias + beta C + resid
+  const float* resid = nullptr;
 };
 
 size_t gemm_workspace_bytes(const GemmArgs& g);

@@ -108,11 +108,12 @@ enum OpKind {
   OP_ATTENTION,
   OP_SOFTMAX_CE,
   OP_COMPACT,  // dense copy of a row-padded tensor (inserted by the library)
+  OP_LINEAR_RES,  // x @ w + b + r: a Linear and the residual Add that follows it
 };
 
 struct Rec {
   OpKind op;
-  int in[3] = {-1, -1, -1};
+  int in[4] = {-1, -1, -1, -1};
   int out = -1;
   float f = 0.f;
   int64_t i0 = 0, i1 = 0, i2 = 0, i3 = 0;
@@ -395,7 +396,8 @@ struct Ctx {
     if (!bf16_mode() || t.producer < 0 || t.producer >= (int)c->tape.size()) return false;
     const Rec& p = c->tape[t.producer];
     if (&c->tensors[p.out] != &t) return false;
-    return p.op == OP_LINEAR || p.op == OP_MATMUL || p.op == OP_MATMUL_T || (p.op == OP_ATTENTION && p.i1 == 1);
+    return p.op == OP_LINEAR || p.op == OP_LINEAR_RES || p.op == OP_MATMUL || p.op == OP_MATMUL_T ||
+           (p.op == OP_ATTENTION && p.i1 == 1);
   }
 
   // An op output read by exactly one op (this one, during its backward) whose
@@ -508,12 +510,12 @@ void set_b(GemmArgs& g, Opnd o) {
 
 // y[rows, N] = x[rows, K] @ w[K, N] (+ bias)
 void gemm_nn(Ctx& C, Opnd x, Opnd w, float* y, int64_t rows, int64_t K, int64_t N, float beta, const float* bias,
-             int64_t lda = -1, uint16_t* ybf = nullptr) {
+             int64_t lda = -1, uint16_t* ybf = nullptr, const float* resid = nullptr) {
   GemmArgs g = C.gemm_base();
   g.M = (int)rows, g.N = (int)N, g.K = (int)K;
   set_a(g, x), g.lda = lda < 0 ? K : lda;
   set_b(g, w), g.ldb = N;
-  g.C = y, g.ldc = N, g.Cbf = ybf;
+  g.C = y, g.ldc = N, g.Cbf = ybf, g.resid = resid;
   g.beta = beta, g.bias = bias;
   C.run_gemm(g);
 }
@@ -614,6 +616,15 @@ void backward_rec(Ctx& C, const Rec& r) {
       if (db) a.gbf_valid = true;
       break;
     }
+    case OP_LINEAR_RES: {
+      // the residual input's gradient is the output's gradient itself
+      TensorRec& res = C.T(r.in[3]);
+      if (!(C.share_grad(res, out) || C.defer_grad(res, out))) {
+        auto dr = C.gdst(r.in[3]);
+        hip_check(axpby(dr.first, g, 1.f, dr.second, res.numel, s), "residual bwd");
+      }
+    }
+      [[fallthrough]];
     case OP_MATMUL:
     case OP_LINEAR: {
       TensorRec& x = C.T(r.in[0]);
@@ -627,7 +638,7 @@ void backward_rec(Ctx& C, const Rec& r) {
       if (dxb) x.gbf_valid = true;
       auto dw = C.gdst(r.in[1]);
       gemm_tn(C, op_data(C, x), go, dw.first, K, rows, N, dw.second);   // dw = x^T @ g
-      if (r.op == OP_LINEAR) {
+      if (r.op != OP_MATMUL) {
         auto db = C.gdst(r.in[2]);
         if (out.gcol_valid && out.cols() == N) {  // summed by the kernel that finished g
           hip_check(axpby(db.first, out.gcol, 1.f, db.second, N, s), "linear bias bwd");
@@ -1154,11 +1165,12 @@ int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
 }
 
 static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y, OpKind kind,
-                       bool bf_out = false) {
+                       bool bf_out = false, tfb_tensor res = -1) {
   return guarded([&] {
     Ctx C(ctx);
     x = C.dense_in(x), w = C.dense_in(w);
-    if (kind == OP_LINEAR) b = C.dense_in(b);
+    if (kind != OP_MATMUL && kind != OP_MATMUL_T) b = C.dense_in(b);
+    if (kind == OP_LINEAR_RES) res = C.dense_in(res);
     TensorRec& X = C.T(x);
     TensorRec& W = C.T(w);
     need(y != nullptr, TFB_ERR_ARG, "null output");
@@ -1173,10 +1185,18 @@ static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, t
       N = W.shape[1];
     }
     const float* bias = nullptr;
-    if (kind == OP_LINEAR) {
+    if (kind == OP_LINEAR || kind == OP_LINEAR_RES) {
       TensorRec& Bv = C.T(b);
       need(Bv.numel == N && Bv.ndim == 1, TFB_ERR_SHAPE, "linear bias must be [" + std::to_string(N) + "]");
       bias = Bv.data;
+    }
+    const float* rd = nullptr;
+    if (kind == OP_LINEAR_RES) {
+      TensorRec& R = C.T(res);
+      need(R.numel == X.rows() * N && R.cols() == N, TFB_ERR_SHAPE,
+           "residual must have the output's shape: " + shape_str(R) + " for [" + std::to_string(X.rows()) + ", " +
+               std::to_string(N) + "]");
+      rd = R.data;
     }
     check_gemm_dims(rows, K, N);
     std::vector<int64_t> shp = shape_vec(X);
@@ -1194,10 +1214,11 @@ static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, t
     if (kind == OP_MATMUL_T)
       gemm_nt(C, xo, wo, yd, rows, K, N, 0.f, ld ? ld : N, yb);
     else
-      gemm_nn(C, xo, wo, yd, rows, K, N, 0.f, bias, -1, yb);
+      gemm_nn(C, xo, wo, yd, rows, K, N, 0.f, bias, -1, yb, rd);
     if (yb) ctx->tensors[h].bf_valid = true;
     Rec r{kind};
-    r.in[0] = x, r.in[1] = w, r.in[2] = kind == OP_LINEAR ? b : -1, r.out = h;
+    r.in[0] = x, r.in[1] = w, r.in[2] = (kind == OP_LINEAR || kind == OP_LINEAR_RES) ? b : -1, r.out = h;
+    if (kind == OP_LINEAR_RES) r.in[3] = res;
     C.record(r);
     *y = h;
   });
@@ -1211,6 +1232,10 @@ int tfb_matmul_t(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y) {
 }
 int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y) {
   return matmul_impl(ctx, x, w, b, y, OP_LINEAR);
+}
+
+int tfb_linear_residual(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor r, tfb_tensor* y) {
+  return matmul_impl(ctx, x, w, b, y, OP_LINEAR_RES, false, r);
 }
 
 int tfb_linear_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int flags, tfb_tensor* y) {

@@ -4,8 +4,9 @@ Composition follows the pages ([Autograd-1, "Training loop": Linear = MatMul +
 bias Add, Tanh, SoftmaxCrossEntropy; GPT2-4, "Loading the weights" and
 "Generation with KV cache": token + position embedding, pre-LN blocks with a
 fused c_attn [C, 3C], MLP C -> 4C -> C with GELU, ln_f, the LM head tied to
-wte).  Linear is the fused MatMul+bias op and the attention core is the single
-tfb_causal_attention op; both compute exactly the pages' op sequence.
+wte).  Linear is the fused MatMul+bias op (with the residual Add folded in where a
+projection feeds the residual stream) and the attention core is the single
+tfb_causal_attention op; each computes exactly the pages' op sequence.
 """
 from __future__ import annotations
 
@@ -52,10 +53,10 @@ class Gpt:
             h = layernorm(x, P[p + "ln_1.weight"], P[p + "ln_1.bias"])
             qkv = linear(h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"], bf16_copy=True)
             a = causal_attention(qkv, self.n_head)
-            x = add(x, linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"]))
+            x = linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"], residual=x)
             h = layernorm(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"])
             f = gelu(linear(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"]))
-            x = add(x, linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"]))
+            x = linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"], residual=x)
         xf = layernorm(x, P["ln_f.weight"], P["ln_f.bias"])
         return matmul_t(xf, P["wte.weight"])
 
@@ -85,10 +86,10 @@ class Gpt:
             if i == self.n_layer - 1:
                 break   # the last block's output is not needed: the next token comes from a decode step
             a = causal_attention(qkv, self.n_head)
-            x = add(x, linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"]))
+            x = linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"], residual=x)
             h = layernorm(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"])
             f = gelu(linear(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"]))
-            x = add(x, linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"]))
+            x = linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"], residual=x)
 
     def decode_step(self, tokens, pos: int, kv: KvCache, tmax: int) -> Tensor:
         """One token per sequence (tokens: [B] int32) at position pos -> logits [B, 1, V]."""
@@ -102,10 +103,10 @@ class Gpt:
             h = layernorm(x, P[p + "ln_1.weight"], P[p + "ln_1.bias"])
             qkv = linear(h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"])
             a = kv.attend(i, qkv, pos, self.n_head)
-            x = add(x, linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"]))
+            x = linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"], residual=x)
             h = layernorm(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"])
             f = gelu(linear(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"]))
-            x = add(x, linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"]))
+            x = linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"], residual=x)
         return matmul_t(layernorm(x, P["ln_f.weight"], P["ln_f.bias"]), P["wte.weight"])
 
     def generate(self, prompts, steps: int, uniforms, k: int, temperature: float, on_step=None):
