@@ -35,6 +35,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr int NT = 256;     // 4 wavefronts
 constexpr int KVB = 64;     // keys (or queries) per staged block
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float RESCALE_MARGIN = 8.f;  // the forward's running reference may trail the max by this (log2 units)
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -228,9 +229,23 @@ __global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
           }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx);
-      const float mref = mn == -INFINITY ? 0.f : mn;
-      const float alpha = fexp2(m - mref);
+      // m is the reference the running sum l and the output o are scaled to.  It
+      // only moves when a score exceeds it by more than RESCALE_MARGIN (log2
+      // units), so p <= 2^RESCALE_MARGIN; o / l and m + log2(l) are unchanged by
+      // the choice of reference.  After the first visible block a wave almost
+      // never has to rescale, and the test is one wave-uniform branch.
+      const bool need = mx > m + RESCALE_MARGIN;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float mn = need ? mx : m;
+        const float alpha = need ? fexp2(m - mn) : 1.f;  // m = -inf: alpha = 0, o and l are 0
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < HS / 32; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+        m = mn;
+      }
+      const float mref = m == -INFINITY ? 0.f : m;
       float sum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -241,12 +256,7 @@ __global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
           sum += p;
         }
       sum += __shfl_xor(sum, 32, 64);
-      l = l * alpha + sum;
-      m = mn;
-#pragma unroll
-      for (int i = 0; i < HS / 32; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      l += sum;
 #pragma unroll
       for (int s = 0; s < KVB / 16; ++s) {
         const bf16x8 pb = pack8(st[s >> 1], 8 * (s & 1));

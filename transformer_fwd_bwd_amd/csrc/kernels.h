@@ -109,13 +109,19 @@ hipError_t causal_softmax_fwd(const float* x, float* p, int64_t rows, int64_t T,
 hipError_t causal_softmax_bwd(const float* g, const float* p, float* d, int64_t rows, int64_t T, float scale,
                               float beta, bool full, hipStream_t s);
 size_t softmax_ce_workspace_bytes(int64_t rows);
-// logits rows have V valid columns at a row stride of ld >= V
+// logits rows have V valid columns at a row stride of ld >= V.  dlbf (optional):
+// the bf16 gradient of the logits for an upstream gradient of 1 is also written
+// there, in softmax_ce_bwd's expression, where the one-pass path runs
+// (*dlbf_written says whether it did)
 hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* targets, int64_t rows, int64_t V,
-                          float* lse, float* loss, void* ws, hipStream_t s);
-// dl may be null when dlbf is given (and beta == 0): only the bf16 copy is written
+                          float* lse, float* loss, void* ws, hipStream_t s, uint16_t* dlbf = nullptr,
+                          bool* dlbf_written = nullptr);
+// dl may be null when dlbf is given (and beta == 0): only the bf16 copy is written.
+// skip_if_unit: nothing is done when g_scalar[0] == 1 (checked on the device): the
+// forward already wrote that gradient into dlbf.
 hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* targets, const float* lse,
                           const float* g_scalar, float* dl, uint16_t* dlbf, int64_t rows, int64_t V, float beta,
-                          hipStream_t s);
+                          hipStream_t s, bool skip_if_unit = false);
 
 // ---- fused causal attention, bf16 variant (attention.hip)
 // qkv: bf16 [B, T, 3C] (q | k | v thirds, head h = columns h*hs .. h*hs+hs-1 of each third)

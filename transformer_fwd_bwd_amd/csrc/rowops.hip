@@ -538,7 +538,9 @@ __global__ __launch_bounds__(NT) void mean_k(const float* __restrict__ v, int64_
 __global__ __launch_bounds__(NT) void ce_bwd_k(const float* __restrict__ logits, int64_t ld,
                                                const int32_t* __restrict__ tgt, const float* __restrict__ lse,
                                                const float* __restrict__ gsc, float* __restrict__ dl,
-                                               uint16_t* __restrict__ dlbf, int64_t rows, int64_t V, float beta) {
+                                               uint16_t* __restrict__ dlbf, int64_t rows, int64_t V, float beta,
+                                               int skip_unit) {
+  if (skip_unit && gsc[0] == 1.f) return;
   const int64_t r = blockIdx.x;
   const float gn = gsc[0] / (float)rows;
   const float L = lse[r];
@@ -619,11 +621,78 @@ __global__ __launch_bounds__(NT) void ce_fwd4_k(const float* __restrict__ logits
 }
 
 
+// Cross-entropy forward that also writes the bf16 gradient the backward would
+// write for an upstream gradient of 1, (p - onehot) / rows, in the backward's own
+// expression: one 1024-thread workgroup per row holds the row in registers (PER
+// float4 per thread), so the logits are read once for both passes.
+template <int PER>
+__global__ __launch_bounds__(1024) void ce_fwd_grad4_k(const float* __restrict__ logits, int64_t ld,
+                                                       const int32_t* __restrict__ tgt, int64_t V,
+                                                       float* __restrict__ lse, float* __restrict__ loss_rows,
+                                                       uint16_t* __restrict__ dlbf, float gn) {
+  constexpr int NW = 16;
+  __shared__ float red[NW];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t r = blockIdx.x;
+  const float* lr = logits + r * ld;
+  const f4* lr4 = reinterpret_cast<const f4*>(lr);
+  const int64_t V4 = V / 4;
+  const int tail = (int)(V - 4 * V4);
+  f4 x[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int64_t i = tid + (int64_t)u * 1024;
+    x[u] = i < V4 ? lr4[i] : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  }
+  const float xt = tid < tail ? lr[4 * V4 + tid] : -INFINITY;
+  float m = xt;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) m = fmaxf(m, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) m = fmaxf(m, red[i]);
+  __syncthreads();
+  float sum = expf(xt - m);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) sum += (expf(x[u][0] - m) + expf(x[u][1] - m)) + (expf(x[u][2] - m) + expf(x[u][3] - m));
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  if (lane == 0) red[w] = sum;
+  __syncthreads();
+  float S = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) S += red[i];
+  const float L = m + logf(S);
+  const int t = tgt[r];
+  if (tid == 0) {
+    lse[r] = L;
+    loss_rows[r] = (t >= 0 && t < V) ? fminf(L - lr[t], 69.07755278982137f) : NAN;
+  }
+  u16x4* br4 = reinterpret_cast<u16x4*>(dlbf + r * ld);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int64_t i = tid + (int64_t)u * 1024;
+    if (i >= V4) break;
+    f4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = gn * (expf(x[u][e] - L) - (4 * i + e == t ? 1.f : 0.f));
+    br4[i] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
+  }
+  if (tid < tail) {
+    const int64_t c = 4 * V4 + tid;
+    dlbf[r * ld + c] = bf16_bits(gn * (expf(xt - L) - (c == t ? 1.f : 0.f)));
+  }
+}
+
 // float4 form of ce_bwd_k (rows 16-byte aligned): two float4 per thread in flight
 __global__ __launch_bounds__(NT) void ce_bwd4_k(const float* __restrict__ logits, int64_t ld,
                                                 const int32_t* __restrict__ tgt, const float* __restrict__ lse,
                                                 const float* __restrict__ gsc, float* __restrict__ dl,
-                                                uint16_t* __restrict__ dlbf, int64_t rows, int64_t V, float beta) {
+                                                uint16_t* __restrict__ dlbf, int64_t rows, int64_t V, float beta,
+                                                int skip_unit) {
+  if (skip_unit && gsc[0] == 1.f) return;  // the forward already wrote this gradient
   const int64_t r = blockIdx.x;
   const float gn = gsc[0] / (float)rows;
   const float L = lse[r];
@@ -778,10 +847,25 @@ hipError_t causal_softmax_bwd(const float* g, const float* p, float* d, int64_t 
 size_t softmax_ce_workspace_bytes(int64_t rows) { return (size_t)rows * sizeof(float); }
 
 hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* targets, int64_t rows, int64_t V,
-                          float* lse, float* loss, void* ws, hipStream_t s) {
+                          float* lse, float* loss, void* ws, hipStream_t s, uint16_t* dlbf, bool* dlbf_written) {
+  if (dlbf_written) *dlbf_written = false;
   if (rows <= 0) return hipSuccess;
   float* loss_rows = static_cast<float*>(ws);
-  if (ld % 4 == 0 && aligned16(logits))
+  const int64_t per = (V / 4 + 1023) / 1024;
+  if (dlbf && ld % 4 == 0 && aligned16(logits) && (reinterpret_cast<uintptr_t>(dlbf) & 7) == 0 && per >= 1 &&
+      per <= 16) {
+    const float gn = 1.f / (float)rows;  // the backward's g / rows for g = 1
+    const dim3 grid((unsigned)rows), block(1024);
+    if (per <= 4)
+      hipLaunchKernelGGL(ce_fwd_grad4_k<4>, grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+    else if (per <= 8)
+      hipLaunchKernelGGL(ce_fwd_grad4_k<8>, grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+    else if (per <= 13)
+      hipLaunchKernelGGL(ce_fwd_grad4_k<13>, grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+    else
+      hipLaunchKernelGGL(ce_fwd_grad4_k<16>, grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+    if (dlbf_written) *dlbf_written = true;
+  } else if (ld % 4 == 0 && aligned16(logits))
     hipLaunchKernelGGL(ce_fwd4_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
   else
     hipLaunchKernelGGL(ce_fwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
@@ -791,15 +875,15 @@ hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* target
 
 hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* targets, const float* lse,
                           const float* g_scalar, float* dl, uint16_t* dlbf, int64_t rows, int64_t V, float beta,
-                          hipStream_t s) {
+                          hipStream_t s, bool skip_if_unit) {
   if (rows <= 0) return hipSuccess;
   if (!dl && (!dlbf || beta != 0.f)) return hipErrorInvalidValue;
   if (ld % 4 == 0 && aligned16(logits) && aligned16(dl) && (reinterpret_cast<uintptr_t>(dlbf) & 7) == 0)
     hipLaunchKernelGGL(ce_bwd4_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
-                       rows, V, beta);
+                       rows, V, beta, (int)skip_if_unit);
   else
     hipLaunchKernelGGL(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
-                       rows, V, beta);
+                       rows, V, beta, (int)skip_if_unit);
   return hipGetLastError();
 }
 

@@ -836,9 +836,11 @@ void backward_rec(Ctx& C, const Rec& r) {
       if ((r.i0 & TFB_CE_GRAD_BF16_ONLY) && lg.uses == 1 && !lg.leaf && !lg.gpend && lg.gstate != G_VALID &&
           C.grad_read_as_bf16(lg)) {
         // the logits' only gradient, read by their producer as bf16: that copy alone
+        // (written by the forward already when r.i1 == 1: then only for g != 1)
         uint16_t* dlb = C.twin_grad(lg);
         hip_check(softmax_ce_bwd(lg.data, lg.stride(), static_cast<const int32_t*>(r.s0),
-                                 static_cast<const float*>(r.s1), g, nullptr, dlb, lg.rows(), lg.cols(), 0.f, s),
+                                 static_cast<const float*>(r.s1), g, nullptr, dlb, lg.rows(), lg.cols(), 0.f, s,
+                                 r.i1 == 1),
                   "softmax_ce bwd");
         lg.gstate = G_BF16;
         lg.gbf_valid = true;
@@ -1488,16 +1490,24 @@ int tfb_softmax_cross_entropy_ex(tfb_ctx* ctx, tfb_tensor logits, const int32_t*
     if (rows)
       hip_check(hipMemcpyAsync(tg, dev_targets, (size_t)rows * sizeof(int32_t), hipMemcpyDeviceToDevice, C.s()),
                 "copy targets");
+    // with the bf16-only option the logits' bf16 gradient for an upstream gradient of 1
+    // comes out of the same pass over the logits (allocated before the scratch below)
+    uint16_t* pre = nullptr;
+    if ((flags & TFB_CE_GRAD_BF16_ONLY) && ctx->grad_enabled && !ctx->tensors[logits].leaf &&
+        C.grad_read_as_bf16(ctx->tensors[logits]))
+      pre = C.twin_grad(ctx->tensors[logits]);
     size_t mark = ctx->arena.hi;
     void* ws = C.scratch(softmax_ce_workspace_bytes(rows));
+    bool pre_written = false;
     hip_check(softmax_ce_fwd(ctx->tensors[logits].data, ctx->tensors[logits].stride(), tg, rows, V, lse,
-                             ctx->tensors[h].data, ws, C.s()),
+                             ctx->tensors[h].data, ws, C.s(), pre, &pre_written),
               "softmax_ce");
     ctx->arena.hi = mark;
     Rec r{OP_SOFTMAX_CE};
     r.in[0] = logits, r.out = h;
     r.s0 = tg, r.s1 = lse;
     r.i0 = flags;
+    r.i1 = pre_written ? 1 : 0;
     C.record(r);
     *loss = h;
   });
