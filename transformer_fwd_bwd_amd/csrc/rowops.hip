@@ -223,7 +223,9 @@ __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, 
   for (int j = 0; j < J; ++j) pa[j] = pb[j] = pc[j] = f4{0.f, 0.f, 0.f, 0.f};
   for (int64_t r0 = (int64_t)blockIdx.x * WAVES + w; r0 < rows; r0 += 2 * nw) {
     const int64_t rr[2] = {r0, r0 + nw};
-    f4 xv[2][J], gv[2][J];
+    // both rows' x, g and earlier dx are loaded before any store: each lane reads
+    // and writes only its own elements, so this holds even when dx_src is dx
+    f4 xv[2][J], gv[2][J], sv[2][J];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -232,6 +234,7 @@ __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, 
         const bool ok = c < C4 && rr[u] < rows;
         xv[u][j] = ok ? x[rr[u] * C4 + c] : f4{0.f, 0.f, 0.f, 0.f};
         gv[u][j] = ok ? g[rr[u] * C4 + c] : f4{0.f, 0.f, 0.f, 0.f};
+        sv[u][j] = ok && beta_dx != 0.f ? dx_src[rr[u] * C4 + c] : f4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, 
         const int c = lane + 64 * j;
         if (c < C4) {
           f4 v = rs * (dg[j] - m1 - xh[j] * m2);
-          if (beta_dx != 0.f) v += dx_src[r * C4 + c];  // may be dx itself: read before the write
+          v += sv[u][j];  // the earlier gradient (zero when beta_dx == 0)
           dx[r * C4 + c] = v;
           if constexpr (SUMDX) pc[j] += v;
           if (dxbf) dxbf[r * C4 + c] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
@@ -336,7 +339,24 @@ __global__ __launch_bounds__(1024) void ln_bwd_reduce(const float* __restrict__ 
   const int c = blockIdx.x * 16 + tx;
   float a = 0.f, b = 0.f, d = 0.f;
   if (c < C) {
-    for (int p = ty; p < nparts; p += 64) {
+    int p = ty;
+    for (; p + 192 < nparts; p += 256) {  // four partials in flight per thread
+      float ta[4], tb[4], td[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t o = ((int64_t)(p + 64 * u) * np) * C + c;
+        ta[u] = part[o];
+        tb[u] = part[o + C];
+        td[u] = dxsum ? part[o + 2 * C] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a += ta[u];
+        b += tb[u];
+        d += td[u];
+      }
+    }
+    for (; p < nparts; p += 64) {
       a += part[((int64_t)p * np) * C + c];
       b += part[((int64_t)p * np + 1) * C + c];
       if (dxsum) d += part[((int64_t)p * np + 2) * C + c];
@@ -348,6 +368,7 @@ __global__ __launch_bounds__(1024) void ln_bwd_reduce(const float* __restrict__ 
   __syncthreads();
   if (ty == 0 && c < C) {
     float ra = 0.f, rb = 0.f, rd = 0.f;
+#pragma unroll 4
     for (int i = 0; i < 64; ++i) {
       ra += sa[i][tx];
       rb += sb[i][tx];
@@ -476,10 +497,15 @@ __global__ __launch_bounds__(NT) void csm_bwd_k(const float* __restrict__ g, con
 }
 
 // ------------------------------------------------------------ softmax + cross-entropy
+// e^a for the cross-entropy kernels: the hardware 2^x on a * log2(e) (about 2 ulp
+// on the softmax terms; 0 for a = -inf).  The forward and backward use it alike,
+// so a gradient the forward writes equals the one the backward would.
+__device__ __forceinline__ float ce_exp(float a) { return __builtin_amdgcn_exp2f(a * 1.4426950408889634f); }
+
 __device__ __forceinline__ void online_merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);
   if (mn == -INFINITY) return;
-  s = s * expf(m - mn) + s2 * expf(m2 - mn);
+  s = s * ce_exp(m - mn) + s2 * ce_exp(m2 - mn);
   m = mn;
 }
 
@@ -494,10 +520,10 @@ __global__ __launch_bounds__(NT) void ce_fwd_k(const float* __restrict__ logits,
   for (int64_t c = threadIdx.x; c < V; c += NT) {
     const float x = lr[c];
     if (x > m) {
-      s = s * expf(m - x) + 1.f;
+      s = s * ce_exp(m - x) + 1.f;
       m = x;
     } else {
-      s += expf(x - m);
+      s += ce_exp(x - m);
     }
   }
   for (int o = 32; o > 0; o >>= 1) {
@@ -549,7 +575,7 @@ __global__ __launch_bounds__(NT) void ce_bwd_k(const float* __restrict__ logits,
   float* dr = dl ? dl + r * ld : nullptr;  // null: the bf16 copy alone
   uint16_t* br = dlbf ? dlbf + r * ld : nullptr;
   for (int64_t c = threadIdx.x; c < V; c += NT) {
-    float v = gn * (expf(lr[c] - L) - (c == t ? 1.f : 0.f));
+    float v = gn * (ce_exp(lr[c] - L) - (c == t ? 1.f : 0.f));
     if (dr) {
       if (beta != 0.f) v += dr[c];
       dr[c] = v;
@@ -586,18 +612,18 @@ __global__ __launch_bounds__(NT) void ce_fwd4_k(const float* __restrict__ logits
     float mx = m;
 #pragma unroll
     for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
-    s *= expf(m - mx);  // m = -inf the first time: s is 0 and stays 0
+    s *= ce_exp(m - mx);  // m = -inf the first time: s is 0 and stays 0
     m = mx;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) s += (expf(x[u][0] - m) + expf(x[u][1] - m)) + (expf(x[u][2] - m) + expf(x[u][3] - m));
+    for (int u = 0; u < 4; ++u) s += (ce_exp(x[u][0] - m) + ce_exp(x[u][1] - m)) + (ce_exp(x[u][2] - m) + ce_exp(x[u][3] - m));
   }
   for (int64_t c = 4 * V4 + threadIdx.x; c < V; c += NT) {
     const float x = lr[c];
     if (x > m) {
-      s = s * expf(m - x) + 1.f;
+      s = s * ce_exp(m - x) + 1.f;
       m = x;
     } else {
-      s += expf(x - m);
+      s += ce_exp(x - m);
     }
   }
   for (int o = 32; o > 0; o >>= 1) {
@@ -655,9 +681,9 @@ __global__ __launch_bounds__(1024) void ce_fwd_grad4_k(const float* __restrict__
 #pragma unroll
   for (int i = 1; i < NW; ++i) m = fmaxf(m, red[i]);
   __syncthreads();
-  float sum = expf(xt - m);
+  float sum = ce_exp(xt - m);
 #pragma unroll
-  for (int u = 0; u < PER; ++u) sum += (expf(x[u][0] - m) + expf(x[u][1] - m)) + (expf(x[u][2] - m) + expf(x[u][3] - m));
+  for (int u = 0; u < PER; ++u) sum += (ce_exp(x[u][0] - m) + ce_exp(x[u][1] - m)) + (ce_exp(x[u][2] - m) + ce_exp(x[u][3] - m));
   for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
   if (lane == 0) red[w] = sum;
   __syncthreads();
@@ -677,12 +703,12 @@ __global__ __launch_bounds__(1024) void ce_fwd_grad4_k(const float* __restrict__
     if (i >= V4) break;
     f4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = gn * (expf(x[u][e] - L) - (4 * i + e == t ? 1.f : 0.f));
+    for (int e = 0; e < 4; ++e) v[e] = gn * (ce_exp(x[u][e] - L) - (4 * i + e == t ? 1.f : 0.f));
     br4[i] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
   }
   if (tid < tail) {
     const int64_t c = 4 * V4 + tid;
-    dlbf[r * ld + c] = bf16_bits(gn * (expf(xt - L) - (c == t ? 1.f : 0.f)));
+    dlbf[r * ld + c] = bf16_bits(gn * (ce_exp(xt - L) - (c == t ? 1.f : 0.f)));
   }
 }
 
@@ -714,7 +740,7 @@ __global__ __launch_bounds__(NT) void ce_bwd4_k(const float* __restrict__ logits
       if (i >= V4) continue;
       f4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = gn * (expf(x[u][e] - L) - (4 * i + e == t ? 1.f : 0.f));
+      for (int e = 0; e < 4; ++e) v[e] = gn * (ce_exp(x[u][e] - L) - (4 * i + e == t ? 1.f : 0.f));
       if (dr4) {
         if (beta != 0.f) v += dr4[i];
         dr4[i] = v;
@@ -725,7 +751,7 @@ __global__ __launch_bounds__(NT) void ce_bwd4_k(const float* __restrict__ logits
   const float* lr = logits + r * ld;
   float* dr = dl ? dl + r * ld : nullptr;
   for (int64_t c = 4 * V4 + threadIdx.x; c < V; c += NT) {
-    float v = gn * (expf(lr[c] - L) - (c == t ? 1.f : 0.f));
+    float v = gn * (ce_exp(lr[c] - L) - (c == t ? 1.f : 0.f));
     if (dr) {
       if (beta != 0.f) v += dr[c];
       dr[c] = v;
@@ -744,6 +770,9 @@ hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, 
     const int C4 = (int)(C / 4);
     if (C4 <= 64)
       hipLaunchKernelGGL(ln_fwd4_k<1>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
+                         (const f4*)beta, (f4*)y, (u16x4*)ybf, mean, rstd, rows, C4, eps);
+    else if (C4 <= 192)
+      hipLaunchKernelGGL(ln_fwd4_k<3>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
                          (const f4*)beta, (f4*)y, (u16x4*)ybf, mean, rstd, rows, C4, eps);
     else
       hipLaunchKernelGGL(ln_fwd4_k<4>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
@@ -782,12 +811,18 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
       if (C4 <= 64)
         hipLaunchKernelGGL((ln_bwd_fused4_k<1, true>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
                            (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+      else if (C4 <= 192)
+        hipLaunchKernelGGL((ln_bwd_fused4_k<3, true>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
+                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
       else
         hipLaunchKernelGGL((ln_bwd_fused4_k<4, true>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
                            (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
     } else {
       if (C4 <= 64)
         hipLaunchKernelGGL((ln_bwd_fused4_k<1, false>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
+                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+      else if (C4 <= 192)
+        hipLaunchKernelGGL((ln_bwd_fused4_k<3, false>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
                            (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
       else
         hipLaunchKernelGGL((ln_bwd_fused4_k<4, false>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
