@@ -114,6 +114,8 @@ int tfb_tanh(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y);
 /* y = 0.5 a (1 + tanh(sqrt(2/pi)(a + 0.044715 a^3))), GPT-2's tanh form.
  * [GPT2-4, "Common mistakes"] */
 int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y);
+/* tfb_gelu with flags (TFB_OUT_BF16_ONLY; unknown flags: TFB_ERR_ARG). */
+int tfb_gelu_ex(tfb_ctx* ctx, tfb_tensor a, int flags, tfb_tensor* y);
 /* y = x[..., K] @ w[K, M] (rows of x flattened).  Backward dx = g w^T,
  * dw = x^T g.  [Autograd-1, "Ops": MatMul] */
 int tfb_matmul(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y);
@@ -130,6 +132,12 @@ int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tenso
  * value and is ignored in the fp32 variant.  Unknown flags: TFB_ERR_ARG.
  * [GPT2-4, "Loading the weights": Linear weights stored [in, out]] */
 #define TFB_OUT_BF16_COPY 1
+/* Output flag of tfb_linear_ex, tfb_layernorm_ex and tfb_gelu_ex (bf16 variant):
+ * only the bf16 copy of y is written, for an output whose readers take bf16
+ * (the contractions, the fused attention).  A reader that needs fp32 data (any
+ * other op, tfb_tensor_read, tfb_tensor_info) gets the exact float values of
+ * those bf16 numbers, converted on first use.  Ignored in the fp32 variant. */
+#define TFB_OUT_BF16_ONLY 2
 /* y = r + (x @ w + b): a Linear and the residual Add that follows it, with the
  * Add done in the product's epilogue (r is read there, once).  r has the
  * output's shape [rows(x), cols(w)].  One op on the tape; its backward gives r
@@ -141,6 +149,9 @@ int tfb_linear_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int fl
 /* Per row over the last dim: (x - mean)/sqrt(var + eps) * gamma + beta with the
  * biased variance.  [Autograd-1, table of ops: LayerNorm] */
 int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y);
+/* tfb_layernorm with flags (TFB_OUT_BF16_ONLY; unknown flags: TFB_ERR_ARG). */
+int tfb_layernorm_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, int flags,
+                     tfb_tensor* y);
 /* y[b, t, :] = table[ids[b*T + t], :], y shape [batch, n/batch, C]; backward
  * scatter-adds rows into table's gradient (sorted segment sum: deterministic).
  * dev_ids: n int32 device values in [0, rows(table)), copied by the call.

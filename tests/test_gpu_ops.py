@@ -490,6 +490,57 @@ def test_bias_gradients_from_fused_column_sums(ctx, prec):
     ctx.set_precision("fp32")
 
 
+def _bf16_round(a):
+    """float32 -> nearest-even bf16 -> float32, in numpy (the rounding the kernels apply)."""
+    b = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return (b << 16).astype(np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_bf16_only_outputs(ctx, prec):
+    """Outputs kept as bf16 copies alone (LayerNorm, GELU, Linear): read back as the exact
+    bf16 rounding of the plain op's output (unchanged in fp32); a contraction or attention
+    reading them and every gradient are bit-identical to the plain ops; an fp32 reader
+    (Tanh) sees the converted values."""
+    ctx.set_precision(prec)
+    B, Tn, C, H = 2, 80, 64, 2
+    xv, g1, b1 = rnd(131, (B, Tn, C)), rnd(132, (C,), 0.5) + 1.0, rnd(133, (C,), 0.1)
+    W1, c1 = rnd(134, (C, 3 * C), 0.1), rnd(135, (3 * C,), 0.1)
+    W2, c2 = rnd(136, (C, 96), 0.1), rnd(137, (96,), 0.1)
+    R1, R2 = rnd(138, (B, Tn, C)), rnd(139, (B, Tn, 96))
+    res = []
+    for only in (False, True):
+        t = {k: ctx.tensor(v.shape, v) for k, v in dict(x=xv, g1=g1, b1=b1, W1=W1, c1=c1, W2=W2, c2=c2,
+                                                          R1=R1, R2=R2).items()}
+        h = T.layernorm(t["x"], t["g1"], t["b1"], bf16_only=only)
+        qkv = T.linear(h, t["W1"], t["c1"], bf16_only=only)
+        att = T.causal_attention(qkv, H)
+        f = T.gelu(T.linear(h, t["W2"], t["c2"]), bf16_only=only)
+        th = T.tanh(f)                                            # an fp32 reader
+        loss = T.add(T.sum_all(T.mul(att, t["R1"])), T.sum_all(T.mul(th, t["R2"])))
+        ctx.backward(loss)
+        res.append(dict(h=h.numpy(), qkv=qkv.numpy(), f=f.numpy(), att=att.numpy(), th=th.numpy(),
+                        **{"d" + k: t[k].grad() for k in ("x", "g1", "b1", "W1", "c1", "W2", "c2")}))
+        ctx.tape_reset()
+        for v in t.values():
+            v.release()
+    plain, only = res
+    for k in ("h", "qkv", "f"):
+        want = _bf16_round(plain[k]) if prec == "bf16" else plain[k]
+        np.testing.assert_array_equal(only[k], want, err_msg=k)
+    np.testing.assert_array_equal(only["att"], plain["att"])
+    # Tanh reads the converted bf16 values (exactly those) in the bf16 variant
+    assert_close(only["th"], np.tanh(only["f"].astype(np.float64)), 1e-6, "tanh of the bf16-only output")
+    if prec == "fp32":
+        np.testing.assert_array_equal(only["th"], plain["th"])
+    for k in ("dW1", "dc1"):                                   # through the contraction / attention path only
+        np.testing.assert_array_equal(only[k], plain[k], err_msg=k)
+    for k in ("dx", "dg1", "db1", "dW2", "dc2"):               # the Tanh branch sees rounded inputs
+        assert_close(only[k], plain[k], 1e-6 if prec == "fp32" else 2e-2, k)
+    ctx.set_precision("fp32")
+
+
 def test_no_grad_records_nothing(ctx):
     a = ctx.tensor((2, 3), rnd(40, (2, 3)))
     ctx.set_grad_enabled(False)

@@ -51,6 +51,8 @@ SIGNATURES = {
     "tfb_matmul_t": [c_void_p, c_int32, c_int32, P(c_int32)],
     "tfb_linear": [c_void_p, c_int32, c_int32, c_int32, P(c_int32)],
     "tfb_linear_ex": [c_void_p, c_int32, c_int32, c_int32, c_int32, P(c_int32)],
+    "tfb_layernorm_ex": [c_void_p, c_int32, c_int32, c_int32, c_float, c_int32, P(c_int32)],
+    "tfb_gelu_ex": [c_void_p, c_int32, c_int32, P(c_int32)],
     "tfb_linear_residual": [c_void_p, c_int32, c_int32, c_int32, c_int32, P(c_int32)],
     "tfb_layernorm": [c_void_p, c_int32, c_int32, c_int32, c_float, P(c_int32)],
     "tfb_embedding": [c_void_p, c_int32, c_void_p, c_int64, c_int64, P(c_int32)],
@@ -260,6 +262,10 @@ def _out(ctx: Context, fn, *args) -> Tensor:
 
 
 # ------------------------------------------------------------------------- ops
+OUT_BF16_COPY = 1
+OUT_BF16_ONLY = 2
+
+
 def add(a: Tensor, b: Tensor) -> Tensor:
     return _out(a.ctx, _lib.tfb_add, a.h, b.h)
 
@@ -285,7 +291,11 @@ def tanh(a: Tensor) -> Tensor:
     return _out(a.ctx, _lib.tfb_tanh, a.h)
 
 
-def gelu(a: Tensor) -> Tensor:
+def gelu(a: Tensor, bf16_only: bool = False) -> Tensor:
+    """bf16_only (bf16 variant): only the output's bf16 copy is written, for an output
+    that contractions read next; fp32 readers get it converted from those values."""
+    if bf16_only:
+        return _out(a.ctx, _lib.tfb_gelu_ex, a.h, OUT_BF16_ONLY)
     return _out(a.ctx, _lib.tfb_gelu, a.h)
 
 
@@ -297,23 +307,25 @@ def matmul_t(x: Tensor, w: Tensor) -> Tensor:
     return _out(x.ctx, _lib.tfb_matmul_t, x.h, w.h)
 
 
-OUT_BF16_COPY = 1
-
-
-def linear(x: Tensor, w: Tensor, b: Tensor, bf16_copy: bool = False, residual: Tensor = None) -> Tensor:
+def linear(x: Tensor, w: Tensor, b: Tensor, bf16_copy: bool = False, residual: Tensor = None,
+           bf16_only: bool = False) -> Tensor:
     """x @ w + b (+ residual).  bf16_copy: the product also writes the output's bf16
     copy (bf16 variant), for an output that a contraction or the attention kernels
-    read next.  residual: added in the product's epilogue (one op on the tape)."""
+    read next; bf16_only: that copy alone.  residual: added in the product's
+    epilogue (one op on the tape)."""
     if residual is not None:
-        if bf16_copy:
-            raise ValueError("linear: bf16_copy and residual are not combined")
+        if bf16_copy or bf16_only:
+            raise ValueError("linear: bf16 output options and residual are not combined")
         return _out(x.ctx, _lib.tfb_linear_residual, x.h, w.h, b.h, residual.h)
-    if bf16_copy:
-        return _out(x.ctx, _lib.tfb_linear_ex, x.h, w.h, b.h, OUT_BF16_COPY)
+    if bf16_copy or bf16_only:
+        return _out(x.ctx, _lib.tfb_linear_ex, x.h, w.h, b.h, OUT_BF16_ONLY if bf16_only else OUT_BF16_COPY)
     return _out(x.ctx, _lib.tfb_linear, x.h, w.h, b.h)
 
 
-def layernorm(x: Tensor, gamma: Tensor, beta: Tensor, eps: float = 1e-5) -> Tensor:
+def layernorm(x: Tensor, gamma: Tensor, beta: Tensor, eps: float = 1e-5, bf16_only: bool = False) -> Tensor:
+    """bf16_only: as for gelu."""
+    if bf16_only:
+        return _out(x.ctx, _lib.tfb_layernorm_ex, x.h, gamma.h, beta.h, c_float(eps), OUT_BF16_ONLY)
     return _out(x.ctx, _lib.tfb_layernorm, x.h, gamma.h, beta.h, c_float(eps))
 
 

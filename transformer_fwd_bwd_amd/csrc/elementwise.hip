@@ -315,6 +315,13 @@ hipError_t tanh_bwd(const float* g, const float* y, float* d, float beta, int64_
   return hipGetLastError();
 }
 
+hipError_t to_f32(const uint16_t* src, float* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  auto f = [=] __device__(int64_t i) { dst[i] = __uint_as_float((unsigned)src[i] << 16); };
+  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  return hipGetLastError();
+}
+
 hipError_t gelu_fwd(const float* a, float* y, uint16_t* ybf, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (n % 4 == 0 && aligned16(a) && aligned16(y) && (reinterpret_cast<uintptr_t>(ybf) & 7) == 0) {
@@ -324,14 +331,14 @@ hipError_t gelu_fwd(const float* a, float* y, uint16_t* ybf, int64_t n, hipStrea
     auto f = [=] __device__(int64_t i) {
       f4 v = a4[i];
       const f4 o = {gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3])};
-      y4[i] = o;
+      if (y4) y4[i] = o;  // null: the bf16 copy alone
       if (b4) b4[i] = u16x4{bf16_bits(o[0]), bf16_bits(o[1]), bf16_bits(o[2]), bf16_bits(o[3])};
     };
     hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
   } else {
     auto f = [=] __device__(int64_t i) {
       const float o = gelu_f(a[i]);
-      y[i] = o;
+      if (y) y[i] = o;
       if (ybf) ybf[i] = bf16_bits(o);
     };
     hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);

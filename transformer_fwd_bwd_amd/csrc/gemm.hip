@@ -603,6 +603,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
   const float* bias = to_ws ? nullptr : g.bias;
   const float* resid = to_ws ? nullptr : g.resid;
   uint16_t* Cbf = to_ws ? nullptr : g.Cbf;
+  const bool skipc = !to_ws && g.c_bf16_only;  // the bf16 copy alone
   const bool vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(bias) & 15) == 0) && ((reinterpret_cast<uintptr_t>(Cbf) & 7) == 0) &&
                    ((reinterpret_cast<uintptr_t>(resid) & 15) == 0);
@@ -636,7 +637,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
           f4* dst = reinterpret_cast<f4*>(row + n);
           if (!to_ws && g.beta != 0.f) v += g.beta * *dst;
           if (resid) v += *reinterpret_cast<const f4*>(resid + (int64_t)m * ldc + n);
-          *dst = v;
+          if (!skipc) *dst = v;
           if (Cbf) *reinterpret_cast<u16x4*>(Cbf + (int64_t)m * ldc + n) = bf16x4_bits(v);
         } else {
 #pragma unroll
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
             if (bias) x += bias[n + e];
             if (!to_ws && g.beta != 0.f) x += g.beta * row[n + e];
             if (resid) x += resid[(int64_t)m * ldc + n + e];
-            row[n + e] = x;
+            if (!skipc) row[n + e] = x;
             if (Cbf) Cbf[(int64_t)m * ldc + n + e] = bf16_bits(x);
           }
         }
@@ -674,7 +675,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
           if (bias) x += bias[n + e];
           if (!to_ws && g.beta != 0.f) x += g.beta * row[n + e];
           if (resid) x += resid[(int64_t)m * ldc + n + e];
-          row[n + e] = x;
+          if (!skipc) row[n + e] = x;
           if (Cbf) Cbf[(int64_t)m * ldc + n + e] = bf16_bits(x);
         }
       }
@@ -685,7 +686,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
 // The same over float4 (N, ldc multiples of 4, 16-byte aligned C and bias)
 __global__ void splitk_reduce4(const f4* __restrict__ ws, int splits, int M, int N4, float* C, int64_t ldc,
                                int batch_div, int64_t sc1, int64_t sc2, float beta, const f4* bias, uint16_t* Cbf,
-                               const float* resid) {
+                               const float* resid, int skipc) {
   const int z = blockIdx.y;
   const int64_t MN4 = (int64_t)M * N4;
   const int z1 = z / batch_div, z2 = z % batch_div;
@@ -698,7 +699,7 @@ __global__ void splitk_reduce4(const f4* __restrict__ ws, int splits, int M, int
     f4* dst = reinterpret_cast<f4*>(Cz + (int64_t)m * ldc) + n4;
     if (beta != 0.f) s += beta * *dst;
     if (resid) s += *reinterpret_cast<const f4*>(resid + (int64_t)m * ldc + 4 * n4);
-    *dst = s;
+    if (!skipc) *dst = s;
     if (Cbf) *reinterpret_cast<u16x4*>(Cbf + (Cz - C) + (int64_t)m * ldc + 4 * n4) = bf16x4_bits(s);
   }
 }
@@ -706,7 +707,7 @@ __global__ void splitk_reduce4(const f4* __restrict__ ws, int splits, int M, int
 // C = sum over splits of the partials + beta*C + bias
 __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, int N, float* C, int64_t ldc,
                               int batch_div, int64_t sc1, int64_t sc2, float beta, const float* bias, uint16_t* Cbf,
-                              const float* resid) {
+                              const float* resid, int skipc) {
   const int z = blockIdx.y;
   const int64_t MN = (int64_t)M * N;
   const int z1 = z / batch_div, z2 = z % batch_div;
@@ -719,7 +720,7 @@ __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, i
     float* dst = Cz + (int64_t)m * ldc + n;
     if (beta != 0.f) s += beta * *dst;
     if (resid) s += resid[(int64_t)m * ldc + n];
-    *dst = s;
+    if (!skipc) *dst = s;
     if (Cbf) Cbf[(Cz - C) + (int64_t)m * ldc + n] = bf16_bits(s);
   }
 }
@@ -819,6 +820,7 @@ size_t gemm_workspace_bytes(const GemmArgs& g) {
 hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   if (g.resid && g.batch != 1) return hipErrorInvalidValue;
+  if (g.c_bf16_only && (!g.Cbf || g.beta != 0.f)) return hipErrorInvalidValue;
   // K == 0 needs no special case: the k loop is empty and the epilogue writes beta*C + bias
   Plan p = make_plan(g);
   if (p.splits > 1 && (size_t)p.splits * g.batch * g.M * g.N * sizeof(float) > ws_bytes) p.splits = 1;
@@ -847,11 +849,11 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
     dim3 rgrid((unsigned)std::min<int64_t>((MN / 4 + 255) / 256, 4096), g.batch);
     hipLaunchKernelGGL(splitk_reduce4, rgrid, dim3(256), 0, s, reinterpret_cast<const f4*>(ka.ws), p.splits, g.M,
                        g.N / 4, g.C, g.ldc, g.batch_div, g.sc1, g.sc2, g.beta, reinterpret_cast<const f4*>(g.bias),
-                       g.Cbf, g.resid);
+                       g.Cbf, g.resid, (int)g.c_bf16_only);
   } else {
     dim3 rgrid((unsigned)std::min<int64_t>((MN + 255) / 256, 4096), g.batch);
     hipLaunchKernelGGL(splitk_reduce, rgrid, dim3(256), 0, s, ka.ws, p.splits, g.M, g.N, g.C, g.ldc, g.batch_div,
-                       g.sc1, g.sc2, g.beta, g.bias, g.Cbf, g.resid);
+                       g.sc1, g.sc2, g.beta, g.bias, g.Cbf, g.resid, (int)g.c_bf16_only);
   }
   return hipGetLastError();
 }

@@ -47,6 +47,8 @@ struct GemmArgs {
   // optional residual added to the result, same layout and ldc as C (batch 1):
   // C = alpha A B + bias + beta C + resid
   const float* resid = nullptr;
+  // with Cbf and beta == 0: the bf16 copy alone is written, C (fp32) is left untouched
+  bool c_bf16_only = false;
 };
 
 size_t gemm_workspace_bytes(const GemmArgs& g);
@@ -56,6 +58,8 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
 hipError_t fill(float* p, float v, int64_t n, hipStream_t s);
 // dst[i] = bf16(src[i]), round to nearest even
 hipError_t to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
+// dst[i] = the float value of the bf16 bits src[i] (exact)
+hipError_t to_f32(const uint16_t* src, float* dst, int64_t n, hipStream_t s);
 hipError_t add_bcast(const float* a, const float* b, float* y, int64_t n, int64_t nb, hipStream_t s);
 hipError_t axpby(float* dst, const float* src, float alpha, float beta, int64_t n, hipStream_t s);
 // dst[r*ldd + c] = src[r*lds + c] (+ dst when beta == 1), c < cols

@@ -78,14 +78,14 @@ __global__ __launch_bounds__(NT) void ln_fwd_k(const float* __restrict__ x, cons
         const int c = lane + 64 * j;
         if (c < C) {
           const float o = (v[j] - mu) * rs * gamma[c] + beta[c];
-          yr[c] = o;
+          if (y) yr[c] = o;  // null: the bf16 copy alone
           if (ybf) ybf[r * C + c] = bf16_bits(o);
         }
       }
     } else {
       for (int c = lane; c < C; c += 64) {
         const float o = (xr[c] - mu) * rs * gamma[c] + beta[c];
-        yr[c] = o;
+        if (y) yr[c] = o;
         if (ybf) ybf[r * C + c] = bf16_bits(o);
       }
     }
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(NT) void ln_fwd4_k(const f4* __restrict__ x, const 
       const int c = lane + 64 * j;
       if (c < C4) {
         const f4 o = (v[j] - mu) * rs * gamma[c] + beta[c];
-        yr[c] = o;
+        if (y) yr[c] = o;  // null: the bf16 copy alone
         if (ybf) ybf[r * C4 + c] = u16x4{bf16_bits(o[0]), bf16_bits(o[1]), bf16_bits(o[2]), bf16_bits(o[3])};
       }
     }

@@ -62,6 +62,9 @@ struct TensorRec {
   // bf16 copies of data / grad used as contraction operands in the bf16 variant
   uint16_t* bf = nullptr;
   bool bf_valid = false;
+  // false: only the bf16 copy was written (an output whose readers take bf16); any
+  // fp32 reader first converts it back (Ctx::f32), exactly, from the bf16 values
+  bool f32_valid = true;
   uint16_t* gbf = nullptr;
   bool gbf_valid = false;
   // column sums (over every row of the [rows, cols] view) of the finished gradient,
@@ -243,10 +246,21 @@ struct Ctx {
     return h;
   }
 
-  // ops other than the cross-entropy read dense rows: a padded input is first
-  // copied to a dense tensor by a recorded compaction op
-  int dense_in(int h) {
+  // fp32 data of t: converted from its bf16 copy first when only that was written
+  const float* f32(TensorRec& t) {
+    if (!t.f32_valid) {
+      hip_check(to_f32(t.bf, t.data, t.storage(), s()), "to_f32");
+      t.f32_valid = true;
+    }
+    return t.data;
+  }
+
+  // ops other than the cross-entropy read dense fp32 rows: a padded input is first
+  // copied to a dense tensor by a recorded compaction op, and an input held only as
+  // bf16 is converted (bf16_ok: the op reads bf16 copies itself, so it is not)
+  int dense_in(int h, bool bf16_ok = false) {
     TensorRec& t = T(h);
+    if (!bf16_ok || t.padded()) f32(t);
     if (!t.padded()) return h;
     const int64_t rows = t.rows(), cols = t.cols(), ld = t.ld;
     const float* src = t.data;
@@ -346,6 +360,52 @@ struct Ctx {
     if (!bf16_mode()) return nullptr;
     if (!t.gbf) t.gbf = alloc_bf16(t);
     return t.gbf;
+  }
+
+  // Before a backward rule: the tensors it reads as fp32 data, converted where only
+  // their bf16 copy exists.  The contraction rules read their inputs through
+  // op_data (bf16 copies, or converted fp32 in the fp32 variant) and the fused
+  // attention reads q, k, v as bf16 and its output in fp32.
+  void f32_for_bwd(const Rec& r) {
+    switch (r.op) {
+      case OP_LINEAR:
+      case OP_LINEAR_RES:
+      case OP_MATMUL:
+      case OP_MATMUL_T:
+      case OP_ADD:
+      case OP_SCALE:
+      case OP_SUM:
+      case OP_RESHAPE:
+      case OP_EMBEDDING:
+      case OP_NARROW:
+      case OP_SPLIT_HEADS:
+      case OP_MERGE_HEADS:
+      case OP_COMPACT:
+        return;  // these read gradients only (or inputs through op_data)
+      case OP_TANH:
+      case OP_CSOFTMAX:
+        f32(T(r.out));
+        return;
+      case OP_GELU:
+      case OP_SOFTMAX_CE:
+        f32(T(r.in[0]));
+        return;
+      case OP_LAYERNORM:
+        f32(T(r.in[0]));
+        f32(T(r.in[1]));
+        return;
+      case OP_ATTENTION:
+        if (r.i1 == 1) {
+          f32(T(r.out));
+          return;
+        }
+        break;
+      default:
+        break;
+    }
+    for (int h : r.in)
+      if (h >= 0) f32(T(h));
+    f32(T(r.out));
   }
 
   // buffer for t's gradient column sums (non-leaf tensors only)
@@ -491,7 +551,7 @@ struct Opnd {
 
 Opnd op_data(Ctx& C, TensorRec& t) {
   if (C.bf16_mode()) return {C.data_bf16(t), true};
-  return {t.data, false};
+  return {C.f32(t), false};
 }
 Opnd op_grad(Ctx& C, TensorRec& t) {
   if (C.bf16_mode()) return {C.grad_bf16(t), true};
@@ -510,12 +570,12 @@ void set_b(GemmArgs& g, Opnd o) {
 
 // y[rows, N] = x[rows, K] @ w[K, N] (+ bias)
 void gemm_nn(Ctx& C, Opnd x, Opnd w, float* y, int64_t rows, int64_t K, int64_t N, float beta, const float* bias,
-             int64_t lda = -1, uint16_t* ybf = nullptr, const float* resid = nullptr) {
+             int64_t lda = -1, uint16_t* ybf = nullptr, const float* resid = nullptr, bool ybf_only = false) {
   GemmArgs g = C.gemm_base();
   g.M = (int)rows, g.N = (int)N, g.K = (int)K;
   set_a(g, x), g.lda = lda < 0 ? K : lda;
   set_b(g, w), g.ldb = N;
-  g.C = y, g.ldc = N, g.Cbf = ybf, g.resid = resid;
+  g.C = y, g.ldc = N, g.Cbf = ybf, g.resid = resid, g.c_bf16_only = ybf_only && ybf;
   g.beta = beta, g.bias = bias;
   C.run_gemm(g);
 }
@@ -973,7 +1033,7 @@ int tfb_tensor_info(tfb_ctx* ctx, tfb_tensor h, int64_t* shape, int* ndim, void*
     if (shape)
       for (int i = 0; i < t.ndim; ++i) shape[i] = t.shape[i];
     if (ndim) *ndim = t.ndim;
-    if (data) *data = t.data;
+    if (data) *data = const_cast<float*>(C.f32(t));
     if (grad) {
       C.materialize_zero(t);
       *grad = t.grad;
@@ -994,6 +1054,7 @@ int tfb_tensor_write(tfb_ctx* ctx, tfb_tensor h, const float* src, int64_t n) {
     else
       hip_check(hipMemcpyAsync(t.data, src, (size_t)n * sizeof(float), hipMemcpyHostToDevice, C.s()), "copy in");
     t.bf_valid = false;
+    t.f32_valid = true;
     hip_check(hipStreamSynchronize(C.s()), "sync");
   });
 }
@@ -1005,7 +1066,7 @@ int tfb_tensor_read(tfb_ctx* ctx, tfb_tensor h, int which, float* dst, int64_t n
     need(dst != nullptr && n == t.numel, TFB_ERR_SHAPE, "read of " + std::to_string(n) + " floats from " +
                                                             shape_str(t));
     need(which == 0 || which == 1, TFB_ERR_ARG, "which must be 0 (data) or 1 (grad)");
-    const float* src = t.data;
+    const float* src = which == 0 ? C.f32(t) : t.data;
     if (which == 1) {
       need(t.grad != nullptr, TFB_ERR_STATE, "tensor has no gradient");
       C.materialize_zero(t);
@@ -1149,16 +1210,22 @@ int tfb_tanh(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
   });
 }
 
-int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
+int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) { return tfb_gelu_ex(ctx, a, 0, y); }
+
+int tfb_gelu_ex(tfb_ctx* ctx, tfb_tensor a, int flags, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    need((flags & ~TFB_OUT_BF16_ONLY) == 0, TFB_ERR_ARG, "unknown tfb_gelu_ex flags");
     a = C.dense_in(a);
     TensorRec& A = C.T(a);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     int h = C.make_output(shape_vec(A));
     uint16_t* yb = C.twin_data(ctx->tensors[h]);
-    hip_check(gelu_fwd(ctx->tensors[a].data, ctx->tensors[h].data, yb, ctx->tensors[h].numel, C.s()), "gelu");
+    const bool only = yb && (flags & TFB_OUT_BF16_ONLY);
+    hip_check(gelu_fwd(ctx->tensors[a].data, only ? nullptr : ctx->tensors[h].data, yb, ctx->tensors[h].numel, C.s()),
+              "gelu");
     if (yb) ctx->tensors[h].bf_valid = true;
+    if (only) ctx->tensors[h].f32_valid = false;
     Rec r{OP_GELU};
     r.in[0] = a, r.out = h;
     C.record(r);
@@ -1167,10 +1234,11 @@ int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y) {
 }
 
 static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y, OpKind kind,
-                       bool bf_out = false, tfb_tensor res = -1) {
+                       int out_flags = 0, tfb_tensor res = -1) {
   return guarded([&] {
     Ctx C(ctx);
-    x = C.dense_in(x), w = C.dense_in(w);
+    // the contraction reads x and w as bf16 copies in the bf16 variant
+    x = C.dense_in(x, C.bf16_mode()), w = C.dense_in(w, C.bf16_mode());
     if (kind != OP_MATMUL && kind != OP_MATMUL_T) b = C.dense_in(b);
     if (kind == OP_LINEAR_RES) res = C.dense_in(res);
     TensorRec& X = C.T(x);
@@ -1212,12 +1280,14 @@ static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, t
     const float* wd = ctx->tensors[w].data;
     const Opnd xo = op_data(C, ctx->tensors[x]), wo = op_data(C, ctx->tensors[w]);
     (void)xd, (void)wd;
-    uint16_t* yb = bf_out ? C.twin_data(ctx->tensors[h]) : nullptr;
+    uint16_t* yb = out_flags ? C.twin_data(ctx->tensors[h]) : nullptr;
+    const bool only = yb && (out_flags & TFB_OUT_BF16_ONLY) && kind != OP_MATMUL_T;
     if (kind == OP_MATMUL_T)
       gemm_nt(C, xo, wo, yd, rows, K, N, 0.f, ld ? ld : N, yb);
     else
-      gemm_nn(C, xo, wo, yd, rows, K, N, 0.f, bias, -1, yb, rd);
+      gemm_nn(C, xo, wo, yd, rows, K, N, 0.f, bias, -1, yb, rd, only);
     if (yb) ctx->tensors[h].bf_valid = true;
+    if (only) ctx->tensors[h].f32_valid = false;
     Rec r{kind};
     r.in[0] = x, r.in[1] = w, r.in[2] = (kind == OP_LINEAR || kind == OP_LINEAR_RES) ? b : -1, r.out = h;
     if (kind == OP_LINEAR_RES) r.in[3] = res;
@@ -1237,17 +1307,24 @@ int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tenso
 }
 
 int tfb_linear_residual(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor r, tfb_tensor* y) {
-  return matmul_impl(ctx, x, w, b, y, OP_LINEAR_RES, false, r);
+  return matmul_impl(ctx, x, w, b, y, OP_LINEAR_RES, 0, r);
 }
 
 int tfb_linear_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int flags, tfb_tensor* y) {
-  if (flags & ~TFB_OUT_BF16_COPY) return guarded([&] { need(false, TFB_ERR_ARG, "unknown tfb_linear_ex flags"); });
-  return matmul_impl(ctx, x, w, b, y, OP_LINEAR, (flags & TFB_OUT_BF16_COPY) != 0);
+  if (flags & ~(TFB_OUT_BF16_COPY | TFB_OUT_BF16_ONLY))
+    return guarded([&] { need(false, TFB_ERR_ARG, "unknown tfb_linear_ex flags"); });
+  return matmul_impl(ctx, x, w, b, y, OP_LINEAR, flags);
 }
 
 int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y) {
+  return tfb_layernorm_ex(ctx, x, gamma, beta, eps, 0, y);
+}
+
+int tfb_layernorm_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, int flags,
+                     tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    need((flags & ~TFB_OUT_BF16_ONLY) == 0, TFB_ERR_ARG, "unknown tfb_layernorm_ex flags");
     x = C.dense_in(x), gamma = C.dense_in(gamma), beta = C.dense_in(beta);
     TensorRec& X = C.T(x);
     TensorRec& G = C.T(gamma);
@@ -1261,10 +1338,12 @@ int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta,
     float* mean = static_cast<float*>(C.scratch((size_t)rows * sizeof(float)));
     float* rstd = static_cast<float*>(C.scratch((size_t)rows * sizeof(float)));
     uint16_t* yb = C.twin_data(ctx->tensors[h]);
+    const bool only = yb && (flags & TFB_OUT_BF16_ONLY);
     hip_check(layernorm_fwd(ctx->tensors[x].data, ctx->tensors[gamma].data, ctx->tensors[beta].data,
-                            ctx->tensors[h].data, yb, mean, rstd, rows, Cc, eps, C.s()),
+                            only ? nullptr : ctx->tensors[h].data, yb, mean, rstd, rows, Cc, eps, C.s()),
               "layernorm");
     if (yb) ctx->tensors[h].bf_valid = true;
+    if (only) ctx->tensors[h].f32_valid = false;
     Rec r{OP_LAYERNORM};
     r.in[0] = x, r.in[1] = gamma, r.in[2] = beta, r.out = h, r.f = eps;
     r.s0 = mean, r.s1 = rstd;
@@ -1414,7 +1493,7 @@ int tfb_causal_softmax(tfb_ctx* ctx, tfb_tensor sx, tfb_tensor* y) {
 int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
-    qkv = C.dense_in(qkv);
+    qkv = C.dense_in(qkv, true);  // the fused kernels read the bf16 copy; the fp32 path converts below
     TensorRec& Q = C.T(qkv);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     need(Q.ndim == 3 && Q.shape[2] % 3 == 0 && heads > 0 && (Q.shape[2] / 3) % heads == 0, TFB_ERR_SHAPE,
@@ -1440,7 +1519,7 @@ int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y)
       return;
     }
     float* P = static_cast<float*>(C.scratch((size_t)B * H * T * T * sizeof(float)));
-    const float* q = ctx->tensors[qkv].data;
+    const float* q = C.f32(ctx->tensors[qkv]);
     float* yd = ctx->tensors[h].data;
     {  // S = (Q_h K_h^T) * scale, tiles on or below the diagonal
       GemmArgs a = C.gemm_base();
@@ -1499,6 +1578,7 @@ int tfb_softmax_cross_entropy_ex(tfb_ctx* ctx, tfb_tensor logits, const int32_t*
     size_t mark = ctx->arena.hi;
     void* ws = C.scratch(softmax_ce_workspace_bytes(rows));
     bool pre_written = false;
+    C.f32(ctx->tensors[logits]);
     hip_check(softmax_ce_fwd(ctx->tensors[logits].data, ctx->tensors[logits].stride(), tg, rows, V, lse,
                              ctx->tensors[h].data, ws, C.s(), pre, &pre_written),
               "softmax_ce");
@@ -1535,6 +1615,7 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
       if (!out.live) continue;
       C.settle(out);  // its gradient is complete: nothing else contributes
       if (out.gstate != G_VALID && out.gstate != G_BF16) continue;
+      C.f32_for_bwd(r);
       backward_rec(C, r);
     }
     for (TensorRec& t : ctx->tensors)
@@ -1790,7 +1871,7 @@ int tfb_sample_topk(tfb_ctx* ctx, tfb_tensor logits, int k, float temperature, c
     need(temperature > 0.f, TFB_ERR_ARG, "temperature must be positive");
     need(k >= 0, TFB_ERR_ARG, "k must be >= 0");
     need(L.cols() < (1LL << 31) && L.rows() < 65536, TFB_ERR_SHAPE, "logits too large");
-    hip_check(sample_topk(L.data, L.stride(), (int)L.rows(), (int)L.cols(), k, temperature, dev_uniforms, dev_out,
+    hip_check(sample_topk(C.f32(L), L.stride(), (int)L.rows(), (int)L.cols(), k, temperature, dev_uniforms, dev_out,
                           C.s()),
               "sample_topk");
   });
