@@ -541,6 +541,36 @@ def test_bf16_only_outputs(ctx, prec):
     ctx.set_precision("fp32")
 
 
+def test_gelu_of_bf16_only_input(ctx):
+    """A GELU whose input (a Linear's output) is held only as bf16 reads those bf16 values:
+    its output is exactly the plain GELU of the bf16-rounded product, and its gradients
+    stay within the bf16 tolerance of the oracle (300 and 1000 rows: the row-slab
+    backward and its ragged end)."""
+    ctx.set_precision("bf16")
+    for rows in (300, 1000):
+        xv, W, bv, Rv = rnd(141, (rows, 64)), rnd(142, (64, 96), 0.2), rnd(143, (96,), 0.1), rnd(144, (rows, 96))
+        x, w, b, R = (ctx.tensor(a.shape, a) for a in (xv, W, bv, Rv))
+        lin_plain = T.linear(x, w, b).numpy()
+        ctx.tape_reset()
+        lin = T.linear(x, w, b, bf16_only=True)
+        f = T.gelu(lin, bf16_only=True)
+        ctx.backward(T.sum_all(T.mul(T.tanh(f), R)))
+        got = f.numpy()
+        dx, dw, db = x.grad(), w.grad(), b.grad()
+        ctx.tape_reset()
+        rin = ctx.tensor(lin_plain.shape, _bf16_round(lin_plain))
+        want = _bf16_round(T.gelu(rin).numpy())
+        ctx.tape_reset()
+        np.testing.assert_array_equal(got, want)
+        ox, ow, ob = (E.Tensor(a.astype(np.float64)) for a in (xv, W, bv))
+        E.sum_all(E.mul(E.tanh(E.gelu(E.add(E.matmul(ox, ow), ob))), E.Tensor(Rv.astype(np.float64)))).backward()
+        for g_, o_, name in ((dx, ox.grad, "dx"), (dw, ow.grad, "dw"), (db, ob.grad, "db")):
+            assert_close(g_, o_, GRAD_TOL["bf16"], f"{name} ({rows} rows)")
+        for t in (x, w, b, R, rin):
+            t.release()
+    ctx.set_precision("fp32")
+
+
 def test_no_grad_records_nothing(ctx):
     a = ctx.tensor((2, 3), rnd(40, (2, 3)))
     ctx.set_grad_enabled(False)

@@ -139,7 +139,16 @@ __global__ __launch_bounds__(NT) void colsum4_stage1(const f4* __restrict__ g, i
 // gradient): workgroups as in colsum4_stage1 (256 columns x a slab of rows, 4
 // interleaved row groups, 4 rows in flight per thread), each element written once
 // and added into its column's slab partial.
-__global__ __launch_bounds__(NT) void gelu_bwd_cols4_k(const f4* __restrict__ g, const f4* __restrict__ x,
+__device__ __forceinline__ f4 load4(const f4* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ f4 load4(const u16x4* p, int64_t i) {  // exact float values of 4 bf16 numbers
+  const u16x4 b = p[i];
+  return f4{__uint_as_float((unsigned)b[0] << 16), __uint_as_float((unsigned)b[1] << 16),
+            __uint_as_float((unsigned)b[2] << 16), __uint_as_float((unsigned)b[3] << 16)};
+}
+
+// XT: f4 (fp32 input) or u16x4 (the input's bf16 copy)
+template <typename XT>
+__global__ __launch_bounds__(NT) void gelu_bwd_cols4_k(const f4* __restrict__ g, const XT* __restrict__ x,
                                                       f4* __restrict__ d, u16x4* __restrict__ dbf, float beta,
                                                       int64_t rows, int64_t cols4, int64_t rows_per,
                                                       f4* __restrict__ partial) {
@@ -163,12 +172,12 @@ __global__ __launch_bounds__(NT) void gelu_bwd_cols4_k(const f4* __restrict__ g,
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         gv[u] = g[(r + 4 * u) * cols4 + c];
-        xv[u] = x[(r + 4 * u) * cols4 + c];
+        xv[u] = load4(x, (r + 4 * u) * cols4 + c);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) one(gv[u], xv[u], (r + 4 * u) * cols4 + c);
     }
-    for (; r < r1; r += 4) one(g[r * cols4 + c], x[r * cols4 + c], r * cols4 + c);
+    for (; r < r1; r += 4) one(g[r * cols4 + c], load4(x, r * cols4 + c), r * cols4 + c);
   }
   if (ty > 0) sh[ty - 1][tx] = acc;
   __syncthreads();
@@ -322,6 +331,31 @@ hipError_t to_f32(const uint16_t* src, float* dst, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t gelu_fwd_bf(const uint16_t* a, float* y, uint16_t* ybf, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(a) & 7) == 0 && aligned16(y) &&
+      (reinterpret_cast<uintptr_t>(ybf) & 7) == 0) {
+    const u16x4* a4 = (const u16x4*)a;
+    f4* y4 = (f4*)y;
+    u16x4* b4 = (u16x4*)ybf;
+    auto f = [=] __device__(int64_t i) {
+      const f4 v = load4(a4, i);
+      const f4 o = {gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3])};
+      if (y4) y4[i] = o;
+      if (b4) b4[i] = u16x4{bf16_bits(o[0]), bf16_bits(o[1]), bf16_bits(o[2]), bf16_bits(o[3])};
+    };
+    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
+  } else {
+    auto f = [=] __device__(int64_t i) {
+      const float o = gelu_f(__uint_as_float((unsigned)a[i] << 16));
+      if (y) y[i] = o;
+      if (ybf) ybf[i] = bf16_bits(o);
+    };
+    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  }
+  return hipGetLastError();
+}
+
 hipError_t gelu_fwd(const float* a, float* y, uint16_t* ybf, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (n % 4 == 0 && aligned16(a) && aligned16(y) && (reinterpret_cast<uintptr_t>(ybf) & 7) == 0) {
@@ -389,16 +423,29 @@ size_t colsum_workspace_bytes(int64_t rows, int64_t cols) {
   return (size_t)std::max(colsum_parts(rows, cols), colsum4_parts(rows)) * cols * sizeof(float);
 }
 
+bool gelu_bwd_cols_fits(const float* g, const void* x, const float* d, const uint16_t* dbf, int64_t rows,
+                        int64_t cols, const void* ws) {
+  return rows >= 128 && cols % 4 == 0 && aligned16(g) && (reinterpret_cast<uintptr_t>(x) & 7) == 0 &&
+         aligned16(d) && aligned16(ws) && (reinterpret_cast<uintptr_t>(dbf) & 7) == 0;
+}
+
 hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t rows,
-                         int64_t cols, float* dcol, void* ws, hipStream_t s, bool* dcol_written) {
+                         int64_t cols, float* dcol, void* ws, hipStream_t s, bool* dcol_written, const uint16_t* xbf) {
   *dcol_written = false;
   float* partial = static_cast<float*>(ws);
-  if (rows < 128 || cols % 4 != 0 || !aligned16(g) || !aligned16(x) || !aligned16(d) || !aligned16(partial) ||
-      (reinterpret_cast<uintptr_t>(dbf) & 7) != 0)
+  if (!gelu_bwd_cols_fits(g, xbf ? (const void*)xbf : (const void*)x, d, dbf, rows, cols, ws) ||
+      (!xbf && !aligned16(x))) {
+    if (xbf) return hipErrorInvalidValue;  // the caller converts x and takes the fp32 form
     return gelu_bwd(g, x, d, dbf, beta, rows * cols, s);
+  }
   const int64_t parts = colsum4_parts(rows), rows_per = (rows + parts - 1) / parts, cols4 = cols / 4;
-  hipLaunchKernelGGL(gelu_bwd_cols4_k, dim3((unsigned)((cols4 + 63) / 64), (unsigned)parts), dim3(NT), 0, s,
-                     (const f4*)g, (const f4*)x, (f4*)d, (u16x4*)dbf, beta, rows, cols4, rows_per, (f4*)partial);
+  const dim3 grid((unsigned)((cols4 + 63) / 64), (unsigned)parts);
+  if (xbf)
+    hipLaunchKernelGGL(gelu_bwd_cols4_k<u16x4>, grid, dim3(NT), 0, s, (const f4*)g, (const u16x4*)xbf, (f4*)d,
+                       (u16x4*)dbf, beta, rows, cols4, rows_per, (f4*)partial);
+  else
+    hipLaunchKernelGGL(gelu_bwd_cols4_k<f4>, grid, dim3(NT), 0, s, (const f4*)g, (const f4*)x, (f4*)d, (u16x4*)dbf,
+                       beta, rows, cols4, rows_per, (f4*)partial);
   hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, (int)parts, cols,
                      dcol, 0.f);
   *dcol_written = true;

@@ -387,6 +387,7 @@ struct Ctx {
         f32(T(r.out));
         return;
       case OP_GELU:
+        return;  // the rule reads its input's bf16 copy or converts it
       case OP_SOFTMAX_CE:
         f32(T(r.in[0]));
         return;
@@ -665,13 +666,16 @@ void backward_rec(Ctx& C, const Rec& r) {
       if (dcol) {  // with the column sums a reading Linear takes as its bias gradient
         size_t mark = C.c->arena.hi;
         void* ws = C.scratch(colsum_workspace_bytes(a.rows(), a.cols()));
+        // an input held only as bf16 is read as such where the row-slab kernel fits
+        const bool abf = !a.f32_valid && gelu_bwd_cols_fits(g, a.bf, da.first, db, a.rows(), a.cols(), ws);
         bool written = false;
-        hip_check(gelu_bwd_cols(g, a.data, da.first, db, da.second, a.rows(), a.cols(), dcol, ws, s, &written),
+        hip_check(gelu_bwd_cols(g, abf ? nullptr : C.f32(a), da.first, db, da.second, a.rows(), a.cols(), dcol, ws,
+                                s, &written, abf ? a.bf : nullptr),
                   "gelu bwd");
         C.c->arena.hi = mark;
         a.gcol_valid = written;
       } else {
-        hip_check(gelu_bwd(g, a.data, da.first, db, da.second, out.numel, s), "gelu bwd");
+        hip_check(gelu_bwd(g, C.f32(a), da.first, db, da.second, out.numel, s), "gelu bwd");
       }
       if (db) a.gbf_valid = true;
       break;
@@ -1216,14 +1220,17 @@ int tfb_gelu_ex(tfb_ctx* ctx, tfb_tensor a, int flags, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
     need((flags & ~TFB_OUT_BF16_ONLY) == 0, TFB_ERR_ARG, "unknown tfb_gelu_ex flags");
-    a = C.dense_in(a);
+    a = C.dense_in(a, C.bf16_mode());  // an input held only as bf16 is read as such
     TensorRec& A = C.T(a);
     need(y != nullptr, TFB_ERR_ARG, "null output");
     int h = C.make_output(shape_vec(A));
     uint16_t* yb = C.twin_data(ctx->tensors[h]);
     const bool only = yb && (flags & TFB_OUT_BF16_ONLY);
-    hip_check(gelu_fwd(ctx->tensors[a].data, only ? nullptr : ctx->tensors[h].data, yb, ctx->tensors[h].numel, C.s()),
-              "gelu");
+    float* yd = only ? nullptr : ctx->tensors[h].data;
+    if (!ctx->tensors[a].f32_valid)
+      hip_check(gelu_fwd_bf(ctx->tensors[a].bf, yd, yb, ctx->tensors[h].numel, C.s()), "gelu");
+    else
+      hip_check(gelu_fwd(ctx->tensors[a].data, yd, yb, ctx->tensors[h].numel, C.s()), "gelu");
     if (yb) ctx->tensors[h].bf_valid = true;
     if (only) ctx->tensors[h].f32_valid = false;
     Rec r{OP_GELU};
