@@ -545,7 +545,8 @@ def test_gelu_of_bf16_only_input(ctx):
     """A GELU whose input (a Linear's output) is held only as bf16 reads those bf16 values:
     its output is exactly the plain GELU of the bf16-rounded product, and its gradients
     stay within the bf16 tolerance of the oracle (300 and 1000 rows: the row-slab
-    backward and its ragged end)."""
+    backward and its ragged end).  The product's gradient is then written only as the
+    bf16 copy its backward reads, so reading it is an error."""
     ctx.set_precision("bf16")
     for rows in (300, 1000):
         xv, W, bv, Rv = rnd(141, (rows, 64)), rnd(142, (64, 96), 0.2), rnd(143, (96,), 0.1), rnd(144, (rows, 96))
@@ -557,6 +558,8 @@ def test_gelu_of_bf16_only_input(ctx):
         ctx.backward(T.sum_all(T.mul(T.tanh(f), R)))
         got = f.numpy()
         dx, dw, db = x.grad(), w.grad(), b.grad()
+        with pytest.raises(T.TfbError):   # the product's gradient was kept only as bf16
+            lin.grad()
         ctx.tape_reset()
         rin = ctx.tensor(lin_plain.shape, _bf16_round(lin_plain))
         want = _bf16_round(T.gelu(rin).numpy())

@@ -160,8 +160,10 @@ __global__ __launch_bounds__(NT) void gelu_bwd_cols4_k(const f4* __restrict__ g,
   f4 acc = {0.f, 0.f, 0.f, 0.f};
   auto one = [&](f4 gv, f4 xv, int64_t i) {
     f4 v = {gv[0] * gelu_grad(xv[0]), gv[1] * gelu_grad(xv[1]), gv[2] * gelu_grad(xv[2]), gv[3] * gelu_grad(xv[3])};
-    if (beta != 0.f) v += d[i];
-    d[i] = v;
+    if (d) {  // null: the bf16 copy alone (beta is 0 then)
+      if (beta != 0.f) v += d[i];
+      d[i] = v;
+    }
     if (dbf) dbf[i] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
     acc += v;
   };
@@ -433,9 +435,10 @@ hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf
                          int64_t cols, float* dcol, void* ws, hipStream_t s, bool* dcol_written, const uint16_t* xbf) {
   *dcol_written = false;
   float* partial = static_cast<float*>(ws);
+  if (!d && (!dbf || beta != 0.f)) return hipErrorInvalidValue;
   if (!gelu_bwd_cols_fits(g, xbf ? (const void*)xbf : (const void*)x, d, dbf, rows, cols, ws) ||
       (!xbf && !aligned16(x))) {
-    if (xbf) return hipErrorInvalidValue;  // the caller converts x and takes the fp32 form
+    if (xbf || !d) return hipErrorInvalidValue;  // the caller takes the fp32 form (converting x)
     return gelu_bwd(g, x, d, dbf, beta, rows * cols, s);
   }
   const int64_t parts = colsum4_parts(rows), rows_per = (rows + parts - 1) / parts, cols4 = cols / 4;

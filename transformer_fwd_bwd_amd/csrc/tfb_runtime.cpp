@@ -65,6 +65,9 @@ struct TensorRec {
   // false: only the bf16 copy was written (an output whose readers take bf16); any
   // fp32 reader first converts it back (Ctx::f32), exactly, from the bf16 values
   bool f32_valid = true;
+  // made with the bf16-only output flag: where the contraction that produced it is
+  // the only reader of its gradient, that gradient too may be kept as bf16 alone
+  bool bf16_out = false;
   uint16_t* gbf = nullptr;
   bool gbf_valid = false;
   // column sums (over every row of the [rows, cols] view) of the finished gradient,
@@ -660,9 +663,30 @@ void backward_rec(Ctx& C, const Rec& r) {
     }
     case OP_GELU: {
       TensorRec& a = C.T(r.in[0]);
+      float* dcol = a.padded() ? nullptr : C.gcol_buf(a);
+      // A bf16-only input whose one gradient is read by its producer as bf16 (with the
+      // bias gradient from the column sums below): that copy alone, no fp32 gradient
+      if (dcol && a.bf16_out && a.uses == 1 && !a.gpend && a.gstate != G_VALID && C.grad_read_as_bf16(a)) {
+        uint16_t* db = C.twin_grad(a);
+        size_t mark = C.c->arena.hi;
+        void* ws = C.scratch(colsum_workspace_bytes(a.rows(), a.cols()));
+        const void* xin = a.f32_valid ? (const void*)a.data : (const void*)a.bf;
+        if (db && gelu_bwd_cols_fits(g, xin, nullptr, db, a.rows(), a.cols(), ws) &&
+            (!a.f32_valid || (reinterpret_cast<uintptr_t>(a.data) & 15) == 0)) {
+          bool written = false;
+          hip_check(gelu_bwd_cols(g, a.f32_valid ? a.data : nullptr, nullptr, db, 0.f, a.rows(), a.cols(), dcol, ws, s,
+                                  &written, a.f32_valid ? nullptr : a.bf),
+                    "gelu bwd");
+          C.c->arena.hi = mark;
+          a.gstate = G_BF16;
+          a.gbf_valid = true;
+          a.gcol_valid = written;
+          break;
+        }
+        C.c->arena.hi = mark;
+      }
       auto da = C.gdst(r.in[0]);
       uint16_t* db = C.twin_grad(a);
-      float* dcol = a.padded() ? nullptr : C.gcol_buf(a);
       if (dcol) {  // with the column sums a reading Linear takes as its bias gradient
         size_t mark = C.c->arena.hi;
         void* ws = C.scratch(colsum_workspace_bytes(a.rows(), a.cols()));
@@ -1072,6 +1096,7 @@ int tfb_tensor_read(tfb_ctx* ctx, tfb_tensor h, int which, float* dst, int64_t n
     need(which == 0 || which == 1, TFB_ERR_ARG, "which must be 0 (data) or 1 (grad)");
     const float* src = which == 0 ? C.f32(t) : t.data;
     if (which == 1) {
+      need(t.gstate != G_BF16, TFB_ERR_STATE, "the gradient was kept only as its bf16 copy");
       need(t.grad != nullptr, TFB_ERR_STATE, "tensor has no gradient");
       C.materialize_zero(t);
       src = t.grad;
@@ -1232,7 +1257,7 @@ int tfb_gelu_ex(tfb_ctx* ctx, tfb_tensor a, int flags, tfb_tensor* y) {
     else
       hip_check(gelu_fwd(ctx->tensors[a].data, yd, yb, ctx->tensors[h].numel, C.s()), "gelu");
     if (yb) ctx->tensors[h].bf_valid = true;
-    if (only) ctx->tensors[h].f32_valid = false;
+    if (only) ctx->tensors[h].f32_valid = false, ctx->tensors[h].bf16_out = true;
     Rec r{OP_GELU};
     r.in[0] = a, r.out = h;
     C.record(r);
@@ -1294,7 +1319,7 @@ static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, t
     else
       gemm_nn(C, xo, wo, yd, rows, K, N, 0.f, bias, -1, yb, rd, only);
     if (yb) ctx->tensors[h].bf_valid = true;
-    if (only) ctx->tensors[h].f32_valid = false;
+    if (only) ctx->tensors[h].f32_valid = false, ctx->tensors[h].bf16_out = true;
     Rec r{kind};
     r.in[0] = x, r.in[1] = w, r.in[2] = (kind == OP_LINEAR || kind == OP_LINEAR_RES) ? b : -1, r.out = h;
     if (kind == OP_LINEAR_RES) r.in[3] = res;
@@ -1350,7 +1375,7 @@ int tfb_layernorm_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor be
                             only ? nullptr : ctx->tensors[h].data, yb, mean, rstd, rows, Cc, eps, C.s()),
               "layernorm");
     if (yb) ctx->tensors[h].bf_valid = true;
-    if (only) ctx->tensors[h].f32_valid = false;
+    if (only) ctx->tensors[h].f32_valid = false, ctx->tensors[h].bf16_out = true;
     Rec r{OP_LAYERNORM};
     r.in[0] = x, r.in[1] = gamma, r.in[2] = beta, r.out = h, r.f = eps;
     r.s0 = mean, r.s1 = rstd;
