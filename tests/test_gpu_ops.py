@@ -86,6 +86,28 @@ def test_linear_residual_long_k_split(ctx, N):
                                   rnd(121, (200, N))], (200, N))
 
 
+@pytest.mark.parametrize("case", ["fwd_nn", "bwd_nt"])
+def test_linear_one_tile_per_cu(ctx, case):
+    """About one 128x192 output tile per CU (768 columns against ~8100 rows, long
+    reductions) takes the wide-tile kernel: forward x @ w + b + r (fwd_nn) or the
+    backward g @ w^T (bwd_nt), ragged in rows and in the reduction; the tiles at
+    the ragged end are checked on their own as well."""
+    ctx.set_precision("bf16")
+    if case == "fwd_nn":
+        arrays = [rnd(131, (8100, 2100)), rnd(132, (2100, 768), 0.02), rnd(133, (768,)), rnd(134, (8100, 768))]
+    else:
+        arrays = [rnd(135, (8100, 768)), rnd(136, (768, 2304), 0.03), rnd(137, (2304,)), rnd(138, (8100, 2304))]
+    R = rnd(139, arrays[3].shape)
+    out, grads = gpu_op_with_grads(ctx, lambda x, w, b, r: T.linear(x, w, b, residual=r), arrays, R)
+    ref, rgrads = oracle_op_with_grads(lambda x, w, b, r: E.add(r, E.add(E.matmul(x, w), b)), arrays, R)
+    ctx.set_precision("fp32")
+    assert_close(out, ref, FWD_TOL["bf16"], "forward")
+    assert_close(out[-100:], ref[-100:], FWD_TOL["bf16"], "forward, last rows")
+    for i, (g, r) in enumerate(zip(grads, rgrads)):
+        assert_close(g, r, GRAD_TOL["bf16"], f"grad {i}")
+    assert_close(grads[0][-100:], rgrads[0][-100:], GRAD_TOL["bf16"], "dx, last rows")
+
+
 def test_linear_long_k_split(ctx):
     # a long reduction (the dW contractions of the GPT have K = 8192) takes the split-K path
     check(ctx, "fp32", T.linear, lambda x, w, b: E.add(E.matmul(x, w), b),

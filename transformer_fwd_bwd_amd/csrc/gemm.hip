@@ -501,7 +501,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
   using SA = typename std::conditional<TRA, StageTr<BM, NT, BK>, Stage<BM, NT, A_RC, A_BF, BK>>::type;
   using SB = typename std::conditional<TRB, StageTr<BN, NT, BK>, Stage<BN, NT, !B_KC, B_BF, BK>>::type;
   bool done = false;
-  if constexpr (GEMM_PIPE && BF16 && A_BF && B_BF && TM * TN <= 4 && BK == 64) {
+  if constexpr (GEMM_PIPE && BF16 && A_BF && B_BF && TM * TN <= 6 && BK == 64) {
     // Interior tile free of the causal mask: a branch-free two-deep pipeline over
     // its whole k-tiles.  Tile j waits in register set j % 2; at step t the loads
     // of tile t + 2, the LDS stores of tile t + 1 and the MFMAs of tile t are
@@ -725,7 +725,7 @@ __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, i
   }
 }
 
-enum Cfg { CFG_128x128 = 1, CFG_128x64 = 2, CFG_256x128 = 3 };
+enum Cfg { CFG_128x128 = 1, CFG_128x64 = 2, CFG_256x128 = 3, CFG_128x192 = 4 };
 
 struct Plan {
   int cfg;
@@ -744,6 +744,14 @@ Plan make_plan(const GemmArgs& g) {
     // 4 waves of 128x64 read a quarter less LDS per MFMA; two workgroups fit per CU
     // only with 32-deep k-tiles, which pays off on vocabulary-sized products
     p.cfg = CFG_256x128, p.BM = 256, p.BN = 128;
+  } else if (g.prec == PREC_BF16 && g.a_bf16 && g.b_bf16 && g.causal_a == CAUSAL_NONE && !g.causal_out &&
+             g.N % 192 == 0 && g.K >= 2048 && (int64_t)((g.M + 127) / 128) * (g.N / 192) * g.batch <= 256 &&
+             (int64_t)((g.M + 127) / 128) * (g.N / 192) * g.batch > 192) {
+    // About one 128x192 tile per CU (N = 768 against 8192 rows): the 128x128
+    // tiling would leave half the CUs with two tiles and half with one.  These
+    // tiles take 92 KB of LDS and ~410 registers, one workgroup per CU; with
+    // long reductions that beats the 128x128 tiles (and their K split)
+    p.cfg = CFG_128x192, p.BM = 128, p.BN = 192;
   } else {
     p.cfg = CFG_128x128, p.BM = 128, p.BN = 128;
   }
@@ -759,7 +767,7 @@ Plan make_plan(const GemmArgs& g) {
   // on the GPT-2 dW products), with at least 512 k per item.
   p.splits = 1;
   if (g.causal_a == CAUSAL_NONE && !g.causal_out && g.K >= 1024) {
-    const int64_t slots = 256 * (p.bk == 32 ? 3 : 2);
+    const int64_t slots = 256 * (p.cfg == CFG_128x192 ? 1 : p.bk == 32 ? 3 : 2);
     const double tile_s_per_k = 2.0 * p.BM * p.BN / 1.0e12;  // ~1 TFLOP/s per resident workgroup
     const double out_bytes = 4.0 * g.M * g.N * g.batch;
     double best = 0.0;
@@ -838,6 +846,8 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
     e = launch_prec<2, 2, 2, 2>(ka, p.bk, grid, s);
   else if (p.cfg == CFG_256x128)
     e = launch_prec<2, 2, 4, 2>(ka, 32, grid, s);
+  else if (p.cfg == CFG_128x192)
+    e = launch_layout<2, 2, 2, 3, 64, true, true, true>(ka, grid, s);
   else
     e = launch_prec<4, 1, 1, 2>(ka, p.bk, grid, s);
   if (e != hipSuccess || p.splits == 1) return e;
