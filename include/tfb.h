@@ -122,6 +122,10 @@ int tfb_matmul(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y);
 /* y = x[..., C] @ w[V, C]^T, the weight-tied LM head.  Backward dx = g w,
  * dw = g^T x.  [GPT2-4, "Loading the weights": weight tying] */
 int tfb_matmul_t(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y);
+/* tfb_matmul_t with flags (TFB_OUT_BF16_COPY, TFB_OUT_BF16_ONLY below; unknown
+ * flags: TFB_ERR_ARG).  With TFB_OUT_BF16_ONLY the logits are stored as bf16
+ * alone and tfb_softmax_cross_entropy reads them as such. */
+int tfb_matmul_t_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, int flags, tfb_tensor* y);
 /* y = x @ w + b as one op (MatMul followed by the bias Add, fused into the
  * contraction's epilogue); w is [in, out] as GPT-2 stores it.
  * [GPT2-4, "Loading the weights": Linear weights stored [in, out]] */
@@ -132,7 +136,7 @@ int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tenso
  * value and is ignored in the fp32 variant.  Unknown flags: TFB_ERR_ARG.
  * [GPT2-4, "Loading the weights": Linear weights stored [in, out]] */
 #define TFB_OUT_BF16_COPY 1
-/* Output flag of tfb_linear_ex, tfb_layernorm_ex and tfb_gelu_ex (bf16 variant):
+/* Output flag of tfb_linear_ex, tfb_matmul_t_ex, tfb_layernorm_ex and tfb_gelu_ex (bf16 variant):
  * only the bf16 copy of y is written, for an output whose readers take bf16
  * (the contractions, the fused attention).  A reader that needs fp32 data (any
  * other op, tfb_tensor_read, tfb_tensor_info) gets the exact float values of

@@ -412,6 +412,42 @@ def test_linear_bf16_copy_changes_nothing(ctx):
     ctx.set_precision("fp32")
 
 
+@pytest.mark.parametrize("grad_only", [False, True])
+def test_cross_entropy_of_bf16_only_logits(ctx, grad_only):
+    """Logits stored as bf16 alone (an LM head with the bf16-only output flag, rows
+    padded past 1030 columns) are exactly the bf16 rounding of the plain product; the
+    cross-entropy reads them directly: its loss is the oracle's on those bf16 values,
+    and the gradients (upstream gradient 1, then 3) stay within the bf16 tolerance."""
+    V, C, rows = 1030, 64, 300
+    x, w = rnd(47, (rows, C)), rnd(48, (V, C), 0.2)
+    tg = S.random_ids(49, (rows,), V)
+    ctx.set_precision("bf16")
+    xt, wt = ctx.tensor(x.shape, x), ctx.tensor(w.shape, w)
+    plain = T.matmul_t(xt, wt).numpy()
+    ctx.tape_reset()
+    for up in (1.0, 3.0):
+        logits = T.matmul_t(xt, wt, bf16_only=True)
+        got = logits.numpy()
+        np.testing.assert_array_equal(got, _bf16_round(plain))
+        loss = T.softmax_cross_entropy(logits, tg, bf16_grad_only=grad_only)
+        ctx.backward(T.scale(loss, up))
+        lv, dx, dw = loss.numpy(), xt.grad(), wt.grad()
+        if grad_only:
+            with pytest.raises(T.TfbError):
+                logits.grad()
+        ctx.tape_reset()
+        want = E.softmax_cross_entropy(E.Tensor(got.astype(np.float64)), tg).data
+        assert_close(lv, want, 1e-5, f"loss (upstream {up})")
+        ox, ow = E.Tensor(x.astype(np.float64)), E.Tensor(w.astype(np.float64))
+        E.scale(E.softmax_cross_entropy(E.matmul_t(ox, ow), tg), up).backward()
+        assert_close(dx, ox.grad, GRAD_TOL["bf16"], f"dx (upstream {up})")
+        assert_close(dw, ow.grad, GRAD_TOL["bf16"], f"dw (upstream {up})")
+        ctx.zero_grad([xt, wt])   # leaf gradients add up over backward passes
+    xt.release()
+    wt.release()
+    ctx.set_precision("fp32")
+
+
 @pytest.mark.parametrize("prec", PRECS)
 def test_cross_entropy_bf16_only_logit_gradient(ctx, prec):
     """With the bf16-only option, an LM head's gradients are those of the plain call

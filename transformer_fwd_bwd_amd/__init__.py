@@ -49,6 +49,7 @@ SIGNATURES = {
     "tfb_gelu": [c_void_p, c_int32, P(c_int32)],
     "tfb_matmul": [c_void_p, c_int32, c_int32, P(c_int32)],
     "tfb_matmul_t": [c_void_p, c_int32, c_int32, P(c_int32)],
+    "tfb_matmul_t_ex": [c_void_p, c_int32, c_int32, c_int32, P(c_int32)],
     "tfb_linear": [c_void_p, c_int32, c_int32, c_int32, P(c_int32)],
     "tfb_linear_ex": [c_void_p, c_int32, c_int32, c_int32, c_int32, P(c_int32)],
     "tfb_layernorm_ex": [c_void_p, c_int32, c_int32, c_int32, c_float, c_int32, P(c_int32)],
@@ -303,7 +304,11 @@ def matmul(x: Tensor, w: Tensor) -> Tensor:
     return _out(x.ctx, _lib.tfb_matmul, x.h, w.h)
 
 
-def matmul_t(x: Tensor, w: Tensor) -> Tensor:
+def matmul_t(x: Tensor, w: Tensor, bf16_only: bool = False) -> Tensor:
+    """y = x @ w^T.  bf16_only: in the bf16 variant y is stored as bf16 alone (the
+    cross-entropy reads such logits directly)."""
+    if bf16_only:
+        return _out(x.ctx, _lib.tfb_matmul_t_ex, x.h, w.h, OUT_BF16_ONLY)
     return _out(x.ctx, _lib.tfb_matmul_t, x.h, w.h)
 
 

@@ -124,16 +124,19 @@ size_t softmax_ce_workspace_bytes(int64_t rows);
 // logits rows have V valid columns at a row stride of ld >= V.  dlbf (optional):
 // the bf16 gradient of the logits for an upstream gradient of 1 is also written
 // there, in softmax_ce_bwd's expression, where the one-pass path runs
-// (*dlbf_written says whether it did)
+// (*dlbf_written says whether it did).  logits_bf (optional, logits then unused):
+// the logits stored as bf16, read by the one-pass kernel (hipErrorInvalidValue
+// where softmax_ce_bf16_fits is false); dlbf may be null then
+bool softmax_ce_bf16_fits(int64_t ld, int64_t V, const uint16_t* logits_bf);
 hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* targets, int64_t rows, int64_t V,
                           float* lse, float* loss, void* ws, hipStream_t s, uint16_t* dlbf = nullptr,
-                          bool* dlbf_written = nullptr);
+                          bool* dlbf_written = nullptr, const uint16_t* logits_bf = nullptr);
 // dl may be null when dlbf is given (and beta == 0): only the bf16 copy is written.
 // skip_if_unit: nothing is done when g_scalar[0] == 1 (checked on the device): the
-// forward already wrote that gradient into dlbf.
+// forward already wrote that gradient into dlbf.  logits_bf: as in softmax_ce_fwd.
 hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* targets, const float* lse,
                           const float* g_scalar, float* dl, uint16_t* dlbf, int64_t rows, int64_t V, float beta,
-                          hipStream_t s, bool skip_if_unit = false);
+                          hipStream_t s, bool skip_if_unit = false, const uint16_t* logits_bf = nullptr);
 
 // ---- fused causal attention, bf16 variant (attention.hip)
 // qkv: bf16 [B, T, 3C] (q | k | v thirds, head h = columns h*hs .. h*hs+hs-1 of each third)

@@ -647,12 +647,30 @@ __global__ __launch_bounds__(NT) void ce_fwd4_k(const float* __restrict__ logits
 }
 
 
+// logits read as float, from fp32 or from bf16 storage
+__device__ __forceinline__ float ld_x(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_x(const uint16_t* p, int64_t i) { return __uint_as_float((unsigned)p[i] << 16); }
+__device__ __forceinline__ f4 ld_x4(const float* p, int64_t i4) { return reinterpret_cast<const f4*>(p)[i4]; }
+__device__ __forceinline__ f4 ld_x4(const uint16_t* p, int64_t i4) {
+  const u16x4 v = reinterpret_cast<const u16x4*>(p)[i4];
+  return f4{__uint_as_float((unsigned)v[0] << 16), __uint_as_float((unsigned)v[1] << 16),
+            __uint_as_float((unsigned)v[2] << 16), __uint_as_float((unsigned)v[3] << 16)};
+}
+
 // Cross-entropy forward that also writes the bf16 gradient the backward would
 // write for an upstream gradient of 1, (p - onehot) / rows, in the backward's own
 // expression: one 1024-thread workgroup per row holds the row in registers (PER
 // float4 per thread), so the logits are read once for both passes.
-template <int PER>
-__global__ __launch_bounds__(1024) void ce_fwd_grad4_k(const float* __restrict__ logits, int64_t ld,
+// bf16 logits stay packed in registers (converted at each use): under 64 VGPRs,
+// two 1024-thread workgroups share a CU and one's reductions overlap the other's loads
+__device__ __forceinline__ f4 cvt4(f4 v) { return v; }
+__device__ __forceinline__ f4 cvt4(u16x4 v) {
+  return f4{__uint_as_float((unsigned)v[0] << 16), __uint_as_float((unsigned)v[1] << 16),
+            __uint_as_float((unsigned)v[2] << 16), __uint_as_float((unsigned)v[3] << 16)};
+}
+template <int PER, class X>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(sizeof(X) == 2 ? 8 : 1)))
+void ce_fwd_grad4_k(const X* __restrict__ logits, int64_t ld,
                                                        const int32_t* __restrict__ tgt, int64_t V,
                                                        float* __restrict__ lse, float* __restrict__ loss_rows,
                                                        uint16_t* __restrict__ dlbf, float gn) {
@@ -660,20 +678,43 @@ __global__ __launch_bounds__(1024) void ce_fwd_grad4_k(const float* __restrict__
   __shared__ float red[NW];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t r = blockIdx.x;
-  const float* lr = logits + r * ld;
-  const f4* lr4 = reinterpret_cast<const f4*>(lr);
-  const int64_t V4 = V / 4;
+  const X* lr = logits + r * ld;
+  const int V4 = (int)(V / 4);
   const int tail = (int)(V - 4 * V4);
-  f4 x[PER];
+  using XS = typename std::conditional<sizeof(X) == 2, u16x4, f4>::type;
+  XS xs[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int64_t i = tid + (int64_t)u * 1024;
-    x[u] = i < V4 ? lr4[i] : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    const int i = tid + u * 1024;
+    if constexpr (sizeof(X) == 2) {
+      // buffer loads over the row's whole groups of 4: one offset register serves
+      // every load, and the hardware's range check returns 0 past the end (replaced
+      // by -inf below)
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)lr, (short)0, (int)(V4 * 8), 0x00020000);
+      const auto raw = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(i * 8), 0, 0);
+      const u16x4 ninf = {0xFF80, 0xFF80, 0xFF80, 0xFF80};  // bf16 -inf
+      xs[u] = i < V4 ? __builtin_bit_cast(u16x4, raw) : ninf;
+    } else {
+      xs[u] = i < V4 ? ld_x4(lr, i) : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
   }
-  const float xt = tid < tail ? lr[4 * V4 + tid] : -INFINITY;
+  // each pass converts the packed values afresh: an empty asm marks them as changed so
+  // that the compiler cannot keep the first pass's fp32 copies live instead
+  auto refresh = [&]() {
+    if constexpr (sizeof(X) == 2) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(xs[u]));
+    }
+  };
+#define x_(u) cvt4(xs[u])
+  const float xt = tid < tail ? ld_x(lr, 4 * V4 + tid) : -INFINITY;
   float m = xt;
 #pragma unroll
-  for (int u = 0; u < PER; ++u) m = fmaxf(m, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
+  for (int u = 0; u < PER; ++u) {
+    const f4 x = x_(u);
+    m = fmaxf(m, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  }
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   if (lane == 0) red[w] = m;
   __syncthreads();
@@ -682,8 +723,12 @@ __global__ __launch_bounds__(1024) void ce_fwd_grad4_k(const float* __restrict__
   for (int i = 1; i < NW; ++i) m = fmaxf(m, red[i]);
   __syncthreads();
   float sum = ce_exp(xt - m);
+  refresh();
 #pragma unroll
-  for (int u = 0; u < PER; ++u) sum += (ce_exp(x[u][0] - m) + ce_exp(x[u][1] - m)) + (ce_exp(x[u][2] - m) + ce_exp(x[u][3] - m));
+  for (int u = 0; u < PER; ++u) {
+    const f4 x = x_(u);
+    sum += (ce_exp(x[0] - m) + ce_exp(x[1] - m)) + (ce_exp(x[2] - m) + ce_exp(x[3] - m));
+  }
   for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
   if (lane == 0) red[w] = sum;
   __syncthreads();
@@ -694,18 +739,31 @@ __global__ __launch_bounds__(1024) void ce_fwd_grad4_k(const float* __restrict__
   const int t = tgt[r];
   if (tid == 0) {
     lse[r] = L;
-    loss_rows[r] = (t >= 0 && t < V) ? fminf(L - lr[t], 69.07755278982137f) : NAN;
+    loss_rows[r] = (t >= 0 && t < V) ? fminf(L - ld_x(lr, t), 69.07755278982137f) : NAN;
   }
+  if (!dlbf) return;  // no gradient wanted
   u16x4* br4 = reinterpret_cast<u16x4*>(dlbf + r * ld);
+  refresh();
+  __amdgpu_buffer_rsrc_t ws_;
+  if constexpr (sizeof(X) == 2)
+    ws_ = __builtin_amdgcn_make_buffer_rsrc((void*)br4, (short)0, (int)(V4 * 8), 0x00020000);
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int64_t i = tid + (int64_t)u * 1024;
+    const int i = tid + u * 1024;
     if (i >= V4) break;
+    const f4 x = x_(u);
     f4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = gn * (ce_exp(x[u][e] - L) - (4 * i + e == t ? 1.f : 0.f));
-    br4[i] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
+    for (int e = 0; e < 4; ++e) v[e] = gn * (ce_exp(x[e] - L) - (4 * i + e == t ? 1.f : 0.f));
+    const u16x4 b = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
+    if constexpr (sizeof(X) == 2) {
+      typedef int i32x2 __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, b), ws_, (int)(i * 8), 0, 0);
+    } else {
+      br4[i] = b;
+    }
   }
+#undef x_
   if (tid < tail) {
     const int64_t c = 4 * V4 + tid;
     dlbf[r * ld + c] = bf16_bits(gn * (ce_exp(xt - L) - (c == t ? 1.f : 0.f)));
@@ -713,7 +771,8 @@ __global__ __launch_bounds__(1024) void ce_fwd_grad4_k(const float* __restrict__
 }
 
 // float4 form of ce_bwd_k (rows 16-byte aligned): two float4 per thread in flight
-__global__ __launch_bounds__(NT) void ce_bwd4_k(const float* __restrict__ logits, int64_t ld,
+template <class X>
+__global__ __launch_bounds__(NT) void ce_bwd4_k(const X* __restrict__ logits, int64_t ld,
                                                 const int32_t* __restrict__ tgt, const float* __restrict__ lse,
                                                 const float* __restrict__ gsc, float* __restrict__ dl,
                                                 uint16_t* __restrict__ dlbf, int64_t rows, int64_t V, float beta,
@@ -723,7 +782,7 @@ __global__ __launch_bounds__(NT) void ce_bwd4_k(const float* __restrict__ logits
   const float gn = gsc[0] / (float)rows;
   const float L = lse[r];
   const int t = tgt[r];
-  const f4* lr4 = reinterpret_cast<const f4*>(logits + r * ld);
+  const X* lr = logits + r * ld;
   f4* dr4 = dl ? reinterpret_cast<f4*>(dl + r * ld) : nullptr;  // null: the bf16 copy alone
   u16x4* br4 = dlbf ? reinterpret_cast<u16x4*>(dlbf + r * ld) : nullptr;
   const int64_t V4 = V / 4;
@@ -732,7 +791,7 @@ __global__ __launch_bounds__(NT) void ce_bwd4_k(const float* __restrict__ logits
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int64_t i = c + u * NT;
-      if (i < V4) x[u] = lr4[i];
+      if (i < V4) x[u] = ld_x4(lr, i);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -748,10 +807,9 @@ __global__ __launch_bounds__(NT) void ce_bwd4_k(const float* __restrict__ logits
       if (br4) br4[i] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
     }
   }
-  const float* lr = logits + r * ld;
   float* dr = dl ? dl + r * ld : nullptr;
   for (int64_t c = 4 * V4 + threadIdx.x; c < V; c += NT) {
-    float v = gn * (ce_exp(lr[c] - L) - (c == t ? 1.f : 0.f));
+    float v = gn * (ce_exp(ld_x(lr, c) - L) - (c == t ? 1.f : 0.f));
     if (dr) {
       if (beta != 0.f) v += dr[c];
       dr[c] = v;
@@ -881,24 +939,44 @@ hipError_t causal_softmax_bwd(const float* g, const float* p, float* d, int64_t 
 
 size_t softmax_ce_workspace_bytes(int64_t rows) { return (size_t)rows * sizeof(float); }
 
+namespace {
+template <class X>
+void launch_ce_fwd_grad(const X* logits, int64_t ld, const int32_t* targets, int64_t rows, int64_t V, float* lse,
+                        float* loss_rows, uint16_t* dlbf, hipStream_t s) {
+  const int64_t per = (V / 4 + 1023) / 1024;
+  const float gn = 1.f / (float)rows;  // the backward's g / rows for g = 1
+  const dim3 grid((unsigned)rows), block(1024);
+  if (per <= 4)
+    hipLaunchKernelGGL((ce_fwd_grad4_k<4, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+  else if (per <= 8)
+    hipLaunchKernelGGL((ce_fwd_grad4_k<8, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+  else if (per <= 13)
+    hipLaunchKernelGGL((ce_fwd_grad4_k<13, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+  else
+    hipLaunchKernelGGL((ce_fwd_grad4_k<16, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+}
+}  // namespace
+
+bool softmax_ce_bf16_fits(int64_t ld, int64_t V, const uint16_t* logits_bf) {
+  const int64_t per = (V / 4 + 1023) / 1024;
+  return ld % 4 == 0 && (reinterpret_cast<uintptr_t>(logits_bf) & 7) == 0 && per >= 1 && per <= 16;
+}
+
 hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* targets, int64_t rows, int64_t V,
-                          float* lse, float* loss, void* ws, hipStream_t s, uint16_t* dlbf, bool* dlbf_written) {
+                          float* lse, float* loss, void* ws, hipStream_t s, uint16_t* dlbf, bool* dlbf_written,
+                          const uint16_t* logits_bf) {
   if (dlbf_written) *dlbf_written = false;
   if (rows <= 0) return hipSuccess;
   float* loss_rows = static_cast<float*>(ws);
   const int64_t per = (V / 4 + 1023) / 1024;
-  if (dlbf && ld % 4 == 0 && aligned16(logits) && (reinterpret_cast<uintptr_t>(dlbf) & 7) == 0 && per >= 1 &&
-      per <= 16) {
-    const float gn = 1.f / (float)rows;  // the backward's g / rows for g = 1
-    const dim3 grid((unsigned)rows), block(1024);
-    if (per <= 4)
-      hipLaunchKernelGGL(ce_fwd_grad4_k<4>, grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
-    else if (per <= 8)
-      hipLaunchKernelGGL(ce_fwd_grad4_k<8>, grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
-    else if (per <= 13)
-      hipLaunchKernelGGL(ce_fwd_grad4_k<13>, grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
-    else
-      hipLaunchKernelGGL(ce_fwd_grad4_k<16>, grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+  if (logits_bf) {  // bf16 logits: the one-pass kernel only (the gradient where dlbf is given)
+    if (!softmax_ce_bf16_fits(ld, V, logits_bf) || (reinterpret_cast<uintptr_t>(dlbf) & 7) != 0)
+      return hipErrorInvalidValue;
+    launch_ce_fwd_grad(logits_bf, ld, targets, rows, V, lse, loss_rows, dlbf, s);
+    if (dlbf_written) *dlbf_written = dlbf != nullptr;
+  } else if (dlbf && ld % 4 == 0 && aligned16(logits) && (reinterpret_cast<uintptr_t>(dlbf) & 7) == 0 && per >= 1 &&
+             per <= 16) {
+    launch_ce_fwd_grad(logits, ld, targets, rows, V, lse, loss_rows, dlbf, s);
     if (dlbf_written) *dlbf_written = true;
   } else if (ld % 4 == 0 && aligned16(logits))
     hipLaunchKernelGGL(ce_fwd4_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
@@ -910,11 +988,18 @@ hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* target
 
 hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* targets, const float* lse,
                           const float* g_scalar, float* dl, uint16_t* dlbf, int64_t rows, int64_t V, float beta,
-                          hipStream_t s, bool skip_if_unit) {
+                          hipStream_t s, bool skip_if_unit, const uint16_t* logits_bf) {
   if (rows <= 0) return hipSuccess;
   if (!dl && (!dlbf || beta != 0.f)) return hipErrorInvalidValue;
+  if (logits_bf) {
+    if (!softmax_ce_bf16_fits(ld, V, logits_bf) || !aligned16(dl) || (reinterpret_cast<uintptr_t>(dlbf) & 7) != 0)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(ce_bwd4_k<uint16_t>, dim3((unsigned)rows), dim3(NT), 0, s, logits_bf, ld, targets, lse, g_scalar,
+                       dl, dlbf, rows, V, beta, (int)skip_if_unit);
+    return hipGetLastError();
+  }
   if (ld % 4 == 0 && aligned16(logits) && aligned16(dl) && (reinterpret_cast<uintptr_t>(dlbf) & 7) == 0)
-    hipLaunchKernelGGL(ce_bwd4_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
+    hipLaunchKernelGGL(ce_bwd4_k<float>, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
                        rows, V, beta, (int)skip_if_unit);
   else
     hipLaunchKernelGGL(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,

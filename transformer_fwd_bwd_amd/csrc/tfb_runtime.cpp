@@ -392,8 +392,7 @@ struct Ctx {
       case OP_GELU:
         return;  // the rule reads its input's bf16 copy or converts it
       case OP_SOFTMAX_CE:
-        f32(T(r.in[0]));
-        return;
+        return;  // the rule reads bf16-only logits as such or converts them
       case OP_LAYERNORM:
         f32(T(r.in[0]));
         f32(T(r.in[1]));
@@ -585,12 +584,12 @@ void gemm_nn(Ctx& C, Opnd x, Opnd w, float* y, int64_t rows, int64_t K, int64_t 
 }
 // y[rows, N] = x[rows, K] @ w[N, K]^T
 void gemm_nt(Ctx& C, Opnd x, Opnd w, float* y, int64_t rows, int64_t K, int64_t N, float beta, int64_t ldc = -1,
-             uint16_t* ybf = nullptr) {
+             uint16_t* ybf = nullptr, bool bf16_only = false) {
   GemmArgs g = C.gemm_base();
   g.M = (int)rows, g.N = (int)N, g.K = (int)K;
   set_a(g, x), g.lda = K;
   set_b(g, w), g.ldb = K, g.b_kcontig = true;
-  g.C = y, g.ldc = ldc < 0 ? N : ldc, g.Cbf = ybf;
+  g.C = y, g.ldc = ldc < 0 ? N : ldc, g.Cbf = ybf, g.c_bf16_only = bf16_only;
   g.beta = beta;
   C.run_gemm(g);
 }
@@ -921,14 +920,17 @@ void backward_rec(Ctx& C, const Rec& r) {
     }
     case OP_SOFTMAX_CE: {
       TensorRec& lg = C.T(r.in[0]);
+      // logits held only as bf16 are read as such
+      const uint16_t* lgb = !lg.f32_valid && softmax_ce_bf16_fits(lg.stride(), lg.cols(), lg.bf) ? lg.bf : nullptr;
+      const float* lgd = lgb ? nullptr : C.f32(lg);
       if ((r.i0 & TFB_CE_GRAD_BF16_ONLY) && lg.uses == 1 && !lg.leaf && !lg.gpend && lg.gstate != G_VALID &&
           C.grad_read_as_bf16(lg)) {
         // the logits' only gradient, read by their producer as bf16: that copy alone
         // (written by the forward already when r.i1 == 1: then only for g != 1)
         uint16_t* dlb = C.twin_grad(lg);
-        hip_check(softmax_ce_bwd(lg.data, lg.stride(), static_cast<const int32_t*>(r.s0),
+        hip_check(softmax_ce_bwd(lgd, lg.stride(), static_cast<const int32_t*>(r.s0),
                                  static_cast<const float*>(r.s1), g, nullptr, dlb, lg.rows(), lg.cols(), 0.f, s,
-                                 r.i1 == 1),
+                                 r.i1 == 1, lgb),
                   "softmax_ce bwd");
         lg.gstate = G_BF16;
         lg.gbf_valid = true;
@@ -936,8 +938,9 @@ void backward_rec(Ctx& C, const Rec& r) {
       }
       auto dl = C.gdst(r.in[0]);
       uint16_t* dlb = C.twin_grad(lg);
-      hip_check(softmax_ce_bwd(lg.data, lg.stride(), static_cast<const int32_t*>(r.s0),
-                               static_cast<const float*>(r.s1), g, dl.first, dlb, lg.rows(), lg.cols(), dl.second, s),
+      hip_check(softmax_ce_bwd(lgd, lg.stride(), static_cast<const int32_t*>(r.s0),
+                               static_cast<const float*>(r.s1), g, dl.first, dlb, lg.rows(), lg.cols(), dl.second, s,
+                               false, lgb),
                 "softmax_ce bwd");
       if (dlb) lg.gbf_valid = true;
       break;
@@ -1313,9 +1316,9 @@ static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, t
     const Opnd xo = op_data(C, ctx->tensors[x]), wo = op_data(C, ctx->tensors[w]);
     (void)xd, (void)wd;
     uint16_t* yb = out_flags ? C.twin_data(ctx->tensors[h]) : nullptr;
-    const bool only = yb && (out_flags & TFB_OUT_BF16_ONLY) && kind != OP_MATMUL_T;
+    const bool only = yb && (out_flags & TFB_OUT_BF16_ONLY);
     if (kind == OP_MATMUL_T)
-      gemm_nt(C, xo, wo, yd, rows, K, N, 0.f, ld ? ld : N, yb);
+      gemm_nt(C, xo, wo, yd, rows, K, N, 0.f, ld ? ld : N, yb, only);
     else
       gemm_nn(C, xo, wo, yd, rows, K, N, 0.f, bias, -1, yb, rd, only);
     if (yb) ctx->tensors[h].bf_valid = true;
@@ -1333,6 +1336,11 @@ int tfb_matmul(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y) {
 }
 int tfb_matmul_t(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor* y) {
   return matmul_impl(ctx, x, w, -1, y, OP_MATMUL_T);
+}
+int tfb_matmul_t_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, int flags, tfb_tensor* y) {
+  if (flags & ~(TFB_OUT_BF16_COPY | TFB_OUT_BF16_ONLY))
+    return guarded([&] { need(false, TFB_ERR_ARG, "unknown tfb_matmul_t_ex flags"); });
+  return matmul_impl(ctx, x, w, -1, y, OP_MATMUL_T, flags);
 }
 int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor* y) {
   return matmul_impl(ctx, x, w, b, y, OP_LINEAR);
@@ -1610,9 +1618,12 @@ int tfb_softmax_cross_entropy_ex(tfb_ctx* ctx, tfb_tensor logits, const int32_t*
     size_t mark = ctx->arena.hi;
     void* ws = C.scratch(softmax_ce_workspace_bytes(rows));
     bool pre_written = false;
-    C.f32(ctx->tensors[logits]);
-    hip_check(softmax_ce_fwd(ctx->tensors[logits].data, ctx->tensors[logits].stride(), tg, rows, V, lse,
-                             ctx->tensors[h].data, ws, C.s(), pre, &pre_written),
+    // logits held only as bf16 are read as such
+    TensorRec& LG = ctx->tensors[logits];
+    const bool lbf = !LG.f32_valid && softmax_ce_bf16_fits(LG.stride(), V, LG.bf);
+    if (!lbf) C.f32(LG);
+    hip_check(softmax_ce_fwd(lbf ? nullptr : LG.data, LG.stride(), tg, rows, V, lse, ctx->tensors[h].data, ws, C.s(),
+                             pre, &pre_written, lbf ? LG.bf : nullptr),
               "softmax_ce");
     ctx->arena.hi = mark;
     Rec r{OP_SOFTMAX_CE};

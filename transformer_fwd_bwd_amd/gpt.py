@@ -48,9 +48,9 @@ class Gpt:
         tok = embedding(P["wte.weight"], ids, B)                          # [B, T, C]
         pos = reshape(embedding(P["wpe.weight"], self.positions(T), 1), (T, C))
         x = add(tok, pos)
-        # Outputs whose only readers are contractions, the fused attention or the GELU
-        # are kept as bf16 copies alone in the bf16 variant (the LayerNorms', qkv, the
-        # MLP's first product, the GELU's)
+        # Outputs whose only readers are contractions, the fused attention, the GELU or
+        # the cross-entropy are kept as bf16 copies alone in the bf16 variant (the
+        # LayerNorms', qkv, the MLP's first product, the GELU's, the logits)
         for i in range(self.n_layer):
             p = f"h.{i}."
             h = layernorm(x, P[p + "ln_1.weight"], P[p + "ln_1.bias"], bf16_only=True)
@@ -61,7 +61,7 @@ class Gpt:
             f = gelu(linear(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"], bf16_only=True), bf16_only=True)
             x = linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"], residual=x)
         xf = layernorm(x, P["ln_f.weight"], P["ln_f.bias"], bf16_only=True)
-        return matmul_t(xf, P["wte.weight"])
+        return matmul_t(xf, P["wte.weight"], bf16_only=True)   # read by the fused cross-entropy
 
     def loss(self, inputs, targets):
         """(mean cross-entropy, logits).  In the bf16 variant the logits' gradient exists
