@@ -61,34 +61,38 @@ __device__ __forceinline__ u16x4 pack4(f4 v) { return u16x4{f2bf(v[0]), f2bf(v[1
 
 // row index (within a 32x32 block) held by accumulator r of lane half h
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+// the part of it that depends on r alone (a constant after unrolling)
+__device__ __forceinline__ constexpr int acc_row0(int r) { return 8 * (r >> 2) + (r & 3); }
 
 // --- staging ------------------------------------------------------------------------------
 // A KVB x HS block of rows (keys or queries) goes global -> registers -> LDS as
 // X[row][HS + 8], one 16-byte chunk of 8 values per transfer; rows past
 // `valid` are zero.  The register step lets the next block be fetched while
 // the current one is multiplied.
-template <int HS>
+template <int HS, int NTH = NT>
 struct RowStage {
-  static constexpr int CPR = HS / 8, CHUNKS = KVB * CPR, PER = (CHUNKS + NT - 1) / NT;
+  static constexpr int CPR = HS / 8, CHUNKS = KVB * CPR, PER = (CHUNKS + NTH - 1) / NTH;
   u16x8 v[PER];
+  // Buffer loads over the first `valid` rows of src (valid * ld * 2 < 2^31 bytes):
+  // the hardware's range check returns zeros for rows past them, and the
+  // per-thread offsets are loop-invariant, so a load costs one add.
   __device__ __forceinline__ void load(const unsigned short* __restrict__ src, int64_t ld, int row0, int valid,
                                        int tid) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, valid * (int)ld * 2, 0x00020000);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * NT;
-      if (CHUNKS % NT != 0 && c >= CHUNKS) break;
+      const int c = tid + i * NTH;
+      if (CHUNKS % NTH != 0 && c >= CHUNKS) break;
       const int row = c / CPR, col = (c % CPR) * 8;
-      // branch-free: read a row clamped into range (valid >= 1), then zero it if it was past the end
-      const int rr = min(row0 + row, valid - 1);
-      const u16x8 t = *reinterpret_cast<const u16x8*>(src + (int64_t)rr * ld + col);
-      v[i] = row0 + row < valid ? t : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      v[i] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, ((row0 + row) * (int)ld + col) * 2, 0, 0));
     }
   }
   __device__ __forceinline__ void store(unsigned short* dst, int tid) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * NT;
-      if (CHUNKS % NT != 0 && c >= CHUNKS) break;
+      const int c = tid + i * NTH;
+      if (CHUNKS % NTH != 0 && c >= CHUNKS) break;
       *reinterpret_cast<u16x8*>(dst + (c / CPR) * (HS + 8) + (c % CPR) * 8) = v[i];
     }
   }
@@ -158,16 +162,25 @@ struct AttnArgs {
 };
 
 // ------------------------------------------------------------------------------------ forward
+// A workgroup of 4 waves owns 64 queries.  Waves w and w + 2 hold the same 32
+// queries and take alternate 64-key blocks (even blocks: waves 0-1, odd: 2-3), so
+// each wave's chain of dependent blocks is half as long as the query block's; the
+// two partial results (output, running sum, reference) are merged through LDS.
+constexpr int FQ = 64;  // queries per forward workgroup
 template <int HS>
 __global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned short Ks[2][KVB * (HS + 8)];
-  __shared__ __attribute__((aligned(16))) unsigned short Vs[2][KVB * (HS + 8)];
+  constexpr int XS = KVB * (HS + 8), HT = NT / 2;
+  // [K half 0 | K half 1 | V half 0 | V half 1]; after the loop: the merge area
+  __shared__ __attribute__((aligned(16))) unsigned short S[4 * XS];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform by construction
-  const BlockId id = block_id((a.T + 127) / 128, true);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform by construction
+  const int w = wv & 1, half = wv >> 1, htid = tid & (HT - 1);
+  unsigned short* Kh = S + half * XS;
+  unsigned short* Vh = S + (2 + half) * XS;
+  const BlockId id = block_id((a.T + FQ - 1) / FQ, true);
   if (id.bh >= a.B * a.H) return;
   const int bh = id.bh, b = bh / a.H, hd = bh % a.H;
-  const int q0 = id.x * 128, qw = q0 + 32 * w, q = qw + l32;
+  const int q0 = id.x * FQ, qw = q0 + 32 * w, q = qw + l32;
   const int64_t ld = 3LL * a.C;
   const unsigned short* base = a.qkv + (int64_t)b * a.T * ld + hd * HS;
   const unsigned short* Kg = base + a.C;
@@ -185,49 +198,50 @@ __global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
   float m = -INFINITY, l = 0.f;
   const float sc = a.scale * LOG2E;
 
-  const int kv_end = min(a.T, q0 + 128);
-  RowStage<HS> kst, vst;
-  kst.load(Kg, ld, 0, a.T, tid);
-  vst.load(Vg, ld, 0, a.T, tid);
-  kst.store(Ks[0], tid);
-  vst.store(Vs[0], tid);
-  __syncthreads();
-  int buf = 0;
-  for (int kv0 = 0; kv0 < kv_end; kv0 += KVB) {
-    const bool more = kv0 + KVB < kv_end;
-    if (more) {
-      kst.load(Kg, ld, kv0 + KVB, a.T, tid);
-      vst.load(Vg, ld, kv0 + KVB, a.T, tid);
+  const int kv_end = min(a.T, q0 + FQ);
+  // each half stages its own block: one LDS buffer, the next block waits in registers
+  const int nit = (kv_end + 2 * KVB - 1) / (2 * KVB);
+  RowStage<HS, HT> kst, vst;
+  kst.load(Kg, ld, half * KVB, a.T, htid);
+  vst.load(Vg, ld, half * KVB, a.T, htid);
+  for (int j = 0; j < nit; ++j) {
+    const int kv0 = (2 * j + half) * KVB;
+    kst.store(Kh, htid);
+    vst.store(Vh, htid);
+    __syncthreads();
+    if (j + 1 < nit) {
+      kst.load(Kg, ld, kv0 + 2 * KVB, a.T, htid);
+      vst.load(Vg, ld, kv0 + 2 * KVB, a.T, htid);
     }
-    if (kv0 <= qw + 31) {  // else every key of this block is after every query of this wave
+    // else every key of this block is after every query of this wave (or past the end)
+    if (kv0 < kv_end && kv0 <= qw + 31) {
       f32x16 st[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < HS / 16; ++s) st[kt] = mfma(frag_r<HS>(Ks[buf], 32 * kt + l32, s, h), qf[s], st[kt]);
+        for (int s = 0; s < HS / 16; ++s) st[kt] = mfma(frag_r<HS>(Kh, 32 * kt + l32, s, h), qf[s], st[kt]);
       }
-      // every key of the block visible to every query of the wave: no mask
+      // every key of the block visible to every query of the wave: no mask.  Other
+      // blocks set the scores of hidden keys to -inf; the empty asm keeps that a
+      // real (wave-uniform) branch instead of selects that every block would run.
       const bool full = kv0 + KVB - 1 <= qw && kv0 + KVB <= a.T;
-      float mx = -INFINITY;
-      if (full) {
+      if (!full) {
+        asm volatile("");
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt) {
+          const int lim = min(q, a.T - 1) - kv0 - 32 * kt - 4 * h;  // key visible: acc_row0(r) <= lim
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
-        mx *= sc;
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * kt + acc_row(r, h);
-            const bool vis = key <= q && key < a.T;
-            st[kt][r] = vis ? st[kt][r] : -INFINITY;
-            mx = fmaxf(mx, vis ? st[kt][r] * sc : -INFINITY);
-          }
+          for (int r = 0; r < 16; ++r) st[kt][r] = acc_row0(r) <= lim ? st[kt][r] : -INFINITY;
+        }
       }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
+      mx *= sc;
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       // m is the reference the running sum l and the output o are scaled to.  It
       // only moves when a score exceeds it by more than RESCALE_MARGIN (log2
@@ -261,15 +275,37 @@ __global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
       for (int s = 0; s < KVB / 16; ++s) {
         const bf16x8 pb = pack8(st[s >> 1], 8 * (s & 1));
 #pragma unroll
-        for (int i = 0; i < HS / 32; ++i) o[i] = mfma(frag_tr<HS>(Vs[buf], 32 * i, s, lane), pb, o[i]);
+        for (int i = 0; i < HS / 32; ++i) o[i] = mfma(frag_tr<HS>(Vh, 32 * i, s, lane), pb, o[i]);
       }
     }
-    if (more) {
-      kst.store(Ks[buf ^ 1], tid);
-      vst.store(Vs[buf ^ 1], tid);
-    }
     __syncthreads();
-    buf ^= 1;
+  }
+  // merge: waves 2-3 leave output, reference and sum in LDS (lane-major, so the
+  // accesses are conflict-free); waves 0-1 rescale both parts to the larger reference
+  constexpr int NR = HS / 32 * 16;
+  float* Pm = reinterpret_cast<float*>(S);
+  const int slot = w * 64 + lane;
+  if (half == 1) {
+#pragma unroll
+    for (int i = 0; i < HS / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Pm[(i * 16 + r) * HT + slot] = o[i][r];
+    Pm[NR * HT + slot] = m;
+    Pm[(NR + 1) * HT + slot] = l;
+  }
+  __syncthreads();
+  if (half == 1) return;
+  {
+    const float m1 = Pm[NR * HT + slot], l1 = Pm[(NR + 1) * HT + slot];
+    const float mn = fmaxf(m, m1);
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float a0 = fexp2(m - mref), a1 = fexp2(m1 - mref);  // a part that saw no key: 0
+    l = l * a0 + l1 * a1;
+#pragma unroll
+    for (int i = 0; i < HS / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] = o[i][r] * a0 + Pm[(i * 16 + r) * HT + slot] * a1;
+    m = mn;
   }
   if (q < a.T) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -363,22 +399,21 @@ __global__ __launch_bounds__(NT, 2) void attn_dq_k(AttnArgs a) {
       // dS^T = P^T (dP^T - D); a block every query of the wave sees whole needs no
       // mask.  The test is wave-uniform: one scalar branch per block, then a
       // straight loop either way.
+      // Hidden keys get score -inf (so p = 0) in a real branch, as in the forward
       const bool full = kv0 + KVB - 1 <= qw && kv0 + KVB <= a.T;
-      if (full) {
+      if (!full) {
+        asm volatile("");
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt) {
+          const int lim = min(q, a.T - 1) - kv0 - 32 * kt - 4 * h;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) st[kt][r] = fexp2(fmaf(st[kt][r], sc, -lse)) * (dp[kt][r] - Dq);
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * kt + acc_row(r, h);
-            const float p = fexp2(fmaf(st[kt][r], sc, -lse));
-            st[kt][r] = (key <= q && key < a.T) ? p * (dp[kt][r] - Dq) : 0.f;
-          }
+          for (int r = 0; r < 16; ++r) st[kt][r] = acc_row0(r) <= lim ? st[kt][r] : -INFINITY;
+        }
       }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[kt][r] = fexp2(fmaf(st[kt][r], sc, -lse)) * (dp[kt][r] - Dq);
 #pragma unroll
       for (int s = 0; s < KVB / 16; ++s) {
         const bf16x8 sb = pack8(st[s >> 1], 8 * (s & 1));
@@ -567,19 +602,25 @@ unsigned attn_grid(int T, int BH) { return (unsigned)(((T + 127) / 128) * ((BH +
 
 }  // namespace
 
-bool flash_attention_supported(int hs, int64_t C) { return (hs == 64 || hs == 32) && C % 8 == 0; }
+// the staging's buffer offsets are 32-bit: one batch entry's rows must span < 2 GB
+static bool offsets_fit(int64_t T, int64_t C) { return (T + 2 * KVB) * 3 * C * 2 < (1LL << 31); }
+
+bool flash_attention_supported(int hs, int64_t C, int64_t T) {
+  return (hs == 64 || hs == 32) && C % 8 == 0 && offsets_fit(T, C);
+}
 
 hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, uint16_t* ybf, float* lse, int B, int T, int H, int C,
                                float scale, hipStream_t s) {
   if (B <= 0 || T <= 0) return hipSuccess;
+  if (!offsets_fit(T, C)) return hipErrorInvalidValue;
   AttnArgs a{};
   a.qkv = qkv, a.out = y, a.outbf = ybf, a.lse = lse, a.B = B, a.T = T, a.H = H, a.C = C, a.scale = scale;
-  dim3 grid(attn_grid(T, B * H));
+  const dim3 fgrid((unsigned)(((T + FQ - 1) / FQ) * ((B * H + 7) / 8 * 8)));
   const int hs = C / H;
   if (hs == 64)
-    hipLaunchKernelGGL(attn_fwd_k<64>, grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(attn_fwd_k<64>, fgrid, dim3(NT), 0, s, a);
   else if (hs == 32)
-    hipLaunchKernelGGL(attn_fwd_k<32>, grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(attn_fwd_k<32>, fgrid, dim3(NT), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -589,6 +630,7 @@ hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float*
                                const float* lse, float* D, float* dqkv, uint16_t* dqkv_bf, float beta, int B, int T,
                                int H, int C, float scale, hipStream_t s) {
   if (B <= 0 || T <= 0) return hipSuccess;
+  if (!offsets_fit(T, C)) return hipErrorInvalidValue;
   AttnArgs a{};
   a.qkv = qkv, a.y = y, a.dyf = dyf, a.dy = dy, a.lse = const_cast<float*>(lse), a.D = D, a.out = dqkv;
   a.outbf = dqkv_bf;

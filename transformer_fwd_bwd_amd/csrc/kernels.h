@@ -141,7 +141,7 @@ hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* target
 // ---- fused causal attention, bf16 variant (attention.hip)
 // qkv: bf16 [B, T, 3C] (q | k | v thirds, head h = columns h*hs .. h*hs+hs-1 of each third)
 // y: fp32 [B, T, C]; lse: [B*H, T] base-2 log-sum-exp of the scaled scores (saved for backward)
-bool flash_attention_supported(int hs, int64_t C);
+bool flash_attention_supported(int hs, int64_t C, int64_t T);
 hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, uint16_t* ybf, float* lse, int B, int T, int H, int C,
                                float scale, hipStream_t s);
 // dqkv = beta*dqkv + d(qkv); D: [B*H, T] scratch

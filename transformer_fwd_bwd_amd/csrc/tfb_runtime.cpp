@@ -1543,7 +1543,7 @@ int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y)
     need(B * H < 65536, TFB_ERR_SHAPE, "too many (batch, head) pairs");
     const float scale = 1.f / std::sqrt((float)hs);
     int h = C.make_output({B, T, Cc});
-    if (C.bf16_mode() && flash_attention_supported((int)hs, Cc) && T < (1 << 30)) {
+    if (C.bf16_mode() && flash_attention_supported((int)hs, Cc, T)) {
       // bf16 variant: fused kernels, no T x T buffers
       const uint16_t* qb = C.data_bf16(ctx->tensors[qkv]);
       float* lse = static_cast<float*>(C.scratch((size_t)B * H * T * sizeof(float)));
