@@ -74,6 +74,12 @@ __global__ void axpby_k(float* __restrict__ d, const float* __restrict__ s, floa
   }
 }
 
+__global__ void axpby_batch_k(AxpbyJobs jobs) {
+  const AxpbyJob& j = jobs.j[blockIdx.y];
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < j.n; i += (int64_t)gridDim.x * NT)
+    j.dst[i] = j.beta != 0.f ? j.src[i] + j.beta * j.dst[i] : j.src[i];
+}
+
 __device__ __forceinline__ float gelu_f(float x) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
   const float u = c * (x + 0.044715f * x * x * x);
@@ -265,6 +271,17 @@ hipError_t add_bcast(const float* a, const float* b, float* y, int64_t n, int64_
 hipError_t axpby(float* dst, const float* src, float alpha, float beta, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(axpby_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, dst, src, alpha, beta, n);
+  return hipGetLastError();
+}
+
+hipError_t axpby_batch(const AxpbyJobs& jobs, hipStream_t s) {
+  if (jobs.count <= 0) return hipSuccess;
+  if (jobs.count > AXPBY_BATCH) return hipErrorInvalidValue;
+  int64_t nmax = 0;
+  for (int i = 0; i < jobs.count; ++i) nmax = std::max(nmax, jobs.j[i].n);
+  if (nmax <= 0) return hipSuccess;
+  hipLaunchKernelGGL(axpby_batch_k, dim3((unsigned)std::min<int64_t>((nmax + NT - 1) / NT, 64), jobs.count),
+                     dim3(NT), 0, s, jobs);
   return hipGetLastError();
 }
 

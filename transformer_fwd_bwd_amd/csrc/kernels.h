@@ -62,6 +62,20 @@ hipError_t to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 hipError_t to_f32(const uint16_t* src, float* dst, int64_t n, hipStream_t s);
 hipError_t add_bcast(const float* a, const float* b, float* y, int64_t n, int64_t nb, hipStream_t s);
 hipError_t axpby(float* dst, const float* src, float alpha, float beta, int64_t n, hipStream_t s);
+// Several independent dst = src + beta * dst (beta 0: dst = src) in one launch; the
+// destinations must be pairwise distinct (the jobs run concurrently)
+constexpr int AXPBY_BATCH = 64;
+struct AxpbyJob {
+  float* dst;
+  const float* src;
+  int64_t n;
+  float beta;
+};
+struct AxpbyJobs {
+  AxpbyJob j[AXPBY_BATCH];
+  int count = 0;
+};
+hipError_t axpby_batch(const AxpbyJobs& jobs, hipStream_t s);
 // dst[r*ldd + c] = src[r*lds + c] (+ dst when beta == 1), c < cols
 hipError_t copy_pitched(const float* src, int64_t lds, float* dst, int64_t ldd, int64_t rows, int64_t cols,
                         float beta, hipStream_t s);

@@ -171,6 +171,9 @@ struct tfb_ctx {
   std::deque<TensorRec> tensors;  // deque: handles' references survive growth
   std::vector<int> free_handles;
   std::vector<Rec> tape;
+  // bias gradients taken from column sums, added in one launch at the end of the
+  // backward pass (nothing reads a leaf's gradient before then)
+  AxpbyJobs bias_jobs;
 };
 
 struct tfb_kv {
@@ -292,6 +295,7 @@ struct Ctx {
     TensorRec& t = T(h);
     settle(t);
     ensure_grad_buffer(t);
+    flush_bias_into(t.grad);
     t.gbf_valid = false;
     t.gcol_valid = false;
     if (t.gstate == G_VALID) return {t.grad, 1.f};
@@ -308,6 +312,7 @@ struct Ctx {
   };
   GradDst gdst_src(int h) {
     TensorRec& t = T(h);
+    flush_bias_into(t.grad);
     if (t.gpend) {
       ensure_grad_buffer(t);
       const float* src = t.gpend;
@@ -412,6 +417,28 @@ struct Ctx {
   }
 
   // buffer for t's gradient column sums (non-leaf tensors only)
+  // a queued bias job must land before any other contribution to the same gradient
+  void flush_bias_into(const float* g) {
+    for (int i = 0; g && i < c->bias_jobs.count; ++i)
+      if (c->bias_jobs.j[i].dst == g) {
+        flush_bias();
+        return;
+      }
+  }
+  void flush_bias() {
+    hip_check(axpby_batch(c->bias_jobs, s()), "bias gradients");
+    c->bias_jobs.count = 0;
+  }
+  // dst = src + beta * dst at the end of the pass (earlier if dst is already queued:
+  // a second contribution must see the first)
+  void defer_bias(float* dst, const float* src, int64_t n, float beta) {
+    AxpbyJobs& q = c->bias_jobs;
+    bool clash = q.count == AXPBY_BATCH;
+    for (int i = 0; i < q.count && !clash; ++i) clash = q.j[i].dst == dst;
+    if (clash) flush_bias();
+    q.j[q.count++] = AxpbyJob{dst, src, n, beta};
+  }
+
   float* gcol_buf(TensorRec& t) {
     if (t.leaf || t.cols() <= 0) return nullptr;
     if (!t.gcol) t.gcol = static_cast<float*>(c->arena.alloc_step((size_t)t.cols() * sizeof(float)));
@@ -728,7 +755,7 @@ void backward_rec(Ctx& C, const Rec& r) {
       if (r.op != OP_MATMUL) {
         auto db = C.gdst(r.in[2]);
         if (out.gcol_valid && out.cols() == N) {  // summed by the kernel that finished g
-          hip_check(axpby(db.first, out.gcol, 1.f, db.second, N, s), "linear bias bwd");
+          C.defer_bias(db.first, out.gcol, N, db.second);
         } else {
           size_t mark = C.c->arena.hi;
           void* ws = C.scratch(colsum_workspace_bytes(rows, N));
@@ -1652,6 +1679,7 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
     C.ensure_grad_buffer(L);
     hip_check(fill(L.grad, 1.f, 1, C.s()), "seed");
     L.gstate = G_VALID;
+    ctx->bias_jobs.count = 0;
     for (int i = (int)ctx->tape.size() - 1; i >= 0; --i) {
       const Rec& r = ctx->tape[i];
       TensorRec& out = ctx->tensors[r.out];
@@ -1661,6 +1689,7 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
       C.f32_for_bwd(r);
       backward_rec(C, r);
     }
+    C.flush_bias();
     for (TensorRec& t : ctx->tensors)
       if (t.live) C.settle(t);
   });
