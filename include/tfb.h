@@ -140,11 +140,11 @@ int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tenso
  * only the bf16 copy of y is written, for an output whose readers take bf16
  * (the contractions, the fused attention).  A reader that needs fp32 data (any
  * other op, tfb_tensor_read, tfb_tensor_info) gets the exact float values of
- * those bf16 numbers, converted on first use.  In the backward, where the
- * contraction that produced y is the only reader of y's gradient and that
- * gradient has one contribution, the gradient too may be written only as the
- * bf16 copy the contraction reads (with its column sums for the bias gradient);
- * reading it then gives TFB_ERR_STATE.  Ignored in the fp32 variant. */
+ * those bf16 numbers, converted on first use.  In the backward, where y's
+ * gradient has one contribution and its only reader takes bf16 (the contraction
+ * that produced y, with column sums for the bias gradient, or the GELU that
+ * produced y), that gradient too may be written only as bf16; reading it then
+ * gives TFB_ERR_STATE.  Ignored in the fp32 variant. */
 #define TFB_OUT_BF16_ONLY 2
 /* y = r + (x @ w + b): a Linear and the residual Add that follows it, with the
  * Add done in the product's epilogue (r is read there, once).  r has the

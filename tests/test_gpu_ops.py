@@ -632,6 +632,37 @@ def test_gelu_of_bf16_only_input(ctx):
     ctx.set_precision("fp32")
 
 
+def test_mlp_gelu_gradient_kept_as_bf16(ctx):
+    """An MLP block as the GPT runs it: Linear (bf16-only output) -> GELU (bf16-only
+    output) -> Linear.  The second Linear's dX is then written as bf16 alone and the
+    GELU backward reads it that way (reading the GELU output's gradient is an error);
+    every parameter gradient stays within the bf16 tolerance of the oracle (300 rows:
+    the row-slab backward and its ragged end)."""
+    ctx.set_precision("bf16")
+    xv, W1, b1, W2, b2 = rnd(151, (300, 64)), rnd(152, (64, 96), 0.2), rnd(153, (96,), 0.1), rnd(154, (96, 40), 0.2), \
+        rnd(155, (40,), 0.1)
+    R = rnd(156, (300, 40))
+    ts = [ctx.tensor(a.shape, a) for a in (xv, W1, b1, W2, b2)]
+    x, w1, bb1, w2, bb2 = ts
+    f = T.gelu(T.linear(x, w1, bb1, bf16_only=True), bf16_only=True)
+    y = T.linear(f, w2, bb2)
+    Rt = ctx.tensor(R.shape, R)
+    ctx.backward(T.sum_all(T.mul(y, Rt)))
+    grads = [t.grad() for t in ts]
+    with pytest.raises(T.TfbError):
+        f.grad()
+    ctx.tape_reset()
+    for t in ts + [Rt]:
+        t.release()
+    ctx.set_precision("fp32")
+    os_ = [E.Tensor(a.astype(np.float64)) for a in (xv, W1, b1, W2, b2)]
+    ox, ow1, ob1, ow2, ob2 = os_
+    E.sum_all(E.mul(E.add(E.matmul(E.gelu(E.add(E.matmul(ox, ow1), ob1)), ow2), ob2),
+                    E.Tensor(R.astype(np.float64)))).backward()
+    for g_, o_, name in zip(grads, os_, ("dx", "dw1", "db1", "dw2", "db2")):
+        assert_close(g_, o_.grad, GRAD_TOL["bf16"], name)
+
+
 def test_no_grad_records_nothing(ctx):
     a = ctx.tensor((2, 3), rnd(40, (2, 3)))
     ctx.set_grad_enabled(False)

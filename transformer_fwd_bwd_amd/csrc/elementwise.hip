@@ -8,6 +8,8 @@
 // deterministic.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace tfb {
@@ -152,9 +154,9 @@ __device__ __forceinline__ f4 load4(const u16x4* p, int64_t i) {  // exact float
             __uint_as_float((unsigned)b[2] << 16), __uint_as_float((unsigned)b[3] << 16)};
 }
 
-// XT: f4 (fp32 input) or u16x4 (the input's bf16 copy)
-template <typename XT>
-__global__ __launch_bounds__(NT) void gelu_bwd_cols4_k(const f4* __restrict__ g, const XT* __restrict__ x,
+// XT: f4 (fp32 input) or u16x4 (the input's bf16 copy); GT likewise for the upstream gradient
+template <typename XT, typename GT>
+__global__ __launch_bounds__(NT) void gelu_bwd_cols4_k(const GT* __restrict__ g, const XT* __restrict__ x,
                                                       f4* __restrict__ d, u16x4* __restrict__ dbf, float beta,
                                                       int64_t rows, int64_t cols4, int64_t rows_per,
                                                       f4* __restrict__ partial) {
@@ -179,13 +181,13 @@ __global__ __launch_bounds__(NT) void gelu_bwd_cols4_k(const f4* __restrict__ g,
       f4 gv[4], xv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        gv[u] = g[(r + 4 * u) * cols4 + c];
+        gv[u] = load4(g, (r + 4 * u) * cols4 + c);
         xv[u] = load4(x, (r + 4 * u) * cols4 + c);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) one(gv[u], xv[u], (r + 4 * u) * cols4 + c);
     }
-    for (; r < r1; r += 4) one(g[r * cols4 + c], load4(x, r * cols4 + c), r * cols4 + c);
+    for (; r < r1; r += 4) one(load4(g, r * cols4 + c), load4(x, r * cols4 + c), r * cols4 + c);
   }
   if (ty > 0) sh[ty - 1][tx] = acc;
   __syncthreads();
@@ -449,23 +451,36 @@ bool gelu_bwd_cols_fits(const float* g, const void* x, const float* d, const uin
 }
 
 hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t rows,
-                         int64_t cols, float* dcol, void* ws, hipStream_t s, bool* dcol_written, const uint16_t* xbf) {
+                         int64_t cols, float* dcol, void* ws, hipStream_t s, bool* dcol_written, const uint16_t* xbf,
+                         const uint16_t* gbf) {
   *dcol_written = false;
   float* partial = static_cast<float*>(ws);
   if (!d && (!dbf || beta != 0.f)) return hipErrorInvalidValue;
-  if (!gelu_bwd_cols_fits(g, xbf ? (const void*)xbf : (const void*)x, d, dbf, rows, cols, ws) ||
+  const float* gchk = gbf ? reinterpret_cast<const float*>(gbf) : g;
+  if (!gelu_bwd_cols_fits(gchk, xbf ? (const void*)xbf : (const void*)x, d, dbf, rows, cols, ws) ||
       (!xbf && !aligned16(x))) {
-    if (xbf || !d) return hipErrorInvalidValue;  // the caller takes the fp32 form (converting x)
+    if (xbf || gbf || !d) return hipErrorInvalidValue;  // the caller takes the fp32 forms (converting)
     return gelu_bwd(g, x, d, dbf, beta, rows * cols, s);
   }
   const int64_t parts = colsum4_parts(rows), rows_per = (rows + parts - 1) / parts, cols4 = cols / 4;
   const dim3 grid((unsigned)((cols4 + 63) / 64), (unsigned)parts);
-  if (xbf)
-    hipLaunchKernelGGL(gelu_bwd_cols4_k<u16x4>, grid, dim3(NT), 0, s, (const f4*)g, (const u16x4*)xbf, (f4*)d,
-                       (u16x4*)dbf, beta, rows, cols4, rows_per, (f4*)partial);
-  else
-    hipLaunchKernelGGL(gelu_bwd_cols4_k<f4>, grid, dim3(NT), 0, s, (const f4*)g, (const f4*)x, (f4*)d, (u16x4*)dbf,
-                       beta, rows, cols4, rows_per, (f4*)partial);
+  auto launch = [&](auto gp, auto xp) {
+    using GT = std::remove_const_t<std::remove_pointer_t<decltype(gp)>>;
+    using XT = std::remove_const_t<std::remove_pointer_t<decltype(xp)>>;
+    hipLaunchKernelGGL((gelu_bwd_cols4_k<XT, GT>), grid, dim3(NT), 0, s, gp, xp, (f4*)d, (u16x4*)dbf, beta, rows,
+                       cols4, rows_per, (f4*)partial);
+  };
+  if (gbf) {
+    if (xbf)
+      launch((const u16x4*)gbf, (const u16x4*)xbf);
+    else
+      launch((const u16x4*)gbf, (const f4*)x);
+  } else {
+    if (xbf)
+      launch((const f4*)g, (const u16x4*)xbf);
+    else
+      launch((const f4*)g, (const f4*)x);
+  }
   hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, (int)parts, cols,
                      dcol, 0.f);
   *dcol_written = true;

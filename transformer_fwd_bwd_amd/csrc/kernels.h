@@ -91,12 +91,12 @@ hipError_t gelu_fwd(const float* a, float* y, uint16_t* ybf, int64_t n, hipStrea
 hipError_t gelu_bwd(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t n, hipStream_t s);
 // the same over [rows, cols], also writing dcol[c] = sum over rows of the result
 // where the row-slab path runs (*dcol_written); ws: colsum_workspace_bytes(rows, cols)
-// xbf (optional): x given as its bf16 copy instead; d may be null with dbf given and
-// beta == 0 (the bf16 copy alone).  Both need the row-slab path: hipErrorInvalidValue
-// where it does not fit (gelu_bwd_cols_fits)
+// xbf (optional): x given as its bf16 copy instead; gbf (optional): g given as bf16
+// instead; d may be null with dbf given and beta == 0 (the bf16 copy alone).  These
+// need the row-slab path: hipErrorInvalidValue where it does not fit (gelu_bwd_cols_fits)
 hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t rows,
                          int64_t cols, float* dcol, void* ws, hipStream_t s, bool* dcol_written,
-                         const uint16_t* xbf = nullptr);
+                         const uint16_t* xbf = nullptr, const uint16_t* gbf = nullptr);
 bool gelu_bwd_cols_fits(const float* g, const void* x, const float* d, const uint16_t* dbf, int64_t rows,
                         int64_t cols, const void* ws);
 // gelu_fwd reading the input's bf16 copy

@@ -481,6 +481,16 @@ struct Ctx {
     c->tensors[r.out].producer = (int)c->tape.size() - 1;
   }
 
+  // t is a bf16-only GELU output whose backward can read t's gradient as bf16 alone
+  // (the row-slab kernel, whose shape and alignment conditions are checked here)
+  bool gelu_takes_bf16_grad(const TensorRec& t) const {
+    if (!bf16_mode() || !t.bf16_out || t.producer < 0 || t.producer >= (int)c->tape.size()) return false;
+    const Rec& p = c->tape[t.producer];
+    if (&c->tensors[p.out] != &t || p.op != OP_GELU) return false;
+    const TensorRec& a = c->tensors[p.in[0]];
+    return !a.padded() && !t.padded() && !a.leaf && a.rows() >= 128 && a.cols() % 4 == 0;
+  }
+
   // the backward of t's producer reads t's gradient as the bf16 copy
   bool grad_read_as_bf16(const TensorRec& t) const {
     if (!bf16_mode() || t.producer < 0 || t.producer >= (int)c->tape.size()) return false;
@@ -690,6 +700,8 @@ void backward_rec(Ctx& C, const Rec& r) {
     case OP_GELU: {
       TensorRec& a = C.T(r.in[0]);
       float* dcol = a.padded() ? nullptr : C.gcol_buf(a);
+      // the upstream gradient held only as bf16 (see gelu_takes_bf16_grad): read as such
+      const uint16_t* gb = out.gstate == G_BF16 ? out.gbf : nullptr;
       // A bf16-only input whose one gradient is read by its producer as bf16 (with the
       // bias gradient from the column sums below): that copy alone, no fp32 gradient
       if (dcol && a.bf16_out && a.uses == 1 && !a.gpend && a.gstate != G_VALID && C.grad_read_as_bf16(a)) {
@@ -697,11 +709,11 @@ void backward_rec(Ctx& C, const Rec& r) {
         size_t mark = C.c->arena.hi;
         void* ws = C.scratch(colsum_workspace_bytes(a.rows(), a.cols()));
         const void* xin = a.f32_valid ? (const void*)a.data : (const void*)a.bf;
-        if (db && gelu_bwd_cols_fits(g, xin, nullptr, db, a.rows(), a.cols(), ws) &&
+        if (db && gelu_bwd_cols_fits(gb ? reinterpret_cast<const float*>(gb) : g, xin, nullptr, db, a.rows(), a.cols(), ws) &&
             (!a.f32_valid || (reinterpret_cast<uintptr_t>(a.data) & 15) == 0)) {
           bool written = false;
           hip_check(gelu_bwd_cols(g, a.f32_valid ? a.data : nullptr, nullptr, db, 0.f, a.rows(), a.cols(), dcol, ws, s,
-                                  &written, a.f32_valid ? nullptr : a.bf),
+                                  &written, a.f32_valid ? nullptr : a.bf, gb),
                     "gelu bwd");
           C.c->arena.hi = mark;
           a.gstate = G_BF16;
@@ -710,6 +722,11 @@ void backward_rec(Ctx& C, const Rec& r) {
           break;
         }
         C.c->arena.hi = mark;
+      }
+      if (gb) {  // the general paths read fp32: convert the upstream gradient
+        hip_check(to_f32(gb, out.grad, out.storage(), s), "gelu upstream gradient");
+        out.gstate = G_VALID;
+        gb = nullptr;
       }
       auto da = C.gdst(r.in[0]);
       uint16_t* db = C.twin_grad(a);
@@ -747,9 +764,14 @@ void backward_rec(Ctx& C, const Rec& r) {
       const Opnd go = op_grad(C, out);
       auto dx = C.gdst(r.in[0]);
       // a first and only contribution read as bf16 by x's producer: the product writes that copy too
-      uint16_t* dxb = dx.second == 0.f && x.uses == 1 && !x.leaf && C.grad_read_as_bf16(x) ? C.twin_grad(x) : nullptr;
-      gemm_nt(C, go, op_data(C, w), dx.first, rows, N, K, dx.second, -1, dxb);   // dx = g @ w^T
+      const bool first_only = dx.second == 0.f && x.uses == 1 && !x.leaf;
+      uint16_t* dxb = first_only && C.grad_read_as_bf16(x) ? C.twin_grad(x) : nullptr;
+      // ... or that copy alone, for a bf16-only GELU output (the GELU backward reads bf16)
+      const bool only = first_only && !dxb && C.gelu_takes_bf16_grad(x);
+      if (only) dxb = C.twin_grad(x);
+      gemm_nt(C, go, op_data(C, w), dx.first, rows, N, K, dx.second, -1, dxb, only);   // dx = g @ w^T
       if (dxb) x.gbf_valid = true;
+      if (only) x.gstate = G_BF16;
       auto dw = C.gdst(r.in[1]);
       gemm_tn(C, op_data(C, x), go, dw.first, K, rows, N, dw.second);   // dw = x^T @ g
       if (r.op != OP_MATMUL) {
