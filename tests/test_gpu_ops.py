@@ -559,8 +559,10 @@ def _bf16_round(a):
 def test_bf16_only_outputs(ctx, prec):
     """Outputs kept as bf16 copies alone (LayerNorm, GELU, Linear): read back as the exact
     bf16 rounding of the plain op's output (unchanged in fp32); a contraction or attention
-    reading them and every gradient are bit-identical to the plain ops; an fp32 reader
-    (Tanh) sees the converted values."""
+    reading them and every gradient are bit-identical to the plain ops, except qkv's bias
+    gradient in the bf16 variant: its gradient is then kept as bf16 alone, so that bias
+    gradient is the column sum of those bf16 values; an fp32 reader (Tanh) sees the
+    converted values."""
     ctx.set_precision(prec)
     B, Tn, C, H = 2, 80, 64, 2
     xv, g1, b1 = rnd(131, (B, Tn, C)), rnd(132, (C,), 0.5) + 1.0, rnd(133, (C,), 0.1)
@@ -580,6 +582,8 @@ def test_bf16_only_outputs(ctx, prec):
         ctx.backward(loss)
         res.append(dict(h=h.numpy(), qkv=qkv.numpy(), f=f.numpy(), att=att.numpy(), th=th.numpy(),
                         **{"d" + k: t[k].grad() for k in ("x", "g1", "b1", "W1", "c1", "W2", "c2")}))
+        if not only:
+            res[-1]["dqkv"] = qkv.grad()
         ctx.tape_reset()
         for v in t.values():
             v.release()
@@ -592,8 +596,12 @@ def test_bf16_only_outputs(ctx, prec):
     assert_close(only["th"], np.tanh(only["f"].astype(np.float64)), 1e-6, "tanh of the bf16-only output")
     if prec == "fp32":
         np.testing.assert_array_equal(only["th"], plain["th"])
-    for k in ("dW1", "dc1"):                                   # through the contraction / attention path only
-        np.testing.assert_array_equal(only[k], plain[k], err_msg=k)
+    np.testing.assert_array_equal(only["dW1"], plain["dW1"], err_msg="dW1")  # the contraction reads bf16 in both
+    if prec == "fp32":
+        np.testing.assert_array_equal(only["dc1"], plain["dc1"], err_msg="dc1")
+    else:
+        want = _bf16_round(plain["dqkv"]).astype(np.float64).reshape(-1, 3 * C).sum(axis=0)
+        assert_close(only["dc1"], want, 1e-5, "dc1: column sums of the bf16 gradient")
     for k in ("dx", "dg1", "db1", "dW2", "dc2"):               # the Tanh branch sees rounded inputs
         assert_close(only[k], plain[k], 1e-6 if prec == "fp32" else 2e-2, k)
     ctx.set_precision("fp32")
@@ -660,6 +668,34 @@ def test_mlp_gelu_gradient_kept_as_bf16(ctx):
     E.sum_all(E.mul(E.add(E.matmul(E.gelu(E.add(E.matmul(ox, ow1), ob1)), ow2), ob2),
                     E.Tensor(R.astype(np.float64)))).backward()
     for g_, o_, name in zip(grads, os_, ("dx", "dw1", "db1", "dw2", "db2")):
+        assert_close(g_, o_.grad, GRAD_TOL["bf16"], name)
+
+
+def test_attention_qkv_gradient_kept_as_bf16(ctx):
+    """qkv from a Linear with the bf16-only output flag, then the fused attention: its
+    backward writes the qkv gradient as bf16 alone, the Linear reads it (and sums its
+    columns for the bias gradient) as such, and reading qkv's gradient is an error.
+    Gradients of x, w and b against the oracle (ragged T = 130, 2 heads of 32)."""
+    ctx.set_precision("bf16")
+    B, Tn, C, H = 2, 130, 64, 2
+    xv, W, bv = rnd(161, (B, Tn, C)), rnd(162, (C, 3 * C), 0.2), rnd(163, (3 * C,), 0.1)
+    R = rnd(164, (B, Tn, C))
+    ts = [ctx.tensor(a.shape, a) for a in (xv, W, bv)]
+    qkv = T.linear(ts[0], ts[1], ts[2], bf16_only=True)
+    y = T.causal_attention(qkv, H)
+    Rt = ctx.tensor(R.shape, R)
+    ctx.backward(T.sum_all(T.mul(y, Rt)))
+    grads = [t.grad() for t in ts]
+    with pytest.raises(T.TfbError):
+        qkv.grad()
+    ctx.tape_reset()
+    for t in ts + [Rt]:
+        t.release()
+    ctx.set_precision("fp32")
+    os_ = [E.Tensor(a.astype(np.float64)) for a in (xv, W, bv)]
+    oq = E.add(E.matmul(os_[0], os_[1]), os_[2])
+    E.sum_all(E.mul(_attention_oracle(oq, H), E.Tensor(R.astype(np.float64)))).backward()
+    for g_, o_, name in zip(grads, os_, ("dx", "dw", "db")):
         assert_close(g_, o_.grad, GRAD_TOL["bf16"], name)
 
 

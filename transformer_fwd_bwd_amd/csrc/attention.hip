@@ -435,10 +435,12 @@ __global__ __launch_bounds__(NT, 2) void attn_dq_k(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
         const int d = 32 * i + acc_row(r, h);
-        f4* p = reinterpret_cast<f4*>(a.out + off + d);
         f4 v = f4{dq[i][r], dq[i][r + 1], dq[i][r + 2], dq[i][r + 3]} * a.scale;
-        if (a.beta != 0.f) v += *p;
-        *p = v;
+        if (a.out) {  // null: the bf16 copy alone
+          f4* p = reinterpret_cast<f4*>(a.out + off + d);
+          if (a.beta != 0.f) v += *p;
+          *p = v;
+        }
         if (a.outbf) *reinterpret_cast<u16x4*>(a.outbf + off + d) = pack4(v);
       }
   }
@@ -579,16 +581,18 @@ __global__ __launch_bounds__(NT, 2) void attn_dkv_k(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
         const int d = 32 * i + acc_row(r, h);
-        f4* pk = reinterpret_cast<f4*>(a.out + off + a.C + d);
-        f4* pv = reinterpret_cast<f4*>(a.out + off + 2 * a.C + d);
         f4 vk = f4{dk[i][r], dk[i][r + 1], dk[i][r + 2], dk[i][r + 3]} * a.scale;
         f4 vv = f4{dv[i][r], dv[i][r + 1], dv[i][r + 2], dv[i][r + 3]};
-        if (a.beta != 0.f) {
-          vk += *pk;
-          vv += *pv;
+        if (a.out) {  // null: the bf16 copy alone
+          f4* pk = reinterpret_cast<f4*>(a.out + off + a.C + d);
+          f4* pv = reinterpret_cast<f4*>(a.out + off + 2 * a.C + d);
+          if (a.beta != 0.f) {
+            vk += *pk;
+            vv += *pv;
+          }
+          *pk = vk;
+          *pv = vv;
         }
-        *pk = vk;
-        *pv = vv;
         if (a.outbf) {
           *reinterpret_cast<u16x4*>(a.outbf + off + a.C + d) = pack4(vk);
           *reinterpret_cast<u16x4*>(a.outbf + off + 2 * a.C + d) = pack4(vv);
@@ -631,6 +635,7 @@ hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float*
                                int H, int C, float scale, hipStream_t s) {
   if (B <= 0 || T <= 0) return hipSuccess;
   if (!offsets_fit(T, C)) return hipErrorInvalidValue;
+  if (!dqkv && (!dqkv_bf || beta != 0.f)) return hipErrorInvalidValue;
   AttnArgs a{};
   a.qkv = qkv, a.y = y, a.dyf = dyf, a.dy = dy, a.lse = const_cast<float*>(lse), a.D = D, a.out = dqkv;
   a.outbf = dqkv_bf;

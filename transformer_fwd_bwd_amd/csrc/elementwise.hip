@@ -117,7 +117,15 @@ __global__ void colsum_stage1(const float* __restrict__ g, int64_t rows, int64_t
 // The same over float4 columns: a workgroup covers 256 columns (64 lanes x 4)
 // and 4 row groups that interleave over the slab's rows, 8 rows in flight per
 // thread; the 4 group sums are added in LDS, in a fixed order.
-__global__ __launch_bounds__(NT) void colsum4_stage1(const f4* __restrict__ g, int64_t rows, int64_t cols4,
+__device__ __forceinline__ f4 load4(const f4* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ f4 load4(const u16x4* p, int64_t i) {  // exact float values of 4 bf16 numbers
+  const u16x4 b = p[i];
+  return f4{__uint_as_float((unsigned)b[0] << 16), __uint_as_float((unsigned)b[1] << 16),
+            __uint_as_float((unsigned)b[2] << 16), __uint_as_float((unsigned)b[3] << 16)};
+}
+
+template <typename GT>  // f4, or u16x4 for a gradient held as bf16
+__global__ __launch_bounds__(NT) void colsum4_stage1(const GT* __restrict__ g, int64_t rows, int64_t cols4,
                                                     int64_t rows_per, f4* __restrict__ partial) {
   __shared__ f4 sh[3][64];
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -130,11 +138,11 @@ __global__ __launch_bounds__(NT) void colsum4_stage1(const f4* __restrict__ g, i
     for (; r + 28 < r1; r += 32) {
       f4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = g[(r + 4 * u) * cols4 + c];
+      for (int u = 0; u < 8; ++u) v[u] = load4(g, (r + 4 * u) * cols4 + c);
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc[u & 1] += v[u];
     }
-    for (; r < r1; r += 4) acc[0] += g[r * cols4 + c];
+    for (; r < r1; r += 4) acc[0] += load4(g, r * cols4 + c);
   }
   const f4 t = acc[0] + acc[1];
   if (ty > 0) sh[ty - 1][tx] = t;
@@ -147,12 +155,6 @@ __global__ __launch_bounds__(NT) void colsum4_stage1(const f4* __restrict__ g, i
 // gradient): workgroups as in colsum4_stage1 (256 columns x a slab of rows, 4
 // interleaved row groups, 4 rows in flight per thread), each element written once
 // and added into its column's slab partial.
-__device__ __forceinline__ f4 load4(const f4* p, int64_t i) { return p[i]; }
-__device__ __forceinline__ f4 load4(const u16x4* p, int64_t i) {  // exact float values of 4 bf16 numbers
-  const u16x4 b = p[i];
-  return f4{__uint_as_float((unsigned)b[0] << 16), __uint_as_float((unsigned)b[1] << 16),
-            __uint_as_float((unsigned)b[2] << 16), __uint_as_float((unsigned)b[3] << 16)};
-}
 
 // XT: f4 (fp32 input) or u16x4 (the input's bf16 copy); GT likewise for the upstream gradient
 template <typename XT, typename GT>
@@ -487,17 +489,28 @@ hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf
   return hipGetLastError();
 }
 
-hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s) {
+hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s,
+                  const uint16_t* gbf) {
   if (cols <= 0) return hipSuccess;
-  if (rows == 1) return axpby(out, g, 1.f, beta, cols, s);
   float* partial = static_cast<float*>(ws);
+  if (gbf) {  // the gradient as bf16: the float4-group path only
+    if (cols % 4 != 0 || (reinterpret_cast<uintptr_t>(gbf) & 7) != 0 || !aligned16(partial) || rows <= 0)
+      return hipErrorInvalidValue;
+    const int64_t parts = colsum4_parts(rows), rows_per = (rows + parts - 1) / parts, cols4 = cols / 4;
+    hipLaunchKernelGGL(colsum4_stage1<u16x4>, dim3((unsigned)((cols4 + 63) / 64), (unsigned)parts), dim3(NT), 0, s,
+                       (const u16x4*)gbf, rows, cols4, rows_per, (f4*)partial);
+    hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, (int)parts, cols,
+                       out, beta);
+    return hipGetLastError();
+  }
+  if (rows == 1) return axpby(out, g, 1.f, beta, cols, s);
   const bool vec = cols % 4 == 0 && aligned16(g) && aligned16(partial);
   const int64_t parts = vec ? colsum4_parts(rows) : colsum_parts(rows, cols);
   const int64_t rows_per = (rows + parts - 1) / parts;
   if (vec) {
     const int64_t cols4 = cols / 4;
     dim3 g1((unsigned)((cols4 + 63) / 64), (unsigned)parts);
-    hipLaunchKernelGGL(colsum4_stage1, g1, dim3(NT), 0, s, (const f4*)g, rows, cols4, rows_per, (f4*)partial);
+    hipLaunchKernelGGL(colsum4_stage1<f4>, g1, dim3(NT), 0, s, (const f4*)g, rows, cols4, rows_per, (f4*)partial);
   } else {
     dim3 g1((unsigned)((cols + NT - 1) / NT), (unsigned)parts);
     hipLaunchKernelGGL(colsum_stage1, g1, dim3(NT), 0, s, g, rows, cols, rows_per, partial);

@@ -101,9 +101,12 @@ bool gelu_bwd_cols_fits(const float* g, const void* x, const float* d, const uin
                         int64_t cols, const void* ws);
 // gelu_fwd reading the input's bf16 copy
 hipError_t gelu_fwd_bf(const uint16_t* a, float* y, uint16_t* ybf, int64_t n, hipStream_t s);
-// out[c] = beta*out[c] + sum_r g[r*cols + c]; deterministic two-stage reduction
+// out[c] = beta*out[c] + sum_r g[r*cols + c]; deterministic two-stage reduction.
+// gbf (optional, g then unused): the gradient held as bf16 (cols % 4 == 0, else
+// hipErrorInvalidValue)
 size_t colsum_workspace_bytes(int64_t rows, int64_t cols);
-hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s);
+hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s,
+                  const uint16_t* gbf = nullptr);
 // out[0] = sum of a (deterministic); sum_bwd: d = beta*d + g[0]
 size_t sum_workspace_bytes(int64_t n);
 hipError_t sum_all(const float* a, int64_t n, float* out, void* ws, hipStream_t s);

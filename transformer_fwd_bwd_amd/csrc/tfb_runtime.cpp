@@ -781,7 +781,8 @@ void backward_rec(Ctx& C, const Rec& r) {
         } else {
           size_t mark = C.c->arena.hi;
           void* ws = C.scratch(colsum_workspace_bytes(rows, N));
-          hip_check(colsum(g, rows, N, db.first, db.second, ws, s), "linear bias bwd");
+          hip_check(colsum(g, rows, N, db.first, db.second, ws, s, out.gstate == G_BF16 ? out.gbf : nullptr),
+                    "linear bias bwd");
           C.c->arena.hi = mark;
         }
       }
@@ -909,13 +910,19 @@ void backward_rec(Ctx& C, const Rec& r) {
         const uint16_t* dyb = C.grad_bf16(out);
         auto dq = C.gdst(r.in[0]);
         uint16_t* dqb = C.twin_grad(qkv);
+        // a bf16-only qkv whose one gradient its Linear reads as bf16 (with the bias
+        // gradient summed from that copy): the copy alone
+        const bool only = dqb && dq.second == 0.f && qkv.uses == 1 && !qkv.leaf && qkv.bf16_out &&
+                          qkv.cols() % 4 == 0 && C.grad_read_as_bf16(qkv);
         size_t mark = C.c->arena.hi;
         float* D = static_cast<float*>(C.scratch((size_t)B * H * T * sizeof(float)));
-        hip_check(flash_attention_bwd(qb, out.data, g, dyb, static_cast<const float*>(r.s1), D, dq.first, dqb,
-                                      dq.second, (int)B, (int)T, (int)H, (int)Cc, scale, s),
+        hip_check(flash_attention_bwd(qb, out.data, g, dyb, static_cast<const float*>(r.s1), D,
+                                      only ? nullptr : dq.first, dqb, dq.second, (int)B, (int)T, (int)H, (int)Cc,
+                                      scale, s),
                   "attention bwd");
         C.c->arena.hi = mark;
         qkv.gbf_valid = true;
+        if (only) qkv.gstate = G_BF16;
         break;
       }
       float* P = static_cast<float*>(r.s0);
