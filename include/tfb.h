@@ -136,15 +136,15 @@ int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tenso
  * value and is ignored in the fp32 variant.  Unknown flags: TFB_ERR_ARG.
  * [GPT2-4, "Loading the weights": Linear weights stored [in, out]] */
 #define TFB_OUT_BF16_COPY 1
-/* Output flag of tfb_linear_ex, tfb_matmul_t_ex, tfb_layernorm_ex and tfb_gelu_ex (bf16 variant):
+/* Output flag of tfb_linear_ex, tfb_matmul_t_ex, tfb_layernorm_ex, tfb_gelu_ex and tfb_causal_attention_ex (bf16 variant):
  * only the bf16 copy of y is written, for an output whose readers take bf16
  * (the contractions, the fused attention).  A reader that needs fp32 data (any
  * other op, tfb_tensor_read, tfb_tensor_info) gets the exact float values of
  * those bf16 numbers, converted on first use.  In the backward, where y's
  * gradient has one contribution and its only reader takes bf16 (the contraction
- * that produced y, with column sums for the bias gradient, or the GELU that
- * produced y), that gradient too may be written only as bf16; reading it then
- * gives TFB_ERR_STATE.  Ignored in the fp32 variant. */
+ * that produced y, with column sums for the bias gradient, or the GELU or fused
+ * attention that produced y), that gradient too may be written only as bf16;
+ * reading it then gives TFB_ERR_STATE.  Ignored in the fp32 variant. */
 #define TFB_OUT_BF16_ONLY 2
 /* y = r + (x @ w + b): a Linear and the residual Add that follows it, with the
  * Add done in the product's epilogue (r is read there, once).  r has the
@@ -188,6 +188,10 @@ int tfb_causal_softmax(tfb_ctx* ctx, tfb_tensor s, tfb_tensor* y);
  * addressing and the masked upper triangle is never computed.
  * [Autograd-1, table of ops; GPT2-4, "Generation with KV cache"] */
 int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y);
+/* tfb_causal_attention with flags (TFB_OUT_BF16_ONLY, bf16 variant with the fused
+ * kernels: y kept as bf16 alone; its backward then takes rowsum(dy * y) from the
+ * bf16 copies.  Unknown flags: TFB_ERR_ARG). */
+int tfb_causal_attention_ex(tfb_ctx* ctx, tfb_tensor qkv, int heads, int flags, tfb_tensor* y);
 /* loss[0] = mean over rows of -log(max(softmax(logits_row)[target], 1e-30));
  * backward (g/n)(p - onehot).  dev_targets: n = rows(logits) int32 device
  * values in [0, cols), copied by the call.  [Autograd-1, "Ops":

@@ -671,18 +671,23 @@ def test_mlp_gelu_gradient_kept_as_bf16(ctx):
         assert_close(g_, o_.grad, GRAD_TOL["bf16"], name)
 
 
-def test_attention_qkv_gradient_kept_as_bf16(ctx):
+@pytest.mark.parametrize("out_only", [False, True])
+def test_attention_qkv_gradient_kept_as_bf16(ctx, out_only):
     """qkv from a Linear with the bf16-only output flag, then the fused attention: its
     backward writes the qkv gradient as bf16 alone, the Linear reads it (and sums its
     columns for the bias gradient) as such, and reading qkv's gradient is an error.
-    Gradients of x, w and b against the oracle (ragged T = 130, 2 heads of 32)."""
+    out_only: the attention output is bf16-only too and feeds a projection, whose dX
+    is then written as bf16 alone (the backward takes rowsum(dy * y) from the bf16
+    copies).  Gradients of every input against the oracle (ragged T = 130, 2 heads of 32)."""
     ctx.set_precision("bf16")
     B, Tn, C, H = 2, 130, 64, 2
     xv, W, bv = rnd(161, (B, Tn, C)), rnd(162, (C, 3 * C), 0.2), rnd(163, (3 * C,), 0.1)
+    Wp, bp = rnd(165, (C, C), 0.2), rnd(166, (C,), 0.1)
     R = rnd(164, (B, Tn, C))
-    ts = [ctx.tensor(a.shape, a) for a in (xv, W, bv)]
+    ts = [ctx.tensor(a.shape, a) for a in (xv, W, bv, Wp, bp)]
     qkv = T.linear(ts[0], ts[1], ts[2], bf16_only=True)
-    y = T.causal_attention(qkv, H)
+    y = T.causal_attention(qkv, H, bf16_only=out_only)
+    y = T.linear(y, ts[3], ts[4])
     Rt = ctx.tensor(R.shape, R)
     ctx.backward(T.sum_all(T.mul(y, Rt)))
     grads = [t.grad() for t in ts]
@@ -692,10 +697,11 @@ def test_attention_qkv_gradient_kept_as_bf16(ctx):
     for t in ts + [Rt]:
         t.release()
     ctx.set_precision("fp32")
-    os_ = [E.Tensor(a.astype(np.float64)) for a in (xv, W, bv)]
+    os_ = [E.Tensor(a.astype(np.float64)) for a in (xv, W, bv, Wp, bp)]
     oq = E.add(E.matmul(os_[0], os_[1]), os_[2])
-    E.sum_all(E.mul(_attention_oracle(oq, H), E.Tensor(R.astype(np.float64)))).backward()
-    for g_, o_, name in zip(grads, os_, ("dx", "dw", "db")):
+    oy = E.add(E.matmul(_attention_oracle(oq, H), os_[3]), os_[4])
+    E.sum_all(E.mul(oy, E.Tensor(R.astype(np.float64)))).backward()
+    for g_, o_, name in zip(grads, os_, ("dx", "dw", "db", "dwp", "dbp")):
         assert_close(g_, o_.grad, GRAD_TOL["bf16"], name)
 
 

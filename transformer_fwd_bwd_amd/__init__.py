@@ -64,6 +64,7 @@ SIGNATURES = {
     "tfb_batch_matmul_t": [c_void_p, c_int32, c_int32, P(c_int32)],
     "tfb_causal_softmax": [c_void_p, c_int32, P(c_int32)],
     "tfb_causal_attention": [c_void_p, c_int32, c_int, P(c_int32)],
+    "tfb_causal_attention_ex": [c_void_p, c_int32, c_int, c_int32, P(c_int32)],
     "tfb_softmax_cross_entropy": [c_void_p, c_int32, c_void_p, c_int64, P(c_int32)],
     "tfb_softmax_cross_entropy_ex": [c_void_p, c_int32, c_void_p, c_int64, c_int32, P(c_int32)],
     "tfb_backward": [c_void_p, c_int32],
@@ -364,7 +365,10 @@ def causal_softmax(s: Tensor) -> Tensor:
     return _out(s.ctx, _lib.tfb_causal_softmax, s.h)
 
 
-def causal_attention(qkv: Tensor, heads: int) -> Tensor:
+def causal_attention(qkv: Tensor, heads: int, bf16_only: bool = False) -> Tensor:
+    """bf16_only: in the bf16 variant (fused kernels) the output is stored as bf16 alone."""
+    if bf16_only:
+        return _out(qkv.ctx, _lib.tfb_causal_attention_ex, qkv.h, int(heads), OUT_BF16_ONLY)
     return _out(qkv.ctx, _lib.tfb_causal_attention, qkv.h, int(heads))
 
 

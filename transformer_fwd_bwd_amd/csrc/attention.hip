@@ -58,6 +58,10 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& acc, int base) {
 }
 
 __device__ __forceinline__ u16x4 pack4(f4 v) { return u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])}; }
+__device__ __forceinline__ f4 bf4(u16x4 v) {  // exact float values of 4 bf16 numbers
+  return f4{__uint_as_float((unsigned)v[0] << 16), __uint_as_float((unsigned)v[1] << 16),
+            __uint_as_float((unsigned)v[2] << 16), __uint_as_float((unsigned)v[3] << 16)};
+}
 
 // row index (within a 32x32 block) held by accumulator r of lane half h
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -152,6 +156,7 @@ struct AttnArgs {
   const unsigned short* dy;   // bf16 [B, T, C] (backward)
   const float* y;             // fp32 [B, T, C] forward output (backward: D = rowsum(dy * y))
   const float* dyf;           // fp32 [B, T, C] (backward)
+  const unsigned short* ybf;  // bf16 copy of y (backward: D from dy and ybf when y or dyf is null)
   float* out;                 // forward: y; backward: dqkv fp32 [B, T, 3C]
   unsigned short* outbf;      // optional bf16 copy of `out` (same layout)
   float* lse;                 // [B*H, T] base-2 log-sum-exp of the scaled scores
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
       for (int r = 0; r < 16; r += 4) {  // registers r .. r+3 hold 4 consecutive columns of this query's row
         const f4 v = f4{o[i][r], o[i][r + 1], o[i][r + 2], o[i][r + 3]} * inv;
         const int d = 32 * i + acc_row(r, h);
-        *reinterpret_cast<f4*>(a.out + off + d) = v;
+        if (a.out) *reinterpret_cast<f4*>(a.out + off + d) = v;  // null: the bf16 copy alone
         if (a.outbf) *reinterpret_cast<u16x4*>(a.outbf + off + d) = pack4(v);
       }
     if (h == 0) a.lse[(int64_t)bh * a.T + q] = m + log2f(l);
@@ -348,16 +353,24 @@ __global__ __launch_bounds__(NT, 2) void attn_dq_k(AttnArgs a) {
     df[s] = frag_g(dyg, a.C, q, a.T, s, h);
   }
   const float lse = q < a.T ? a.lse[(int64_t)bh * a.T + q] : 0.f;
-  // D = rowsum(dO * O) of this query (fp32 inputs): each lane half sums half the head's
-  // columns, one exchange adds the halves; it is stored for the dK/dV kernel that follows
+  // D = rowsum(dO * O) of this query: each lane half sums half the head's columns,
+  // one exchange adds the halves; it is stored for the dK/dV kernel that follows.
+  // From the fp32 values where both exist, else from the bf16 copies of both.
   float Dq = 0.f;
   if (q < a.T) {
     const int64_t off = ((int64_t)b * a.T + q) * a.C + hd * HS + h * (HS / 2);
-    const f4* g4 = reinterpret_cast<const f4*>(a.dyf + off);
-    const f4* y4 = reinterpret_cast<const f4*>(a.y + off);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (a.y && a.dyf) {
+      const f4* g4 = reinterpret_cast<const f4*>(a.dyf + off);
+      const f4* y4 = reinterpret_cast<const f4*>(a.y + off);
 #pragma unroll
-    for (int j = 0; j < HS / 8; ++j) acc += g4[j] * y4[j];
+      for (int j = 0; j < HS / 8; ++j) acc += g4[j] * y4[j];
+    } else {
+      const u16x4* g4 = reinterpret_cast<const u16x4*>(a.dy + off);
+      const u16x4* y4 = reinterpret_cast<const u16x4*>(a.ybf + off);
+#pragma unroll
+      for (int j = 0; j < HS / 8; ++j) acc += bf4(g4[j]) * bf4(y4[j]);
+    }
     Dq = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
   Dq += __shfl_xor(Dq, 32, 64);
@@ -617,6 +630,7 @@ hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, uint16_t* ybf, flo
                                float scale, hipStream_t s) {
   if (B <= 0 || T <= 0) return hipSuccess;
   if (!offsets_fit(T, C)) return hipErrorInvalidValue;
+  if (!y && !ybf) return hipErrorInvalidValue;
   AttnArgs a{};
   a.qkv = qkv, a.out = y, a.outbf = ybf, a.lse = lse, a.B = B, a.T = T, a.H = H, a.C = C, a.scale = scale;
   const dim3 fgrid((unsigned)(((T + FQ - 1) / FQ) * ((B * H + 7) / 8 * 8)));
@@ -632,12 +646,13 @@ hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, uint16_t* ybf, flo
 
 hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float* dyf, const uint16_t* dy,
                                const float* lse, float* D, float* dqkv, uint16_t* dqkv_bf, float beta, int B, int T,
-                               int H, int C, float scale, hipStream_t s) {
+                               int H, int C, float scale, hipStream_t s, const uint16_t* ybf) {
   if (B <= 0 || T <= 0) return hipSuccess;
   if (!offsets_fit(T, C)) return hipErrorInvalidValue;
   if (!dqkv && (!dqkv_bf || beta != 0.f)) return hipErrorInvalidValue;
+  if ((!y || !dyf) && !ybf) return hipErrorInvalidValue;
   AttnArgs a{};
-  a.qkv = qkv, a.y = y, a.dyf = dyf, a.dy = dy, a.lse = const_cast<float*>(lse), a.D = D, a.out = dqkv;
+  a.qkv = qkv, a.y = y, a.dyf = dyf, a.dy = dy, a.ybf = ybf, a.lse = const_cast<float*>(lse), a.D = D, a.out = dqkv;
   a.outbf = dqkv_bf;
   a.B = B, a.T = T, a.H = H, a.C = C, a.scale = scale, a.beta = beta;
   const int hs = C / H;

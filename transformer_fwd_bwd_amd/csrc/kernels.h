@@ -157,14 +157,16 @@ hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* target
 
 // ---- fused causal attention, bf16 variant (attention.hip)
 // qkv: bf16 [B, T, 3C] (q | k | v thirds, head h = columns h*hs .. h*hs+hs-1 of each third)
-// y: fp32 [B, T, C]; lse: [B*H, T] base-2 log-sum-exp of the scaled scores (saved for backward)
+// y: fp32 [B, T, C] (null: only its bf16 copy ybf is written); lse: [B*H, T] base-2
+// log-sum-exp of the scaled scores (saved for backward)
 bool flash_attention_supported(int hs, int64_t C, int64_t T);
 hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, uint16_t* ybf, float* lse, int B, int T, int H, int C,
                                float scale, hipStream_t s);
-// dqkv = beta*dqkv + d(qkv); D: [B*H, T] scratch
+// dqkv = beta*dqkv + d(qkv) (dqkv null with beta 0: the bf16 copy alone); D: [B*H, T]
+// scratch, rowsum(dy * y) from y and dyf, or from ybf and dy where either is null
 hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float* dyf, const uint16_t* dy,
                                const float* lse, float* D, float* dqkv, uint16_t* dqkv_bf, float beta, int B, int T,
-                               int H, int C, float scale, hipStream_t s);
+                               int H, int C, float scale, hipStream_t s, const uint16_t* ybf = nullptr);
 
 // ---- KV-cached inference (decode.hip); cache fp32 [L][2][B][Tmax][C]
 hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, int B, int Tmax, int pos0,

@@ -403,10 +403,7 @@ struct Ctx {
         f32(T(r.in[1]));
         return;
       case OP_ATTENTION:
-        if (r.i1 == 1) {
-          f32(T(r.out));
-          return;
-        }
+        if (r.i1 == 1) return;  // the fused backward reads the output's fp32 form or its bf16 copy
         break;
       default:
         break;
@@ -489,6 +486,14 @@ struct Ctx {
     if (&c->tensors[p.out] != &t || p.op != OP_GELU) return false;
     const TensorRec& a = c->tensors[p.in[0]];
     return !a.padded() && !t.padded() && !a.leaf && a.rows() >= 128 && a.cols() % 4 == 0;
+  }
+
+  // t is a bf16-only output of the fused attention (whose backward reads its
+  // gradient as bf16 and can take D from the bf16 copies)
+  bool attention_out_bf16(const TensorRec& t) const {
+    if (!bf16_mode() || !t.bf16_out || t.producer < 0 || t.producer >= (int)c->tape.size()) return false;
+    const Rec& p = c->tape[t.producer];
+    return &c->tensors[p.out] == &t && p.op == OP_ATTENTION && p.i1 == 1;
   }
 
   // the backward of t's producer reads t's gradient as the bf16 copy
@@ -767,7 +772,8 @@ void backward_rec(Ctx& C, const Rec& r) {
       const bool first_only = dx.second == 0.f && x.uses == 1 && !x.leaf;
       uint16_t* dxb = first_only && C.grad_read_as_bf16(x) ? C.twin_grad(x) : nullptr;
       // ... or that copy alone, for a bf16-only GELU output (the GELU backward reads bf16)
-      const bool only = first_only && !dxb && C.gelu_takes_bf16_grad(x);
+      // or a bf16-only attention output (its backward then takes D from bf16 copies)
+      const bool only = first_only && ((!dxb && C.gelu_takes_bf16_grad(x)) || (dxb && C.attention_out_bf16(x)));
       if (only) dxb = C.twin_grad(x);
       gemm_nt(C, go, op_data(C, w), dx.first, rows, N, K, dx.second, -1, dxb, only);   // dx = g @ w^T
       if (dxb) x.gbf_valid = true;
@@ -908,6 +914,9 @@ void backward_rec(Ctx& C, const Rec& r) {
       if (r.i1 == 1) {  // fused kernels: recompute probabilities from the saved log-sum-exp
         const uint16_t* qb = C.data_bf16(qkv);
         const uint16_t* dyb = C.grad_bf16(out);
+        // D from the fp32 output and gradient where both exist, else from their bf16 copies
+        const float* yf = out.f32_valid ? out.data : nullptr;
+        const float* dyf = out.gstate == G_BF16 ? nullptr : g;
         auto dq = C.gdst(r.in[0]);
         uint16_t* dqb = C.twin_grad(qkv);
         // a bf16-only qkv whose one gradient its Linear reads as bf16 (with the bias
@@ -916,9 +925,9 @@ void backward_rec(Ctx& C, const Rec& r) {
                           qkv.cols() % 4 == 0 && C.grad_read_as_bf16(qkv);
         size_t mark = C.c->arena.hi;
         float* D = static_cast<float*>(C.scratch((size_t)B * H * T * sizeof(float)));
-        hip_check(flash_attention_bwd(qb, out.data, g, dyb, static_cast<const float*>(r.s1), D,
+        hip_check(flash_attention_bwd(qb, yf, dyf, dyb, static_cast<const float*>(r.s1), D,
                                       only ? nullptr : dq.first, dqb, dq.second, (int)B, (int)T, (int)H, (int)Cc,
-                                      scale, s),
+                                      scale, s, out.bf),
                   "attention bwd");
         C.c->arena.hi = mark;
         qkv.gbf_valid = true;
@@ -1587,8 +1596,13 @@ int tfb_causal_softmax(tfb_ctx* ctx, tfb_tensor sx, tfb_tensor* y) {
 }
 
 int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y) {
+  return tfb_causal_attention_ex(ctx, qkv, heads, 0, y);
+}
+
+int tfb_causal_attention_ex(tfb_ctx* ctx, tfb_tensor qkv, int heads, int flags, tfb_tensor* y) {
   return guarded([&] {
     Ctx C(ctx);
+    need((flags & ~TFB_OUT_BF16_ONLY) == 0, TFB_ERR_ARG, "unknown tfb_causal_attention_ex flags");
     qkv = C.dense_in(qkv, true);  // the fused kernels read the bf16 copy; the fp32 path converts below
     TensorRec& Q = C.T(qkv);
     need(y != nullptr, TFB_ERR_ARG, "null output");
@@ -1604,9 +1618,12 @@ int tfb_causal_attention(tfb_ctx* ctx, tfb_tensor qkv, int heads, tfb_tensor* y)
       const uint16_t* qb = C.data_bf16(ctx->tensors[qkv]);
       float* lse = static_cast<float*>(C.scratch((size_t)B * H * T * sizeof(float)));
       uint16_t* yb = C.twin_data(ctx->tensors[h]);
-      hip_check(flash_attention_fwd(qb, ctx->tensors[h].data, yb, lse, (int)B, (int)T, (int)H, (int)Cc, scale, C.s()),
+      const bool only = yb && (flags & TFB_OUT_BF16_ONLY);
+      hip_check(flash_attention_fwd(qb, only ? nullptr : ctx->tensors[h].data, yb, lse, (int)B, (int)T, (int)H, (int)Cc,
+                                    scale, C.s()),
                 "attention");
       ctx->tensors[h].bf_valid = true;
+      if (only) ctx->tensors[h].f32_valid = false, ctx->tensors[h].bf16_out = true;
       Rec r{OP_ATTENTION};
       r.in[0] = qkv, r.out = h, r.i0 = H, r.i1 = 1, r.f = scale;
       r.s1 = lse;

@@ -50,12 +50,12 @@ class Gpt:
         x = add(tok, pos)
         # Outputs whose only readers are contractions, the fused attention, the GELU or
         # the cross-entropy are kept as bf16 copies alone in the bf16 variant (the
-        # LayerNorms', qkv, the MLP's first product, the GELU's, the logits)
+        # LayerNorms', qkv, the attention's, the MLP's first product, the GELU's, the logits)
         for i in range(self.n_layer):
             p = f"h.{i}."
             h = layernorm(x, P[p + "ln_1.weight"], P[p + "ln_1.bias"], bf16_only=True)
             qkv = linear(h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"], bf16_only=True)
-            a = causal_attention(qkv, self.n_head)
+            a = causal_attention(qkv, self.n_head, bf16_only=True)
             x = linear(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"], residual=x)
             h = layernorm(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"], bf16_only=True)
             f = gelu(linear(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"], bf16_only=True), bf16_only=True)
