@@ -705,6 +705,35 @@ def test_attention_qkv_gradient_kept_as_bf16(ctx, out_only):
         assert_close(g_, o_.grad, GRAD_TOL["bf16"], name)
 
 
+@pytest.mark.parametrize("C", [64, 768])
+def test_layernorm_gradient_kept_as_bf16(ctx, C):
+    """LayerNorm with the bf16-only output flag feeding a Linear: the Linear's dX is
+    written as bf16 alone and the fused LayerNorm backward reads it that way (reading
+    the LayerNorm output's gradient is an error).  Every input's gradient against the
+    oracle (300 rows, C = 64 and the GPT's 768)."""
+    ctx.set_precision("bf16")
+    xv, gv, bv = rnd(171, (300, C), 2.0) + 0.5, 1 + rnd(172, (C,), 0.2), rnd(173, (C,), 0.2)
+    W, c = rnd(174, (C, 40), 0.2), rnd(175, (40,), 0.1)
+    R = rnd(176, (300, 40))
+    ts = [ctx.tensor(a.shape, a) for a in (xv, gv, bv, W, c)]
+    h = T.layernorm(ts[0], ts[1], ts[2], bf16_only=True)
+    y = T.linear(h, ts[3], ts[4])
+    Rt = ctx.tensor(R.shape, R)
+    ctx.backward(T.sum_all(T.mul(y, Rt)))
+    grads = [t.grad() for t in ts]
+    with pytest.raises(T.TfbError):
+        h.grad()
+    ctx.tape_reset()
+    for t in ts + [Rt]:
+        t.release()
+    ctx.set_precision("fp32")
+    os_ = [E.Tensor(a.astype(np.float64)) for a in (xv, gv, bv, W, c)]
+    oy = E.add(E.matmul(E.layernorm(os_[0], os_[1], os_[2], 1e-5), os_[3]), os_[4])
+    E.sum_all(E.mul(oy, E.Tensor(R.astype(np.float64)))).backward()
+    for g_, o_, name in zip(grads, os_, ("dx", "dgamma", "dbeta", "dw", "db")):
+        assert_close(g_, o_.grad, GRAD_TOL["bf16"], name)
+
+
 def test_no_grad_records_nothing(ctx):
     a = ctx.tensor((2, 3), rnd(40, (2, 3)))
     ctx.set_grad_enabled(False)

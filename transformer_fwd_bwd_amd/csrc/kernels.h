@@ -127,11 +127,15 @@ size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C);
 // dxbf (optional) receives the bf16 copy of the final dx.  With beta_dx != 0 the
 // earlier gradient is read from dx_src (null: dx itself) and the sum written to dx.
 // dxsum (optional, [C]) receives the column sums of the final dx where the fused
-// path runs; *dxsum_written says whether it did.
+// path runs; *dxsum_written says whether it did.  gbf (optional, g then unused): the
+// upstream gradient held as bf16, read by the fused path only (hipErrorInvalidValue
+// where layernorm_bwd_bf16_fits is false; gamma, dx_src and the workspace must then
+// be 16-byte aligned as well)
+bool layernorm_bwd_bf16_fits(const float* x, const float* dx, const uint16_t* gbf, int64_t rows, int64_t C);
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
                          float* dx, const float* dx_src, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows,
                          int64_t C, float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s,
-                         float* dxsum = nullptr, bool* dxsum_written = nullptr);
+                         float* dxsum = nullptr, bool* dxsum_written = nullptr, const uint16_t* gbf = nullptr);
 // full == true: every element of the [rows, T] view is written (zeros where masked);
 // full == false: only the visible prefix of each row is touched.
 hipError_t causal_softmax_fwd(const float* x, float* p, int64_t rows, int64_t T, bool full, hipStream_t s);

@@ -8,6 +8,8 @@
 // so every result is deterministic.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace tfb {
@@ -207,8 +209,16 @@ __global__ __launch_bounds__(NT) void ln_bwd_dx_k(const float* __restrict__ g, c
 // the column sums of the final dx (the bias gradient of a Linear whose output
 // gradient this is).  A wave loads its rows two at a time, so two rows' reads are
 // in flight.
-template <int J, bool SUMDX>
-__global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, const f4* __restrict__ x,
+__device__ __forceinline__ f4 ld_g4(const f4* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ f4 ld_g4(const u16x4* p, int64_t i) {  // exact float values of 4 bf16 numbers
+  const u16x4 v = p[i];
+  return f4{__uint_as_float((unsigned)v[0] << 16), __uint_as_float((unsigned)v[1] << 16),
+            __uint_as_float((unsigned)v[2] << 16), __uint_as_float((unsigned)v[3] << 16)};
+}
+
+// GT: f4, or u16x4 for an upstream gradient held as bf16
+template <int J, bool SUMDX, typename GT = f4>
+__global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const GT* __restrict__ g, const f4* __restrict__ x,
                                                       const f4* __restrict__ gamma, const float* __restrict__ mean,
                                                       const float* __restrict__ rstd, f4* dx, const f4* dx_src,
                                                       u16x4* __restrict__ dxbf, f4* __restrict__ part, int64_t rows,
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const f4* __restrict__ g, 
         const int c = lane + 64 * j;
         const bool ok = c < C4 && rr[u] < rows;
         xv[u][j] = ok ? x[rr[u] * C4 + c] : f4{0.f, 0.f, 0.f, 0.f};
-        gv[u][j] = ok ? g[rr[u] * C4 + c] : f4{0.f, 0.f, 0.f, 0.f};
+        gv[u][j] = ok ? ld_g4(g, rr[u] * C4 + c) : f4{0.f, 0.f, 0.f, 0.f};
         sv[u][j] = ok && beta_dx != 0.f ? dx_src[rr[u] * C4 + c] : f4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
@@ -848,46 +858,61 @@ size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t C) {
   return (size_t)std::max<int64_t>(ln_bwd_parts(rows), ln_fused_blocks(rows)) * 3 * C * sizeof(float);
 }
 
+bool layernorm_bwd_bf16_fits(const float* x, const float* dx, const uint16_t* gbf, int64_t rows, int64_t C) {
+  return rows > 0 && C % 4 == 0 && C <= 1024 && aligned16(x) && aligned16(dx) &&
+         (reinterpret_cast<uintptr_t>(gbf) & 7) == 0;
+}
+
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
                          float* dx, const float* dx_src, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows,
                          int64_t C, float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s,
-                         float* dxsum, bool* dxsum_written) {
+                         float* dxsum, bool* dxsum_written, const uint16_t* gbf) {
   if (dxsum_written) *dxsum_written = false;
   if (C <= 0) return hipSuccess;
   if (!dx_src) dx_src = dx;
   float* part = static_cast<float*>(ws);
   int parts = 0, np = 2;
-  if (rows > 0 && C % 4 == 0 && C <= 1024 && aligned16(g) && aligned16(x) && aligned16(gamma) && aligned16(dx) &&
-      aligned16(dx_src) && aligned16(part) && (reinterpret_cast<uintptr_t>(dxbf) & 7) == 0) {
+  if (gbf && !layernorm_bwd_bf16_fits(x, dx, gbf, rows, C)) return hipErrorInvalidValue;
+  if (rows > 0 && C % 4 == 0 && C <= 1024 && (gbf || aligned16(g)) && aligned16(x) && aligned16(gamma) &&
+      aligned16(dx) && aligned16(dx_src) && aligned16(part) && (reinterpret_cast<uintptr_t>(dxbf) & 7) == 0 &&
+      (reinterpret_cast<uintptr_t>(gbf) & 7) == 0) {
     // dx (and its bf16 copy) and the column partials in one pass over g and x
     const int C4 = (int)(C / 4);
     const int64_t blocks = ln_fused_blocks(rows);
     const dim3 grid((unsigned)blocks), block(NT);
-    const f4 *g4 = (const f4*)g, *x4 = (const f4*)x, *gm4 = (const f4*)gamma, *src4 = (const f4*)dx_src;
-    if (dxsum) {
-      np = 3;
-      if (C4 <= 64)
-        hipLaunchKernelGGL((ln_bwd_fused4_k<1, true>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
-                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
-      else if (C4 <= 192)
-        hipLaunchKernelGGL((ln_bwd_fused4_k<3, true>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
-                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
-      else
-        hipLaunchKernelGGL((ln_bwd_fused4_k<4, true>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
-                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
-    } else {
-      if (C4 <= 64)
-        hipLaunchKernelGGL((ln_bwd_fused4_k<1, false>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
-                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
-      else if (C4 <= 192)
-        hipLaunchKernelGGL((ln_bwd_fused4_k<3, false>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
-                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
-      else
-        hipLaunchKernelGGL((ln_bwd_fused4_k<4, false>), grid, block, 0, s, g4, x4, gm4, mean, rstd, (f4*)dx, src4,
-                           (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
-    }
+    const f4 *x4 = (const f4*)x, *gm4 = (const f4*)gamma, *src4 = (const f4*)dx_src;
+    auto launch = [&](auto gp) {
+      using GT = std::remove_const_t<std::remove_pointer_t<decltype(gp)>>;
+      if (dxsum) {
+        if (C4 <= 64)
+          hipLaunchKernelGGL((ln_bwd_fused4_k<1, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
+                             (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+        else if (C4 <= 192)
+          hipLaunchKernelGGL((ln_bwd_fused4_k<3, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
+                             (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+        else
+          hipLaunchKernelGGL((ln_bwd_fused4_k<4, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
+                             (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+      } else {
+        if (C4 <= 64)
+          hipLaunchKernelGGL((ln_bwd_fused4_k<1, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
+                             (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+        else if (C4 <= 192)
+          hipLaunchKernelGGL((ln_bwd_fused4_k<3, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx,
+                             src4, (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+        else
+          hipLaunchKernelGGL((ln_bwd_fused4_k<4, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx,
+                             src4, (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+      }
+    };
+    if (dxsum) np = 3;
+    if (gbf)
+      launch((const u16x4*)gbf);
+    else
+      launch((const f4*)g);
     parts = (int)blocks;
   } else {
+    if (gbf) return hipErrorInvalidValue;  // the general kernels read fp32 (the caller converts)
     dxsum = nullptr;  // not produced on this path
     if (rows > 0 && beta_dx != 0.f && dx_src != dx) {  // the kernels below accumulate into dx itself
       const hipError_t e = hipMemcpyAsync(dx, dx_src, (size_t)(rows * C) * sizeof(float), hipMemcpyDeviceToDevice, s);

@@ -488,6 +488,18 @@ struct Ctx {
     return !a.padded() && !t.padded() && !a.leaf && a.rows() >= 128 && a.cols() % 4 == 0;
   }
 
+  // t is a bf16-only LayerNorm output whose backward can read t's gradient as bf16
+  // (the fused kernel; its shape and alignment conditions are checked here)
+  bool layernorm_takes_bf16_grad(const TensorRec& t) const {
+    if (!bf16_mode() || !t.bf16_out || t.padded() || t.producer < 0 || t.producer >= (int)c->tape.size()) return false;
+    const Rec& p = c->tape[t.producer];
+    if (&c->tensors[p.out] != &t || p.op != OP_LAYERNORM) return false;
+    const TensorRec& x = c->tensors[p.in[0]];
+    const TensorRec& gm = c->tensors[p.in[1]];
+    return !x.padded() && (reinterpret_cast<uintptr_t>(x.data) & 15) == 0 &&
+           (reinterpret_cast<uintptr_t>(gm.data) & 15) == 0 && x.cols() % 4 == 0 && x.cols() <= 1024 && x.rows() > 0;
+  }
+
   // t is a bf16-only output of the fused attention (whose backward reads its
   // gradient as bf16 and can take D from the bf16 copies)
   bool attention_out_bf16(const TensorRec& t) const {
@@ -773,7 +785,8 @@ void backward_rec(Ctx& C, const Rec& r) {
       uint16_t* dxb = first_only && C.grad_read_as_bf16(x) ? C.twin_grad(x) : nullptr;
       // ... or that copy alone, for a bf16-only GELU output (the GELU backward reads bf16)
       // or a bf16-only attention output (its backward then takes D from bf16 copies)
-      const bool only = first_only && ((!dxb && C.gelu_takes_bf16_grad(x)) || (dxb && C.attention_out_bf16(x)));
+      const bool only = first_only && ((!dxb && (C.gelu_takes_bf16_grad(x) || C.layernorm_takes_bf16_grad(x))) ||
+                                        (dxb && C.attention_out_bf16(x)));
       if (only) dxb = C.twin_grad(x);
       gemm_nt(C, go, op_data(C, w), dx.first, rows, N, K, dx.second, -1, dxb, only);   // dx = g @ w^T
       if (dxb) x.gbf_valid = true;
@@ -821,9 +834,18 @@ void backward_rec(Ctx& C, const Rec& r) {
       size_t mark = C.c->arena.hi;
       void* ws = C.scratch(layernorm_bwd_workspace_bytes(rows, Cc));
       bool summed = false;
+      // an upstream gradient held only as bf16 is read as such where the fused kernel runs
+      const uint16_t* gb = out.gstate == G_BF16 ? out.gbf : nullptr;
+      if (gb && !(layernorm_bwd_bf16_fits(x.data, dx.dst, gb, rows, Cc) && (reinterpret_cast<uintptr_t>(gm.data) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(dx.src ? dx.src : dx.dst) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(ws) & 15) == 0)) {
+        hip_check(to_f32(gb, out.grad, out.storage(), s), "layernorm upstream gradient");
+        out.gstate = G_VALID;
+        gb = nullptr;
+      }
       hip_check(layernorm_bwd(g, x.data, gm.data, static_cast<float*>(r.s0), static_cast<float*>(r.s1), dx.dst,
                               dx.src, dxb, dg.first, db.first, rows, Cc, dx.beta, dg.second, db.second, ws, s, dxs,
-                              &summed),
+                              &summed, gb),
                 "layernorm bwd");
       C.c->arena.hi = mark;
       if (dxb) x.gbf_valid = true;
