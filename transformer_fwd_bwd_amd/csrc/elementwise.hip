@@ -11,6 +11,7 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "reduce_dev.h"
 
 namespace tfb {
 namespace {
@@ -210,21 +211,7 @@ __global__ __launch_bounds__(NT) void gelu_bwd_cols4_k(const GT* __restrict__ g,
 // out[c] (+)= sum over the partial rows; 64 columns x 16 partial-groups per workgroup
 __global__ __launch_bounds__(1024) void colsum_stage2(const float* __restrict__ partial, int nparts, int64_t cols,
                                                       float* __restrict__ out, float beta) {
-  __shared__ float sh[16][65];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const int64_t c = (int64_t)blockIdx.x * 64 + tx;
-  float a = 0.f;
-  if (c < cols)
-    for (int p = ty; p < nparts; p += 16) a += partial[(int64_t)p * cols + c];
-  sh[ty][tx] = a;
-  __syncthreads();
-  if (ty == 0 && c < cols) {
-    float r = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r += sh[i][tx];
-    if (beta != 0.f) r += beta * out[c];
-    out[c] = r;
-  }
+  colsum_reduce_cols(partial, nparts, cols, out, beta, blockIdx.x);
 }
 
 __device__ __forceinline__ float block_sum(float v) {
@@ -463,10 +450,24 @@ bool gelu_bwd_cols_fits(const float* g, const void* x, const float* d, const uin
          aligned16(d) && aligned16(ws) && (reinterpret_cast<uintptr_t>(dbf) & 7) == 0;
 }
 
+// the column reduction of slab partials: launched now, or described in *defer
+static void stage2(const float* partial, int parts, int64_t cols, float* out, float beta, hipStream_t s,
+                   ReduceJob* defer) {
+  if (defer) {
+    *defer = ReduceJob{};
+    defer->kind = REDUCE_COLSUM, defer->part = partial, defer->nparts = parts, defer->cols = cols;
+    defer->out[0] = out, defer->beta[0] = beta;
+    return;
+  }
+  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, parts, cols, out,
+                     beta);
+}
+
 hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t rows,
                          int64_t cols, float* dcol, void* ws, hipStream_t s, bool* dcol_written, const uint16_t* xbf,
-                         const uint16_t* gbf) {
+                         const uint16_t* gbf, ReduceJob* defer) {
   *dcol_written = false;
+  if (defer) defer->kind = 0;  // nothing deferred unless the row-slab path runs
   float* partial = static_cast<float*>(ws);
   if (!d && (!dbf || beta != 0.f)) return hipErrorInvalidValue;
   const float* gchk = gbf ? reinterpret_cast<const float*>(gbf) : g;
@@ -494,14 +495,13 @@ hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf
     else
       launch((const f4*)g, (const f4*)x);
   }
-  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, (int)parts, cols,
-                     dcol, 0.f);
+  stage2(partial, (int)parts, cols, dcol, 0.f, s, defer);
   *dcol_written = true;
   return hipGetLastError();
 }
 
 hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s,
-                  const uint16_t* gbf) {
+                  const uint16_t* gbf, ReduceJob* defer) {
   if (cols <= 0) return hipSuccess;
   float* partial = static_cast<float*>(ws);
   if (gbf) {  // the gradient as bf16: the float4-group path only
@@ -510,10 +510,10 @@ hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float 
     const int64_t parts = colsum4_parts(rows), rows_per = (rows + parts - 1) / parts, cols4 = cols / 4;
     hipLaunchKernelGGL(colsum4_stage1<u16x4>, dim3((unsigned)((cols4 + 63) / 64), (unsigned)parts), dim3(NT), 0, s,
                        (const u16x4*)gbf, rows, cols4, rows_per, (f4*)partial);
-    hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, (int)parts, cols,
-                       out, beta);
+    stage2(partial, (int)parts, cols, out, beta, s, defer);
     return hipGetLastError();
   }
+  if (defer) defer->kind = 0;  // nothing deferred unless the two-stage path runs
   if (rows == 1) return axpby(out, g, 1.f, beta, cols, s);
   const bool vec = cols % 4 == 0 && aligned16(g) && aligned16(partial);
   const int64_t parts = vec ? colsum4_parts(rows) : colsum_parts(rows, cols);
@@ -526,8 +526,7 @@ hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float 
     dim3 g1((unsigned)((cols + NT - 1) / NT), (unsigned)parts);
     hipLaunchKernelGGL(colsum_stage1, g1, dim3(NT), 0, s, g, rows, cols, rows_per, partial);
   }
-  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, (int)parts, cols,
-                     out, beta);
+  stage2(partial, (int)parts, cols, out, beta, s, defer);
   return hipGetLastError();
 }
 

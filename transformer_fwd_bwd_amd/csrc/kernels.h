@@ -76,6 +76,25 @@ struct AxpbyJobs {
   int count = 0;
 };
 hipError_t axpby_batch(const AxpbyJobs& jobs, hipStream_t s);
+// The second stage of a column reduction (LayerNorm parameter gradients, column sums
+// of a gradient), described instead of launched where a caller passes a ReduceJob*:
+// the caller then runs it later, batched with others (reduce_batch), each job with the
+// same arithmetic as the one-at-a-time launch.  Outputs of one batch must be distinct.
+enum { REDUCE_LN = 1, REDUCE_COLSUM = 2 };
+struct ReduceJob {
+  int kind = 0;
+  const float* part = nullptr;  // slab partials (kept alive by the caller until the batch runs)
+  int nparts = 0, np = 1;       // slabs; planes per slab (REDUCE_LN)
+  int64_t cols = 0;
+  float* out[3] = {nullptr, nullptr, nullptr};  // LN: dgamma, dbeta, dx column sums (optional)
+  float beta[3] = {0.f, 0.f, 0.f};
+};
+constexpr int REDUCE_BATCH = 32;
+struct ReduceJobs {
+  ReduceJob j[REDUCE_BATCH];
+  int count = 0;
+};
+hipError_t reduce_batch(const ReduceJobs& jobs, hipStream_t s);
 // dst[r*ldd + c] = src[r*lds + c] (+ dst when beta == 1), c < cols
 hipError_t copy_pitched(const float* src, int64_t lds, float* dst, int64_t ldd, int64_t rows, int64_t cols,
                         float beta, hipStream_t s);
@@ -96,7 +115,7 @@ hipError_t gelu_bwd(const float* g, const float* x, float* d, uint16_t* dbf, flo
 // need the row-slab path: hipErrorInvalidValue where it does not fit (gelu_bwd_cols_fits)
 hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf, float beta, int64_t rows,
                          int64_t cols, float* dcol, void* ws, hipStream_t s, bool* dcol_written,
-                         const uint16_t* xbf = nullptr, const uint16_t* gbf = nullptr);
+                         const uint16_t* xbf = nullptr, const uint16_t* gbf = nullptr, ReduceJob* defer = nullptr);
 bool gelu_bwd_cols_fits(const float* g, const void* x, const float* d, const uint16_t* dbf, int64_t rows,
                         int64_t cols, const void* ws);
 // gelu_fwd reading the input's bf16 copy
@@ -106,7 +125,7 @@ hipError_t gelu_fwd_bf(const uint16_t* a, float* y, uint16_t* ybf, int64_t n, hi
 // hipErrorInvalidValue)
 size_t colsum_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float beta, void* ws, hipStream_t s,
-                  const uint16_t* gbf = nullptr);
+                  const uint16_t* gbf = nullptr, ReduceJob* defer = nullptr);
 // out[0] = sum of a (deterministic); sum_bwd: d = beta*d + g[0]
 size_t sum_workspace_bytes(int64_t n);
 hipError_t sum_all(const float* a, int64_t n, float* out, void* ws, hipStream_t s);
@@ -135,7 +154,8 @@ bool layernorm_bwd_bf16_fits(const float* x, const float* dx, const uint16_t* gb
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
                          float* dx, const float* dx_src, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows,
                          int64_t C, float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s,
-                         float* dxsum = nullptr, bool* dxsum_written = nullptr, const uint16_t* gbf = nullptr);
+                         float* dxsum = nullptr, bool* dxsum_written = nullptr, const uint16_t* gbf = nullptr,
+                         ReduceJob* defer = nullptr);
 // full == true: every element of the [rows, T] view is written (zeros where masked);
 // full == false: only the visible prefix of each row is touched.
 hipError_t causal_softmax_fwd(const float* x, float* p, int64_t rows, int64_t T, bool full, hipStream_t s);

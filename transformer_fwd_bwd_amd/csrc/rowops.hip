@@ -11,6 +11,7 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "reduce_dev.h"
 
 namespace tfb {
 namespace {
@@ -343,52 +344,17 @@ __global__ __launch_bounds__(NT) void ln_bwd_cols_k(const float* __restrict__ g,
 __global__ __launch_bounds__(1024) void ln_bwd_reduce(const float* __restrict__ part, int nparts, int np, int C,
                                                       float* __restrict__ dgamma, float* __restrict__ dbeta,
                                                       float* __restrict__ dxsum, float beta_dg, float beta_db) {
-  // 16 columns x 64 partial groups per workgroup; the groups are added in a fixed order
-  __shared__ float sa[64][17], sb[64][17], sd[64][17];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int c = blockIdx.x * 16 + tx;
-  float a = 0.f, b = 0.f, d = 0.f;
-  if (c < C) {
-    int p = ty;
-    for (; p + 192 < nparts; p += 256) {  // four partials in flight per thread
-      float ta[4], tb[4], td[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t o = ((int64_t)(p + 64 * u) * np) * C + c;
-        ta[u] = part[o];
-        tb[u] = part[o + C];
-        td[u] = dxsum ? part[o + 2 * C] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a += ta[u];
-        b += tb[u];
-        d += td[u];
-      }
-    }
-    for (; p < nparts; p += 64) {
-      a += part[((int64_t)p * np) * C + c];
-      b += part[((int64_t)p * np + 1) * C + c];
-      if (dxsum) d += part[((int64_t)p * np + 2) * C + c];
-    }
-  }
-  sa[ty][tx] = a;
-  sb[ty][tx] = b;
-  sd[ty][tx] = d;
-  __syncthreads();
-  if (ty == 0 && c < C) {
-    float ra = 0.f, rb = 0.f, rd = 0.f;
-#pragma unroll 4
-    for (int i = 0; i < 64; ++i) {
-      ra += sa[i][tx];
-      rb += sb[i][tx];
-      rd += sd[i][tx];
-    }
-    if (beta_dg != 0.f) ra += dgamma[c];
-    if (beta_db != 0.f) rb += dbeta[c];
-    dgamma[c] = ra;
-    dbeta[c] = rb;
-    if (dxsum) dxsum[c] = rd;
+  ln_reduce_cols(part, nparts, np, C, dgamma, dbeta, dxsum, beta_dg, beta_db, blockIdx.x);
+}
+
+__global__ __launch_bounds__(1024) void reduce_batch_k(ReduceJobs jobs) {
+  const ReduceJob& j = jobs.j[blockIdx.y];
+  const int bx = blockIdx.x;
+  if (j.kind == REDUCE_LN) {
+    if (bx * 16 < j.cols)
+      ln_reduce_cols(j.part, j.nparts, j.np, (int)j.cols, j.out[0], j.out[1], j.out[2], j.beta[0], j.beta[1], bx);
+  } else {
+    if ((int64_t)bx * 64 < j.cols) colsum_reduce_cols(j.part, j.nparts, j.cols, j.out[0], j.beta[0], bx);
   }
 }
 
@@ -866,7 +832,7 @@ bool layernorm_bwd_bf16_fits(const float* x, const float* dx, const uint16_t* gb
 hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, const float* mean, const float* rstd,
                          float* dx, const float* dx_src, uint16_t* dxbf, float* dgamma, float* dbeta, int64_t rows,
                          int64_t C, float beta_dx, float beta_dg, float beta_db, void* ws, hipStream_t s,
-                         float* dxsum, bool* dxsum_written, const uint16_t* gbf) {
+                         float* dxsum, bool* dxsum_written, const uint16_t* gbf, ReduceJob* defer) {
   if (dxsum_written) *dxsum_written = false;
   if (C <= 0) return hipSuccess;
   if (!dx_src) dx_src = dx;
@@ -935,9 +901,28 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + 15) / 16)), dim3(1024), 0, s, part, parts, np, (int)C,
-                     dgamma, dbeta, dxsum, beta_dg, beta_db);
+  if (defer) {
+    *defer = ReduceJob{};
+    defer->kind = REDUCE_LN, defer->part = part, defer->nparts = parts, defer->np = np, defer->cols = C;
+    defer->out[0] = dgamma, defer->out[1] = dbeta, defer->out[2] = dxsum;
+    defer->beta[0] = beta_dg, defer->beta[1] = beta_db;
+  } else {
+    hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + 15) / 16)), dim3(1024), 0, s, part, parts, np, (int)C,
+                       dgamma, dbeta, dxsum, beta_dg, beta_db);
+  }
   if (dxsum_written) *dxsum_written = dxsum != nullptr;
+  return hipGetLastError();
+}
+
+hipError_t reduce_batch(const ReduceJobs& jobs, hipStream_t s) {
+  if (jobs.count <= 0) return hipSuccess;
+  if (jobs.count > REDUCE_BATCH) return hipErrorInvalidValue;
+  int64_t blocks = 1;
+  for (int i = 0; i < jobs.count; ++i) {
+    const ReduceJob& j = jobs.j[i];
+    blocks = std::max<int64_t>(blocks, j.kind == REDUCE_LN ? (j.cols + 15) / 16 : (j.cols + 63) / 64);
+  }
+  hipLaunchKernelGGL(reduce_batch_k, dim3((unsigned)blocks, (unsigned)jobs.count), dim3(1024), 0, s, jobs);
   return hipGetLastError();
 }
 

@@ -174,6 +174,10 @@ struct tfb_ctx {
   // bias gradients taken from column sums, added in one launch at the end of the
   // backward pass (nothing reads a leaf's gradient before then)
   AxpbyJobs bias_jobs;
+  // second stages of column reductions (LayerNorm parameter gradients, column sums of
+  // gradients), run in one launch before the bias jobs; their partials live in the
+  // step arena until then
+  ReduceJobs reduce_jobs;
 };
 
 struct tfb_kv {
@@ -414,15 +418,41 @@ struct Ctx {
   }
 
   // buffer for t's gradient column sums (non-leaf tensors only)
-  // a queued bias job must land before any other contribution to the same gradient
+  // a queued job must land before any other contribution to the same gradient
   void flush_bias_into(const float* g) {
-    for (int i = 0; g && i < c->bias_jobs.count; ++i)
+    if (!g) return;
+    for (int i = 0; i < c->reduce_jobs.count; ++i)
+      for (float* o : c->reduce_jobs.j[i].out)
+        if (o == g) {
+          flush_bias();  // the reductions first, then the bias jobs that read their sums
+          return;
+        }
+    for (int i = 0; i < c->bias_jobs.count; ++i)
       if (c->bias_jobs.j[i].dst == g) {
         flush_bias();
         return;
       }
   }
+  void flush_reduce() {
+    hip_check(reduce_batch(c->reduce_jobs, s()), "column reductions");
+    c->reduce_jobs.count = 0;
+  }
+  // queue a described reduction (kind 0: nothing was deferred); a job writing an output
+  // that a queued one writes first lets the queue run
+  void defer_reduce(const ReduceJob& j) {
+    if (j.kind == 0) return;
+    ReduceJobs& q = c->reduce_jobs;
+    bool clash = q.count == REDUCE_BATCH;
+    for (int i = 0; i < q.count && !clash; ++i)
+      for (float* a : q.j[i].out)
+        for (float* b : j.out) clash = clash || (a && a == b);
+    if (clash) flush_reduce();
+    q.j[q.count++] = j;
+  }
+  // workspace for partials that a deferred reduction reads later: the step arena
+  void* keep(size_t bytes) { return c->arena.alloc_step(std::max<size_t>(bytes, 256)); }
   void flush_bias() {
+    flush_reduce();
     hip_check(axpby_batch(c->bias_jobs, s()), "bias gradients");
     c->bias_jobs.count = 0;
   }
@@ -723,22 +753,21 @@ void backward_rec(Ctx& C, const Rec& r) {
       // bias gradient from the column sums below): that copy alone, no fp32 gradient
       if (dcol && a.bf16_out && a.uses == 1 && !a.gpend && a.gstate != G_VALID && C.grad_read_as_bf16(a)) {
         uint16_t* db = C.twin_grad(a);
-        size_t mark = C.c->arena.hi;
-        void* ws = C.scratch(colsum_workspace_bytes(a.rows(), a.cols()));
+        void* ws = C.keep(colsum_workspace_bytes(a.rows(), a.cols()));  // read by the deferred reduction
         const void* xin = a.f32_valid ? (const void*)a.data : (const void*)a.bf;
         if (db && gelu_bwd_cols_fits(gb ? reinterpret_cast<const float*>(gb) : g, xin, nullptr, db, a.rows(), a.cols(), ws) &&
             (!a.f32_valid || (reinterpret_cast<uintptr_t>(a.data) & 15) == 0)) {
           bool written = false;
+          ReduceJob job;
           hip_check(gelu_bwd_cols(g, a.f32_valid ? a.data : nullptr, nullptr, db, 0.f, a.rows(), a.cols(), dcol, ws, s,
-                                  &written, a.f32_valid ? nullptr : a.bf, gb),
+                                  &written, a.f32_valid ? nullptr : a.bf, gb, &job),
                     "gelu bwd");
-          C.c->arena.hi = mark;
+          C.defer_reduce(job);
           a.gstate = G_BF16;
           a.gbf_valid = true;
           a.gcol_valid = written;
           break;
         }
-        C.c->arena.hi = mark;
       }
       if (gb) {  // the general paths read fp32: convert the upstream gradient
         hip_check(to_f32(gb, out.grad, out.storage(), s), "gelu upstream gradient");
@@ -748,15 +777,15 @@ void backward_rec(Ctx& C, const Rec& r) {
       auto da = C.gdst(r.in[0]);
       uint16_t* db = C.twin_grad(a);
       if (dcol) {  // with the column sums a reading Linear takes as its bias gradient
-        size_t mark = C.c->arena.hi;
-        void* ws = C.scratch(colsum_workspace_bytes(a.rows(), a.cols()));
+        void* ws = C.keep(colsum_workspace_bytes(a.rows(), a.cols()));  // read by the deferred reduction
         // an input held only as bf16 is read as such where the row-slab kernel fits
         const bool abf = !a.f32_valid && gelu_bwd_cols_fits(g, a.bf, da.first, db, a.rows(), a.cols(), ws);
         bool written = false;
+        ReduceJob job;
         hip_check(gelu_bwd_cols(g, abf ? nullptr : C.f32(a), da.first, db, da.second, a.rows(), a.cols(), dcol, ws,
-                                s, &written, abf ? a.bf : nullptr),
+                                s, &written, abf ? a.bf : nullptr, nullptr, &job),
                   "gelu bwd");
-        C.c->arena.hi = mark;
+        C.defer_reduce(job);
         a.gcol_valid = written;
       } else {
         hip_check(gelu_bwd(g, C.f32(a), da.first, db, da.second, out.numel, s), "gelu bwd");
@@ -798,11 +827,11 @@ void backward_rec(Ctx& C, const Rec& r) {
         if (out.gcol_valid && out.cols() == N) {  // summed by the kernel that finished g
           C.defer_bias(db.first, out.gcol, N, db.second);
         } else {
-          size_t mark = C.c->arena.hi;
-          void* ws = C.scratch(colsum_workspace_bytes(rows, N));
-          hip_check(colsum(g, rows, N, db.first, db.second, ws, s, out.gstate == G_BF16 ? out.gbf : nullptr),
+          void* ws = C.keep(colsum_workspace_bytes(rows, N));  // read by the deferred reduction
+          ReduceJob job;
+          hip_check(colsum(g, rows, N, db.first, db.second, ws, s, out.gstate == G_BF16 ? out.gbf : nullptr, &job),
                     "linear bias bwd");
-          C.c->arena.hi = mark;
+          C.defer_reduce(job);
         }
       }
       break;
@@ -831,8 +860,7 @@ void backward_rec(Ctx& C, const Rec& r) {
       uint16_t* dxb = x.leaf ? nullptr : C.twin_grad(x);
       // and its column sums: the bias gradient of a Linear whose output this gradient also is
       float* dxs = C.gcol_buf(x);
-      size_t mark = C.c->arena.hi;
-      void* ws = C.scratch(layernorm_bwd_workspace_bytes(rows, Cc));
+      void* ws = C.keep(layernorm_bwd_workspace_bytes(rows, Cc));  // read by the deferred reduction
       bool summed = false;
       // an upstream gradient held only as bf16 is read as such where the fused kernel runs
       const uint16_t* gb = out.gstate == G_BF16 ? out.gbf : nullptr;
@@ -843,11 +871,12 @@ void backward_rec(Ctx& C, const Rec& r) {
         out.gstate = G_VALID;
         gb = nullptr;
       }
+      ReduceJob job;
       hip_check(layernorm_bwd(g, x.data, gm.data, static_cast<float*>(r.s0), static_cast<float*>(r.s1), dx.dst,
                               dx.src, dxb, dg.first, db.first, rows, Cc, dx.beta, dg.second, db.second, ws, s, dxs,
-                              &summed, gb),
+                              &summed, gb, &job),
                 "layernorm bwd");
-      C.c->arena.hi = mark;
+      C.defer_reduce(job);
       if (dxb) x.gbf_valid = true;
       x.gcol_valid = summed;
       break;
@@ -1748,6 +1777,7 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss) {
     hip_check(fill(L.grad, 1.f, 1, C.s()), "seed");
     L.gstate = G_VALID;
     ctx->bias_jobs.count = 0;
+    ctx->reduce_jobs.count = 0;
     for (int i = (int)ctx->tape.size() - 1; i >= 0; --i) {
       const Rec& r = ctx->tape[i];
       TensorRec& out = ctx->tensors[r.out];
