@@ -521,6 +521,10 @@ hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float 
   if (vec) {
     const int64_t cols4 = cols / 4;
     dim3 g1((unsigned)((cols4 + 63) / 64), (unsigned)parts);
+    if (parts == 1 && beta == 0.f && aligned16(out)) {  // few rows (a broadcast add over the batch): one pass
+      hipLaunchKernelGGL(colsum4_stage1<f4>, g1, dim3(NT), 0, s, (const f4*)g, rows, cols4, rows_per, (f4*)out);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(colsum4_stage1<f4>, g1, dim3(NT), 0, s, (const f4*)g, rows, cols4, rows_per, (f4*)partial);
   } else {
     dim3 g1((unsigned)((cols + NT - 1) / NT), (unsigned)parts);
