@@ -734,6 +734,38 @@ def test_layernorm_gradient_kept_as_bf16(ctx, C):
         assert_close(g_, o_.grad, GRAD_TOL["bf16"], name)
 
 
+@pytest.mark.parametrize("prec", PRECS)
+def test_shared_parameters_accumulate_through_deferred_sums(ctx, prec):
+    """One LayerNorm's gamma/beta and one Linear's weight/bias used twice in a row
+    (x -> LN -> Linear -> GELU -> LN -> Linear): the bias and LayerNorm gradients come
+    from column sums that are queued and run at the end of the backward pass; the second
+    contribution to each shared gradient must land on the first.  Every gradient against
+    the oracle (300 rows, 64 columns)."""
+    ctx.set_precision(prec)
+    C = 64
+    xv, gv, bv = rnd(181, (300, C), 2.0), 1 + rnd(182, (C,), 0.2), rnd(183, (C,), 0.2)
+    W, c = rnd(184, (C, C), 0.2), rnd(185, (C,), 0.1)
+    R = rnd(186, (300, C))
+    ts = [ctx.tensor(a.shape, a) for a in (xv, gv, bv, W, c)]
+    x, g, b, w, cb = ts
+    h = T.linear(T.layernorm(x, g, b), w, cb)
+    y = T.linear(T.layernorm(T.gelu(h), g, b), w, cb)
+    Rt = ctx.tensor(R.shape, R)
+    ctx.backward(T.sum_all(T.mul(y, Rt)))
+    grads = [t.grad() for t in ts]
+    ctx.tape_reset()
+    for t in ts + [Rt]:
+        t.release()
+    ctx.set_precision("fp32")
+    os_ = [E.Tensor(a.astype(np.float64)) for a in (xv, gv, bv, W, c)]
+    ox, og, ob, ow, oc = os_
+    oh = E.add(E.matmul(E.layernorm(ox, og, ob, 1e-5), ow), oc)
+    oy = E.add(E.matmul(E.layernorm(E.gelu(oh), og, ob, 1e-5), ow), oc)
+    E.sum_all(E.mul(oy, E.Tensor(R.astype(np.float64)))).backward()
+    for g_, o_, name in zip(grads, os_, ("dx", "dgamma", "dbeta", "dw", "db")):
+        assert_close(g_, o_.grad, GRAD_TOL[prec], name)
+
+
 def test_no_grad_records_nothing(ctx):
     a = ctx.tensor((2, 3), rnd(40, (2, 3)))
     ctx.set_grad_enabled(False)
