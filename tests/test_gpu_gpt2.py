@@ -6,6 +6,9 @@
   sequence against the oracle's forward of that sequence (sequences are
   independent in the forward), and the gradient checked at full size by a
   central finite difference of the GPU's own loss along the computed gradient.
+  The bf16 variant's 148 gradients at that size are checked against the fp32
+  variant's (the kernels and tilings this size selects differ from the
+  256-token case's).
 """
 import numpy as np
 import pytest
@@ -109,3 +112,28 @@ def test_gpt2_full_launch_config(big, prec):
     for t in model.param_list:
         t.release()
     big.set_precision("fp32")
+
+
+def test_gpt2_full_launch_config_bf16_gradients(big):
+    """All 148 parameter gradients of the bf16 variant at 8 x 1024 tokens (the tile
+    shapes, raster groups, bf16-only intermediates and deferred column sums of the
+    timed configuration) against the fp32 variant's on the same batch, within the
+    bf16 tolerance; the fp32 gradient is itself checked above by finite differences."""
+    s, params, ids = S.gpt2(batch=8, seq=1024)
+    import torch
+    ids_dev = torch.from_numpy(ids).to("cuda:0")
+    inputs, targets = G.split_ids(ids_dev)
+    grads = {}
+    for prec in ("fp32", "bf16"):
+        big.set_precision(prec)
+        model = G.Gpt(big, s.n_layer, s.n_head, params)
+        loss, _ = model.loss(inputs, targets)
+        big.backward(loss)
+        grads[prec] = {k: model.P[k].grad() for k in model.names}
+        big.tape_reset()
+        for t in model.param_list:
+            t.release()
+    big.set_precision("fp32")
+    assert len(grads["bf16"]) == 148
+    for k, g32 in grads["fp32"].items():
+        assert_close(grads["bf16"][k], g32, GRAD_TOL["bf16"], k)
