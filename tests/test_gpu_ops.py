@@ -766,6 +766,30 @@ def test_shared_parameters_accumulate_through_deferred_sums(ctx, prec):
         assert_close(g_, o_.grad, GRAD_TOL[prec], name)
 
 
+def test_unknown_output_flags_are_rejected(ctx):
+    """Every entry point with output flags rejects unknown bits with TFB_ERR_ARG (-1)
+    and records nothing."""
+    import ctypes
+    from transformer_fwd_bwd_amd import _out
+    lib = T.load_library()
+    x, w, b = ctx.tensor((4, 8), rnd(191, (4, 8))), ctx.tensor((8, 8), rnd(192, (8, 8))), ctx.tensor((8,), rnd(193, (8,)))
+    g1, qkv = ctx.tensor((8,), np.ones(8, np.float32)), ctx.tensor((1, 4, 96), rnd(194, (1, 4, 96)))
+    calls = [
+        lambda: _out(ctx, lib.tfb_linear_ex, x.h, w.h, b.h, 8),
+        lambda: _out(ctx, lib.tfb_matmul_t_ex, x.h, w.h, 8),
+        lambda: _out(ctx, lib.tfb_gelu_ex, x.h, 8),
+        lambda: _out(ctx, lib.tfb_layernorm_ex, x.h, g1.h, b.h, ctypes.c_float(1e-5), 8),
+        lambda: _out(ctx, lib.tfb_causal_attention_ex, qkv.h, 2, 8),
+    ]
+    for call in calls:
+        with pytest.raises(T.TfbError) as e:
+            call()
+        assert e.value.code == -1
+    ctx.tape_reset()
+    for t in (x, w, b, g1, qkv):
+        t.release()
+
+
 def test_no_grad_records_nothing(ctx):
     a = ctx.tensor((2, 3), rnd(40, (2, 3)))
     ctx.set_grad_enabled(False)
