@@ -167,3 +167,57 @@ def test_tiny_gpt_step(ctx, prec):
     for t in model.param_list:
         t.release()
     ctx.set_precision("fp32")
+
+
+@pytest.mark.parametrize("adam", [False, True])
+def test_circle_classifier_trains_like_the_oracle(ctx, adam):
+    """[Autograd-1, "Training loop"]: the 2 -> 16 (tanh) -> 2 classifier of the circle
+    x^2 + y^2 < 0.5 trained for 500 steps on the GPU with SGD or AdamW (lr 0.05, no
+    weight decay), from the same seeded start as the oracle run: the losses follow the
+    oracle's trajectory (float32 against float64 over 500 steps), and AdamW ends well
+    under SGD with the points separated."""
+    from oracle import optim as OPT
+    rng = S.rng_for(11)
+    xs = rng.uniform(-1, 1, size=(256, 2)).astype(np.float32)
+    ys = ((xs.astype(np.float64) ** 2).sum(1) < 0.5).astype(np.int32)
+    r = S.rng_for(12)
+    init = [(r.standard_normal((2, 16)) * 0.5).astype(np.float32), np.zeros(16, np.float32),
+            (r.standard_normal((16, 2)) * 0.5).astype(np.float32), np.zeros(2, np.float32)]
+
+    # oracle (float64) from the float32 start
+    P = [E.Tensor(a.astype(np.float64)) for a in init]
+    oopt = OPT.AdamW(P, lr=0.05, weight_decay=0.0) if adam else OPT.SGD(P, lr=0.05)
+    X = E.Tensor(xs.astype(np.float64))
+    ref = []
+    for _ in range(500):
+        logits = E.add(E.matmul(E.tanh(E.add(E.matmul(X, P[0]), P[1])), P[2]), P[3])
+        loss = E.softmax_cross_entropy(logits, ys)
+        oopt.zero_grad()
+        loss.backward()
+        oopt.step()
+        ref.append(loss.item())
+
+    ctx.set_precision("fp32")
+    ts = [ctx.tensor(a.shape, a, param=True) for a in init]
+    xt = ctx.tensor(xs.shape, xs)
+    gopt = T.AdamW(ts, lr=0.05, weight_decay=0.0) if adam else None
+    got = []
+    for _ in range(500):
+        logits = T.linear(T.tanh(T.linear(xt, ts[0], ts[1])), ts[2], ts[3])
+        loss = T.softmax_cross_entropy(logits, ys)
+        ctx.zero_grad(ts)
+        ctx.backward(loss)
+        if adam:
+            gopt.step()
+        else:
+            T.sgd_step(ts, 0.05)
+        got.append(loss.item())
+        ctx.tape_reset()
+    pred = T.linear(T.tanh(T.linear(xt, ts[0], ts[1])), ts[2], ts[3]).numpy().argmax(1)
+    ctx.tape_reset()
+    for t in ts + [xt]:
+        t.release()
+    got, ref = np.array(got), np.array(ref)
+    assert np.max(np.abs(got - ref) / np.maximum(ref, 1e-3)) < 2e-2, "loss trajectory"
+    if adam:
+        assert got[-1] < 0.1 and (pred == ys).mean() > 0.97
