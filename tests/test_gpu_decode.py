@@ -103,6 +103,51 @@ def test_kv_step_equals_full_forward(ctx):
         t.release()
 
 
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_uncached_generation_equals_cached_at_every_step(ctx, prec):
+    """[GPT2-4, "Generation with KV cache"]: generation without the cache (the whole
+    forward per new token, sampled from the last position) against the cached path
+    at every step -- same logits, same tokens -- and against the oracle's full forward
+    over the sequence it sampled.  The sequences run up to the last position embedding."""
+    import torch
+    s, params, _ = S.tiny_gpt()
+    ctx.set_precision(prec)
+    model = G.Gpt(ctx, s.n_layer, s.n_head, params)
+    B, Pn, k = 3, 9, 20
+    steps = s.n_positions - Pn + 1                      # the last step's input is position n_positions - 1
+    prompts = S.random_ids(74, (B, Pn), s.vocab)
+    u = S.rng_for(75).random((B, steps))
+    pd, ud = torch.from_numpy(prompts).to("cuda:0"), torch.from_numpy(u).to("cuda:0")
+    cached, full = [], []
+    tc = model.generate(pd, steps, ud, k, 1.0, on_step=lambda i, lg, tk: cached.append(lg.numpy().reshape(B, -1)))
+    tu = model.generate_uncached(pd, steps, ud, k, 1.0, on_step=lambda i, lg, tk: full.append(lg.numpy().reshape(B, -1)))
+    tc, tu = tc.cpu().numpy(), tu.cpu().numpy()
+    assert tu.shape == (B, steps) and len(full) == steps
+    seq = np.concatenate([prompts, tu[:, :-1]], axis=1)
+    with E.no_grad():
+        ref = M.gpt_logits(M.as_tensors(params), seq, s.n_layer, s.n_head).data
+    for b in range(B):
+        diff = np.flatnonzero(tc[b] != tu[b])
+        same_until = diff[0] if diff.size else steps      # the two paths saw the same sequence up to here
+        if prec == "fp32":
+            assert same_until == steps or near_boundary(
+                D.top_k_temperature_probs(ref[b, Pn - 1 + same_until], k, 1.0), u[b, same_until]), (b, same_until)
+        for i in range(steps):
+            assert_close(full[i][b], ref[b, Pn - 1 + i], FWD_TOL[prec], f"uncached step {i} row {b}")
+            if i <= same_until and i < steps:
+                assert_close(full[i][b], cached[i][b], FWD_TOL[prec], f"uncached vs cached step {i} row {b}")
+            p = D.top_k_temperature_probs(ref[b, Pn - 1 + i], k, 1.0)
+            assert tu[b, i] == D.sample(p, u[b, i]) or near_boundary(p, u[b, i]) or prec == "bf16", (b, i)
+    with pytest.raises(ValueError):
+        model.generate_uncached(pd, steps + 1, torch.from_numpy(S.rng_for(76).random((B, steps + 1))).to("cuda:0"),
+                                k, 1.0)
+    with pytest.raises(ValueError):
+        model.generate(pd, steps + 1, torch.from_numpy(S.rng_for(76).random((B, steps + 1))).to("cuda:0"), k, 1.0)
+    for t in model.param_list:
+        t.release()
+    ctx.set_precision("fp32")
+
+
 def test_inference_workload_gpt2_shape(ctx):
     """16 prompts x 768 tokens, then 256 sampled steps (top-k 40, temperature 1)
     at the GPT-2-124M shape; sampled steps of sequence 5 against the oracle's

@@ -15,7 +15,7 @@ from typing import Dict, List, Sequence
 import numpy as np
 
 from . import (AdamW, Context, KvCache, Tensor, add, causal_attention, embedding, gelu, layernorm, linear, matmul_t,
-               reshape, sample_topk, softmax_cross_entropy, tanh)
+               narrow, reshape, sample_topk, softmax_cross_entropy, tanh)
 
 
 def upload_params(ctx: Context, params: Dict[str, np.ndarray]) -> Dict[str, Tensor]:
@@ -40,11 +40,13 @@ class Gpt:
             self._pos[T] = torch.arange(T, dtype=torch.int32, device=f"cuda:{self.ctx.device}")
         return self._pos[T]
 
-    def logits(self, ids) -> Tensor:
-        """ids: [B, T] int32 (numpy or a device torch tensor)."""
+    def hidden(self, ids) -> Tensor:
+        """ids: [B, T] int32 (numpy or a device torch tensor) -> the last block's output [B, T, C]."""
         P = self.P
         B, T = ids.shape
         C = P["wte.weight"].shape[1]
+        if T > P["wpe.weight"].shape[0]:
+            raise ValueError(f"{T} positions exceed the {P['wpe.weight'].shape[0]} position embeddings")
         tok = embedding(P["wte.weight"], ids, B)                          # [B, T, C]
         pos = reshape(embedding(P["wpe.weight"], self.positions(T), 1), (T, C))
         x = add(tok, pos)
@@ -60,7 +62,12 @@ class Gpt:
             h = layernorm(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"], bf16_only=True)
             f = gelu(linear(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"], bf16_only=True), bf16_only=True)
             x = linear(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"], residual=x)
-        xf = layernorm(x, P["ln_f.weight"], P["ln_f.bias"], bf16_only=True)
+        return x
+
+    def logits(self, ids) -> Tensor:
+        """ids: [B, T] int32 (numpy or a device torch tensor) -> logits [B, T, V]."""
+        P = self.P
+        xf = layernorm(self.hidden(ids), P["ln_f.weight"], P["ln_f.bias"], bf16_only=True)
         return matmul_t(xf, P["wte.weight"], bf16_only=True)   # read by the fused cross-entropy
 
     def loss(self, inputs, targets):
@@ -121,6 +128,8 @@ class Gpt:
         B, Pn = prompts.shape
         tmax = Pn + steps - 1
         C = self.P["wte.weight"].shape[1]
+        if tmax > self.P["wpe.weight"].shape[0]:
+            raise ValueError(f"{tmax} positions exceed the {self.P['wpe.weight'].shape[0]} position embeddings")
         kv = KvCache(ctx, self.n_layer, B, max(tmax, 1), C)
         out = torch.empty((steps, B), dtype=torch.int32, device=f"cuda:{ctx.device}")
         u = uniforms.t().contiguous()
@@ -140,6 +149,40 @@ class Gpt:
         finally:
             ctx.set_grad_enabled(True)
             kv.close()
+        return out.t().contiguous()
+
+    def generate_uncached(self, prompts, steps: int, uniforms, k: int, temperature: float, on_step=None):
+        """[GPT2-4, "Generation with KV cache", the variant without a cache]: every new token runs
+        the whole forward over the sequence so far and samples from its last position.  Same
+        arguments and result as generate(); only the last position goes through ln_f and the
+        LM head."""
+        import torch
+        ctx = self.ctx
+        P = self.P
+        B, Pn = prompts.shape
+        C = P["wte.weight"].shape[1]
+        if Pn < 1:
+            raise ValueError("an empty prompt has no last position")
+        if Pn + steps - 1 > P["wpe.weight"].shape[0]:
+            raise ValueError(f"{Pn + steps - 1} positions exceed the {P['wpe.weight'].shape[0]} position embeddings")
+        out = torch.empty((steps, B), dtype=torch.int32, device=f"cuda:{ctx.device}")
+        u = uniforms.t().contiguous()
+        seq = prompts.contiguous()
+        ctx.set_grad_enabled(False)
+        try:
+            for i in range(steps):
+                T = seq.shape[1]
+                x = reshape(self.hidden(seq), (B, T * C))
+                last = narrow(x, (T - 1) * C, C)                              # [B, C]
+                logits = matmul_t(layernorm(last, P["ln_f.weight"], P["ln_f.bias"]), P["wte.weight"])
+                sample_topk(logits, k, temperature, u[i], out=out[i])
+                if on_step is not None:
+                    on_step(i, logits, out[i])
+                ctx.tape_reset()
+                if i + 1 < steps:
+                    seq = torch.cat([seq, out[i][:, None]], dim=1)
+        finally:
+            ctx.set_grad_enabled(True)
         return out.t().contiguous()
 
 
