@@ -43,6 +43,30 @@ def test_sampler_matches_oracle(ctx):
         ctx.tape_reset()
 
 
+def test_sampler_matches_oracle_vocab_rows(ctx):
+    """Rows of 50,257 logits (the GPT-2 vocabulary): a plain cut at k = 40 and k = 500,
+    a block of 600 ties straddling the k-th value, no cut (k = 0), a cut wider than the
+    tie block (k = 1000), and a row whose top logit dominates."""
+    import torch
+    rng = S.rng_for(77)
+    V = 50257
+    cases = [(40, 1.0), (500, 0.8), (40, 1.0), (0, 1.0), (1000, 1.5), (40, 0.05)]
+    B = len(cases)
+    logits = (rng.standard_normal((B, V)) * 2).astype(np.float32)
+    logits[2, rng.choice(V, 600, replace=False)] = 6.0      # 600 ties at the top: all survive k = 40
+    logits[5, 123] = 40.0
+    u = rng.random(B)
+    lt = ctx.tensor(logits.shape, logits)
+    for k, temp in {c for c in cases}:
+        got = T.sample_topk(lt, k, temp, torch.from_numpy(u).to("cuda:0")).cpu().numpy()
+        for b in range(B):
+            p = D.top_k_temperature_probs(logits[b].astype(np.float64), k, temp)
+            want = D.sample(p, u[b])
+            assert got[b] == want or near_boundary(p, u[b]), (k, temp, b, got[b], want)
+    lt.release()
+    ctx.tape_reset()
+
+
 def _teacher_forced(ctx, prec, B=4, Pn=16, steps=20, k=40, temp=1.0):
     import torch
     s, params, _ = S.tiny_gpt()

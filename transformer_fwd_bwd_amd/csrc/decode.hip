@@ -199,6 +199,154 @@ __global__ __launch_bounds__(NT) void sample_topk_k(const float* __restrict__ lo
   }
 }
 
+// The same draw for rows of up to SR * SPER logits, with the row held in
+// registers by one 1024-thread workgroup: logit j*SR + t lives in thread t, so
+// the row is read from memory once, coalesced.  The k-th largest key comes
+// from the same 32-step bitwise search, counted over registers.  When at most
+// SCAP logits survive the cut (the usual case: k plus its ties), their ids are
+// compacted into LDS, put in ascending order by rank (ids are distinct), and
+// one thread accumulates their weights in that order; otherwise the contiguous
+// range scan of sample_topk_k runs with SR threads.
+constexpr int SR = 1024;
+constexpr int SPER = 50;
+constexpr int SCAP = 512;
+
+__device__ __forceinline__ int block_sumi_sr(int v, int* sh) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < SR / 64; ++i) r += sh[i];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t block_maxu_sr(uint32_t v, int* sh) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = (int)v;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < SR / 64; ++i) r = max(r, (uint32_t)sh[i]);
+  return r;
+}
+
+__global__ __launch_bounds__(SR) void sample_topk_reg_k(const float* __restrict__ logits, int64_t ld, int V, int k,
+                                                        float temperature, const double* __restrict__ u,
+                                                        int32_t* __restrict__ out) {
+  __shared__ int ired[SR / 64];
+  __shared__ int ids[SCAP];
+  __shared__ int sorted[SCAP];
+  __shared__ double wts[SR];  // kept weights in id order (fast path) or per-thread range sums (wide path)
+  __shared__ int nkept;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const float* l = logits + (int64_t)b * ld;
+  // order keys; a slot past the row holds key 0, below the key of every float but
+  // a negative NaN, and the cut below is always at least 1, so it never counts
+  uint32_t key[SPER];
+#pragma unroll
+  for (int j = 0; j < SPER; ++j) {
+    const int id = j * SR + t;
+    key[j] = id < V ? order_key(l[id]) : 0u;
+  }
+  uint32_t thr = 1;  // without a cut every logit survives
+  if (k > 0 && k < V) {
+    thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < SPER; ++j) cnt += key[j] >= cand;
+      if (block_sumi_sr(cnt, ired) >= k) thr = cand;
+    }
+  }
+  uint32_t kmax = 0;
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < SPER; ++j) {
+    kmax = max(kmax, key[j]);
+    mine += key[j] >= thr;
+  }
+  kmax = block_maxu_sr(kmax, ired);
+  const float mx = __uint_as_float((kmax & 0x80000000u) ? (kmax ^ 0x80000000u) : ~kmax);
+  const int n = block_sumi_sr(mine, ired);
+  const double T = (double)temperature;
+  if (n <= SCAP) {
+    if (t == 0) nkept = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SPER; ++j)
+      if (key[j] >= thr) ids[atomicAdd(&nkept, 1)] = j * SR + t;
+    __syncthreads();
+    if (t < n) {
+      const int me = ids[t];
+      int rank = 0;
+      for (int i = 0; i < n; ++i) rank += ids[i] < me;
+      sorted[rank] = me;
+    }
+    __syncthreads();
+    if (t < n) wts[t] = exp(((double)l[sorted[t]] - (double)mx) / T);
+    __syncthreads();
+    if (t == 0) {
+      double total = 0.0;
+      for (int i = 0; i < n; ++i) total += wts[i];
+      const double target = u[b] * total;
+      double c = 0.0;
+      int pick = -1, last = sorted[0];
+      for (int i = 0; i < n; ++i) {
+        if (wts[i] > 0.0) last = sorted[i];
+        c += wts[i];
+        if (c > target) {
+          pick = sorted[i];
+          break;
+        }
+      }
+      out[b] = pick >= 0 ? pick : last;  // rounding left target at or above the total
+    }
+    return;
+  }
+  // many survivors (ties across the cut, or a large k): contiguous id ranges
+  const int chunk = (V + SR - 1) / SR;
+  const int j0 = min(V, t * chunk), j1 = min(V, j0 + chunk);
+  double local = 0.0;
+  for (int j = j0; j < j1; ++j)
+    if (order_key(l[j]) >= thr) local += exp(((double)l[j] - (double)mx) / T);
+  wts[t] = local;
+  __syncthreads();
+  if (t == 0)
+    for (int i = 1; i < SR; ++i) wts[i] += wts[i - 1];
+  __syncthreads();
+  const double total = wts[SR - 1];
+  const double target = u[b] * total;
+  const double before = t ? wts[t - 1] : 0.0;
+  if (before <= target && target < wts[t]) {
+    double c = before;
+    int pick = -1, last = -1;
+    for (int j = j0; j < j1; ++j) {
+      if (order_key(l[j]) < thr) continue;
+      const double w = exp(((double)l[j] - (double)mx) / T);
+      if (w > 0.0) last = j;
+      c += w;
+      if (c > target) {
+        pick = j;
+        break;
+      }
+    }
+    out[b] = pick >= 0 ? pick : (last >= 0 ? last : j1 - 1);
+  }
+  if (t == 0 && target >= total) {
+    int last = V - 1;
+    for (int j = V - 1; j >= 0; --j)
+      if (order_key(l[j]) >= thr) {
+        last = j;
+        break;
+      }
+    out[b] = last;
+  }
+}
+
 }  // namespace
 
 hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, int B, int Tmax, int pos0,
@@ -220,7 +368,10 @@ hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, in
 hipError_t sample_topk(const float* logits, int64_t ld, int B, int V, int k, float temperature, const double* u,
                        int32_t* out, hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(sample_topk_k, dim3(B), dim3(NT), 0, s, logits, ld, V, k, temperature, u, out);
+  if (V <= SR * SPER)
+    hipLaunchKernelGGL(sample_topk_reg_k, dim3(B), dim3(SR), 0, s, logits, ld, V, k, temperature, u, out);
+  else
+    hipLaunchKernelGGL(sample_topk_k, dim3(B), dim3(NT), 0, s, logits, ld, V, k, temperature, u, out);
   return hipGetLastError();
 }
 

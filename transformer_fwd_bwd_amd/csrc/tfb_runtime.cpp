@@ -2040,6 +2040,7 @@ int tfb_sample_topk(tfb_ctx* ctx, tfb_tensor logits, int k, float temperature, c
     need(dev_uniforms != nullptr && dev_out != nullptr, TFB_ERR_ARG, "null argument");
     need(temperature > 0.f, TFB_ERR_ARG, "temperature must be positive");
     need(k >= 0, TFB_ERR_ARG, "k must be >= 0");
+    need(L.cols() > 0, TFB_ERR_SHAPE, "logits rows are empty");
     need(L.cols() < (1LL << 31) && L.rows() < 65536, TFB_ERR_SHAPE, "logits too large");
     hip_check(sample_topk(C.f32(L), L.stride(), (int)L.rows(), (int)L.cols(), k, temperature, dev_uniforms, dev_out,
                           C.s()),
