@@ -67,6 +67,47 @@ def test_sampler_matches_oracle_vocab_rows(ctx):
     ctx.tape_reset()
 
 
+@pytest.mark.parametrize("hs,H", [(32, 4), (64, 3), (128, 2), (48, 2)])
+def test_kv_attend_across_position_blocks(ctx, hs, H):
+    """[GPT2-4, "Generation with KV cache"]: one cached attention step of layer 1
+    against the oracle's per-head softmax over every stored key, at positions on
+    both sides of the 128-position blocks the step is split into, and at the last
+    position of the cache.  Head size 48 takes the unsplit kernel."""
+    from oracle import ops as O
+    rng = S.rng_for(78 + hs)
+    B, C, Tmax = 3, hs * H, 300
+    kv = T.KvCache(ctx, 2, B, Tmax, C)
+    K = np.zeros((B, Tmax, C)); Vv = np.zeros((B, Tmax, C))
+
+    def store(p0, n):
+        q = rng.standard_normal((B, n, 3 * C)).astype(np.float32)
+        t = ctx.tensor(q.shape, q)
+        kv.store(1, t, p0)
+        K[:, p0:p0 + n] = q[:, :, C:2 * C]
+        Vv[:, p0:p0 + n] = q[:, :, 2 * C:]
+        t.release()
+
+    store(0, 126)
+    for pos in (126, 127, 128, 129, 255, 256, 299):
+        if pos > 130 and not K[:, pos - 1].any():
+            store(130, pos - 130)
+        q = rng.standard_normal((B, 1, 3 * C)).astype(np.float32)
+        t = ctx.tensor(q.shape, q)
+        y = kv.attend(1, t, pos, H).numpy().reshape(B, C)
+        K[:, pos] = q[:, 0, C:2 * C]
+        Vv[:, pos] = q[:, 0, 2 * C:]
+        ref = np.zeros((B, C))
+        for b in range(B):
+            for h in range(H):
+                sl = slice(h * hs, (h + 1) * hs)
+                p = O.softmax_row(K[b, :pos + 1, sl] @ q[b, 0, sl].astype(np.float64) / np.sqrt(hs))
+                ref[b, sl] = p @ Vv[b, :pos + 1, sl]
+        assert_close(y, ref, FWD_TOL["fp32"], f"pos {pos}")
+        t.release()
+        ctx.tape_reset()
+    kv.close()
+
+
 def _teacher_forced(ctx, prec, B=4, Pn=16, steps=20, k=40, temp=1.0):
     import torch
     s, params, _ = S.tiny_gpt()

@@ -135,6 +135,120 @@ __global__ __launch_bounds__(NT) void kv_attend_k(const float* __restrict__ qkv,
   }
 }
 
+// Split form of kv_attend for head sizes 32, 64 and 128 (rows of float4).  One
+// workgroup per (sequence, head, block of KVP positions): each wave takes KVP/4
+// positions, a group of HS/4 lanes reads one cached key row (coalesced float4s)
+// and reduces its dot product across the group, then the wave keeps its own
+// maximum m, weight sum l and sum_j e^(s_j - m) v_j; the four waves merge in
+// LDS and the block writes (m, l, acc).  kv_attend_merge_k rescales the blocks
+// to their common maximum and divides.  The block that holds position pos
+// first appends the new key and value.
+constexpr int KVP = 128;
+typedef float kf4 __attribute__((ext_vector_type(4)));
+
+template <int HS>
+__global__ __launch_bounds__(256) void kv_attend_part_k(const float* __restrict__ qkv, float* __restrict__ kv,
+                                                        float* __restrict__ pacc, float* __restrict__ pml, int layer,
+                                                        int B, int Tmax, int C, int H, int pos, int S, float scale) {
+  constexpr int LPR = HS / 4, RPI = 64 / LPR, PW = KVP / 4, IT = PW / RPI;
+  __shared__ float wm[4], wl[4];
+  __shared__ kf4 wacc[4][LPR];
+  const int s = blockIdx.x % S, bh = blockIdx.x / S;
+  const int b = bh / H, hd = bh % H;
+  const float* src = qkv + (int64_t)b * 3 * C;
+  float* Kc = kv + ((int64_t)(layer * 2 + 0) * B + b) * Tmax * C + hd * HS;
+  float* Vc = kv + ((int64_t)(layer * 2 + 1) * B + b) * Tmax * C + hd * HS;
+  const int j_lo = s * KVP, j_hi = min(j_lo + KVP, pos + 1);
+  if (pos < j_lo + KVP) {  // the last block: append the new token's key and value (uniform per block)
+    for (int d = threadIdx.x; d < HS; d += 256) {
+      Kc[(int64_t)pos * C + d] = src[C + hd * HS + d];
+      Vc[(int64_t)pos * C + d] = src[2 * C + hd * HS + d];
+    }
+    __syncthreads();
+  }
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / LPR, c = lane % LPR;
+  const kf4 q = *reinterpret_cast<const kf4*>(src + hd * HS + c * 4);
+  const int jw = j_lo + w * PW;
+  float sc[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int j = jw + it * RPI + r;
+    float d = 0.f;
+    if (j < j_hi) {
+      const kf4 kr = *reinterpret_cast<const kf4*>(Kc + (int64_t)j * C + c * 4);
+      d = q.x * kr.x + q.y * kr.y + q.z * kr.z + q.w * kr.w;
+    }
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+    sc[it] = j < j_hi ? d * scale : -INFINITY;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) m = fmaxf(m, sc[it]);
+#pragma unroll
+  for (int o = 32; o >= LPR; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float l = 0.f;
+  kf4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (m != -INFINITY) {  // the wave holds at least one position
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int j = jw + it * RPI + r;
+      if (j < j_hi) {
+        const float p = expf(sc[it] - m);
+        const kf4 v = *reinterpret_cast<const kf4*>(Vc + (int64_t)j * C + c * 4);
+        acc += p * v;
+        l += p;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= LPR; o >>= 1) {
+    l += __shfl_xor(l, o, 64);
+    acc.x += __shfl_xor(acc.x, o, 64);
+    acc.y += __shfl_xor(acc.y, o, 64);
+    acc.z += __shfl_xor(acc.z, o, 64);
+    acc.w += __shfl_xor(acc.w, o, 64);
+  }
+  if (lane == 0) wm[w] = m, wl[w] = l;
+  if (r == 0) wacc[w][c] = acc;
+  __syncthreads();
+  if (w == 0 && lane < LPR) {
+    float M = wm[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) M = fmaxf(M, wm[i]);
+    float L = 0.f;
+    kf4 A = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (wm[i] != -INFINITY) {
+        const float f = expf(wm[i] - M);
+        L += f * wl[i];
+        A += f * wacc[i][lane];
+      }
+    const int64_t blk = (int64_t)bh * S + s;
+    *reinterpret_cast<kf4*>(pacc + blk * HS + lane * 4) = A;
+    if (lane == 0) pml[blk * 2] = M, pml[blk * 2 + 1] = L;
+  }
+}
+
+// one thread per output element (b, head, d); y [B, 1, C]
+__global__ __launch_bounds__(256) void kv_attend_merge_k(const float* __restrict__ pacc, const float* __restrict__ pml,
+                                                         float* __restrict__ y, int BH, int HS, int S) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= BH * HS) return;
+  const int bh = i / HS, d = i % HS;
+  const float* ml = pml + (int64_t)bh * S * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f, A = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float f = expf(ml[2 * s] - M);
+    L += f * ml[2 * s + 1];
+    A += f * pacc[((int64_t)bh * S + s) * HS + d];
+  }
+  y[i] = A / L;  // y [B, C] with C = H * HS: element (b, head, d) sits at bh * HS + d
+}
+
 // one workgroup per sequence; logits rows [B, V] at stride ld; u [B] (double); out [B] ids
 __global__ __launch_bounds__(NT) void sample_topk_k(const float* __restrict__ logits, int64_t ld, int V, int k,
                                                     float temperature, const double* __restrict__ u,
@@ -358,10 +472,39 @@ hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, in
   return hipGetLastError();
 }
 
+static bool kv_split_ok(int C, int H) {
+  const int hs = C / H;
+  return C % 4 == 0 && (hs == 32 || hs == 64 || hs == 128);
+}
+
+size_t kv_attend_workspace_bytes(int B, int C, int H, int pos) {
+  if (!kv_split_ok(C, H)) return 0;
+  const int64_t S = (pos + KVP) / KVP;
+  return (size_t)(B * S * ((int64_t)C + 2 * H)) * sizeof(float);
+}
+
 hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, int Tmax, int C, int H, int pos,
-                     float scale, hipStream_t s) {
-  const size_t shmem = ((size_t)Tmax + 4 * 64) * sizeof(float);
-  hipLaunchKernelGGL(kv_attend_k, dim3(B * H), dim3(NT), shmem, s, qkv, kv, y, layer, B, Tmax, C, H, pos, scale);
+                     float scale, void* ws, hipStream_t s) {
+  if (!kv_split_ok(C, H) || ws == nullptr) {
+    const size_t shmem = ((size_t)Tmax + 4 * 64) * sizeof(float);
+    hipLaunchKernelGGL(kv_attend_k, dim3(B * H), dim3(NT), shmem, s, qkv, kv, y, layer, B, Tmax, C, H, pos, scale);
+    return hipGetLastError();
+  }
+  const int hs = C / H, S = (pos + KVP) / KVP;  // blocks covering positions 0..pos
+  float* pacc = static_cast<float*>(ws);
+  float* pml = pacc + (int64_t)B * H * S * hs;
+  const dim3 grid((unsigned)(B * H * S));
+  if (hs == 32)
+    hipLaunchKernelGGL(kv_attend_part_k<32>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos, S,
+                       scale);
+  else if (hs == 64)
+    hipLaunchKernelGGL(kv_attend_part_k<64>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos, S,
+                       scale);
+  else
+    hipLaunchKernelGGL(kv_attend_part_k<128>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos,
+                       S, scale);
+  const int n = B * H * hs;
+  hipLaunchKernelGGL(kv_attend_merge_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pacc, pml, y, B * H, hs, S);
   return hipGetLastError();
 }
 

@@ -195,8 +195,10 @@ hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float*
 // ---- KV-cached inference (decode.hip); cache fp32 [L][2][B][Tmax][C]
 hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, int B, int Tmax, int pos0,
                     hipStream_t s);
+// ws: kv_attend_workspace_bytes(B, C, H, pos) bytes of scratch (partial results per block of positions)
+size_t kv_attend_workspace_bytes(int B, int C, int H, int pos);
 hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, int Tmax, int C, int H, int pos,
-                     float scale, hipStream_t s);
+                     float scale, void* ws, hipStream_t s);
 hipError_t sample_topk(const float* logits, int64_t ld, int B, int V, int k, float temperature, const double* u,
                        int32_t* out, hipStream_t s);
 

@@ -2026,8 +2026,10 @@ int tfb_kv_attend(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos, 
     const float scale = 1.f / std::sqrt((float)(Cc / heads));
     const float* qd = Q.data;
     int h = C.make_output({kv->batch, 1, Cc});
-    hip_check(kv_attend(qd, kv->data, ctx->tensors[h].data, layer, kv->batch, kv->tmax, Cc, heads, pos, scale, C.s()),
-              "kv_attend");
+    void* ws = C.scratch(std::max<size_t>(kv_attend_workspace_bytes(kv->batch, Cc, heads, pos), 256));
+    hip_check(
+        kv_attend(qd, kv->data, ctx->tensors[h].data, layer, kv->batch, kv->tmax, Cc, heads, pos, scale, ws, C.s()),
+        "kv_attend");
     *y = h;  // inference only: not recorded on the tape
   });
 }
