@@ -773,14 +773,19 @@ Plan make_plan(const GemmArgs& g) {
   // traffic (written and read once more by the reduction, priced at 2.5 TB/s:
   // it competes with the product's own traffic; 5 TB/s chose splits 7% slower
   // on the GPT-2 dW products), with at least 512 k per item.
+  // Products of at most 64 rows (cached decoding: one token per sequence) have
+  // a few tiles whose k loop is pure latency: there the split goes down to two
+  // k-tiles per item.
   p.splits = 1;
-  if (g.causal_a == CAUSAL_NONE && !g.causal_out && g.K >= 1024) {
+  const bool skinny = g.M <= 64 && g.batch == 1;
+  if (g.causal_a == CAUSAL_NONE && !g.causal_out && (g.K >= 1024 || (skinny && g.K >= 256))) {
     const int64_t slots = 256 * (p.cfg == CFG_128x192 ? 1 : p.bk == 32 ? 3 : 2);
     const double tile_s_per_k = 2.0 * p.BM * p.BN / 1.0e12;  // ~1 TFLOP/s per resident workgroup
     const double out_bytes = 4.0 * g.M * g.N * g.batch;
+    const int min_k = skinny ? 128 : 512;
     double best = 0.0;
-    for (int sp = 1; sp <= 16; ++sp) {
-      if (sp > 1 && g.K / sp < 512) break;
+    for (int sp = 1; sp <= (skinny ? 32 : 16); ++sp) {
+      if (sp > 1 && g.K / sp < min_k) break;
       const int64_t items = tiles * sp;
       const double rounds = (double)((items + slots - 1) / slots);
       const double t = rounds * ((double)g.K / sp) * tile_s_per_k + (sp > 1 ? (sp + 1) * out_bytes / 2.5e12 : 0.0);
