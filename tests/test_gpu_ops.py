@@ -86,6 +86,22 @@ def test_linear_residual_long_k_split(ctx, N):
                                   rnd(121, (200, N))], (200, N))
 
 
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("M,K,N", [(1, 3, 4), (5, 130, 132), (16, 768, 2304), (7, 3100, 68), (16, 256, 1028),
+                                   (17, 300, 132)])
+def test_linear_few_rows(ctx, prec, M, K, N):
+    """Products of at most 16 rows (one token per sequence) take the small-row kernel:
+    one k chunk, several chunks summed by the strip's last workgroup, ragged column
+    strips; 17 rows take the tiled kernel.  r + (x @ w + b) and every gradient."""
+    def gpu(x, w, b, r):
+        return T.linear(x, w, b, residual=r)
+
+    def ora(x, w, b, r):
+        return E.add(r, E.add(E.matmul(x, w), b))
+    check(ctx, prec, gpu, ora, [rnd(130 + M, (M, K)), rnd(131 + K, (K, N), 1 / np.sqrt(K)), rnd(132, (N,)),
+                                rnd(133, (M, N))], (M, N))
+
+
 @pytest.mark.parametrize("case", ["fwd_nn", "bwd_nt"])
 def test_linear_one_tile_per_cu(ctx, case):
     """About one 128x192 output tile per CU (768 columns against ~8100 rows, long

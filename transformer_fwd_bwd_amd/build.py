@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtfb.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "rowops.hip", "embedding.hip", "optim.hip",
+SOURCES = ["gemm.hip", "gemv.hip", "attention.hip", "elementwise.hip", "rowops.hip", "embedding.hip", "optim.hip",
            "decode.hip", "tfb_runtime.cpp"]
 
 ARCH = "gfx950"

@@ -832,16 +832,37 @@ hipError_t launch_prec(const KArgs& ka, int bk, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
+// C = sum of the partials ws[split][M][N] (per batch) + beta C + bias (+ resid), the bf16 copy
+static hipError_t reduce_splits(const GemmArgs& g, const float* ws, int splits, hipStream_t s) {
+  const int64_t MN = (int64_t)g.M * g.N;
+  const bool vec = g.N % 4 == 0 && g.ldc % 4 == 0 && g.sc1 % 4 == 0 && g.sc2 % 4 == 0 &&
+                   (reinterpret_cast<uintptr_t>(g.C) & 15) == 0 && (reinterpret_cast<uintptr_t>(g.bias) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(g.Cbf) & 7) == 0 && (reinterpret_cast<uintptr_t>(g.resid) & 15) == 0;
+  if (vec) {
+    dim3 rgrid((unsigned)std::min<int64_t>((MN / 4 + 255) / 256, 4096), g.batch);
+    hipLaunchKernelGGL(splitk_reduce4, rgrid, dim3(256), 0, s, reinterpret_cast<const f4*>(ws), splits, g.M,
+                       g.N / 4, g.C, g.ldc, g.batch_div, g.sc1, g.sc2, g.beta, reinterpret_cast<const f4*>(g.bias),
+                       g.Cbf, g.resid, (int)g.c_bf16_only);
+  } else {
+    dim3 rgrid((unsigned)std::min<int64_t>((MN + 255) / 256, 4096), g.batch);
+    hipLaunchKernelGGL(splitk_reduce, rgrid, dim3(256), 0, s, ws, splits, g.M, g.N, g.C, g.ldc, g.batch_div,
+                       g.sc1, g.sc2, g.beta, g.bias, g.Cbf, g.resid, (int)g.c_bf16_only);
+  }
+  return hipGetLastError();
+}
+
 size_t gemm_workspace_bytes(const GemmArgs& g) {
   Plan p = make_plan(g);
-  if (p.splits <= 1) return 0;
-  return (size_t)p.splits * g.batch * g.M * g.N * sizeof(float);
+  const size_t tiled = p.splits <= 1 ? 0 : (size_t)p.splits * g.batch * g.M * g.N * sizeof(float);
+  return std::max(tiled, gemv_workspace_bytes(g));
 }
 
 hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   if (g.resid && g.batch != 1) return hipErrorInvalidValue;
   if (g.c_bf16_only && (!g.Cbf || g.beta != 0.f)) return hipErrorInvalidValue;
+  hipError_t ge;
+  if (gemv(g, workspace, ws_bytes, s, &ge)) return ge;
   // K == 0 needs no special case: the k loop is empty and the epilogue writes beta*C + bias
   Plan p = make_plan(g);
   if (p.splits > 1 && (size_t)p.splits * g.batch * g.M * g.N * sizeof(float) > ws_bytes) p.splits = 1;
@@ -871,21 +892,7 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   else
     e = launch_prec<4, 1, 1, 2>(ka, p.bk, grid, s);
   if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t MN = (int64_t)g.M * g.N;
-  const bool vec = g.N % 4 == 0 && g.ldc % 4 == 0 && g.sc1 % 4 == 0 && g.sc2 % 4 == 0 &&
-                   (reinterpret_cast<uintptr_t>(g.C) & 15) == 0 && (reinterpret_cast<uintptr_t>(g.bias) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(g.Cbf) & 7) == 0 && (reinterpret_cast<uintptr_t>(g.resid) & 15) == 0;
-  if (vec) {
-    dim3 rgrid((unsigned)std::min<int64_t>((MN / 4 + 255) / 256, 4096), g.batch);
-    hipLaunchKernelGGL(splitk_reduce4, rgrid, dim3(256), 0, s, reinterpret_cast<const f4*>(ka.ws), p.splits, g.M,
-                       g.N / 4, g.C, g.ldc, g.batch_div, g.sc1, g.sc2, g.beta, reinterpret_cast<const f4*>(g.bias),
-                       g.Cbf, g.resid, (int)g.c_bf16_only);
-  } else {
-    dim3 rgrid((unsigned)std::min<int64_t>((MN + 255) / 256, 4096), g.batch);
-    hipLaunchKernelGGL(splitk_reduce, rgrid, dim3(256), 0, s, ka.ws, p.splits, g.M, g.N, g.C, g.ldc, g.batch_div,
-                       g.sc1, g.sc2, g.beta, g.bias, g.Cbf, g.resid, (int)g.c_bf16_only);
-  }
-  return hipGetLastError();
+  return reduce_splits(g, ka.ws, p.splits, s);
 }
 
 }  // namespace tfb

@@ -1,0 +1,262 @@
+// Products with at most 16 rows: C = alpha A B + bias + beta C + resid with A
+// [M, K] row-major and B [K, N] row-major (the Linear of one token per sequence
+// in cached decoding; [Autograd-1, "Why fast MatMul"] defines the product).
+//
+// Such a product reads its weight once and does 16 multiply-adds per weight,
+// so it is bound by how many bytes are in flight, not by arithmetic.  The
+// columns go in strips of 64 and k in chunks of kc <= 128 rows, one 256-thread
+// workgroup per (strip, chunk), which puts a few hundred workgroups on the
+// 256 CUs.  In a workgroup, lane 4c + r of wave w multiplies columns 4c..4c+3
+// of k rows 4w + r + 16i by the 16 rows of A (staged in LDS, k-major, as
+// fp32); the four lanes of a quad sum through DPP, the four waves through LDS.
+// With one chunk the workgroup applies the epilogue; otherwise it writes its
+// partial to ws[chunk][M][N] and gemv_reduce_k sums the chunks in order and
+// applies the epilogue.  (Letting the last
+// workgroup of a strip do that sum needs device-scope fences, which write back
+// and invalidate the L2 of the workgroup's XCD: far slower here.)
+#include <algorithm>
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace tfb {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int SM = 16;    // rows of A held
+constexpr int SNS = 64;   // columns per strip
+constexpr int SKC = 128;  // largest k chunk
+constexpr int ST = 256;
+
+__device__ __forceinline__ float bf16_val(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
+__device__ __forceinline__ unsigned short bf16_of(float x) { return __builtin_bit_cast(unsigned short, (__bf16)x); }
+__device__ __forceinline__ float round_bf16(float x) { return bf16_val(bf16_of(x)); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// sum over the four lanes of a quad (quad_perm [1,0,3,2], then [2,3,0,1])
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<0xb1>(v);
+  return v + dpp<0x4e>(v);
+}
+
+struct SkArgs {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  float* C;
+  int64_t ldc;
+  uint16_t* Cbf;
+  const float* bias;
+  const float* resid;
+  float alpha, beta;
+  int M, N, K, kc, chunks, skipc;
+  float* ws;  // [chunks][M][N] partials
+};
+
+template <bool A_BF, bool B_BF, bool RND>
+__global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
+  __shared__ f4 sA[SKC][SM / 4];  // sA[k][q] = A rows 4q..4q+3 at k
+  __shared__ f4 red[4][SM * SNS / 4];
+  const int strips = (a.N + SNS - 1) / SNS;
+  const int strip = blockIdx.x % strips, chunk = blockIdx.x / strips;
+  const int n0 = strip * SNS, k0 = chunk * a.kc;
+  const int kn = min(a.kc, a.K - k0);
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, r = lane & 3, c = lane >> 2;
+
+  // every load is issued before any value is used: indexes out of range are
+  // clamped to a valid element and the value is zeroed afterwards (a load under a
+  // branch would be waited for on its own)
+  using braw_t = typename std::conditional<B_BF, u16x4, f4>::type;
+  using araw_t = typename std::conditional<A_BF, unsigned short, float>::type;
+  using belem_t = typename std::conditional<B_BF, unsigned short, float>::type;
+  const belem_t* Bp = static_cast<const belem_t*>(a.B);
+  const int n = n0 + 4 * c;
+  const bool ncol = n < a.N;
+  braw_t braw[SKC / 16];
+#pragma unroll
+  for (int i = 0; i < SKC / 16; ++i) {
+    const int kk = 4 * w + r + 16 * i;
+    const int64_t off = (int64_t)(k0 + (kk < kn ? kk : 0)) * a.ldb + (ncol ? n : 0);
+    braw[i] = *reinterpret_cast<const braw_t*>(Bp + off);
+  }
+  // A[0..M) x [k0, k0 + kn): element i of this thread's share is (i / SKC, i % SKC)
+  araw_t araw[SM * SKC / ST];
+#pragma unroll
+  for (int j = 0; j < SM * SKC / ST; ++j) {
+    const int i = t + j * ST, m = i / SKC, kk = i % SKC;
+    araw[j] = static_cast<const araw_t*>(a.A)[(int64_t)(m < a.M ? m : 0) * a.lda + k0 + (kk < kn ? kk : 0)];
+  }
+  f4 b[SKC / 16];
+#pragma unroll
+  for (int i = 0; i < SKC / 16; ++i) {
+    const int kk = 4 * w + r + 16 * i;
+    f4 v;
+    if constexpr (B_BF) {
+      v = f4{bf16_val(braw[i].x), bf16_val(braw[i].y), bf16_val(braw[i].z), bf16_val(braw[i].w)};
+    } else {
+      v = braw[i];
+      if constexpr (RND) v = f4{round_bf16(v.x), round_bf16(v.y), round_bf16(v.z), round_bf16(v.w)};
+    }
+    b[i] = ncol && kk < kn ? v : f4{0.f, 0.f, 0.f, 0.f};
+  }
+  // staged as fp32, k-major; rows past M and k past the chunk are zero
+#pragma unroll
+  for (int j = 0; j < SM * SKC / ST; ++j) {
+    const int i = t + j * ST, m = i / SKC, kk = i % SKC;
+    float v;
+    if constexpr (A_BF) {
+      v = bf16_val(araw[j]);
+    } else {
+      v = araw[j];
+      if constexpr (RND) v = round_bf16(v);
+    }
+    reinterpret_cast<float*>(sA)[kk * SM + m] = m < a.M && kk < kn ? v : 0.f;
+  }
+  __syncthreads();
+
+  f4 acc[SM];
+#pragma unroll
+  for (int m = 0; m < SM; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < SKC / 16; ++i) {
+    const int kk = 4 * w + r + 16 * i;
+    if (kk < kn) {
+#pragma unroll
+      for (int q = 0; q < SM / 4; ++q) {
+        const f4 av = sA[kk][q];
+        acc[4 * q + 0] += av.x * b[i];
+        acc[4 * q + 1] += av.y * b[i];
+        acc[4 * q + 2] += av.z * b[i];
+        acc[4 * q + 3] += av.w * b[i];
+      }
+    }
+  }
+  // quad sum over r; lane r of the quad keeps rows 4r..4r+3
+#pragma unroll
+  for (int m = 0; m < SM; ++m) {
+    acc[m].x = quad_sum(acc[m].x);
+    acc[m].y = quad_sum(acc[m].y);
+    acc[m].z = quad_sum(acc[m].z);
+    acc[m].w = quad_sum(acc[m].w);
+  }
+  // red[w][m * 16 + c] = rows m, columns 4c..4c+3
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // selects, not an indexed register array (that would live in scratch)
+    const f4 x = r == 0 ? acc[j] : r == 1 ? acc[4 + j] : r == 2 ? acc[8 + j] : acc[12 + j];
+    red[w][(4 * r + j) * (SNS / 4) + c] = x;
+  }
+  __syncthreads();
+  // thread t owns output f4 t: row t / 16, columns n0 + 4 (t % 16)
+  f4 v = red[0][t] + red[1][t] + red[2][t] + red[3][t];
+  const int m = t / (SNS / 4), nn = n0 + 4 * (t % (SNS / 4));
+  if (m >= a.M || nn >= a.N) return;
+  v *= a.alpha;
+  if (a.chunks > 1) {  // the reduction adds bias, beta C and resid
+    *reinterpret_cast<f4*>(a.ws + ((int64_t)chunk * a.M + m) * a.N + nn) = v;
+    return;
+  }
+  if (a.bias) v += *reinterpret_cast<const f4*>(a.bias + nn);
+  float* dst = a.C + (int64_t)m * a.ldc + nn;
+  if (a.beta != 0.f) v += a.beta * *reinterpret_cast<const f4*>(dst);
+  if (a.resid) v += *reinterpret_cast<const f4*>(a.resid + (int64_t)m * a.ldc + nn);
+  if (!a.skipc) *reinterpret_cast<f4*>(dst) = v;
+  if (a.Cbf)
+    *reinterpret_cast<u16x4*>(a.Cbf + (int64_t)m * a.ldc + nn) = u16x4{bf16_of(v.x), bf16_of(v.y), bf16_of(v.z), bf16_of(v.w)};
+}
+
+// C = sum over chunks (in chunk order) of ws[chunk][M][N] + bias + beta C + resid, one
+// thread per 4 outputs; the partials are loaded eight chunks at a time before they
+// are added, so a thread has eight loads in flight
+__global__ __launch_bounds__(ST) void gemv_reduce_k(SkArgs a) {
+  const int N4 = a.N / 4;
+  const int e = blockIdx.x * ST + threadIdx.x;
+  if (e >= a.M * N4) return;
+  const int m = e / N4, nn = 4 * (e % N4);
+  const f4* p = reinterpret_cast<const f4*>(a.ws) + e;
+  const int64_t stride = (int64_t)a.M * N4;
+  f4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < a.chunks; c0 += 8) {
+    f4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = p[(int64_t)min(c0 + j, a.chunks - 1) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < a.chunks) v += x[j];
+  }
+  if (a.bias) v += *reinterpret_cast<const f4*>(a.bias + nn);
+  float* dst = a.C + (int64_t)m * a.ldc + nn;
+  if (a.beta != 0.f) v += a.beta * *reinterpret_cast<const f4*>(dst);
+  if (a.resid) v += *reinterpret_cast<const f4*>(a.resid + (int64_t)m * a.ldc + nn);
+  if (!a.skipc) *reinterpret_cast<f4*>(dst) = v;
+  if (a.Cbf)
+    *reinterpret_cast<u16x4*>(a.Cbf + (int64_t)m * a.ldc + nn) = u16x4{bf16_of(v.x), bf16_of(v.y), bf16_of(v.z), bf16_of(v.w)};
+}
+
+struct SkPlan {
+  bool ok = false;
+  int kc = SKC, chunks = 1, strips = 0;
+};
+
+SkPlan plan(const GemmArgs& g) {
+  SkPlan p;
+  const auto al = [](const void* q, int bytes) { return (reinterpret_cast<uintptr_t>(q) & (bytes - 1)) == 0; };
+  if (g.M < 1 || g.M > SM || g.batch != 1 || g.K < 1 || g.N < 1) return p;
+  if (g.causal_a != CAUSAL_NONE || g.causal_out || g.a_mcontig || g.b_kcontig) return p;
+  if (g.N % 4 || g.ldb % 4 || g.ldc % 4 || !al(g.B, g.b_bf16 ? 8 : 16) || !al(g.C, 16) || !al(g.bias, 16) ||
+      !al(g.resid, 16) || !al(g.Cbf, 8))
+    return p;
+  p.strips = (g.N + SNS - 1) / SNS;
+  // a few hundred workgroups: 64-row chunks when 128-row ones leave under ~200
+  p.kc = (int64_t)p.strips * ((g.K + SKC - 1) / SKC) < 192 ? SKC / 2 : SKC;
+  p.chunks = (g.K + p.kc - 1) / p.kc;
+  p.ok = true;
+  return p;
+}
+
+template <bool A_BF, bool B_BF, bool RND>
+void launch(const SkArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemv_k<A_BF, B_BF, RND>), dim3(grid), dim3(ST), 0, s, a);
+}
+
+}  // namespace
+
+size_t gemv_workspace_bytes(const GemmArgs& g) {
+  const SkPlan p = plan(g);
+  if (!p.ok || p.chunks == 1) return 0;
+  return (size_t)p.chunks * g.M * g.N * sizeof(float);
+}
+
+bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_t* err) {
+  const SkPlan p = plan(g);
+  if (!p.ok) return false;
+  if (p.chunks > 1 && (!ws || ws_bytes < gemv_workspace_bytes(g))) return false;
+  SkArgs a;
+  a.A = g.A, a.lda = g.lda, a.B = g.B, a.ldb = g.ldb, a.C = g.C, a.ldc = g.ldc, a.Cbf = g.Cbf;
+  a.bias = g.bias, a.resid = g.resid, a.alpha = g.alpha, a.beta = g.beta;
+  a.M = g.M, a.N = g.N, a.K = g.K, a.kc = p.kc, a.chunks = p.chunks, a.skipc = g.c_bf16_only ? 1 : 0;
+  a.ws = static_cast<float*>(ws);
+  const int grid = p.strips * p.chunks;
+  const bool rnd = g.prec == PREC_BF16;
+  if (g.a_bf16 && g.b_bf16)
+    launch<true, true, false>(a, grid, s);
+  else if (g.a_bf16)
+    rnd ? launch<true, false, true>(a, grid, s) : launch<true, false, false>(a, grid, s);
+  else if (g.b_bf16)
+    rnd ? launch<false, true, true>(a, grid, s) : launch<false, true, false>(a, grid, s);
+  else
+    rnd ? launch<false, false, true>(a, grid, s) : launch<false, false, false>(a, grid, s);
+  if (p.chunks > 1) {
+    const int n4 = g.M * (g.N / 4);
+    hipLaunchKernelGGL(gemv_reduce_k, dim3((n4 + ST - 1) / ST), dim3(ST), 0, s, a);
+  }
+  *err = hipGetLastError();
+  return true;
+}
+
+}  // namespace tfb

@@ -54,6 +54,11 @@ struct GemmArgs {
 size_t gemm_workspace_bytes(const GemmArgs& g);
 hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t s);
 
+// Products of at most 16 rows, A [M, K] and B [K, N] row-major (gemv.hip), taken
+// by gemm() when the layout fits; returns false (launching nothing) otherwise
+size_t gemv_workspace_bytes(const GemmArgs& g);
+bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_t* err);
+
 // ---- elementwise (elementwise.hip); beta in {0, 1}: overwrite or accumulate
 hipError_t fill(float* p, float v, int64_t n, hipStream_t s);
 // dst[i] = bf16(src[i]), round to nearest even
