@@ -169,15 +169,21 @@ __global__ __launch_bounds__(256) void kv_attend_part_k(const float* __restrict_
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / LPR, c = lane % LPR;
   const kf4 q = *reinterpret_cast<const kf4*>(src + hd * HS + c * 4);
   const int jw = j_lo + w * PW;
+  // every key and value row of this wave is requested before the first is used;
+  // rows past the block read row j_lo (in range) and are masked below
+  kf4 kr[IT], vr[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int j = jw + it * RPI + r;
+    const int64_t row = (int64_t)(j < j_hi ? j : j_lo) * C + c * 4;
+    kr[it] = *reinterpret_cast<const kf4*>(Kc + row);
+    vr[it] = *reinterpret_cast<const kf4*>(Vc + row);
+  }
   float sc[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int j = jw + it * RPI + r;
-    float d = 0.f;
-    if (j < j_hi) {
-      const kf4 kr = *reinterpret_cast<const kf4*>(Kc + (int64_t)j * C + c * 4);
-      d = q.x * kr.x + q.y * kr.y + q.z * kr.z + q.w * kr.w;
-    }
+    float d = q.x * kr[it].x + q.y * kr[it].y + q.z * kr[it].z + q.w * kr[it].w;
 #pragma unroll
     for (int o = LPR / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
     sc[it] = j < j_hi ? d * scale : -INFINITY;
@@ -187,19 +193,16 @@ __global__ __launch_bounds__(256) void kv_attend_part_k(const float* __restrict_
   for (int it = 0; it < IT; ++it) m = fmaxf(m, sc[it]);
 #pragma unroll
   for (int o = 32; o >= LPR; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  // a wave past the block's end (m = -inf) gets weights exp(-inf) = 0; no branch,
+  // so the value loads stay where they were issued
+  const float ms = m == -INFINITY ? 0.f : m;
   float l = 0.f;
   kf4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (m != -INFINITY) {  // the wave holds at least one position
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int j = jw + it * RPI + r;
-      if (j < j_hi) {
-        const float p = expf(sc[it] - m);
-        const kf4 v = *reinterpret_cast<const kf4*>(Vc + (int64_t)j * C + c * 4);
-        acc += p * v;
-        l += p;
-      }
-    }
+  for (int it = 0; it < IT; ++it) {
+    const float p = expf(sc[it] - ms);  // sc = -inf past the block: p = 0
+    acc += p * vr[it];
+    l += p;
   }
 #pragma unroll
   for (int o = 32; o >= LPR; o >>= 1) {
