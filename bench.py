@@ -16,6 +16,9 @@ Prints one JSON line (see the fields below).  Options:
   --no-cpu-baseline  skip timing the CPU oracle
   --copy-probe     first run a plain 1 GiB device-to-device copy (3 times), the
                    known-size reference that HBM byte counters are scaled by
+  --decode         time KV-cached generation instead (16 prompts of 768 tokens,
+                   256 steps sampled with top-k 40); --steps full generations
+                   are timed; --uncached adds generation without the cache
 
 roofline.traffic is the contraction kernel's HBM bytes per launch as read by the
 FETCH_SIZE and WRITE_SIZE counters (scaled by the copy probe), taken from the
@@ -48,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seq", type=int, default=1024)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="time KV-cached generation (16 prompts of 768 tokens, 256 sampled steps) instead")
+    ap.add_argument("--uncached", action="store_true", help="with --decode: also time generation without the cache")
     return ap.parse_args()
 
 
@@ -110,12 +116,78 @@ def copy_probe():
     del src, dst
 
 
+def decode_bench(args):
+    """KV-cached generation at the GPT-2-124M shape: 16 prompts of 768 tokens, then 256
+    steps sampled with top-k 40 at temperature 1 (uniforms drawn beforehand).  --warmup
+    short generations, then --steps timed full generations; the prefill alone is timed
+    the same way so that the per-step cost of decoding can be separated from it."""
+    import torch
+
+    import synthetic as S
+    import transformer_fwd_bwd_amd as T
+    from transformer_fwd_bwd_amd import gpt as G
+
+    s, params, prompts, u = S.gpt2_infer()
+    B, Pn = prompts.shape
+    n_new = u.shape[1]
+    ctx = T.Context(arena_bytes=int(os.environ.get("TFB_ARENA_GB", "64")) << 30, precision=args.precision)
+    model = G.Gpt(ctx, s.n_layer, s.n_head, params)
+    del params
+    pd, ud = torch.from_numpy(prompts).to("cuda:0"), torch.from_numpy(u).to("cuda:0")
+    for _ in range(args.warmup):
+        model.generate(pd[:, :64].contiguous(), 4, ud[:, :4].contiguous(), 40, 1.0)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps
+
+    def prefill():
+        kv = T.KvCache(ctx, s.n_layer, B, Pn + n_new - 1, s.n_embd)
+        ctx.set_grad_enabled(False)
+        model.prefill(pd[:, :-1].contiguous(), kv)
+        ctx.tape_reset()
+        ctx.set_grad_enabled(True)
+        kv.close()
+
+    t_gen = timed(lambda: model.generate(pd, n_new, ud, 40, 1.0))
+    t_pre = timed(prefill)
+    step_ms = (t_gen - t_pre) / n_new * 1e3
+    out = {
+        "metric": "KV-cached generation: sampled tokens/s (16 x 768-token prompts, 256 steps, top-k 40)",
+        "value": round(B * n_new / t_gen, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_generation": round(t_gen * 1e3, 2),
+        "prefill_ms": round(t_pre * 1e3, 2),
+        "decode_ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "dtype": args.precision,
+        "data": "synthetic",
+        "config": {"workload": "gpt2-124m-shape KV-cached generation", "batch": B, "prompt": Pn, "new_tokens": n_new},
+    }
+    if args.uncached:
+        t_unc = timed(lambda: model.generate_uncached(pd, n_new, ud, 40, 1.0))
+        out["uncached_ms_per_generation"] = round(t_unc * 1e3, 2)
+        out["cached_speedup"] = round(t_unc / t_gen, 2)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: libtfb runs on exactly one GPU (asked for --gpus {args.gpus}); "
               "data parallelism across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
+    if args.decode:
+        decode_bench(args)
+        return
     import numpy as np
     import torch
 

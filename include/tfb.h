@@ -251,6 +251,10 @@ typedef struct tfb_kv tfb_kv;
 /* A key/value cache of `layers` x 2 x batch x tmax x channels fp32 values in the
  * persistent arena, zero-filled (tmax <= 16384). */
 int tfb_kv_create(tfb_ctx* ctx, int layers, int batch, int tmax, int channels, tfb_kv** out);
+/* Frees the handle.  The cache's arena memory is given back when no persistent
+ * allocation (a parameter, an optimizer state, another cache) was made after it;
+ * otherwise it stays reserved until the context is destroyed.  Queued work that
+ * reads the cache still completes before later work on the stream reuses it. */
 int tfb_kv_destroy(tfb_kv* kv);
 /* Copy the keys and values (the second and third column thirds) of qkv
  * [batch, T, 3C] into positions pos0 .. pos0+T-1 of `layer` (a batched prompt). */

@@ -108,6 +108,28 @@ def test_kv_attend_across_position_blocks(ctx, hs, H):
     kv.close()
 
 
+def test_kv_cache_memory_returns_to_the_arena(ctx):
+    """Destroying the most recent cache gives its memory back: repeated generations in one
+    context do not grow the persistent arena; a cache followed by a parameter stays."""
+    import torch
+    s, params, _ = S.tiny_gpt()
+    model = G.Gpt(ctx, s.n_layer, s.n_head, params)
+    prompts = torch.from_numpy(S.random_ids(79, (2, 5), s.vocab)).to("cuda:0")
+    u = torch.from_numpy(S.rng_for(80).random((2, 3))).to("cuda:0")
+    base = ctx.arena_usage()[0]
+    for _ in range(3):
+        model.generate(prompts, 3, u, 5, 1.0)
+        assert ctx.arena_usage()[0] == base
+    kv = T.KvCache(ctx, 1, 2, 8, s.n_embd)
+    held = ctx.arena_usage()[0]
+    p = ctx.tensor((4,), np.ones(4, np.float32), param=True)
+    kv.close()
+    assert ctx.arena_usage()[0] > held > base
+    p.release()
+    for t in model.param_list:
+        t.release()
+
+
 def _teacher_forced(ctx, prec, B=4, Pn=16, steps=20, k=40, temp=1.0):
     import torch
     s, params, _ = S.tiny_gpt()

@@ -184,6 +184,7 @@ struct tfb_kv {
   tfb_ctx* ctx = nullptr;
   int layers = 0, batch = 0, tmax = 0, channels = 0;
   float* data = nullptr;  // persistent arena: [layers][2][batch][tmax][channels] fp32
+  size_t off = 0, end = 0;  // its arena range
 };
 
 struct tfb_opt {
@@ -1981,10 +1982,12 @@ int tfb_kv_create(tfb_ctx* ctx, int layers, int batch, int tmax, int channels, t
     need(layers > 0 && batch > 0 && tmax > 0 && channels > 0, TFB_ERR_SHAPE, "kv cache sizes must be positive");
     need(tmax <= 16384, TFB_ERR_SHAPE, "kv cache longer than 16384 positions is not supported");
     const size_t n = (size_t)layers * 2 * batch * tmax * channels;
-    float* p = reinterpret_cast<float*>(ctx->arena.base + ctx->arena.alloc_persist(n * sizeof(float)));
+    const size_t off = ctx->arena.alloc_persist(n * sizeof(float));
+    float* p = reinterpret_cast<float*>(ctx->arena.base + off);
     hip_check(fill(p, 0.f, (int64_t)n, C.s()), "kv clear");
     tfb_kv* kv = new tfb_kv();
     kv->ctx = ctx, kv->layers = layers, kv->batch = batch, kv->tmax = tmax, kv->channels = channels, kv->data = p;
+    kv->off = off, kv->end = ctx->arena.lo;
     *out = kv;
   });
 }
@@ -1992,6 +1995,11 @@ int tfb_kv_create(tfb_ctx* ctx, int layers, int batch, int tmax, int channels, t
 int tfb_kv_destroy(tfb_kv* kv) {
   return guarded([&] {
     need(kv != nullptr, TFB_ERR_ARG, "null cache");
+    // the persistent arena is a stack: the cache's range returns to it when it is the
+    // most recent persistent allocation.  Work already queued on the stream that reads
+    // the cache runs before anything later queued can reuse the range.
+    Arena& A = kv->ctx->arena;
+    if (A.lo == kv->end) A.lo = kv->off;
     delete kv;
   });
 }
