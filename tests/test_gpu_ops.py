@@ -102,13 +102,6 @@ def test_linear_few_rows(ctx, prec, M, K, N):
                                 rnd(133, (M, N))], (M, N))
 
 
-def bf16_round(a):
-    """float32 -> nearest bfloat16 value (ties to even), as float32."""
-    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
-
-
 @pytest.mark.parametrize("M,K,N", [(16, 768, 2304), (16, 3072, 768), (3, 130, 132), (17, 300, 132)])
 def test_linear_few_rows_bf16_operands_exact(ctx, M, K, N):
     """In the bf16 variant a product multiplies the bf16 values of its operands exactly
@@ -119,8 +112,12 @@ def test_linear_few_rows_bf16_operands_exact(ctx, M, K, N):
     x, w, b = rnd(140, (M, K)), rnd(141, (K, N), 1 / np.sqrt(K)), rnd(142, (N,))
     ts = [ctx.tensor(a.shape, a) for a in (x, w, b)]
     y = T.linear(*ts).numpy()
-    ref = bf16_round(x).astype(np.float64) @ bf16_round(w).astype(np.float64) + b
+    ref = _bf16_round(x).astype(np.float64) @ _bf16_round(w).astype(np.float64) + b
     assert_close(y, ref, 1e-5, "forward")
+    ctx.tape_reset()
+    # kept as bf16 alone: the exact bf16 rounding of the plain output
+    yb = T.linear(*ts, bf16_only=True).numpy()
+    np.testing.assert_array_equal(yb, _bf16_round(y))
     ctx.tape_reset()
     for t in ts:
         t.release()
