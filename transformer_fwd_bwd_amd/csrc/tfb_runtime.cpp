@@ -1430,7 +1430,13 @@ static int matmul_impl(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, t
     float* yd = ctx->tensors[h].data;
     const float* xd = ctx->tensors[x].data;
     const float* wd = ctx->tensors[w].data;
-    const Opnd xo = op_data(C, ctx->tensors[x]), wo = op_data(C, ctx->tensors[w]);
+    // a product of at most 16 rows whose input has no bf16 copy yet (the cached
+    // attention's output in decoding) rounds the fp32 input as it loads it: the same
+    // values without a conversion launch
+    const bool round_on_load = C.bf16_mode() && kind != OP_MATMUL_T && rows <= 16 && !ctx->tensors[x].bf_valid &&
+                               ctx->tensors[x].f32_valid;
+    const Opnd xo = round_on_load ? Opnd{C.f32(ctx->tensors[x]), false} : op_data(C, ctx->tensors[x]);
+    const Opnd wo = op_data(C, ctx->tensors[w]);
     (void)xd, (void)wd;
     uint16_t* yb = out_flags ? C.twin_data(ctx->tensors[h]) : nullptr;
     const bool only = yb && (out_flags & TFB_OUT_BF16_ONLY);
