@@ -9,11 +9,14 @@
 // 256 CUs.  In a workgroup, lane 4c + r of wave w multiplies columns 4c..4c+3
 // of k rows 4w + r + 16i by the 16 rows of A (staged in LDS, k-major, as
 // fp32); the four lanes of a quad sum through DPP, the four waves through LDS.
+// In the bf16 variant an operand stored as fp32 is rounded to bf16 as it is
+// loaded, so the products are those of the bf16 values either way.
+//
 // With one chunk the workgroup applies the epilogue; otherwise it writes its
 // partial to ws[chunk][M][N] and gemv_reduce_k sums the chunks in order and
-// applies the epilogue.  (Letting the last
-// workgroup of a strip do that sum needs device-scope fences, which write back
-// and invalidate the L2 of the workgroup's XCD: far slower here.)
+// applies the epilogue.  Summing them in the workgroup of a strip that
+// finishes last would need device-scope fences, which write back and
+// invalidate the L2 of the workgroup's XCD: far slower here.
 #include <algorithm>
 #include <type_traits>
 
@@ -207,6 +210,7 @@ SkPlan plan(const GemmArgs& g) {
   SkPlan p;
   const auto al = [](const void* q, int bytes) { return (reinterpret_cast<uintptr_t>(q) & (bytes - 1)) == 0; };
   if (g.M < 1 || g.M > SM || g.batch != 1 || g.K < 1 || g.N < 1) return p;
+  if ((int64_t)g.M * g.N > (1 << 28)) return p;  // keeps the launches' int indexes in range
   if (g.causal_a != CAUSAL_NONE || g.causal_out || g.a_mcontig || g.b_kcontig) return p;
   if (g.N % 4 || g.ldb % 4 || g.ldc % 4 || !al(g.B, g.b_bf16 ? 8 : 16) || !al(g.C, 16) || !al(g.bias, 16) ||
       !al(g.resid, 16) || !al(g.Cbf, 8))
@@ -215,6 +219,7 @@ SkPlan plan(const GemmArgs& g) {
   // a few hundred workgroups: 64-row chunks when 128-row ones leave under ~200
   p.kc = (int64_t)p.strips * ((g.K + SKC - 1) / SKC) < 192 ? SKC / 2 : SKC;
   p.chunks = (g.K + p.kc - 1) / p.kc;
+  if ((int64_t)p.strips * p.chunks > (1 << 24)) return p;
   p.ok = true;
   return p;
 }
