@@ -102,6 +102,20 @@ def test_linear_few_rows(ctx, prec, M, K, N):
                                 rnd(133, (M, N))], (M, N))
 
 
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("V", [130, 1030])
+def test_matmul_t_few_rows_accumulating_grad(ctx, prec, V):
+    """x [5, 64] read by two products x @ w^T: the input gradient g @ w of each is a
+    few-row product, the second added onto the first (beta = 1); with 1030 rows of w
+    the output's rows are padded, so g is read at its padded stride."""
+    def gpu(x, w1, w2):
+        return T.add(T.matmul_t(x, w1), T.matmul_t(x, w2))
+
+    def ora(x, w1, w2):
+        return E.add(E.matmul_t(x, w1), E.matmul_t(x, w2))
+    check(ctx, prec, gpu, ora, [rnd(150, (5, 64)), rnd(151, (V, 64), 0.1), rnd(152, (V, 64), 0.1)], (5, V))
+
+
 @pytest.mark.parametrize("M,K,N", [(16, 768, 2304), (16, 3072, 768), (3, 130, 132), (17, 300, 132)])
 def test_linear_few_rows_bf16_operands_exact(ctx, M, K, N):
     """In the bf16 variant a product multiplies the bf16 values of its operands exactly
