@@ -123,7 +123,7 @@ def test_planted_mistake_in_scalar_rule_is_caught(monkeypatch):
     # a wrong tanh rule (g * y instead of g * (1 - y^2)) must fail the scalar check
     def bad_tanh(self):
         t = math.tanh(self.data)
-        return self._unary(t, t, "tanh")
+        return Value.node(t, "tanh", (self, t))
     monkeypatch.setattr(Value, "tanh", bad_tanh)
     _, _, diff = scalar_gradient_check(lambda v: (v ** 3 + v * 2 + 1).tanh(), 0.5)
     assert diff > 1e-3
