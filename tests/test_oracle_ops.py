@@ -264,15 +264,37 @@ def test_layernorm_moments_and_orthogonality():
 
 def test_gelu_tanh_vs_erf_form():
     """The tanh form approximates x * Phi(x) (math.erf) closely but not exactly
-    ([GPT2-4, §"Common mistakes"]: the exact form is a different function)."""
-    xs = np.linspace(-6, 6, 2001)
+    ([GPT2-4, §"Common mistakes"]: the exact form is a different function).
+
+    Pins that do not restate the formula:
+    * its largest deviation from x * Phi(x) on [-8, 8] lies in (4e-4, 5e-4).  The
+      published constants give 4.73e-4; a slip in either constant moves it out of
+      that band (sqrt(2/pi) -> 0.8 gives 6.4e-4; 0.044715 -> 0.045 gives 5.6e-4,
+      -> 0.04 gives 2.9e-3, a dropped cubic term gives 3.4e-2);
+    * at 0 the tanh form must share the exact function's first two derivatives:
+      d/dx [x Phi(x)] = Phi(0) = 1/2 and d2/dx2 [x Phi(x)] = 2 phi(0) = sqrt(2/pi)
+      (the constant in front of the bracket is chosen for exactly this)."""
+    xs = np.linspace(-8, 8, 32001)
     exact = np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in xs])
     d = np.abs(O.gelu_fwd(xs) - exact)
-    assert d.max() < 1e-3
-    assert d.max() > 1e-5
+    assert 4e-4 < d.max() < 5e-4, d.max()
+    h = 1e-3
+    g = lambda v: O.gelu_fwd(np.array([v], np.float64))[0]
+    d1 = (g(h) - g(-h)) / (2 * h)
+    d2 = (g(h) - 2 * g(0.0) + g(-h)) / (h * h)
+    phi0 = 1.0 / math.sqrt(2 * math.pi)
+    assert abs(d1 - 0.5) < 1e-9
+    assert abs(d2 - 2 * phi0) < 1e-5, (d2, 2 * phi0)
     assert O.gelu_fwd(np.array([0.0]))[0] == 0.0
     assert abs(O.gelu_fwd(np.array([20.0]))[0] - 20.0) < 1e-12
     assert abs(O.gelu_fwd(np.array([-20.0]))[0]) < 1e-12
+
+
+@pytest.mark.parametrize("const,bad", [("GELU_C", 0.8), ("GELU_A", 0.045), ("GELU_A", 0.0)])
+def test_planted_gelu_constant_mistakes_fail(monkeypatch, const, bad):
+    monkeypatch.setattr(O, const, bad)
+    with pytest.raises(AssertionError):
+        test_gelu_tanh_vs_erf_form()
 
 
 def test_embedding_routing_is_exact():
