@@ -41,3 +41,34 @@ def ctx():
     c = T.Context(arena_bytes=4 << 30, precision="fp32")
     yield c
     c.close()
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Achieved parity errors of this session's GPU comparisons, as fractions of
+    their tolerance (1.0 = at the gate): per test its worst L2 and worst
+    element-wise figure, tightest last, then the overall worst."""
+    try:
+        from parity import RESULTS
+    except Exception:
+        return
+    if not RESULTS:
+        return
+    per = {}
+    for test, what, l2, el in RESULTS:
+        w = per.setdefault(test, [0.0, "", 0.0, "", 0])
+        w[4] += 1
+        if l2 >= w[0]:
+            w[0], w[1] = l2, what
+        if el >= w[2]:
+            w[2], w[3] = el, what
+    tr = terminalreporter
+    tr.write_line("")
+    tr.write_line(f"parity headroom: {len(RESULTS)} checks in {len(per)} tests "
+                  "(error / tolerance; L2 = relative L2 gate, elem = element-wise gate)")
+    for test, (l2, w2, el, we, n) in sorted(per.items(), key=lambda kv: max(kv[1][0], kv[1][2])):
+        name = test.split("::", 1)[-1]
+        tr.write_line(f"  {max(l2, el):6.3f}  L2 {l2:6.3f} elem {el:6.3f}  n={n:<4d} {name}  [{we if el >= l2 else w2}]")
+    worst_l2 = max(RESULTS, key=lambda r: r[2])
+    worst_el = max(RESULTS, key=lambda r: r[3])
+    tr.write_line(f"parity worst: L2 {worst_l2[2]:.3f} of tol ({worst_l2[0].split('::', 1)[-1]}: {worst_l2[1]}); "
+                  f"elem {worst_el[3]:.3f} of tol ({worst_el[0].split('::', 1)[-1]}: {worst_el[1]})")

@@ -88,11 +88,14 @@ def test_linear_residual_long_k_split(ctx, N):
 
 @pytest.mark.parametrize("prec", PRECS)
 @pytest.mark.parametrize("M,K,N", [(1, 3, 4), (5, 130, 132), (16, 768, 2304), (7, 3100, 68), (16, 256, 1028),
-                                   (17, 300, 132)])
+                                   (17, 300, 132), (5, 130, 130), (3, 70, 6)])
 def test_linear_few_rows(ctx, prec, M, K, N):
     """Products of at most 16 rows (one token per sequence) take the small-row kernel:
-    one k chunk, several chunks summed by the strip's last workgroup, ragged column
-    strips; 17 rows take the tiled kernel.  r + (x @ w + b) and every gradient."""
+    one k chunk, several chunks summed by the separate chunk-sum pass (gemv_reduce_k),
+    ragged column strips; 17 rows take the tiled kernel, and so do few-row products
+    whose column count is not a multiple of 4 (rows of w, b, r and y then sit off
+    16-byte alignment), which in the bf16 variant read the fp32 input and round it
+    as they load it.  r + (x @ w + b) and every gradient."""
     def gpu(x, w, b, r):
         return T.linear(x, w, b, residual=r)
 
@@ -116,7 +119,8 @@ def test_matmul_t_few_rows_accumulating_grad(ctx, prec, V):
     check(ctx, prec, gpu, ora, [rnd(150, (5, 64)), rnd(151, (V, 64), 0.1), rnd(152, (V, 64), 0.1)], (5, V))
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 768, 2304), (16, 3072, 768), (3, 130, 132), (17, 300, 132)])
+@pytest.mark.parametrize("M,K,N", [(16, 768, 2304), (16, 3072, 768), (3, 130, 132), (17, 300, 132), (5, 130, 130),
+                                   (16, 64, 18)])
 def test_linear_few_rows_bf16_operands_exact(ctx, M, K, N):
     """In the bf16 variant a product multiplies the bf16 values of its operands exactly
     and accumulates in fp32: against the float64 product of the rounded operands the
