@@ -57,41 +57,79 @@ typedef int32_t tfb_tensor;
                             every other op and all stored tensors stay fp32 */
 
 #define TFB_MAX_DIMS 6
+#define TFB_MAX_NAME 128  /* a tensor name is kept up to 127 bytes */
 
 /* ---------------------------------------------------------------- context */
 
 /* Create a context on `device` that enqueues on `hip_stream` (a hipStream_t;
  * NULL = the null stream) and sub-allocates from [arena, arena + arena_bytes)
- * (device memory owned by the caller, at least 256-byte aligned). */
+ * (device memory owned by the caller, at least 256-byte aligned).  The context
+ * holds what the pages keep in the Tensor objects and the graph they link:
+ * every tensor's data and gradient, and the recorded backward rules
+ * ([Autograd-1, "The Tensor class"; "How each op records itself in the
+ * graph"]).  precision: TFB_FP32 or TFB_BF16_MFMA.  Errors: TFB_ERR_ARG for a
+ * null out/arena, an unknown precision or a missing device. */
 int tfb_init(tfb_ctx** out, int device, void* hip_stream, void* arena, size_t arena_bytes, int precision);
+/* Destroy the context and every handle it owns; the arena itself stays the
+ * caller's.  Work still queued on the stream must not be running after this
+ * returns, so it synchronises first.  (The pages' objects are garbage
+ * collected; here the owner ends them: [Autograd-1, "The Tensor class"].) */
 int tfb_destroy(tfb_ctx* ctx);
+/* Text of the calling thread's last error (valid until its next call): the
+ * counterpart of the pages' exception messages, e.g. the shape message of
+ * MatMul or "Backward() starts from a scalar loss" ([Autograd-1, "Ops";
+ * "How each op records itself in the graph"]).  Never NULL. */
 const char* tfb_last_error(void);
+/* Switch the contraction arithmetic for ops recorded from now on (TFB_FP32 or
+ * TFB_BF16_MFMA).  The pages compute in float ([Autograd-1, "Why fast
+ * MatMul"]); the bf16 variant rounds the contraction operands only. */
 int tfb_set_precision(tfb_ctx* ctx, int precision);
 /* Inference mode: with enabled == 0 ops record nothing ([Autograd-1, "The
  * Tensor class": the NoGrad flag]).  Per context. */
 int tfb_set_grad_enabled(tfb_ctx* ctx, int enabled);
-/* Wait for all enqueued work; returns TFB_ERR_HIP if any of it failed. */
+/* Wait for all enqueued work; returns TFB_ERR_HIP if any of it failed.  The
+ * pages' calls return finished values ([Autograd-1, "The Tensor class"]);
+ * here results are final once this returns (tfb_tensor_read also waits). */
 int tfb_sync(tfb_ctx* ctx);
-/* Bytes in use at the low (persistent) and high (step) ends of the arena. */
+/* Bytes in use at the low (persistent) and high (step) ends of the arena
+ * (the persistent figure includes ranges given back below its top that later
+ * persistent allocations reuse).  Either pointer may be NULL.  Memory
+ * bookkeeping of the tensors the pages allocate per op ([Autograd-1, "The
+ * Tensor class": Grad created on demand]). */
 int tfb_arena_usage(tfb_ctx* ctx, size_t* persistent, size_t* step);
 
 /* ---------------------------------------------------------------- tensors */
 
-/* A leaf tensor ([Autograd-1, "The Tensor class": op "leaf"]).  With dev_ptr
- * != NULL the tensor borrows that device memory (the caller keeps it alive and
- * 256-byte aligned); with NULL it is allocated in the persistent arena and
- * zero-filled.  is_param marks optimizer parameters (informational). */
-int tfb_tensor_create(tfb_ctx* ctx, const int64_t* shape, int ndim, void* dev_ptr, int is_param,
+/* A leaf tensor ([Autograd-1, "The Tensor class": op "leaf", flat row-major
+ * Data with a Shape, and a Name for parameters]).  shape: ndim (1..6)
+ * positive sizes.  With dev_ptr != NULL the tensor borrows that device memory
+ * (the caller keeps it alive and 256-byte aligned); with NULL it is allocated
+ * in the persistent arena and zero-filled.  is_param marks optimizer
+ * parameters (informational).  name: NULL or a NUL-terminated string, copied
+ * (up to TFB_MAX_NAME - 1 bytes); it appears in shape error messages.
+ * Errors: TFB_ERR_SHAPE (bad rank or size), TFB_ERR_ARG (misaligned dev_ptr),
+ * TFB_ERR_OOM. */
+int tfb_tensor_create(tfb_ctx* ctx, const int64_t* shape, int ndim, void* dev_ptr, int is_param, const char* name,
                       tfb_tensor* out);
+/* The tensor's name, NUL-terminated, truncated to cap - 1 bytes (empty for op
+ * outputs and unnamed leaves).  [Autograd-1, "The Tensor class": Name] */
+int tfb_tensor_name(tfb_ctx* ctx, tfb_tensor t, char* buf, size_t cap);
 /* Shape, rank and device pointers of a tensor; *grad is NULL while the tensor
- * has no gradient buffer.  Any output pointer may be NULL. */
+ * has no gradient buffer ([Autograd-1, "The Tensor class": Grad is created on
+ * demand]).  Any output pointer may be NULL.  The pointers stay owned by the
+ * context. */
 int tfb_tensor_info(tfb_ctx* ctx, tfb_tensor t, int64_t* shape, int* ndim, void** data, void** grad);
-/* Copy n floats between host memory and the tensor's data (which == 0) or
- * gradient (which == 1; reading a gradient that was cleared returns zeros,
- * reading one that never existed is TFB_ERR_STATE).  Synchronous. */
+/* Copy n floats (n == the tensor's size, else TFB_ERR_SHAPE) between host
+ * memory and the tensor's Data (which == 0) or Grad (which == 1; reading a
+ * gradient that was cleared returns zeros, reading one that never existed or
+ * that is kept only as bf16 is TFB_ERR_STATE).  Synchronous: the read waits
+ * for the work queued before it.  [Autograd-1, "The Tensor class": Data and
+ * Grad, same size] */
 int tfb_tensor_write(tfb_ctx* ctx, tfb_tensor t, const float* host_src, int64_t n);
 int tfb_tensor_read(tfb_ctx* ctx, tfb_tensor t, int which, float* host_dst, int64_t n);
-/* Release a leaf tensor.  Op outputs are released by tfb_tape_reset. */
+/* Release a leaf tensor (TFB_ERR_STATE while the tape still references it).
+ * Op outputs are released by tfb_tape_reset.  [Autograd-1, "The Tensor
+ * class"] */
 int tfb_tensor_release(tfb_ctx* ctx, tfb_tensor t);
 
 /* ---------------------------------------------------------------- ops
@@ -114,7 +152,8 @@ int tfb_tanh(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y);
 /* y = 0.5 a (1 + tanh(sqrt(2/pi)(a + 0.044715 a^3))), GPT-2's tanh form.
  * [GPT2-4, "Common mistakes"] */
 int tfb_gelu(tfb_ctx* ctx, tfb_tensor a, tfb_tensor* y);
-/* tfb_gelu with flags (TFB_OUT_BF16_ONLY; unknown flags: TFB_ERR_ARG). */
+/* tfb_gelu with flags (TFB_OUT_BF16_ONLY; unknown flags: TFB_ERR_ARG).
+ * [GPT2-4, "Common mistakes"] */
 int tfb_gelu_ex(tfb_ctx* ctx, tfb_tensor a, int flags, tfb_tensor* y);
 /* y = x[..., K] @ w[K, M] (rows of x flattened).  Backward dx = g w^T,
  * dw = x^T g.  [Autograd-1, "Ops": MatMul] */
@@ -153,11 +192,14 @@ int tfb_linear(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tenso
  * [Autograd-1, "Ops": MatMul, the bias Add and Add; GPT2-4, "Loading the
  * weights": the residual stream x = x + attn(ln_1(x)), x = x + mlp(ln_2(x))] */
 int tfb_linear_residual(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor r, tfb_tensor* y);
+/* tfb_linear with flags (TFB_OUT_BF16_COPY, TFB_OUT_BF16_ONLY above).
+ * [GPT2-4, "Loading the weights": Linear weights stored [in, out]] */
 int tfb_linear_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int flags, tfb_tensor* y);
 /* Per row over the last dim: (x - mean)/sqrt(var + eps) * gamma + beta with the
  * biased variance.  [Autograd-1, table of ops: LayerNorm] */
 int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y);
-/* tfb_layernorm with flags (TFB_OUT_BF16_ONLY; unknown flags: TFB_ERR_ARG). */
+/* tfb_layernorm with flags (TFB_OUT_BF16_ONLY; unknown flags: TFB_ERR_ARG).
+ * [Autograd-1, table of ops: LayerNorm] */
 int tfb_layernorm_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, int flags,
                      tfb_tensor* y);
 /* y[b, t, :] = table[ids[b*T + t], :], y shape [batch, n/batch, C]; backward
@@ -221,7 +263,11 @@ int tfb_backward(tfb_ctx* ctx, tfb_tensor loss);
  * Optimizer": ZeroGrad]).  Tensors that never had a gradient are skipped. */
 int tfb_zero_grad(tfb_ctx* ctx, const tfb_tensor* params, int n);
 /* End of step: drop the tape, release every op output and free the step end
- * of the arena. */
+ * of the arena.  The pages' graph is dropped with the loss tensor that roots
+ * it ([Autograd-1, "How each op records itself in the graph": the graph is
+ * the parents and backward fields of each output]); here it is dropped
+ * explicitly.  Leaf tensors and their gradients are kept.  Work already queued
+ * that reads the freed memory completes before later work reuses it. */
 int tfb_tape_reset(tfb_ctx* ctx);
 
 /* ---------------------------------------------------------------- optimizers */
@@ -234,10 +280,17 @@ int tfb_tape_reset(tfb_ctx* ctx);
  * One fused launch updates all parameters. */
 int tfb_adamw_create(tfb_ctx* ctx, const tfb_tensor* params, int n, float lr, float weight_decay, float beta1,
                      float beta2, float eps, tfb_opt** out);
+/* One AdamW step over every parameter given at creation ([Autograd-1, "The
+ * Optimizer": Step]). */
 int tfb_adamw_step(tfb_opt* opt);
+/* Change the learning rate of later steps ([Autograd-1, "The Optimizer": the
+ * lr field]). */
 int tfb_adamw_set_lr(tfb_opt* opt, float lr);
-/* Read the moments of parameter i (copies n floats each; NULL skips). */
+/* Read the moments m and v of parameter i (n floats each, n == its size;
+ * NULL skips one).  Synchronous.  [Autograd-1, "The Optimizer": AdamW's m, v] */
 int tfb_adamw_moments(tfb_opt* opt, int i, float* host_m, float* host_v, int64_t n);
+/* Free the optimizer handle; its moments' arena memory stays reserved until the
+ * context is destroyed.  [Autograd-1, "The Optimizer"] */
 int tfb_adamw_destroy(tfb_opt* opt);
 /* w -= lr * g for every given parameter that has a gradient.
  * [Autograd-1, "The Optimizer": SGD] */
@@ -251,10 +304,11 @@ typedef struct tfb_kv tfb_kv;
 /* A key/value cache of `layers` x 2 x batch x tmax x channels fp32 values in the
  * persistent arena, zero-filled (tmax <= 16384). */
 int tfb_kv_create(tfb_ctx* ctx, int layers, int batch, int tmax, int channels, tfb_kv** out);
-/* Frees the handle.  The cache's arena memory is given back when no persistent
- * allocation (a parameter, an optimizer state, another cache) was made after it;
- * otherwise it stays reserved until the context is destroyed.  Queued work that
- * reads the cache still completes before later work on the stream reuses it. */
+/* Frees the handle and gives the cache's arena memory back: to the top of the
+ * persistent end when nothing was allocated there after it, otherwise as a hole
+ * that later persistent allocations (the next cache, a parameter, a bf16 weight
+ * copy) take first.  Queued work that reads the cache still completes before
+ * later work on the stream reuses it.  [GPT2-4, "Generation with KV cache"] */
 int tfb_kv_destroy(tfb_kv* kv);
 /* Copy the keys and values (the second and third column thirds) of qkv
  * [batch, T, 3C] into positions pos0 .. pos0+T-1 of `layer` (a batched prompt). */
@@ -272,7 +326,9 @@ int tfb_sample_topk(tfb_ctx* ctx, tfb_tensor logits, int k, float temperature, c
 
 /* ---------------------------------------------------------------- measurement */
 
-/* Between begin and end, every contraction launch (the MatMul family and the
+/* Measurement of the pages' claim that matrix multiplication takes most of
+ * the time ([Autograd-1, "Why fast MatMul"]).
+ * Between begin and end, every contraction launch (the MatMul family and the
  * attention products, with any split-K reduction) is bracketed by HIP events on
  * the context's stream.  end() synchronises and returns the summed kernel time
  * in milliseconds, the algorithmic flops of those launches (2*M*N*K, causal

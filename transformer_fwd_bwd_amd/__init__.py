@@ -35,7 +35,8 @@ SIGNATURES = {
     "tfb_set_grad_enabled": [c_void_p, c_int],
     "tfb_sync": [c_void_p],
     "tfb_arena_usage": [c_void_p, P(c_size_t), P(c_size_t)],
-    "tfb_tensor_create": [c_void_p, P(c_int64), c_int, c_void_p, c_int, P(c_int32)],
+    "tfb_tensor_create": [c_void_p, P(c_int64), c_int, c_void_p, c_int, ctypes.c_char_p, P(c_int32)],
+    "tfb_tensor_name": [c_void_p, c_int32, ctypes.c_char_p, c_size_t],
     "tfb_tensor_info": [c_void_p, c_int32, P(c_int64), P(c_int), P(c_void_p), P(c_void_p)],
     "tfb_tensor_write": [c_void_p, c_int32, c_void_p, c_int64],
     "tfb_tensor_read": [c_void_p, c_int32, c_int, c_void_p, c_int64],
@@ -151,6 +152,12 @@ class Tensor:
         _check(_lib.tfb_tensor_info(self.ctx.ptr, self.h, None, None, ctypes.byref(p), None))
         return p.value or 0
 
+    @property
+    def name(self) -> str:
+        buf = ctypes.create_string_buffer(128)
+        _check(_lib.tfb_tensor_name(self.ctx.ptr, self.h, buf, 128))
+        return buf.value.decode()
+
     def numpy(self) -> np.ndarray:
         out = np.empty(self.shape, np.float32)
         _check(_lib.tfb_tensor_read(self.ctx.ptr, self.h, 0, out.ctypes.data, out.size))
@@ -215,11 +222,11 @@ class Context:
         _check(_lib.tfb_arena_usage(self.ptr, ctypes.byref(a), ctypes.byref(b)))
         return a.value, b.value
 
-    def tensor(self, shape, data=None, param: bool = False, dev_ptr: Optional[int] = None) -> Tensor:
+    def tensor(self, shape, data=None, param: bool = False, dev_ptr: Optional[int] = None, name: str = "") -> Tensor:
         shape = tuple(int(s) for s in shape)
         h = c_int32()
         _check(_lib.tfb_tensor_create(self.ptr, _i64s(shape), len(shape), c_void_p(dev_ptr) if dev_ptr else None,
-                                      int(param), ctypes.byref(h)))
+                                      int(param), name.encode() if name else None, ctypes.byref(h)))
         t = Tensor(self, h.value)
         if data is not None:
             t.write(np.asarray(data, np.float32).reshape(shape))

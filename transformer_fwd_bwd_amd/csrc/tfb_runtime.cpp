@@ -48,6 +48,7 @@ void hip_check(hipError_t e, const char* what) {
 enum GradState { G_NONE = 0, G_ZERO = 1, G_VALID = 2, G_BF16 = 3 };
 
 struct TensorRec {
+  std::string name;  // a leaf's name as given at creation (may be empty)
   bool live = false;
   bool leaf = true;
   bool is_param = false;
@@ -134,14 +135,45 @@ struct Arena {
   size_t size = 0;
   size_t lo = 0;   // persistent allocations: [0, lo)
   size_t hi = 0;   // step allocations: [hi, size)
+  // ranges below lo given back out of stack order (offset, bytes), sorted by
+  // offset and coalesced; persistent allocations take the first that fits
+  std::vector<std::pair<size_t, size_t>> holes;
 
   static size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
   size_t alloc_persist(size_t n) {
     n = up(std::max<size_t>(n, 1));
+    for (size_t i = 0; i < holes.size(); ++i) {
+      if (holes[i].second < n) continue;
+      const size_t off = holes[i].first;
+      holes[i].first += n, holes[i].second -= n;
+      if (holes[i].second == 0) holes.erase(holes.begin() + i);
+      return off;
+    }
     if (lo + n > hi) fail(TFB_ERR_OOM, "arena exhausted (persistent allocation of " + std::to_string(n) + " bytes)");
     size_t off = lo;
     lo += n;
     return off;
+  }
+  // Give back [off, off + n) of the persistent end.  Work already queued on the
+  // stream that uses the range runs before any later-queued work can reuse it.
+  void release_persist(size_t off, size_t n) {
+    n = up(std::max<size_t>(n, 1));
+    size_t i = 0;
+    while (i < holes.size() && holes[i].first < off) ++i;
+    holes.insert(holes.begin() + i, {off, n});
+    // coalesce with the neighbours, then let a hole that reaches lo lower it
+    if (i + 1 < holes.size() && holes[i].first + holes[i].second == holes[i + 1].first) {
+      holes[i].second += holes[i + 1].second;
+      holes.erase(holes.begin() + i + 1);
+    }
+    if (i > 0 && holes[i - 1].first + holes[i - 1].second == holes[i].first) {
+      holes[i - 1].second += holes[i].second;
+      holes.erase(holes.begin() + i);
+    }
+    if (!holes.empty() && holes.back().first + holes.back().second == lo) {
+      lo = holes.back().first;
+      holes.pop_back();
+    }
   }
   void* alloc_step(size_t n) {
     n = up(std::max<size_t>(n, 1));
@@ -184,7 +216,7 @@ struct tfb_kv {
   tfb_ctx* ctx = nullptr;
   int layers = 0, batch = 0, tmax = 0, channels = 0;
   float* data = nullptr;  // persistent arena: [layers][2][batch][tmax][channels] fp32
-  size_t off = 0, end = 0;  // its arena range
+  size_t off = 0, end = 0;  // its arena range [off, end)
 };
 
 struct tfb_opt {
@@ -625,7 +657,8 @@ void need(bool cond, int code, const std::string& msg) {
 std::string shape_str(const TensorRec& t) {
   std::string s = "[";
   for (int i = 0; i < t.ndim; ++i) s += (i ? "," : "") + std::to_string(t.shape[i]);
-  return s + "]";
+  // a named leaf (a parameter) is named in shape errors, as the pages' messages do
+  return s + "]" + (t.name.empty() ? "" : " (" + t.name + ")");
 }
 
 std::vector<int64_t> shape_vec(const TensorRec& t) { return std::vector<int64_t>(t.shape, t.shape + t.ndim); }
@@ -1141,7 +1174,8 @@ int tfb_arena_usage(tfb_ctx* ctx, size_t* persistent, size_t* step) {
   });
 }
 
-int tfb_tensor_create(tfb_ctx* ctx, const int64_t* shape, int ndim, void* dev_ptr, int is_param, tfb_tensor* out) {
+int tfb_tensor_create(tfb_ctx* ctx, const int64_t* shape, int ndim, void* dev_ptr, int is_param, const char* name,
+                      tfb_tensor* out) {
   return guarded([&] {
     Ctx C(ctx);
     need(shape != nullptr && out != nullptr, TFB_ERR_ARG, "null argument");
@@ -1170,7 +1204,19 @@ int tfb_tensor_create(tfb_ctx* ctx, const int64_t* shape, int ndim, void* dev_pt
     t.owns_persistent = dev_ptr == nullptr;
     t.persist_off = off;
     t.persist_bytes = Arena::up(std::max<size_t>(bytes, 1));
+    t.name = name ? std::string(name).substr(0, TFB_MAX_NAME - 1) : std::string();
     *out = h;
+  });
+}
+
+int tfb_tensor_name(tfb_ctx* ctx, tfb_tensor h, char* buf, size_t cap) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need(buf != nullptr && cap > 0, TFB_ERR_ARG, "null or empty name buffer");
+    const std::string& n = C.T(h).name;
+    const size_t k = std::min(n.size(), cap - 1);
+    std::memcpy(buf, n.data(), k);
+    buf[k] = 0;
   });
 }
 
@@ -1239,8 +1285,10 @@ int tfb_tensor_release(tfb_ctx* ctx, tfb_tensor h) {
     for (const Rec& r : ctx->tape)
       for (int i : r.in)
         need(i != h, TFB_ERR_STATE, "tensor is still referenced by the tape");
-    // free the tail of the persistent region when possible
-    if (t.owns_persistent && t.persist_off + t.persist_bytes == ctx->arena.lo) ctx->arena.lo = t.persist_off;
+    // a leaf's memory returns only from the top of the persistent end (an optimizer
+    // may still hold its address); a hole it leaves below is never reused
+    if (t.owns_persistent && t.persist_off + t.persist_bytes == ctx->arena.lo)
+      ctx->arena.release_persist(t.persist_off, t.persist_bytes);
     t.live = false;
     ctx->free_handles.push_back(h);
   });
@@ -1993,7 +2041,7 @@ int tfb_kv_create(tfb_ctx* ctx, int layers, int batch, int tmax, int channels, t
     hip_check(fill(p, 0.f, (int64_t)n, C.s()), "kv clear");
     tfb_kv* kv = new tfb_kv();
     kv->ctx = ctx, kv->layers = layers, kv->batch = batch, kv->tmax = tmax, kv->channels = channels, kv->data = p;
-    kv->off = off, kv->end = ctx->arena.lo;
+    kv->off = off, kv->end = off + Arena::up(n * sizeof(float));
     *out = kv;
   });
 }
@@ -2001,11 +2049,7 @@ int tfb_kv_create(tfb_ctx* ctx, int layers, int batch, int tmax, int channels, t
 int tfb_kv_destroy(tfb_kv* kv) {
   return guarded([&] {
     need(kv != nullptr, TFB_ERR_ARG, "null cache");
-    // the persistent arena is a stack: the cache's range returns to it when it is the
-    // most recent persistent allocation.  Work already queued on the stream that reads
-    // the cache runs before anything later queued can reuse the range.
-    Arena& A = kv->ctx->arena;
-    if (A.lo == kv->end) A.lo = kv->off;
+    kv->ctx->arena.release_persist(kv->off, kv->end - kv->off);
     delete kv;
   });
 }

@@ -19,7 +19,7 @@ from . import (AdamW, Context, KvCache, Tensor, add, causal_attention, embedding
 
 
 def upload_params(ctx: Context, params: Dict[str, np.ndarray]) -> Dict[str, Tensor]:
-    return {k: ctx.tensor(v.shape, v, param=True) for k, v in params.items()}
+    return {k: ctx.tensor(v.shape, v, param=True, name=k) for k, v in params.items()}
 
 
 class Gpt:
