@@ -327,14 +327,35 @@ int tfb_sample_topk(tfb_ctx* ctx, tfb_tensor logits, int k, float temperature, c
 /* ---------------------------------------------------------------- measurement */
 
 /* Measurement of the pages' claim that matrix multiplication takes most of
- * the time ([Autograd-1, "Why fast MatMul"]).
- * Between begin and end, every contraction launch (the MatMul family and the
- * attention products, with any split-K reduction) is bracketed by HIP events on
- * the context's stream.  end() synchronises and returns the summed kernel time
- * in milliseconds, the algorithmic flops of those launches (2*M*N*K, causal
- * products counted over the needed triangle only) and the number of launches. */
+ * the time ([Autograd-1, "Why fast MatMul"]) and that cached generation is
+ * bound by memory ([GPT2-4, "Generation with KV cache"]).
+ * Between begin and end, the launches of the kernel families below are each
+ * bracketed by HIP events on the context's stream, and each family adds up the
+ * algorithmic work of its launches: flops (2*M*N*K, causal
+ * products counted over the needed triangle only) for the contractions, bytes
+ * (each operand read once, each output written once, in the form it is stored)
+ * for the others.  end() synchronises and returns the contraction family's
+ * summed time in milliseconds, its flops and its launch count; after it,
+ * tfb_profile_kind gives the same three figures for any family. */
+#define TFB_PROF_GEMM 0       /* MatMul family (MFMA tiles), flops */
+#define TFB_PROF_ATTN_FWD 1   /* fused causal attention forward: QK^T and PV, flops */
+#define TFB_PROF_ATTN_BWD 2   /* fused attention backward (dQ and dK/dV kernels): the four
+                                 products dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q, flops */
+#define TFB_PROF_CE 3         /* SoftmaxCrossEntropy forward (with the fused gradient) and backward, bytes */
+#define TFB_PROF_ADAMW 4      /* the fused AdamW pass, bytes */
+#define TFB_PROF_LN_FWD 5     /* LayerNorm forward, bytes */
+#define TFB_PROF_LN_BWD 6     /* LayerNorm backward (dx and the column partials), bytes */
+#define TFB_PROF_GELU_FWD 7   /* GELU forward, bytes */
+#define TFB_PROF_GELU_BWD 8   /* GELU backward, bytes */
+#define TFB_PROF_GEMV 9       /* products of at most 16 rows (the decode Linears), bytes */
+#define TFB_PROF_KV_ATTEND 10 /* cached single-query attention, bytes */
+#define TFB_PROF_SAMPLE 11    /* top-k / temperature sampler, bytes */
+#define TFB_PROF_KINDS 12
 int tfb_profile_begin(tfb_ctx* ctx);
 int tfb_profile_end(tfb_ctx* ctx, double* gemm_ms, double* gemm_flops, int* launches);
+/* After tfb_profile_end: summed milliseconds, work and launches of one family
+ * (TFB_ERR_ARG for an unknown kind, TFB_ERR_STATE while profiling runs). */
+int tfb_profile_kind(tfb_ctx* ctx, int kind, double* ms, double* work, int* launches);
 
 #ifdef __cplusplus
 }

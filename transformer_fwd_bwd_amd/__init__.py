@@ -23,6 +23,11 @@ _PREC = {"fp32": FP32, "bf16": BF16_MFMA, FP32: FP32, BF16_MFMA: BF16_MFMA}
 
 _lib = None
 
+# kernel families timed by Context.profile_* (TFB_PROF_* in tfb.h): name -> (id, unit of work)
+PROF_KINDS = {"gemm": 0, "attn_fwd": 1, "attn_bwd": 2, "ce": 3, "adamw": 4, "ln_fwd": 5, "ln_bwd": 6, "gelu_fwd": 7,
+              "gelu_bwd": 8, "gemv": 9, "kv_attend": 10, "sample": 11}
+PROF_UNIT = {"gemm": "flop", "attn_fwd": "flop", "attn_bwd": "flop"}  # the others: bytes
+
 c_int, c_int32, c_int64, c_float = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 c_void_p, c_size_t = ctypes.c_void_p, ctypes.c_size_t
 P = ctypes.POINTER
@@ -84,6 +89,7 @@ SIGNATURES = {
     "tfb_sample_topk": [c_void_p, c_int32, c_int, c_float, c_void_p, c_void_p],
     "tfb_profile_begin": [c_void_p],
     "tfb_profile_end": [c_void_p, P(ctypes.c_double), P(ctypes.c_double), P(c_int)],
+    "tfb_profile_kind": [c_void_p, c_int, P(ctypes.c_double), P(ctypes.c_double), P(c_int)],
 }
 
 
@@ -258,6 +264,21 @@ class Context:
         ms, fl, n = ctypes.c_double(), ctypes.c_double(), c_int()
         _check(_lib.tfb_profile_end(self.ptr, ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(n)))
         return ms.value, fl.value, n.value
+
+    def profile_kind(self, kind: int):
+        """(ms, algorithmic work, launches) of one kernel family (PROF_*) after profile_end."""
+        ms, w, n = ctypes.c_double(), ctypes.c_double(), c_int()
+        _check(_lib.tfb_profile_kind(self.ptr, int(kind), ctypes.byref(ms), ctypes.byref(w), ctypes.byref(n)))
+        return ms.value, w.value, n.value
+
+    def profile_families(self):
+        """{family name: (ms, work, launches)} for every family with launches, after profile_end."""
+        out = {}
+        for name, k in PROF_KINDS.items():
+            r = self.profile_kind(k)
+            if r[2]:
+                out[name] = r
+        return out
 
     def tape_reset(self):
         _check(_lib.tfb_tape_reset(self.ptr))

@@ -185,12 +185,20 @@ struct Arena {
 
 }  // namespace
 
+// Launch timing by kernel family (tfb_profile_*): each bracketed launch gets an
+// event pair on the context's stream and adds its algorithmic work (flops or
+// bytes, per TFB_PROF_*) to its family.
 struct ProfileState {
   bool on = false;
   std::vector<hipEvent_t> pool;
   int used = 0;
-  double flops = 0.0;
-  int launches = 0;
+  struct Span {
+    int ev, kind;
+    double work;
+  };
+  std::vector<Span> spans;
+  double ms[TFB_PROF_KINDS] = {0}, work[TFB_PROF_KINDS] = {0};
+  int launches[TFB_PROF_KINDS] = {0};
 };
 
 struct tfb_ctx {
@@ -249,6 +257,27 @@ struct Ctx {
     return c->tensors[h];
   }
   hipStream_t s() const { return c->stream; }
+
+  // Bracket the launches made by f() with events when profiling is on, counting
+  // `work` (flops or bytes: TFB_PROF_*) for family `kind`.
+  template <typename F>
+  void timed(int kind, double work, F&& f) {
+    ProfileState& pf = c->prof;
+    if (!pf.on) {
+      f();
+      return;
+    }
+    while ((int)pf.pool.size() < pf.used + 2) {
+      hipEvent_t e;
+      hip_check(hipEventCreate(&e), "hipEventCreate");
+      pf.pool.push_back(e);
+    }
+    hip_check(hipEventRecord(pf.pool[pf.used], s()), "hipEventRecord");
+    f();
+    hip_check(hipEventRecord(pf.pool[pf.used + 1], s()), "hipEventRecord");
+    pf.spans.push_back({pf.used, kind, work});
+    pf.used += 2;
+  }
 
   int new_handle() {
     if (!c->free_handles.empty()) {
@@ -605,23 +634,22 @@ struct Ctx {
     size_t ws = gemm_workspace_bytes(g);
     size_t mark = c->arena.hi;
     void* w = ws ? c->arena.alloc_step(ws) : nullptr;
-    ProfileState& pf = c->prof;
-    if (pf.on) {
-      while ((int)pf.pool.size() < pf.used + 2) {
-        hipEvent_t e;
-        hip_check(hipEventCreate(&e), "hipEventCreate");
-        pf.pool.push_back(e);
-      }
-      hip_check(hipEventRecord(pf.pool[pf.used], s()), "hipEventRecord");
-    }
-    hip_check(gemm(g, w, ws, s()), "gemm launch");
-    if (pf.on) {
-      hip_check(hipEventRecord(pf.pool[pf.used + 1], s()), "hipEventRecord");
-      pf.used += 2;
-      pf.flops += needed_flops(g);
-      pf.launches += 1;
-    }
+    // a product of at most 16 rows is a weight stream (the decode Linears): bytes
+    const bool few = g.M <= 16 && g.batch == 1;
+    const double work = few ? gemv_bytes(g) : needed_flops(g);
+    timed(few ? TFB_PROF_GEMV : TFB_PROF_GEMM, work, [&] { hip_check(gemm(g, w, ws, s()), "gemm launch"); });
     c->arena.hi = mark;  // scratch: later work on the same stream runs after this gemm
+  }
+
+  // bytes a few-row product must move: its operands once, its output once
+  static double gemv_bytes(const GemmArgs& g) {
+    const double ea = g.a_bf16 ? 2 : 4, eb = g.b_bf16 ? 2 : 4;
+    double b = ea * g.M * (double)g.K + eb * (double)g.K * g.N;
+    b += (g.c_bf16_only ? 2.0 : 4.0 + (g.Cbf ? 2.0 : 0.0)) * g.M * (double)g.N;
+    if (g.bias) b += 4.0 * g.N;
+    if (g.resid) b += 4.0 * g.M * (double)g.N;
+    if (g.beta != 0.f) b += 4.0 * g.M * (double)g.N;
+    return b;
   }
 
   // multiply-adds the contraction must do, x2; a causal product needs only the
@@ -793,9 +821,12 @@ void backward_rec(Ctx& C, const Rec& r) {
             (!a.f32_valid || (reinterpret_cast<uintptr_t>(a.data) & 15) == 0)) {
           bool written = false;
           ReduceJob job;
-          hip_check(gelu_bwd_cols(g, a.f32_valid ? a.data : nullptr, nullptr, db, 0.f, a.rows(), a.cols(), dcol, ws, s,
-                                  &written, a.f32_valid ? nullptr : a.bf, gb, &job),
-                    "gelu bwd");
+          const double bytes = (double)a.numel * ((gb ? 2 : 4) + (a.f32_valid ? 4 : 2) + 2);
+          C.timed(TFB_PROF_GELU_BWD, bytes, [&] {
+            hip_check(gelu_bwd_cols(g, a.f32_valid ? a.data : nullptr, nullptr, db, 0.f, a.rows(), a.cols(), dcol, ws,
+                                    s, &written, a.f32_valid ? nullptr : a.bf, gb, &job),
+                      "gelu bwd");
+          });
           C.defer_reduce(job);
           a.gstate = G_BF16;
           a.gbf_valid = true;
@@ -816,13 +847,20 @@ void backward_rec(Ctx& C, const Rec& r) {
         const bool abf = !a.f32_valid && gelu_bwd_cols_fits(g, a.bf, da.first, db, a.rows(), a.cols(), ws);
         bool written = false;
         ReduceJob job;
-        hip_check(gelu_bwd_cols(g, abf ? nullptr : C.f32(a), da.first, db, da.second, a.rows(), a.cols(), dcol, ws,
-                                s, &written, abf ? a.bf : nullptr, nullptr, &job),
-                  "gelu bwd");
+        const float* xa = abf ? nullptr : C.f32(a);
+        const double bytes = (double)a.numel * (4 + (abf ? 2 : 4) + 4 + (da.second != 0.f ? 4 : 0) + (db ? 2 : 0));
+        C.timed(TFB_PROF_GELU_BWD, bytes, [&] {
+          hip_check(gelu_bwd_cols(g, xa, da.first, db, da.second, a.rows(), a.cols(), dcol, ws, s, &written,
+                                  abf ? a.bf : nullptr, nullptr, &job),
+                    "gelu bwd");
+        });
         C.defer_reduce(job);
         a.gcol_valid = written;
       } else {
-        hip_check(gelu_bwd(g, C.f32(a), da.first, db, da.second, out.numel, s), "gelu bwd");
+        const float* xa = C.f32(a);
+        const double bytes = (double)out.numel * (4 + 4 + 4 + (da.second != 0.f ? 4 : 0) + (db ? 2 : 0));
+        C.timed(TFB_PROF_GELU_BWD, bytes,
+                [&] { hip_check(gelu_bwd(g, xa, da.first, db, da.second, out.numel, s), "gelu bwd"); });
       }
       if (db) a.gbf_valid = true;
       break;
@@ -906,10 +944,15 @@ void backward_rec(Ctx& C, const Rec& r) {
         gb = nullptr;
       }
       ReduceJob job;
-      hip_check(layernorm_bwd(g, x.data, gm.data, static_cast<float*>(r.s0), static_cast<float*>(r.s1), dx.dst,
-                              dx.src, dxb, dg.first, db.first, rows, Cc, dx.beta, dg.second, db.second, ws, s, dxs,
-                              &summed, gb, &job),
-                "layernorm bwd");
+      // g, x, dx (and the earlier dx it adds to), its bf16 copy, the row statistics
+      const double bytes = (double)rows * Cc * ((gb ? 2 : 4) + 4 + 4 + ((dx.src || dx.beta != 0.f) ? 4 : 0) +
+                                                (dxb ? 2 : 0)) + 8.0 * rows;
+      C.timed(TFB_PROF_LN_BWD, bytes, [&] {
+        hip_check(layernorm_bwd(g, x.data, gm.data, static_cast<float*>(r.s0), static_cast<float*>(r.s1), dx.dst,
+                                dx.src, dxb, dg.first, db.first, rows, Cc, dx.beta, dg.second, db.second, ws, s, dxs,
+                                &summed, gb, &job),
+                  "layernorm bwd");
+      });
       C.defer_reduce(job);
       if (dxb) x.gbf_valid = true;
       x.gcol_valid = summed;
@@ -1010,10 +1053,14 @@ void backward_rec(Ctx& C, const Rec& r) {
                           qkv.cols() % 4 == 0 && C.grad_read_as_bf16(qkv);
         size_t mark = C.c->arena.hi;
         float* D = static_cast<float*>(C.scratch((size_t)B * H * T * sizeof(float)));
-        hip_check(flash_attention_bwd(qb, yf, dyf, dyb, static_cast<const float*>(r.s1), D,
-                                      only ? nullptr : dq.first, dqb, dq.second, (int)B, (int)T, (int)H, (int)Cc,
-                                      scale, s, out.bf),
-                  "attention bwd");
+        // the method's four backward products over the causal triangle
+        const double flops = 4.0 * 2.0 * hs * (T * (T + 1.0) / 2.0) * B * H;
+        C.timed(TFB_PROF_ATTN_BWD, flops, [&] {
+          hip_check(flash_attention_bwd(qb, yf, dyf, dyb, static_cast<const float*>(r.s1), D,
+                                        only ? nullptr : dq.first, dqb, dq.second, (int)B, (int)T, (int)H, (int)Cc,
+                                        scale, s, out.bf),
+                    "attention bwd");
+        });
         C.c->arena.hi = mark;
         qkv.gbf_valid = true;
         if (only) qkv.gstate = G_BF16;
@@ -1078,20 +1125,28 @@ void backward_rec(Ctx& C, const Rec& r) {
         // the logits' only gradient, read by their producer as bf16: that copy alone
         // (written by the forward already when r.i1 == 1: then only for g != 1)
         uint16_t* dlb = C.twin_grad(lg);
-        hip_check(softmax_ce_bwd(lgd, lg.stride(), static_cast<const int32_t*>(r.s0),
-                                 static_cast<const float*>(r.s1), g, nullptr, dlb, lg.rows(), lg.cols(), 0.f, s,
-                                 r.i1 == 1, lgb),
-                  "softmax_ce bwd");
+        // when the forward wrote the gradient this launch only checks g == 1 on the device
+        const double bytes = r.i1 == 1 ? 0.0 : (double)lg.rows() * lg.cols() * ((lgb ? 2 : 4) + 2);
+        C.timed(TFB_PROF_CE, bytes, [&] {
+          hip_check(softmax_ce_bwd(lgd, lg.stride(), static_cast<const int32_t*>(r.s0),
+                                   static_cast<const float*>(r.s1), g, nullptr, dlb, lg.rows(), lg.cols(), 0.f, s,
+                                   r.i1 == 1, lgb),
+                    "softmax_ce bwd");
+        });
         lg.gstate = G_BF16;
         lg.gbf_valid = true;
         break;
       }
       auto dl = C.gdst(r.in[0]);
       uint16_t* dlb = C.twin_grad(lg);
-      hip_check(softmax_ce_bwd(lgd, lg.stride(), static_cast<const int32_t*>(r.s0),
-                               static_cast<const float*>(r.s1), g, dl.first, dlb, lg.rows(), lg.cols(), dl.second, s,
-                               false, lgb),
-                "softmax_ce bwd");
+      const double bytes = (double)lg.rows() * lg.cols() *
+                           ((lgb ? 2 : 4) + 4 + (dl.second != 0.f ? 4 : 0) + (dlb ? 2 : 0));
+      C.timed(TFB_PROF_CE, bytes, [&] {
+        hip_check(softmax_ce_bwd(lgd, lg.stride(), static_cast<const int32_t*>(r.s0),
+                                 static_cast<const float*>(r.s1), g, dl.first, dlb, lg.rows(), lg.cols(), dl.second,
+                                 s, false, lgb),
+                  "softmax_ce bwd");
+      });
       if (dlb) lg.gbf_valid = true;
       break;
     }
@@ -1420,10 +1475,14 @@ int tfb_gelu_ex(tfb_ctx* ctx, tfb_tensor a, int flags, tfb_tensor* y) {
     uint16_t* yb = C.twin_data(ctx->tensors[h]);
     const bool only = yb && (flags & TFB_OUT_BF16_ONLY);
     float* yd = only ? nullptr : ctx->tensors[h].data;
-    if (!ctx->tensors[a].f32_valid)
-      hip_check(gelu_fwd_bf(ctx->tensors[a].bf, yd, yb, ctx->tensors[h].numel, C.s()), "gelu");
-    else
-      hip_check(gelu_fwd(ctx->tensors[a].data, yd, yb, ctx->tensors[h].numel, C.s()), "gelu");
+    const bool abf = !ctx->tensors[a].f32_valid;
+    const double bytes = (double)ctx->tensors[h].numel * ((abf ? 2 : 4) + (yd ? 4 : 0) + (yb ? 2 : 0));
+    C.timed(TFB_PROF_GELU_FWD, bytes, [&] {
+      if (abf)
+        hip_check(gelu_fwd_bf(ctx->tensors[a].bf, yd, yb, ctx->tensors[h].numel, C.s()), "gelu");
+      else
+        hip_check(gelu_fwd(ctx->tensors[a].data, yd, yb, ctx->tensors[h].numel, C.s()), "gelu");
+    });
     if (yb) ctx->tensors[h].bf_valid = true;
     if (only) ctx->tensors[h].f32_valid = false, ctx->tensors[h].bf16_out = true;
     Rec r{OP_GELU};
@@ -1550,9 +1609,12 @@ int tfb_layernorm_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor be
     float* rstd = static_cast<float*>(C.scratch((size_t)rows * sizeof(float)));
     uint16_t* yb = C.twin_data(ctx->tensors[h]);
     const bool only = yb && (flags & TFB_OUT_BF16_ONLY);
-    hip_check(layernorm_fwd(ctx->tensors[x].data, ctx->tensors[gamma].data, ctx->tensors[beta].data,
-                            only ? nullptr : ctx->tensors[h].data, yb, mean, rstd, rows, Cc, eps, C.s()),
-              "layernorm");
+    const double bytes = (double)rows * Cc * (4 + (only ? 0 : 4) + (yb ? 2 : 0)) + 8.0 * rows;
+    C.timed(TFB_PROF_LN_FWD, bytes, [&] {
+      hip_check(layernorm_fwd(ctx->tensors[x].data, ctx->tensors[gamma].data, ctx->tensors[beta].data,
+                              only ? nullptr : ctx->tensors[h].data, yb, mean, rstd, rows, Cc, eps, C.s()),
+                "layernorm");
+    });
     if (yb) ctx->tensors[h].bf_valid = true;
     if (only) ctx->tensors[h].f32_valid = false, ctx->tensors[h].bf16_out = true;
     Rec r{OP_LAYERNORM};
@@ -1725,9 +1787,13 @@ int tfb_causal_attention_ex(tfb_ctx* ctx, tfb_tensor qkv, int heads, int flags, 
       float* lse = static_cast<float*>(C.scratch((size_t)B * H * T * sizeof(float)));
       uint16_t* yb = C.twin_data(ctx->tensors[h]);
       const bool only = yb && (flags & TFB_OUT_BF16_ONLY);
-      hip_check(flash_attention_fwd(qb, only ? nullptr : ctx->tensors[h].data, yb, lse, (int)B, (int)T, (int)H, (int)Cc,
-                                    scale, C.s()),
-                "attention");
+      // QK^T and PV over the causal triangle
+      const double flops = 2.0 * 2.0 * hs * (T * (T + 1.0) / 2.0) * B * H;
+      C.timed(TFB_PROF_ATTN_FWD, flops, [&] {
+        hip_check(flash_attention_fwd(qb, only ? nullptr : ctx->tensors[h].data, yb, lse, (int)B, (int)T, (int)H,
+                                      (int)Cc, scale, C.s()),
+                  "attention");
+      });
       ctx->tensors[h].bf_valid = true;
       if (only) ctx->tensors[h].f32_valid = false, ctx->tensors[h].bf16_out = true;
       Rec r{OP_ATTENTION};
@@ -1801,9 +1867,13 @@ int tfb_softmax_cross_entropy_ex(tfb_ctx* ctx, tfb_tensor logits, const int32_t*
     TensorRec& LG = ctx->tensors[logits];
     const bool lbf = !LG.f32_valid && softmax_ce_bf16_fits(LG.stride(), V, LG.bf);
     if (!lbf) C.f32(LG);
-    hip_check(softmax_ce_fwd(lbf ? nullptr : LG.data, LG.stride(), tg, rows, V, lse, ctx->tensors[h].data, ws, C.s(),
-                             pre, &pre_written, lbf ? LG.bf : nullptr),
-              "softmax_ce");
+    // the logits once, and the fused gradient where it is written in the same pass
+    const double bytes = (double)rows * V * ((lbf ? 2 : 4) + (pre ? 2 : 0));
+    C.timed(TFB_PROF_CE, bytes, [&] {
+      hip_check(softmax_ce_fwd(lbf ? nullptr : LG.data, LG.stride(), tg, rows, V, lse, ctx->tensors[h].data, ws,
+                               C.s(), pre, &pre_written, lbf ? LG.bf : nullptr),
+                "softmax_ce");
+    });
     ctx->arena.hi = mark;
     Rec r{OP_SOFTMAX_CE};
     r.in[0] = logits, r.out = h;
@@ -1965,14 +2035,19 @@ int tfb_adamw_step(tfb_opt* o) {
       o->uploaded_active = active;
       o->uploaded_shadows = shadows;
     }
+    // per element: read p, g, m, v; write p, m, v; and the bf16 copy of p where one is kept
+    double bytes = 0.0;
     for (int i : active) {
       TensorRec& t = C.T(o->params[i]);
       t.bf_valid = t.bf != nullptr;
+      bytes += (double)t.numel * (28 + (t.bf ? 2 : 0));
     }
     (void)ctx;
-    hip_check(adamw_step(o->d_segs, o->d_chunks, o->nchunks, o->chunk_elems, o->lr, o->b1, o->b2, o->eps, bc1, bc2,
-                         C.s()),
-              "adamw");
+    C.timed(TFB_PROF_ADAMW, bytes, [&] {
+      hip_check(adamw_step(o->d_segs, o->d_chunks, o->nchunks, o->chunk_elems, o->lr, o->b1, o->b2, o->eps, bc1, bc2,
+                           C.s()),
+                "adamw");
+    });
   });
 }
 
@@ -2004,8 +2079,8 @@ int tfb_profile_begin(tfb_ctx* ctx) {
     ProfileState& pf = ctx->prof;
     pf.on = true;
     pf.used = 0;
-    pf.flops = 0.0;
-    pf.launches = 0;
+    pf.spans.clear();
+    for (int k = 0; k < TFB_PROF_KINDS; ++k) pf.ms[k] = pf.work[k] = 0.0, pf.launches[k] = 0;
   });
 }
 
@@ -2016,15 +2091,29 @@ int tfb_profile_end(tfb_ctx* ctx, double* gemm_ms, double* gemm_flops, int* laun
     need(pf.on, TFB_ERR_STATE, "profiling was not started");
     pf.on = false;
     hip_check(hipStreamSynchronize(C.s()), "sync");
-    double ms = 0.0;
-    for (int i = 0; i + 1 < pf.used; i += 2) {
+    for (const ProfileState::Span& sp : pf.spans) {
       float e = 0.f;
-      hip_check(hipEventElapsedTime(&e, pf.pool[i], pf.pool[i + 1]), "hipEventElapsedTime");
-      ms += e;
+      hip_check(hipEventElapsedTime(&e, pf.pool[sp.ev], pf.pool[sp.ev + 1]), "hipEventElapsedTime");
+      pf.ms[sp.kind] += e;
+      pf.work[sp.kind] += sp.work;
+      pf.launches[sp.kind] += 1;
     }
-    if (gemm_ms) *gemm_ms = ms;
-    if (gemm_flops) *gemm_flops = pf.flops;
-    if (launches) *launches = pf.launches;
+    pf.spans.clear();
+    if (gemm_ms) *gemm_ms = pf.ms[TFB_PROF_GEMM];
+    if (gemm_flops) *gemm_flops = pf.work[TFB_PROF_GEMM];
+    if (launches) *launches = pf.launches[TFB_PROF_GEMM];
+  });
+}
+
+int tfb_profile_kind(tfb_ctx* ctx, int kind, double* ms, double* work, int* launches) {
+  return guarded([&] {
+    need(ctx != nullptr, TFB_ERR_ARG, "null context");
+    need(kind >= 0 && kind < TFB_PROF_KINDS, TFB_ERR_ARG, "unknown profile kind");
+    const ProfileState& pf = ctx->prof;
+    need(!pf.on, TFB_ERR_STATE, "profiling still running: call tfb_profile_end first");
+    if (ms) *ms = pf.ms[kind];
+    if (work) *work = pf.work[kind];
+    if (launches) *launches = pf.launches[kind];
   });
 }
 
@@ -2085,9 +2174,13 @@ int tfb_kv_attend(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos, 
     const float* qd = Q.data;
     int h = C.make_output({kv->batch, 1, Cc});
     void* ws = C.scratch(std::max<size_t>(kv_attend_workspace_bytes(kv->batch, Cc, heads, pos), 256));
-    hip_check(
-        kv_attend(qd, kv->data, ctx->tensors[h].data, layer, kv->batch, kv->tmax, Cc, heads, pos, scale, ws, C.s()),
-        "kv_attend");
+    // every cached key and value of positions 0..pos (fp32), the new one stored, q read, y written
+    const double bytes = (double)kv->batch * Cc * (8.0 * (pos + 1) + 8.0 + 4.0 + 4.0);
+    C.timed(TFB_PROF_KV_ATTEND, bytes, [&] {
+      hip_check(
+          kv_attend(qd, kv->data, ctx->tensors[h].data, layer, kv->batch, kv->tmax, Cc, heads, pos, scale, ws, C.s()),
+          "kv_attend");
+    });
     *y = h;  // inference only: not recorded on the tape
   });
 }
@@ -2102,9 +2195,12 @@ int tfb_sample_topk(tfb_ctx* ctx, tfb_tensor logits, int k, float temperature, c
     need(k >= 0, TFB_ERR_ARG, "k must be >= 0");
     need(L.cols() > 0, TFB_ERR_SHAPE, "logits rows are empty");
     need(L.cols() < (1LL << 31) && L.rows() < 65536, TFB_ERR_SHAPE, "logits too large");
-    hip_check(sample_topk(C.f32(L), L.stride(), (int)L.rows(), (int)L.cols(), k, temperature, dev_uniforms, dev_out,
-                          C.s()),
-              "sample_topk");
+    const float* ld = C.f32(L);
+    C.timed(TFB_PROF_SAMPLE, 4.0 * L.rows() * L.cols(), [&] {
+      hip_check(sample_topk(ld, L.stride(), (int)L.rows(), (int)L.cols(), k, temperature, dev_uniforms, dev_out,
+                            C.s()),
+                "sample_topk");
+    });
   });
 }
 
