@@ -251,6 +251,24 @@ int tfb_softmax_cross_entropy(tfb_ctx* ctx, tfb_tensor logits, const int32_t* de
 int tfb_softmax_cross_entropy_ex(tfb_ctx* ctx, tfb_tensor logits, const int32_t* dev_targets, int64_t n, int flags,
                                  tfb_tensor* loss);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * of tfb_softmax_cross_entropy on plain device pointers, with no context and no
+ * arena.  dev_loss[0] = mean over the rows of -log(max(softmax(row)[target],
+ * 1e-30)) -- the same kernels and the same value as tfb_softmax_cross_entropy's
+ * loss for fp32 logits.  dev_logits: rows x cols fp32 at a row stride of ld >=
+ * cols floats; dev_targets: rows int32 in [0, cols) (an id outside gives a NaN
+ * loss, never an access outside the row); all three device pointers are the
+ * caller's.  Enqueued on hip_stream (a hipStream_t, NULL = the null stream) of
+ * the current device.  Its scratch (2 * rows floats) is a fixed array on each
+ * GPU the library runs on, held until the process ends: rows above
+ * TFB_NOALLOC_MAX_ROWS give TFB_ERR_SHAPE, and calls that overlap on one GPU
+ * (other streams or threads) race on it.  Calls no allocating routine.
+ * Errors: TFB_ERR_ARG (null pointer), TFB_ERR_SHAPE (sizes), TFB_ERR_HIP. */
+#define TFB_NOALLOC_MAX_ROWS 65536
+int tfb_softmax_cross_entropy_noalloc(const float* dev_logits, int64_t ld, const int32_t* dev_targets, int64_t rows,
+                                      int64_t cols, float* dev_loss, void* hip_stream);
+
 /* ---------------------------------------------------------------- autograd */
 
 /* [Autograd-1, "How each op records itself in the graph"]: loss must have one

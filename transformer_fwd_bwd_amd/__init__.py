@@ -73,6 +73,7 @@ SIGNATURES = {
     "tfb_causal_attention_ex": [c_void_p, c_int32, c_int, c_int32, P(c_int32)],
     "tfb_softmax_cross_entropy": [c_void_p, c_int32, c_void_p, c_int64, P(c_int32)],
     "tfb_softmax_cross_entropy_ex": [c_void_p, c_int32, c_void_p, c_int64, c_int32, P(c_int32)],
+    "tfb_softmax_cross_entropy_noalloc": [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_void_p, c_void_p],
     "tfb_backward": [c_void_p, c_int32],
     "tfb_zero_grad": [c_void_p, P(c_int32), c_int],
     "tfb_tape_reset": [c_void_p],

@@ -17,7 +17,7 @@ OUT = os.path.join(HERE, "libtfb.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["gemm.hip", "gemv.hip", "attention.hip", "elementwise.hip", "rowops.hip", "embedding.hip", "optim.hip",
-           "decode.hip", "tfb_runtime.cpp"]
+           "decode.hip", "noalloc.hip", "tfb_runtime.cpp"]
 
 ARCH = "gfx950"
 # packed fp32 instructions are kept out of generated code on purpose

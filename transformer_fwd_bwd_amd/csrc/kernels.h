@@ -236,4 +236,7 @@ hipError_t adamw_step(const AdamSeg* segs, const AdamChunk* chunks, int nchunks,
                       float b1, float b2, float eps, float bc1, float bc2, hipStream_t s);
 hipError_t sgd_step(float* p, const float* g, float lr, int64_t n, hipStream_t s);
 
+// ---- runtime (tfb_runtime.cpp): sets the calling thread's tfb_last_error text, returns code
+int set_last_error(int code, const char* msg);
+
 }  // namespace tfb

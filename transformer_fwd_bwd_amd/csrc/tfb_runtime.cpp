@@ -1162,6 +1162,13 @@ void backward_rec(Ctx& C, const Rec& r) {
 }  // namespace
 
 // ==================================================================== C ABI
+// for entry points defined in other sources (noalloc.hip): record the calling
+// thread's error text and return the code
+int tfb::set_last_error(int code, const char* msg) {
+  g_last_error = msg ? msg : "";
+  return code;
+}
+
 extern "C" {
 
 const char* tfb_last_error(void) { return g_last_error.c_str(); }
