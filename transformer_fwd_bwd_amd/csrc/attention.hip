@@ -636,9 +636,9 @@ hipError_t flash_attention_fwd(const uint16_t* qkv, float* y, uint16_t* ybf, flo
   const dim3 fgrid((unsigned)(((T + FQ - 1) / FQ) * ((B * H + 7) / 8 * 8)));
   const int hs = C / H;
   if (hs == 64)
-    hipLaunchKernelGGL(attn_fwd_k<64>, fgrid, dim3(NT), 0, s, a);
+    run_kernel(attn_fwd_k<64>, fgrid, dim3(NT), 0, s, a);
   else if (hs == 32)
-    hipLaunchKernelGGL(attn_fwd_k<32>, fgrid, dim3(NT), 0, s, a);
+    run_kernel(attn_fwd_k<32>, fgrid, dim3(NT), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -658,11 +658,11 @@ hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float*
   const int hs = C / H;
   dim3 grid(attn_grid(T, B * H));
   if (hs == 64) {
-    hipLaunchKernelGGL(attn_dq_k<64>, grid, dim3(NT), 0, s, a);
-    hipLaunchKernelGGL(attn_dkv_k<64>, grid, dim3(NT), 0, s, a);
+    run_kernel(attn_dq_k<64>, grid, dim3(NT), 0, s, a);
+    run_kernel(attn_dkv_k<64>, grid, dim3(NT), 0, s, a);
   } else if (hs == 32) {
-    hipLaunchKernelGGL(attn_dq_k<32>, grid, dim3(NT), 0, s, a);
-    hipLaunchKernelGGL(attn_dkv_k<32>, grid, dim3(NT), 0, s, a);
+    run_kernel(attn_dq_k<32>, grid, dim3(NT), 0, s, a);
+    run_kernel(attn_dkv_k<32>, grid, dim3(NT), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -471,7 +471,7 @@ hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, in
   const int64_t n = (int64_t)B * T * C;
   if (n <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)std::min<int64_t>((n + NT - 1) / NT, 65536);
-  hipLaunchKernelGGL(kv_store_k, dim3(blocks), dim3(NT), 0, s, qkv, T, C, kv, layer, B, Tmax, pos0);
+  run_kernel(kv_store_k, dim3(blocks), dim3(NT), 0, s, qkv, T, C, kv, layer, B, Tmax, pos0);
   return hipGetLastError();
 }
 
@@ -490,7 +490,7 @@ hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, in
                      float scale, void* ws, hipStream_t s) {
   if (!kv_split_ok(C, H) || ws == nullptr) {
     const size_t shmem = ((size_t)Tmax + 4 * 64) * sizeof(float);
-    hipLaunchKernelGGL(kv_attend_k, dim3(B * H), dim3(NT), shmem, s, qkv, kv, y, layer, B, Tmax, C, H, pos, scale);
+    run_kernel(kv_attend_k, dim3(B * H), dim3(NT), shmem, s, qkv, kv, y, layer, B, Tmax, C, H, pos, scale);
     return hipGetLastError();
   }
   const int hs = C / H, S = (pos + KVP) / KVP;  // blocks covering positions 0..pos
@@ -498,16 +498,16 @@ hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, in
   float* pml = pacc + (int64_t)B * H * S * hs;
   const dim3 grid((unsigned)(B * H * S));
   if (hs == 32)
-    hipLaunchKernelGGL(kv_attend_part_k<32>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos, S,
+    run_kernel(kv_attend_part_k<32>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos, S,
                        scale);
   else if (hs == 64)
-    hipLaunchKernelGGL(kv_attend_part_k<64>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos, S,
+    run_kernel(kv_attend_part_k<64>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos, S,
                        scale);
   else
-    hipLaunchKernelGGL(kv_attend_part_k<128>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos,
+    run_kernel(kv_attend_part_k<128>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos,
                        S, scale);
   const int n = B * H * hs;
-  hipLaunchKernelGGL(kv_attend_merge_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pacc, pml, y, B * H, hs, S);
+  run_kernel(kv_attend_merge_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pacc, pml, y, B * H, hs, S);
   return hipGetLastError();
 }
 
@@ -515,9 +515,9 @@ hipError_t sample_topk(const float* logits, int64_t ld, int B, int V, int k, flo
                        int32_t* out, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (V <= SR * SPER)
-    hipLaunchKernelGGL(sample_topk_reg_k, dim3(B), dim3(SR), 0, s, logits, ld, V, k, temperature, u, out);
+    run_kernel(sample_topk_reg_k, dim3(B), dim3(SR), 0, s, logits, ld, V, k, temperature, u, out);
   else
-    hipLaunchKernelGGL(sample_topk_k, dim3(B), dim3(NT), 0, s, logits, ld, V, k, temperature, u, out);
+    run_kernel(sample_topk_k, dim3(B), dim3(NT), 0, s, logits, ld, V, k, temperature, u, out);
   return hipGetLastError();
 }
 

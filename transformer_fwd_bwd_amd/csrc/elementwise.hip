@@ -247,32 +247,32 @@ constexpr int SUM_BLOCKS = 1024;
 
 hipError_t fill(float* p, float v, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, p, v, n);
+  run_kernel(fill_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, p, v, n);
   return hipGetLastError();
 }
 
 hipError_t to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (n % 4 == 0 && aligned16(src) && (reinterpret_cast<uintptr_t>(dst) & 7) == 0)
-    hipLaunchKernelGGL(to_bf16_4_k, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, (const f4*)src, (u16x4*)dst, n / 4);
+    run_kernel(to_bf16_4_k, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, (const f4*)src, (u16x4*)dst, n / 4);
   else
-    hipLaunchKernelGGL(to_bf16_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, src, dst, n);
+    run_kernel(to_bf16_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, src, dst, n);
   return hipGetLastError();
 }
 
 hipError_t add_bcast(const float* a, const float* b, float* y, int64_t n, int64_t nb, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (nb % 4 == 0 && aligned16(a) && aligned16(b) && aligned16(y))
-    hipLaunchKernelGGL(add_bcast4_k, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, (const f4*)a, (const f4*)b, (f4*)y,
+    run_kernel(add_bcast4_k, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, (const f4*)a, (const f4*)b, (f4*)y,
                        n / 4, nb / 4);
   else
-    hipLaunchKernelGGL(add_bcast_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, a, b, y, n, nb);
+    run_kernel(add_bcast_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, a, b, y, n, nb);
   return hipGetLastError();
 }
 
 hipError_t axpby(float* dst, const float* src, float alpha, float beta, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(axpby_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, dst, src, alpha, beta, n);
+  run_kernel(axpby_k, dim3(grid_for(n, 4)), dim3(NT), 0, s, dst, src, alpha, beta, n);
   return hipGetLastError();
 }
 
@@ -282,7 +282,7 @@ hipError_t axpby_batch(const AxpbyJobs& jobs, hipStream_t s) {
   int64_t nmax = 0;
   for (int i = 0; i < jobs.count; ++i) nmax = std::max(nmax, jobs.j[i].n);
   if (nmax <= 0) return hipSuccess;
-  hipLaunchKernelGGL(axpby_batch_k, dim3((unsigned)std::min<int64_t>((nmax + NT - 1) / NT, 64), jobs.count),
+  run_kernel(axpby_batch_k, dim3((unsigned)std::min<int64_t>((nmax + NT - 1) / NT, 64), jobs.count),
                      dim3(NT), 0, s, jobs);
   return hipGetLastError();
 }
@@ -297,14 +297,14 @@ hipError_t copy_pitched(const float* src, int64_t lds, float* dst, int64_t ldd, 
     if (beta != 0.f) v += dst[r * ldd + c];
     dst[r * ldd + c] = v;
   };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
 hipError_t mul_fwd(const float* a, const float* b, float* y, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   auto f = [=] __device__(int64_t i) { y[i] = a[i] * b[i]; };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
@@ -315,21 +315,21 @@ hipError_t mul_bwd(const float* g, const float* other, float* d, float beta, int
     if (beta != 0.f) v += d[i];
     d[i] = v;
   };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
 hipError_t scale_fwd(const float* a, float sc, float* y, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   auto f = [=] __device__(int64_t i) { y[i] = sc * a[i]; };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
 hipError_t tanh_fwd(const float* a, float* y, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   auto f = [=] __device__(int64_t i) { y[i] = tanhf(a[i]); };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
@@ -341,14 +341,14 @@ hipError_t tanh_bwd(const float* g, const float* y, float* d, float beta, int64_
     if (beta != 0.f) v += d[i];
     d[i] = v;
   };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
 hipError_t to_f32(const uint16_t* src, float* dst, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   auto f = [=] __device__(int64_t i) { dst[i] = __uint_as_float((unsigned)src[i] << 16); };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
@@ -365,14 +365,14 @@ hipError_t gelu_fwd_bf(const uint16_t* a, float* y, uint16_t* ybf, int64_t n, hi
       if (y4) y4[i] = o;
       if (b4) b4[i] = u16x4{bf16_bits(o[0]), bf16_bits(o[1]), bf16_bits(o[2]), bf16_bits(o[3])};
     };
-    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
+    run_kernel(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
   } else {
     auto f = [=] __device__(int64_t i) {
       const float o = gelu_f(__uint_as_float((unsigned)a[i] << 16));
       if (y) y[i] = o;
       if (ybf) ybf[i] = bf16_bits(o);
     };
-    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+    run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   }
   return hipGetLastError();
 }
@@ -389,14 +389,14 @@ hipError_t gelu_fwd(const float* a, float* y, uint16_t* ybf, int64_t n, hipStrea
       if (y4) y4[i] = o;  // null: the bf16 copy alone
       if (b4) b4[i] = u16x4{bf16_bits(o[0]), bf16_bits(o[1]), bf16_bits(o[2]), bf16_bits(o[3])};
     };
-    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
+    run_kernel(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
   } else {
     auto f = [=] __device__(int64_t i) {
       const float o = gelu_f(a[i]);
       if (y) y[i] = o;
       if (ybf) ybf[i] = bf16_bits(o);
     };
-    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+    run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   }
   return hipGetLastError();
 }
@@ -416,7 +416,7 @@ hipError_t gelu_bwd(const float* g, const float* x, float* d, uint16_t* dbf, flo
       d4[i] = v;
       if (b4) b4[i] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
     };
-    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
+    run_kernel(map1<decltype(f)>, dim3(grid_for(n / 4, 2)), dim3(NT), 0, s, n / 4, f);
   } else {
     auto f = [=] __device__(int64_t i) {
       float v = g[i] * gelu_grad(x[i]);
@@ -424,7 +424,7 @@ hipError_t gelu_bwd(const float* g, const float* x, float* d, uint16_t* dbf, flo
       d[i] = v;
       if (dbf) dbf[i] = bf16_bits(v);
     };
-    hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+    run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   }
   return hipGetLastError();
 }
@@ -459,7 +459,7 @@ static void stage2(const float* partial, int parts, int64_t cols, float* out, fl
     defer->out[0] = out, defer->beta[0] = beta;
     return;
   }
-  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, parts, cols, out,
+  run_kernel(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0, s, partial, parts, cols, out,
                      beta);
 }
 
@@ -481,7 +481,7 @@ hipError_t gelu_bwd_cols(const float* g, const float* x, float* d, uint16_t* dbf
   auto launch = [&](auto gp, auto xp) {
     using GT = std::remove_const_t<std::remove_pointer_t<decltype(gp)>>;
     using XT = std::remove_const_t<std::remove_pointer_t<decltype(xp)>>;
-    hipLaunchKernelGGL((gelu_bwd_cols4_k<XT, GT>), grid, dim3(NT), 0, s, gp, xp, (f4*)d, (u16x4*)dbf, beta, rows,
+    run_kernel((gelu_bwd_cols4_k<XT, GT>), grid, dim3(NT), 0, s, gp, xp, (f4*)d, (u16x4*)dbf, beta, rows,
                        cols4, rows_per, (f4*)partial);
   };
   if (gbf) {
@@ -508,7 +508,7 @@ hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float 
     if (cols % 4 != 0 || (reinterpret_cast<uintptr_t>(gbf) & 7) != 0 || !aligned16(partial) || rows <= 0)
       return hipErrorInvalidValue;
     const int64_t parts = colsum4_parts(rows), rows_per = (rows + parts - 1) / parts, cols4 = cols / 4;
-    hipLaunchKernelGGL(colsum4_stage1<u16x4>, dim3((unsigned)((cols4 + 63) / 64), (unsigned)parts), dim3(NT), 0, s,
+    run_kernel(colsum4_stage1<u16x4>, dim3((unsigned)((cols4 + 63) / 64), (unsigned)parts), dim3(NT), 0, s,
                        (const u16x4*)gbf, rows, cols4, rows_per, (f4*)partial);
     stage2(partial, (int)parts, cols, out, beta, s, defer);
     return hipGetLastError();
@@ -522,13 +522,13 @@ hipError_t colsum(const float* g, int64_t rows, int64_t cols, float* out, float 
     const int64_t cols4 = cols / 4;
     dim3 g1((unsigned)((cols4 + 63) / 64), (unsigned)parts);
     if (parts == 1 && beta == 0.f && aligned16(out)) {  // few rows (a broadcast add over the batch): one pass
-      hipLaunchKernelGGL(colsum4_stage1<f4>, g1, dim3(NT), 0, s, (const f4*)g, rows, cols4, rows_per, (f4*)out);
+      run_kernel(colsum4_stage1<f4>, g1, dim3(NT), 0, s, (const f4*)g, rows, cols4, rows_per, (f4*)out);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL(colsum4_stage1<f4>, g1, dim3(NT), 0, s, (const f4*)g, rows, cols4, rows_per, (f4*)partial);
+    run_kernel(colsum4_stage1<f4>, g1, dim3(NT), 0, s, (const f4*)g, rows, cols4, rows_per, (f4*)partial);
   } else {
     dim3 g1((unsigned)((cols + NT - 1) / NT), (unsigned)parts);
-    hipLaunchKernelGGL(colsum_stage1, g1, dim3(NT), 0, s, g, rows, cols, rows_per, partial);
+    run_kernel(colsum_stage1, g1, dim3(NT), 0, s, g, rows, cols, rows_per, partial);
   }
   stage2(partial, (int)parts, cols, out, beta, s, defer);
   return hipGetLastError();
@@ -538,8 +538,8 @@ size_t sum_workspace_bytes(int64_t) { return SUM_BLOCKS * sizeof(float); }
 
 hipError_t sum_all(const float* a, int64_t n, float* out, void* ws, hipStream_t s) {
   float* partial = static_cast<float*>(ws);
-  hipLaunchKernelGGL(sum_stage1, dim3(SUM_BLOCKS), dim3(NT), 0, s, a, n, partial);
-  hipLaunchKernelGGL(sum_stage2, dim3(1), dim3(NT), 0, s, partial, SUM_BLOCKS, out);
+  run_kernel(sum_stage1, dim3(SUM_BLOCKS), dim3(NT), 0, s, a, n, partial);
+  run_kernel(sum_stage2, dim3(1), dim3(NT), 0, s, partial, SUM_BLOCKS, out);
   return hipGetLastError();
 }
 
@@ -550,7 +550,7 @@ hipError_t bcast_scalar_bwd(const float* gs, float* d, float beta, int64_t n, hi
     if (beta != 0.f) v += d[i];
     d[i] = v;
   };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
@@ -562,7 +562,7 @@ hipError_t narrow_fwd(const float* x, float* y, int64_t rows, int64_t cols, int6
     const int64_t r = i / len, c = i % len;
     y[i] = x[r * cols + start + c];
   };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
@@ -579,7 +579,7 @@ hipError_t narrow_bwd(const float* g, float* d, int64_t rows, int64_t cols, int6
       d[i] = in ? g[r * len + c - start] : 0.f;
     }
   };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 
@@ -607,7 +607,7 @@ hipError_t permute_heads(const float* x, float* y, int64_t B, int64_t T, int64_t
     if (beta != 0.f) v += y[i];
     y[i] = v;
   };
-  hipLaunchKernelGGL(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
+  run_kernel(map1<decltype(f)>, dim3(grid_for(n, 4)), dim3(NT), 0, s, n, f);
   return hipGetLastError();
 }
 

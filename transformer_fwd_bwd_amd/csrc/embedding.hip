@@ -116,10 +116,10 @@ hipError_t embedding_fwd(const float* table, int64_t rows, const int32_t* ids, f
   if (v4) {
     const int64_t t4 = total / 4;
     unsigned blocks = (unsigned)std::min<int64_t>((t4 + NT - 1) / NT, 65536);
-    hipLaunchKernelGGL(gather4_k, dim3(blocks), dim3(NT), 0, s, (const f4*)table, rows, ids, (f4*)y, n, C / 4);
+    run_kernel(gather4_k, dim3(blocks), dim3(NT), 0, s, (const f4*)table, rows, ids, (f4*)y, n, C / 4);
   } else {
     unsigned blocks = (unsigned)std::min<int64_t>((total + NT - 1) / NT, 65536);
-    hipLaunchKernelGGL(gather_k, dim3(blocks), dim3(NT), 0, s, table, rows, ids, y, n, C);
+    run_kernel(gather_k, dim3(blocks), dim3(NT), 0, s, table, rows, ids, y, n, C);
   }
   return hipGetLastError();
 }
@@ -135,11 +135,11 @@ hipError_t embedding_bwd(const float* g, const int32_t* ids, int64_t n, int64_t 
   if (n > 0x7fffffff) return hipErrorInvalidValue;
   const int64_t chunks = (n + CHUNK - 1) / CHUNK;
   uint64_t* keys = static_cast<uint64_t*>(ws);
-  hipLaunchKernelGGL(sort_chunks_k, dim3((unsigned)chunks), dim3(SORT_THREADS), 0, s, ids, n, keys);
+  run_kernel(sort_chunks_k, dim3((unsigned)chunks), dim3(SORT_THREADS), 0, s, ids, n, keys);
   for (int64_t c = 0; c < chunks; ++c) {
     const int len = (int)std::min<int64_t>(CHUNK, n - c * CHUNK);
     const unsigned blocks = (unsigned)((len + (NT / 64) - 1) / (NT / 64));
-    hipLaunchKernelGGL(segsum_k, dim3(blocks), dim3(NT), 0, s, keys + c * CHUNK, len, g, C, dtable, rows);
+    run_kernel(segsum_k, dim3(blocks), dim3(NT), 0, s, keys + c * CHUNK, len, g, C, dtable, rows);
   }
   return hipGetLastError();
 }

@@ -803,11 +803,11 @@ hipError_t launch_layout(const KArgs& ka, dim3 grid, hipStream_t s) {
   const GemmArgs& g = ka.g;
   dim3 block(WM * WN * 64);
   if (!g.a_mcontig && !g.b_kcontig)
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BK, BF16, false, false, A_BF, B_BF>), grid, block, 0, s, ka);
+    run_kernel((gemm_kernel<WM, WN, TM, TN, BK, BF16, false, false, A_BF, B_BF>), grid, block, 0, s, ka);
   else if (!g.a_mcontig && g.b_kcontig)
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BK, BF16, false, true, A_BF, B_BF>), grid, block, 0, s, ka);
+    run_kernel((gemm_kernel<WM, WN, TM, TN, BK, BF16, false, true, A_BF, B_BF>), grid, block, 0, s, ka);
   else if (g.a_mcontig && !g.b_kcontig)
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BK, BF16, true, false, A_BF, B_BF>), grid, block, 0, s, ka);
+    run_kernel((gemm_kernel<WM, WN, TM, TN, BK, BF16, true, false, A_BF, B_BF>), grid, block, 0, s, ka);
   else
     return hipErrorInvalidValue;  // A^T B^T is never needed
   return hipGetLastError();
@@ -840,12 +840,12 @@ static hipError_t reduce_splits(const GemmArgs& g, const float* ws, int splits, 
                    (reinterpret_cast<uintptr_t>(g.Cbf) & 7) == 0 && (reinterpret_cast<uintptr_t>(g.resid) & 15) == 0;
   if (vec) {
     dim3 rgrid((unsigned)std::min<int64_t>((MN / 4 + 255) / 256, 4096), g.batch);
-    hipLaunchKernelGGL(splitk_reduce4, rgrid, dim3(256), 0, s, reinterpret_cast<const f4*>(ws), splits, g.M,
+    run_kernel(splitk_reduce4, rgrid, dim3(256), 0, s, reinterpret_cast<const f4*>(ws), splits, g.M,
                        g.N / 4, g.C, g.ldc, g.batch_div, g.sc1, g.sc2, g.beta, reinterpret_cast<const f4*>(g.bias),
                        g.Cbf, g.resid, (int)g.c_bf16_only);
   } else {
     dim3 rgrid((unsigned)std::min<int64_t>((MN + 255) / 256, 4096), g.batch);
-    hipLaunchKernelGGL(splitk_reduce, rgrid, dim3(256), 0, s, ws, splits, g.M, g.N, g.C, g.ldc, g.batch_div,
+    run_kernel(splitk_reduce, rgrid, dim3(256), 0, s, ws, splits, g.M, g.N, g.C, g.ldc, g.batch_div,
                        g.sc1, g.sc2, g.beta, g.bias, g.Cbf, g.resid, (int)g.c_bf16_only);
   }
   return hipGetLastError();

@@ -226,7 +226,7 @@ SkPlan plan(const GemmArgs& g) {
 
 template <bool A_BF, bool B_BF, bool RND>
 void launch(const SkArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_k<A_BF, B_BF, RND>), dim3(grid), dim3(ST), 0, s, a);
+  run_kernel((gemv_k<A_BF, B_BF, RND>), dim3(grid), dim3(ST), 0, s, a);
 }
 
 }  // namespace
@@ -258,7 +258,7 @@ bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_
     rnd ? launch<false, false, true>(a, grid, s) : launch<false, false, false>(a, grid, s);
   if (p.chunks > 1) {
     const int n4 = g.M * (g.N / 4);
-    hipLaunchKernelGGL(gemv_reduce_k, dim3((n4 + ST - 1) / ST), dim3(ST), 0, s, a);
+    run_kernel(gemv_reduce_k, dim3((n4 + ST - 1) / ST), dim3(ST), 0, s, a);
   }
   *err = hipGetLastError();
   return true;

@@ -2,12 +2,36 @@
 // kernels.  Every launcher enqueues on the given stream and returns the launch
 // status; shape checks are the runtime's job.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
 
 namespace tfb {
+
+// Kernel timing for the runtime's profiler.  While `stop` is set (per host
+// thread, by the runtime around one family's launches), tfb::run_kernel attaches
+// the events to the dispatches themselves: `start` to the first launch, `stop`
+// to every launch (the last one's end counts), so the elapsed time is that of
+// the kernels alone, without the gaps an event recorded on the stream adds.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  int launches = 0;
+};
+LaunchEvents& launch_events();
+
+template <typename F, typename... Args>
+inline void run_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.launches == 0 ? ev.start : nullptr, ev.stop, 0u,
+                          args...);
+    ev.launches++;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+  }
+}
 
 enum Prec { PREC_F32 = 0, PREC_BF16 = 1 };
 

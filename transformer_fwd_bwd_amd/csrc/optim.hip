@@ -78,14 +78,14 @@ __global__ void sgd_k(float* __restrict__ p, const float* __restrict__ g, float 
 hipError_t adamw_step(const AdamSeg* segs, const AdamChunk* chunks, int nchunks, int64_t chunk_elems, float lr,
                       float b1, float b2, float eps, float bc1, float bc2, hipStream_t s) {
   if (nchunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(adamw_k, dim3(nchunks), dim3(NT), 0, s, segs, chunks, chunk_elems, lr, b1, b2, eps, bc1, bc2);
+  run_kernel(adamw_k, dim3(nchunks), dim3(NT), 0, s, segs, chunks, chunk_elems, lr, b1, b2, eps, bc1, bc2);
   return hipGetLastError();
 }
 
 hipError_t sgd_step(float* p, const float* g, float lr, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)std::min<int64_t>((n + NT - 1) / NT, 65536);
-  hipLaunchKernelGGL(sgd_k, dim3(blocks), dim3(NT), 0, s, p, g, lr, n);
+  run_kernel(sgd_k, dim3(blocks), dim3(NT), 0, s, p, g, lr, n);
   return hipGetLastError();
 }
 

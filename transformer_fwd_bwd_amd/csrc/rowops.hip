@@ -803,19 +803,19 @@ hipError_t layernorm_fwd(const float* x, const float* gamma, const float* beta, 
       (reinterpret_cast<uintptr_t>(ybf) & 7) == 0) {
     const int C4 = (int)(C / 4);
     if (C4 <= 64)
-      hipLaunchKernelGGL(ln_fwd4_k<1>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
+      run_kernel(ln_fwd4_k<1>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
                          (const f4*)beta, (f4*)y, (u16x4*)ybf, mean, rstd, rows, C4, eps);
     else if (C4 <= 192)
-      hipLaunchKernelGGL(ln_fwd4_k<3>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
+      run_kernel(ln_fwd4_k<3>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
                          (const f4*)beta, (f4*)y, (u16x4*)ybf, mean, rstd, rows, C4, eps);
     else
-      hipLaunchKernelGGL(ln_fwd4_k<4>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
+      run_kernel(ln_fwd4_k<4>, dim3(row_blocks(rows)), dim3(NT), 0, s, (const f4*)x, (const f4*)gamma,
                          (const f4*)beta, (f4*)y, (u16x4*)ybf, mean, rstd, rows, C4, eps);
   } else if (C <= 64 * MAXV)
-    hipLaunchKernelGGL(ln_fwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, ybf, mean, rstd, rows,
+    run_kernel(ln_fwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, ybf, mean, rstd, rows,
                        (int)C, eps);
   else
-    hipLaunchKernelGGL(ln_fwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, ybf, mean, rstd, rows,
+    run_kernel(ln_fwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, gamma, beta, y, ybf, mean, rstd, rows,
                        (int)C, eps);
   return hipGetLastError();
 }
@@ -851,23 +851,23 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
       using GT = std::remove_const_t<std::remove_pointer_t<decltype(gp)>>;
       if (dxsum) {
         if (C4 <= 64)
-          hipLaunchKernelGGL((ln_bwd_fused4_k<1, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
+          run_kernel((ln_bwd_fused4_k<1, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
                              (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
         else if (C4 <= 192)
-          hipLaunchKernelGGL((ln_bwd_fused4_k<3, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
+          run_kernel((ln_bwd_fused4_k<3, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
                              (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
         else
-          hipLaunchKernelGGL((ln_bwd_fused4_k<4, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
+          run_kernel((ln_bwd_fused4_k<4, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
                              (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
       } else {
         if (C4 <= 64)
-          hipLaunchKernelGGL((ln_bwd_fused4_k<1, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
+          run_kernel((ln_bwd_fused4_k<1, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
                              (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
         else if (C4 <= 192)
-          hipLaunchKernelGGL((ln_bwd_fused4_k<3, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx,
+          run_kernel((ln_bwd_fused4_k<3, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx,
                              src4, (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
         else
-          hipLaunchKernelGGL((ln_bwd_fused4_k<4, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx,
+          run_kernel((ln_bwd_fused4_k<4, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx,
                              src4, (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
       }
     };
@@ -886,15 +886,15 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
     }
     if (rows > 0) {
       if (C <= 64 * MAXV)
-        hipLaunchKernelGGL(ln_bwd_dx_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
+        run_kernel(ln_bwd_dx_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
                            rows, (int)C, beta_dx);
       else
-        hipLaunchKernelGGL(ln_bwd_dx_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
+        run_kernel(ln_bwd_dx_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, x, gamma, mean, rstd, dx,
                            rows, (int)C, beta_dx);
     }
     parts = ln_bwd_parts(rows);
     const int64_t rows_per = (rows + parts - 1) / parts;
-    hipLaunchKernelGGL(ln_bwd_cols_k, dim3((unsigned)((C + NT - 1) / NT), (unsigned)parts), dim3(NT), 0, s, g, x,
+    run_kernel(ln_bwd_cols_k, dim3((unsigned)((C + NT - 1) / NT), (unsigned)parts), dim3(NT), 0, s, g, x,
                        mean, rstd, part, rows, (int)C, rows_per);
     if (dxbf) {
       const hipError_t e = to_bf16(dx, dxbf, rows * C, s);
@@ -907,7 +907,7 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
     defer->out[0] = dgamma, defer->out[1] = dbeta, defer->out[2] = dxsum;
     defer->beta[0] = beta_dg, defer->beta[1] = beta_db;
   } else {
-    hipLaunchKernelGGL(ln_bwd_reduce, dim3((unsigned)((C + 15) / 16)), dim3(1024), 0, s, part, parts, np, (int)C,
+    run_kernel(ln_bwd_reduce, dim3((unsigned)((C + 15) / 16)), dim3(1024), 0, s, part, parts, np, (int)C,
                        dgamma, dbeta, dxsum, beta_dg, beta_db);
   }
   if (dxsum_written) *dxsum_written = dxsum != nullptr;
@@ -922,16 +922,16 @@ hipError_t reduce_batch(const ReduceJobs& jobs, hipStream_t s) {
     const ReduceJob& j = jobs.j[i];
     blocks = std::max<int64_t>(blocks, j.kind == REDUCE_LN ? (j.cols + 15) / 16 : (j.cols + 63) / 64);
   }
-  hipLaunchKernelGGL(reduce_batch_k, dim3((unsigned)blocks, (unsigned)jobs.count), dim3(1024), 0, s, jobs);
+  run_kernel(reduce_batch_k, dim3((unsigned)blocks, (unsigned)jobs.count), dim3(1024), 0, s, jobs);
   return hipGetLastError();
 }
 
 hipError_t causal_softmax_fwd(const float* x, float* p, int64_t rows, int64_t T, bool full, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (T <= 64 * MAXV)
-    hipLaunchKernelGGL(csm_fwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, p, rows, (int)T, full);
+    run_kernel(csm_fwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, p, rows, (int)T, full);
   else
-    hipLaunchKernelGGL(csm_fwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, p, rows, (int)T, full);
+    run_kernel(csm_fwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, x, p, rows, (int)T, full);
   return hipGetLastError();
 }
 
@@ -939,10 +939,10 @@ hipError_t causal_softmax_bwd(const float* g, const float* p, float* d, int64_t 
                               float beta, bool full, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (T <= 64 * MAXV)
-    hipLaunchKernelGGL(csm_bwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, p, d, rows, (int)T, scale, beta,
+    run_kernel(csm_bwd_k<true>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, p, d, rows, (int)T, scale, beta,
                        full);
   else
-    hipLaunchKernelGGL(csm_bwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, p, d, rows, (int)T, scale, beta,
+    run_kernel(csm_bwd_k<false>, dim3(row_blocks(rows)), dim3(NT), 0, s, g, p, d, rows, (int)T, scale, beta,
                        full);
   return hipGetLastError();
 }
@@ -957,13 +957,13 @@ void launch_ce_fwd_grad(const X* logits, int64_t ld, const int32_t* targets, int
   const float gn = 1.f / (float)rows;  // the backward's g / rows for g = 1
   const dim3 grid((unsigned)rows), block(1024);
   if (per <= 4)
-    hipLaunchKernelGGL((ce_fwd_grad4_k<4, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+    run_kernel((ce_fwd_grad4_k<4, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
   else if (per <= 8)
-    hipLaunchKernelGGL((ce_fwd_grad4_k<8, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+    run_kernel((ce_fwd_grad4_k<8, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
   else if (per <= 13)
-    hipLaunchKernelGGL((ce_fwd_grad4_k<13, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+    run_kernel((ce_fwd_grad4_k<13, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
   else
-    hipLaunchKernelGGL((ce_fwd_grad4_k<16, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
+    run_kernel((ce_fwd_grad4_k<16, X>), grid, block, 0, s, logits, ld, targets, V, lse, loss_rows, dlbf, gn);
 }
 }  // namespace
 
@@ -989,10 +989,10 @@ hipError_t softmax_ce_fwd(const float* logits, int64_t ld, const int32_t* target
     launch_ce_fwd_grad(logits, ld, targets, rows, V, lse, loss_rows, dlbf, s);
     if (dlbf_written) *dlbf_written = true;
   } else if (ld % 4 == 0 && aligned16(logits))
-    hipLaunchKernelGGL(ce_fwd4_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
+    run_kernel(ce_fwd4_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
   else
-    hipLaunchKernelGGL(ce_fwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
-  hipLaunchKernelGGL(mean_k, dim3(1), dim3(NT), 0, s, loss_rows, rows, loss);
+    run_kernel(ce_fwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, V, lse, loss_rows);
+  run_kernel(mean_k, dim3(1), dim3(NT), 0, s, loss_rows, rows, loss);
   return hipGetLastError();
 }
 
@@ -1004,15 +1004,15 @@ hipError_t softmax_ce_bwd(const float* logits, int64_t ld, const int32_t* target
   if (logits_bf) {
     if (!softmax_ce_bf16_fits(ld, V, logits_bf) || !aligned16(dl) || (reinterpret_cast<uintptr_t>(dlbf) & 7) != 0)
       return hipErrorInvalidValue;
-    hipLaunchKernelGGL(ce_bwd4_k<uint16_t>, dim3((unsigned)rows), dim3(NT), 0, s, logits_bf, ld, targets, lse, g_scalar,
+    run_kernel(ce_bwd4_k<uint16_t>, dim3((unsigned)rows), dim3(NT), 0, s, logits_bf, ld, targets, lse, g_scalar,
                        dl, dlbf, rows, V, beta, (int)skip_if_unit);
     return hipGetLastError();
   }
   if (ld % 4 == 0 && aligned16(logits) && aligned16(dl) && (reinterpret_cast<uintptr_t>(dlbf) & 7) == 0)
-    hipLaunchKernelGGL(ce_bwd4_k<float>, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
+    run_kernel(ce_bwd4_k<float>, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
                        rows, V, beta, (int)skip_if_unit);
   else
-    hipLaunchKernelGGL(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
+    run_kernel(ce_bwd_k, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, targets, lse, g_scalar, dl, dlbf,
                        rows, V, beta, (int)skip_if_unit);
   return hipGetLastError();
 }

@@ -272,9 +272,20 @@ struct Ctx {
       hip_check(hipEventCreate(&e), "hipEventCreate");
       pf.pool.push_back(e);
     }
+    // the kernels' own dispatches carry the events (tfb::run_kernel); a launch made
+    // some other way (a copy) falls back to events recorded on the stream around it
     hip_check(hipEventRecord(pf.pool[pf.used], s()), "hipEventRecord");
-    f();
-    hip_check(hipEventRecord(pf.pool[pf.used + 1], s()), "hipEventRecord");
+    LaunchEvents& le = launch_events();
+    le.start = pf.pool[pf.used], le.stop = pf.pool[pf.used + 1], le.launches = 0;
+    try {
+      f();
+    } catch (...) {
+      le = LaunchEvents();
+      throw;
+    }
+    const int n = le.launches;
+    le = LaunchEvents();
+    if (n == 0) hip_check(hipEventRecord(pf.pool[pf.used + 1], s()), "hipEventRecord");
     pf.spans.push_back({pf.used, kind, work});
     pf.used += 2;
   }
@@ -1164,6 +1175,11 @@ void backward_rec(Ctx& C, const Rec& r) {
 // ==================================================================== C ABI
 // for entry points defined in other sources (noalloc.hip): record the calling
 // thread's error text and return the code
+LaunchEvents& tfb::launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+
 int tfb::set_last_error(int code, const char* msg) {
   g_last_error = msg ? msg : "";
   return code;
