@@ -221,3 +221,65 @@ def test_circle_classifier_trains_like_the_oracle(ctx, adam):
     assert np.max(np.abs(got - ref) / np.maximum(ref, 1e-3)) < 2e-2, "loss trajectory"
     if adam:
         assert got[-1] < 0.1 and (pred == ys).mean() > 0.97
+
+
+def test_small_gpt_whole_model_gpu_gradcheck(ctx):
+    """The pages' gradient check applied to a whole small GPT on the GPU ([Autograd-1,
+    "Gradient check"], and its note that the same check runs over a complete small GPT
+    with every layer): every number of every parameter tensor (28, laid out as GPT-2's 148) is
+    moved by +-h = 0.01, the float32 central difference of the GPU's own loss is compared
+    with the analytic gradient, and the norm-wise relative error |a - n| / (|a| + |n|)
+    must stay below 1e-3 per tensor.  The model is small enough for one forward per
+    number (vocab 16, 16 channels, 2 heads, 2 blocks, 8 positions, batch 2: 6,976
+    numbers); its weights are drawn wider than GPT-2's (std 0.2, random LayerNorm gains,
+    shifts and biases) so that a step of h moves the float32 loss by far more than its
+    rounding."""
+    shape = S.GptShape(vocab=16, n_positions=8, n_layer=2, n_head=2, n_embd=16)
+    params = S.gpt_params(shape, 90, std=0.2)
+    rng = S.rng_for(91)
+    for k in params:
+        if params[k].ndim == 1:
+            params[k] = (params[k] + 0.1 * rng.standard_normal(params[k].shape)).astype(np.float32)
+    ids = S.random_ids(92, (2, shape.n_positions + 1), shape.vocab)
+    ctx.set_precision("fp32")
+    model = G.Gpt(ctx, shape.n_layer, shape.n_head, params)
+    inputs, targets = G.split_ids(ids)
+    ctx.zero_grad(model.param_list)
+    loss, _ = model.loss(inputs, targets)
+    ctx.backward(loss)
+    analytic = {k: model.P[k].grad() for k in model.names}
+    ctx.tape_reset()
+    ctx.set_grad_enabled(False)
+    h = np.float32(0.01)
+    worst, worst_k = 0.0, None
+    try:
+        for k in model.names:
+            base = params[k].copy()
+            flat = base.reshape(-1)
+            num = np.zeros(flat.size, np.float32)
+            for i in range(flat.size):
+                old = flat[i]
+                flat[i] = old + h
+                model.P[k].write(base)
+                lp = np.float32(model.loss(inputs, targets)[0].item())
+                ctx.tape_reset()
+                flat[i] = old - h
+                model.P[k].write(base)
+                lm = np.float32(model.loss(inputs, targets)[0].item())
+                ctx.tape_reset()
+                flat[i] = old
+                num[i] = (lp - lm) / (np.float32(2) * h)
+            model.P[k].write(base)
+            a = analytic[k].reshape(-1).astype(np.float64)
+            n = num.astype(np.float64)
+            den = np.linalg.norm(a) + np.linalg.norm(n)
+            rel = np.linalg.norm(a - n) / den if den > 0 else 0.0
+            if rel > worst:
+                worst, worst_k = rel, k
+    finally:
+        ctx.set_grad_enabled(True)
+    print(f"whole-model gradient check: worst relative error {worst:.2e} ({worst_k}) over {len(model.names)} tensors")
+    assert len(model.names) == 4 + 12 * shape.n_layer
+    assert worst < 1e-3, (worst, worst_k)
+    for t in model.param_list:
+        t.release()
