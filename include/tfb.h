@@ -195,6 +195,26 @@ int tfb_linear_residual(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, 
 /* tfb_linear with flags (TFB_OUT_BF16_COPY, TFB_OUT_BF16_ONLY above).
  * [GPT2-4, "Loading the weights": Linear weights stored [in, out]] */
 int tfb_linear_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int flags, tfb_tensor* y);
+/* Inference only (gradients disabled, else TFB_ERR_STATE; nothing is recorded):
+ * y = gelu(x @ w + b), the Linear and the GELU that follows it in GPT-2's MLP, as one
+ * call.  In a product of at most 16 rows (a decode step) the GELU is applied where
+ * the few-row kernel sums its partial products, so no separate pass reads and
+ * writes the product; otherwise it runs as tfb_linear_ex then tfb_gelu_ex.  Flags:
+ * TFB_OUT_BF16_ONLY (y kept as bf16 alone, bf16 variant).
+ * [GPT2-4, "Loading the weights": the MLP c_fc then GELU; "Common mistakes"] */
+int tfb_linear_gelu(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int flags, tfb_tensor* y);
+/* Inference only (as above): y = r + (x @ w + b) and h = LayerNorm(y) with gamma,
+ * beta, eps (biased variance) -- a block's projection with its residual Add and the
+ * LayerNorm that reads the result next (the following block's ln_1, or ln_f), as
+ * one call.  In a product of at most 16 rows the few-row kernel's chunk sum adds
+ * bias and residual and normalises each row; otherwise it runs as
+ * tfb_linear_residual then tfb_layernorm_ex.  y [rows, N] fp32; h the same shape
+ * (TFB_OUT_BF16_ONLY: bf16 alone in the bf16 variant); N <= 2048.
+ * [GPT2-4, "Loading the weights": x = x + attn(ln_1(x)), x = x + mlp(ln_2(x));
+ * Autograd-1, table of ops: LayerNorm] */
+int tfb_linear_residual_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor r,
+                                  tfb_tensor gamma, tfb_tensor beta, float eps, int flags, tfb_tensor* y,
+                                  tfb_tensor* h);
 /* Per row over the last dim: (x - mean)/sqrt(var + eps) * gamma + beta with the
  * biased variance.  [Autograd-1, table of ops: LayerNorm] */
 int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y);

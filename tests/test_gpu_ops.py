@@ -105,6 +105,70 @@ def test_linear_few_rows(ctx, prec, M, K, N):
                                 rnd(133, (M, N))], (M, N))
 
 
+def _infer(ctx, prec, arrays, build):
+    ctx.set_precision(prec)
+    ts = [ctx.tensor(a.shape, a) for a in arrays]
+    ctx.set_grad_enabled(False)
+    try:
+        outs = build(*ts)
+        outs = outs if isinstance(outs, tuple) else (outs,)
+        res = [o.numpy() for o in outs]
+    finally:
+        ctx.set_grad_enabled(True)
+        ctx.tape_reset()
+        for t in ts:
+            t.release()
+        ctx.set_precision("fp32")
+    return res
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("M,K,N", [(16, 768, 3072), (1, 128, 64), (3, 200, 132), (5, 64, 18), (20, 100, 96)])
+def test_linear_gelu_inference(ctx, prec, M, K, N):
+    """[GPT2-4, "Loading the weights": c_fc then GELU] gelu(x @ w + b) as one inference
+    call: the GELU in the few-row kernel's chunk sum (several chunks), in its single-chunk
+    epilogue (K = 128), and through the separate ops where that kernel does not take the
+    product (18 columns; 20 rows)."""
+    arrays = [rnd(170 + M, (M, K)), rnd(171 + K, (K, N), 1 / np.sqrt(K)), rnd(172, (N,), 0.5)]
+    (y,) = _infer(ctx, prec, arrays, lambda x, w, b: T.linear_gelu(x, w, b, bf16_only=True))
+    x, w, b = (a.astype(np.float64) for a in arrays)
+    from oracle import ops as O
+    assert_close(y, O.gelu_fwd(x @ w + b), FWD_TOL[prec], "gelu(x @ w + b)")
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("M,K,N", [(16, 768, 768), (16, 3072, 768), (4, 64, 64), (5, 130, 132), (5, 130, 130),
+                                   (20, 100, 96)])
+def test_linear_residual_layernorm_inference(ctx, prec, M, K, N):
+    """[GPT2-4, "Loading the weights": x = x + proj(.), then the next LayerNorm]
+    y = r + (x @ w + b) and h = LayerNorm(y) as one inference call: normalised in the
+    few-row kernel's chunk sum (6 and 24 chunks; one chunk), and through the separate ops
+    where that kernel does not take the product (130 columns; 20 rows)."""
+    arrays = [rnd(180 + M, (M, K)), rnd(181 + K, (K, N), 1 / np.sqrt(K)), rnd(182, (N,), 0.5), rnd(183, (M, N)),
+              1 + rnd(184, (N,), 0.2), rnd(185, (N,), 0.2)]
+    y, h = _infer(ctx, prec, arrays, lambda x, w, b, r, g, bt: T.linear_residual_layernorm(x, w, b, r, g, bt,
+                                                                                            bf16_only=True))
+    x, w, b, r, g, bt = (a.astype(np.float64) for a in arrays)
+    from oracle import ops as O
+    ry = r + x @ w + b
+    rh = O.layernorm_fwd(ry, g, bt)[0]
+    assert_close(y, ry, FWD_TOL[prec], "y")
+    assert_close(h, rh, FWD_TOL[prec], "LayerNorm(y)")
+
+
+def test_inference_fusions_refuse_to_record(ctx):
+    x, w, b = ctx.tensor((2, 8), np.ones((2, 8), np.float32)), ctx.tensor((8, 8)), ctx.tensor((8,))
+    with pytest.raises(T.TfbError) as e:
+        T.linear_gelu(x, w, b)
+    assert e.value.code == -3 and "inference-only" in str(e.value)
+    with pytest.raises(T.TfbError) as e:
+        T.linear_residual_layernorm(x, w, b, x, b, b)
+    assert e.value.code == -3
+    ctx.tape_reset()
+    for t in (x, w, b):
+        t.release()
+
+
 @pytest.mark.parametrize("prec", PRECS)
 @pytest.mark.parametrize("V", [130, 1030])
 def test_matmul_t_few_rows_accumulating_grad(ctx, prec, V):

@@ -62,6 +62,9 @@ SIGNATURES = {
     "tfb_gelu_ex": [c_void_p, c_int32, c_int32, P(c_int32)],
     "tfb_linear_residual": [c_void_p, c_int32, c_int32, c_int32, c_int32, P(c_int32)],
     "tfb_layernorm": [c_void_p, c_int32, c_int32, c_int32, c_float, P(c_int32)],
+    "tfb_linear_gelu": [c_void_p, c_int32, c_int32, c_int32, c_int32, P(c_int32)],
+    "tfb_linear_residual_layernorm": [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_float,
+                                      c_int32, P(c_int32), P(c_int32)],
     "tfb_embedding": [c_void_p, c_int32, c_void_p, c_int64, c_int64, P(c_int32)],
     "tfb_narrow": [c_void_p, c_int32, c_int64, c_int64, P(c_int32)],
     "tfb_split_heads": [c_void_p, c_int32, c_int, P(c_int32)],
@@ -362,6 +365,24 @@ def layernorm(x: Tensor, gamma: Tensor, beta: Tensor, eps: float = 1e-5, bf16_on
     if bf16_only:
         return _out(x.ctx, _lib.tfb_layernorm_ex, x.h, gamma.h, beta.h, c_float(eps), OUT_BF16_ONLY)
     return _out(x.ctx, _lib.tfb_layernorm, x.h, gamma.h, beta.h, c_float(eps))
+
+
+def linear_gelu(x: Tensor, w: Tensor, b: Tensor, bf16_only: bool = False) -> Tensor:
+    """Inference only: gelu(x @ w + b) as one call (in a product of at most 16 rows the
+    GELU is applied where the partial products are summed)."""
+    return _out(x.ctx, _lib.tfb_linear_gelu, x.h, w.h, b.h, OUT_BF16_ONLY if bf16_only else 0)
+
+
+def linear_residual_layernorm(x: Tensor, w: Tensor, b: Tensor, residual: Tensor, gamma: Tensor, beta: Tensor,
+                              eps: float = 1e-5, bf16_only: bool = False):
+    """Inference only: (y, h) with y = residual + (x @ w + b) and h = LayerNorm(y) as one
+    call (the few-row kernel's chunk sum adds the bias and residual and normalises each
+    row).  bf16_only applies to h."""
+    ctx = x.ctx
+    y, h = c_int32(), c_int32()
+    _check(_lib.tfb_linear_residual_layernorm(ctx.ptr, x.h, w.h, b.h, residual.h, gamma.h, beta.h, c_float(eps),
+                                              OUT_BF16_ONLY if bf16_only else 0, ctypes.byref(y), ctypes.byref(h)))
+    return Tensor(ctx, y.value), Tensor(ctx, h.value)
 
 
 def embedding(table: Tensor, ids, batch: int) -> Tensor:

@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "gelu_dev.h"
 #include "kernels.h"
 
 namespace tfb {
@@ -60,6 +61,12 @@ struct SkArgs {
   float alpha, beta;
   int M, N, K, kc, chunks, skipc;
   float* ws;  // [chunks][M][N] partials
+  int post;   // GemmPost
+  const float* ln_gamma;
+  const float* ln_beta;
+  float ln_eps;
+  float* ln_y;
+  uint16_t* ln_ybf;
 };
 
 template <bool A_BF, bool B_BF, bool RND>
@@ -160,11 +167,12 @@ __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
   const int m = t / (SNS / 4), nn = n0 + 4 * (t % (SNS / 4));
   if (m >= a.M || nn >= a.N) return;
   v *= a.alpha;
-  if (a.chunks > 1) {  // the reduction adds bias, beta C and resid
+  if (a.chunks > 1 || a.post == POST_LN) {  // the reduction adds bias, beta C and resid
     *reinterpret_cast<f4*>(a.ws + ((int64_t)chunk * a.M + m) * a.N + nn) = v;
     return;
   }
   if (a.bias) v += *reinterpret_cast<const f4*>(a.bias + nn);
+  if (a.post == POST_GELU) v = f4{gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)};
   float* dst = a.C + (int64_t)m * a.ldc + nn;
   if (a.beta != 0.f) v += a.beta * *reinterpret_cast<const f4*>(dst);
   if (a.resid) v += *reinterpret_cast<const f4*>(a.resid + (int64_t)m * a.ldc + nn);
@@ -193,12 +201,86 @@ __global__ __launch_bounds__(ST) void gemv_reduce_k(SkArgs a) {
       if (c0 + j < a.chunks) v += x[j];
   }
   if (a.bias) v += *reinterpret_cast<const f4*>(a.bias + nn);
+  if (a.post == POST_GELU) v = f4{gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)};
   float* dst = a.C + (int64_t)m * a.ldc + nn;
   if (a.beta != 0.f) v += a.beta * *reinterpret_cast<const f4*>(dst);
   if (a.resid) v += *reinterpret_cast<const f4*>(a.resid + (int64_t)m * a.ldc + nn);
   if (!a.skipc) *reinterpret_cast<f4*>(dst) = v;
   if (a.Cbf)
     *reinterpret_cast<u16x4*>(a.Cbf + (int64_t)m * a.ldc + nn) = u16x4{bf16_of(v.x), bf16_of(v.y), bf16_of(v.z), bf16_of(v.w)};
+}
+
+// POST_LN: one workgroup per row m.  C = the sum of the chunks (in chunk order) + bias +
+// beta C + resid, stored as usual; the row is then layer-normalised from registers (its
+// mean, then the mean square of the centred values) and written to ln_y and/or ln_ybf.
+constexpr int LN_MAXN = 2048;
+constexpr int LN_PER = LN_MAXN / 4 / ST;  // float4s per thread
+
+__device__ __forceinline__ float block_sum_ln(float v, float* sh) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int i = 0; i < ST / 64; ++i) r += sh[i];
+  return r;
+}
+
+__global__ __launch_bounds__(ST) void gemv_reduce_ln_k(SkArgs a) {
+  __shared__ float red[ST / 64];
+  const int m = blockIdx.x, t = threadIdx.x, N4 = a.N / 4;
+  const int64_t stride = (int64_t)a.M * N4;
+  const f4* p = reinterpret_cast<const f4*>(a.ws) + (int64_t)m * N4;
+  f4 v[LN_PER];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < LN_PER; ++j) {
+    const int e = t + j * ST;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (e < N4) {
+      for (int c0 = 0; c0 < a.chunks; c0 += 8) {
+        f4 x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = p[(int64_t)min(c0 + q, a.chunks - 1) * stride + e];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (c0 + q < a.chunks) acc += x[q];
+      }
+      const int nn = 4 * e;
+      if (a.bias) acc += *reinterpret_cast<const f4*>(a.bias + nn);
+      float* dst = a.C + (int64_t)m * a.ldc + nn;
+      if (a.beta != 0.f) acc += a.beta * *reinterpret_cast<const f4*>(dst);
+      if (a.resid) acc += *reinterpret_cast<const f4*>(a.resid + (int64_t)m * a.ldc + nn);
+      if (!a.skipc) *reinterpret_cast<f4*>(dst) = acc;
+      if (a.Cbf)
+        *reinterpret_cast<u16x4*>(a.Cbf + (int64_t)m * a.ldc + nn) =
+            u16x4{bf16_of(acc.x), bf16_of(acc.y), bf16_of(acc.z), bf16_of(acc.w)};
+      s += (acc.x + acc.y) + (acc.z + acc.w);
+    }
+    v[j] = acc;
+  }
+  const float invN = 1.f / (float)a.N;
+  const float mu = block_sum_ln(s, red) * invN;
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < LN_PER; ++j)
+    if (t + j * ST < N4) {
+      const f4 d = v[j] - mu;
+      q += (d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w);
+    }
+  const float rs = rsqrtf(block_sum_ln(q, red) * invN + a.ln_eps);
+#pragma unroll
+  for (int j = 0; j < LN_PER; ++j) {
+    const int e = t + j * ST;
+    if (e >= N4) continue;
+    const int nn = 4 * e;
+    const f4 o = (v[j] - mu) * rs * *reinterpret_cast<const f4*>(a.ln_gamma + nn) +
+                 *reinterpret_cast<const f4*>(a.ln_beta + nn);
+    if (a.ln_y) *reinterpret_cast<f4*>(a.ln_y + (int64_t)m * a.N + nn) = o;
+    if (a.ln_ybf)
+      *reinterpret_cast<u16x4*>(a.ln_ybf + (int64_t)m * a.N + nn) = u16x4{bf16_of(o.x), bf16_of(o.y), bf16_of(o.z), bf16_of(o.w)};
+  }
 }
 
 struct SkPlan {
@@ -210,6 +292,10 @@ SkPlan plan(const GemmArgs& g) {
   SkPlan p;
   const auto al = [](const void* q, int bytes) { return (reinterpret_cast<uintptr_t>(q) & (bytes - 1)) == 0; };
   if (g.M < 1 || g.M > SM || g.batch != 1 || g.K < 1 || g.N < 1) return p;
+  if (g.post == POST_GELU && (g.resid || g.beta != 0.f)) return p;
+  if (g.post == POST_LN && (g.N > LN_MAXN || !g.ln_gamma || !g.ln_beta || !al(g.ln_gamma, 16) || !al(g.ln_beta, 16) ||
+                            !al(g.ln_y, 16) || !al(g.ln_ybf, 8) || (!g.ln_y && !g.ln_ybf)))
+    return p;
   if ((int64_t)g.M * g.N > (1 << 28)) return p;  // keeps the launches' int indexes in range
   if (g.causal_a != CAUSAL_NONE || g.causal_out || g.a_mcontig || g.b_kcontig) return p;
   if (g.N % 4 || g.ldb % 4 || g.ldc % 4 || !al(g.B, g.b_bf16 ? 8 : 16) || !al(g.C, 16) || !al(g.bias, 16) ||
@@ -233,19 +319,23 @@ void launch(const SkArgs& a, int grid, hipStream_t s) {
 
 size_t gemv_workspace_bytes(const GemmArgs& g) {
   const SkPlan p = plan(g);
-  if (!p.ok || p.chunks == 1) return 0;
+  if (!p.ok || (p.chunks == 1 && g.post != POST_LN)) return 0;
   return (size_t)p.chunks * g.M * g.N * sizeof(float);
 }
+
+bool gemv_accepts(const GemmArgs& g) { return plan(g).ok; }
 
 bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_t* err) {
   const SkPlan p = plan(g);
   if (!p.ok) return false;
-  if (p.chunks > 1 && (!ws || ws_bytes < gemv_workspace_bytes(g))) return false;
+  if ((p.chunks > 1 || g.post == POST_LN) && (!ws || ws_bytes < gemv_workspace_bytes(g))) return false;
   SkArgs a;
   a.A = g.A, a.lda = g.lda, a.B = g.B, a.ldb = g.ldb, a.C = g.C, a.ldc = g.ldc, a.Cbf = g.Cbf;
   a.bias = g.bias, a.resid = g.resid, a.alpha = g.alpha, a.beta = g.beta;
   a.M = g.M, a.N = g.N, a.K = g.K, a.kc = p.kc, a.chunks = p.chunks, a.skipc = g.c_bf16_only ? 1 : 0;
   a.ws = static_cast<float*>(ws);
+  a.post = g.post, a.ln_gamma = g.ln_gamma, a.ln_beta = g.ln_beta, a.ln_eps = g.ln_eps, a.ln_y = g.ln_y;
+  a.ln_ybf = g.ln_ybf;
   const int grid = p.strips * p.chunks;
   const bool rnd = g.prec == PREC_BF16;
   if (g.a_bf16 && g.b_bf16)
@@ -256,7 +346,9 @@ bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_
     rnd ? launch<false, true, true>(a, grid, s) : launch<false, true, false>(a, grid, s);
   else
     rnd ? launch<false, false, true>(a, grid, s) : launch<false, false, false>(a, grid, s);
-  if (p.chunks > 1) {
+  if (g.post == POST_LN) {
+    run_kernel(gemv_reduce_ln_k, dim3(g.M), dim3(ST), 0, s, a);
+  } else if (p.chunks > 1) {
     const int n4 = g.M * (g.N / 4);
     run_kernel(gemv_reduce_k, dim3((n4 + ST - 1) / ST), dim3(ST), 0, s, a);
   }

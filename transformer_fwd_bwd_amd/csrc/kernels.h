@@ -73,7 +73,21 @@ struct GemmArgs {
   const float* resid = nullptr;
   // with Cbf and beta == 0: the bf16 copy alone is written, C (fp32) is left untouched
   bool c_bf16_only = false;
+  // Inference epilogues of the few-row path only (gemv.hip; gemm() refuses them
+  // elsewhere with hipErrorInvalidValue):
+  //   POST_GELU: C = gelu(alpha A B + bias) (no beta term, no residual)
+  //   POST_LN:   C = alpha A B + bias + resid as usual, then each row of C is
+  //              layer-normalised: ln_y = (C - mean) / sqrt(var + ln_eps) * ln_gamma
+  //              + ln_beta (biased variance), written as fp32 (ln_y, may be null)
+  //              and/or bf16 (ln_ybf, may be null); N <= 2048
+  int post = 0;
+  const float* ln_gamma = nullptr;
+  const float* ln_beta = nullptr;
+  float ln_eps = 0.f;
+  float* ln_y = nullptr;
+  uint16_t* ln_ybf = nullptr;
 };
+enum GemmPost { POST_NONE = 0, POST_GELU = 1, POST_LN = 2 };
 
 size_t gemm_workspace_bytes(const GemmArgs& g);
 hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t s);
@@ -82,6 +96,9 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
 // by gemm() when the layout fits; returns false (launching nothing) otherwise
 size_t gemv_workspace_bytes(const GemmArgs& g);
 bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_t* err);
+// whether gemv() takes this product (alignment, sizes); a product with an inference
+// epilogue (g.post) must be taken by it
+bool gemv_accepts(const GemmArgs& g);
 
 // ---- elementwise (elementwise.hip); beta in {0, 1}: overwrite or accumulate
 hipError_t fill(float* p, float v, int64_t n, hipStream_t s);

@@ -1609,6 +1609,126 @@ int tfb_linear_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int fl
   return matmul_impl(ctx, x, w, b, y, OP_LINEAR, flags);
 }
 
+// ------------------------------------------------------------------ inference fusions
+// A Linear of at most 16 rows with its consumer folded into the chunk sum of the
+// few-row product (gemv.hip): GELU, or the residual Add followed by LayerNorm.  Both
+// are inference-only (nothing is recorded); where the few-row kernel does not take
+// the product they run as the separate ops, with the same results up to rounding.
+namespace {
+
+// The few-row product y = x @ w + b (+ resid) with the epilogue `post`, its output
+// pointers still unset; `ok` says whether the few-row kernel takes it (checked with
+// 256-byte aligned stand-ins for the outputs, which the step arena gives them).
+GemmArgs linear_post_args(Ctx& C, int x, int w, int b, int res, int post, const float* ln_gamma,
+                          const float* ln_beta, bool* ok) {
+  TensorRec& X = C.T(x);
+  TensorRec& W = C.T(w);
+  const int64_t K = X.cols(), rows = X.rows(), N = W.shape[1];
+  const bool round_on_load = C.bf16_mode() && rows <= 16 && !X.bf_valid && X.f32_valid;
+  const Opnd xo = round_on_load ? Opnd{C.f32(X), false} : op_data(C, X);
+  const Opnd wo = op_data(C, W);
+  GemmArgs g = C.gemm_base();
+  g.M = (int)rows, g.N = (int)N, g.K = (int)K;
+  set_a(g, xo), g.lda = K;
+  set_b(g, wo), g.ldb = N;
+  g.ldc = N;
+  g.bias = C.T(b).data;
+  g.resid = res >= 0 ? C.f32(C.T(res)) : nullptr;
+  g.post = post, g.ln_gamma = ln_gamma, g.ln_beta = ln_beta;
+  float* stand_in = reinterpret_cast<float*>(C.c->arena.base);
+  g.C = stand_in;
+  if (post == POST_LN) g.ln_y = stand_in;
+  *ok = gemv_accepts(g);
+  return g;
+}
+
+void check_linear(Ctx& C, int x, int w, int b) {
+  TensorRec& X = C.T(x);
+  TensorRec& W = C.T(w);
+  need(W.ndim == 2 && W.shape[0] == X.cols(), TFB_ERR_SHAPE, "matmul " + shape_str(X) + " @ " + shape_str(W));
+  need(C.T(b).numel == W.shape[1] && C.T(b).ndim == 1, TFB_ERR_SHAPE,
+       "linear bias must be [" + std::to_string(W.shape[1]) + "]");
+  check_gemm_dims(X.rows(), X.cols(), W.shape[1]);
+}
+
+[[noreturn]] void rethrow(int rc) { fail(rc, g_last_error); }
+
+}  // namespace
+
+int tfb_linear_gelu(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int flags, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need((flags & ~TFB_OUT_BF16_ONLY) == 0, TFB_ERR_ARG, "unknown tfb_linear_gelu flags");
+    need(!ctx->grad_enabled, TFB_ERR_STATE, "tfb_linear_gelu is inference-only: disable gradients first");
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    x = C.dense_in(x, C.bf16_mode()), w = C.dense_in(w, C.bf16_mode()), b = C.dense_in(b);
+    check_linear(C, x, w, b);
+    std::vector<int64_t> shp = shape_vec(C.T(x));
+    shp.back() = C.T(w).shape[1];
+    bool ok = false;
+    GemmArgs g = linear_post_args(C, x, w, b, -1, POST_GELU, nullptr, nullptr, &ok);
+    if (ok) {
+      int h = C.make_output(shp);
+      uint16_t* yb = C.twin_data(ctx->tensors[h]);
+      const bool only = yb && (flags & TFB_OUT_BF16_ONLY);
+      g.C = ctx->tensors[h].data, g.Cbf = yb, g.c_bf16_only = only;
+      C.run_gemm(g);
+      if (yb) ctx->tensors[h].bf_valid = true;
+      if (only) ctx->tensors[h].f32_valid = false, ctx->tensors[h].bf16_out = true;
+      *y = h;
+      return;
+    }
+    tfb_tensor l;
+    int rc = tfb_linear_ex(ctx, x, w, b, flags, &l);
+    if (rc) rethrow(rc);
+    rc = tfb_gelu_ex(ctx, l, flags, y);
+    if (rc) rethrow(rc);
+  });
+}
+
+int tfb_linear_residual_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor r,
+                                  tfb_tensor gamma, tfb_tensor beta, float eps, int flags, tfb_tensor* y,
+                                  tfb_tensor* h) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need((flags & ~TFB_OUT_BF16_ONLY) == 0, TFB_ERR_ARG, "unknown tfb_linear_residual_layernorm flags");
+    need(!ctx->grad_enabled, TFB_ERR_STATE,
+         "tfb_linear_residual_layernorm is inference-only: disable gradients first");
+    need(y != nullptr && h != nullptr, TFB_ERR_ARG, "null output");
+    x = C.dense_in(x, C.bf16_mode()), w = C.dense_in(w, C.bf16_mode()), b = C.dense_in(b);
+    r = C.dense_in(r), gamma = C.dense_in(gamma), beta = C.dense_in(beta);
+    check_linear(C, x, w, b);
+    const int64_t N = C.T(w).shape[1];
+    need(C.T(r).numel == C.T(x).rows() * N && C.T(r).cols() == N, TFB_ERR_SHAPE,
+         "residual must have the output's shape, got " + shape_str(C.T(r)));
+    need(C.T(gamma).numel == N && C.T(beta).numel == N, TFB_ERR_SHAPE,
+         "layernorm gain/shift must have " + std::to_string(N) + " elements");
+    need(N <= 2048, TFB_ERR_SHAPE, "layernorm rows longer than 2048 are not supported");
+    std::vector<int64_t> shp = shape_vec(C.T(x));
+    shp.back() = N;
+    bool ok = false;
+    GemmArgs g = linear_post_args(C, x, w, b, r, POST_LN, C.T(gamma).data, C.T(beta).data, &ok);
+    if (ok) {
+      int yh = C.make_output(shp);
+      int hh = C.make_output(shp);
+      uint16_t* hb = C.twin_data(ctx->tensors[hh]);
+      const bool only = hb && (flags & TFB_OUT_BF16_ONLY);
+      g.C = ctx->tensors[yh].data;
+      g.ln_eps = eps;
+      g.ln_y = only ? nullptr : ctx->tensors[hh].data, g.ln_ybf = hb;
+      C.run_gemm(g);
+      if (hb) ctx->tensors[hh].bf_valid = true;
+      if (only) ctx->tensors[hh].f32_valid = false, ctx->tensors[hh].bf16_out = true;
+      *y = yh, *h = hh;
+      return;
+    }
+    int rc = tfb_linear_residual(ctx, x, w, b, r, y);
+    if (rc) rethrow(rc);
+    rc = tfb_layernorm_ex(ctx, *y, gamma, beta, eps, flags, h);
+    if (rc) rethrow(rc);
+  });
+}
+
 int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y) {
   return tfb_layernorm_ex(ctx, x, gamma, beta, eps, 0, y);
 }
