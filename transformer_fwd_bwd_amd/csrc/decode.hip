@@ -327,6 +327,7 @@ __global__ __launch_bounds__(NT) void sample_topk_k(const float* __restrict__ lo
 constexpr int SR = 1024;
 constexpr int SPER = 50;
 constexpr int SCAP = 512;
+constexpr int SCAND = 1024;
 
 __device__ __forceinline__ int block_sumi_sr(int v, int* sh) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -358,6 +359,10 @@ __global__ __launch_bounds__(SR) void sample_topk_reg_k(const float* __restrict_
   __shared__ int sorted[SCAP];
   __shared__ double wts[SR];  // kept weights in id order (fast path) or per-thread range sums (wide path)
   __shared__ int nkept;
+  __shared__ uint32_t tmx[SR];       // per-thread maxima (the cut's lower bound)
+  __shared__ uint32_t cands[SCAND];  // keys at or above the bound
+  __shared__ uint32_t bound;
+  __shared__ int ncand;
   const int b = blockIdx.x, t = threadIdx.x;
   const float* l = logits + (int64_t)b * ld;
   // order keys; a slot past the row holds key 0, below the key of every float but
@@ -370,13 +375,67 @@ __global__ __launch_bounds__(SR) void sample_topk_reg_k(const float* __restrict_
   }
   uint32_t thr = 1;  // without a cut every logit survives
   if (k > 0 && k < V) {
-    thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      int cnt = 0;
+    // The cut is the k-th largest key: the largest x with #(key >= x) >= k.
+    // A lower bound first: the k-th largest of the 1024 per-thread maxima (k of the
+    // row's keys are at least that).  One wave finds it bit by bit without block
+    // barriers; the keys at or above it (typically a few k) are gathered, and the
+    // cut is the largest gathered key with at least k gathered keys at or above it --
+    // the same value, since the counts of keys >= x agree for every x >= the bound.
+    // Many gathered keys (ties across the bound) take the full search below.
+    bool found = false;
+    if (k <= SR) {
+      uint32_t tmax = 0;
 #pragma unroll
-      for (int j = 0; j < SPER; ++j) cnt += key[j] >= cand;
-      if (block_sumi_sr(cnt, ired) >= k) thr = cand;
+      for (int j = 0; j < SPER; ++j) tmax = max(tmax, key[j]);
+      tmx[t] = tmax;
+      __syncthreads();
+      if (t < 64) {
+        uint32_t v[SR / 64];
+#pragma unroll
+        for (int i = 0; i < SR / 64; ++i) v[i] = tmx[t + 64 * i];
+        uint32_t lb = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = lb | (1u << bit);
+          int c = 0;
+#pragma unroll
+          for (int i = 0; i < SR / 64; ++i) c += v[i] >= cand;
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+          if (c >= k) lb = cand;
+        }
+        if (t == 0) bound = lb, ncand = 0;
+      }
+      __syncthreads();
+      const uint32_t lb = bound;
+      int mine = 0;
+#pragma unroll
+      for (int j = 0; j < SPER; ++j) mine += key[j] >= lb;
+      const int n = block_sumi_sr(mine, ired);
+      if (n <= SCAND) {
+#pragma unroll
+        for (int j = 0; j < SPER; ++j)
+          if (key[j] >= lb) cands[atomicAdd(&ncand, 1)] = key[j];
+        __syncthreads();
+        uint32_t best = 0;
+        for (int i = t; i < n; i += SR) {
+          const uint32_t c = cands[i];
+          int ge = 0;
+          for (int j = 0; j < n; ++j) ge += cands[j] >= c;
+          if (ge >= k) best = max(best, c);
+        }
+        thr = block_maxu_sr(best, ired);
+        found = true;
+      }
+    }
+    if (!found) {
+      thr = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < SPER; ++j) cnt += key[j] >= cand;
+        if (block_sumi_sr(cnt, ired) >= k) thr = cand;
+      }
     }
   }
   uint32_t kmax = 0;
