@@ -215,6 +215,18 @@ int tfb_linear_gelu(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int 
 int tfb_linear_residual_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, tfb_tensor r,
                                   tfb_tensor gamma, tfb_tensor beta, float eps, int flags, tfb_tensor* y,
                                   tfb_tensor* h);
+/* Inference only (as above): a whole MLP sub-block of a pre-LN block and the
+ * LayerNorm after it: y = r + gelu(x @ w_fc + b_fc) @ w_proj + b_proj and
+ * h = LayerNorm(y) with gamma, beta, eps.  For at most 16 rows the c_fc product's
+ * partial sums are read straight by the projection, which adds them with the bias
+ * and applies the GELU as it loads its input (the values tfb_linear_gelu would
+ * have stored, bf16 in the bf16 variant), so neither the hidden activation nor its
+ * chunk sum is a pass of its own; otherwise tfb_linear_gelu then
+ * tfb_linear_residual_layernorm.  Flags as there (TFB_OUT_BF16_ONLY for h).
+ * [GPT2-4, "Loading the weights": x = x + mlp(ln_2(x)), MLP C -> 4C -> C] */
+int tfb_mlp_residual_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w_fc, tfb_tensor b_fc, tfb_tensor w_proj,
+                               tfb_tensor b_proj, tfb_tensor r, tfb_tensor gamma, tfb_tensor beta, float eps, int flags,
+                               tfb_tensor* y, tfb_tensor* h);
 /* Per row over the last dim: (x - mean)/sqrt(var + eps) * gamma + beta with the
  * biased variance.  [Autograd-1, table of ops: LayerNorm] */
 int tfb_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor gamma, tfb_tensor beta, float eps, tfb_tensor* y);
@@ -355,6 +367,15 @@ int tfb_kv_store(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos0);
  * `pos`, then y[b, 0, head slice] = sum_j softmax_j(q . k_j / sqrt(hs)) v_j over
  * positions 0..pos -- no mask, the cache holds only the past.  y [batch, 1, C]. */
 int tfb_kv_attend(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos, int heads, tfb_tensor* y);
+/* The c_attn Linear of one new token per sequence and tfb_kv_attend as one call:
+ * qkv = x @ w + b with x [batch, 1, K] and w [K, 3C], then the append and the
+ * single-query attention of tfb_kv_attend; y [batch, 1, C].  With gradients
+ * disabled, at most 16 sequences and head size 32, 64 or 128 the attention kernel
+ * sums the product's partials (plus the bias) as it reads q, k and v, so qkv is
+ * never stored; otherwise it runs as tfb_linear then tfb_kv_attend.  Not recorded.
+ * [GPT2-4, "Generation with KV cache"] */
+int tfb_kv_attend_linear(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor x, tfb_tensor w, tfb_tensor b, int pos,
+                         int heads, tfb_tensor* y);
 /* One id per row of logits [..., V]: keep every logit >= the k-th largest (ties
  * kept; k = 0 or k >= V keeps all), p = softmax((l - max)/temperature) summed in
  * double, and return the first id (ascending) whose cumulative p exceeds u[row].

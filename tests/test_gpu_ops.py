@@ -156,6 +156,70 @@ def test_linear_residual_layernorm_inference(ctx, prec, M, K, N):
     assert_close(h, rh, FWD_TOL[prec], "LayerNorm(y)")
 
 
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("M,K,F", [(16, 768, 3072), (3, 64, 256), (20, 64, 128)])
+def test_mlp_residual_layernorm_inference(ctx, prec, M, K, F):
+    """[GPT2-4, "Loading the weights": x = x + mlp(ln_2(x)), then the next LayerNorm]
+    y = r + gelu(x @ w1 + b1) @ w2 + b2 and h = LayerNorm(y) as one inference call: the
+    projection sums the c_fc partials (6 chunks; 1 chunk) and applies the GELU as it
+    loads them; 20 rows take the separate ops."""
+    arrays = [rnd(190 + M, (M, K)), rnd(191, (K, F), 1 / np.sqrt(K)), rnd(192, (F,), 0.5),
+              rnd(193, (F, K), 1 / np.sqrt(F)), rnd(194, (K,), 0.5), rnd(195, (M, K)), 1 + rnd(196, (K,), 0.2),
+              rnd(197, (K,), 0.2)]
+    y, h = _infer(ctx, prec, arrays, lambda *t: T.mlp_residual_layernorm(*t, bf16_only=True))
+    x, w1, b1, w2, b2, r, g, bt = (a.astype(np.float64) for a in arrays)
+    from oracle import ops as O
+    ry = r + O.gelu_fwd(x @ w1 + b1) @ w2 + b2
+    assert_close(y, ry, FWD_TOL[prec], "y")
+    assert_close(h, O.layernorm_fwd(ry, g, bt)[0], FWD_TOL[prec], "LayerNorm(y)")
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("hs,H", [(64, 3), (48, 2)])
+def test_kv_attend_linear(ctx, prec, hs, H):
+    """[GPT2-4, "Generation with KV cache"] the c_attn Linear and the cached attention as
+    one call, at positions on both sides of a 128-position block: the attention sums the
+    product's partials as it reads q, k, v (head size 64) or runs after the stored
+    product (head size 48); the next call must see the key and value it appended."""
+    from oracle import ops as O
+    ctx.set_precision(prec)
+    rng = S.rng_for(200 + hs)
+    B, C, K, Tmax = 4, hs * H, 96, 200
+    kv = T.KvCache(ctx, 2, B, Tmax, C)
+    Kc, Vc = np.zeros((B, Tmax, C)), np.zeros((B, Tmax, C))
+    pre = rng.standard_normal((B, 127, 3 * C)).astype(np.float32)
+    tq = ctx.tensor(pre.shape, pre)
+    kv.store(1, tq, 0)
+    Kc[:, :127], Vc[:, :127] = pre[:, :, C:2 * C], pre[:, :, 2 * C:]
+    tq.release()
+    w = rnd(201, (K, 3 * C), 1 / np.sqrt(K))
+    b = rnd(202, (3 * C,), 0.3)
+    tw, tb = ctx.tensor(w.shape, w), ctx.tensor(b.shape, b)
+    ctx.set_grad_enabled(False)
+    try:
+        for pos in (127, 128, 129):
+            x = rnd(203 + pos, (B, 1, K))
+            tx = ctx.tensor(x.shape, x)
+            y = kv.attend_linear(1, tx, tw, tb, pos, H).numpy().reshape(B, C)
+            qkv = x.reshape(B, K).astype(np.float64) @ w + b
+            Kc[:, pos], Vc[:, pos] = qkv[:, C:2 * C], qkv[:, 2 * C:]
+            ref = np.zeros((B, C))
+            for bb in range(B):
+                for h in range(H):
+                    sl = slice(h * hs, (h + 1) * hs)
+                    p = O.softmax_row(Kc[bb, :pos + 1, sl] @ qkv[bb, sl] / np.sqrt(hs))
+                    ref[bb, sl] = p @ Vc[bb, :pos + 1, sl]
+            assert_close(y, ref, FWD_TOL[prec], f"pos {pos}")
+            ctx.tape_reset()
+            tx.release()
+    finally:
+        ctx.set_grad_enabled(True)
+        ctx.set_precision("fp32")
+    kv.close()
+    tw.release()
+    tb.release()
+
+
 def test_inference_fusions_refuse_to_record(ctx):
     x, w, b = ctx.tensor((2, 8), np.ones((2, 8), np.float32)), ctx.tensor((8, 8)), ctx.tensor((8,))
     with pytest.raises(T.TfbError) as e:

@@ -63,6 +63,9 @@ SIGNATURES = {
     "tfb_linear_residual": [c_void_p, c_int32, c_int32, c_int32, c_int32, P(c_int32)],
     "tfb_layernorm": [c_void_p, c_int32, c_int32, c_int32, c_float, P(c_int32)],
     "tfb_linear_gelu": [c_void_p, c_int32, c_int32, c_int32, c_int32, P(c_int32)],
+    "tfb_mlp_residual_layernorm": [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                   c_float, c_int32, P(c_int32), P(c_int32)],
+    "tfb_kv_attend_linear": [c_void_p, c_void_p, c_int, c_int32, c_int32, c_int32, c_int, c_int, P(c_int32)],
     "tfb_linear_residual_layernorm": [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_float,
                                       c_int32, P(c_int32), P(c_int32)],
     "tfb_embedding": [c_void_p, c_int32, c_void_p, c_int64, c_int64, P(c_int32)],
@@ -385,6 +388,18 @@ def linear_residual_layernorm(x: Tensor, w: Tensor, b: Tensor, residual: Tensor,
     return Tensor(ctx, y.value), Tensor(ctx, h.value)
 
 
+def mlp_residual_layernorm(x: Tensor, w_fc: Tensor, b_fc: Tensor, w_proj: Tensor, b_proj: Tensor, residual: Tensor,
+                           gamma: Tensor, beta: Tensor, eps: float = 1e-5, bf16_only: bool = False):
+    """Inference only: (y, h) with y = residual + gelu(x @ w_fc + b_fc) @ w_proj + b_proj and
+    h = LayerNorm(y), as one call (the hidden activation is never stored for at most 16 rows)."""
+    ctx = x.ctx
+    y, h = c_int32(), c_int32()
+    _check(_lib.tfb_mlp_residual_layernorm(ctx.ptr, x.h, w_fc.h, b_fc.h, w_proj.h, b_proj.h, residual.h, gamma.h,
+                                           beta.h, c_float(eps), OUT_BF16_ONLY if bf16_only else 0, ctypes.byref(y),
+                                           ctypes.byref(h)))
+    return Tensor(ctx, y.value), Tensor(ctx, h.value)
+
+
 def embedding(table: Tensor, ids, batch: int) -> Tensor:
     ctx = table.ctx
     d = ctx.device_ints(ids)
@@ -485,6 +500,10 @@ class KvCache:
 
     def attend(self, layer: int, qkv: Tensor, pos: int, heads: int) -> Tensor:
         return _out(self.ctx, _lib.tfb_kv_attend, self.ptr, layer, qkv.h, pos, heads)
+
+    def attend_linear(self, layer: int, x: Tensor, w: Tensor, b: Tensor, pos: int, heads: int) -> Tensor:
+        """The c_attn Linear (x @ w + b) and attend() as one call (inference)."""
+        return _out(self.ctx, _lib.tfb_kv_attend_linear, self.ptr, layer, x.h, w.h, b.h, pos, heads)
 
     def close(self):
         if getattr(self, "ptr", None):

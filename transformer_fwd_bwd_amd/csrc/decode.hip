@@ -146,8 +146,33 @@ __global__ __launch_bounds__(NT) void kv_attend_k(const float* __restrict__ qkv,
 constexpr int KVP = 128;
 typedef float kf4 __attribute__((ext_vector_type(4)));
 
+// qkv values of sequence b, columns i..i+3: from the stored qkv, or summed from the
+// c_attn product's partials (chunks in order) plus its bias -- the values its chunk
+// sum would have stored
+struct QkvSrc {
+  const float* qkv;
+  const float* part;
+  const float* bias;
+  int chunks;
+};
+__device__ __forceinline__ kf4 qkv4(const QkvSrc& q, int B, int C, int b, int i) {
+  if (!q.part) return *reinterpret_cast<const kf4*>(q.qkv + (int64_t)b * 3 * C + i);
+  const int64_t stride = (int64_t)B * 3 * C;
+  const float* p = q.part + (int64_t)b * 3 * C + i;
+  kf4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < q.chunks; c0 += 8) {  // eight loads in flight, added in chunk order
+    kf4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const kf4*>(p + min(c0 + j, q.chunks - 1) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < q.chunks) v += x[j];
+  }
+  return v + *reinterpret_cast<const kf4*>(q.bias + i);
+}
+
 template <int HS>
-__global__ __launch_bounds__(256) void kv_attend_part_k(const float* __restrict__ qkv, float* __restrict__ kv,
+__global__ __launch_bounds__(256) void kv_attend_part_k(QkvSrc qs, float* __restrict__ kv,
                                                         float* __restrict__ pacc, float* __restrict__ pml, int layer,
                                                         int B, int Tmax, int C, int H, int pos, int S, float scale) {
   constexpr int LPR = HS / 4, RPI = 64 / LPR, PW = KVP / 4, IT = PW / RPI;
@@ -155,19 +180,18 @@ __global__ __launch_bounds__(256) void kv_attend_part_k(const float* __restrict_
   __shared__ kf4 wacc[4][LPR];
   const int s = blockIdx.x % S, bh = blockIdx.x / S;
   const int b = bh / H, hd = bh % H;
-  const float* src = qkv + (int64_t)b * 3 * C;
   float* Kc = kv + ((int64_t)(layer * 2 + 0) * B + b) * Tmax * C + hd * HS;
   float* Vc = kv + ((int64_t)(layer * 2 + 1) * B + b) * Tmax * C + hd * HS;
   const int j_lo = s * KVP, j_hi = min(j_lo + KVP, pos + 1);
   if (pos < j_lo + KVP) {  // the last block: append the new token's key and value (uniform per block)
-    for (int d = threadIdx.x; d < HS; d += 256) {
-      Kc[(int64_t)pos * C + d] = src[C + hd * HS + d];
-      Vc[(int64_t)pos * C + d] = src[2 * C + hd * HS + d];
+    for (int d4 = threadIdx.x; d4 < HS / 4; d4 += 256) {
+      *reinterpret_cast<kf4*>(Kc + (int64_t)pos * C + 4 * d4) = qkv4(qs, B, C, b, C + hd * HS + 4 * d4);
+      *reinterpret_cast<kf4*>(Vc + (int64_t)pos * C + 4 * d4) = qkv4(qs, B, C, b, 2 * C + hd * HS + 4 * d4);
     }
     __syncthreads();
   }
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / LPR, c = lane % LPR;
-  const kf4 q = *reinterpret_cast<const kf4*>(src + hd * HS + c * 4);
+  const kf4 q = qkv4(qs, B, C, b, hd * HS + c * 4);
   const int jw = j_lo + w * PW;
   // every key and value row of this wave is requested before the first is used;
   // rows past the block read row j_lo (in range) and are masked below
@@ -545,26 +569,28 @@ size_t kv_attend_workspace_bytes(int B, int C, int H, int pos) {
   return (size_t)(B * S * ((int64_t)C + 2 * H)) * sizeof(float);
 }
 
+bool kv_attend_takes_parts(int C, int H) { return kv_split_ok(C, H); }
+
 hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, int Tmax, int C, int H, int pos,
-                     float scale, void* ws, hipStream_t s) {
+                     float scale, void* ws, hipStream_t s, const float* qkv_part, int qkv_chunks,
+                     const float* qkv_bias) {
   if (!kv_split_ok(C, H) || ws == nullptr) {
+    if (qkv_part) return hipErrorInvalidValue;  // the unsplit kernel reads stored qkv only
     const size_t shmem = ((size_t)Tmax + 4 * 64) * sizeof(float);
     run_kernel(kv_attend_k, dim3(B * H), dim3(NT), shmem, s, qkv, kv, y, layer, B, Tmax, C, H, pos, scale);
     return hipGetLastError();
   }
+  const QkvSrc qs{qkv, qkv_part, qkv_bias, qkv_chunks};
   const int hs = C / H, S = (pos + KVP) / KVP;  // blocks covering positions 0..pos
   float* pacc = static_cast<float*>(ws);
   float* pml = pacc + (int64_t)B * H * S * hs;
   const dim3 grid((unsigned)(B * H * S));
   if (hs == 32)
-    run_kernel(kv_attend_part_k<32>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos, S,
-                       scale);
+    run_kernel(kv_attend_part_k<32>, grid, dim3(256), 0, s, qs, kv, pacc, pml, layer, B, Tmax, C, H, pos, S, scale);
   else if (hs == 64)
-    run_kernel(kv_attend_part_k<64>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos, S,
-                       scale);
+    run_kernel(kv_attend_part_k<64>, grid, dim3(256), 0, s, qs, kv, pacc, pml, layer, B, Tmax, C, H, pos, S, scale);
   else
-    run_kernel(kv_attend_part_k<128>, grid, dim3(256), 0, s, qkv, kv, pacc, pml, layer, B, Tmax, C, H, pos,
-                       S, scale);
+    run_kernel(kv_attend_part_k<128>, grid, dim3(256), 0, s, qs, kv, pacc, pml, layer, B, Tmax, C, H, pos, S, scale);
   const int n = B * H * hs;
   run_kernel(kv_attend_merge_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pacc, pml, y, B * H, hs, S);
   return hipGetLastError();

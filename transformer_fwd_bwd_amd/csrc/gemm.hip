@@ -863,7 +863,7 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   if (g.c_bf16_only && (!g.Cbf || g.beta != 0.f)) return hipErrorInvalidValue;
   hipError_t ge;
   if (gemv(g, workspace, ws_bytes, s, &ge)) return ge;
-  if (g.post != POST_NONE) return hipErrorInvalidValue;  // the inference epilogues are few-row only
+  if (g.post != POST_NONE || g.a_part) return hipErrorInvalidValue;  // the inference fusions are few-row only
   // K == 0 needs no special case: the k loop is empty and the epilogue writes beta*C + bias
   Plan p = make_plan(g);
   if (p.splits > 1 && (size_t)p.splits * g.batch * g.M * g.N * sizeof(float) > ws_bytes) p.splits = 1;

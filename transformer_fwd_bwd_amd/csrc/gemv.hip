@@ -67,9 +67,32 @@ struct SkArgs {
   float ln_eps;
   float* ln_y;
   uint16_t* ln_ybf;
+  const float* a_part;  // APART: A from the previous product's partials (GemmArgs)
+  const float* a_bias;
+  int a_chunks;
 };
 
-template <bool A_BF, bool B_BF, bool RND>
+// A from the previous few-row product's partials: gelu(sum of its chunks + bias), as
+// that product's reduction would have computed it (same order), rounded to bf16 in
+// the bf16 variant
+template <bool RND>
+__device__ __forceinline__ float a_from_parts(const SkArgs& a, int m, int k) {
+  const int64_t stride = (int64_t)a.M * a.K;
+  const float* p = a.a_part + (int64_t)m * a.K + k;
+  float v = 0.f;
+  for (int c0 = 0; c0 < a.a_chunks; c0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = p[(int64_t)min(c0 + j, a.a_chunks - 1) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < a.a_chunks) v += x[j];
+  }
+  v = gelu_f(v + a.a_bias[k]);
+  return RND ? round_bf16(v) : v;
+}
+
+template <bool A_BF, bool B_BF, bool RND, bool APART>
 __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
   __shared__ f4 sA[SKC][SM / 4];  // sA[k][q] = A rows 4q..4q+3 at k
   __shared__ f4 red[4][SM * SNS / 4];
@@ -97,10 +120,12 @@ __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
   }
   // A[0..M) x [k0, k0 + kn): element i of this thread's share is (i / SKC, i % SKC)
   araw_t araw[SM * SKC / ST];
+  if constexpr (!APART) {
 #pragma unroll
-  for (int j = 0; j < SM * SKC / ST; ++j) {
-    const int i = t + j * ST, m = i / SKC, kk = i % SKC;
-    araw[j] = static_cast<const araw_t*>(a.A)[(int64_t)(m < a.M ? m : 0) * a.lda + k0 + (kk < kn ? kk : 0)];
+    for (int j = 0; j < SM * SKC / ST; ++j) {
+      const int i = t + j * ST, m = i / SKC, kk = i % SKC;
+      araw[j] = static_cast<const araw_t*>(a.A)[(int64_t)(m < a.M ? m : 0) * a.lda + k0 + (kk < kn ? kk : 0)];
+    }
   }
   f4 b[SKC / 16];
 #pragma unroll
@@ -120,7 +145,9 @@ __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
   for (int j = 0; j < SM * SKC / ST; ++j) {
     const int i = t + j * ST, m = i / SKC, kk = i % SKC;
     float v;
-    if constexpr (A_BF) {
+    if constexpr (APART) {
+      v = a_from_parts<RND>(a, m < a.M ? m : 0, k0 + (kk < kn ? kk : 0));
+    } else if constexpr (A_BF) {
       v = bf16_val(araw[j]);
     } else {
       v = araw[j];
@@ -167,7 +194,7 @@ __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
   const int m = t / (SNS / 4), nn = n0 + 4 * (t % (SNS / 4));
   if (m >= a.M || nn >= a.N) return;
   v *= a.alpha;
-  if (a.chunks > 1 || a.post == POST_LN) {  // the reduction adds bias, beta C and resid
+  if (a.chunks > 1 || a.post == POST_LN || a.post == POST_PARTIALS) {  // the reduction adds bias, beta C, resid
     *reinterpret_cast<f4*>(a.ws + ((int64_t)chunk * a.M + m) * a.N + nn) = v;
     return;
   }
@@ -293,6 +320,8 @@ SkPlan plan(const GemmArgs& g) {
   const auto al = [](const void* q, int bytes) { return (reinterpret_cast<uintptr_t>(q) & (bytes - 1)) == 0; };
   if (g.M < 1 || g.M > SM || g.batch != 1 || g.K < 1 || g.N < 1) return p;
   if (g.post == POST_GELU && (g.resid || g.beta != 0.f)) return p;
+  if (g.a_part && (!g.a_bias || g.a_chunks < 1 || g.a_bf16 || g.post == POST_PARTIALS)) return p;
+  if (g.post == POST_PARTIALS && (g.bias || g.resid || g.beta != 0.f || g.Cbf)) return p;
   if (g.post == POST_LN && (g.N > LN_MAXN || !g.ln_gamma || !g.ln_beta || !al(g.ln_gamma, 16) || !al(g.ln_beta, 16) ||
                             !al(g.ln_y, 16) || !al(g.ln_ybf, 8) || (!g.ln_y && !g.ln_ybf)))
     return p;
@@ -310,25 +339,31 @@ SkPlan plan(const GemmArgs& g) {
   return p;
 }
 
-template <bool A_BF, bool B_BF, bool RND>
+template <bool A_BF, bool B_BF, bool RND, bool APART = false>
 void launch(const SkArgs& a, int grid, hipStream_t s) {
-  run_kernel((gemv_k<A_BF, B_BF, RND>), dim3(grid), dim3(ST), 0, s, a);
+  run_kernel((gemv_k<A_BF, B_BF, RND, APART>), dim3(grid), dim3(ST), 0, s, a);
 }
 
 }  // namespace
 
 size_t gemv_workspace_bytes(const GemmArgs& g) {
   const SkPlan p = plan(g);
-  if (!p.ok || (p.chunks == 1 && g.post != POST_LN)) return 0;
+  if (!p.ok || (p.chunks == 1 && g.post != POST_LN && g.post != POST_PARTIALS)) return 0;
   return (size_t)p.chunks * g.M * g.N * sizeof(float);
 }
 
 bool gemv_accepts(const GemmArgs& g) { return plan(g).ok; }
 
+int gemv_chunks(const GemmArgs& g) {
+  const SkPlan p = plan(g);
+  return p.ok ? p.chunks : 0;
+}
+
 bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_t* err) {
   const SkPlan p = plan(g);
   if (!p.ok) return false;
-  if ((p.chunks > 1 || g.post == POST_LN) && (!ws || ws_bytes < gemv_workspace_bytes(g))) return false;
+  if ((p.chunks > 1 || g.post == POST_LN || g.post == POST_PARTIALS) && (!ws || ws_bytes < gemv_workspace_bytes(g)))
+    return false;
   SkArgs a;
   a.A = g.A, a.lda = g.lda, a.B = g.B, a.ldb = g.ldb, a.C = g.C, a.ldc = g.ldc, a.Cbf = g.Cbf;
   a.bias = g.bias, a.resid = g.resid, a.alpha = g.alpha, a.beta = g.beta;
@@ -336,9 +371,15 @@ bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_
   a.ws = static_cast<float*>(ws);
   a.post = g.post, a.ln_gamma = g.ln_gamma, a.ln_beta = g.ln_beta, a.ln_eps = g.ln_eps, a.ln_y = g.ln_y;
   a.ln_ybf = g.ln_ybf;
+  a.a_part = g.a_part, a.a_bias = g.a_bias, a.a_chunks = g.a_chunks;
   const int grid = p.strips * p.chunks;
   const bool rnd = g.prec == PREC_BF16;
-  if (g.a_bf16 && g.b_bf16)
+  if (g.a_part) {
+    if (g.b_bf16)
+      rnd ? launch<false, true, true, true>(a, grid, s) : launch<false, true, false, true>(a, grid, s);
+    else
+      rnd ? launch<false, false, true, true>(a, grid, s) : launch<false, false, false, true>(a, grid, s);
+  } else if (g.a_bf16 && g.b_bf16)
     launch<true, true, false>(a, grid, s);
   else if (g.a_bf16)
     rnd ? launch<true, false, true>(a, grid, s) : launch<true, false, false>(a, grid, s);
@@ -348,7 +389,7 @@ bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_
     rnd ? launch<false, false, true>(a, grid, s) : launch<false, false, false>(a, grid, s);
   if (g.post == POST_LN) {
     run_kernel(gemv_reduce_ln_k, dim3(g.M), dim3(ST), 0, s, a);
-  } else if (p.chunks > 1) {
+  } else if (p.chunks > 1 && g.post != POST_PARTIALS) {
     const int n4 = g.M * (g.N / 4);
     run_kernel(gemv_reduce_k, dim3((n4 + ST - 1) / ST), dim3(ST), 0, s, a);
   }

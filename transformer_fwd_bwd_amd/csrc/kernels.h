@@ -86,8 +86,18 @@ struct GemmArgs {
   float ln_eps = 0.f;
   float* ln_y = nullptr;
   uint16_t* ln_ybf = nullptr;
+  //   POST_PARTIALS: only the per-chunk partial products are written, to the
+  //              workspace as [chunks][M][N] (no bias, no C): the next few-row
+  //              kernel sums them itself (gemv_chunks() gives their number)
+  // A taken from such partials (few-row path only; A, lda, a_bf16 unused):
+  //   A(m, k) = gelu(sum over the a_chunks chunks, in order, of a_part[c][m][k] +
+  //   a_bias[k]), the previous product's GELU epilogue, rounded to bf16 in the bf16
+  //   variant -- the values that product would have stored with TFB_OUT_BF16_ONLY
+  const float* a_part = nullptr;
+  const float* a_bias = nullptr;
+  int a_chunks = 0;
 };
-enum GemmPost { POST_NONE = 0, POST_GELU = 1, POST_LN = 2 };
+enum GemmPost { POST_NONE = 0, POST_GELU = 1, POST_LN = 2, POST_PARTIALS = 3 };
 
 size_t gemm_workspace_bytes(const GemmArgs& g);
 hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t s);
@@ -99,6 +109,7 @@ bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_
 // whether gemv() takes this product (alignment, sizes); a product with an inference
 // epilogue (g.post) must be taken by it
 bool gemv_accepts(const GemmArgs& g);
+int gemv_chunks(const GemmArgs& g);
 
 // ---- elementwise (elementwise.hip); beta in {0, 1}: overwrite or accumulate
 hipError_t fill(float* p, float v, int64_t n, hipStream_t s);
@@ -243,8 +254,13 @@ hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, in
                     hipStream_t s);
 // ws: kv_attend_workspace_bytes(B, C, H, pos) bytes of scratch (partial results per block of positions)
 size_t kv_attend_workspace_bytes(int B, int C, int H, int pos);
+// qkv_part (optional; qkv then unused): qkv is the sum over qkv_chunks chunks of
+// qkv_part[c][B][3C] plus qkv_bias, the partials of the few-row c_attn product
+// (POST_PARTIALS); taken only where kv_attend_takes_parts(C, H)
+bool kv_attend_takes_parts(int C, int H);
 hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, int Tmax, int C, int H, int pos,
-                     float scale, void* ws, hipStream_t s);
+                     float scale, void* ws, hipStream_t s,
+                     const float* qkv_part = nullptr, int qkv_chunks = 0, const float* qkv_bias = nullptr);
 hipError_t sample_topk(const float* logits, int64_t ld, int B, int V, int k, float temperature, const double* u,
                        int32_t* out, hipStream_t s);
 

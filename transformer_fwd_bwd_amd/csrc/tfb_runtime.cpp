@@ -652,10 +652,20 @@ struct Ctx {
     c->arena.hi = mark;  // scratch: later work on the same stream runs after this gemm
   }
 
+  // a few-row product whose workspace (its partial products) the caller keeps for a
+  // later kernel: no scratch of its own
+  void run_gemm_ws(const GemmArgs& g, void* ws, size_t bytes) {
+    hipError_t e = hipSuccess;
+    timed(TFB_PROF_GEMV, gemv_bytes(g), [&] {
+      if (!gemv(g, ws, bytes, s(), &e)) fail(TFB_ERR_STATE, "few-row product declined");
+      hip_check(e, "gemv launch");
+    });
+  }
+
   // bytes a few-row product must move: its operands once, its output once
   static double gemv_bytes(const GemmArgs& g) {
     const double ea = g.a_bf16 ? 2 : 4, eb = g.b_bf16 ? 2 : 4;
-    double b = ea * g.M * (double)g.K + eb * (double)g.K * g.N;
+    double b = (g.a_part ? 4.0 * g.a_chunks : ea) * g.M * (double)g.K + eb * (double)g.K * g.N;
     b += (g.c_bf16_only ? 2.0 : 4.0 + (g.Cbf ? 2.0 : 0.0)) * g.M * (double)g.N;
     if (g.bias) b += 4.0 * g.N;
     if (g.resid) b += 4.0 * g.M * (double)g.N;
@@ -1614,6 +1624,8 @@ int tfb_linear_ex(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int fl
 // few-row product (gemv.hip): GELU, or the residual Add followed by LayerNorm.  Both
 // are inference-only (nothing is recorded); where the few-row kernel does not take
 // the product they run as the separate ops, with the same results up to rounding.
+}  // extern "C"
+
 namespace {
 
 // The few-row product y = x @ w + b (+ resid) with the epilogue `post`, its output
@@ -1654,6 +1666,8 @@ void check_linear(Ctx& C, int x, int w, int b) {
 [[noreturn]] void rethrow(int rc) { fail(rc, g_last_error); }
 
 }  // namespace
+
+extern "C" {
 
 int tfb_linear_gelu(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_tensor b, int flags, tfb_tensor* y) {
   return guarded([&] {
@@ -1726,6 +1740,118 @@ int tfb_linear_residual_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w, tfb_
     if (rc) rethrow(rc);
     rc = tfb_layernorm_ex(ctx, *y, gamma, beta, eps, flags, h);
     if (rc) rethrow(rc);
+  });
+}
+
+int tfb_mlp_residual_layernorm(tfb_ctx* ctx, tfb_tensor x, tfb_tensor w_fc, tfb_tensor b_fc, tfb_tensor w_proj,
+                               tfb_tensor b_proj, tfb_tensor r, tfb_tensor gamma, tfb_tensor beta, float eps, int flags,
+                               tfb_tensor* y, tfb_tensor* h) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need((flags & ~TFB_OUT_BF16_ONLY) == 0, TFB_ERR_ARG, "unknown tfb_mlp_residual_layernorm flags");
+    need(!ctx->grad_enabled, TFB_ERR_STATE, "tfb_mlp_residual_layernorm is inference-only: disable gradients first");
+    need(y != nullptr && h != nullptr, TFB_ERR_ARG, "null output");
+    x = C.dense_in(x, C.bf16_mode()), w_fc = C.dense_in(w_fc, C.bf16_mode()), b_fc = C.dense_in(b_fc);
+    w_proj = C.dense_in(w_proj, C.bf16_mode()), b_proj = C.dense_in(b_proj);
+    r = C.dense_in(r), gamma = C.dense_in(gamma), beta = C.dense_in(beta);
+    check_linear(C, x, w_fc, b_fc);
+    const int64_t F = C.T(w_fc).shape[1];
+    need(C.T(w_proj).ndim == 2 && C.T(w_proj).shape[0] == F, TFB_ERR_SHAPE,
+         "mlp projection must be [" + std::to_string(F) + ", N], got " + shape_str(C.T(w_proj)));
+    const int64_t N = C.T(w_proj).shape[1];
+    need(C.T(b_proj).numel == N && C.T(b_proj).ndim == 1, TFB_ERR_SHAPE,
+         "linear bias must be [" + std::to_string(N) + "]");
+    need(C.T(r).numel == C.T(x).rows() * N && C.T(r).cols() == N, TFB_ERR_SHAPE,
+         "residual must have the output's shape, got " + shape_str(C.T(r)));
+    need(C.T(gamma).numel == N && C.T(beta).numel == N, TFB_ERR_SHAPE,
+         "layernorm gain/shift must have " + std::to_string(N) + " elements");
+    need(N <= 2048, TFB_ERR_SHAPE, "layernorm rows longer than 2048 are not supported");
+    // the c_fc product leaves its partials; the projection sums them (+ bias, GELU) as
+    // it loads its input, then normalises its own chunk sum
+    bool ok1 = false;
+    GemmArgs g1 = linear_post_args(C, x, w_fc, b_fc, -1, POST_PARTIALS, nullptr, nullptr, &ok1);
+    g1.bias = nullptr;
+    ok1 = gemv_accepts(g1);
+    GemmArgs g2 = C.gemm_base();
+    const int64_t rows = C.T(x).rows();
+    g2.M = (int)rows, g2.N = (int)N, g2.K = (int)F;
+    set_b(g2, op_data(C, C.T(w_proj))), g2.ldb = N;
+    g2.ldc = N, g2.bias = C.T(b_proj).data, g2.resid = C.f32(C.T(r));
+    g2.post = POST_LN, g2.ln_gamma = C.T(gamma).data, g2.ln_beta = C.T(beta).data, g2.ln_eps = eps;
+    float* stand_in = reinterpret_cast<float*>(C.c->arena.base);
+    g2.C = stand_in, g2.ln_y = stand_in;
+    g2.a_part = stand_in, g2.a_bias = C.T(b_fc).data, g2.a_chunks = ok1 ? gemv_chunks(g1) : 0;
+    if (ok1 && gemv_accepts(g2)) {
+      const size_t wb = gemv_workspace_bytes(g1);
+      void* parts = C.scratch(wb);  // kept until the projection below has read it (stream order)
+      std::vector<int64_t> shp = shape_vec(C.T(x));
+      shp.back() = N;
+      int yh = C.make_output(shp);
+      int hh = C.make_output(shp);
+      uint16_t* hb = C.twin_data(ctx->tensors[hh]);
+      const bool only = hb && (flags & TFB_OUT_BF16_ONLY);
+      g1.C = nullptr;
+      C.run_gemm_ws(g1, parts, wb);
+      g2.a_part = static_cast<const float*>(parts);
+      g2.C = ctx->tensors[yh].data;
+      g2.ln_y = only ? nullptr : ctx->tensors[hh].data, g2.ln_ybf = hb;
+      C.run_gemm(g2);
+      if (hb) ctx->tensors[hh].bf_valid = true;
+      if (only) ctx->tensors[hh].f32_valid = false, ctx->tensors[hh].bf16_out = true;
+      *y = yh, *h = hh;
+      return;
+    }
+    tfb_tensor f;
+    int rc = tfb_linear_gelu(ctx, x, w_fc, b_fc, TFB_OUT_BF16_ONLY, &f);
+    if (rc) rethrow(rc);
+    rc = tfb_linear_residual_layernorm(ctx, f, w_proj, b_proj, r, gamma, beta, eps, flags, y, h);
+    if (rc) rethrow(rc);
+  });
+}
+
+int tfb_kv_attend_linear(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor x, tfb_tensor w, tfb_tensor b, int pos,
+                         int heads, tfb_tensor* y) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need(kv != nullptr && kv->ctx == ctx, TFB_ERR_ARG, "cache of another context");
+    need(y != nullptr, TFB_ERR_ARG, "null output");
+    x = C.dense_in(x, C.bf16_mode()), w = C.dense_in(w, C.bf16_mode()), b = C.dense_in(b);
+    check_linear(C, x, w, b);
+    const int Cc = kv->channels;
+    TensorRec& X = C.T(x);
+    need(X.ndim == 3 && X.shape[0] == kv->batch && X.shape[1] == 1 && C.T(w).shape[1] == 3LL * Cc, TFB_ERR_SHAPE,
+         "kv_attend_linear needs x [batch, 1, K] and w [K, 3C]");
+    need(layer >= 0 && layer < kv->layers, TFB_ERR_ARG, "no such layer");
+    need(pos >= 0 && pos < kv->tmax, TFB_ERR_SHAPE, "position past the cache length");
+    need(heads > 0 && Cc % heads == 0, TFB_ERR_SHAPE, "channels not divisible by heads");
+    bool ok = false;
+    GemmArgs g = linear_post_args(C, x, w, b, -1, POST_PARTIALS, nullptr, nullptr, &ok);
+    g.bias = nullptr;
+    ok = gemv_accepts(g) && kv_attend_takes_parts(Cc, heads) && !ctx->grad_enabled;
+    if (!ok) {
+      tfb_tensor qkv;
+      int rc = tfb_linear(ctx, x, w, b, &qkv);
+      if (rc) rethrow(rc);
+      rc = tfb_kv_attend(ctx, kv, layer, qkv, pos, heads, y);
+      if (rc) rethrow(rc);
+      return;
+    }
+    const size_t wb = gemv_workspace_bytes(g);
+    void* parts = C.scratch(wb);
+    g.C = nullptr;
+    C.run_gemm_ws(g, parts, wb);
+    const float scale = 1.f / std::sqrt((float)(Cc / heads));
+    int h = C.make_output({kv->batch, 1, Cc});
+    void* ws = C.scratch(std::max<size_t>(kv_attend_workspace_bytes(kv->batch, Cc, heads, pos), 256));
+    const double bytes = (double)kv->batch * Cc * (8.0 * (pos + 1) + 8.0 + 4.0 + 4.0);
+    const float* bias = C.T(b).data;
+    const int chunks = gemv_chunks(g);
+    C.timed(TFB_PROF_KV_ATTEND, bytes, [&] {
+      hip_check(kv_attend(nullptr, kv->data, ctx->tensors[h].data, layer, kv->batch, kv->tmax, Cc, heads, pos, scale,
+                          ws, C.s(), static_cast<const float*>(parts), chunks, bias),
+                "kv_attend");
+    });
+    *y = h;  // inference only: not recorded on the tape
   });
 }
 

@@ -14,8 +14,9 @@ from typing import Dict, List, Sequence
 
 import numpy as np
 
-from . import (AdamW, Context, KvCache, Tensor, add, causal_attention, embedding, gelu, layernorm, linear, linear_gelu,
-               linear_residual_layernorm, matmul_t, narrow, reshape, sample_topk, softmax_cross_entropy, tanh)
+from . import (AdamW, Context, KvCache, Tensor, add, causal_attention, embedding, gelu, layernorm, linear,
+               linear_residual_layernorm, matmul_t, mlp_residual_layernorm, narrow, reshape, sample_topk,
+               softmax_cross_entropy, tanh)
 
 
 def upload_params(ctx: Context, params: Dict[str, np.ndarray]) -> Dict[str, Tensor]:
@@ -108,20 +109,20 @@ class Gpt:
         C = P["wte.weight"].shape[1]
         x = add(embedding(P["wte.weight"], tokens, B),
                 reshape(embedding(P["wpe.weight"], self.positions(tmax)[pos:pos + 1], 1), (1, C)))
-        # each LayerNorm is folded into the chunk sum of the few-row product before it
-        # (the residual projection), and each GELU into that of the c_fc product:
-        # the same ops, fewer passes
+        # the same ops in fewer passes: each LayerNorm is folded into the chunk sum of
+        # the residual projection before it, the c_attn product's chunk sum into the
+        # cached attention's loads, and the MLP's hidden activation (c_fc and GELU)
+        # into the projection's loads
         h = layernorm(x, P["h.0.ln_1.weight"], P["h.0.ln_1.bias"], bf16_only=True)
         for i in range(self.n_layer):
             p = f"h.{i}."
-            qkv = linear(h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"])
-            a = kv.attend(i, qkv, pos, self.n_head)
+            a = kv.attend_linear(i, h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"], pos, self.n_head)
             x, h = linear_residual_layernorm(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"], x,
                                              P[p + "ln_2.weight"], P[p + "ln_2.bias"], bf16_only=True)
-            f = linear_gelu(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"], bf16_only=True)
             ln = f"h.{i + 1}.ln_1" if i + 1 < self.n_layer else "ln_f"
-            x, h = linear_residual_layernorm(f, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"], x,
-                                             P[ln + ".weight"], P[ln + ".bias"], bf16_only=True)
+            x, h = mlp_residual_layernorm(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"],
+                                          P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"], x,
+                                          P[ln + ".weight"], P[ln + ".bias"], bf16_only=True)
         return matmul_t(h, P["wte.weight"])
 
     def generate(self, prompts, steps: int, uniforms, k: int, temperature: float, on_step=None):
