@@ -241,13 +241,13 @@ def decode_bytes_per_step(s, B: int, prompt: int, n_new: int, precision: str) ->
     """Algorithmic HBM bytes of one decode step, averaged over the generation: every
     block weight and the tied LM-head table once (in the form the products read: bf16
     copies in the bf16 variant), the cached keys and values of all earlier positions
-    (fp32), and the logits written and read by the sampler."""
+    (fp32, or bf16 in the bf16 variant), and the logits written and read by the sampler."""
     C, V, nl = s.n_embd, s.vocab, s.n_layer
     w_block = nl * (C * 3 * C + C * C + C * 4 * C + 4 * C * C)
     ew = 2 if precision == "bf16" else 4
     weights = ew * (w_block + V * C)
     mean_len = prompt + (n_new - 1) / 2.0          # positions 0..pos read at pos = prompt-1+i, i < n_new
-    kv = nl * B * mean_len * C * 2 * 4
+    kv = nl * B * mean_len * C * 2 * ew             # the cache holds the variant's operand type
     logits = B * V * 4 * 2
     return weights + kv + logits
 

@@ -351,8 +351,11 @@ int tfb_sgd_step(tfb_ctx* ctx, const tfb_tensor* params, int n, float lr);
  * calls is recorded on the tape. */
 
 typedef struct tfb_kv tfb_kv;
-/* A key/value cache of `layers` x 2 x batch x tmax x channels fp32 values in the
- * persistent arena, zero-filled (tmax <= 16384). */
+/* A key/value cache of `layers` x 2 x batch x tmax x channels values in the
+ * persistent arena, zero-filled (tmax <= 16384): fp32, or bf16 (round to nearest
+ * even) when the context is in the bf16 variant at creation -- keys and values are
+ * operands of the q.k and p.v products, and the bf16 variant rounds every
+ * contraction operand to bf16; the attention arithmetic stays fp32. */
 int tfb_kv_create(tfb_ctx* ctx, int layers, int batch, int tmax, int channels, tfb_kv** out);
 /* Frees the handle and gives the cache's arena memory back: to the top of the
  * persistent end when nothing was allocated there after it, otherwise as a hole

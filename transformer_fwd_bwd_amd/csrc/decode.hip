@@ -1,9 +1,11 @@
 // KV-cached inference ([GPT2-4, "Generation with KV cache" and "Temperature
 // and Top-k"]).
 //
-// Cache layout: fp32 [L][2][B][Tmax][C] (keys then values of every layer);
-// position p of sequence b in layer l is one contiguous row of C floats, so a
-// head's slice is hs contiguous floats.
+// Cache layout: [L][2][B][Tmax][C] (keys then values of every layer); position
+// p of sequence b in layer l is one contiguous row of C values, so a head's slice
+// is hs contiguous values.  The values are fp32, or bf16 (round to nearest even)
+// in the bf16 variant, where keys and values are operands of the q.k and p.v
+// products like every other contraction operand there; arithmetic stays fp32.
 //
 // kv_attend: one workgroup per (sequence, head).  It appends the new token's
 // key and value at position pos, then computes the single-query attention
@@ -66,7 +68,15 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__global__ __launch_bounds__(NT) void kv_store_k(const float* __restrict__ qkv, int64_t T, int C, float* __restrict__ kv,
+// cache elements: fp32, or bf16 bits
+__device__ __forceinline__ float kv_get(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float kv_get(const uint16_t* p, int64_t i) { return __uint_as_float((unsigned)p[i] << 16); }
+__device__ __forceinline__ void kv_put(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void kv_put(uint16_t* p, int64_t i, float v) { p[i] = __builtin_bit_cast(uint16_t, (__bf16)v); }
+typedef uint16_t ku4 __attribute__((ext_vector_type(4)));
+
+template <typename KT>
+__global__ __launch_bounds__(NT) void kv_store_k(const float* __restrict__ qkv, int64_t T, int C, KT* __restrict__ kv,
                                                  int layer, int B, int Tmax, int pos0) {
   // qkv [B, T, 3C] -> cache rows pos0 .. pos0 + T - 1
   const int64_t n = (int64_t)B * T * C;
@@ -76,13 +86,14 @@ __global__ __launch_bounds__(NT) void kv_store_k(const float* __restrict__ qkv, 
     const int b = (int)(bt / T), t = (int)(bt % T);
     const float* src = qkv + bt * 3 * C;
     const int64_t row = (int64_t)b * Tmax + pos0 + t;
-    kv[((int64_t)(layer * 2 + 0) * B * Tmax + row) * C + c] = src[C + c];
-    kv[((int64_t)(layer * 2 + 1) * B * Tmax + row) * C + c] = src[2 * C + c];
+    kv_put(kv, ((int64_t)(layer * 2 + 0) * B * Tmax + row) * C + c, src[C + c]);
+    kv_put(kv, ((int64_t)(layer * 2 + 1) * B * Tmax + row) * C + c, src[2 * C + c]);
   }
 }
 
 // one workgroup per (b, head); qkv [B, 1, 3C]; y [B, 1, C]; scratch: Tmax floats of LDS
-__global__ __launch_bounds__(NT) void kv_attend_k(const float* __restrict__ qkv, float* __restrict__ kv,
+template <typename KT>
+__global__ __launch_bounds__(NT) void kv_attend_k(const float* __restrict__ qkv, KT* __restrict__ kv,
                                                   float* __restrict__ y, int layer, int B, int Tmax, int C, int H,
                                                   int pos, float scale) {
   extern __shared__ float sc[];  // [pos + 1] scores, then 4 x hs partial outputs
@@ -90,18 +101,18 @@ __global__ __launch_bounds__(NT) void kv_attend_k(const float* __restrict__ qkv,
   const int b = blockIdx.x / H, hd = blockIdx.x % H;
   const int hs = C / H;
   const float* src = qkv + (int64_t)b * 3 * C;
-  float* Kc = kv + ((int64_t)(layer * 2 + 0) * B + b) * Tmax * C + hd * hs;
-  float* Vc = kv + ((int64_t)(layer * 2 + 1) * B + b) * Tmax * C + hd * hs;
+  KT* Kc = kv + ((int64_t)(layer * 2 + 0) * B + b) * Tmax * C + hd * hs;
+  KT* Vc = kv + ((int64_t)(layer * 2 + 1) * B + b) * Tmax * C + hd * hs;
   for (int d = threadIdx.x; d < hs; d += NT) {
-    Kc[(int64_t)pos * C + d] = src[C + hd * hs + d];
-    Vc[(int64_t)pos * C + d] = src[2 * C + hd * hs + d];
+    kv_put(Kc, (int64_t)pos * C + d, src[C + hd * hs + d]);
+    kv_put(Vc, (int64_t)pos * C + d, src[2 * C + hd * hs + d]);
   }
   __syncthreads();
   const float* q = src + hd * hs;
   for (int j = threadIdx.x; j <= pos; j += NT) {
-    const float* kr = Kc + (int64_t)j * C;
+    const KT* kr = Kc + (int64_t)j * C;
     float s = 0.f;
-    for (int d = 0; d < hs; ++d) s += q[d] * kr[d];
+    for (int d = 0; d < hs; ++d) s += q[d] * kv_get(kr, d);
     sc[j] = s * scale;
   }
   __syncthreads();
@@ -123,7 +134,7 @@ __global__ __launch_bounds__(NT) void kv_attend_k(const float* __restrict__ qkv,
   for (int d0 = 0; d0 < hs; d0 += 64) {
     float acc = 0.f;
     if (d0 + d < hs)
-      for (int j = grp; j <= pos; j += NT / 64) acc += sc[j] * Vc[(int64_t)j * C + d0 + d];
+      for (int j = grp; j <= pos; j += NT / 64) acc += sc[j] * kv_get(Vc, (int64_t)j * C + d0 + d);
     part[grp * 64 + d] = acc;
     __syncthreads();
     if (grp == 0 && d0 + d < hs) {
@@ -171,8 +182,21 @@ __device__ __forceinline__ kf4 qkv4(const QkvSrc& q, int B, int C, int b, int i)
   return v + *reinterpret_cast<const kf4*>(q.bias + i);
 }
 
-template <int HS>
-__global__ __launch_bounds__(256) void kv_attend_part_k(QkvSrc qs, float* __restrict__ kv,
+// four consecutive cache values as fp32
+__device__ __forceinline__ kf4 kv_get4(const float* p) { return *reinterpret_cast<const kf4*>(p); }
+__device__ __forceinline__ kf4 kv_get4(const uint16_t* p) {
+  const ku4 v = *reinterpret_cast<const ku4*>(p);
+  return kf4{__uint_as_float((unsigned)v.x << 16), __uint_as_float((unsigned)v.y << 16),
+             __uint_as_float((unsigned)v.z << 16), __uint_as_float((unsigned)v.w << 16)};
+}
+__device__ __forceinline__ void kv_put4(float* p, kf4 v) { *reinterpret_cast<kf4*>(p) = v; }
+__device__ __forceinline__ void kv_put4(uint16_t* p, kf4 v) {
+  *reinterpret_cast<ku4*>(p) = ku4{__builtin_bit_cast(uint16_t, (__bf16)v.x), __builtin_bit_cast(uint16_t, (__bf16)v.y),
+                                   __builtin_bit_cast(uint16_t, (__bf16)v.z), __builtin_bit_cast(uint16_t, (__bf16)v.w)};
+}
+
+template <int HS, typename KT>
+__global__ __launch_bounds__(256) void kv_attend_part_k(QkvSrc qs, KT* __restrict__ kv,
                                                         float* __restrict__ pacc, float* __restrict__ pml, int layer,
                                                         int B, int Tmax, int C, int H, int pos, int S, float scale) {
   constexpr int LPR = HS / 4, RPI = 64 / LPR, PW = KVP / 4, IT = PW / RPI;
@@ -180,13 +204,13 @@ __global__ __launch_bounds__(256) void kv_attend_part_k(QkvSrc qs, float* __rest
   __shared__ kf4 wacc[4][LPR];
   const int s = blockIdx.x % S, bh = blockIdx.x / S;
   const int b = bh / H, hd = bh % H;
-  float* Kc = kv + ((int64_t)(layer * 2 + 0) * B + b) * Tmax * C + hd * HS;
-  float* Vc = kv + ((int64_t)(layer * 2 + 1) * B + b) * Tmax * C + hd * HS;
+  KT* Kc = kv + ((int64_t)(layer * 2 + 0) * B + b) * Tmax * C + hd * HS;
+  KT* Vc = kv + ((int64_t)(layer * 2 + 1) * B + b) * Tmax * C + hd * HS;
   const int j_lo = s * KVP, j_hi = min(j_lo + KVP, pos + 1);
   if (pos < j_lo + KVP) {  // the last block: append the new token's key and value (uniform per block)
     for (int d4 = threadIdx.x; d4 < HS / 4; d4 += 256) {
-      *reinterpret_cast<kf4*>(Kc + (int64_t)pos * C + 4 * d4) = qkv4(qs, B, C, b, C + hd * HS + 4 * d4);
-      *reinterpret_cast<kf4*>(Vc + (int64_t)pos * C + 4 * d4) = qkv4(qs, B, C, b, 2 * C + hd * HS + 4 * d4);
+      kv_put4(Kc + (int64_t)pos * C + 4 * d4, qkv4(qs, B, C, b, C + hd * HS + 4 * d4));
+      kv_put4(Vc + (int64_t)pos * C + 4 * d4, qkv4(qs, B, C, b, 2 * C + hd * HS + 4 * d4));
     }
     __syncthreads();
   }
@@ -200,8 +224,8 @@ __global__ __launch_bounds__(256) void kv_attend_part_k(QkvSrc qs, float* __rest
   for (int it = 0; it < IT; ++it) {
     const int j = jw + it * RPI + r;
     const int64_t row = (int64_t)(j < j_hi ? j : j_lo) * C + c * 4;
-    kr[it] = *reinterpret_cast<const kf4*>(Kc + row);
-    vr[it] = *reinterpret_cast<const kf4*>(Vc + row);
+    kr[it] = kv_get4(Kc + row);
+    vr[it] = kv_get4(Vc + row);
   }
   float sc[IT];
 #pragma unroll
@@ -549,12 +573,17 @@ __global__ __launch_bounds__(SR) void sample_topk_reg_k(const float* __restrict_
 
 }  // namespace
 
-hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, int B, int Tmax, int pos0,
+hipError_t kv_store(const float* qkv, int64_t T, int C, void* kv, bool kv_bf16, int layer, int B, int Tmax, int pos0,
                     hipStream_t s) {
   const int64_t n = (int64_t)B * T * C;
   if (n <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)std::min<int64_t>((n + NT - 1) / NT, 65536);
-  run_kernel(kv_store_k, dim3(blocks), dim3(NT), 0, s, qkv, T, C, kv, layer, B, Tmax, pos0);
+  if (kv_bf16)
+    run_kernel(kv_store_k<uint16_t>, dim3(blocks), dim3(NT), 0, s, qkv, T, C, static_cast<uint16_t*>(kv), layer, B,
+               Tmax, pos0);
+  else
+    run_kernel(kv_store_k<float>, dim3(blocks), dim3(NT), 0, s, qkv, T, C, static_cast<float*>(kv), layer, B, Tmax,
+               pos0);
   return hipGetLastError();
 }
 
@@ -571,13 +600,14 @@ size_t kv_attend_workspace_bytes(int B, int C, int H, int pos) {
 
 bool kv_attend_takes_parts(int C, int H) { return kv_split_ok(C, H); }
 
-hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, int Tmax, int C, int H, int pos,
-                     float scale, void* ws, hipStream_t s, const float* qkv_part, int qkv_chunks,
-                     const float* qkv_bias) {
+template <typename KT>
+hipError_t kv_attend_t(const float* qkv, KT* kv, float* y, int layer, int B, int Tmax, int C, int H, int pos,
+                       float scale, void* ws, hipStream_t s, const float* qkv_part, int qkv_chunks,
+                       const float* qkv_bias) {
   if (!kv_split_ok(C, H) || ws == nullptr) {
     if (qkv_part) return hipErrorInvalidValue;  // the unsplit kernel reads stored qkv only
     const size_t shmem = ((size_t)Tmax + 4 * 64) * sizeof(float);
-    run_kernel(kv_attend_k, dim3(B * H), dim3(NT), shmem, s, qkv, kv, y, layer, B, Tmax, C, H, pos, scale);
+    run_kernel(kv_attend_k<KT>, dim3(B * H), dim3(NT), shmem, s, qkv, kv, y, layer, B, Tmax, C, H, pos, scale);
     return hipGetLastError();
   }
   const QkvSrc qs{qkv, qkv_part, qkv_bias, qkv_chunks};
@@ -586,14 +616,25 @@ hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, in
   float* pml = pacc + (int64_t)B * H * S * hs;
   const dim3 grid((unsigned)(B * H * S));
   if (hs == 32)
-    run_kernel(kv_attend_part_k<32>, grid, dim3(256), 0, s, qs, kv, pacc, pml, layer, B, Tmax, C, H, pos, S, scale);
+    run_kernel(kv_attend_part_k<32, KT>, grid, dim3(256), 0, s, qs, kv, pacc, pml, layer, B, Tmax, C, H, pos, S, scale);
   else if (hs == 64)
-    run_kernel(kv_attend_part_k<64>, grid, dim3(256), 0, s, qs, kv, pacc, pml, layer, B, Tmax, C, H, pos, S, scale);
+    run_kernel(kv_attend_part_k<64, KT>, grid, dim3(256), 0, s, qs, kv, pacc, pml, layer, B, Tmax, C, H, pos, S, scale);
   else
-    run_kernel(kv_attend_part_k<128>, grid, dim3(256), 0, s, qs, kv, pacc, pml, layer, B, Tmax, C, H, pos, S, scale);
+    run_kernel(kv_attend_part_k<128, KT>, grid, dim3(256), 0, s, qs, kv, pacc, pml, layer, B, Tmax, C, H, pos, S,
+               scale);
   const int n = B * H * hs;
   run_kernel(kv_attend_merge_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pacc, pml, y, B * H, hs, S);
   return hipGetLastError();
+}
+
+hipError_t kv_attend(const float* qkv, void* kv, bool kv_bf16, float* y, int layer, int B, int Tmax, int C, int H,
+                     int pos, float scale, void* ws, hipStream_t s, const float* qkv_part, int qkv_chunks,
+                     const float* qkv_bias) {
+  if (kv_bf16)
+    return kv_attend_t(qkv, static_cast<uint16_t*>(kv), y, layer, B, Tmax, C, H, pos, scale, ws, s, qkv_part,
+                       qkv_chunks, qkv_bias);
+  return kv_attend_t(qkv, static_cast<float*>(kv), y, layer, B, Tmax, C, H, pos, scale, ws, s, qkv_part, qkv_chunks,
+                     qkv_bias);
 }
 
 hipError_t sample_topk(const float* logits, int64_t ld, int B, int V, int k, float temperature, const double* u,

@@ -249,8 +249,8 @@ hipError_t flash_attention_bwd(const uint16_t* qkv, const float* y, const float*
                                const float* lse, float* D, float* dqkv, uint16_t* dqkv_bf, float beta, int B, int T,
                                int H, int C, float scale, hipStream_t s, const uint16_t* ybf = nullptr);
 
-// ---- KV-cached inference (decode.hip); cache fp32 [L][2][B][Tmax][C]
-hipError_t kv_store(const float* qkv, int64_t T, int C, float* kv, int layer, int B, int Tmax, int pos0,
+// ---- KV-cached inference (decode.hip); cache [L][2][B][Tmax][C], fp32 or (kv_bf16) bf16
+hipError_t kv_store(const float* qkv, int64_t T, int C, void* kv, bool kv_bf16, int layer, int B, int Tmax, int pos0,
                     hipStream_t s);
 // ws: kv_attend_workspace_bytes(B, C, H, pos) bytes of scratch (partial results per block of positions)
 size_t kv_attend_workspace_bytes(int B, int C, int H, int pos);
@@ -258,9 +258,9 @@ size_t kv_attend_workspace_bytes(int B, int C, int H, int pos);
 // qkv_part[c][B][3C] plus qkv_bias, the partials of the few-row c_attn product
 // (POST_PARTIALS); taken only where kv_attend_takes_parts(C, H)
 bool kv_attend_takes_parts(int C, int H);
-hipError_t kv_attend(const float* qkv, float* kv, float* y, int layer, int B, int Tmax, int C, int H, int pos,
-                     float scale, void* ws, hipStream_t s,
-                     const float* qkv_part = nullptr, int qkv_chunks = 0, const float* qkv_bias = nullptr);
+hipError_t kv_attend(const float* qkv, void* kv, bool kv_bf16, float* y, int layer, int B, int Tmax, int C, int H,
+                     int pos, float scale, void* ws, hipStream_t s, const float* qkv_part = nullptr, int qkv_chunks = 0,
+                     const float* qkv_bias = nullptr);
 hipError_t sample_topk(const float* logits, int64_t ld, int B, int V, int k, float temperature, const double* u,
                        int32_t* out, hipStream_t s);
 

@@ -223,7 +223,8 @@ struct tfb_ctx {
 struct tfb_kv {
   tfb_ctx* ctx = nullptr;
   int layers = 0, batch = 0, tmax = 0, channels = 0;
-  float* data = nullptr;  // persistent arena: [layers][2][batch][tmax][channels] fp32
+  void* data = nullptr;  // persistent arena: [layers][2][batch][tmax][channels], fp32 or bf16
+  bool bf16 = false;     // made in the bf16 variant: keys and values stored as bf16
   size_t off = 0, end = 0;  // its arena range [off, end)
 };
 
@@ -1843,12 +1844,13 @@ int tfb_kv_attend_linear(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor x, tfb_
     const float scale = 1.f / std::sqrt((float)(Cc / heads));
     int h = C.make_output({kv->batch, 1, Cc});
     void* ws = C.scratch(std::max<size_t>(kv_attend_workspace_bytes(kv->batch, Cc, heads, pos), 256));
-    const double bytes = (double)kv->batch * Cc * (8.0 * (pos + 1) + 8.0 + 4.0 + 4.0);
+    const double e = kv->bf16 ? 2.0 : 4.0;
+    const double bytes = (double)kv->batch * Cc * (2 * e * (pos + 1) + 2 * e + 4.0 + 4.0);
     const float* bias = C.T(b).data;
     const int chunks = gemv_chunks(g);
     C.timed(TFB_PROF_KV_ATTEND, bytes, [&] {
-      hip_check(kv_attend(nullptr, kv->data, ctx->tensors[h].data, layer, kv->batch, kv->tmax, Cc, heads, pos, scale,
-                          ws, C.s(), static_cast<const float*>(parts), chunks, bias),
+      hip_check(kv_attend(nullptr, kv->data, kv->bf16, ctx->tensors[h].data, layer, kv->batch, kv->tmax, Cc, heads,
+                          pos, scale, ws, C.s(), static_cast<const float*>(parts), chunks, bias),
                 "kv_attend");
     });
     *y = h;  // inference only: not recorded on the tape
@@ -2394,12 +2396,15 @@ int tfb_kv_create(tfb_ctx* ctx, int layers, int batch, int tmax, int channels, t
     need(layers > 0 && batch > 0 && tmax > 0 && channels > 0, TFB_ERR_SHAPE, "kv cache sizes must be positive");
     need(tmax <= 16384, TFB_ERR_SHAPE, "kv cache longer than 16384 positions is not supported");
     const size_t n = (size_t)layers * 2 * batch * tmax * channels;
-    const size_t off = ctx->arena.alloc_persist(n * sizeof(float));
+    const bool bf = C.bf16_mode();
+    const size_t bytes = Arena::up(n * (bf ? 2 : 4));
+    const size_t off = ctx->arena.alloc_persist(bytes);
     float* p = reinterpret_cast<float*>(ctx->arena.base + off);
-    hip_check(fill(p, 0.f, (int64_t)n, C.s()), "kv clear");
+    hip_check(fill(p, 0.f, (int64_t)(bytes / 4), C.s()), "kv clear");  // zero bits: 0.0 in either form
     tfb_kv* kv = new tfb_kv();
     kv->ctx = ctx, kv->layers = layers, kv->batch = batch, kv->tmax = tmax, kv->channels = channels, kv->data = p;
-    kv->off = off, kv->end = off + Arena::up(n * sizeof(float));
+    kv->bf16 = bf;
+    kv->off = off, kv->end = off + bytes;
     *out = kv;
   });
 }
@@ -2422,7 +2427,7 @@ int tfb_kv_store(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos0) 
          "kv_store needs qkv [batch, T, 3C], got " + shape_str(Q));
     need(layer >= 0 && layer < kv->layers, TFB_ERR_ARG, "no such layer");
     need(pos0 >= 0 && pos0 + Q.shape[1] <= kv->tmax, TFB_ERR_SHAPE, "positions past the cache length");
-    hip_check(kv_store(Q.data, Q.shape[1], kv->channels, kv->data, layer, kv->batch, kv->tmax, pos0, C.s()),
+    hip_check(kv_store(C.f32(Q), Q.shape[1], kv->channels, kv->data, kv->bf16, layer, kv->batch, kv->tmax, pos0, C.s()),
               "kv_store");
   });
 }
@@ -2443,12 +2448,13 @@ int tfb_kv_attend(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos, 
     const float* qd = Q.data;
     int h = C.make_output({kv->batch, 1, Cc});
     void* ws = C.scratch(std::max<size_t>(kv_attend_workspace_bytes(kv->batch, Cc, heads, pos), 256));
-    // every cached key and value of positions 0..pos (fp32), the new one stored, q read, y written
-    const double bytes = (double)kv->batch * Cc * (8.0 * (pos + 1) + 8.0 + 4.0 + 4.0);
+    // every cached key and value of positions 0..pos, the new one stored, q read, y written
+    const double e = kv->bf16 ? 2.0 : 4.0;
+    const double bytes = (double)kv->batch * Cc * (2 * e * (pos + 1) + 2 * e + 4.0 + 4.0);
     C.timed(TFB_PROF_KV_ATTEND, bytes, [&] {
-      hip_check(
-          kv_attend(qd, kv->data, ctx->tensors[h].data, layer, kv->batch, kv->tmax, Cc, heads, pos, scale, ws, C.s()),
-          "kv_attend");
+      hip_check(kv_attend(qd, kv->data, kv->bf16, ctx->tensors[h].data, layer, kv->batch, kv->tmax, Cc, heads, pos,
+                          scale, ws, C.s()),
+                "kv_attend");
     });
     *y = h;  // inference only: not recorded on the tape
   });
