@@ -14,7 +14,8 @@ Beside it the line carries:
                 `families`: every timed kernel family's achieved rate against
                 its own bound (MFMA peak for the contractions and the fused
                 attention, HBM peak for the rest), all from HIP events on the
-                library's stream over --steps extra steps
+                library's stream over --steps extra steps; `hbm_reference`: what
+                a plain copy and a plain fill reach on this GPU
   fp32          the fp32 variant of the same step: ms/step, tokens/s and its
                 contraction roofline against the fp32 MFMA peak
   decode        KV-cached generation at the same shape (16 prompts of 768
@@ -147,6 +148,30 @@ def copy_probe():
         torch.neg(src, out=dst)                   # one streaming kernel: reads 1 GiB, writes 1 GiB
     torch.cuda.synchronize()
     del src, dst
+
+
+def hbm_reference():
+    """Achieved rate of plain streaming kernels on this GPU (torch's own, 1 GiB per
+    stream): the practical ceiling the bandwidth-bound families are measured against
+    beside the 8 TB/s published peak."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, nbytes in (("copy_1r1w", lambda: b.copy_(a), 8 * n), ("fill_1w", lambda: b.fill_(1.0), 4 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_gbs"] = round(nbytes / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def families(ctx, steps: int, precision: str):
@@ -360,6 +385,7 @@ def main():
         "loss_last_step": round(r["last_loss"], 5) if r["last_loss"] is not None else None,
     }
     out["roofline"]["families"] = r["families"]
+    out["roofline"]["hbm_reference"] = hbm_reference()
     if args.precision == "bf16" and not args.no_fp32:
         k32, w32 = min(args.steps, 8), min(args.warmup, 2)
         r32 = train_leg("fp32", B, L, k32, w32, arena_gb)
