@@ -292,6 +292,32 @@ def test_linear_one_tile_per_cu(ctx, case):
     assert_close(grads[0][-100:], rgrads[0][-100:], GRAD_TOL["bf16"], "dx, last rows")
 
 
+@pytest.mark.parametrize("case", ["nt_fwd", "nn_fwd", "tn_dw"])
+def test_large_products_on_256_tiles(ctx, case):
+    """Products with at least 512 output tiles of 256x256 in the bf16 variant take
+    the kernel that loads its operands straight into LDS: the LM-head shapes, here
+    ragged in every dimension.  nt_fwd: x @ w^T with K = 200 (the last k-tile of
+    both k-contiguous operands is cleared past K) and 8190 columns (a padded row
+    pitch, a partial last group of four); nn_fwd: x @ w with K = 200; tn_dw: the
+    weight gradient of x @ w^T, 16300 x 2048 over 520 rows."""
+    ctx.set_precision("bf16")
+    if case == "nt_fwd":
+        arrays, build, ob, shape = [rnd(141, (4100, 200)), rnd(142, (8190, 200), 0.1)], T.matmul_t, E.matmul_t, (4100, 8190)
+    elif case == "nn_fwd":
+        arrays, build, ob, shape = [rnd(143, (4100, 200)), rnd(144, (200, 8192), 0.1)], T.matmul, E.matmul, (4100, 8192)
+    else:
+        arrays, build, ob, shape = [rnd(145, (520, 2048)), rnd(146, (16300, 2048), 0.02)], T.matmul_t, E.matmul_t, (520, 16300)
+    R = rnd(147, shape)
+    out, grads = gpu_op_with_grads(ctx, build, arrays, R)
+    ref, rgrads = oracle_op_with_grads(ob, arrays, R)
+    ctx.set_precision("fp32")
+    assert_close(out, ref, FWD_TOL["bf16"], "forward")
+    assert_close(out[-60:, -70:], ref[-60:, -70:], FWD_TOL["bf16"], "forward, last tile corner")
+    for i, (g, r) in enumerate(zip(grads, rgrads)):
+        assert_close(g, r, GRAD_TOL["bf16"], f"grad {i}")
+    assert_close(grads[1][-60:], rgrads[1][-60:], GRAD_TOL["bf16"], "grad 1, last rows")
+
+
 def test_linear_long_k_split(ctx):
     # a long reduction (the dW contractions of the GPT have K = 8192) takes the split-K path
     check(ctx, "fp32", T.linear, lambda x, w, b: E.add(E.matmul(x, w), b),

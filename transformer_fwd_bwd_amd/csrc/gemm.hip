@@ -48,6 +48,9 @@ constexpr int KALIGN = 64;  // split-K chunks are multiples of this (and of ever
 #ifndef GEMM_PIPE
 #define GEMM_PIPE 1
 #endif
+#ifndef GEMM_DMA_TILES
+#define GEMM_DMA_TILES 512   // products with at least this many 256x256 tiles take gemm_dma_kernel
+#endif
 #ifndef GEMM_GROUP_M
 #define GEMM_GROUP_M 8       // tile rows per raster group
 #endif
@@ -691,6 +694,244 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large products with both operands stored as bf16 (the LM head and its weight
+// gradient): 256x256 tiles, eight waves of 128x64, operands loaded from global
+// memory straight into LDS (buffer_load ... lds), two LDS stages of 64-deep
+// k-tiles.  A tile this size does twice the MFMA work per byte fetched of a
+// 128x128 one, and the loads need neither staging registers nor LDS stores.
+//
+// LDS layout.  One load instruction moves 64 lanes x 16 bytes into 1 KB of LDS
+// at consecutive addresses, so the layout is chosen through which global chunk
+// each lane fetches:
+//   k-contiguous operand: rows of 64 k (128 bytes); 16-byte chunk p of row r
+//     holds k-chunk p ^ ((r >> 1) & 7), so the 16 rows a fragment read touches
+//     at once cover all 64 banks;
+//   m- or n-contiguous operand: k-rows of 256 elements (512 bytes); 64-byte
+//     block b of k-row k holds column block b ^ (k & 3), so the four k-rows a
+//     transposing read (ds_read_b64_tr_b16) touches at once cover all banks.
+// Buffer loads return zeros past the operand's last element: rows and columns
+// beyond M, N or K read nothing outside the operand.  In a k-tile that runs past
+// K, the columns beyond K of a k-contiguous operand (the next row's elements)
+// are cleared in LDS before use.
+namespace dma {
+
+constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 4, TM = 4, TN = 2;
+constexpr int NT = WM * WN * 64;
+constexpr int OPB = 256 * BK * 2;  // bytes of one operand's k-tile
+constexpr int STAGE = 2 * OPB;
+constexpr int EP = TN * 32 + 4;    // epilogue row pitch (floats)
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct Args {
+  const void* A;
+  const void* B;
+  float* C;
+  uint16_t* Cbf;
+  const float* bias;
+  const float* resid;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  float alpha, beta;
+  int skipc;
+  int tiles_m, tiles_n, group_m;
+  int a_bytes, b_bytes;  // readable bytes of A and B
+};
+
+// Per-lane global byte offsets of one operand's share of a k-tile (k-tile 0):
+// wave w issues the 1 KB segments w, w + 8, w + 16, w + 24.
+template <bool RC>
+__device__ __forceinline__ void seg_offsets(int voff[4], int r0, int64_t ld, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = i * 8 + wave;
+    if constexpr (!RC) {  // 8 rows of 128 bytes per segment
+      const int r = s * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      voff[i] = (int)(((int64_t)(r0 + r) * ld + c * 8) * 2);
+    } else {              // 2 k-rows of 512 bytes per segment
+      const int k = s * 2 + (lane >> 5), p = lane & 31;
+      const int c = (((p >> 2) ^ (k & 3)) << 2) | (p & 3);
+      voff[i] = (int)(((int64_t)k * ld + r0 + 8 * c) * 2);
+    }
+  }
+}
+
+__device__ __forceinline__ void load_segs(__amdgpu_buffer_rsrc_t rs, char* stage, const int voff[4], int adv,
+                                          int wave) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage + (i * 8 + wave) * 1024), 16, voff[i] + adv, 0, 0,
+                                             0);
+}
+
+// k-contiguous layout: the 8 k of the MFMA fragment of row `row`, k-step q
+__device__ __forceinline__ bf16x8 frag_rows(const char* st, int row, int q, int lane) {
+  const int c = 2 * q + (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(st + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+}
+// m/n-contiguous layout: the fragment of column block blk (32 columns), k-step q
+__device__ __forceinline__ bf16x8 frag_cols(const char* st, int blk, int q, int lane) {
+  const int tr_row = 8 * (lane >> 5) + ((lane & 15) >> 2), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int k = q * 16 + tr_row;
+  const char* p = st + k * 512 + ((blk ^ (k & 3)) << 6) + tr_col * 2;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 2048));
+  const v8i16 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// clear k-columns kr..63 of a k-contiguous operand's k-tile in LDS
+__device__ __forceinline__ void clear_tail(char* st, int kr, int tid) {
+  for (int u = tid; u < 256 * 8; u += NT) {
+    const int r = u >> 3, p = u & 7, c = p ^ ((r >> 1) & 7);
+    unsigned short* e = reinterpret_cast<unsigned short*>(st + r * 128 + p * 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c * 8 + j >= kr) e[j] = 0;
+  }
+}
+
+}  // namespace dma
+
+template <bool A_RC, bool B_KC>
+__global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
+  using namespace dma;
+  constexpr bool B_RC = !B_KC;
+  constexpr int SMEM = 2 * STAGE;
+  static_assert(WM * WN * 32 * EP * 4 <= SMEM, "epilogue staging fits in the operand stages");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  // the XCD-contiguous, row-grouped tile order of gemm_kernel
+  const int total = (int)gridDim.x;
+  int t;
+  {
+    const int w = blockIdx.x, xcd = w & 7, per = total >> 3, rem = total & 7;
+    t = xcd * per + min(xcd, rem) + (w >> 3);
+  }
+  int tm, tn;
+  {
+    const int gm = g.group_m, band = gm * g.tiles_n, first = (t / band) * gm;
+    const int rows = min(g.tiles_m - first, gm);
+    t -= (first / gm) * band;
+    tm = first + t % rows;
+    tn = t / rows;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, g.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, (short)0, g.b_bytes, 0x00020000);
+  int va[4], vb[4];
+  seg_offsets<A_RC>(va, m0, g.lda, wave, lane);
+  seg_offsets<B_RC>(vb, n0, g.ldb, wave, lane);
+  const int adv_a = A_RC ? (int)(BK * g.lda * 2) : BK * 2;
+  const int adv_b = B_RC ? (int)(BK * g.ldb * 2) : BK * 2;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lrow = lane & 31;
+  const int nt = (g.K + BK - 1) / BK, kr = g.K - (nt - 1) * BK;  // kr: k in the last k-tile
+  load_segs(ra, smem, va, 0, wave);
+  load_segs(rb, smem + OPB, vb, 0, wave);
+  // k-tile kt is multiplied out of stage kt % 2 while k-tile kt + 1 loads into
+  // the other: its fragments are read first, then the next loads are issued
+  // (the compiler waits for every outstanding LDS load before an LDS read, so
+  // the reads must precede them), then the MFMAs run.
+  for (int kt = 0; kt < nt; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of k-tile kt is in LDS
+    __syncthreads();                     // everyone's is; everyone is done reading k-tile kt - 1
+    char* As = smem + (kt & 1) * STAGE;
+    char* Bs = As + OPB;
+    if (kt == nt - 1 && kr < BK && (!A_RC || B_KC)) {
+      if constexpr (!A_RC) clear_tail(As, kr, tid);
+      if constexpr (B_KC) clear_tail(Bs, kr, tid);
+      __syncthreads();
+    }
+    bf16x8 af[BK / 16][TM], bf[BK / 16][TN];
+#pragma unroll
+    for (int q = 0; q < BK / 16; ++q) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[q][i] = A_RC ? frag_cols(As, wm * TM + i, q, lane) : frag_rows(As, wm * TM * 32 + i * 32 + lrow, q, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[q][j] = B_RC ? frag_cols(Bs, wn * TN + j, q, lane) : frag_rows(Bs, wn * TN * 32 + j * 32 + lrow, q, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nt) {
+      char* nx = smem + ((kt + 1) & 1) * STAGE;  // last read in iteration kt - 1, before the barrier above
+      load_segs(ra, nx, va, (kt + 1) * adv_a, wave);
+      load_segs(rb, nx + OPB, vb, (kt + 1) * adv_b, wave);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < BK / 16; ++q)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[q][j], af[q][i], acc[i][j], 0, 0, 0);
+  }
+
+  // Epilogue as in gemm_kernel: each wave restages a 32-row slab of its blocks
+  // (C^T per block: register r holds row lane%32, column 8(r/4) + 4(lane/32) + r%4)
+  // through its own LDS region into whole rows.
+  __syncthreads();
+  const int lhalf = lane >> 5;
+  float* E = reinterpret_cast<float*>(smem) + wave * 32 * EP;
+  constexpr int C4 = TN * 8;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f4*>(E + lrow * EP + j * 32 + 8 * q + 4 * lhalf) =
+            f4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 32 * C4 / 64; ++it) {
+      const int f = it * 64 + lane, r = f / C4, c4 = f % C4;
+      f4 v = *reinterpret_cast<const f4*>(E + r * EP + c4 * 4) * g.alpha;
+      const int m = m0 + wm * TM * 32 + i * 32 + r, n = n0 + wn * TN * 32 + c4 * 4;
+      if (m >= g.M || n >= g.N) continue;
+      float* row = g.C + (int64_t)m * g.ldc;
+      if (n + 3 < g.N) {
+        if (g.bias) v += *reinterpret_cast<const f4*>(g.bias + n);
+        f4* dst = reinterpret_cast<f4*>(row + n);
+        if (g.beta != 0.f) v += g.beta * *dst;
+        if (g.resid) v += *reinterpret_cast<const f4*>(g.resid + (int64_t)m * g.ldc + n);
+        if (!g.skipc) *dst = v;
+        if (g.Cbf) *reinterpret_cast<u16x4*>(g.Cbf + (int64_t)m * g.ldc + n) = bf16x4_bits(v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (n + e >= g.N) break;
+          float x = v[e];
+          if (g.bias) x += g.bias[n + e];
+          if (g.beta != 0.f) x += g.beta * row[n + e];
+          if (g.resid) x += g.resid[(int64_t)m * g.ldc + n + e];
+          if (!g.skipc) row[n + e] = x;
+          if (g.Cbf) g.Cbf[(int64_t)m * g.ldc + n + e] = bf16_bits(x);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // The same over float4 (N, ldc multiples of 4, 16-byte aligned C and bias)
 __global__ void splitk_reduce4(const f4* __restrict__ ws, int splits, int M, int N4, float* C, int64_t ldc,
                                int batch_div, int64_t sc1, int64_t sc2, float beta, const f4* bias, uint16_t* Cbf,
@@ -830,6 +1071,44 @@ hipError_t launch_prec(const KArgs& ka, int bk, dim3 grid, hipStream_t s) {
   return launch_layout<WM, WN, TM, TN, 32, true, false, false>(ka, grid, s);
 }
 
+// gemm_dma_kernel's conditions: both operands bf16 with 16-byte rows, one
+// product, no mask, a vector epilogue, enough 256x256 tiles to fill the GPU
+// twice, and every byte offset the loads form within 31 bits.
+bool dma_fits(const GemmArgs& g) {
+  auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+  if (g.prec != PREC_BF16 || !g.a_bf16 || !g.b_bf16 || g.batch != 1 || g.causal_a != CAUSAL_NONE || g.causal_out)
+    return false;
+  if (g.K < 1 || g.lda % 8 || g.ldb % 8 || !al(g.A, 16) || !al(g.B, 16)) return false;
+  if (g.ldc % 4 || !al(g.C, 16) || !al(g.bias, 16) || !al(g.resid, 16) || !al(g.Cbf, 8)) return false;
+  const int64_t tm = (g.M + 255) / 256, tn = (g.N + 255) / 256;
+  if (tm * tn < GEMM_DMA_TILES) return false;
+  const int64_t kp = (g.K + 63) / 64 * 64;
+  const int64_t reach_a = g.a_mcontig ? (kp - 1) * g.lda + tm * 256 : (tm * 256 - 1) * g.lda + kp;
+  const int64_t reach_b = g.b_kcontig ? (tn * 256 - 1) * g.ldb + kp : (kp - 1) * g.ldb + tn * 256;
+  return 2 * std::max(reach_a, reach_b) < ((int64_t)1 << 31) - 64;
+}
+
+hipError_t launch_dma(const GemmArgs& g, int group_m, hipStream_t s) {
+  dma::Args a;
+  a.A = g.A, a.B = g.B, a.C = g.C, a.Cbf = g.Cbf, a.bias = g.bias, a.resid = g.resid;
+  a.M = g.M, a.N = g.N, a.K = g.K, a.lda = g.lda, a.ldb = g.ldb, a.ldc = g.ldc;
+  a.alpha = g.alpha, a.beta = g.beta, a.skipc = g.c_bf16_only ? 1 : 0;
+  a.tiles_m = (g.M + 255) / 256, a.tiles_n = (g.N + 255) / 256, a.group_m = group_m;
+  // readable bytes: up to the last element of the last row (loads past it read zeros)
+  a.a_bytes = (int)(2 * (g.a_mcontig ? (int64_t)(g.K - 1) * g.lda + g.M : (int64_t)(g.M - 1) * g.lda + g.K));
+  a.b_bytes = (int)(2 * (g.b_kcontig ? (int64_t)(g.N - 1) * g.ldb + g.K : (int64_t)(g.K - 1) * g.ldb + g.N));
+  const dim3 grid(a.tiles_m * a.tiles_n), block(dma::NT);
+  if (!g.a_mcontig && !g.b_kcontig)
+    run_kernel(gemm_dma_kernel<false, false>, grid, block, 0, s, a);
+  else if (!g.a_mcontig && g.b_kcontig)
+    run_kernel(gemm_dma_kernel<false, true>, grid, block, 0, s, a);
+  else if (g.a_mcontig && !g.b_kcontig)
+    run_kernel(gemm_dma_kernel<true, false>, grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // C = sum of the partials ws[split][M][N] (per batch) + beta C + bias (+ resid), the bf16 copy
@@ -852,6 +1131,7 @@ static hipError_t reduce_splits(const GemmArgs& g, const float* ws, int splits, 
 }
 
 size_t gemm_workspace_bytes(const GemmArgs& g) {
+  if (dma_fits(g)) return gemv_workspace_bytes(g);
   Plan p = make_plan(g);
   const size_t tiled = p.splits <= 1 ? 0 : (size_t)p.splits * g.batch * g.M * g.N * sizeof(float);
   return std::max(tiled, gemv_workspace_bytes(g));
@@ -864,6 +1144,11 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   hipError_t ge;
   if (gemv(g, workspace, ws_bytes, s, &ge)) return ge;
   if (g.post != POST_NONE || g.a_part) return hipErrorInvalidValue;  // the inference fusions are few-row only
+  if (dma_fits(g)) {
+    // tall and narrow (the LM-head weight gradient, 197 x 3 tiles): long row groups
+    const int tiles_m = (g.M + 255) / 256, tiles_n = (g.N + 255) / 256;
+    return launch_dma(g, tiles_n <= 4 && tiles_m >= 128 ? GEMM_GROUP_TALL : GEMM_GROUP_M, s);
+  }
   // K == 0 needs no special case: the k loop is empty and the epilogue writes beta*C + bias
   Plan p = make_plan(g);
   if (p.splits > 1 && (size_t)p.splits * g.batch * g.M * g.N * sizeof(float) > ws_bytes) p.splits = 1;
