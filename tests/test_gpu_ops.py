@@ -318,6 +318,36 @@ def test_large_products_on_256_tiles(ctx, case):
     assert_close(grads[1][-60:], rgrads[1][-60:], GRAD_TOL["bf16"], "grad 1, last rows")
 
 
+@pytest.mark.parametrize("case", ["nt_fwd", "nn_fwd", "tn_dw"])
+def test_large_products_exact_on_integer_inputs(ctx, case):
+    """The 256x256-tile products of the test above on integers in [-3, 3]: exact
+    in bf16, and every partial sum is an integer below 2**24, so fp32 adds them
+    exactly in any order and the results must equal the oracle's bit for bit.  A
+    term dropped, repeated or taken from the wrong place anywhere (a tile edge, a
+    chunk at an operand's end, a K split) fails, however small its share."""
+    rng = np.random.default_rng({"nt_fwd": 151, "nn_fwd": 152, "tn_dw": 153}[case])
+
+    def ints(shape):
+        return rng.integers(-3, 4, size=shape).astype(np.float64)
+
+    ctx.set_precision("bf16")
+    if case == "nt_fwd":
+        arrays, build, ob, shape = [ints((4100, 200)), ints((8190, 200))], T.matmul_t, E.matmul_t, (4100, 8190)
+    elif case == "nn_fwd":
+        arrays, build, ob, shape = [ints((4100, 200)), ints((200, 8192))], T.matmul, E.matmul, (4100, 8192)
+    else:
+        arrays, build, ob, shape = [ints((520, 2048)), ints((16300, 2048))], T.matmul_t, E.matmul_t, (520, 16300)
+    R = ints(shape)
+    out, grads = gpu_op_with_grads(ctx, build, arrays, R)
+    ref, rgrads = oracle_op_with_grads(ob, arrays, R)
+    ctx.set_precision("fp32")
+    bad = np.argwhere(out != ref)
+    assert bad.size == 0, f"forward differs at {len(bad)} elements, first {bad[:3].tolist()}"
+    for i, (g, r) in enumerate(zip(grads, rgrads)):
+        bad = np.argwhere(g != r)
+        assert bad.size == 0, f"grad {i} differs at {len(bad)} elements, first {bad[:3].tolist()}"
+
+
 def test_linear_long_k_split(ctx):
     # a long reduction (the dW contractions of the GPT have K = 8192) takes the split-K path
     check(ctx, "fp32", T.linear, lambda x, w, b: E.add(E.matmul(x, w), b),

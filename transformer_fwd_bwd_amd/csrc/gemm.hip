@@ -51,6 +51,12 @@ constexpr int KALIGN = 64;  // split-K chunks are multiples of this (and of ever
 #ifndef GEMM_DMA_TILES
 #define GEMM_DMA_TILES 512   // products with at least this many 256x256 tiles take gemm_dma_kernel
 #endif
+#ifndef GEMM_DMA_SPLIT_K
+#define GEMM_DMA_SPLIT_K 2048  // fewer tiles than that, but K at least this: the same kernel split over K
+#endif
+#ifndef GEMM_DMA_VS_TFLOPS
+#define GEMM_DMA_VS_TFLOPS 750.0  // a split product takes it only if priced faster than gemm_kernel at this rate
+#endif
 #ifndef GEMM_GROUP_M
 #define GEMM_GROUP_M 8       // tile rows per raster group
 #endif
@@ -710,10 +716,10 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
 //   m- or n-contiguous operand: k-rows of 256 elements (512 bytes); 64-byte
 //     block b of k-row k holds column block b ^ (k & 3), so the four k-rows a
 //     transposing read (ds_read_b64_tr_b16) touches at once cover all banks.
-// Buffer loads return zeros past the operand's last element: rows and columns
-// beyond M, N or K read nothing outside the operand.  In a k-tile that runs past
-// K, the columns beyond K of a k-contiguous operand (the next row's elements)
-// are cleared in LDS before use.
+// Buffer loads return zeros past the operand's end (rounded up to its last
+// 16-byte chunk): rows and columns beyond M, N or K read nothing outside the
+// operand.  In a k-tile that runs past K, the columns beyond K of a k-contiguous
+// operand (the next row's elements) are cleared in LDS before use.
 namespace dma {
 
 constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 4, TM = 4, TN = 2;
@@ -739,6 +745,8 @@ struct Args {
   int skipc;
   int tiles_m, tiles_n, group_m;
   int a_bytes, b_bytes;  // readable bytes of A and B
+  int splits, kps;       // K split: items of kps k (a multiple of BK) ...
+  float* ws;             // ... write raw partials ws[split][M][N] (splits > 1)
 };
 
 // Per-lane global byte offsets of one operand's share of a k-tile (k-tile 0):
@@ -808,13 +816,15 @@ __global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  // the XCD-contiguous, row-grouped tile order of gemm_kernel
+  // the XCD-contiguous, row-grouped tile order of gemm_kernel, K splits outermost
   const int total = (int)gridDim.x;
   int t;
   {
     const int w = blockIdx.x, xcd = w & 7, per = total >> 3, rem = total & 7;
     t = xcd * per + min(xcd, rem) + (w >> 3);
   }
+  const int split = t / (g.tiles_m * g.tiles_n);
+  t -= split * (g.tiles_m * g.tiles_n);
   int tm, tn;
   {
     const int gm = g.group_m, band = gm * g.tiles_n, first = (t / band) * gm;
@@ -824,6 +834,7 @@ __global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
     tn = t / rows;
   }
   const int m0 = tm * BM, n0 = tn * BN;
+  const int kb = split * g.kps, ke = min(g.K, kb + g.kps);
 
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, g.a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, (short)0, g.b_bytes, 0x00020000);
@@ -842,9 +853,10 @@ __global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int lrow = lane & 31;
-  const int nt = (g.K + BK - 1) / BK, kr = g.K - (nt - 1) * BK;  // kr: k in the last k-tile
-  load_segs(ra, smem, va, 0, wave);
-  load_segs(rb, smem + OPB, vb, 0, wave);
+  const int nt = (ke - kb + BK - 1) / BK, kr = ke - kb - (nt - 1) * BK;  // kr: k in the last k-tile
+  const int t0 = kb / BK;
+  load_segs(ra, smem, va, t0 * adv_a, wave);
+  load_segs(rb, smem + OPB, vb, t0 * adv_b, wave);
   // k-tile kt is multiplied out of stage kt % 2 while k-tile kt + 1 loads into
   // the other: its fragments are read first, then the next loads are issued
   // (the compiler waits for every outstanding LDS load before an LDS read, so
@@ -872,8 +884,8 @@ __global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
     __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < nt) {
       char* nx = smem + ((kt + 1) & 1) * STAGE;  // last read in iteration kt - 1, before the barrier above
-      load_segs(ra, nx, va, (kt + 1) * adv_a, wave);
-      load_segs(rb, nx + OPB, vb, (kt + 1) * adv_b, wave);
+      load_segs(ra, nx, va, (t0 + kt + 1) * adv_a, wave);
+      load_segs(rb, nx + OPB, vb, (t0 + kt + 1) * adv_b, wave);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -892,6 +904,15 @@ __global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
   const int lhalf = lane >> 5;
   float* E = reinterpret_cast<float*>(smem) + wave * 32 * EP;
   constexpr int C4 = TN * 8;
+  // a K split writes its raw partial; the reduction applies the rest
+  const bool part = g.splits > 1;
+  float* const Cd = part ? g.ws + (int64_t)split * g.M * g.N : g.C;
+  const int64_t ldc = part ? g.N : g.ldc;
+  const float* const bias = part ? nullptr : g.bias;
+  const float* const resid = part ? nullptr : g.resid;
+  uint16_t* const Cbf = part ? nullptr : g.Cbf;
+  const float beta = part ? 0.f : g.beta;
+  const bool skipc = !part && g.skipc;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -907,24 +928,24 @@ __global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
       f4 v = *reinterpret_cast<const f4*>(E + r * EP + c4 * 4) * g.alpha;
       const int m = m0 + wm * TM * 32 + i * 32 + r, n = n0 + wn * TN * 32 + c4 * 4;
       if (m >= g.M || n >= g.N) continue;
-      float* row = g.C + (int64_t)m * g.ldc;
+      float* row = Cd + (int64_t)m * ldc;
       if (n + 3 < g.N) {
-        if (g.bias) v += *reinterpret_cast<const f4*>(g.bias + n);
+        if (bias) v += *reinterpret_cast<const f4*>(bias + n);
         f4* dst = reinterpret_cast<f4*>(row + n);
-        if (g.beta != 0.f) v += g.beta * *dst;
-        if (g.resid) v += *reinterpret_cast<const f4*>(g.resid + (int64_t)m * g.ldc + n);
-        if (!g.skipc) *dst = v;
-        if (g.Cbf) *reinterpret_cast<u16x4*>(g.Cbf + (int64_t)m * g.ldc + n) = bf16x4_bits(v);
+        if (beta != 0.f) v += beta * *dst;
+        if (resid) v += *reinterpret_cast<const f4*>(resid + (int64_t)m * ldc + n);
+        if (!skipc) *dst = v;
+        if (Cbf) *reinterpret_cast<u16x4*>(Cbf + (int64_t)m * ldc + n) = bf16x4_bits(v);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (n + e >= g.N) break;
           float x = v[e];
-          if (g.bias) x += g.bias[n + e];
-          if (g.beta != 0.f) x += g.beta * row[n + e];
-          if (g.resid) x += g.resid[(int64_t)m * g.ldc + n + e];
-          if (!g.skipc) row[n + e] = x;
-          if (g.Cbf) g.Cbf[(int64_t)m * g.ldc + n + e] = bf16_bits(x);
+          if (bias) x += bias[n + e];
+          if (beta != 0.f) x += beta * row[n + e];
+          if (resid) x += resid[(int64_t)m * ldc + n + e];
+          if (!skipc) row[n + e] = x;
+          if (Cbf) Cbf[(int64_t)m * ldc + n + e] = bf16_bits(x);
         }
       }
     }
@@ -1071,33 +1092,62 @@ hipError_t launch_prec(const KArgs& ka, int bk, dim3 grid, hipStream_t s) {
   return launch_layout<WM, WN, TM, TN, 32, true, false, false>(ka, grid, s);
 }
 
-// gemm_dma_kernel's conditions: both operands bf16 with 16-byte rows, one
-// product, no mask, a vector epilogue, enough 256x256 tiles to fill the GPU
-// twice, and every byte offset the loads form within 31 bits.
-bool dma_fits(const GemmArgs& g) {
+// gemm_dma_kernel's plan: 0 when it does not take the product, else its K
+// splits.  Conditions: both operands bf16 with 16-byte rows, one product, no
+// mask, a vector epilogue, every byte offset the loads form within 31 bits, and
+// either enough 256x256 tiles to fill the GPU twice or a K long enough to split
+// into items that fill it (N a multiple of 4 then, for the partials' rows).
+// Splits are priced as rounds of 256 items (one per CU) of 1.7 us per 64-deep
+// k-tile plus 3 us per item, plus the partials' round trip at 2.5 TB/s, and
+// taken only when that beats gemm_kernel's typical rate on such products.
+int dma_plan(const GemmArgs& g, int* kps_out) {
   auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
   if (g.prec != PREC_BF16 || !g.a_bf16 || !g.b_bf16 || g.batch != 1 || g.causal_a != CAUSAL_NONE || g.causal_out)
-    return false;
-  if (g.K < 1 || g.lda % 8 || g.ldb % 8 || !al(g.A, 16) || !al(g.B, 16)) return false;
-  if (g.ldc % 4 || !al(g.C, 16) || !al(g.bias, 16) || !al(g.resid, 16) || !al(g.Cbf, 8)) return false;
+    return 0;
+  if (g.K < 1 || g.lda % 8 || g.ldb % 8 || !al(g.A, 16) || !al(g.B, 16)) return 0;
+  if (g.ldc % 4 || !al(g.C, 16) || !al(g.bias, 16) || !al(g.resid, 16) || !al(g.Cbf, 8)) return 0;
   const int64_t tm = (g.M + 255) / 256, tn = (g.N + 255) / 256;
-  if (tm * tn < GEMM_DMA_TILES) return false;
   const int64_t kp = (g.K + 63) / 64 * 64;
   const int64_t reach_a = g.a_mcontig ? (kp - 1) * g.lda + tm * 256 : (tm * 256 - 1) * g.lda + kp;
   const int64_t reach_b = g.b_kcontig ? (tn * 256 - 1) * g.ldb + kp : (kp - 1) * g.ldb + tn * 256;
-  return 2 * std::max(reach_a, reach_b) < ((int64_t)1 << 31) - 64;
+  if (2 * std::max(reach_a, reach_b) >= ((int64_t)1 << 31) - 64) return 0;
+  const int nt = (int)(kp / 64);
+  *kps_out = (int)kp;
+  if (tm * tn >= GEMM_DMA_TILES) return 1;
+  if (g.K < GEMM_DMA_SPLIT_K || g.N % 4) return 0;
+  int best_sp = 0;
+  double best = 0.0;
+  for (int sp = 2; sp <= 32; ++sp) {
+    const int per = (nt + sp - 1) / sp;
+    if (per < 8) break;
+    const int64_t items = tm * tn * sp;
+    const double t = (double)((items + 255) / 256) * (per * 1.7e-6 + 3e-6) + (sp + 1) * 4.0 * g.M * g.N / 2.5e12;
+    if (best_sp == 0 || t < best) best = t, best_sp = sp;
+  }
+  if (best_sp == 0 || tm * tn * best_sp < 192) return 0;
+  if (best > 2.0 * g.M * g.N * (double)g.K / (GEMM_DMA_VS_TFLOPS * 1e12)) return 0;
+  const int per = (nt + best_sp - 1) / best_sp;
+  *kps_out = per * 64;
+  return (nt + per - 1) / per;  // no empty split
 }
 
-hipError_t launch_dma(const GemmArgs& g, int group_m, hipStream_t s) {
+hipError_t launch_dma(const GemmArgs& g, int splits, int kps, float* ws, int group_m, hipStream_t s) {
   dma::Args a;
+  a.splits = splits, a.kps = kps, a.ws = ws;
   a.A = g.A, a.B = g.B, a.C = g.C, a.Cbf = g.Cbf, a.bias = g.bias, a.resid = g.resid;
   a.M = g.M, a.N = g.N, a.K = g.K, a.lda = g.lda, a.ldb = g.ldb, a.ldc = g.ldc;
   a.alpha = g.alpha, a.beta = g.beta, a.skipc = g.c_bf16_only ? 1 : 0;
   a.tiles_m = (g.M + 255) / 256, a.tiles_n = (g.N + 255) / 256, a.group_m = group_m;
-  // readable bytes: up to the last element of the last row (loads past it read zeros)
-  a.a_bytes = (int)(2 * (g.a_mcontig ? (int64_t)(g.K - 1) * g.lda + g.M : (int64_t)(g.M - 1) * g.lda + g.K));
-  a.b_bytes = (int)(2 * (g.b_kcontig ? (int64_t)(g.N - 1) * g.ldb + g.K : (int64_t)(g.K - 1) * g.ldb + g.N));
-  const dim3 grid(a.tiles_m * a.tiles_n), block(dma::NT);
+  // Readable bytes: through the 16-byte chunk that holds the last element of the
+  // last row.  A 16-byte load that crosses the bound returns zeros for all of it,
+  // so the bound must not cut that chunk; the chunk starts 16-byte aligned (rows
+  // are), so it lies in the operand's own allocation granule.  Its elements past
+  // the end only meet rows or columns of C that are not stored, or k past K,
+  // which is cleared in LDS.
+  auto chunk_end = [](int64_t elems) { return (int)((2 * elems + 15) / 16 * 16); };
+  a.a_bytes = chunk_end(g.a_mcontig ? (int64_t)(g.K - 1) * g.lda + g.M : (int64_t)(g.M - 1) * g.lda + g.K);
+  a.b_bytes = chunk_end(g.b_kcontig ? (int64_t)(g.N - 1) * g.ldb + g.K : (int64_t)(g.K - 1) * g.ldb + g.N);
+  const dim3 grid(a.tiles_m * a.tiles_n * splits), block(dma::NT);
   if (!g.a_mcontig && !g.b_kcontig)
     run_kernel(gemm_dma_kernel<false, false>, grid, block, 0, s, a);
   else if (!g.a_mcontig && g.b_kcontig)
@@ -1131,7 +1181,10 @@ static hipError_t reduce_splits(const GemmArgs& g, const float* ws, int splits, 
 }
 
 size_t gemm_workspace_bytes(const GemmArgs& g) {
-  if (dma_fits(g)) return gemv_workspace_bytes(g);
+  int kps;
+  const int dsp = dma_plan(g, &kps);
+  if (dsp == 1) return gemv_workspace_bytes(g);
+  if (dsp > 1) return std::max((size_t)dsp * g.M * g.N * sizeof(float), gemv_workspace_bytes(g));
   Plan p = make_plan(g);
   const size_t tiled = p.splits <= 1 ? 0 : (size_t)p.splits * g.batch * g.M * g.N * sizeof(float);
   return std::max(tiled, gemv_workspace_bytes(g));
@@ -1144,10 +1197,15 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   hipError_t ge;
   if (gemv(g, workspace, ws_bytes, s, &ge)) return ge;
   if (g.post != POST_NONE || g.a_part) return hipErrorInvalidValue;  // the inference fusions are few-row only
-  if (dma_fits(g)) {
+  int kps;
+  const int dsp = dma_plan(g, &kps);
+  if (dsp > 0 && (dsp == 1 || (size_t)dsp * g.M * g.N * sizeof(float) <= ws_bytes)) {
     // tall and narrow (the LM-head weight gradient, 197 x 3 tiles): long row groups
     const int tiles_m = (g.M + 255) / 256, tiles_n = (g.N + 255) / 256;
-    return launch_dma(g, tiles_n <= 4 && tiles_m >= 128 ? GEMM_GROUP_TALL : GEMM_GROUP_M, s);
+    const hipError_t e = launch_dma(g, dsp, kps, static_cast<float*>(workspace),
+                                    tiles_n <= 4 && tiles_m >= 128 ? GEMM_GROUP_TALL : GEMM_GROUP_M, s);
+    if (e != hipSuccess || dsp == 1) return e;
+    return reduce_splits(g, static_cast<const float*>(workspace), dsp, s);
   }
   // K == 0 needs no special case: the k loop is empty and the epilogue writes beta*C + bias
   Plan p = make_plan(g);
