@@ -318,14 +318,18 @@ def test_large_products_on_256_tiles(ctx, case):
     assert_close(grads[1][-60:], rgrads[1][-60:], GRAD_TOL["bf16"], "grad 1, last rows")
 
 
-@pytest.mark.parametrize("case", ["nt_fwd", "nn_fwd", "tn_dw"])
+@pytest.mark.parametrize("case", ["nt_fwd", "nn_fwd", "tn_dw", "tn_split", "nn_split"])
 def test_large_products_exact_on_integer_inputs(ctx, case):
     """The 256x256-tile products of the test above on integers in [-3, 3]: exact
     in bf16, and every partial sum is an integer below 2**24, so fp32 adds them
     exactly in any order and the results must equal the oracle's bit for bit.  A
     term dropped, repeated or taken from the wrong place anywhere (a tile edge, a
-    chunk at an operand's end, a K split) fails, however small its share."""
-    rng = np.random.default_rng({"nt_fwd": 151, "nn_fwd": 152, "tn_dw": 153}[case])
+    chunk at an operand's end, a K split) fails, however small its share.
+    tn_split: a weight gradient over 8190 rows (760 x 2300), split over K;
+    nn_split: the dX of x @ w^T with a 20,000-long reduction, split over K with a
+    ragged last k-tile in the last split (and its weight gradient, 20000 x 1540
+    over 1030 rows, on whole 256x256 tiles)."""
+    rng = np.random.default_rng({"nt_fwd": 151, "nn_fwd": 152, "tn_dw": 153, "tn_split": 154, "nn_split": 155}[case])
 
     def ints(shape):
         return rng.integers(-3, 4, size=shape).astype(np.float64)
@@ -335,8 +339,12 @@ def test_large_products_exact_on_integer_inputs(ctx, case):
         arrays, build, ob, shape = [ints((4100, 200)), ints((8190, 200))], T.matmul_t, E.matmul_t, (4100, 8190)
     elif case == "nn_fwd":
         arrays, build, ob, shape = [ints((4100, 200)), ints((200, 8192))], T.matmul, E.matmul, (4100, 8192)
-    else:
+    elif case == "tn_dw":
         arrays, build, ob, shape = [ints((520, 2048)), ints((16300, 2048))], T.matmul_t, E.matmul_t, (520, 16300)
+    elif case == "tn_split":
+        arrays, build, ob, shape = [ints((8190, 760)), ints((760, 2300))], T.matmul, E.matmul, (8190, 2300)
+    else:
+        arrays, build, ob, shape = [ints((1030, 1540)), ints((20000, 1540))], T.matmul_t, E.matmul_t, (1030, 20000)
     R = ints(shape)
     out, grads = gpu_op_with_grads(ctx, build, arrays, R)
     ref, rgrads = oracle_op_with_grads(ob, arrays, R)

@@ -52,10 +52,10 @@ constexpr int KALIGN = 64;  // split-K chunks are multiples of this (and of ever
 #define GEMM_DMA_TILES 512   // products with at least this many 256x256 tiles take gemm_dma_kernel
 #endif
 #ifndef GEMM_DMA_SPLIT_K
-#define GEMM_DMA_SPLIT_K 2048  // fewer tiles than that, but K at least this: the same kernel split over K
+#define GEMM_DMA_SPLIT_K 4096        // fewer tiles, but K at least this: the same kernel split over K, for ...
 #endif
-#ifndef GEMM_DMA_VS_TFLOPS
-#define GEMM_DMA_VS_TFLOPS 750.0  // a split product takes it only if priced faster than gemm_kernel at this rate
+#ifndef GEMM_DMA_SPLIT_K_ANY
+#define GEMM_DMA_SPLIT_K_ANY 16384   // ... weight gradients (A m-contiguous), or any layout with K at least this
 #endif
 #ifndef GEMM_GROUP_M
 #define GEMM_GROUP_M 8       // tile rows per raster group
@@ -1097,9 +1097,12 @@ hipError_t launch_prec(const KArgs& ka, int bk, dim3 grid, hipStream_t s) {
 // mask, a vector epilogue, every byte offset the loads form within 31 bits, and
 // either enough 256x256 tiles to fill the GPU twice or a K long enough to split
 // into items that fill it (N a multiple of 4 then, for the partials' rows).
+// Split this way, the GPT-2 weight gradients (K = 8192, 768-3072 wide) run 14-16%
+// faster than on gemm_kernel and the LM head's dX (K = 50,257) 7%, while the
+// 768-wide products with K = 2304-3072 run 20-30% slower (gemm_kernel's
+// one-tile-per-CU 128x192 plan suits them), hence the layout and K rule.
 // Splits are priced as rounds of 256 items (one per CU) of 1.7 us per 64-deep
-// k-tile plus 3 us per item, plus the partials' round trip at 2.5 TB/s, and
-// taken only when that beats gemm_kernel's typical rate on such products.
+// k-tile plus 3 us per item, plus the partials' round trip at 2.5 TB/s.
 int dma_plan(const GemmArgs& g, int* kps_out) {
   auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
   if (g.prec != PREC_BF16 || !g.a_bf16 || !g.b_bf16 || g.batch != 1 || g.causal_a != CAUSAL_NONE || g.causal_out)
@@ -1114,7 +1117,7 @@ int dma_plan(const GemmArgs& g, int* kps_out) {
   const int nt = (int)(kp / 64);
   *kps_out = (int)kp;
   if (tm * tn >= GEMM_DMA_TILES) return 1;
-  if (g.K < GEMM_DMA_SPLIT_K || g.N % 4) return 0;
+  if (g.K < GEMM_DMA_SPLIT_K || g.N % 4 || (!g.a_mcontig && g.K < GEMM_DMA_SPLIT_K_ANY)) return 0;
   int best_sp = 0;
   double best = 0.0;
   for (int sp = 2; sp <= 32; ++sp) {
@@ -1125,7 +1128,6 @@ int dma_plan(const GemmArgs& g, int* kps_out) {
     if (best_sp == 0 || t < best) best = t, best_sp = sp;
   }
   if (best_sp == 0 || tm * tn * best_sp < 192) return 0;
-  if (best > 2.0 * g.M * g.N * (double)g.K / (GEMM_DMA_VS_TFLOPS * 1e12)) return 0;
   const int per = (nt + best_sp - 1) / best_sp;
   *kps_out = per * 64;
   return (nt + per - 1) / per;  // no empty split
