@@ -43,6 +43,19 @@ def ctx():
     c.close()
 
 
+@pytest.fixture
+def own_ctx():
+    """A context of its own for one test (4 GiB arena, closed after it): released
+    leaves give back their gradient and bf16 buffers only when their context
+    closes, so tests with operands of hundreds of MB do not share one."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import transformer_fwd_bwd_amd as T
+    c = T.Context(arena_bytes=4 << 30, precision="fp32")
+    yield c
+    c.close()
+
+
 def pytest_terminal_summary(terminalreporter):
     """Achieved parity errors of this session's GPU comparisons, as fractions of
     their tolerance (1.0 = at the gate): per test its worst L2 and worst

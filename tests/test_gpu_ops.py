@@ -293,14 +293,14 @@ def test_linear_one_tile_per_cu(ctx, case):
 
 
 @pytest.mark.parametrize("case", ["nt_fwd", "nn_fwd", "tn_dw"])
-def test_large_products_on_256_tiles(ctx, case):
+def test_large_products_on_256_tiles(own_ctx, case):
     """Products with at least 512 output tiles of 256x256 in the bf16 variant take
     the kernel that loads its operands straight into LDS: the LM-head shapes, here
     ragged in every dimension.  nt_fwd: x @ w^T with K = 200 (the last k-tile of
     both k-contiguous operands is cleared past K) and 8190 columns (a padded row
     pitch, a partial last group of four); nn_fwd: x @ w with K = 200; tn_dw: the
     weight gradient of x @ w^T, 16300 x 2048 over 520 rows."""
-    ctx.set_precision("bf16")
+    own_ctx.set_precision("bf16")
     if case == "nt_fwd":
         arrays, build, ob, shape = [rnd(141, (4100, 200)), rnd(142, (8190, 200), 0.1)], T.matmul_t, E.matmul_t, (4100, 8190)
     elif case == "nn_fwd":
@@ -308,9 +308,9 @@ def test_large_products_on_256_tiles(ctx, case):
     else:
         arrays, build, ob, shape = [rnd(145, (520, 2048)), rnd(146, (16300, 2048), 0.02)], T.matmul_t, E.matmul_t, (520, 16300)
     R = rnd(147, shape)
-    out, grads = gpu_op_with_grads(ctx, build, arrays, R)
+    out, grads = gpu_op_with_grads(own_ctx, build, arrays, R)
     ref, rgrads = oracle_op_with_grads(ob, arrays, R)
-    ctx.set_precision("fp32")
+    own_ctx.set_precision("fp32")
     assert_close(out, ref, FWD_TOL["bf16"], "forward")
     assert_close(out[-60:, -70:], ref[-60:, -70:], FWD_TOL["bf16"], "forward, last tile corner")
     for i, (g, r) in enumerate(zip(grads, rgrads)):
@@ -319,7 +319,7 @@ def test_large_products_on_256_tiles(ctx, case):
 
 
 @pytest.mark.parametrize("case", ["nt_fwd", "nn_fwd", "tn_dw", "tn_split", "nn_split"])
-def test_large_products_exact_on_integer_inputs(ctx, case):
+def test_large_products_exact_on_integer_inputs(own_ctx, case):
     """The 256x256-tile products of the test above on integers in [-3, 3]: exact
     in bf16, and every partial sum is an integer below 2**24, so fp32 adds them
     exactly in any order and the results must equal the oracle's bit for bit.  A
@@ -334,7 +334,7 @@ def test_large_products_exact_on_integer_inputs(ctx, case):
     def ints(shape):
         return rng.integers(-3, 4, size=shape).astype(np.float64)
 
-    ctx.set_precision("bf16")
+    own_ctx.set_precision("bf16")
     if case == "nt_fwd":
         arrays, build, ob, shape = [ints((4100, 200)), ints((8190, 200))], T.matmul_t, E.matmul_t, (4100, 8190)
     elif case == "nn_fwd":
@@ -346,9 +346,9 @@ def test_large_products_exact_on_integer_inputs(ctx, case):
     else:
         arrays, build, ob, shape = [ints((1030, 1540)), ints((20000, 1540))], T.matmul_t, E.matmul_t, (1030, 20000)
     R = ints(shape)
-    out, grads = gpu_op_with_grads(ctx, build, arrays, R)
+    out, grads = gpu_op_with_grads(own_ctx, build, arrays, R)
     ref, rgrads = oracle_op_with_grads(ob, arrays, R)
-    ctx.set_precision("fp32")
+    own_ctx.set_precision("fp32")
     bad = np.argwhere(out != ref)
     assert bad.size == 0, f"forward differs at {len(bad)} elements, first {bad[:3].tolist()}"
     for i, (g, r) in enumerate(zip(grads, rgrads)):
