@@ -51,10 +51,10 @@ METRIC = "train tokens/sec (fwd+bwd+AdamW) at GPT-2-124M shape; MFMA util %, HBM
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0                            # MI355X HBM3E, published
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_SUMMARY = {p: os.path.join(ROOT, "profiles", f"gemm_kernel_hbm_traffic_gpt2_124m_train_step_{p}.md")
+TRAFFIC_SUMMARY = {p: os.path.join(ROOT, "profiles", f"gemm_hbm_traffic_gpt2_124m_train_step_{p}.md")
                    for p in ("bf16", "fp32")}
 FAMILY_NAMES = {
-    "gemm": "gemm_kernel (MatMul family)", "attn_fwd": "attn_fwd_k (fused causal attention)",
+    "gemm": "gemm_kernel + gemm_dma_kernel (MatMul family, split-K reductions included)", "attn_fwd": "attn_fwd_k (fused causal attention)",
     "attn_bwd": "attn_dq_k + attn_dkv_k (fused attention backward)", "ce": "ce_fwd_grad4_k / ce kernels",
     "adamw": "adamw_k", "ln_fwd": "ln_fwd4_k", "ln_bwd": "ln_bwd_fused4_k", "gelu_fwd": "gelu forward",
     "gelu_bwd": "gelu backward", "gemv": "gemv_k + gemv_reduce_k (decode Linears)",
@@ -254,7 +254,7 @@ def train_leg(precision: str, B: int, L: int, steps: int, warmup: int, arena_gb:
 def gemm_roofline(r, precision: str, steps: int, traffic):
     achieved = r["gemm_flops"] / (r["gemm_ms"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[precision]
-    return {"bound": "mfma", "kernel": "gemm_kernel (all contraction launches)",
+    return {"bound": "mfma", "kernel": "gemm_kernel + gemm_dma_kernel (all contraction launches, split-K reductions included)",
             "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "gemm_ms_per_step": round(r["gemm_ms"] / steps, 3),
