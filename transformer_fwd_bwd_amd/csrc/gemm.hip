@@ -57,6 +57,9 @@ constexpr int KALIGN = 64;  // split-K chunks are multiples of this (and of ever
 #ifndef GEMM_DMA_SPLIT_K_ANY
 #define GEMM_DMA_SPLIT_K_ANY 16384   // ... weight gradients (A m-contiguous), or any layout with K at least this
 #endif
+#ifndef GEMM_DMA128_DW
+#define GEMM_DMA128_DW 1  // weight gradients split over K on 128x128 tiles (two workgroups per CU)
+#endif
 #ifndef GEMM_GROUP_M
 #define GEMM_GROUP_M 8       // tile rows per raster group
 #endif
@@ -722,11 +725,7 @@ __global__ __launch_bounds__(WM* WN * 64, 2) void gemm_kernel(KArgs ka) {
 // operand (the next row's elements) are cleared in LDS before use.
 namespace dma {
 
-constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 4, TM = 4, TN = 2;
-constexpr int NT = WM * WN * 64;
-constexpr int OPB = 256 * BK * 2;  // bytes of one operand's k-tile
-constexpr int STAGE = 2 * OPB;
-constexpr int EP = TN * 32 + 4;    // epilogue row pitch (floats)
+constexpr int BK = 64;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -749,31 +748,41 @@ struct Args {
   float* ws;             // ... write raw partials ws[split][M][N] (splits > 1)
 };
 
-// Per-lane global byte offsets of one operand's share of a k-tile (k-tile 0):
-// wave w issues the 1 KB segments w, w + 8, w + 16, w + 24.
-template <bool RC>
-__device__ __forceinline__ void seg_offsets(int voff[4], int r0, int64_t ld, int wave, int lane) {
+// One operand's k-tile: R rows (m or n) x 64 k, R * 128 bytes in 1 KB segments,
+// PER of them per wave (wave w issues segments w, w + NW, w + 2 NW, ...).
+template <int R, int NW>
+struct Seg {
+  static constexpr int BYTES = R * BK * 2;
+  static constexpr int PER = BYTES / 1024 / NW;
+  static_assert(PER * NW * 1024 == BYTES, "whole segments per wave");
+};
+
+// Per-lane global byte offsets of one operand's share of k-tile 0
+template <bool RC, int R, int NW>
+__device__ __forceinline__ void seg_offsets(int* voff, int r0, int64_t ld, int wave, int lane) {
+  constexpr int PER = Seg<R, NW>::PER;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = i * 8 + wave;
+  for (int i = 0; i < PER; ++i) {
+    const int s = i * NW + wave;
     if constexpr (!RC) {  // 8 rows of 128 bytes per segment
       const int r = s * 8 + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       voff[i] = (int)(((int64_t)(r0 + r) * ld + c * 8) * 2);
-    } else {              // 2 k-rows of 512 bytes per segment
-      const int k = s * 2 + (lane >> 5), p = lane & 31;
+    } else {              // 512 / R k-rows of 2R bytes per segment
+      constexpr int CPR = R / 8;  // 16-byte chunks per k-row
+      const int k = s * (64 / CPR) + lane / CPR, p = lane % CPR;
       const int c = (((p >> 2) ^ (k & 3)) << 2) | (p & 3);
       voff[i] = (int)(((int64_t)k * ld + r0 + 8 * c) * 2);
     }
   }
 }
 
-__device__ __forceinline__ void load_segs(__amdgpu_buffer_rsrc_t rs, char* stage, const int voff[4], int adv,
-                                          int wave) {
+template <int R, int NW>
+__device__ __forceinline__ void load_segs(__amdgpu_buffer_rsrc_t rs, char* stage, const int* voff, int adv, int wave) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage + (i * 8 + wave) * 1024), 16, voff[i] + adv, 0, 0,
-                                             0);
+  for (int i = 0; i < Seg<R, NW>::PER; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage + (i * NW + wave) * 1024), 16, voff[i] + adv, 0,
+                                             0, 0);
 }
 
 // k-contiguous layout: the 8 k of the MFMA fragment of row `row`, k-step q
@@ -781,20 +790,22 @@ __device__ __forceinline__ bf16x8 frag_rows(const char* st, int row, int q, int 
   const int c = 2 * q + (lane >> 5);
   return *reinterpret_cast<const bf16x8*>(st + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
 }
-// m/n-contiguous layout: the fragment of column block blk (32 columns), k-step q
+// m/n-contiguous layout (k-rows of R elements): the fragment of column block blk (32 columns), k-step q
+template <int R>
 __device__ __forceinline__ bf16x8 frag_cols(const char* st, int blk, int q, int lane) {
   const int tr_row = 8 * (lane >> 5) + ((lane & 15) >> 2), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int k = q * 16 + tr_row;
-  const char* p = st + k * 512 + ((blk ^ (k & 3)) << 6) + tr_col * 2;
+  const char* p = st + k * (2 * R) + ((blk ^ (k & 3)) << 6) + tr_col * 2;
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 2048));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 8 * R));
   const v8i16 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, c);
 }
 
-// clear k-columns kr..63 of a k-contiguous operand's k-tile in LDS
+// clear k-columns kr..63 of a k-contiguous operand's k-tile (R rows) in LDS
+template <int R, int NT>
 __device__ __forceinline__ void clear_tail(char* st, int kr, int tid) {
-  for (int u = tid; u < 256 * 8; u += NT) {
+  for (int u = tid; u < R * 8; u += NT) {
     const int r = u >> 3, p = u & 7, c = p ^ ((r >> 1) & 7);
     unsigned short* e = reinterpret_cast<unsigned short*>(st + r * 128 + p * 16);
 #pragma unroll
@@ -805,10 +816,17 @@ __device__ __forceinline__ void clear_tail(char* st, int kr, int tid) {
 
 }  // namespace dma
 
-template <bool A_RC, bool B_KC>
-__global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
+// WM x WN waves of TM x TN blocks: 2x4 of 4x2 (256x256 tiles, one workgroup per
+// CU) or 2x2 of 2x2 (128x128 tiles, two per CU)
+template <int WM, int WN, int TM, int TN, bool A_RC, bool B_KC>
+__global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 ? 2 : 1) void gemm_dma_kernel(dma::Args g) {
   using namespace dma;
   constexpr bool B_RC = !B_KC;
+  constexpr int NT = WM * WN * 64, NW = WM * WN;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int OPA = Seg<BM, NW>::BYTES, OPB = Seg<BN, NW>::BYTES;
+  constexpr int STAGE = OPA + OPB;
+  constexpr int EP = TN * 32 + 4;  // epilogue row pitch (floats)
   constexpr int SMEM = 2 * STAGE;
   static_assert(WM * WN * 32 * EP * 4 <= SMEM, "epilogue staging fits in the operand stages");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
@@ -838,9 +856,9 @@ __global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
 
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, g.a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, (short)0, g.b_bytes, 0x00020000);
-  int va[4], vb[4];
-  seg_offsets<A_RC>(va, m0, g.lda, wave, lane);
-  seg_offsets<B_RC>(vb, n0, g.ldb, wave, lane);
+  int va[Seg<BM, NW>::PER], vb[Seg<BN, NW>::PER];
+  seg_offsets<A_RC, BM, NW>(va, m0, g.lda, wave, lane);
+  seg_offsets<B_RC, BN, NW>(vb, n0, g.ldb, wave, lane);
   const int adv_a = A_RC ? (int)(BK * g.lda * 2) : BK * 2;
   const int adv_b = B_RC ? (int)(BK * g.ldb * 2) : BK * 2;
 
@@ -855,8 +873,8 @@ __global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
   const int lrow = lane & 31;
   const int nt = (ke - kb + BK - 1) / BK, kr = ke - kb - (nt - 1) * BK;  // kr: k in the last k-tile
   const int t0 = kb / BK;
-  load_segs(ra, smem, va, t0 * adv_a, wave);
-  load_segs(rb, smem + OPB, vb, t0 * adv_b, wave);
+  load_segs<BM, NW>(ra, smem, va, t0 * adv_a, wave);
+  load_segs<BN, NW>(rb, smem + OPA, vb, t0 * adv_b, wave);
   // k-tile kt is multiplied out of stage kt % 2 while k-tile kt + 1 loads into
   // the other: its fragments are read first, then the next loads are issued
   // (the compiler waits for every outstanding LDS load before an LDS read, so
@@ -865,10 +883,10 @@ __global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of k-tile kt is in LDS
     __syncthreads();                     // everyone's is; everyone is done reading k-tile kt - 1
     char* As = smem + (kt & 1) * STAGE;
-    char* Bs = As + OPB;
+    char* Bs = As + OPA;
     if (kt == nt - 1 && kr < BK && (!A_RC || B_KC)) {
-      if constexpr (!A_RC) clear_tail(As, kr, tid);
-      if constexpr (B_KC) clear_tail(Bs, kr, tid);
+      if constexpr (!A_RC) clear_tail<BM, NT>(As, kr, tid);
+      if constexpr (B_KC) clear_tail<BN, NT>(Bs, kr, tid);
       __syncthreads();
     }
     bf16x8 af[BK / 16][TM], bf[BK / 16][TN];
@@ -876,16 +894,16 @@ __global__ __launch_bounds__(dma::NT, 1) void gemm_dma_kernel(dma::Args g) {
     for (int q = 0; q < BK / 16; ++q) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[q][i] = A_RC ? frag_cols(As, wm * TM + i, q, lane) : frag_rows(As, wm * TM * 32 + i * 32 + lrow, q, lane);
+        af[q][i] = A_RC ? frag_cols<BM>(As, wm * TM + i, q, lane) : frag_rows(As, wm * TM * 32 + i * 32 + lrow, q, lane);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bf[q][j] = B_RC ? frag_cols(Bs, wn * TN + j, q, lane) : frag_rows(Bs, wn * TN * 32 + j * 32 + lrow, q, lane);
+        bf[q][j] = B_RC ? frag_cols<BN>(Bs, wn * TN + j, q, lane) : frag_rows(Bs, wn * TN * 32 + j * 32 + lrow, q, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < nt) {
       char* nx = smem + ((kt + 1) & 1) * STAGE;  // last read in iteration kt - 1, before the barrier above
-      load_segs(ra, nx, va, (t0 + kt + 1) * adv_a, wave);
-      load_segs(rb, nx + OPB, vb, (t0 + kt + 1) * adv_b, wave);
+      load_segs<BM, NW>(ra, nx, va, (t0 + kt + 1) * adv_a, wave);
+      load_segs<BN, NW>(rb, nx + OPA, vb, (t0 + kt + 1) * adv_b, wave);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1093,17 +1111,25 @@ hipError_t launch_prec(const KArgs& ka, int bk, dim3 grid, hipStream_t s) {
 }
 
 // gemm_dma_kernel's plan: 0 when it does not take the product, else its K
-// splits.  Conditions: both operands bf16 with 16-byte rows, one product, no
-// mask, a vector epilogue, every byte offset the loads form within 31 bits, and
-// either enough 256x256 tiles to fill the GPU twice or a K long enough to split
-// into items that fill it (N a multiple of 4 then, for the partials' rows).
-// Split this way, the GPT-2 weight gradients (K = 8192, 768-3072 wide) run 14-16%
-// faster than on gemm_kernel and the LM head's dX (K = 50,257) 7%, while the
-// 768-wide products with K = 2304-3072 run 20-30% slower (gemm_kernel's
-// one-tile-per-CU 128x192 plan suits them), hence the layout and K rule.
-// Splits are priced as rounds of 256 items (one per CU) of 1.7 us per 64-deep
-// k-tile plus 3 us per item, plus the partials' round trip at 2.5 TB/s.
-int dma_plan(const GemmArgs& g, int* kps_out) {
+// splits (*small: 128x128 tiles instead of 256x256).  Conditions: both operands
+// bf16 with 16-byte rows, one product, no mask, a vector epilogue, every byte
+// offset the loads form within 31 bits, and either enough 256x256 tiles to fill
+// the GPU twice or a K long enough to split into items that fill it (N a
+// multiple of 4 then, for the partials' rows):
+//  - weight gradients (A m-contiguous, K >= 4096) split over K on 128x128 tiles
+//    (four waves of 64x64, 64 KB of LDS, two workgroups per CU), with as many
+//    splits as fill the CUs once: on the GPT-2 ones (K = 8192) 3-14 splits, 8-17%
+//    faster with the reduction than 7-8 splits of 256x256 tiles (half the
+//    partials), which ran 14-16% faster than gemm_kernel;
+//  - any other layout only with K >= 16,384 (the LM head's dX, K = 50,257: 7%
+//    faster), on 256x256 tiles: the 768-wide products with K = 2304-3072 ran
+//    20-30% slower split this way (gemm_kernel's one-tile-per-CU 128x192 plan suits
+//    them), and the K = 768 products gained nothing from 128x128 tiles of this
+//    kernel in the training step.
+// 256x256 splits are priced as rounds of 256 items (one per CU) of 1.7 us per
+// 64-deep k-tile plus 3 us per item, plus the partials' round trip at 2.5 TB/s.
+int dma_plan(const GemmArgs& g, int* kps_out, bool* small) {
+  *small = false;
   auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
   if (g.prec != PREC_BF16 || !g.a_bf16 || !g.b_bf16 || g.batch != 1 || g.causal_a != CAUSAL_NONE || g.causal_out)
     return 0;
@@ -1118,6 +1144,14 @@ int dma_plan(const GemmArgs& g, int* kps_out) {
   *kps_out = (int)kp;
   if (tm * tn >= GEMM_DMA_TILES) return 1;
   if (g.K < GEMM_DMA_SPLIT_K || g.N % 4 || (!g.a_mcontig && g.K < GEMM_DMA_SPLIT_K_ANY)) return 0;
+  if (GEMM_DMA128_DW && g.a_mcontig) {  // as many K splits of 128x128 tiles as fill two per CU once
+    const int64_t t128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
+    const int sp = (int)std::max<int64_t>(1, std::min<int64_t>(512 / t128, nt / 8));
+    const int per = (nt + sp - 1) / sp;
+    *small = true;
+    *kps_out = per * 64;
+    return (nt + per - 1) / per;
+  }
   int best_sp = 0;
   double best = 0.0;
   for (int sp = 2; sp <= 32; ++sp) {
@@ -1133,13 +1167,18 @@ int dma_plan(const GemmArgs& g, int* kps_out) {
   return (nt + per - 1) / per;  // no empty split
 }
 
-hipError_t launch_dma(const GemmArgs& g, int splits, int kps, float* ws, int group_m, hipStream_t s) {
+hipError_t launch_dma(const GemmArgs& g, int splits, int kps, float* ws, bool small, hipStream_t s) {
   dma::Args a;
   a.splits = splits, a.kps = kps, a.ws = ws;
   a.A = g.A, a.B = g.B, a.C = g.C, a.Cbf = g.Cbf, a.bias = g.bias, a.resid = g.resid;
   a.M = g.M, a.N = g.N, a.K = g.K, a.lda = g.lda, a.ldb = g.ldb, a.ldc = g.ldc;
   a.alpha = g.alpha, a.beta = g.beta, a.skipc = g.c_bf16_only ? 1 : 0;
-  a.tiles_m = (g.M + 255) / 256, a.tiles_n = (g.N + 255) / 256, a.group_m = group_m;
+  const int bt = small ? 128 : 256;
+  a.tiles_m = (g.M + bt - 1) / bt, a.tiles_n = (g.N + bt - 1) / bt;
+  // row groups as gemm_kernel's; tall and narrow (the LM-head weight gradient, 197 x 3 tiles): long ones
+  a.group_m = a.tiles_n <= 8 && a.tiles_m >= (small ? 256 : 128)                   ? GEMM_GROUP_TALL
+              : small && a.tiles_m >= 32 && a.tiles_n >= 16 && a.tiles_n <= 32 ? GEMM_GROUP_WIDE
+                                                                               : GEMM_GROUP_M;
   // Readable bytes: through the 16-byte chunk that holds the last element of the
   // last row.  A 16-byte load that crosses the bound returns zeros for all of it,
   // so the bound must not cut that chunk; the chunk starts 16-byte aligned (rows
@@ -1149,13 +1188,26 @@ hipError_t launch_dma(const GemmArgs& g, int splits, int kps, float* ws, int gro
   auto chunk_end = [](int64_t elems) { return (int)((2 * elems + 15) / 16 * 16); };
   a.a_bytes = chunk_end(g.a_mcontig ? (int64_t)(g.K - 1) * g.lda + g.M : (int64_t)(g.M - 1) * g.lda + g.K);
   a.b_bytes = chunk_end(g.b_kcontig ? (int64_t)(g.N - 1) * g.ldb + g.K : (int64_t)(g.K - 1) * g.ldb + g.N);
-  const dim3 grid(a.tiles_m * a.tiles_n * splits), block(dma::NT);
+  const dim3 grid(a.tiles_m * a.tiles_n * splits);
+  if (small) {
+    const dim3 block(256);
+    if (!g.a_mcontig && !g.b_kcontig)
+      run_kernel(gemm_dma_kernel<2, 2, 2, 2, false, false>, grid, block, 0, s, a);
+    else if (!g.a_mcontig && g.b_kcontig)
+      run_kernel(gemm_dma_kernel<2, 2, 2, 2, false, true>, grid, block, 0, s, a);
+    else if (g.a_mcontig && !g.b_kcontig)
+      run_kernel(gemm_dma_kernel<2, 2, 2, 2, true, false>, grid, block, 0, s, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  const dim3 block(512);
   if (!g.a_mcontig && !g.b_kcontig)
-    run_kernel(gemm_dma_kernel<false, false>, grid, block, 0, s, a);
+    run_kernel(gemm_dma_kernel<2, 4, 4, 2, false, false>, grid, block, 0, s, a);
   else if (!g.a_mcontig && g.b_kcontig)
-    run_kernel(gemm_dma_kernel<false, true>, grid, block, 0, s, a);
+    run_kernel(gemm_dma_kernel<2, 4, 4, 2, false, true>, grid, block, 0, s, a);
   else if (g.a_mcontig && !g.b_kcontig)
-    run_kernel(gemm_dma_kernel<true, false>, grid, block, 0, s, a);
+    run_kernel(gemm_dma_kernel<2, 4, 4, 2, true, false>, grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -1184,7 +1236,8 @@ static hipError_t reduce_splits(const GemmArgs& g, const float* ws, int splits, 
 
 size_t gemm_workspace_bytes(const GemmArgs& g) {
   int kps;
-  const int dsp = dma_plan(g, &kps);
+  bool small;
+  const int dsp = dma_plan(g, &kps, &small);
   if (dsp == 1) return gemv_workspace_bytes(g);
   if (dsp > 1) return std::max((size_t)dsp * g.M * g.N * sizeof(float), gemv_workspace_bytes(g));
   Plan p = make_plan(g);
@@ -1200,12 +1253,10 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   if (gemv(g, workspace, ws_bytes, s, &ge)) return ge;
   if (g.post != POST_NONE || g.a_part) return hipErrorInvalidValue;  // the inference fusions are few-row only
   int kps;
-  const int dsp = dma_plan(g, &kps);
+  bool small;
+  const int dsp = dma_plan(g, &kps, &small);
   if (dsp > 0 && (dsp == 1 || (size_t)dsp * g.M * g.N * sizeof(float) <= ws_bytes)) {
-    // tall and narrow (the LM-head weight gradient, 197 x 3 tiles): long row groups
-    const int tiles_m = (g.M + 255) / 256, tiles_n = (g.N + 255) / 256;
-    const hipError_t e = launch_dma(g, dsp, kps, static_cast<float*>(workspace),
-                                    tiles_n <= 4 && tiles_m >= 128 ? GEMM_GROUP_TALL : GEMM_GROUP_M, s);
+    const hipError_t e = launch_dma(g, dsp, kps, static_cast<float*>(workspace), small, s);
     if (e != hipSuccess || dsp == 1) return e;
     return reduce_splits(g, static_cast<const float*>(workspace), dsp, s);
   }
