@@ -40,6 +40,13 @@ ELEM_A = 8.0
 RESULTS = []
 
 
+def bf16_round(a):
+    """float32 -> nearest-even bf16 -> float32, in numpy (the rounding the kernels apply)."""
+    b = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return (b << 16).astype(np.uint32).view(np.float32)
+
+
 def rel_err(x, ref):
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64)

@@ -8,7 +8,7 @@ import pytest
 
 import synthetic as S
 from oracle import engine as E
-from parity import FWD_TOL, GRAD_TOL, assert_close, gpu_op_with_grads, oracle_op_with_grads
+from parity import FWD_TOL, GRAD_TOL, assert_close, bf16_round as _bf16_round, gpu_op_with_grads, oracle_op_with_grads
 
 pytestmark = pytest.mark.gpu
 
@@ -794,13 +794,6 @@ def test_bias_gradients_from_fused_column_sums(ctx, prec):
         for t in G.values():
             t.release()
     ctx.set_precision("fp32")
-
-
-def _bf16_round(a):
-    """float32 -> nearest-even bf16 -> float32, in numpy (the rounding the kernels apply)."""
-    b = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return (b << 16).astype(np.uint32).view(np.float32)
 
 
 @pytest.mark.parametrize("prec", PRECS)

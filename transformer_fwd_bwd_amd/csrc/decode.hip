@@ -146,16 +146,43 @@ __global__ __launch_bounds__(NT) void kv_attend_k(const float* __restrict__ qkv,
   }
 }
 
-// Split form of kv_attend for head sizes 32, 64 and 128 (rows of float4).  One
-// workgroup per (sequence, head, block of KVP positions): each wave takes KVP/4
-// positions, a group of HS/4 lanes reads one cached key row (coalesced float4s)
-// and reduces its dot product across the group, then the wave keeps its own
-// maximum m, weight sum l and sum_j e^(s_j - m) v_j; the four waves merge in
-// LDS and the block writes (m, l, acc).  kv_attend_merge_k rescales the blocks
-// to their common maximum and divides.  The block that holds position pos
-// first appends the new key and value.
-constexpr int KVP = 128;
+// Split form of kv_attend for head sizes 32, 64 and 128.  One workgroup per
+// (sequence, head, block of KVP positions): each wave takes KVP/4 positions, a
+// group of lanes reads one cached key row in 16-byte pieces (8 bf16 or 4 fp32
+// values per lane) and reduces its dot product across the group, then the wave
+// keeps its own maximum m, weight sum l and sum_j e^(s_j - m) v_j; the four
+// waves merge in LDS and the block writes (m, l, acc).  kv_attend_merge_k
+// rescales the blocks to their common maximum and divides.  The block that
+// holds position pos appends the new key and value and takes that row from
+// registers rather than reading it back, so no block waits on the append.  The
+// query, summed once per wave by a lane per float4, reaches the other lanes by
+// cross-lane moves.  A block covers the same bytes of cache in either
+// precision, 256 bf16 positions or 128 fp32 ones, so that a GPT-2-sized batch
+// at a context near 1024 is one round of blocks.
+template <typename KT>
+constexpr int kv_block_positions() {
+  return sizeof(KT) == 2 ? 256 : 128;
+}
+constexpr int KVP_MIN = 128;  // the smaller of the two: the most blocks, for workspace sizing
 typedef float kf4 __attribute__((ext_vector_type(4)));
+typedef unsigned kr4 __attribute__((ext_vector_type(4)));  // 16 raw bytes of a cache row
+
+// element e of a 16-byte piece of a cache row, as fp32
+template <typename KT>
+struct KvPiece;
+template <>
+struct KvPiece<float> {
+  static constexpr int W = 4;
+  static __device__ __forceinline__ float at(const kr4& v, int e) { return __uint_as_float(v[e]); }
+};
+template <>
+struct KvPiece<uint16_t> {
+  static constexpr int W = 8;
+  static __device__ __forceinline__ float at(const kr4& v, int e) {
+    const unsigned u = v[e >> 1];
+    return __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
+  }
+};
 
 // qkv values of sequence b, columns i..i+3: from the stored qkv, or summed from the
 // c_attn product's partials (chunks in order) plus its bias -- the values its chunk
@@ -182,56 +209,110 @@ __device__ __forceinline__ kf4 qkv4(const QkvSrc& q, int B, int C, int b, int i)
   return v + *reinterpret_cast<const kf4*>(q.bias + i);
 }
 
-// four consecutive cache values as fp32
-__device__ __forceinline__ kf4 kv_get4(const float* p) { return *reinterpret_cast<const kf4*>(p); }
-__device__ __forceinline__ kf4 kv_get4(const uint16_t* p) {
-  const ku4 v = *reinterpret_cast<const ku4*>(p);
-  return kf4{__uint_as_float((unsigned)v.x << 16), __uint_as_float((unsigned)v.y << 16),
-             __uint_as_float((unsigned)v.z << 16), __uint_as_float((unsigned)v.w << 16)};
-}
 __device__ __forceinline__ void kv_put4(float* p, kf4 v) { *reinterpret_cast<kf4*>(p) = v; }
 __device__ __forceinline__ void kv_put4(uint16_t* p, kf4 v) {
   *reinterpret_cast<ku4*>(p) = ku4{__builtin_bit_cast(uint16_t, (__bf16)v.x), __builtin_bit_cast(uint16_t, (__bf16)v.y),
                                    __builtin_bit_cast(uint16_t, (__bf16)v.z), __builtin_bit_cast(uint16_t, (__bf16)v.w)};
 }
 
+// raw cache bits of four values: fp32 as is, bf16 rounded to nearest-even and
+// packed two to a dword (the stored form kv_put4 writes)
+__device__ __forceinline__ void kv_raw4(kf4 v, unsigned* o, float*) {
+  o[0] = __float_as_uint(v.x), o[1] = __float_as_uint(v.y), o[2] = __float_as_uint(v.z), o[3] = __float_as_uint(v.w);
+}
+__device__ __forceinline__ void kv_raw4(kf4 v, unsigned* o, uint16_t*) {
+  o[0] = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)v.x) | ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)v.y) << 16);
+  o[1] = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)v.z) | ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)v.w) << 16);
+}
+
+// lane (r, c) of a wave takes float4s c*N4 .. c*N4+N4-1 of a head-sized vector
+// whose float4 f sits in lane f
+template <int N4>
+__device__ __forceinline__ void share4(kf4 v, int c, kf4* out) {
+#pragma unroll
+  for (int e = 0; e < N4; ++e) {
+    const int src = c * N4 + e;
+    out[e] = kf4{__shfl(v.x, src, 64), __shfl(v.y, src, 64), __shfl(v.z, src, 64), __shfl(v.w, src, 64)};
+  }
+}
+
 template <int HS, typename KT>
-__global__ __launch_bounds__(256) void kv_attend_part_k(QkvSrc qs, KT* __restrict__ kv,
+__global__ __launch_bounds__(256, HS <= 64 ? 4 : 2) void kv_attend_part_k(QkvSrc qs, KT* __restrict__ kv,
                                                         float* __restrict__ pacc, float* __restrict__ pml, int layer,
                                                         int B, int Tmax, int C, int H, int pos, int S, float scale) {
-  constexpr int LPR = HS / 4, RPI = 64 / LPR, PW = KVP / 4, IT = PW / RPI;
+  constexpr int KVP = kv_block_positions<KT>(), VW = KvPiece<KT>::W, N4 = VW / 4;
+  constexpr int LPR = HS / VW, RPI = 64 / LPR, PW = KVP / 4, IT = PW / RPI;
+  static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0 && IT >= 1 && PW % RPI == 0 && HS / 4 <= 64, "row split");
   __shared__ float wm[4], wl[4];
-  __shared__ kf4 wacc[4][LPR];
-  const int s = blockIdx.x % S, bh = blockIdx.x / S;
-  const int b = bh / H, hd = bh % H;
+  __shared__ float wacc[4][HS];
+  // heads fastest: the blocks that read the same cache rows (every head of one
+  // block of positions) run together, so the rows' DRAM pages are opened once
+  const int hd = blockIdx.x % H, s = blockIdx.x / H % S, b = blockIdx.x / H / S, bh = b * H + hd;
   KT* Kc = kv + ((int64_t)(layer * 2 + 0) * B + b) * Tmax * C + hd * HS;
   KT* Vc = kv + ((int64_t)(layer * 2 + 1) * B + b) * Tmax * C + hd * HS;
   const int j_lo = s * KVP, j_hi = min(j_lo + KVP, pos + 1);
-  if (pos < j_lo + KVP) {  // the last block: append the new token's key and value (uniform per block)
-    for (int d4 = threadIdx.x; d4 < HS / 4; d4 += 256) {
-      kv_put4(Kc + (int64_t)pos * C + 4 * d4, qkv4(qs, B, C, b, C + hd * HS + 4 * d4));
-      kv_put4(Vc + (int64_t)pos * C + 4 * d4, qkv4(qs, B, C, b, 2 * C + hd * HS + 4 * d4));
-    }
-    __syncthreads();
-  }
+  const bool last = pos < j_lo + KVP;  // this block holds the new token (uniform per block)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / LPR, c = lane % LPR;
-  const kf4 q = qkv4(qs, B, C, b, hd * HS + c * 4);
   const int jw = j_lo + w * PW;
   // every key and value row of this wave is requested before the first is used;
-  // rows past the block read row j_lo (in range) and are masked below
-  kf4 kr[IT], vr[IT];
+  // rows past the block and the new token's row (not stored yet) read row j_lo
+  // instead, an in-range address: their loaded values are replaced below
+  const int j_mem = last ? pos : j_hi;
+  kr4 kr[IT], vr[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int j = jw + it * RPI + r;
-    const int64_t row = (int64_t)(j < j_hi ? j : j_lo) * C + c * 4;
-    kr[it] = kv_get4(Kc + row);
-    vr[it] = kv_get4(Vc + row);
+    const int64_t row = (int64_t)(j < j_mem ? j : j_lo) * C + c * VW;
+    kr[it] = *reinterpret_cast<const kr4*>(Kc + row);
+    vr[it] = *reinterpret_cast<const kr4*>(Vc + row);
   }
+  // the query: lane f < HS/4 sums float4 f once, then the wave shares it
+  kf4 qf = {0.f, 0.f, 0.f, 0.f};
+  if (lane < HS / 4) qf = qkv4(qs, B, C, b, hd * HS + 4 * lane);
+  kf4 q4[N4];
+  share4<N4>(qf, c, q4);
+  if (last) {
+    // the new token's key and value: wave 0 appends them to the cache; every wave
+    // takes their stored (rounded) form in place of the row it did not read
+    kf4 kn = {0.f, 0.f, 0.f, 0.f}, vn = {0.f, 0.f, 0.f, 0.f};
+    if (lane < HS / 4) {
+      kn = qkv4(qs, B, C, b, C + hd * HS + 4 * lane);
+      vn = qkv4(qs, B, C, b, 2 * C + hd * HS + 4 * lane);
+      if (w == 0) {
+        kv_put4(Kc + (int64_t)pos * C + 4 * lane, kn);
+        kv_put4(Vc + (int64_t)pos * C + 4 * lane, vn);
+      }
+    }
+    kf4 k4[N4], v4[N4];
+    share4<N4>(kn, c, k4);
+    share4<N4>(vn, c, v4);
+    unsigned kw[4] = {0u, 0u, 0u, 0u}, vw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < N4; ++e) {  // sizeof(KT) dwords per float4 of values
+      kv_raw4(k4[e], kw + e * (int)sizeof(KT), (KT*)nullptr);
+      kv_raw4(v4[e], vw + e * (int)sizeof(KT), (KT*)nullptr);
+    }
+    const kr4 kraw = {kw[0], kw[1], kw[2], kw[3]}, vraw = {vw[0], vw[1], vw[2], vw[3]};
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+      if (jw + it * RPI + r == pos) kr[it] = kraw, vr[it] = vraw;
+  }
+  // a row past the block read a stand-in row that may not hold finite values
+  // (with pos == j_lo it is the row being appended): its weight is 0, and its
+  // value must be too, since 0 * inf is not 0
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+    if (jw + it * RPI + r >= j_hi) vr[it] = kr4{0u, 0u, 0u, 0u};
+  float q[VW];
+#pragma unroll
+  for (int e = 0; e < N4; ++e) q[4 * e] = q4[e].x, q[4 * e + 1] = q4[e].y, q[4 * e + 2] = q4[e].z, q[4 * e + 3] = q4[e].w;
   float sc[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int j = jw + it * RPI + r;
-    float d = q.x * kr[it].x + q.y * kr[it].y + q.z * kr[it].z + q.w * kr[it].w;
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) d += q[e] * KvPiece<KT>::at(kr[it], e);
 #pragma unroll
     for (int o = LPR / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
     sc[it] = j < j_hi ? d * scale : -INFINITY;
@@ -244,26 +325,30 @@ __global__ __launch_bounds__(256) void kv_attend_part_k(QkvSrc qs, KT* __restric
   // a wave past the block's end (m = -inf) gets weights exp(-inf) = 0; no branch,
   // so the value loads stay where they were issued
   const float ms = m == -INFINITY ? 0.f : m;
-  float l = 0.f;
-  kf4 acc = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f, acc[VW];
+#pragma unroll
+  for (int e = 0; e < VW; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const float p = expf(sc[it] - ms);  // sc = -inf past the block: p = 0
-    acc += p * vr[it];
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[e] += p * KvPiece<KT>::at(vr[it], e);
     l += p;
   }
 #pragma unroll
   for (int o = 32; o >= LPR; o >>= 1) {
     l += __shfl_xor(l, o, 64);
-    acc.x += __shfl_xor(acc.x, o, 64);
-    acc.y += __shfl_xor(acc.y, o, 64);
-    acc.z += __shfl_xor(acc.z, o, 64);
-    acc.w += __shfl_xor(acc.w, o, 64);
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
   }
   if (lane == 0) wm[w] = m, wl[w] = l;
-  if (r == 0) wacc[w][c] = acc;
+  if (r == 0) {
+#pragma unroll
+    for (int e = 0; e < VW; e += 4)
+      *reinterpret_cast<kf4*>(&wacc[w][c * VW + e]) = kf4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+  }
   __syncthreads();
-  if (w == 0 && lane < LPR) {
+  if (w == 0 && lane < HS / 4) {  // one float4 of the head's output per lane
     float M = wm[0];
 #pragma unroll
     for (int i = 1; i < 4; ++i) M = fmaxf(M, wm[i]);
@@ -274,7 +359,7 @@ __global__ __launch_bounds__(256) void kv_attend_part_k(QkvSrc qs, KT* __restric
       if (wm[i] != -INFINITY) {
         const float f = expf(wm[i] - M);
         L += f * wl[i];
-        A += f * wacc[i][lane];
+        A += f * *reinterpret_cast<const kf4*>(&wacc[i][lane * 4]);
       }
     const int64_t blk = (int64_t)bh * S + s;
     *reinterpret_cast<kf4*>(pacc + blk * HS + lane * 4) = A;
@@ -588,13 +673,13 @@ hipError_t kv_store(const float* qkv, int64_t T, int C, void* kv, bool kv_bf16, 
 }
 
 static bool kv_split_ok(int C, int H) {
-  const int hs = C / H;
-  return C % 4 == 0 && (hs == 32 || hs == 64 || hs == 128);
+  const int hs = C / H;  // a head row then starts on a 16-byte boundary in either precision
+  return C % H == 0 && (hs == 32 || hs == 64 || hs == 128);
 }
 
 size_t kv_attend_workspace_bytes(int B, int C, int H, int pos) {
   if (!kv_split_ok(C, H)) return 0;
-  const int64_t S = (pos + KVP) / KVP;
+  const int64_t S = (pos + KVP_MIN) / KVP_MIN;
   return (size_t)(B * S * ((int64_t)C + 2 * H)) * sizeof(float);
 }
 
@@ -611,6 +696,7 @@ hipError_t kv_attend_t(const float* qkv, KT* kv, float* y, int layer, int B, int
     return hipGetLastError();
   }
   const QkvSrc qs{qkv, qkv_part, qkv_bias, qkv_chunks};
+  constexpr int KVP = kv_block_positions<KT>();
   const int hs = C / H, S = (pos + KVP) / KVP;  // blocks covering positions 0..pos
   float* pacc = static_cast<float*>(ws);
   float* pml = pacc + (int64_t)B * H * S * hs;
