@@ -379,6 +379,20 @@ int tfb_kv_attend(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor qkv, int pos, 
  * [GPT2-4, "Generation with KV cache"] */
 int tfb_kv_attend_linear(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor x, tfb_tensor w, tfb_tensor b, int pos,
                          int heads, tfb_tensor* y);
+/* The attention half of a transformer block for one new token per sequence, as
+ * one call: a = tfb_kv_attend_linear(x, w_attn, b_attn) (append at `pos`, then the
+ * single-query attention), y = r + a @ w_proj + b_proj and h = LayerNorm(y; gamma,
+ * beta, eps), y and h [batch, 1, N] with w_proj [C, N].  Inference only: gradients
+ * enabled -> TFB_ERR_STATE; nothing recorded.  Where the fused kernels apply (at
+ * most 16 sequences, head size 32, 64 or 128, N <= 2048 and a multiple of 4) the
+ * attention leaves its per-block results and the projection merges them as it
+ * loads its input, so `a` is never stored; otherwise it runs as
+ * tfb_kv_attend_linear then tfb_linear_residual_layernorm.  Flags: as there
+ * (TFB_OUT_BF16_ONLY for h).  Errors: as those two calls.
+ * [GPT2-4, "Generation with KV cache"; "Loading the weights": x = x + attn(ln_1(x))] */
+int tfb_kv_attention_block(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor x, tfb_tensor w_attn, tfb_tensor b_attn,
+                           int pos, int heads, tfb_tensor w_proj, tfb_tensor b_proj, tfb_tensor r, tfb_tensor gamma,
+                           tfb_tensor beta, float eps, int flags, tfb_tensor* y, tfb_tensor* h);
 /* One id per row of logits [..., V]: keep every logit >= the k-th largest (ties
  * kept; k = 0 or k >= V keeps all), p = softmax((l - max)/temperature) summed in
  * double, and return the first id (ascending) whose cumulative p exceeds u[row].

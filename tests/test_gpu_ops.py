@@ -220,6 +220,68 @@ def test_kv_attend_linear(ctx, prec, hs, H):
     tb.release()
 
 
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("hs,H", [(64, 3), (48, 2)])
+@pytest.mark.parametrize("P0", [254, 1022, 2310])
+def test_kv_attention_block(ctx, prec, hs, H, P0):
+    """[GPT2-4, "Generation with KV cache"; "Loading the weights": x = x + attn(ln_1(x))]
+    the attention half of a block in one call -- c_attn, the cached attention, the
+    projection plus the residual, and ln_2 -- at positions P0..P0+3 after P0 cached
+    ones (head size 64: the projection merges the attention's per-block results as
+    it loads them; head size 48: the unfused ops); each call must see the keys and
+    values the previous ones appended.  Position 256 is a block boundary of either
+    cache; at 1024 an fp32 cache goes from 8 blocks, the most the merge loads at
+    once, to 9; past 2048 both caches take the merge's block-by-block loop."""
+    from oracle import ops as O
+    ctx.set_precision(prec)
+    rng = S.rng_for(300 + hs)
+    B, C, K = 4, hs * H, 96
+    Tmax = P0 + 46
+    kv = T.KvCache(ctx, 2, B, Tmax, C)
+    Kc, Vc = np.zeros((B, Tmax, C)), np.zeros((B, Tmax, C))
+    pre = rng.standard_normal((B, P0, 3 * C)).astype(np.float32)
+    tq = ctx.tensor(pre.shape, pre)
+    kv.store(1, tq, 0)
+    Kc[:, :P0], Vc[:, :P0] = pre[:, :, C:2 * C], pre[:, :, 2 * C:]
+    tq.release()
+    w = rnd(301, (K, 3 * C), 1 / np.sqrt(K))
+    b = rnd(302, (3 * C,), 0.3)
+    wp = rnd(303, (C, C), 1 / np.sqrt(C))
+    bp = rnd(304, (C,), 0.3)
+    g = 1.0 + rnd(305, (C,), 0.2)
+    bt = rnd(306, (C,), 0.2)
+    held = [ctx.tensor(a.shape, a) for a in (w, b, wp, bp, g, bt)]
+    tw, tb, twp, tbp, tg, tbt = held
+    ctx.set_grad_enabled(False)
+    try:
+        for pos in range(P0, P0 + 4):
+            x = rnd(307 + pos, (B, 1, K))
+            r = rnd(407 + pos, (B, 1, C))
+            tx, tr = ctx.tensor(x.shape, x), ctx.tensor(r.shape, r)
+            ty, th = kv.attention_block(1, tx, tw, tb, pos, H, twp, tbp, tr, tg, tbt)
+            y, h = ty.numpy().reshape(B, C), th.numpy().reshape(B, C)
+            qkv = x.reshape(B, K).astype(np.float64) @ w + b
+            Kc[:, pos], Vc[:, pos] = qkv[:, C:2 * C], qkv[:, 2 * C:]
+            a = np.zeros((B, C))
+            for bb in range(B):
+                for hd in range(H):
+                    sl = slice(hd * hs, (hd + 1) * hs)
+                    p = O.softmax_row(Kc[bb, :pos + 1, sl] @ qkv[bb, sl] / np.sqrt(hs))
+                    a[bb, sl] = p @ Vc[bb, :pos + 1, sl]
+            ry = r.reshape(B, C) + a @ wp + bp
+            assert_close(y, ry, FWD_TOL[prec], f"y, pos {pos}")
+            assert_close(h, O.layernorm_fwd(ry, g, bt)[0], FWD_TOL[prec], f"ln_2(y), pos {pos}")
+            ctx.tape_reset()
+            tx.release()
+            tr.release()
+    finally:
+        ctx.set_grad_enabled(True)
+        ctx.set_precision("fp32")
+        kv.close()
+        for t in held:
+            t.release()
+
+
 def test_inference_fusions_refuse_to_record(ctx):
     x, w, b = ctx.tensor((2, 8), np.ones((2, 8), np.float32)), ctx.tensor((8, 8)), ctx.tensor((8,))
     with pytest.raises(T.TfbError) as e:
@@ -228,8 +290,14 @@ def test_inference_fusions_refuse_to_record(ctx):
     with pytest.raises(T.TfbError) as e:
         T.linear_residual_layernorm(x, w, b, x, b, b)
     assert e.value.code == -3
+    kv = T.KvCache(ctx, 1, 2, 8, 8)
+    x1, wa, ba = ctx.tensor((2, 1, 8)), ctx.tensor((8, 24)), ctx.tensor((24,))
+    with pytest.raises(T.TfbError) as e:
+        kv.attention_block(0, x1, wa, ba, 0, 1, w, b, x1, b, b)
+    assert e.value.code == -3 and "inference-only" in str(e.value)
+    kv.close()
     ctx.tape_reset()
-    for t in (x, w, b):
+    for t in (x, w, b, x1, wa, ba):
         t.release()
 
 

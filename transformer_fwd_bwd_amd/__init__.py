@@ -66,6 +66,8 @@ SIGNATURES = {
     "tfb_mlp_residual_layernorm": [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                    c_float, c_int32, P(c_int32), P(c_int32)],
     "tfb_kv_attend_linear": [c_void_p, c_void_p, c_int, c_int32, c_int32, c_int32, c_int, c_int, P(c_int32)],
+    "tfb_kv_attention_block": [c_void_p, c_void_p, c_int, c_int32, c_int32, c_int32, c_int, c_int, c_int32, c_int32,
+                               c_int32, c_int32, c_int32, c_float, c_int32, P(c_int32), P(c_int32)],
     "tfb_linear_residual_layernorm": [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_float,
                                       c_int32, P(c_int32), P(c_int32)],
     "tfb_embedding": [c_void_p, c_int32, c_void_p, c_int64, c_int64, P(c_int32)],
@@ -504,6 +506,18 @@ class KvCache:
     def attend_linear(self, layer: int, x: Tensor, w: Tensor, b: Tensor, pos: int, heads: int) -> Tensor:
         """The c_attn Linear (x @ w + b) and attend() as one call (inference)."""
         return _out(self.ctx, _lib.tfb_kv_attend_linear, self.ptr, layer, x.h, w.h, b.h, pos, heads)
+
+    def attention_block(self, layer: int, x: Tensor, w_attn: Tensor, b_attn: Tensor, pos: int, heads: int,
+                        w_proj: Tensor, b_proj: Tensor, residual: Tensor, gamma: Tensor, beta: Tensor,
+                        eps: float = 1e-5, bf16_only: bool = False):
+        """Inference only: (y, h) with y = residual + attend_linear(...) @ w_proj + b_proj and
+        h = LayerNorm(y), as one call (the attention output is never stored where the
+        fused kernels apply).  bf16_only applies to h."""
+        y, h = c_int32(), c_int32()
+        _check(_lib.tfb_kv_attention_block(self.ctx.ptr, self.ptr, layer, x.h, w_attn.h, b_attn.h, pos, heads,
+                                           w_proj.h, b_proj.h, residual.h, gamma.h, beta.h, c_float(eps),
+                                           OUT_BF16_ONLY if bf16_only else 0, ctypes.byref(y), ctypes.byref(h)))
+        return Tensor(self.ctx, y.value), Tensor(self.ctx, h.value)
 
     def close(self):
         if getattr(self, "ptr", None):

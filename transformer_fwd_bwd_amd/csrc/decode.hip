@@ -685,12 +685,17 @@ size_t kv_attend_workspace_bytes(int B, int C, int H, int pos) {
 
 bool kv_attend_takes_parts(int C, int H) { return kv_split_ok(C, H); }
 
+int kv_attend_blocks(bool kv_bf16, int pos) {
+  const int kvp = kv_bf16 ? kv_block_positions<uint16_t>() : kv_block_positions<float>();
+  return (pos + kvp) / kvp;
+}
+
 template <typename KT>
 hipError_t kv_attend_t(const float* qkv, KT* kv, float* y, int layer, int B, int Tmax, int C, int H, int pos,
                        float scale, void* ws, hipStream_t s, const float* qkv_part, int qkv_chunks,
                        const float* qkv_bias) {
   if (!kv_split_ok(C, H) || ws == nullptr) {
-    if (qkv_part) return hipErrorInvalidValue;  // the unsplit kernel reads stored qkv only
+    if (qkv_part || !y) return hipErrorInvalidValue;  // the unsplit kernel reads stored qkv, writes y
     const size_t shmem = ((size_t)Tmax + 4 * 64) * sizeof(float);
     run_kernel(kv_attend_k<KT>, dim3(B * H), dim3(NT), shmem, s, qkv, kv, y, layer, B, Tmax, C, H, pos, scale);
     return hipGetLastError();
@@ -708,6 +713,7 @@ hipError_t kv_attend_t(const float* qkv, KT* kv, float* y, int layer, int B, int
   else
     run_kernel(kv_attend_part_k<128, KT>, grid, dim3(256), 0, s, qs, kv, pacc, pml, layer, B, Tmax, C, H, pos, S,
                scale);
+  if (!y) return hipGetLastError();  // the per-block results are the output
   const int n = B * H * hs;
   run_kernel(kv_attend_merge_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pacc, pml, y, B * H, hs, S);
   return hipGetLastError();

@@ -1251,7 +1251,7 @@ hipError_t gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t
   if (g.c_bf16_only && (!g.Cbf || g.beta != 0.f)) return hipErrorInvalidValue;
   hipError_t ge;
   if (gemv(g, workspace, ws_bytes, s, &ge)) return ge;
-  if (g.post != POST_NONE || g.a_part) return hipErrorInvalidValue;  // the inference fusions are few-row only
+  if (g.post != POST_NONE || g.a_part || g.att_acc) return hipErrorInvalidValue;  // the inference fusions are few-row only
   int kps;
   bool small;
   const int dsp = dma_plan(g, &kps, &small);

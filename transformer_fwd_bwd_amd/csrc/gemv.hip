@@ -67,10 +67,16 @@ struct SkArgs {
   float ln_eps;
   float* ln_y;
   uint16_t* ln_ybf;
-  const float* a_part;  // APART: A from the previous product's partials (GemmArgs)
+  const float* a_part;  // A_PARTS: A from the previous product's partials (GemmArgs)
   const float* a_bias;
   int a_chunks;
+  const float* att_acc;  // A_ATTN: A merged from the cached attention's blocks (GemmArgs)
+  const float* att_ml;
+  int att_blocks, att_hs, att_heads;
 };
+
+// where the kernel takes A from
+enum ASrc { A_MEM = 0, A_PARTS = 1, A_ATTN = 2 };
 
 // A from the previous few-row product's partials: gelu(sum of its chunks + bias), as
 // that product's reduction would have computed it (same order), rounded to bf16 in
@@ -92,7 +98,22 @@ __device__ __forceinline__ float a_from_parts(const SkArgs& a, int m, int k) {
   return RND ? round_bf16(v) : v;
 }
 
-template <bool A_BF, bool B_BF, bool RND, bool APART>
+// A from the cached attention's per-block results: their merge, in the order and
+// arithmetic of the attention's own merge pass, rounded to bf16 in the bf16
+// variant.  A thread stages four consecutive columns of one head (head sizes are
+// multiples of 4), so one (M_s, l_s) load and one float4 of acc_s serve four
+// elements.  With at most AT_BATCH blocks (a context of 2048 bf16 or 1024 fp32
+// positions) all of a thread's loads are issued before the first is used: one
+// round of loads for the whole staging.  Longer contexts walk the blocks.
+constexpr int AT_BATCH = 8;
+template <bool RND>
+__device__ __forceinline__ f4 att_finish(f4 A, float L) {
+  f4 v = {A.x / L, A.y / L, A.z / L, A.w / L};
+  if constexpr (RND) v = f4{round_bf16(v.x), round_bf16(v.y), round_bf16(v.z), round_bf16(v.w)};
+  return v;
+}
+
+template <bool A_BF, bool B_BF, bool RND, int ASRC>
 __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
   __shared__ f4 sA[SKC][SM / 4];  // sA[k][q] = A rows 4q..4q+3 at k
   __shared__ f4 red[4][SM * SNS / 4];
@@ -120,7 +141,7 @@ __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
   }
   // A[0..M) x [k0, k0 + kn): element i of this thread's share is (i / SKC, i % SKC)
   araw_t araw[SM * SKC / ST];
-  if constexpr (!APART) {
+  if constexpr (ASRC == A_MEM) {
 #pragma unroll
     for (int j = 0; j < SM * SKC / ST; ++j) {
       const int i = t + j * ST, m = i / SKC, kk = i % SKC;
@@ -141,19 +162,85 @@ __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
     b[i] = ncol && kk < kn ? v : f4{0.f, 0.f, 0.f, 0.f};
   }
   // staged as fp32, k-major; rows past M and k past the chunk are zero
+  constexpr int E = SM * SKC / ST;
+  if constexpr (ASRC == A_ATTN) {
+    // thread t stages columns kq..kq+3 of rows m = t / (SKC/4) + g * (ST / (SKC/4))
+    constexpr int Q = SKC / 4, G = E / 4;
+    const int S = a.att_blocks;
+    const int kq = 4 * (t % Q);
+    const bool kin = kq < kn;
+    const int k = k0 + (kin ? kq : 0), hd = k / a.att_hs, d = k - hd * a.att_hs;
+    const float* mlp[G];
+    const float* accp[G];
 #pragma unroll
-  for (int j = 0; j < SM * SKC / ST; ++j) {
-    const int i = t + j * ST, m = i / SKC, kk = i % SKC;
-    float v;
-    if constexpr (APART) {
-      v = a_from_parts<RND>(a, m < a.M ? m : 0, k0 + (kk < kn ? kk : 0));
-    } else if constexpr (A_BF) {
-      v = bf16_val(araw[j]);
-    } else {
-      v = araw[j];
-      if constexpr (RND) v = round_bf16(v);
+    for (int g = 0; g < G; ++g) {
+      const int m = t / Q + g * (ST / Q);
+      const int64_t blk0 = ((int64_t)(m < a.M ? m : 0) * a.att_heads + hd) * S;
+      mlp[g] = a.att_ml + blk0 * 2;
+      accp[g] = a.att_acc + blk0 * a.att_hs + d;
     }
-    reinterpret_cast<float*>(sA)[kk * SM + m] = m < a.M && kk < kn ? v : 0.f;
+    float M[G], L[G];
+    f4 A[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) M[g] = -INFINITY, L[g] = 0.f, A[g] = f4{0.f, 0.f, 0.f, 0.f};
+    if (S <= AT_BATCH) {  // uniform over the grid
+      typedef float ff2 __attribute__((ext_vector_type(2)));
+      ff2 ml[G][AT_BATCH];
+      f4 ac[G][AT_BATCH];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int q = 0; q < AT_BATCH; ++q) {  // blocks past S repeat block S - 1 and are skipped
+          const int sq = min(q, S - 1);
+          ml[g][q] = *reinterpret_cast<const ff2*>(mlp[g] + 2 * sq);
+          ac[g][q] = *reinterpret_cast<const f4*>(accp[g] + (int64_t)sq * a.att_hs);
+        }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int q = 0; q < AT_BATCH; ++q) M[g] = fmaxf(M[g], ml[g][q].x);
+#pragma unroll
+        for (int q = 0; q < AT_BATCH; ++q)
+          if (q < S) {
+            const float f = expf(ml[g][q].x - M[g]);
+            L[g] += f * ml[g][q].y;
+            A[g] += f * ac[g][q];
+          }
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        for (int s = 0; s < S; ++s) M[g] = fmaxf(M[g], mlp[g][2 * s]);
+        for (int s = 0; s < S; ++s) {
+          const float f = expf(mlp[g][2 * s] - M[g]);
+          L[g] += f * mlp[g][2 * s + 1];
+          A[g] += f * *reinterpret_cast<const f4*>(accp[g] + (int64_t)s * a.att_hs);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int m = t / Q + g * (ST / Q);
+      const bool ok = m < a.M && kin;
+      const f4 v = ok ? att_finish<RND>(A[g], L[g]) : f4{0.f, 0.f, 0.f, 0.f};
+      float* col = reinterpret_cast<float*>(sA) + kq * SM + m;
+      col[0] = v.x, col[SM] = v.y, col[2 * SM] = v.z, col[3 * SM] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = t + j * ST, m = i / SKC, kk = i % SKC;
+      float v;
+      if constexpr (ASRC == A_PARTS) {
+        v = a_from_parts<RND>(a, m < a.M ? m : 0, k0 + (kk < kn ? kk : 0));
+      } else if constexpr (A_BF) {
+        v = bf16_val(araw[j]);
+      } else {
+        v = araw[j];
+        if constexpr (RND) v = round_bf16(v);
+      }
+      reinterpret_cast<float*>(sA)[kk * SM + m] = m < a.M && kk < kn ? v : 0.f;
+    }
   }
   __syncthreads();
 
@@ -321,6 +408,9 @@ SkPlan plan(const GemmArgs& g) {
   if (g.M < 1 || g.M > SM || g.batch != 1 || g.K < 1 || g.N < 1) return p;
   if (g.post == POST_GELU && (g.resid || g.beta != 0.f)) return p;
   if (g.a_part && (!g.a_bias || g.a_chunks < 1 || g.a_bf16 || g.post == POST_PARTIALS)) return p;
+  if (g.att_acc && (g.a_part || !g.att_ml || g.att_blocks < 1 || g.att_hs < 1 || g.att_heads < 1 ||
+                    (int64_t)g.att_hs * g.att_heads != g.K || g.a_bf16))
+    return p;
   if (g.post == POST_PARTIALS && (g.bias || g.resid || g.beta != 0.f || g.Cbf)) return p;
   if (g.post == POST_LN && (g.N > LN_MAXN || !g.ln_gamma || !g.ln_beta || !al(g.ln_gamma, 16) || !al(g.ln_beta, 16) ||
                             !al(g.ln_y, 16) || !al(g.ln_ybf, 8) || (!g.ln_y && !g.ln_ybf)))
@@ -339,9 +429,9 @@ SkPlan plan(const GemmArgs& g) {
   return p;
 }
 
-template <bool A_BF, bool B_BF, bool RND, bool APART = false>
+template <bool A_BF, bool B_BF, bool RND, int ASRC = A_MEM>
 void launch(const SkArgs& a, int grid, hipStream_t s) {
-  run_kernel((gemv_k<A_BF, B_BF, RND, APART>), dim3(grid), dim3(ST), 0, s, a);
+  run_kernel((gemv_k<A_BF, B_BF, RND, ASRC>), dim3(grid), dim3(ST), 0, s, a);
 }
 
 }  // namespace
@@ -372,13 +462,20 @@ bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_
   a.post = g.post, a.ln_gamma = g.ln_gamma, a.ln_beta = g.ln_beta, a.ln_eps = g.ln_eps, a.ln_y = g.ln_y;
   a.ln_ybf = g.ln_ybf;
   a.a_part = g.a_part, a.a_bias = g.a_bias, a.a_chunks = g.a_chunks;
+  a.att_acc = g.att_acc, a.att_ml = g.att_ml, a.att_blocks = g.att_blocks, a.att_hs = g.att_hs;
+  a.att_heads = g.att_heads;
   const int grid = p.strips * p.chunks;
   const bool rnd = g.prec == PREC_BF16;
   if (g.a_part) {
     if (g.b_bf16)
-      rnd ? launch<false, true, true, true>(a, grid, s) : launch<false, true, false, true>(a, grid, s);
+      rnd ? launch<false, true, true, A_PARTS>(a, grid, s) : launch<false, true, false, A_PARTS>(a, grid, s);
     else
-      rnd ? launch<false, false, true, true>(a, grid, s) : launch<false, false, false, true>(a, grid, s);
+      rnd ? launch<false, false, true, A_PARTS>(a, grid, s) : launch<false, false, false, A_PARTS>(a, grid, s);
+  } else if (g.att_acc) {
+    if (g.b_bf16)
+      rnd ? launch<false, true, true, A_ATTN>(a, grid, s) : launch<false, true, false, A_ATTN>(a, grid, s);
+    else
+      rnd ? launch<false, false, true, A_ATTN>(a, grid, s) : launch<false, false, false, A_ATTN>(a, grid, s);
   } else if (g.a_bf16 && g.b_bf16)
     launch<true, true, false>(a, grid, s);
   else if (g.a_bf16)

@@ -96,6 +96,16 @@ struct GemmArgs {
   const float* a_part = nullptr;
   const float* a_bias = nullptr;
   int a_chunks = 0;
+  // A taken from the cached attention's per-block results (few-row path only; A,
+  // lda, a_bf16 unused; K = att_heads * att_hs): for column k of row m, head
+  // hd = k / att_hs, d = k % att_hs, bh = m * att_heads + hd and blocks s < att_blocks,
+  //   A(m, k) = sum_s e^(M_s - M) acc_s[d] / sum_s e^(M_s - M) l_s,  M = max_s M_s,
+  // with (M_s, l_s) = att_ml[(bh * att_blocks + s) * 2 + {0, 1}] and acc_s[d] =
+  // att_acc[(bh * att_blocks + s) * att_hs + d] -- the merge kv_attend would have
+  // stored, in the same order, rounded to bf16 in the bf16 variant
+  const float* att_acc = nullptr;
+  const float* att_ml = nullptr;
+  int att_blocks = 0, att_hs = 0, att_heads = 0;
 };
 enum GemmPost { POST_NONE = 0, POST_GELU = 1, POST_LN = 2, POST_PARTIALS = 3 };
 
@@ -258,6 +268,11 @@ size_t kv_attend_workspace_bytes(int B, int C, int H, int pos);
 // qkv_part[c][B][3C] plus qkv_bias, the partials of the few-row c_attn product
 // (POST_PARTIALS); taken only where kv_attend_takes_parts(C, H)
 bool kv_attend_takes_parts(int C, int H);
+// y null (only where kv_attend_takes_parts(C, H), with ws): the attention stops at
+// its per-block results, which stay in ws as acc [B*H][S][C/H] then (M, l) [B*H][S][2]
+// with S = kv_attend_blocks(kv_bf16, pos); a few-row product merges them as it loads
+// them (GemmArgs::att_acc)
+int kv_attend_blocks(bool kv_bf16, int pos);
 hipError_t kv_attend(const float* qkv, void* kv, bool kv_bf16, float* y, int layer, int B, int Tmax, int C, int H,
                      int pos, float scale, void* ws, hipStream_t s, const float* qkv_part = nullptr, int qkv_chunks = 0,
                      const float* qkv_bias = nullptr);

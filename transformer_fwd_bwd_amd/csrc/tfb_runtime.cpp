@@ -666,7 +666,8 @@ struct Ctx {
   // bytes a few-row product must move: its operands once, its output once
   static double gemv_bytes(const GemmArgs& g) {
     const double ea = g.a_bf16 ? 2 : 4, eb = g.b_bf16 ? 2 : 4;
-    double b = (g.a_part ? 4.0 * g.a_chunks : ea) * g.M * (double)g.K + eb * (double)g.K * g.N;
+    double b = (g.a_part ? 4.0 * g.a_chunks : g.att_acc ? 4.0 * g.att_blocks : ea) * g.M * (double)g.K +
+               eb * (double)g.K * g.N;
     b += (g.c_bf16_only ? 2.0 : 4.0 + (g.Cbf ? 2.0 : 0.0)) * g.M * (double)g.N;
     if (g.bias) b += 4.0 * g.N;
     if (g.resid) b += 4.0 * g.M * (double)g.N;
@@ -1854,6 +1855,92 @@ int tfb_kv_attend_linear(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor x, tfb_
                 "kv_attend");
     });
     *y = h;  // inference only: not recorded on the tape
+  });
+}
+
+int tfb_kv_attention_block(tfb_ctx* ctx, tfb_kv* kv, int layer, tfb_tensor x, tfb_tensor w_attn, tfb_tensor b_attn,
+                           int pos, int heads, tfb_tensor w_proj, tfb_tensor b_proj, tfb_tensor r, tfb_tensor gamma,
+                           tfb_tensor beta, float eps, int flags, tfb_tensor* y, tfb_tensor* h) {
+  return guarded([&] {
+    Ctx C(ctx);
+    need((flags & ~TFB_OUT_BF16_ONLY) == 0, TFB_ERR_ARG, "unknown tfb_kv_attention_block flags");
+    need(kv != nullptr && kv->ctx == ctx, TFB_ERR_ARG, "cache of another context");
+    need(!ctx->grad_enabled, TFB_ERR_STATE, "tfb_kv_attention_block is inference-only: disable gradients first");
+    need(y != nullptr && h != nullptr, TFB_ERR_ARG, "null output");
+    x = C.dense_in(x, C.bf16_mode()), w_attn = C.dense_in(w_attn, C.bf16_mode()), b_attn = C.dense_in(b_attn);
+    w_proj = C.dense_in(w_proj, C.bf16_mode()), b_proj = C.dense_in(b_proj);
+    r = C.dense_in(r), gamma = C.dense_in(gamma), beta = C.dense_in(beta);
+    check_linear(C, x, w_attn, b_attn);
+    const int Cc = kv->channels;
+    TensorRec& X = C.T(x);
+    need(X.ndim == 3 && X.shape[0] == kv->batch && X.shape[1] == 1 && C.T(w_attn).shape[1] == 3LL * Cc,
+         TFB_ERR_SHAPE, "kv_attention_block needs x [batch, 1, K] and w_attn [K, 3C]");
+    need(layer >= 0 && layer < kv->layers, TFB_ERR_ARG, "no such layer");
+    need(pos >= 0 && pos < kv->tmax, TFB_ERR_SHAPE, "position past the cache length");
+    need(heads > 0 && Cc % heads == 0, TFB_ERR_SHAPE, "channels not divisible by heads");
+    need(C.T(w_proj).ndim == 2 && C.T(w_proj).shape[0] == Cc, TFB_ERR_SHAPE,
+         "attention projection must be [" + std::to_string(Cc) + ", N], got " + shape_str(C.T(w_proj)));
+    const int64_t N = C.T(w_proj).shape[1];
+    need(C.T(b_proj).numel == N && C.T(b_proj).ndim == 1, TFB_ERR_SHAPE,
+         "linear bias must be [" + std::to_string(N) + "]");
+    need(C.T(r).numel == (int64_t)kv->batch * N && C.T(r).cols() == N, TFB_ERR_SHAPE,
+         "residual must have the output's shape, got " + shape_str(C.T(r)));
+    need(C.T(gamma).numel == N && C.T(beta).numel == N, TFB_ERR_SHAPE,
+         "layernorm gain/shift must have " + std::to_string(N) + " elements");
+    need(N <= 2048, TFB_ERR_SHAPE, "layernorm rows longer than 2048 are not supported");
+    // c_attn leaves its partials, the attention sums them as it reads q, k and v and
+    // leaves its per-block results, and the projection merges those as it loads its
+    // input, then its chunk sum adds bias and residual and normalises the row
+    bool ok1 = false;
+    GemmArgs g1 = linear_post_args(C, x, w_attn, b_attn, -1, POST_PARTIALS, nullptr, nullptr, &ok1);
+    g1.bias = nullptr;
+    ok1 = gemv_accepts(g1) && kv_attend_takes_parts(Cc, heads);
+    const int hs = Cc / heads, S = kv_attend_blocks(kv->bf16, pos);
+    GemmArgs g2 = C.gemm_base();
+    g2.M = kv->batch, g2.N = (int)N, g2.K = Cc;
+    set_b(g2, op_data(C, C.T(w_proj))), g2.ldb = N;
+    g2.ldc = N, g2.bias = C.T(b_proj).data, g2.resid = C.f32(C.T(r));
+    g2.post = POST_LN, g2.ln_gamma = C.T(gamma).data, g2.ln_beta = C.T(beta).data, g2.ln_eps = eps;
+    float* stand_in = reinterpret_cast<float*>(C.c->arena.base);
+    g2.C = stand_in, g2.ln_y = stand_in;
+    g2.att_acc = stand_in, g2.att_ml = stand_in, g2.att_blocks = S, g2.att_hs = hs, g2.att_heads = heads;
+    if (ok1 && gemv_accepts(g2)) {
+      const size_t wb = gemv_workspace_bytes(g1);
+      void* parts = C.scratch(wb);  // kept until the attention below has read it (stream order)
+      float* ws = static_cast<float*>(
+          C.scratch(std::max<size_t>(kv_attend_workspace_bytes(kv->batch, Cc, heads, pos), 256)));
+      std::vector<int64_t> shp = shape_vec(X);
+      shp.back() = N;
+      int yh = C.make_output(shp);
+      int hh = C.make_output(shp);
+      uint16_t* hb = C.twin_data(ctx->tensors[hh]);
+      const bool only = hb && (flags & TFB_OUT_BF16_ONLY);
+      g1.C = nullptr;
+      C.run_gemm_ws(g1, parts, wb);
+      const float scale = 1.f / std::sqrt((float)hs);
+      const double e = kv->bf16 ? 2.0 : 4.0;
+      const double bytes = (double)kv->batch * Cc * (2 * e * (pos + 1) + 2 * e + 4.0 + 4.0);
+      const float* bias = C.T(b_attn).data;
+      const int chunks = gemv_chunks(g1);
+      C.timed(TFB_PROF_KV_ATTEND, bytes, [&] {
+        hip_check(kv_attend(nullptr, kv->data, kv->bf16, nullptr, layer, kv->batch, kv->tmax, Cc, heads, pos, scale,
+                            ws, C.s(), static_cast<const float*>(parts), chunks, bias),
+                  "kv_attend");
+      });
+      g2.att_acc = ws, g2.att_ml = ws + (int64_t)kv->batch * heads * S * hs;
+      g2.C = ctx->tensors[yh].data;
+      g2.ln_y = only ? nullptr : ctx->tensors[hh].data, g2.ln_ybf = hb;
+      C.run_gemm(g2);
+      if (hb) ctx->tensors[hh].bf_valid = true;
+      if (only) ctx->tensors[hh].f32_valid = false, ctx->tensors[hh].bf16_out = true;
+      *y = yh, *h = hh;
+      return;
+    }
+    tfb_tensor a;
+    int rc = tfb_kv_attend_linear(ctx, kv, layer, x, w_attn, b_attn, pos, heads, &a);
+    if (rc) rethrow(rc);
+    rc = tfb_linear_residual_layernorm(ctx, a, w_proj, b_proj, r, gamma, beta, eps, flags, y, h);
+    if (rc) rethrow(rc);
   });
 }
 

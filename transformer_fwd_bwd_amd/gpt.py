@@ -15,8 +15,7 @@ from typing import Dict, List, Sequence
 import numpy as np
 
 from . import (AdamW, Context, KvCache, Tensor, add, causal_attention, embedding, gelu, layernorm, linear,
-               linear_residual_layernorm, matmul_t, mlp_residual_layernorm, narrow, reshape, sample_topk,
-               softmax_cross_entropy, tanh)
+               matmul_t, mlp_residual_layernorm, narrow, reshape, sample_topk, softmax_cross_entropy, tanh)
 
 
 def upload_params(ctx: Context, params: Dict[str, np.ndarray]) -> Dict[str, Tensor]:
@@ -111,14 +110,15 @@ class Gpt:
                 reshape(embedding(P["wpe.weight"], self.positions(tmax)[pos:pos + 1], 1), (1, C)))
         # the same ops in fewer passes: each LayerNorm is folded into the chunk sum of
         # the residual projection before it, the c_attn product's chunk sum into the
-        # cached attention's loads, and the MLP's hidden activation (c_fc and GELU)
-        # into the projection's loads
+        # cached attention's loads, the attention's merge of its position blocks into
+        # the projection's loads, and the MLP's hidden activation (c_fc and GELU) into
+        # the MLP projection's loads
         h = layernorm(x, P["h.0.ln_1.weight"], P["h.0.ln_1.bias"], bf16_only=True)
         for i in range(self.n_layer):
             p = f"h.{i}."
-            a = kv.attend_linear(i, h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"], pos, self.n_head)
-            x, h = linear_residual_layernorm(a, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"], x,
-                                             P[p + "ln_2.weight"], P[p + "ln_2.bias"], bf16_only=True)
+            x, h = kv.attention_block(i, h, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"], pos,
+                                      self.n_head, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"], x,
+                                      P[p + "ln_2.weight"], P[p + "ln_2.bias"], bf16_only=True)
             ln = f"h.{i + 1}.ln_1" if i + 1 < self.n_layer else "ln_f"
             x, h = mlp_residual_layernorm(h, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"],
                                           P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"], x,
