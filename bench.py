@@ -58,7 +58,7 @@ FAMILY_NAMES = {
     "attn_bwd": "attn_dq_k + attn_dkv_k (fused attention backward)", "ce": "ce_fwd_grad4_k / ce kernels",
     "adamw": "adamw_k", "ln_fwd": "ln_fwd4_k", "ln_bwd": "ln_bwd_fused4_k", "gelu_fwd": "gelu forward",
     "gelu_bwd": "gelu backward", "gemv": "gemv_k + gemv_reduce_k (decode Linears)",
-    "kv_attend": "kv_attend_part_k + merge (cached attention)", "sample": "sample_topk_reg_k",
+    "kv_attend": "kv_attend_part_k (cached attention)", "sample": "sample_topk_reg_k",
 }
 
 
