@@ -464,10 +464,21 @@ def test_pointwise(ctx, name):
         check(ctx, "fp32", T.sum_all, E.sum_all, [a], (1,))
 
 
-@pytest.mark.parametrize("C", [768, 100, 1500])
+@pytest.mark.parametrize("C", [768, 100, 400, 1000, 1500])
 def test_layernorm(ctx, C):
+    """Row widths of 1, 3 (partly filled: 400), 3 (exactly: 768) and 4 (1000) float4s per
+    lane in the fused backward, and one (1500) past it."""
     x = rnd(23, (3, 70, C), 2.0) + 0.5
     g, b = 1 + rnd(24, (C,), 0.2), rnd(25, (C,), 0.2)
+    check(ctx, "fp32", lambda x, g, b: T.layernorm(x, g, b, 1e-5), lambda x, g, b: E.layernorm(x, g, b, 1e-5),
+          [x, g, b], x.shape)
+
+
+def test_layernorm_more_rows_than_one_pass(ctx):
+    """8400 rows of 768: more than the fused backward's workgroups take in one pass
+    of two rows per wave, so some waves take a second pass with a single row."""
+    x = rnd(28, (2, 4200, 768), 2.0) + 0.5
+    g, b = 1 + rnd(29, (768,), 0.2), rnd(30, (768,), 0.2)
     check(ctx, "fp32", lambda x, g, b: T.layernorm(x, g, b, 1e-5), lambda x, g, b: E.layernorm(x, g, b, 1e-5),
           [x, g, b], x.shape)
 

@@ -204,87 +204,107 @@ __global__ __launch_bounds__(NT) void ln_bwd_dx_k(const float* __restrict__ g, c
 // LayerNorm backward over float4 rows, one wavefront per row (the row held in
 // registers): dx = rstd (g*gamma - mean(g*gamma) - xhat mean(g*gamma*xhat)),
 // plus the dgamma / dbeta column partials of the rows this workgroup handles:
-// each lane keeps sum g*xhat and sum g for its float4 columns over its wave's
-// rows, the 4 waves are added in LDS in a fixed order, and part[block][plane][C]
-// receives the result (reduced by ln_bwd_reduce).  With SUMDX a third plane holds
-// the column sums of the final dx (the bias gradient of a Linear whose output
-// gradient this is).  A wave loads its rows two at a time, so two rows' reads are
-// in flight.
+// each lane adds g*xhat and g for its float4 columns into its wave's slice of
+// LDS (only that lane touches those entries, so no barrier until the end), the
+// 4 waves' slices are added in a fixed order, and part[block][plane][C] receives
+// the result (reduced by ln_bwd_reduce).  With SUMDX a third plane holds the
+// column sums of the final dx (the bias gradient of a Linear whose output
+// gradient this is).  A wave loads its rows two at a time, so two rows' reads
+// are in flight; keeping the partials out of registers leaves room for four
+// waves per SIMD at C = 768.
 __device__ __forceinline__ f4 ld_g4(const f4* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ f4 ld_g4(const u16x4* p, int64_t i) {  // exact float values of 4 bf16 numbers
   const u16x4 v = p[i];
   return f4{__uint_as_float((unsigned)v[0] << 16), __uint_as_float((unsigned)v[1] << 16),
             __uint_as_float((unsigned)v[2] << 16), __uint_as_float((unsigned)v[3] << 16)};
 }
+// the same in two steps: the stored form (held until used), then its float values
+__device__ __forceinline__ f4 g4_val(const f4& v) { return v; }
+__device__ __forceinline__ f4 g4_val(const u16x4& v) {
+  return f4{__uint_as_float((unsigned)v[0] << 16), __uint_as_float((unsigned)v[1] << 16),
+            __uint_as_float((unsigned)v[2] << 16), __uint_as_float((unsigned)v[3] << 16)};
+}
 
-// GT: f4, or u16x4 for an upstream gradient held as bf16
-template <int J, bool SUMDX, typename GT = f4>
-__global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const GT* __restrict__ g, const f4* __restrict__ x,
-                                                      const f4* __restrict__ gamma, const float* __restrict__ mean,
-                                                      const float* __restrict__ rstd, f4* dx, const f4* dx_src,
-                                                      u16x4* __restrict__ dxbf, f4* __restrict__ part, int64_t rows,
-                                                      int C4, float beta_dx) {
+// GT: f4, or u16x4 for an upstream gradient held as bf16.  FULL: C4 == 64 J (every
+// lane has J float4s of every row; no column checks).  The wave index is made
+// scalar, so a row's base addresses are scalar and each load is that base plus
+// the lane's offset: no per-lane 64-bit addresses to hold.
+template <int J, bool SUMDX, bool FULL, typename GT = f4>
+__global__ __launch_bounds__(NT, J <= 3 ? 4 : 2) void ln_bwd_fused4_k(
+    const GT* __restrict__ g, const f4* __restrict__ x, const f4* __restrict__ gamma, const float* __restrict__ mean,
+    const float* __restrict__ rstd, f4* dx, const f4* dx_src, u16x4* __restrict__ dxbf, f4* __restrict__ part,
+    int64_t rows, int C4, float beta_dx) {
   constexpr int NP = SUMDX ? 3 : 2;
-  __shared__ f4 sh[WAVES - 1][NP][64 * J];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ f4 sh[WAVES][NP][64 * J];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nw = (int64_t)gridDim.x * WAVES;
   const float invC = 1.f / (4 * C4);
-  f4 pa[J], pb[J], pc[J];
+  const auto in = [&](int j) { return FULL || lane + 64 * j < C4; };
 #pragma unroll
-  for (int j = 0; j < J; ++j) pa[j] = pb[j] = pc[j] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int q = 0; q < NP; ++q) sh[w][q][lane + 64 * j] = f4{0.f, 0.f, 0.f, 0.f};
   for (int64_t r0 = (int64_t)blockIdx.x * WAVES + w; r0 < rows; r0 += 2 * nw) {
-    const int64_t rr[2] = {r0, r0 + nw};
-    // both rows' x, g and earlier dx are loaded before any store: each lane reads
-    // and writes only its own elements, so this holds even when dx_src is dx
-    f4 xv[2][J], gv[2][J], sv[2][J];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int c = lane + 64 * j;
-        const bool ok = c < C4 && rr[u] < rows;
-        xv[u][j] = ok ? x[rr[u] * C4 + c] : f4{0.f, 0.f, 0.f, 0.f};
-        gv[u][j] = ok ? ld_g4(g, rr[u] * C4 + c) : f4{0.f, 0.f, 0.f, 0.f};
-        sv[u][j] = ok && beta_dx != 0.f ? dx_src[rr[u] * C4 + c] : f4{0.f, 0.f, 0.f, 0.f};
-      }
+    // the column partials stay in LDS: without this compiler-only fence the
+    // compiler keeps them in registers across rows (nothing else touches them
+    // inside the loop), which is what keeping them in LDS is meant to avoid
+    asm volatile("" ::: "memory");
+    // rows r0 and r0 + nw (the second clamped to an in-range row when past the end,
+    // its results then unused); both rows' x and g are loaded before either is used
+    const int64_t rr[2] = {r0, r0 + nw < rows ? r0 + nw : r0};
+    f4 xv[2][J];
+    GT graw[2][J];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      const f4* xr = x + rr[u] * C4;
+      const GT* gr = g + rr[u] * C4;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int c = in(j) ? lane + 64 * j : 0;  // an in-range column, its value unused
+        xv[u][j] = xr[c];
+        graw[u][j] = gr[c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && r0 + nw >= rows) break;
       const int64_t r = rr[u];
-      if (r >= rows) break;
       const float mu = mean[r], rs = rstd[r];
       f4 xh[J], dg[J];
       float s1 = 0.f, s2 = 0.f;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int c = lane + 64 * j;
-        xh[j] = c < C4 ? (xv[u][j] - mu) * rs : f4{0.f, 0.f, 0.f, 0.f};
-        dg[j] = c < C4 ? gv[u][j] * gamma[c] : f4{0.f, 0.f, 0.f, 0.f};
-        pa[j] += gv[u][j] * xh[j];
-        pb[j] += gv[u][j];
+        const f4 gj = in(j) ? g4_val(graw[u][j]) : f4{0.f, 0.f, 0.f, 0.f};
+        xh[j] = in(j) ? (xv[u][j] - mu) * rs : f4{0.f, 0.f, 0.f, 0.f};
+        dg[j] = in(j) ? gj * gamma[in(j) ? c : 0] : f4{0.f, 0.f, 0.f, 0.f};
+        sh[w][0][c] += gj * xh[j];
+        sh[w][1][c] += gj;
         s1 += (dg[j][0] + dg[j][1]) + (dg[j][2] + dg[j][3]);
         const f4 t = dg[j] * xh[j];
         s2 += (t[0] + t[1]) + (t[2] + t[3]);
       }
+      // the earlier gradient of an element is read just before that element is
+      // stored, by the lane that stores it, so this holds even when dx_src is dx
+      f4 sv[J];
+      const f4* sr = dx_src + r * C4;
+#pragma unroll
+      for (int j = 0; j < J; ++j)  // zero when beta_dx == 0
+        sv[j] = beta_dx != 0.f ? sr[in(j) ? lane + 64 * j : 0] : f4{0.f, 0.f, 0.f, 0.f};
       const float m1 = wave_sum(s1) * invC, m2 = wave_sum(s2) * invC;
+      f4* dr = dx + r * C4;
+      u16x4* dbr = dxbf ? dxbf + r * C4 : nullptr;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int c = lane + 64 * j;
-        if (c < C4) {
+        if (in(j)) {
           f4 v = rs * (dg[j] - m1 - xh[j] * m2);
-          v += sv[u][j];  // the earlier gradient (zero when beta_dx == 0)
-          dx[r * C4 + c] = v;
-          if constexpr (SUMDX) pc[j] += v;
-          if (dxbf) dxbf[r * C4 + c] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
+          v += sv[j];
+          dr[c] = v;
+          if constexpr (SUMDX) sh[w][2][c] += v;
+          if (dbr) dbr[c] = u16x4{bf16_bits(v[0]), bf16_bits(v[1]), bf16_bits(v[2]), bf16_bits(v[3])};
         }
       }
-    }
-  }
-  if (w > 0) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      sh[w - 1][0][lane + 64 * j] = pa[j];
-      sh[w - 1][1][lane + 64 * j] = pb[j];
-      if constexpr (SUMDX) sh[w - 1][2][lane + 64 * j] = pc[j];
     }
   }
   __syncthreads();
@@ -292,17 +312,14 @@ __global__ __launch_bounds__(NT) void ln_bwd_fused4_k(const GT* __restrict__ g, 
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int c = lane + 64 * j;
-      if (c < C4) {
-        f4 a = pa[j], b = pb[j], d = pc[j];
+      if (in(j)) {
 #pragma unroll
-        for (int i = 0; i < WAVES - 1; ++i) {
-          a += sh[i][0][c];
-          b += sh[i][1][c];
-          if constexpr (SUMDX) d += sh[i][2][c];
+        for (int q = 0; q < NP; ++q) {
+          f4 a = sh[0][q][c];
+#pragma unroll
+          for (int i = 1; i < WAVES; ++i) a += sh[i][q][c];
+          part[((int64_t)blockIdx.x * NP + q) * C4 + c] = a;
         }
-        part[((int64_t)blockIdx.x * NP) * C4 + c] = a;
-        part[((int64_t)blockIdx.x * NP + 1) * C4 + c] = b;
-        if constexpr (SUMDX) part[((int64_t)blockIdx.x * NP + 2) * C4 + c] = d;
       }
     }
   }
@@ -364,7 +381,7 @@ int ln_bwd_parts(int64_t rows) {
 
 // workgroups of the fused LayerNorm backward: at most 512 (two per CU), each
 // wave taking two rows per step; the column partials stay a few MB
-int64_t ln_fused_blocks(int64_t rows) { return std::max<int64_t>(1, std::min<int64_t>(512, (rows + WAVES - 1) / WAVES)); }
+int64_t ln_fused_blocks(int64_t rows) { return std::max<int64_t>(1, std::min<int64_t>(1024, (rows + WAVES - 1) / WAVES)); }
 
 // ------------------------------------------------------------ causal softmax
 template <bool CACHED>
@@ -849,26 +866,28 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
     const f4 *x4 = (const f4*)x, *gm4 = (const f4*)gamma, *src4 = (const f4*)dx_src;
     auto launch = [&](auto gp) {
       using GT = std::remove_const_t<std::remove_pointer_t<decltype(gp)>>;
+      auto go = [&](auto kern) {
+        run_kernel(kern, grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4, (u16x4*)dxbf, (f4*)part, rows, C4,
+                   beta_dx);
+      };
       if (dxsum) {
         if (C4 <= 64)
-          run_kernel((ln_bwd_fused4_k<1, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
-                             (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+          go(ln_bwd_fused4_k<1, true, false, GT>);
+        else if (C4 == 192)
+          go(ln_bwd_fused4_k<3, true, true, GT>);
         else if (C4 <= 192)
-          run_kernel((ln_bwd_fused4_k<3, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
-                             (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+          go(ln_bwd_fused4_k<3, true, false, GT>);
         else
-          run_kernel((ln_bwd_fused4_k<4, true, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
-                             (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+          go(ln_bwd_fused4_k<4, true, false, GT>);
       } else {
         if (C4 <= 64)
-          run_kernel((ln_bwd_fused4_k<1, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx, src4,
-                             (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+          go(ln_bwd_fused4_k<1, false, false, GT>);
+        else if (C4 == 192)
+          go(ln_bwd_fused4_k<3, false, true, GT>);
         else if (C4 <= 192)
-          run_kernel((ln_bwd_fused4_k<3, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx,
-                             src4, (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+          go(ln_bwd_fused4_k<3, false, false, GT>);
         else
-          run_kernel((ln_bwd_fused4_k<4, false, GT>), grid, block, 0, s, gp, x4, gm4, mean, rstd, (f4*)dx,
-                             src4, (u16x4*)dxbf, (f4*)part, rows, C4, beta_dx);
+          go(ln_bwd_fused4_k<4, false, false, GT>);
       }
     };
     if (dxsum) np = 3;
