@@ -258,13 +258,15 @@ __global__ __launch_bounds__(256, HS <= 64 ? 4 : 2) void kv_attend_part_k(QkvSrc
   // rows past the block and the new token's row (not stored yet) read row j_lo
   // instead, an in-range address: their loaded values are replaced below
   const int j_mem = last ? pos : j_hi;
+  // (non-temporal: a step streams the whole cache, more than the Infinity Cache
+  // holds, so its rows are not kept there at the weights' expense)
   kr4 kr[IT], vr[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int j = jw + it * RPI + r;
     const int64_t row = (int64_t)(j < j_mem ? j : j_lo) * C + c * VW;
-    kr[it] = *reinterpret_cast<const kr4*>(Kc + row);
-    vr[it] = *reinterpret_cast<const kr4*>(Vc + row);
+    kr[it] = __builtin_nontemporal_load(reinterpret_cast<const kr4*>(Kc + row));
+    vr[it] = __builtin_nontemporal_load(reinterpret_cast<const kr4*>(Vc + row));
   }
   // the query: lane f < HS/4 sums float4 f once, then the wave shares it
   kf4 qf = {0.f, 0.f, 0.f, 0.f};
