@@ -282,6 +282,45 @@ def test_kv_attention_block(ctx, prec, hs, H, P0):
             t.release()
 
 
+def test_kv_attention_block_rejects_bad_shapes(ctx):
+    """The fused attention block checks its operands before launching anything:
+    a projection whose rows are not the cache's channels, a residual of another
+    width, a position past the cache and a head count that does not divide the
+    channels are shape errors; a cache of another context is an argument error."""
+    B, C, K, Tmax = 2, 64, 32, 16
+    kv = T.KvCache(ctx, 1, B, Tmax, C)
+    made = []
+
+    def mk(*shape):
+        made.append(ctx.tensor(shape, rnd(len(shape) + sum(shape), shape)))
+        return made[-1]
+
+    x, wa, ba = mk(B, 1, K), mk(K, 3 * C), mk(3 * C)
+    wp, bp, r, g, bt = mk(C, C), mk(C), mk(B, 1, C), mk(C), mk(C)
+    ctx.set_grad_enabled(False)
+    try:
+        cases = [
+            ("projection rows", lambda: kv.attention_block(0, x, wa, ba, 0, 2, mk(C + 4, C), bp, r, g, bt), -2),
+            ("residual width", lambda: kv.attention_block(0, x, wa, ba, 0, 2, wp, bp, mk(B, 1, C + 4), g, bt), -2),
+            ("position", lambda: kv.attention_block(0, x, wa, ba, Tmax, 2, wp, bp, r, g, bt), -2),
+            ("heads", lambda: kv.attention_block(0, x, wa, ba, 0, 3, wp, bp, r, g, bt), -2),
+            ("layer", lambda: kv.attention_block(1, x, wa, ba, 0, 2, wp, bp, r, g, bt), -1),
+        ]
+        for what, call, code in cases:
+            with pytest.raises(T.TfbError) as e:
+                call()
+            assert e.value.code == code, (what, e.value.code, str(e.value))
+        # the cache is untouched by the rejected calls: a good call still matches
+        y, h = kv.attention_block(0, x, wa, ba, 0, 2, wp, bp, r, g, bt)
+        assert np.isfinite(y.numpy()).all() and np.isfinite(h.numpy()).all()
+    finally:
+        ctx.set_grad_enabled(True)
+        kv.close()
+        ctx.tape_reset()
+        for t in made:
+            t.release()
+
+
 def test_inference_fusions_refuse_to_record(ctx):
     x, w, b = ctx.tensor((2, 8), np.ones((2, 8), np.float32)), ctx.tensor((8, 8)), ctx.tensor((8,))
     with pytest.raises(T.TfbError) as e:
