@@ -229,22 +229,26 @@ __device__ __forceinline__ f4 g4_val(const u16x4& v) {
 // lane has J float4s of every row; no column checks).  The wave index is made
 // scalar, so a row's base addresses are scalar and each load is that base plus
 // the lane's offset: no per-lane 64-bit addresses to hold.
+// Eight waves per workgroup, two workgroups per CU at C = 768 (four waves per
+// SIMD): the workgroups, and so the partial rows that the column reduction reads
+// afterwards, are half as many as with four-wave workgroups.
+constexpr int LNW = 8;
 template <int J, bool SUMDX, bool FULL, typename GT = f4>
-__global__ __launch_bounds__(NT, J <= 3 ? 4 : 2) void ln_bwd_fused4_k(
+__global__ __launch_bounds__(LNW * 64, J <= 3 ? 2 : 1) void ln_bwd_fused4_k(
     const GT* __restrict__ g, const f4* __restrict__ x, const f4* __restrict__ gamma, const float* __restrict__ mean,
     const float* __restrict__ rstd, f4* dx, const f4* dx_src, u16x4* __restrict__ dxbf, f4* __restrict__ part,
     int64_t rows, int C4, float beta_dx) {
   constexpr int NP = SUMDX ? 3 : 2;
-  __shared__ f4 sh[WAVES][NP][64 * J];
+  __shared__ f4 sh[LNW][NP][64 * J];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nw = (int64_t)gridDim.x * WAVES;
+  const int64_t nw = (int64_t)gridDim.x * LNW;
   const float invC = 1.f / (4 * C4);
   const auto in = [&](int j) { return FULL || lane + 64 * j < C4; };
 #pragma unroll
   for (int j = 0; j < J; ++j)
 #pragma unroll
     for (int q = 0; q < NP; ++q) sh[w][q][lane + 64 * j] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t r0 = (int64_t)blockIdx.x * WAVES + w; r0 < rows; r0 += 2 * nw) {
+  for (int64_t r0 = (int64_t)blockIdx.x * LNW + w; r0 < rows; r0 += 2 * nw) {
     // the column partials stay in LDS: without this compiler-only fence the
     // compiler keeps them in registers across rows (nothing else touches them
     // inside the loop), which is what keeping them in LDS is meant to avoid
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(NT, J <= 3 ? 4 : 2) void ln_bwd_fused4_k(
         for (int q = 0; q < NP; ++q) {
           f4 a = sh[0][q][c];
 #pragma unroll
-          for (int i = 1; i < WAVES; ++i) a += sh[i][q][c];
+          for (int i = 1; i < LNW; ++i) a += sh[i][q][c];
           part[((int64_t)blockIdx.x * NP + q) * C4 + c] = a;
         }
       }
@@ -381,7 +385,7 @@ int ln_bwd_parts(int64_t rows) {
 
 // workgroups of the fused LayerNorm backward: at most 512 (two per CU), each
 // wave taking two rows per step; the column partials stay a few MB
-int64_t ln_fused_blocks(int64_t rows) { return std::max<int64_t>(1, std::min<int64_t>(1024, (rows + WAVES - 1) / WAVES)); }
+int64_t ln_fused_blocks(int64_t rows) { return std::max<int64_t>(1, std::min<int64_t>(512, (rows + LNW - 1) / LNW)); }
 
 // ------------------------------------------------------------ causal softmax
 template <bool CACHED>
@@ -862,7 +866,7 @@ hipError_t layernorm_bwd(const float* g, const float* x, const float* gamma, con
     // dx (and its bf16 copy) and the column partials in one pass over g and x
     const int C4 = (int)(C / 4);
     const int64_t blocks = ln_fused_blocks(rows);
-    const dim3 grid((unsigned)blocks), block(NT);
+    const dim3 grid((unsigned)blocks), block(LNW * 64);
     const f4 *x4 = (const f4*)x, *gm4 = (const f4*)gamma, *src4 = (const f4*)dx_src;
     auto launch = [&](auto gp) {
       using GT = std::remove_const_t<std::remove_pointer_t<decltype(gp)>>;
