@@ -28,6 +28,10 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int SM = 16;    // rows of A held
 constexpr int SNS = 64;   // columns per strip
@@ -78,26 +82,6 @@ struct SkArgs {
 // where the kernel takes A from
 enum ASrc { A_MEM = 0, A_PARTS = 1, A_ATTN = 2 };
 
-// A from the previous few-row product's partials: gelu(sum of its chunks + bias), as
-// that product's reduction would have computed it (same order), rounded to bf16 in
-// the bf16 variant
-template <bool RND>
-__device__ __forceinline__ float a_from_parts(const SkArgs& a, int m, int k) {
-  const int64_t stride = (int64_t)a.M * a.K;
-  const float* p = a.a_part + (int64_t)m * a.K + k;
-  float v = 0.f;
-  for (int c0 = 0; c0 < a.a_chunks; c0 += 8) {
-    float x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = p[(int64_t)min(c0 + j, a.a_chunks - 1) * stride];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (c0 + j < a.a_chunks) v += x[j];
-  }
-  v = gelu_f(v + a.a_bias[k]);
-  return RND ? round_bf16(v) : v;
-}
-
 // A from the cached attention's per-block results: their merge, in the order and
 // arithmetic of the attention's own merge pass, rounded to bf16 in the bf16
 // variant.  A thread stages four consecutive columns of one head (head sizes are
@@ -113,9 +97,19 @@ __device__ __forceinline__ f4 att_finish(f4 A, float L) {
   return v;
 }
 
+// MF: both operands are bf16 values (stored so, or rounded as they load), so
+// the 16-row product runs on MFMA: A staged as bf16 rows [m][k], B as bf16
+// k-rows of the strip (64-byte column blocks swapped on every other pair of
+// k-rows, so the four k-rows of a transposing read fall in distinct banks), each
+// wave taking two of the chunk's 16-deep k-steps on 32x32x16 tiles (rows 16..31
+// zero); the waves' partial tiles meet in `red` as the VALU path's do.
 template <bool A_BF, bool B_BF, bool RND, int ASRC>
 __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
-  __shared__ f4 sA[SKC][SM / 4];  // sA[k][q] = A rows 4q..4q+3 at k
+  constexpr bool MF = B_BF && (A_BF || RND);
+  constexpr int AP = SKC + 8;  // sA16 row pitch (elements)
+  __shared__ f4 sA[MF ? 1 : SKC][SM / 4];  // sA[k][q] = A rows 4q..4q+3 at k (VALU path)
+  __shared__ __attribute__((aligned(16))) unsigned short sA16[MF ? SM : 1][AP];    // MFMA path: A[m][k]
+  __shared__ __attribute__((aligned(16))) unsigned short sB[MF ? SKC * SNS : 1];   // MFMA path: B k-rows
   __shared__ f4 red[4][SM * SNS / 4];
   const int strips = (a.N + SNS - 1) / SNS;
   const int strip = blockIdx.x % strips, chunk = blockIdx.x / strips;
@@ -149,6 +143,17 @@ __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
     }
   }
   f4 b[SKC / 16];
+  if constexpr (MF) {
+    // k-row kk of the strip: 128 bytes, column block (32 columns, 64 bytes) cb at
+    // block cb ^ ((kk >> 1) & 1); out-of-range weights are stored as zeros
+#pragma unroll
+    for (int i = 0; i < SKC / 16; ++i) {
+      const int kk = 4 * w + r + 16 * i, cl = 4 * c;
+      const int blk = (cl >> 5) ^ ((kk >> 1) & 1);
+      *reinterpret_cast<u16x4*>(reinterpret_cast<char*>(sB) + kk * 128 + blk * 64 + (cl & 31) * 2) =
+          ncol && kk < kn ? braw[i] : u16x4{0, 0, 0, 0};
+    }
+  } else {
 #pragma unroll
   for (int i = 0; i < SKC / 16; ++i) {
     const int kk = 4 * w + r + 16 * i;
@@ -161,7 +166,15 @@ __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
     }
     b[i] = ncol && kk < kn ? v : f4{0.f, 0.f, 0.f, 0.f};
   }
-  // staged as fp32, k-major; rows past M and k past the chunk are zero
+  }
+  // staged as fp32, k-major (bf16 [m][k] on the MFMA path); rows past M and k past
+  // the chunk are zero
+  auto put = [&](int m, int kk, float v) __attribute__((always_inline)) {
+    if constexpr (MF)
+      sA16[m][kk] = bf16_of(v);  // a bf16 value already: exact
+    else
+      reinterpret_cast<float*>(sA)[kk * SM + m] = v;
+  };
   constexpr int E = SM * SKC / ST;
   if constexpr (ASRC == A_ATTN) {
     // thread t stages columns kq..kq+3 of rows m = t / (SKC/4) + g * (ST / (SKC/4))
@@ -223,27 +236,126 @@ __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
       const int m = t / Q + g * (ST / Q);
       const bool ok = m < a.M && kin;
       const f4 v = ok ? att_finish<RND>(A[g], L[g]) : f4{0.f, 0.f, 0.f, 0.f};
-      float* col = reinterpret_cast<float*>(sA) + kq * SM + m;
-      col[0] = v.x, col[SM] = v.y, col[2 * SM] = v.z, col[3 * SM] = v.w;
+      if constexpr (MF) {
+        *reinterpret_cast<u16x4*>(&sA16[m][kq]) = u16x4{bf16_of(v.x), bf16_of(v.y), bf16_of(v.z), bf16_of(v.w)};
+      } else {
+        float* col = reinterpret_cast<float*>(sA) + kq * SM + m;
+        col[0] = v.x, col[SM] = v.y, col[2 * SM] = v.z, col[3 * SM] = v.w;
+      }
+    }
+  } else if constexpr (ASRC == A_PARTS) {
+    // A from the previous few-row product's partials: gelu(the sum of its chunks in
+    // chunk order + bias), rounded to bf16 in the bf16 variant -- the values that
+    // product's reduction would have stored.  As above, a thread stages four
+    // consecutive columns of one row (K is a multiple of 4 here), and the chunks of
+    // both its rows are requested before any is used.
+    constexpr int Q = SKC / 4, G = E / 4;
+    const int kq = 4 * (t % Q);
+    const bool kin = kq < kn;
+    const int k = k0 + (kin ? kq : 0);
+    const int64_t stride = (int64_t)a.M * a.K;
+    const int CH = a.a_chunks;
+    f4 v[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) v[g] = f4{0.f, 0.f, 0.f, 0.f};
+    if (CH <= 8) {  // uniform over the grid
+      f4 x[G][8];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int m = t / Q + g * (ST / Q);
+        const float* p = a.a_part + (int64_t)(m < a.M ? m : 0) * a.K + k;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[g][j] = *reinterpret_cast<const f4*>(p + min(j, CH - 1) * stride);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < CH) v[g] += x[g][j];
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int m = t / Q + g * (ST / Q);
+        const float* p = a.a_part + (int64_t)(m < a.M ? m : 0) * a.K + k;
+        for (int c0 = 0; c0 < CH; c0 += 8) {
+          f4 x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const f4*>(p + min(c0 + j, CH - 1) * stride);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c0 + j < CH) v[g] += x[j];
+        }
+      }
+    }
+    const f4 bias = *reinterpret_cast<const f4*>(a.a_bias + k);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int m = t / Q + g * (ST / Q);
+      f4 y = v[g] + bias;
+      y = f4{gelu_f(y.x), gelu_f(y.y), gelu_f(y.z), gelu_f(y.w)};
+      if constexpr (RND) y = f4{round_bf16(y.x), round_bf16(y.y), round_bf16(y.z), round_bf16(y.w)};
+      if (!(m < a.M && kin)) y = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (MF) {
+        *reinterpret_cast<u16x4*>(&sA16[m][kq]) = u16x4{bf16_of(y.x), bf16_of(y.y), bf16_of(y.z), bf16_of(y.w)};
+      } else {
+        float* col = reinterpret_cast<float*>(sA) + kq * SM + m;
+        col[0] = y.x, col[SM] = y.y, col[2 * SM] = y.z, col[3 * SM] = y.w;
+      }
     }
   } else {
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const int i = t + j * ST, m = i / SKC, kk = i % SKC;
       float v;
-      if constexpr (ASRC == A_PARTS) {
-        v = a_from_parts<RND>(a, m < a.M ? m : 0, k0 + (kk < kn ? kk : 0));
-      } else if constexpr (A_BF) {
+      if constexpr (A_BF) {
         v = bf16_val(araw[j]);
       } else {
         v = araw[j];
         if constexpr (RND) v = round_bf16(v);
       }
-      reinterpret_cast<float*>(sA)[kk * SM + m] = m < a.M && kk < kn ? v : 0.f;
+      put(m, kk, m < a.M && kk < kn ? v : 0.f);
     }
   }
   __syncthreads();
 
+  if constexpr (MF) {
+    // wave w takes k-steps w and w + 4 (16 k each) of the chunk, both 32-column
+    // blocks of the strip; the tile's rows 16..31 are zero
+    const int l32 = lane & 31, h = lane >> 5;
+    const int tr_row = 8 * h + ((lane & 15) >> 2), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    f32x16 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int q = w + 4 * qq;
+      if (q * 16 >= kn) break;  // uniform per wave: the rest of the chunk is past its end
+      bf16x8 af = *reinterpret_cast<const bf16x8*>(&sA16[l32 & 15][q * 16 + 8 * h]);
+      if (l32 >= SM) af = bf16x8{};
+      const int k = q * 16 + tr_row;
+      const char* rowk = reinterpret_cast<const char*>(sB) + k * 128 + tr_col * 2;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const char* p = rowk + ((j ^ ((k >> 1) & 1)) << 6);  // k + 4 has the same swap
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 4 * 128));
+        const bf16x8 bfr = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr, af, acc[j], 0, 0, 0);
+      }
+    }
+    // register e of lane l holds row l % 32, column 32 j + 8 (e / 4) + 4 h + e % 4
+    if (l32 < SM) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 16; e4 += 4)
+          red[w][l32 * (SNS / 4) + (32 * j + 8 * (e4 >> 2) + 4 * h) / 4] =
+              f4{acc[j][e4], acc[j][e4 + 1], acc[j][e4 + 2], acc[j][e4 + 3]};
+    }
+  } else {
   f4 acc[SM];
 #pragma unroll
   for (int m = 0; m < SM; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
@@ -274,6 +386,7 @@ __global__ __launch_bounds__(ST) void gemv_k(SkArgs a) {
   for (int j = 0; j < 4; ++j) {  // selects, not an indexed register array (that would live in scratch)
     const f4 x = r == 0 ? acc[j] : r == 1 ? acc[4 + j] : r == 2 ? acc[8 + j] : acc[12 + j];
     red[w][(4 * r + j) * (SNS / 4) + c] = x;
+  }
   }
   __syncthreads();
   // thread t owns output f4 t: row t / 16, columns n0 + 4 (t % 16)
@@ -407,7 +520,9 @@ SkPlan plan(const GemmArgs& g) {
   const auto al = [](const void* q, int bytes) { return (reinterpret_cast<uintptr_t>(q) & (bytes - 1)) == 0; };
   if (g.M < 1 || g.M > SM || g.batch != 1 || g.K < 1 || g.N < 1) return p;
   if (g.post == POST_GELU && (g.resid || g.beta != 0.f)) return p;
-  if (g.a_part && (!g.a_bias || g.a_chunks < 1 || g.a_bf16 || g.post == POST_PARTIALS)) return p;
+  if (g.a_part && (!g.a_bias || g.a_chunks < 1 || g.a_bf16 || g.post == POST_PARTIALS || g.K % 4 || !al(g.a_part, 16) ||
+                   !al(g.a_bias, 16)))
+    return p;
   if (g.att_acc && (g.a_part || !g.att_ml || g.att_blocks < 1 || g.att_hs < 1 || g.att_heads < 1 ||
                     (int64_t)g.att_hs * g.att_heads != g.K || g.a_bf16))
     return p;
