@@ -377,6 +377,33 @@ def test_linear_few_rows_bf16_operands_exact(ctx, M, K, N):
     ctx.set_precision("fp32")
 
 
+@pytest.mark.parametrize("M,K,V", [(16, 768, 50257), (16, 768, 2048), (5, 1536, 300), (1, 776, 129), (3, 200, 17),
+                                   (16, 8, 130), (7, 30, 64)])
+def test_matmul_t_few_rows_bf16_exact(ctx, M, K, V):
+    """x @ w^T with at most 16 rows in the bf16 variant (the LM head of one token per
+    sequence, [GPT2-4, "Generation with KV Cache"]): the product of the bf16 operands,
+    accumulated in fp32, checked against the float64 product of the rounded operands
+    to 1e-5.  k in whole 768-deep passes (768, 1536), with a partial last pass (776,
+    200, 8), and not a multiple of 8 (30: the tiled kernel); vocabularies ragged
+    against the 128-row workgroups, and one of 50,257 rows whose output rows are
+    padded.  The bf16-only output is the exact rounding of the plain one."""
+    ctx.set_precision("bf16")
+    x, w = rnd(160 + M, (M, K)), rnd(161 + K, (V, K), 1 / np.sqrt(K))
+    ts = [ctx.tensor(a.shape, a) for a in (x, w)]
+    try:
+        y = T.matmul_t(*ts).numpy()
+        ref = _bf16_round(x).astype(np.float64) @ _bf16_round(w).astype(np.float64).T
+        assert_close(y, ref, 1e-5, "forward")
+        ctx.tape_reset()
+        yb = T.matmul_t(*ts, bf16_only=True).numpy()
+        np.testing.assert_array_equal(yb, _bf16_round(y))
+    finally:
+        ctx.tape_reset()
+        for t in ts:
+            t.release()
+        ctx.set_precision("fp32")
+
+
 @pytest.mark.parametrize("case", ["fwd_nn", "bwd_nt"])
 def test_linear_one_tile_per_cu(ctx, case):
     """About one 128x192 output tile per CU (768 columns against ~8100 rows, long

@@ -501,13 +501,16 @@ __global__ __launch_bounds__(SR) void sample_topk_reg_k(const float* __restrict_
   const int b = blockIdx.x, t = threadIdx.x;
   const float* l = logits + (int64_t)b * ld;
   // order keys; a slot past the row holds key 0, below the key of every float but
-  // a negative NaN, and the cut below is always at least 1, so it never counts
+  // a negative NaN, and the cut below is always at least 1, so it never counts.
+  // Every load is issued before any is used: a slot past the row loads the row's
+  // last logit and is zeroed afterwards (a load under a branch would be waited for
+  // on its own, 50 round trips in a row).
+  float raw[SPER];
+#pragma unroll
+  for (int j = 0; j < SPER; ++j) raw[j] = l[min(j * SR + t, V - 1)];
   uint32_t key[SPER];
 #pragma unroll
-  for (int j = 0; j < SPER; ++j) {
-    const int id = j * SR + t;
-    key[j] = id < V ? order_key(l[id]) : 0u;
-  }
+  for (int j = 0; j < SPER; ++j) key[j] = j * SR + t < V ? order_key(raw[j]) : 0u;
   uint32_t thr = 1;  // without a cut every logit survives
   if (k > 0 && k < V) {
     // The cut is the k-th largest key: the largest x with #(key >= x) >= k.
@@ -528,14 +531,13 @@ __global__ __launch_bounds__(SR) void sample_topk_reg_k(const float* __restrict_
         uint32_t v[SR / 64];
 #pragma unroll
         for (int i = 0; i < SR / 64; ++i) v[i] = tmx[t + 64 * i];
+        // the wave's count of maxima >= cand: one ballot per register, no cross-lane moves
         uint32_t lb = 0;
         for (int bit = 31; bit >= 0; --bit) {
           const uint32_t cand = lb | (1u << bit);
           int c = 0;
 #pragma unroll
-          for (int i = 0; i < SR / 64; ++i) c += v[i] >= cand;
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+          for (int i = 0; i < SR / 64; ++i) c += __popcll(__ballot(v[i] >= cand));
           if (c >= k) lb = cand;
         }
         if (t == 0) bound = lb, ncand = 0;

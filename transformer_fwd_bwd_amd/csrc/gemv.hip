@@ -510,6 +510,147 @@ __global__ __launch_bounds__(ST) void gemv_reduce_ln_k(SkArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ NT form
+// C = alpha A B^T + bias + beta C with A [M <= 16, K] and B [N, K], both
+// k-contiguous and B stored as bf16: the LM head of one token per sequence,
+// logits = h wte^T ([GPT2-4, "Generation with KV Cache"]; the product is
+// MatMulT of [Autograd-1, "Ops"]).  Each lane's MFMA fragment of B, 8
+// consecutive k of one row, is then 16 contiguous bytes of memory, so B goes
+// from HBM straight into registers and only A is staged, once per pass, in
+// LDS.  Wave w of workgroup b owns rows 128b + 16w .. +15 of B over all of k
+// and multiplies them by the 16 rows of A with v_mfma_f32_16x16x32_bf16: lane
+// l brings row l % 16 of B and of A for the k slots of its lane group l / 16,
+// and within a 128-deep k block a lane's share is 64 contiguous bytes (k = 32
+// (l / 16) + 8q + 0..7 for its four products q); both operands list the same k
+// in every slot, so the sum runs over each k once.  No partial leaves the
+// wave: one launch, no reduction.
+constexpr int NTB = 6;           // 128-deep k blocks held in registers per pass
+constexpr int NTK = NTB * 128;   // k per pass
+constexpr int NTW = 8;           // waves per workgroup (A staging then takes 12 VGPRs a lane: four waves a SIMD fit)
+constexpr int NT_ROWS = 16 * NTW;  // rows of B per workgroup
+
+struct NtArgs {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  float* C;
+  int64_t ldc;
+  uint16_t* Cbf;
+  const float* bias;
+  float alpha, beta;
+  int M, N, K, skipc, vec;
+};
+
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+// FULL: K is a multiple of the pass depth, so no k is out of range
+template <bool FULL>
+__global__ __launch_bounds__(64 * NTW, 2) void gemv_nt_k(NtArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[SM][NTK + 8];  // 16-byte row pad: conflict-free fragment reads
+  constexpr int AU = NTK / 8 / 32;  // 16-byte units of A per thread and pass
+  static_assert(64 * NTW == 32 * SM && NTK % 256 == 0, "A staging: 32 threads per row of A");
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int r = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * NT_ROWS + w * 16;
+  // rows past N read the last row again; their results are never stored
+  const uint16_t* brow = a.B + (int64_t)min(n0 + r, a.N - 1) * a.ldb + 32 * lg;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < a.K; kb += NTK) {
+    // Every k block of B this pass needs, then A.  Out-of-range elements load a
+    // valid one (clamped index) and are zeroed afterwards: a load under a branch
+    // would be waited for on its own.  A is stored to LDS once B has arrived
+    // (loads retire in order), which costs nothing: the products wait for B anyway.
+    u16x8 bv[NTB][4];
+#pragma unroll
+    for (int p = 0; p < NTB; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = kb + 128 * p + 32 * lg + 8 * q;
+        bv[p][q] = *reinterpret_cast<const u16x8*>(brow + (FULL || k < a.K ? kb + 128 * p + 8 * q : -32 * lg));
+      }
+    // thread t stages row t / 32 of A, 16-byte units t % 32 + 32 i of the pass
+    const int am = t >> 5, ac = t & 31;
+    const bool arow = am < a.M;
+    u16x8 av[AU];
+    bool aok[AU];
+#pragma unroll
+    for (int i = 0; i < AU; ++i) {
+      const int k = kb + 8 * (ac + 32 * i);
+      aok[i] = arow && (FULL || k < a.K);
+      av[i] = *reinterpret_cast<const u16x8*>(a.A + (int64_t)(arow ? am : 0) * a.lda + (FULL || k < a.K ? k : 0));
+    }
+    if (kb > 0) __syncthreads();  // the previous pass's fragment reads are done
+#pragma unroll
+    for (int i = 0; i < AU; ++i)
+      *reinterpret_cast<u16x8*>(&sA[am][8 * (ac + 32 * i)]) = aok[i] ? av[i] : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NTB; ++p) {
+      if (!FULL && kb + 128 * p >= a.K) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool in = FULL || kb + 128 * p + 32 * lg + 8 * q < a.K;
+        const u16x8 bz = in ? bv[p][q] : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&sA[r][128 * p + 32 * lg + 8 * q]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bz), af, acc, 0, 0, 0);
+      }
+    }
+  }
+  // lane l holds rows 4 (l / 16) + e of this wave's 16 rows of B, for row l % 16 of A
+  const int m = r, n = n0 + 4 * lg;
+  if (m >= a.M || n >= a.N) return;
+  f4 v = acc * a.alpha;
+  float* row = a.C + (int64_t)m * a.ldc;
+  if (a.vec && n + 3 < a.N) {
+    if (a.bias) v += *reinterpret_cast<const f4*>(a.bias + n);
+    if (a.beta != 0.f) v += a.beta * *reinterpret_cast<const f4*>(row + n);
+    if (!a.skipc) *reinterpret_cast<f4*>(row + n) = v;
+    if (a.Cbf)
+      *reinterpret_cast<u16x4*>(a.Cbf + (int64_t)m * a.ldc + n) = u16x4{bf16_of(v.x), bf16_of(v.y), bf16_of(v.z), bf16_of(v.w)};
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (n + e >= a.N) break;
+    float x = v[e];
+    if (a.bias) x += a.bias[n + e];
+    if (a.beta != 0.f) x += a.beta * row[n + e];
+    if (!a.skipc) row[n + e] = x;
+    if (a.Cbf) a.Cbf[(int64_t)m * a.ldc + n + e] = bf16_of(x);
+  }
+}
+
+// the NT form's conditions: few rows, both operands stored as bf16 with rows of
+// whole 16-byte units, and none of the fused epilogues
+bool nt_ok(const GemmArgs& g) {
+  const auto al = [](const void* q, int bytes) { return (reinterpret_cast<uintptr_t>(q) & (bytes - 1)) == 0; };
+  if (!g.b_kcontig || !g.b_bf16 || !g.a_bf16) return false;
+  if (g.M < 1 || g.M > SM || g.batch != 1 || g.K < 1 || g.N < 1 || g.K % 8) return false;
+  if (g.post != POST_NONE || g.resid || g.a_part || g.att_acc || g.a_mcontig || g.causal_a != CAUSAL_NONE ||
+      g.causal_out)
+    return false;
+  if (g.ldb % 8 || !al(g.B, 16) || g.lda % 8 || !al(g.A, 16)) return false;
+  if (!g.C && !g.c_bf16_only) return false;
+  return (int64_t)g.M * g.ldc < (1ll << 40) && (int64_t)(g.N + NT_ROWS - 1) / NT_ROWS < (1 << 24);
+}
+
+hipError_t launch_nt(const GemmArgs& g, hipStream_t s) {
+  const auto al = [](const void* q, int bytes) { return (reinterpret_cast<uintptr_t>(q) & (bytes - 1)) == 0; };
+  NtArgs a;
+  a.A = reinterpret_cast<const uint16_t*>(g.A), a.lda = g.lda, a.B = reinterpret_cast<const uint16_t*>(g.B), a.ldb = g.ldb;
+  a.C = g.C, a.ldc = g.ldc, a.Cbf = g.Cbf, a.bias = g.bias, a.alpha = g.alpha, a.beta = g.beta;
+  a.M = g.M, a.N = g.N, a.K = g.K, a.skipc = g.c_bf16_only ? 1 : 0;
+  a.vec = g.ldc % 4 == 0 && al(g.C, 16) && al(g.bias, 16) && al(g.Cbf, 8);
+  const dim3 grid((unsigned)((g.N + NT_ROWS - 1) / NT_ROWS));
+  const dim3 block(64 * NTW);
+  if (g.K % NTK == 0)
+    run_kernel(gemv_nt_k<true>, grid, block, 0, s, a);
+  else
+    run_kernel(gemv_nt_k<false>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 struct SkPlan {
   bool ok = false;
   int kc = SKC, chunks = 1, strips = 0;
@@ -565,6 +706,10 @@ int gemv_chunks(const GemmArgs& g) {
 }
 
 bool gemv(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t s, hipError_t* err) {
+  if (nt_ok(g)) {
+    *err = launch_nt(g, s);
+    return true;
+  }
   const SkPlan p = plan(g);
   if (!p.ok) return false;
   if ((p.chunks > 1 || g.post == POST_LN || g.post == POST_PARTIALS) && (!ws || ws_bytes < gemv_workspace_bytes(g)))
