@@ -57,7 +57,7 @@ FAMILY_NAMES = {
     "gemm": "gemm_kernel + gemm_dma_kernel (MatMul family, split-K reductions included)", "attn_fwd": "attn_fwd_k (fused causal attention)",
     "attn_bwd": "attn_dq_k + attn_dkv_k (fused attention backward)", "ce": "ce_fwd_grad4_k / ce kernels",
     "adamw": "adamw_k", "ln_fwd": "ln_fwd4_k", "ln_bwd": "ln_bwd_fused4_k", "gelu_fwd": "gelu forward",
-    "gelu_bwd": "gelu backward", "gemv": "gemv_k + gemv_reduce_k (decode Linears)",
+    "gelu_bwd": "gelu backward", "gemv": "gemv_k + gemv_reduce_ln_k + gemv_nt_k (decode Linears and LM head)",
     "kv_attend": "kv_attend_part_k (cached attention)", "sample": "sample_topk_reg_k",
 }
 

@@ -6,11 +6,13 @@
 // so it is bound by how many bytes are in flight, not by arithmetic.  The
 // columns go in strips of 64 and k in chunks of kc <= 128 rows, one 256-thread
 // workgroup per (strip, chunk), which puts a few hundred workgroups on the
-// 256 CUs.  In a workgroup, lane 4c + r of wave w multiplies columns 4c..4c+3
-// of k rows 4w + r + 16i by the 16 rows of A (staged in LDS, k-major, as
-// fp32); the four lanes of a quad sum through DPP, the four waves through LDS.
-// In the bf16 variant an operand stored as fp32 is rounded to bf16 as it is
-// loaded, so the products are those of the bf16 values either way.
+// 256 CUs.  In the bf16 variant (both operands bf16 values, stored so or
+// rounded as they load) a workgroup multiplies on MFMA (gemv_k's MF path); in
+// fp32, lane 4c + r of wave w multiplies columns 4c..4c+3 of k rows
+// 4w + r + 16i by the 16 rows of A (staged in LDS, k-major, as fp32) and the
+// four lanes of a quad sum through DPP.  Either way the four waves' partial
+// tiles meet in LDS.  A product with B stored [N, K] (the LM head) takes the
+// NT form below, one launch with no partials.
 //
 // With one chunk the workgroup applies the epilogue; otherwise it writes its
 // partial to ws[chunk][M][N] and gemv_reduce_k sums the chunks in order and
