@@ -31,6 +31,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// The same sum for a wave whose 64 lanes are all active: DPP within each row of
+// 16 lanes (quad swaps, then the half-row and row mirrors), then the four row
+// sums read as scalars.  No LDS round trips, where the cross-lane shuffles above
+// take six dependent ones.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_full(float v) {
+  v += dpp_f<0xb1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror: the other quad of the half-row
+  v += dpp_f<0x140>(v);  // row_mirror: the other half of the row
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
@@ -109,6 +128,15 @@ __global__ __launch_bounds__(NT) void ln_fwd4_k(const f4* __restrict__ x, const 
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * WAVES;
   const float invC = 1.f / (4 * C4);
+  // gamma and beta once per wave, requested with the first row (a column past the
+  // row reads column 0 and is not used)
+  f4 gm[J], bt[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = lane + 64 * j < C4 ? lane + 64 * j : 0;
+    gm[j] = gamma[c];
+    bt[j] = beta[c];
+  }
   for (int64_t r = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); r < rows; r += nw) {
     const f4* xr = x + r * C4;
     f4 v[J];
@@ -116,10 +144,11 @@ __global__ __launch_bounds__(NT) void ln_fwd4_k(const f4* __restrict__ x, const 
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int c = lane + 64 * j;
-      v[j] = c < C4 ? xr[c] : f4{0.f, 0.f, 0.f, 0.f};
+      v[j] = xr[c < C4 ? c : 0];
+      if (c >= C4) v[j] = f4{0.f, 0.f, 0.f, 0.f};
       s += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
     }
-    const float mu = wave_sum(s) * invC;
+    const float mu = wave_sum_full(s) * invC;
     float q = 0.f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -129,13 +158,13 @@ __global__ __launch_bounds__(NT) void ln_fwd4_k(const f4* __restrict__ x, const 
         q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
       }
     }
-    const float rs = rsqrtf(wave_sum(q) * invC + eps);
+    const float rs = rsqrtf(wave_sum_full(q) * invC + eps);
     f4* yr = y + r * C4;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int c = lane + 64 * j;
       if (c < C4) {
-        const f4 o = (v[j] - mu) * rs * gamma[c] + beta[c];
+        const f4 o = (v[j] - mu) * rs * gm[j] + bt[j];
         if (y) yr[c] = o;  // null: the bf16 copy alone
         if (ybf) ybf[r * C4 + c] = u16x4{bf16_bits(o[0]), bf16_bits(o[1]), bf16_bits(o[2]), bf16_bits(o[3])};
       }
@@ -295,7 +324,7 @@ __global__ __launch_bounds__(LNW * 64, J <= 3 ? 2 : 1) void ln_bwd_fused4_k(
 #pragma unroll
       for (int j = 0; j < J; ++j)  // zero when beta_dx == 0
         sv[j] = beta_dx != 0.f ? sr[in(j) ? lane + 64 * j : 0] : f4{0.f, 0.f, 0.f, 0.f};
-      const float m1 = wave_sum(s1) * invC, m2 = wave_sum(s2) * invC;
+      const float m1 = wave_sum_full(s1) * invC, m2 = wave_sum_full(s2) * invC;
       f4* dr = dx + r * C4;
       u16x4* dbr = dxbf ? dxbf + r * C4 : nullptr;
 #pragma unroll
