@@ -68,6 +68,37 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Cross-lane sums and maxima by DPP inside each 16-lane row (no LDS round trip);
+// only steps that cross rows use the LDS-based shuffle.  Every lane of the wave
+// must be active.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// the sum over each group of G consecutive lanes, in every lane of the group: pair,
+// quad, then the other quad of the half-row and the other half of the row (after
+// the smaller sums those mirrors hold the partner group's sum)
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dppf<0xb1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) v += dppf<0x4e>(v);   // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) v += dppf<0x141>(v);  // row_half_mirror
+  if constexpr (G >= 16) v += dppf<0x140>(v); // row_mirror
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+// the sum (or maximum) over the lanes of this row congruent to this one mod L
+// (L = 4, 8, 16 or 32), in every lane: rotations by 4 and 8 inside the row
+template <int L, bool MAX>
+__device__ __forceinline__ float row_stride_reduce(float v) {
+  static_assert(L == 4 || L == 8 || L == 16 || L == 32, "stride");
+  const auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if constexpr (L <= 4) v = op(v, dppf<0x124>(v));  // row_ror:4
+  if constexpr (L <= 8) v = op(v, dppf<0x128>(v));  // row_ror:8
+  return v;
+}
+
 // cache elements: fp32, or bf16 bits
 __device__ __forceinline__ float kv_get(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float kv_get(const uint16_t* p, int64_t i) { return __uint_as_float((unsigned)p[i] << 16); }
@@ -315,15 +346,16 @@ __global__ __launch_bounds__(256, HS <= 64 ? 4 : 2) void kv_attend_part_k(QkvSrc
     float d = 0.f;
 #pragma unroll
     for (int e = 0; e < VW; ++e) d += q[e] * KvPiece<KT>::at(kr[it], e);
-#pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+    d = group_sum<LPR>(d);
     sc[it] = j < j_hi ? d * scale : -INFINITY;
   }
   float m = -INFINITY;
 #pragma unroll
   for (int it = 0; it < IT; ++it) m = fmaxf(m, sc[it]);
+  m = row_stride_reduce<LPR, true>(m);
 #pragma unroll
-  for (int o = 32; o >= LPR; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  for (int o = 16; o <= 32; o <<= 1)
+    if (o >= LPR) m = fmaxf(m, __shfl_xor(m, o, 64));
   // a wave past the block's end (m = -inf) gets weights exp(-inf) = 0; no branch,
   // so the value loads stay where they were issued
   const float ms = m == -INFINITY ? 0.f : m;
@@ -337,8 +369,13 @@ __global__ __launch_bounds__(256, HS <= 64 ? 4 : 2) void kv_attend_part_k(QkvSrc
     for (int e = 0; e < VW; ++e) acc[e] += p * KvPiece<KT>::at(vr[it], e);
     l += p;
   }
+  // across the row groups of the wave: inside each 16-lane row by DPP, then across rows
+  l = row_stride_reduce<LPR, false>(l);
 #pragma unroll
-  for (int o = 32; o >= LPR; o >>= 1) {
+  for (int e = 0; e < VW; ++e) acc[e] = row_stride_reduce<LPR, false>(acc[e]);
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    if (o < LPR) continue;
     l += __shfl_xor(l, o, 64);
 #pragma unroll
     for (int e = 0; e < VW; ++e) acc[e] += __shfl_xor(acc[e], o, 64);

@@ -445,8 +445,17 @@ __global__ __launch_bounds__(ST) void gemv_reduce_k(SkArgs a) {
 constexpr int LN_MAXN = 2048;
 constexpr int LN_PER = LN_MAXN / 4 / ST;  // float4s per thread
 
+// the workgroup's sum: each wave's by DPP inside its 16-lane rows (the quad_sum
+// steps, then the half-row and row mirrors) and the four row sums read as scalars,
+// then the four waves through LDS
 __device__ __forceinline__ float block_sum_ln(float v, float* sh) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = quad_sum(v);
+  v += dpp<0x141>(v);  // row_half_mirror: the other quad of the half-row
+  v += dpp<0x140>(v);  // row_mirror: the other half of the row
+  v = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
+      (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
