@@ -501,8 +501,31 @@ constexpr int SPER = 50;
 constexpr int SCAP = 512;
 constexpr int SCAND = 1024;
 
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+// a wave's total (or maximum) in every lane: DPP inside the 16-lane rows, then the
+// four row results read as scalars
+__device__ __forceinline__ int wave_sumi(int v) {
+  v += dppi<0xb1>(v);
+  v += dppi<0x4e>(v);
+  v += dppi<0x141>(v);
+  v += dppi<0x140>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+__device__ __forceinline__ uint32_t wave_maxu(uint32_t v) {
+  v = max(v, (uint32_t)dppi<0xb1>((int)v));
+  v = max(v, (uint32_t)dppi<0x4e>((int)v));
+  v = max(v, (uint32_t)dppi<0x141>((int)v));
+  v = max(v, (uint32_t)dppi<0x140>((int)v));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
 __device__ __forceinline__ int block_sumi_sr(int v, int* sh) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sumi(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -513,7 +536,7 @@ __device__ __forceinline__ int block_sumi_sr(int v, int* sh) {
 }
 
 __device__ __forceinline__ uint32_t block_maxu_sr(uint32_t v, int* sh) {
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  v = wave_maxu(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = (int)v;
   __syncthreads();
