@@ -591,14 +591,23 @@ __global__ __launch_bounds__(SR) void sample_topk_reg_k(const float* __restrict_
         uint32_t v[SR / 64];
 #pragma unroll
         for (int i = 0; i < SR / 64; ++i) v[i] = tmx[t + 64 * i];
-        // the wave's count of maxima >= cand: one ballot per register, no cross-lane moves
-        uint32_t lb = 0;
-        for (int bit = 31; bit >= 0; --bit) {
+        // Every value in [min, max] of the maxima shares their bits above the highest
+        // bit where min and max differ, and so does the answer: the search starts
+        // below that bit.  A step counts per lane, then sums the wave by DPP.
+        uint32_t vmx = v[0], vmn = v[0];
+#pragma unroll
+        for (int i = 1; i < SR / 64; ++i) vmx = max(vmx, v[i]), vmn = min(vmn, v[i]);
+        vmx = wave_maxu(vmx);
+        vmn = ~wave_maxu(~vmn);
+        const uint32_t diff = vmx ^ vmn;
+        const int hb = diff ? 31 - __clz(diff) : -1;
+        uint32_t lb = hb < 0 ? vmx : hb == 31 ? 0u : vmx & ~((2u << hb) - 1u);
+        for (int bit = hb; bit >= 0; --bit) {
           const uint32_t cand = lb | (1u << bit);
           int c = 0;
 #pragma unroll
-          for (int i = 0; i < SR / 64; ++i) c += __popcll(__ballot(v[i] >= cand));
-          if (c >= k) lb = cand;
+          for (int i = 0; i < SR / 64; ++i) c += v[i] >= cand;
+          if (wave_sumi(c) >= k) lb = cand;
         }
         if (t == 0) bound = lb, ncand = 0;
       }
