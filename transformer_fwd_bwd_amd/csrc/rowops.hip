@@ -50,6 +50,17 @@ __device__ __forceinline__ float wave_sum_full(float v) {
   const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
   return (r0 + r1) + (r2 + r3);
 }
+__device__ __forceinline__ float wave_max_full(float v) {
+  v = fmaxf(v, dpp_f<0xb1>(v));
+  v = fmaxf(v, dpp_f<0x4e>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
@@ -741,7 +752,7 @@ void ce_fwd_grad4_k(const X* __restrict__ logits, int64_t ld,
     const f4 x = x_(u);
     m = fmaxf(m, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
   }
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  m = wave_max_full(m);
   if (lane == 0) red[w] = m;
   __syncthreads();
   m = red[0];
@@ -755,7 +766,7 @@ void ce_fwd_grad4_k(const X* __restrict__ logits, int64_t ld,
     const f4 x = x_(u);
     sum += (ce_exp(x[0] - m) + ce_exp(x[1] - m)) + (ce_exp(x[2] - m) + ce_exp(x[3] - m));
   }
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  sum = wave_sum_full(sum);
   if (lane == 0) red[w] = sum;
   __syncthreads();
   float S = 0.f;
