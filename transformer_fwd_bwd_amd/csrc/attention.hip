@@ -22,6 +22,7 @@
 #include <algorithm>
 
 #include "kernels.h"
+#include "lanes.h"
 
 namespace tfb {
 namespace {
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
       mx *= sc;
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = lanes_xor32_max(mx);
       // m is the reference the running sum l and the output o are scaled to.  It
       // only moves when a score exceeds it by more than RESCALE_MARGIN (log2
       // units), so p <= 2^RESCALE_MARGIN; o / l and m + log2(l) are unchanged by
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(NT, 3) void attn_fwd_k(AttnArgs a) {
           st[kt][r] = p;
           sum += p;
         }
-      sum += __shfl_xor(sum, 32, 64);
+      sum = lanes_xor32_add(sum);
       l += sum;
 #pragma unroll
       for (int s = 0; s < KVB / 16; ++s) {
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(NT, 2) void attn_dq_k(AttnArgs a) {
     }
     Dq = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
-  Dq += __shfl_xor(Dq, 32, 64);
+  Dq = lanes_xor32_add(Dq);
   if (h == 0 && q < a.T) a.D[(int64_t)bh * a.T + q] = Dq;
   const float sc = a.scale * LOG2E;
 

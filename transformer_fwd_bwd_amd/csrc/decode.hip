@@ -23,6 +23,7 @@
 #include <algorithm>
 
 #include "kernels.h"
+#include "lanes.h"
 
 namespace tfb {
 namespace {
@@ -68,9 +69,8 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Cross-lane sums and maxima by DPP inside each 16-lane row (no LDS round trip);
-// only steps that cross rows use the LDS-based shuffle.  Every lane of the wave
-// must be active.
+// Cross-lane sums and maxima by DPP inside each 16-lane row and by the permlane
+// swaps across rows (no LDS round trip).  Every lane of the wave must be active.
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
@@ -84,8 +84,8 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (G >= 4) v += dppf<0x4e>(v);   // quad_perm [2,3,0,1]
   if constexpr (G >= 8) v += dppf<0x141>(v);  // row_half_mirror
   if constexpr (G >= 16) v += dppf<0x140>(v); // row_mirror
-  if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
-  if constexpr (G >= 64) v += __shfl_xor(v, 32, 64);
+  if constexpr (G >= 32) v = lanes_xor16_add(v);
+  if constexpr (G >= 64) v = lanes_xor32_add(v);
   return v;
 }
 // the sum (or maximum) over the lanes of this row congruent to this one mod L
@@ -353,9 +353,8 @@ __global__ __launch_bounds__(256, HS <= 64 ? 4 : 2) void kv_attend_part_k(QkvSrc
 #pragma unroll
   for (int it = 0; it < IT; ++it) m = fmaxf(m, sc[it]);
   m = row_stride_reduce<LPR, true>(m);
-#pragma unroll
-  for (int o = 16; o <= 32; o <<= 1)
-    if (o >= LPR) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if constexpr (LPR <= 16) m = lanes_xor16_max(m);
+  m = lanes_xor32_max(m);
   // a wave past the block's end (m = -inf) gets weights exp(-inf) = 0; no branch,
   // so the value loads stay where they were issued
   const float ms = m == -INFINITY ? 0.f : m;
@@ -373,13 +372,14 @@ __global__ __launch_bounds__(256, HS <= 64 ? 4 : 2) void kv_attend_part_k(QkvSrc
   l = row_stride_reduce<LPR, false>(l);
 #pragma unroll
   for (int e = 0; e < VW; ++e) acc[e] = row_stride_reduce<LPR, false>(acc[e]);
+  if constexpr (LPR <= 16) {
+    l = lanes_xor16_add(l);
 #pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    if (o < LPR) continue;
-    l += __shfl_xor(l, o, 64);
-#pragma unroll
-    for (int e = 0; e < VW; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+    for (int e = 0; e < VW; ++e) acc[e] = lanes_xor16_add(acc[e]);
   }
+  l = lanes_xor32_add(l);
+#pragma unroll
+  for (int e = 0; e < VW; ++e) acc[e] = lanes_xor32_add(acc[e]);
   if (lane == 0) wm[w] = m, wl[w] = l;
   if (r == 0) {
 #pragma unroll
