@@ -577,6 +577,33 @@ def test_embedding_routing_is_bit_exact(ctx):
     Rt.release()
 
 
+@pytest.mark.parametrize("reps", [[1, 62, 63, 64, 65, 1], [1300, 2, 700, 127, 128, 129]])
+def test_embedding_backward_long_runs_exact(ctx, reps):
+    """[Autograd-1, table of ops: Embedding] backward: a wave reads a window of 64
+    sorted keys at once, so runs of equal ids of 62..65 (the window's edge) and runs
+    far longer than a window (the rest of the run read key by key) must still sum
+    every row once; integer gradients make the sums exact, so the check is bit for bit
+    (the ids are shuffled, so the sort builds the runs; 2,386 ids fit one chunk)."""
+    C = 70
+    base = np.concatenate([np.full(r, i, np.int32) for i, r in enumerate(reps)])
+    ids = base[S.rng_for(31).permutation(base.size)]
+    n, V = ids.size, len(reps)
+    table = rnd(32, (V, C))
+    up = S.rng_for(33).integers(-3, 4, size=(1, n, C)).astype(np.float32)
+    t = ctx.tensor(table.shape, table)
+    Rt = ctx.tensor(up.shape, up)
+    try:
+        out = T.embedding(t, ids, 1)
+        ctx.backward(T.sum_all(T.mul(out, Rt)))
+        expect = np.zeros((V, C), np.float64)
+        np.add.at(expect, ids, up.reshape(n, C))
+        assert np.array_equal(t.grad(), expect.astype(np.float32))
+    finally:
+        ctx.tape_reset()
+        t.release()
+        Rt.release()
+
+
 def test_narrow_split_merge(ctx):
     x = rnd(31, (2, 37, 3 * 96))
     check(ctx, "fp32", lambda a: T.narrow(a, 96, 96), lambda a: E.narrow(a, 96, 96), [x], (2, 37, 96))

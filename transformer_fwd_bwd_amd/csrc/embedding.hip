@@ -72,29 +72,55 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_chunks_k(const int32_t* __r
   for (int i = threadIdx.x; i < CHUNK; i += SORT_THREADS) keys_out[base + i] = k[i];
 }
 
-// one wavefront per chunk position; positions that start a run sum it
+// one wavefront per chunk position; positions that start a run sum it.  The
+// wave reads keys p-1 .. p+62 at once (lane i holds key p-1+i), finds its run
+// with one ballot, takes the run's rows from those lanes, and requests the
+// gradient rows two at a time with every column load issued before the first
+// is added (out-of-range columns and rows load a valid element and are not
+// added; two rather than four keeps four waves a SIMD).  Rows are added in
+// ascending order, as the sort left them.
 __global__ __launch_bounds__(NT) void segsum_k(const uint64_t* __restrict__ keys, int len, const float* __restrict__ g,
                                                int64_t C, float* __restrict__ dtable, int64_t rows) {
-  const int p = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  constexpr int RB = 2;  // rows in flight
+  const int p = __builtin_amdgcn_readfirstlane(blockIdx.x * (NT / 64) + (threadIdx.x >> 6));  // uniform per wave
   const int lane = threadIdx.x & 63;
   if (p >= len) return;
-  const uint32_t id = (uint32_t)(keys[p] >> 32);
+  const int kq = p - 1 + lane;
+  const uint64_t kv = keys[min(max(kq, 0), len - 1)];
+  const uint32_t kid = (uint32_t)(kv >> 32), krow = (uint32_t)kv;
+  const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)kid, 1);
   if ((int64_t)id >= rows) return;  // negative ids sort as large unsigned values
-  if (p > 0 && (uint32_t)(keys[p - 1] >> 32) == id) return;
-  int e = p + 1;
-  while (e < len && (uint32_t)(keys[e] >> 32) == id) ++e;
+  if (p > 0 && (uint32_t)__builtin_amdgcn_readlane((int)kid, 0) == id) return;
+  // lanes 1.. holding this id, consecutively from lane 1: the run inside the window
+  const uint64_t same = __ballot(lane >= 1 && kq < len && kid == id);
+  int e = p + (int)__builtin_ctzll(~(same >> 1));
+  if (e == p + 63)
+    while (e < len && (uint32_t)(keys[e] >> 32) == id) ++e;
   float* dst = dtable + (int64_t)id * C;
   for (int64_t c0 = 0; c0 < C; c0 += 64 * 16) {
     float acc[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-    for (int q = p; q < e; ++q) {
-      const int64_t r = (int64_t)(uint32_t)(keys[q] & 0xffffffffu);
-      const float* src = g + r * C;
+    for (int q = p; q < e; q += RB) {
+      float v[RB][16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t c = c0 + lane + 64 * j;
-        if (c < C) acc[j] += src[c];
+      for (int i = 0; i < RB; ++i) {
+        const int qi = min(q + i, e - 1);
+        const int64_t r = qi - p < 63 ? (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)krow, qi - p + 1)
+                                      : (int64_t)(uint32_t)(keys[qi] & 0xffffffffu);
+        const float* src = g + r * C;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int64_t c = c0 + lane + 64 * j;
+          v[i][j] = src[c < C ? c : 0];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (q + i >= e) break;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (c0 + lane + 64 * j < C) acc[j] += v[i][j];
       }
     }
 #pragma unroll
