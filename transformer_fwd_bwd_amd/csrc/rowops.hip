@@ -588,7 +588,15 @@ __global__ __launch_bounds__(NT) void ce_fwd_k(const float* __restrict__ logits,
 __global__ __launch_bounds__(NT) void mean_k(const float* __restrict__ v, int64_t n, float* __restrict__ out) {
   __shared__ double sh[NT];
   double s = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += NT) s += (double)v[i];
+  int64_t i = threadIdx.x;
+  for (; i + 7 * NT < n; i += 8 * NT) {  // eight loads in flight, added in index order
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = v[i + u * NT];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += (double)x[u];
+  }
+  for (; i < n; i += NT) s += (double)v[i];
   sh[threadIdx.x] = s;
   __syncthreads();
   for (int o = NT / 2; o > 0; o >>= 1) {
