@@ -443,13 +443,14 @@ __global__ __launch_bounds__(NT) void csm_fwd_k(const float* __restrict__ x, flo
 #pragma unroll
       for (int j = 0; j < MAXV; ++j) {
         const int c = lane + 64 * j;
-        v[j] = c < vis ? xr[c] : -INFINITY;
+        const float t = xr[min(c, vis - 1)];  // every load issued before any is used
+        v[j] = c < vis ? t : -INFINITY;
         mx = fmaxf(mx, v[j]);
       }
     } else {
       for (int c = lane; c < vis; c += 64) mx = fmaxf(mx, xr[c]);
     }
-    mx = wave_max(mx);
+    mx = wave_max_full(mx);
     float s = 0.f;
     if (CACHED) {
 #pragma unroll
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(NT) void csm_fwd_k(const float* __restrict__ x, flo
     } else {
       for (int c = lane; c < vis; c += 64) s += expf(xr[c] - mx);
     }
-    const float inv = 1.f / wave_sum(s);
+    const float inv = 1.f / wave_sum_full(s);
     if (CACHED) {
 #pragma unroll
       for (int j = 0; j < MAXV; ++j) {
@@ -499,14 +500,15 @@ __global__ __launch_bounds__(NT) void csm_bwd_k(const float* __restrict__ g, con
 #pragma unroll
       for (int j = 0; j < MAXV; ++j) {
         const int c = lane + 64 * j;
-        gv[j] = c < vis ? gr[c] : 0.f;
-        pv[j] = c < vis ? pr[c] : 0.f;
+        const float tg = gr[min(c, vis - 1)], tp = pr[min(c, vis - 1)];  // loads issued together
+        gv[j] = c < vis ? tg : 0.f;
+        pv[j] = c < vis ? tp : 0.f;
         s += gv[j] * pv[j];
       }
     } else {
       for (int c = lane; c < vis; c += 64) s += gr[c] * pr[c];
     }
-    s = wave_sum(s);
+    s = wave_sum_full(s);
     if (CACHED) {
 #pragma unroll
       for (int j = 0; j < MAXV; ++j) {
